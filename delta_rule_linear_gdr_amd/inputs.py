@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for chunkwise gated delta-rule attention.
+
+This module holds the input recipe only -- random draws, per-token feature
+normalisation, the gate/weight activations that produce the operator's inputs,
+and rounding to the storage dtype. It contains none of the operator's
+arithmetic, and it is the one module that both the GPU path's tests/bench and
+the CPU oracle's callers use.
+
+Recipe (ReWY paper App. G.3 "Numerical coverage": feature-normalised Gaussian
+queries/keys, Gaussian values and output adjoints, query scale, Gaussian
+states scaled by 0.1; log gates from a log-sigmoid; weights in (0, 1)):
+  numpy.random.default_rng(seed), float64 draws in this order:
+    q_raw, k_raw, v ~ N(0, 1)                       [B,T,H,DK|DV]
+    gate_pre ~ N(gate_mean, 1)                      [B,T,H] or [B,T,H,DK]
+    beta_pre ~ N(0, 1)                              [B,T,H]
+    dO ~ N(0, 1)                                    [B,T,H,DV]
+    h0  = h0_std  * N(0, 1)                         [B,H,DK,DV]  (only if h0_std > 0)
+    dht = dht_std * N(0, 1)                         [B,H,DK,DV]  (only if dht_std > 0)
+  q = q_raw / |q_raw| / sqrt(DK);  k = k_raw / |k_raw|   (per token and head)
+  g = log_sigmoid(gate_pre)  (stored fp32);  beta = sigmoid(beta_pre)
+  q, k, v, beta, dO are rounded to the storage dtype (bf16: round-to-nearest-
+  even through fp32); g, h0, dht are fp32.
+Every returned array is float64 holding exactly the rounded values, so a
+reference computed from them sees the same numbers as the device.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def round_fp32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to bfloat16 (nearest-even, via fp32), returned as float64."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return round_bf16(x)
+    if dtype == "fp32":
+        return round_fp32(x)
+    raise ValueError(dtype)
+
+
+@dataclass
+class Workload:
+    """A named synthetic workload (shape + distributions)."""
+    name: str
+    gate: str          # "scalar" (GDN) or "vector" (KDA)
+    B: int
+    T: int
+    H: int
+    dtype: str = "bf16"
+    DK: int = 128
+    DV: int = 128
+    gate_mean: float = 4.0
+    h0_std: float = 0.0
+    dht_std: float = 0.0
+    seed: int = 0
+
+    def make(self) -> dict:
+        return make_inputs(self.B, self.T, self.H, self.DK, self.DV, self.gate, self.dtype,
+                           self.seed, self.gate_mean, self.h0_std, self.dht_std)
+
+
+# The five workloads of the build: GDN at (1,512,4) fp32, (1,2048,16) and
+# (1,8192,16) bf16; KDA at (2,2048,16) and (1,8192,16) bf16 with h0 ~ 0.1 N(0,1).
+WORKLOADS = {
+    "gdn_1x512x4_fp32": Workload("gdn_1x512x4_fp32", "scalar", 1, 512, 4, "fp32"),
+    "gdn_1x2048x16": Workload("gdn_1x2048x16", "scalar", 1, 2048, 16),
+    "gdn_1x8192x16": Workload("gdn_1x8192x16", "scalar", 1, 8192, 16),
+    "kda_2x2048x16": Workload("kda_2x2048x16", "vector", 2, 2048, 16, gate_mean=3.0),
+    "kda_1x8192x16": Workload("kda_1x8192x16", "vector", 1, 8192, 16, gate_mean=3.0,
+                              h0_std=0.1),
+}
+
+
+def make_inputs(B, T, H, DK=128, DV=128, gate="scalar", dtype="bf16", seed=0,
+                gate_mean=4.0, h0_std=0.0, dht_std=0.0) -> dict:
+    rng = np.random.default_rng(seed)
+    q_raw = rng.standard_normal((B, T, H, DK))
+    k_raw = rng.standard_normal((B, T, H, DK))
+    v = rng.standard_normal((B, T, H, DV))
+    gshape = (B, T, H) if gate == "scalar" else (B, T, H, DK)
+    gate_pre = rng.standard_normal(gshape) + gate_mean
+    beta_pre = rng.standard_normal((B, T, H))
+    dO = rng.standard_normal((B, T, H, DV))
+    h0 = h0_std * rng.standard_normal((B, H, DK, DV)) if h0_std > 0 else np.zeros((B, H, DK, DV))
+    dht = dht_std * rng.standard_normal((B, H, DK, DV)) if dht_std > 0 else np.zeros((B, H, DK, DV))
+    qn = np.linalg.norm(q_raw, axis=-1, keepdims=True)
+    kn = np.linalg.norm(k_raw, axis=-1, keepdims=True)
+    q = q_raw / np.maximum(qn, 1e-30) / np.sqrt(DK)
+    k = k_raw / np.maximum(kn, 1e-30)
+    g = -np.logaddexp(0.0, -gate_pre)           # log_sigmoid
+    beta = 1.0 / (1.0 + np.exp(-beta_pre))       # sigmoid
+    return dict(
+        q=round_to(q, dtype), k=round_to(k, dtype), v=round_to(v, dtype),
+        g=round_fp32(g), beta=round_to(beta, dtype), dO=round_to(dO, dtype),
+        h0=round_fp32(h0), dht=round_fp32(dht),
+        gate=gate, dtype=dtype,
+    )

@@ -1,0 +1,249 @@
+"""fp64 chunkwise forms of gated delta-rule attention (numpy).
+
+TEST INFRASTRUCTURE (see oracle/__init__.py). These are the method's own
+algebraic forms, written from the ReWY paper: they pin the token oracle (the
+chunk forms must reproduce it) and pin the algebra (the reduced and the
+expanded backward graphs must agree, with the FLOP counts the pages print).
+
+Notation (paper Sec. 2.3 and Sec. 3; the symbols are the ones the onedev.kr
+summary prints in "How it works" and "What is different"). For one chunk of
+n tokens and one head, rows are tokens, the state S is key-major (DK x DV):
+    G      chunk-local inclusive cumsum of the log decay g; gam = exp(G)
+    E  = diag(beta) (gam * K)     erase factor
+    Y  = K / gam                  write key, undecayed to the chunk start
+    Z  = diag(beta) V
+    Qg = gam * Q,   Kt = exp(G_n - G) * K
+    L  = strict_lower(E Y^T),  M = I + L,  A = M^{-1}
+    W  = A E,   U = A Z,   R = U - W S     (so M R = Z - E S)
+    Hm = lower_incl(Qg Y^T)                inclusive output projection
+    O  = Qg S + Hm R
+    S' = diag(gam_n) S + Kt^T R
+Backward, given the output adjoint Ob and the next-state adjoint Sbn:
+    Rb = Hm^T Ob + Kt Sbn        (both paths summed before the pullback, Sec. 3.1)
+  ReWY producer (three products; Sec. 3.1-3.2):
+    P = A^T Rb;  Zb = P;  Eb_dir = -P S^T;  D = -strict_lower(P R^T);
+    Sb_res = -E^T P
+  expanded WY producer (seven products; Sec. 2.3, "conventional WY backward"):
+    Wb = -Rb S^T;  Ab = Rb Z^T + Wb E^T;  Mb = -A^T Ab A^T;  D = strict_lower(Mb);
+    Eb_dir = A^T Wb;  Zb = A^T Rb;  Sb_res = -W^T Rb
+  shared interaction contractions:
+    Eb = Eb_dir + D Y;  Yb = Hb^T Qg + D^T E  with Hb = lower_incl(Ob R^T);
+    Qgb = Ob S^T + Hb Y;  Ktb = R Sbn^T;  Sb = diag(gam_n) Sbn + Qg^T Ob + Sb_res
+  feature-local chain rules:
+    dq = gam Qgb;  dv = beta Zb;  dbeta = <Zb, v> + <Eb, gam k>  (undivided, App. B.3)
+    dk = beta gam Eb + Yb / gam + exp(G_n - G) Ktb
+    Gb = Qg Qgb + E Eb - Y Yb - Kt Ktb;  Gb_n += sum_j Kt_j Ktb_j + gam_n rowsum(S Sbn)
+    scalar gate: Gb summed over features (App. E.1); dg = reverse cumsum of Gb (Sec. 3.5)
+Consumers of D and Hb:
+  "direct"   the dense D Y, D^T E, Hb Y, Hb^T Qg above;
+  "gram"     Gram elimination for a scalar gate (Sec. 3.4): Gamma = D o Lam,
+             Gq = Hb o Lam (Lam_ij = exp(G_i - G_j)), A_K = Gamma K,
+             B_K = Gamma^T diag(beta) K; gate and beta terms from row inner
+             products, no K K^T;
+  "centred"  centred matrix intra for a vector gate (Sec. 3.3): c = (max G +
+             min G)/2 per feature, alpha = exp(G - c), zeta = exp(c - G),
+             Q' = alpha Q, E' = beta alpha K, Y' = zeta K;
+             U_q = Hb Y', U_e = D Y', U_y = Hb^T Q' + D^T E'.
+Readings where the pages are silent are the ones listed with the design notes:
+decay before erase, inclusive output, key-major state, undivided dbeta.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+class FlopCounter:
+    """Counts dense matmul FLOPs (2 m n k, the pages' convention) per tag."""
+
+    def __init__(self):
+        self.by_tag: dict[str, int] = {}
+        self.calls: dict[str, int] = {}
+
+    def mm(self, a, b, tag="other"):
+        m, k = a.shape
+        k2, n = b.shape
+        assert k == k2
+        self.by_tag[tag] = self.by_tag.get(tag, 0) + 2 * m * n * k
+        self.calls[tag] = self.calls.get(tag, 0) + 1
+        return a @ b
+
+    def __getitem__(self, tag):
+        return self.by_tag.get(tag, 0)
+
+
+def _tril(x, k):
+    return np.tril(x, k)
+
+
+def _chunks(T, C):
+    return [(s, min(s + C, T)) for s in range(0, T, C)]
+
+
+def _gate_parts(gc, vec, DK):
+    """gc: log decays of one chunk, shape (n,) or (n, DK). Returns G (n, DK)."""
+    G = np.cumsum(gc, axis=0)
+    if not vec:
+        G = np.repeat(G[:, None], DK, axis=1)
+    return G
+
+
+def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
+    """Chunkwise forward of one (b, h) sequence.
+
+    q, k: (T, DK); v: (T, DV); g: (T,) or (T, DK); beta: (T,); h0: (DK, DV).
+    Returns o (T, DV), ht (DK, DV) and, if keep, the per-chunk intermediates.
+    """
+    T, DK = q.shape
+    DV = v.shape[1]
+    vec = g.ndim == 2
+    S = np.array(h0, dtype=np.float64, copy=True)
+    o = np.zeros((T, DV))
+    cache = []
+    for s, e in _chunks(T, C):
+        n = e - s
+        Q, K, V, bt = q[s:e], k[s:e], v[s:e], beta[s:e]
+        G = _gate_parts(g[s:e], vec, DK)
+        gam = np.exp(G)
+        E = bt[:, None] * gam * K
+        Y = K / gam
+        Z = bt[:, None] * V
+        Qg = gam * Q
+        Kt = np.exp(G[-1][None, :] - G) * K
+        L = _tril(E @ Y.T, -1)
+        A = np.linalg.inv(np.eye(n) + L)
+        W = A @ E
+        U = A @ Z
+        R = U - W @ S
+        Hm = _tril(Qg @ Y.T, 0)
+        o[s:e] = Qg @ S + Hm @ R
+        if keep:
+            cache.append(dict(s=s, e=e, S=S.copy(), G=G, gam=gam, E=E, Y=Y, Z=Z, Qg=Qg, Kt=Kt,
+                              L=L, A=A, W=W, U=U, R=R, Hm=Hm))
+        S = gam[-1][:, None] * S + Kt.T @ R
+    return (o, S, cache) if keep else (o, S)
+
+
+def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="direct",
+                   flops: FlopCounter | None = None, centre=None):
+    """Chunkwise backward of one (b, h) sequence.
+
+    producer: "rewy" (three products) or "wy7" (expanded graph).
+    consumer: "direct", "gram" (scalar gate only) or "centred" (any gate).
+    centre:   optional override of the centring constants, a function
+              (G (n, DK)) -> c (DK,), used to test centring invariance.
+    Returns dict dq, dk, dv, dg, dbeta, dh0.
+    """
+    fc = flops if flops is not None else FlopCounter()
+    mm = fc.mm
+    T, DK = q.shape
+    DV = v.shape[1]
+    vec = g.ndim == 2
+    if consumer == "gram" and vec:
+        raise ValueError("Gram elimination applies to a scalar gate")
+    _, _, cache = chunk_forward(q, k, v, g, beta, h0, C, keep=True)
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros_like(k, dtype=np.float64)
+    dv = np.zeros_like(v, dtype=np.float64)
+    dbeta = np.zeros(T)
+    dg = np.zeros((T, DK)) if vec else np.zeros(T)
+    Sbn = np.zeros((DK, DV)) if dht is None else np.array(dht, dtype=np.float64)
+    for ch in reversed(cache):
+        s, e = ch["s"], ch["e"]
+        S, G, gam, E, Y, Z, Qg, Kt, A, W, R, Hm = (ch[x] for x in (
+            "S", "G", "gam", "E", "Y", "Z", "Qg", "Kt", "A", "W", "R", "Hm"))
+        Q, K, V, bt, Ob = q[s:e], k[s:e], v[s:e], beta[s:e], dO[s:e]
+        gn = gam[-1]
+        Rb = Hm.T @ Ob + Kt @ Sbn
+        # --- local WY producer ---
+        if producer == "rewy":
+            P = mm(A.T, Rb, "local_wy")
+            Zb = P
+            Eb = -mm(P, S.T, "local_wy")
+            D = -_tril(mm(P, R.T, "local_wy"), -1)
+            Sb_res = -E.T @ P
+        elif producer == "wy7":
+            Wb = -mm(Rb, S.T, "local_wy")
+            Ab = mm(Rb, Z.T, "local_wy") + mm(Wb, E.T, "local_wy")
+            Mb = -mm(mm(A.T, Ab, "local_wy"), A.T, "local_wy")
+            D = _tril(Mb, -1)
+            Eb = mm(A.T, Wb, "local_wy")
+            Zb = mm(A.T, Rb, "local_wy")
+            Sb_res = -W.T @ Rb
+        else:
+            raise ValueError(producer)
+        Hb = _tril(Ob @ R.T, 0)
+        # state-direct terms
+        Qgb = Ob @ S.T
+        Ktb = R @ Sbn.T
+        Yb = np.zeros_like(Y)
+        dq_c = np.zeros_like(Q)
+        dk_c = np.zeros_like(K)
+        db_c = np.zeros(e - s)
+        Gb = np.zeros((e - s, DK))
+        # --- consumers of D and Hb ---
+        if consumer == "direct":
+            Eb = Eb + D @ Y
+            Yb = Yb + Hb.T @ Qg + D.T @ E
+            Qgb = Qgb + Hb @ Y
+        elif consumer == "gram":
+            Gs = G[:, 0]
+            Lam = np.tril(np.exp(Gs[:, None] - Gs[None, :]), 0)
+            Gam = D * Lam
+            Gq = Hb * Lam
+            AK = Gam @ K
+            BK = Gam.T @ (bt[:, None] * K)
+            GqK = Gq @ K
+            GqtQ = Gq.T @ Q
+            dk_c += bt[:, None] * AK + BK + GqtQ
+            dq_c += GqK
+            db_c += np.sum(K * AK, axis=1)
+            gl = bt * np.sum(K * AK, axis=1) - np.sum(K * BK, axis=1) \
+                + np.sum(Q * GqK, axis=1) - np.sum(K * GqtQ, axis=1)
+            Gb[:, 0] += gl  # scalar gate: all feature columns are summed below
+        elif consumer == "centred":
+            c = centre(G) if centre is not None else 0.5 * (G.max(axis=0) + G.min(axis=0))
+            al = np.exp(G - c[None, :])
+            ze = np.exp(c[None, :] - G)
+            Qp = al * Q
+            Ep = bt[:, None] * al * K
+            Yp = ze * K
+            Uq = Hb @ Yp
+            Ue = D @ Yp
+            Uy = Hb.T @ Qp + D.T @ Ep
+            dq_c += al * Uq
+            dk_c += bt[:, None] * al * Ue + ze * Uy
+            db_c += np.sum(Ue * al * K, axis=1)
+            Gb += Qp * Uq + Ep * Ue - Yp * Uy
+        else:
+            raise ValueError(consumer)
+        # --- feature-local chain rules for the remaining terms ---
+        dq_c += gam * Qgb
+        dv[s:e] = bt[:, None] * Zb
+        db_c += np.sum(Zb * V, axis=1) + np.sum(Eb * gam * K, axis=1)
+        dk_c += bt[:, None] * gam * Eb + Yb / gam + np.exp(G[-1][None, :] - G) * Ktb
+        Gb += Qg * Qgb + E * Eb - Y * Yb - Kt * Ktb
+        Gb[-1] += np.sum(Kt * Ktb, axis=0) + gn * np.sum(S * Sbn, axis=1)
+        Gtok = Gb if vec else Gb.sum(axis=1)
+        dg[s:e] = np.flip(np.cumsum(np.flip(Gtok, 0), axis=0), 0)
+        dq[s:e] = dq_c
+        dk[s:e] = dk_c
+        dbeta[s:e] = db_c
+        # --- reverse state scan ---
+        Sbn = gn[:, None] * Sbn + Qg.T @ Ob + Sb_res
+    return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=Sbn)
+
+
+def local_wy_flops(n: int, dk: int, dv: int, producer: str) -> tuple[int, int]:
+    """(FLOPs, number of products) of the local WY producer, counted by running
+    chunk_backward once on one random chunk of n tokens."""
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((n, dk))
+    k = rng.standard_normal((n, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((n, dv))
+    g = -0.01 * np.ones(n)
+    beta = np.full(n, 0.5)
+    h0 = rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((n, dv))
+    fc = FlopCounter()
+    chunk_backward(q, k, v, g, beta, h0, dO, None, n, producer=producer, flops=fc)
+    return fc["local_wy"], fc.calls.get("local_wy", 0)

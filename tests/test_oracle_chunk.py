@@ -1,0 +1,126 @@
+"""Pins of the chunkwise algebra: the chunk forms reproduce the token oracle
+at every chunk size (including tails), the three-product ReWY backward equals
+the seven-product expanded backward, the consumers (Gram elimination,
+centred matrix intra) equal the dense route, and the counted FLOPs reproduce
+the figures the pages print.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import chunk_forms as cf
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _seq(gate, T, DK, DV, seed=0, strong=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, DK)) / np.sqrt(DK)
+    k = rng.standard_normal((T, DK))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((T, DV))
+    gs = (T,) if gate == "scalar" else (T, DK)
+    mean = 0.0 if strong else 3.0
+    g = -np.logaddexp(0, -(rng.standard_normal(gs) + mean))
+    beta = 1 / (1 + np.exp(-rng.standard_normal(T)))
+    beta[::3] = 0.0
+    h0 = 0.1 * rng.standard_normal((DK, DV))
+    dO = rng.standard_normal((T, DV))
+    dht = 0.1 * rng.standard_normal((DK, DV))
+    return q, k, v, g, beta, h0, dO, dht
+
+
+def _token(q, k, v, g, beta, h0, dO, dht):
+    B = lambda x: x[None, :, None]  # noqa: E731  (T,...) -> (1,T,1,...)
+    o, ht = oracle.token_fwd(B(q), B(k), B(v), B(g), B(beta), h0[None, None])
+    gr = oracle.token_bwd(B(q), B(k), B(v), B(g), B(beta), h0[None, None], B(dO), dht[None, None])
+    gr = {n: (a[0, :, 0] if n != "dh0" else a[0, 0]) for n, a in gr.items()}
+    return o[0, :, 0], ht[0, 0], gr
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("C", [1, 2, 4, 16, 64])
+def test_chunk_forms_reproduce_token_oracle(gate, C):
+    T = 150  # not a multiple of 4, 16 or 64: exercises the tail chunk
+    q, k, v, g, beta, h0, dO, dht = _seq(gate, T, 8, 5, seed=C)
+    o_t, ht_t, gr_t = _token(q, k, v, g, beta, h0, dO, dht)
+    o_c, ht_c = cf.chunk_forward(q, k, v, g, beta, h0, C)
+    assert _rel(o_c, o_t) < 1e-12
+    assert _rel(ht_c, ht_t) < 1e-12
+    gr_c = cf.chunk_backward(q, k, v, g, beta, h0, dO, dht, C, "rewy", "direct")
+    for n in gr_t:
+        assert _rel(gr_c[n], gr_t[n]) < 1e-10, n
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_three_product_equals_seven_product(gate):
+    T, DK, DV = 192, 32, 16
+    args = _seq(gate, T, DK, DV, seed=21)
+    a = cf.chunk_backward(*args, 64, "rewy", "direct")
+    b = cf.chunk_backward(*args, 64, "wy7", "direct")
+    for n in a:
+        assert _rel(a[n], b[n]) < 1e-10, n
+
+
+def test_gram_elimination_equals_dense_route():
+    args = _seq("scalar", 160, 16, 12, seed=31)
+    a = cf.chunk_backward(*args, 64, "rewy", "direct")
+    b = cf.chunk_backward(*args, 64, "rewy", "gram")
+    for n in a:
+        assert _rel(b[n], a[n]) < 1e-12, n
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_centred_matrix_intra_equals_dense_route(gate):
+    args = _seq(gate, 160, 16, 12, seed=41, strong=True)
+    a = cf.chunk_backward(*args, 64, "rewy", "direct")
+    b = cf.chunk_backward(*args, 64, "rewy", "centred")
+    for n in a:
+        assert _rel(b[n], a[n]) < 1e-12, n
+
+
+def test_centring_constant_cancels():
+    """Any per-feature centre gives the same gradients (scaling invariance)."""
+    args = _seq("vector", 128, 16, 8, seed=51)
+    rng = np.random.default_rng(52)
+    a = cf.chunk_backward(*args, 64, "rewy", "centred")
+    b = cf.chunk_backward(*args, 64, "rewy", "centred",
+                          centre=lambda G: rng.uniform(-3, 3, size=G.shape[1]))
+    for n in a:
+        assert _rel(b[n], a[n]) < 1e-12, n
+
+
+def test_centring_bounds_the_factors():
+    """With c = (max G + min G)/2 every centred factor is at most exp(range/2)."""
+    rng = np.random.default_rng(61)
+    g = -np.logaddexp(0, -(rng.standard_normal((64, 16)) + 3.0))
+    G = np.cumsum(g, axis=0)
+    c = 0.5 * (G.max(0) + G.min(0))
+    half = 0.5 * (G.max(0) - G.min(0))
+    assert np.all(np.abs(G - c) <= half + 1e-15)
+
+
+def test_local_wy_flops_match_the_pages():
+    gold = json.load(open(os.path.join(GOLDEN, "local_wy_flops.json")))
+    n, dk, dv = gold["n"], gold["dk"], gold["dv"]
+    f7, c7 = cf.local_wy_flops(n, dk, dv, "wy7")
+    f3, c3 = cf.local_wy_flops(n, dk, dv, "rewy")
+    assert (c7, c3) == (gold["wy7_products"], gold["rewy_products"])
+    assert round(f7 / 1e6, 2) == gold["wy7_millions"]
+    assert round(f3 / 1e6, 2) == gold["rewy_millions"]
+    assert round(100 * (f7 - f3) / f7, 1) == gold["removed_percent"]
+
+
+@pytest.mark.parametrize("n,dk,dv", [(64, 128, 128), (16, 8, 4), (32, 64, 96), (8, 3, 7)])
+def test_removed_flops_identity(n, dk, dv):
+    """dF = 4 n^2 d_k + 4 n^3, independent of d_v (onedev.kr summary)."""
+    f7, _ = cf.local_wy_flops(n, dk, dv, "wy7")
+    f3, _ = cf.local_wy_flops(n, dk, dv, "rewy")
+    assert f7 - f3 == 4 * n * n * dk + 4 * n ** 3
