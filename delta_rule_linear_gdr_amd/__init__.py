@@ -1,0 +1,218 @@
+"""MI355X (gfx950) chunkwise gated delta-rule attention with the ReWY backward.
+
+Thin Python binding over ``libgdr.so`` (C ABI in include/gdr.h): the
+functions below only marshal torch device tensors into pointers and sizes and
+pick up torch's current HIP stream. Every step of the computation runs in the
+library's HIP kernels; there is no CPU or PyTorch fallback, and a missing or
+unbuilt library raises.
+
+    o, ht, saved = gdr_fwd(q, k, v, g, beta, h0, policy="recompute")
+    grads = gdr_bwd(q, k, v, g, beta, h0, dO, dht, saved=saved, policy="recompute")
+    grads = gdr_bwd_wy7(...)          # seven-product producer (ablation)
+
+Shapes: q, k, v, dO [B,T,H,128]; g [B,T,H] (GDN, scalar gate) or
+[B,T,H,128] (KDA, per-channel gate), fp32; beta [B,T,H]; h0, dht
+[B,H,128,128] fp32 (key-major) or None. q, k, v, beta, dO share one dtype,
+bfloat16 or float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "workspace_size", "library_path", "load",
+           "GdrError", "RECOMPUTE", "FULL_SAVE"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdr.so")
+_lib = None
+
+RECOMPUTE, FULL_SAVE = 0, 1
+GATE_SCALAR, GATE_VECTOR = 0, 1
+DT_BF16, DT_F32 = 0, 1
+STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
+          -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
+EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_status_string",
+           "gdr_last_error", "gdr_version")
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("DK", ctypes.c_int64), ("DV", ctypes.c_int64), ("C", ctypes.c_int64),
+                ("gate", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libgdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dp = ctypes.POINTER(Desc)
+    lib.gdr_workspace_size.argtypes = [dp, i32, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.gdr_workspace_size.restype = i32
+    lib.gdr_fwd.argtypes = [dp, i32] + [p] * 10 + [sz, p]
+    lib.gdr_fwd.restype = i32
+    for name in ("gdr_bwd", "gdr_bwd_wy7"):
+        fn = getattr(lib, name)
+        fn.argtypes = [dp, i32] + [p] * 16 + [sz, p]
+        fn.restype = i32
+    lib.gdr_status_string.argtypes = [i32]
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_version.argtypes = []
+    lib.gdr_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise GdrError(rc, load().gdr_last_error().decode())
+
+
+def _policy(policy) -> int:
+    if policy in (RECOMPUTE, "recompute", "R"):
+        return RECOMPUTE
+    if policy in (FULL_SAVE, "full_save", "A"):
+        return FULL_SAVE
+    raise ValueError(f"unknown policy {policy!r}")
+
+
+def make_desc(B, T, H, gate, dtype, DK=128, DV=128, C=64) -> Desc:
+    return Desc(B, T, H, DK, DV, C, gate, dtype)
+
+
+def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute"):
+    """(saved_bytes, scratch_bytes) for a problem."""
+    d = make_desc(B, T, H, GATE_VECTOR if gate == "vector" else GATE_SCALAR,
+                  DT_F32 if dtype == "fp32" else DT_BF16)
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().gdr_workspace_size(ctypes.byref(d), _policy(policy), ctypes.byref(sv),
+                                     ctypes.byref(sc)))
+    return sv.value, sc.value
+
+
+# ---------------------------------------------------------------- torch side
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _desc_from(q, g):
+    torch = _torch()
+    B, T, H, DK = q.shape
+    gate = GATE_VECTOR if g.dim() == 4 else GATE_SCALAR
+    if q.dtype == torch.bfloat16:
+        dt = DT_BF16
+    elif q.dtype == torch.float32:
+        dt = DT_F32
+    else:
+        raise TypeError(f"q dtype {q.dtype}: expected bfloat16 or float32")
+    return make_desc(B, T, H, gate, dt, DK=DK)
+
+
+def _validate(q, k, v, g, beta, extra=()):
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), *extra):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in (("k", k), ("v", v), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    if g.dtype != torch.float32:
+        raise TypeError("g must be float32")
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _scratch(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch=None):
+    """Forward. Returns (o, ht or None, saved or None)."""
+    torch = _torch()
+    _validate(q, k, v, g, beta, (("h0", h0),))
+    d = _desc_from(q, g)
+    pol = _policy(policy)
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    lib = load()
+    _check(lib.gdr_workspace_size(ctypes.byref(d), pol, ctypes.byref(sv), ctypes.byref(sc)))
+    B, T, H, _ = q.shape
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, 128, 128), dtype=torch.float32, device=q.device) if want_ht else None
+    saved = torch.empty(sv.value, dtype=torch.uint8, device=q.device) if sv.value else None
+    if scratch is None:
+        scratch = _scratch(sc.value, q.device)
+    _check(lib.gdr_fwd(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                       _ptr(h0), _ptr(o), _ptr(ht), _ptr(saved), _ptr(scratch),
+                       scratch.numel(), _stream()))
+    return o, ht, saved
+
+
+def _bwd(fn, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, out):
+    torch = _torch()
+    _validate(q, k, v, g, beta, (("h0", h0), ("dO", dO), ("dht", dht)))
+    if dO.dtype != q.dtype:
+        raise TypeError("dO dtype differs from q dtype")
+    d = _desc_from(q, g)
+    pol = _policy(policy)
+    lib = load()
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.gdr_workspace_size(ctypes.byref(d), pol, ctypes.byref(sv), ctypes.byref(sc)))
+    B, T, H, _ = q.shape
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                   dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                   dh0=torch.empty((B, H, 128, 128), dtype=torch.float32, device=q.device)
+                   if want_dh0 else None)
+    if scratch is None:
+        scratch = _scratch(sc.value, q.device)
+    _check(fn(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
+              _ptr(dO), _ptr(dht), _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]),
+              _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")),
+              _ptr(scratch), scratch.numel(), _stream()))
+    return out
+
+
+def gdr_bwd(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
+            want_dh0=True, scratch=None, out=None):
+    """Backward (ReWY producer). Returns dict dq, dk, dv, dg, dbeta, dh0."""
+    return _bwd(load().gdr_bwd, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
+                scratch, out)
+
+
+def gdr_bwd_wy7(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
+                want_dh0=True, scratch=None, out=None):
+    """Backward with the expanded seven-product WY producer (ablation)."""
+    return _bwd(load().gdr_bwd_wy7, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
+                scratch, out)

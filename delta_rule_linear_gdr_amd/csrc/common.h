@@ -1,0 +1,146 @@
+// Device helpers shared by the gfx950 kernels of the chunkwise gated delta rule.
+//
+// Matrix products use v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulation). Operand fragments follow the instruction's lane layout:
+//   A (16 x 32, M x K):  lane l holds row (l & 15), k = 8*(l >> 4) .. +7
+//   B (32 x 16, K x N):  lane l holds col (l & 15), k = 8*(l >> 4) .. +7
+//   C (16 x 16):         lane l holds col (l & 15), rows 4*(l >> 4) .. +3
+// Both operands are therefore read from "K-contiguous" storage: A as [M][K]
+// and B transposed as Bt[N][K], one 16-byte read per lane per fragment.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace gdr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS row strides (elements): 16 bytes of padding per row spreads the rows of
+// one fragment read over distinct banks.
+constexpr int LD128 = DKD + 8;  // rows of 128 bf16
+constexpr int LD64 = CH + 8;    // rows of 64 bf16
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Storage element types of the operator's inputs/outputs.
+template <typename T> struct io;
+template <> struct io<bf16> {
+    __device__ static float ld(const bf16* p) { return (float)*p; }
+    __device__ static void st(bf16* p, float x) { *p = (bf16)x; }
+};
+template <> struct io<float> {
+    __device__ static float ld(const float* p) { return *p; }
+    __device__ static void st(float* p, float x) { *p = x; }
+};
+
+// Load 8 consecutive elements of an input row as floats.
+__device__ __forceinline__ void load8(const bf16* p, float (&x)[8])
+{
+    bf16x8 v = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8])
+{
+    float4 a = *(const float4*)p;
+    float4 b = *(const float4*)(p + 4);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&x)[8])
+{
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+    *(bf16x8*)p = v;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8])
+{
+    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+    *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8])
+{
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+    return v;
+}
+
+// Fragment reads (LDS or global), K-contiguous storage with row stride ld.
+__device__ __forceinline__ bf16x8 frag(const bf16* base, int ld, int row0, int k0)
+{
+    const int l = lane_id();
+    return *(const bf16x8*)(base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4));
+}
+
+// acc[mt][nt] += A[m0+16mt.., k] * Bt[n0+16nt.., k] for k in [0, K).
+template <int MT, int NT, int K>
+__device__ __forceinline__ void wave_gemm(const bf16* A, int lda, int m0, const bf16* Bt, int ldb,
+                                          int n0, f32x4 (&acc)[MT][NT])
+{
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+        bf16x8 a[MT], b[NT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) a[mt] = frag(A, lda, m0 + 16 * mt, k);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) b[nt] = frag(Bt, ldb, n0 + 16 * nt, k);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = mfma(a[mt], b[nt], acc[mt][nt]);
+    }
+}
+
+// Row/column of element r of a C fragment whose tile origin is (m0, n0).
+__device__ __forceinline__ int crow(int m0, int r) { return m0 + 4 * (lane_id() >> 4) + r; }
+__device__ __forceinline__ int ccol(int n0) { return n0 + (lane_id() & 15); }
+
+// Write a C fragment into a row-major bf16 buffer: buf[row][col].
+__device__ __forceinline__ void put_c(bf16* buf, int ld, int m0, int n0, const f32x4& c,
+                                      float scale = 1.f)
+{
+    const int col = ccol(n0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) buf[crow(m0, r) * ld + col] = (bf16)(c[r] * scale);
+}
+// Write a C fragment transposed: buf[col][row .. row+3] (one 8-byte write).
+__device__ __forceinline__ void put_c_t(bf16* buf, int ld, int m0, int n0, const f32x4& c,
+                                        float scale = 1.f)
+{
+    bf16x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = (bf16)(c[r] * scale);
+    *(bf16x4*)(buf + ccol(n0) * ld + crow(m0, 0)) = v;
+}
+
+// Sum over the 16 lanes that share (lane >> 4), i.e. over the columns of a C
+// fragment row group.
+__device__ __forceinline__ float sum16(float x)
+{
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    x += __shfl_xor(x, 8);
+    return x;
+}
+
+}  // namespace gdr

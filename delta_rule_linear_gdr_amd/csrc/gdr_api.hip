@@ -1,0 +1,317 @@
+// C ABI of the chunkwise gated delta rule (see include/gdr.h): argument
+// validation, workspace carving and launch sequencing. No allocation, no
+// synchronization; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "gdr.h"
+#include "kernels.h"
+
+namespace gdr {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
+
+// Per-tile byte sizes of the chunk intermediates.
+constexpr size_t B_W = CH * DKD * 2, B_U = CH * DVD * 2, B_KT = CH * DKD * 2, B_QG = CH * DKD * 2;
+constexpr size_t B_A = CH * CH * 2, B_HM = CH * CH * 2, B_GN = DKD * 4;
+constexpr size_t B_H = DKD * DVD * 2, B_R = CH * DVD * 2, B_DH = DKD * DVD * 2, B_RB = CH * DVD * 2;
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    size_t ntiles;
+    Carver(void* b, size_t n) : base((char*)b), ntiles(n) {}
+    template <typename X>
+    X* take(size_t per_tile)
+    {
+        off = align_up(off);
+        X* r = base ? (X*)(base + off) : nullptr;
+        off += per_tile * ntiles;
+        return r;
+    }
+};
+
+// Chunk quantities shared by the forward (full save) and the backward.
+void carve_saved(Carver& c, Inter& it)
+{
+    it.A = c.take<bf16>(B_A);
+    it.W = c.take<bf16>(B_W);
+    it.Hm = c.take<bf16>(B_HM);
+    it.Kt = c.take<bf16>(B_KT);
+    it.Qg = c.take<bf16>(B_QG);
+    it.gn = c.take<float>(B_GN);
+    it.h = c.take<bf16>(B_H);
+    it.R = c.take<bf16>(B_R);
+}
+
+enum Phase { FWD, BWD };
+
+// Lays out saved/scratch for one call; with null bases it only measures.
+void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Inter& it,
+            size_t& saved_bytes, size_t& scratch_bytes)
+{
+    memset(&it, 0, sizeof it);
+    Carver sv(saved, ntiles), sc(scratch, ntiles);
+    if (policy == GDR_FULL_SAVE) {
+        carve_saved(sv, it);
+        if (ph == FWD) {
+            it.U = sc.take<bf16>(B_U);
+        } else {
+            it.dh = sc.take<bf16>(B_DH);
+            it.Rb = sc.take<bf16>(B_RB);
+        }
+    } else {
+        carve_saved(sc, it);
+        it.U = sc.take<bf16>(B_U);
+        if (ph == FWD) {
+            // the forward alone keeps no per-chunk state, A or correction
+            it.A = it.h = it.R = nullptr;
+        } else {
+            it.dh = sc.take<bf16>(B_DH);
+            it.Rb = sc.take<bf16>(B_RB);
+        }
+    }
+    saved_bytes = policy == GDR_FULL_SAVE ? align_up(sv.off) : 0;
+    scratch_bytes = align_up(sc.off);
+}
+
+__global__ void copy_or_zero(float* dst, const float* src, int64_t n)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t fill_state(float* dst, const float* src, int64_t n, hipStream_t st)
+{
+    if (!dst || n == 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    copy_or_zero<<<(unsigned)blocks, 256, 0, st>>>(dst, src, n);
+    return hipGetLastError();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int check_desc(const gdr_desc* d)
+{
+    if (!d) return fail(GDR_ERR_INVALID, "descriptor is NULL");
+    if (d->B < 0 || d->T < 0 || d->H < 0)
+        return fail(GDR_ERR_INVALID, "negative size (B=%lld T=%lld H=%lld)", (long long)d->B,
+                    (long long)d->T, (long long)d->H);
+    if (d->gate != GDR_GATE_SCALAR && d->gate != GDR_GATE_VECTOR)
+        return fail(GDR_ERR_INVALID, "unknown gate kind %d", d->gate);
+    if (d->dtype != GDR_BF16 && d->dtype != GDR_F32)
+        return fail(GDR_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->DK != DKD || d->DV != DVD)
+        return fail(GDR_ERR_UNSUPPORTED, "key/value width %lld/%lld: only 128/128 is supported",
+                    (long long)d->DK, (long long)d->DV);
+    if (d->C != CH)
+        return fail(GDR_ERR_UNSUPPORTED, "chunk length %lld: only 64 is supported", (long long)d->C);
+    if (d->T % CH != 0)
+        return fail(GDR_ERR_UNSUPPORTED, "T=%lld is not a multiple of 64", (long long)d->T);
+    if (d->B * d->H > 65535)
+        return fail(GDR_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(d->B * d->H));
+    if (d->T / CH > (int64_t)1 << 30)
+        return fail(GDR_ERR_UNSUPPORTED, "T=%lld too long", (long long)d->T);
+    return GDR_OK;
+}
+
+int check_policy(int policy)
+{
+    if (policy != GDR_RECOMPUTE && policy != GDR_FULL_SAVE)
+        return fail(GDR_ERR_INVALID, "unknown policy %d", policy);
+    return GDR_OK;
+}
+
+// Row tensors are read with 16-byte vector accesses; the rest element-wise.
+#define REQUIRE_PTR_A(p, a)                                                            \
+    do {                                                                               \
+        if (!(p)) return fail(GDR_ERR_INVALID, "required pointer '%s' is NULL", #p);   \
+        if ((uintptr_t)(p) % (a))                                                      \
+            return fail(GDR_ERR_INVALID, "pointer '%s' is not %d-byte aligned", #p, (int)(a)); \
+    } while (0)
+#define REQUIRE_PTR(p) REQUIRE_PTR_A(p, 16)
+#define CHECK_ALIGN(p, a)                                                              \
+    do {                                                                               \
+        if ((p) && (uintptr_t)(p) % (a))                                               \
+            return fail(GDR_ERR_INVALID, "pointer '%s' is not %d-byte aligned", #p, (int)(a)); \
+    } while (0)
+
+Shape make_shape(const gdr_desc* d)
+{
+    Shape s;
+    s.B = d->B;
+    s.T = d->T;
+    s.H = d->H;
+    s.NT = d->T / CH;
+    s.vec = d->gate == GDR_GATE_VECTOR;
+    s.f32 = d->dtype == GDR_F32;
+    return s;
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
+            const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+            void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nstate = d->B * d->H * DKD * DVD;
+    if (d->B * d->H == 0) return GDR_OK;
+    if (d->T == 0) {
+        hipError_t e = fill_state(dh0, dht, nstate, st);
+        return e == hipSuccess ? GDR_OK : hip_fail(e, "dh0 copy");
+    }
+    const int esz = d->dtype == GDR_F32 ? 4 : 2;
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(dO);
+    REQUIRE_PTR(dq); REQUIRE_PTR(dk); REQUIRE_PTR(dv);
+    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(dg, 4); REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
+    CHECK_ALIGN(h0, 4); CHECK_ALIGN(dht, 4); CHECK_ALIGN(dh0, 4);
+    if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    Inter it;
+    size_t sb = 0, need = 0;
+    layout(policy, BWD, nullptr, nullptr, ntiles, it, sb, need);
+    if (!scratch || scratch_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
+                    scratch ? scratch_bytes : (size_t)0);
+    if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
+    layout(policy, BWD, (void*)saved, scratch, ntiles, it, sb, need);
+
+    const Shape s = make_shape(d);
+    Inputs in{q, k, v, beta, dO, g, h0, dht};
+    Grads gr{dq, dk, dv, dbeta, dg, dh0};
+    hipError_t e;
+    if (policy == GDR_RECOMPUTE) {
+        if ((e = launch_prep(s, in, it, true, st)) != hipSuccess) return hip_fail(e, "prep");
+        if ((e = launch_scan_fwd(s, in, it, nullptr, nullptr, st)) != hipSuccess)
+            return hip_fail(e, "scan_fwd");
+    }
+    if ((e = launch_scan_bwd(s, in, it, dh0, st)) != hipSuccess) return hip_fail(e, "scan_bwd");
+    if ((e = launch_bwd_local(s, in, it, gr, wy7, st)) != hipSuccess)
+        return hip_fail(e, "bwd_local");
+    return GDR_OK;
+}
+
+}  // namespace
+}  // namespace gdr
+
+using namespace gdr;
+
+extern "C" {
+
+int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_t* scratch_bytes)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    Inter it;
+    size_t s1 = 0, c1 = 0, s2 = 0, c2 = 0;
+    layout(policy, FWD, nullptr, nullptr, ntiles, it, s1, c1);
+    layout(policy, BWD, nullptr, nullptr, ntiles, it, s2, c2);
+    if (saved_bytes) *saved_bytes = s1;
+    if (scratch_bytes) *scratch_bytes = c1 > c2 ? c1 : c2;
+    return GDR_OK;
+}
+
+int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
+            void* scratch, size_t scratch_bytes, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    if (d->B * d->H == 0) return GDR_OK;
+    if (d->T == 0) {
+        hipError_t e = fill_state(ht, h0, d->B * d->H * DKD * DVD, st);
+        return e == hipSuccess ? GDR_OK : hip_fail(e, "ht copy");
+    }
+    const int esz = d->dtype == GDR_F32 ? 4 : 2;
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
+    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(beta, esz);
+    CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
+    if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    Inter it;
+    size_t sb = 0, need = 0;
+    layout(policy, FWD, nullptr, nullptr, ntiles, it, sb, need);
+    if (!scratch || scratch_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
+                    scratch ? scratch_bytes : (size_t)0);
+    if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
+    layout(policy, FWD, saved, scratch, ntiles, it, sb, need);
+    const Shape s = make_shape(d);
+    Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
+    hipError_t e;
+    if ((e = launch_prep(s, in, it, policy == GDR_FULL_SAVE, st)) != hipSuccess)
+        return hip_fail(e, "prep");
+    if ((e = launch_scan_fwd(s, in, it, o, ht, st)) != hipSuccess) return hip_fail(e, "scan_fwd");
+    return GDR_OK;
+}
+
+int gdr_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
+            const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+            void* scratch, size_t scratch_bytes, void* stream)
+{
+    return run_bwd(d, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
+                   scratch, scratch_bytes, stream, false);
+}
+
+int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                const float* g, const void* beta, const float* h0, const void* dO,
+                const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
+                void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream)
+{
+    return run_bwd(d, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
+                   scratch, scratch_bytes, stream, true);
+}
+
+const char* gdr_status_string(int status)
+{
+    switch (status) {
+    case GDR_OK: return "ok";
+    case GDR_ERR_INVALID: return "invalid argument";
+    case GDR_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GDR_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDR_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+    }
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+int gdr_version(void) { return 1; }
+
+}  // extern "C"

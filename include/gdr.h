@@ -1,0 +1,117 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) chunkwise gated delta-rule operator:
+ * forward and backward of Gated DeltaNet (scalar gate) and Kimi Delta
+ * Attention (per-key-channel gate), chunk size 64, key and value width 128.
+ *
+ * Operation (ReWY paper, Sec. 2.2 and Table 1). Per batch b and head h, with
+ * a key-major state S (128 x 128), for t = 1..T:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                      (the output includes the write)
+ * with S_0 = h0 and ht = S_T. The gate g is the log decay: one value per
+ * token and head (scalar gate) or one per key channel (vector gate). beta is
+ * the write weight after its activation; q already carries the query scale.
+ * The backward returns the exact gradients of <o, dO> + <ht, dht> with
+ * respect to q, k, v, g, beta and h0 (Sec. 3.1: the ReWY backward changes
+ * the derivative graph, not the gradients). dg has g's shape; for a scalar
+ * gate it is the sum over key channels (App. E.1).
+ *
+ * Computation: chunkwise (Sec. 2.1, 2.3) -- per chunk the unit-triangular
+ * system M R = Z - E S, A = M^{-1}, W = A E, U = A Z; a state scan across
+ * chunks; and a backward whose local producer is the three-product ReWY
+ * pullback P = A^T Rbar, P R^T, P S^T (Sec. 3.1-3.2), followed by Gram
+ * elimination (scalar gate, Sec. 3.4) or centred matrix intra (vector gate,
+ * Sec. 3.3). Dense products run on bf16 MFMA with fp32 accumulation; the
+ * triangular inverse, the state and all gate arithmetic are fp32.
+ *
+ * Layouts (row-major, contiguous, device memory):
+ *   q, k, dq, dk        [B, T, H, 128]      dtype
+ *   v, o, dO, dv        [B, T, H, 128]      dtype
+ *   beta, dbeta         [B, T, H]           dtype
+ *   g, dg               [B, T, H] (scalar gate) or [B, T, H, 128] (vector), fp32
+ *   h0, ht, dht, dh0    [B, H, 128(key), 128(value)], fp32
+ * dtype is GDR_BF16 or GDR_F32 (storage type of the listed tensors; the
+ * arithmetic is the same for both).
+ *
+ * Ownership: every pointer is caller-owned device memory; the library never
+ * allocates or frees per call and keeps no state between calls. `saved` and
+ * `scratch` are caller-provided workspaces sized by gdr_workspace_size.
+ * `saved` must stay untouched between gdr_fwd and the gdr_bwd that uses it.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream);
+ * the library never synchronizes. Concurrent calls must not share `scratch`.
+ *
+ * Errors: arguments are validated before anything is launched; on error
+ * nothing is launched and the call returns a negative status. Unsupported
+ * shapes (key/value width other than 128, chunk other than 64, T not a
+ * multiple of 64) return GDR_ERR_UNSUPPORTED -- there is no fallback. A
+ * launch failure returns GDR_ERR_HIP. gdr_last_error() returns a message for
+ * the calling thread's last failure.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDR_OK = 0,
+    GDR_ERR_INVALID = -1,     /* null pointer, negative size, bad enum */
+    GDR_ERR_UNSUPPORTED = -2, /* valid but not implemented (see above) */
+    GDR_ERR_WORKSPACE = -3,   /* saved/scratch missing or too small */
+    GDR_ERR_HIP = -4          /* a HIP launch failed */
+} gdr_status;
+
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_VECTOR = 1 } gdr_gate;
+typedef enum { GDR_RECOMPUTE = 0, GDR_FULL_SAVE = 1 } gdr_policy;
+typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
+
+typedef struct {
+    int64_t B, T, H;  /* batch, sequence length, heads */
+    int64_t DK, DV;   /* key and value width: must be 128 */
+    int64_t C;        /* chunk length: must be 64 */
+    int32_t gate;     /* gdr_gate */
+    int32_t dtype;    /* gdr_dtype */
+} gdr_desc;
+
+/* Workspace sizes in bytes for a descriptor and policy.
+ * saved_bytes: what gdr_fwd under GDR_FULL_SAVE writes for gdr_bwd
+ *              (0 under GDR_RECOMPUTE).
+ * scratch_bytes: transient memory that gdr_fwd / gdr_bwd / gdr_bwd_wy7 need
+ *              (the maximum over the three). Any pointer may be NULL. */
+int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_t* scratch_bytes);
+
+/* Forward. o: output; ht: final state (NULL: not written); h0 NULL: zero.
+ * Under GDR_FULL_SAVE, saved receives the chunk quantities the backward
+ * reuses ({A, W, Hm, Kt, Qg, gn, h, R} per chunk); under GDR_RECOMPUTE saved
+ * may be NULL. */
+int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
+            void* scratch, size_t scratch_bytes, void* stream);
+
+/* Backward. Under GDR_RECOMPUTE the forward chunk quantities are recomputed
+ * into scratch (saved may be NULL); under GDR_FULL_SAVE they are read from
+ * saved. dht NULL: zero; dh0 NULL: not written. */
+int gdr_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
+            const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+            void* scratch, size_t scratch_bytes, void* stream);
+
+/* Same contract and results as gdr_bwd, with the expanded seven-product WY
+ * producer (Sec. 2.3) in place of ReWY. Ablation only. */
+int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                const float* g, const void* beta, const float* h0, const void* dO,
+                const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
+                void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
+
+const char* gdr_status_string(int status);
+const char* gdr_last_error(void);
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,116 @@
+"""Shared helpers of the GPU parity tests: move seeded inputs to the device,
+run the library through its Python binding, run the CPU oracle on the same
+values, and apply the acceptance rule.
+
+Acceptance (ReWY paper, Sec. 4.5 "Numerical validation": 0.8% relative for
+ordinary outputs and gradients, 2% for gate and beta gradients, a maximum
+absolute threshold for near-zero references, all values finite), read per
+tensor: if max|ref| <= 1e-6 the maximum absolute error must be <= 1e-6,
+otherwise ||x - ref||_2 / ||ref||_2 must be within the tolerance.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+TOL = {"o": 0.008, "ht": 0.008, "dq": 0.008, "dk": 0.008, "dv": 0.008, "dh0": 0.008,
+       "dg": 0.02, "dbeta": 0.02}
+NEAR_ZERO = 1e-6
+
+
+def check(name, got, ref, tol=None):
+    tol = TOL[name] if tol is None else tol
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if np.max(np.abs(ref), initial=0.0) <= NEAR_ZERO:
+        err = np.max(np.abs(got - ref), initial=0.0)
+        assert err <= NEAR_ZERO, f"{name}: near-zero reference, max abs err {err:.3e}"
+        return err
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert rel <= tol, f"{name}: rel L2 {rel:.5f} > {tol}"
+    return rel
+
+
+def to_dev(x, dtype):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=dtype)
+
+
+def torch_dtype(name):
+    import torch
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def device_inputs(x):
+    import torch
+    dt = torch_dtype(x["dtype"])
+    d = {n: to_dev(x[n], dt) for n in ("q", "k", "v", "beta", "dO")}
+    d["g"] = to_dev(x["g"], torch.float32)
+    d["h0"] = to_dev(x["h0"], torch.float32)
+    d["dht"] = to_dev(x["dht"], torch.float32)
+    return d
+
+
+def run_gpu(x, policy="recompute", wy7=False, use_h0=True, use_dht=True):
+    """Forward + backward on the device; returns numpy float64 results."""
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    d = device_inputs(x)
+    h0 = d["h0"] if use_h0 else None
+    dht = d["dht"] if use_dht else None
+    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, policy=policy)
+    fn = gdr.gdr_bwd_wy7 if wy7 else gdr.gdr_bwd
+    gr = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, d["dO"], dht, saved=saved,
+            policy=policy)
+    torch.cuda.synchronize()
+    out = {"o": o, "ht": ht, **gr}
+    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()}
+
+
+def oracle_heads(x, heads=None, threads=None):
+    """Oracle forward + backward restricted to (b, h) pairs (all if None).
+    Returns per-tensor arrays stacked along a leading 'pair' axis."""
+    B, T, H, _ = x["q"].shape
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    res = {n: [] for n in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0")}
+    for b, h in pairs:
+        sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
+        st = lambda a: a[b:b + 1, h:h + 1]     # noqa: E731
+        o, ht = oracle.token_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]),
+                                 sl(x["beta"]), st(x["h0"]), threads=threads)
+        gr = oracle.token_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                              st(x["h0"]), sl(x["dO"]), st(x["dht"]), threads=threads)
+        res["o"].append(o)
+        res["ht"].append(ht)
+        for n in ("dq", "dk", "dv", "dg", "dbeta", "dh0"):
+            res[n].append(gr[n])
+    return pairs, res
+
+
+def select_heads(gpu, pairs):
+    """Restrict full GPU results to the oracle's (b, h) pairs, same stacking."""
+    out = {}
+    for n, a in gpu.items():
+        if a is None:
+            continue
+        if n in ("ht", "dh0"):
+            out[n] = [a[b:b + 1, h:h + 1] for b, h in pairs]
+        else:
+            out[n] = [a[b:b + 1, :, h:h + 1] for b, h in pairs]
+    return out
+
+
+def compare(gpu, x, heads=None, names=None, report=None):
+    pairs, ref = oracle_heads(x, heads)
+    got = select_heads(gpu, pairs)
+    errs = {}
+    for n in names or ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        if n not in got:
+            continue
+        errs[n] = check(n, np.concatenate(got[n]), np.concatenate(ref[n]))
+    if report is not None:
+        report.update(errs)
+    return errs

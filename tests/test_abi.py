@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every function include/gdr.h declares, and
+rejects invalid or unsupported calls before touching the device. No compute
+calls are made here (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import delta_rule_linear_gdr_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function():
+    lib = gdr.load()
+    names = _declared()
+    assert set(names) == set(gdr.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _desc(**kw):
+    base = dict(B=1, T=128, H=2, gate=0, dtype=0)
+    base.update(kw)
+    return gdr.make_desc(base["B"], base["T"], base["H"], base["gate"], base["dtype"],
+                         DK=base.get("DK", 128), DV=base.get("DV", 128), C=base.get("C", 64))
+
+
+def _ws(d, policy=0):
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = gdr.load().gdr_workspace_size(ctypes.byref(d) if d is not None else None, policy,
+                                       ctypes.byref(sv), ctypes.byref(sc))
+    return rc, sv.value, sc.value
+
+
+def test_workspace_sizes():
+    rc, sv, sc = _ws(_desc(T=8192, H=16), 0)
+    assert rc == 0 and sv == 0
+    # recompute scratch holds every per-chunk intermediate of the backward:
+    # W,U,Kt,Qg,R,Rb 16 KiB, A,Hm 8 KiB, gn 512 B, h,dh 32 KiB per (chunk, head)
+    assert sc == 2048 * (6 * 16384 + 2 * 8192 + 512 + 2 * 32768)
+    rc, sv, sc = _ws(_desc(T=8192, H=16), 1)
+    assert rc == 0
+    assert sv == 2048 * (8192 + 16384 + 8192 + 16384 + 16384 + 512 + 32768 + 16384)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(DK=64), -2), (dict(DV=96), -2), (dict(C=32), -2), (dict(T=100), -2),
+    (dict(gate=5), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
+])
+def test_descriptor_validation(kw, status):
+    rc, _, _ = _ws(_desc(**kw))
+    assert rc == status
+    assert gdr.load().gdr_last_error()
+
+
+def test_null_descriptor_and_bad_policy():
+    assert _ws(None)[0] == -1
+    assert _ws(_desc(), policy=3)[0] == -1
+
+
+def _fwd(d, **ptrs):
+    lib = gdr.load()
+    P = {n: ptrs.get(n) for n in ("q", "k", "v", "g", "beta", "h0", "o", "ht", "saved", "scratch")}
+    return lib.gdr_fwd(ctypes.byref(d), ptrs.get("policy", 0), P["q"], P["k"], P["v"], P["g"],
+                       P["beta"], P["h0"], P["o"], P["ht"], P["saved"], P["scratch"],
+                       ptrs.get("scratch_bytes", 0), None)
+
+
+def test_forward_rejects_null_and_small_workspace_without_launching():
+    d = _desc()
+    assert _fwd(d) == -1
+    assert b"NULL" in gdr.load().gdr_last_error()
+    fake = 1 << 20  # never dereferenced: validation fails first
+    assert _fwd(d, q=fake, k=fake, v=fake, g=fake, beta=fake, o=fake, scratch=fake,
+                scratch_bytes=16) == -3
+    assert _fwd(d, q=fake + 8, k=fake, v=fake, g=fake, beta=fake, o=fake, scratch=fake,
+                scratch_bytes=1 << 40) == -1
+    assert _fwd(d, policy=1, q=fake, k=fake, v=fake, g=fake, beta=fake, o=fake, scratch=fake,
+                scratch_bytes=1 << 40) == -1  # full save needs `saved`
+
+
+def test_empty_problems_are_no_ops():
+    assert _fwd(_desc(B=0)) == 0
+    assert _fwd(_desc(H=0)) == 0
+    assert _fwd(_desc(T=0)) == 0  # ht NULL: nothing to write
+
+
+def test_status_strings():
+    lib = gdr.load()
+    for st in (0, -1, -2, -3, -4, 99):
+        assert lib.gdr_status_string(st)

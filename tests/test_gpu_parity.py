@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 token oracle on
+identical seeded inputs, at the five workloads and on the edge cases."""
+import numpy as np
+import pytest
+
+from delta_rule_linear_gdr_amd.inputs import WORKLOADS, make_inputs
+from tests import gdr_testlib as tl
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _report(tag, errs):
+    print(f"[parity] {tag}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_gdn_512x4_fp32(policy):
+    _need_gpu()
+    x = WORKLOADS["gdn_1x512x4_fp32"].make()
+    gpu = tl.run_gpu(x, policy)
+    _report(f"gdn_1x512x4_fp32/{policy}", tl.compare(gpu, x))
+
+
+def test_gdn_2048x16_full_save():
+    _need_gpu()
+    x = WORKLOADS["gdn_1x2048x16"].make()
+    gpu = tl.run_gpu(x, "full_save")
+    _report("gdn_1x2048x16/full_save", tl.compare(gpu, x))
+
+
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_gdn_8192x16_sampled_heads(policy):
+    _need_gpu()
+    x = WORKLOADS["gdn_1x8192x16"].make()
+    gpu = tl.run_gpu(x, policy)
+    _report(f"gdn_1x8192x16/{policy}", tl.compare(gpu, x, heads=[(0, 0), (0, 7), (0, 15)]))
+
+
+def test_kda_2x2048x16():
+    _need_gpu()
+    x = WORKLOADS["kda_2x2048x16"].make()
+    gpu = tl.run_gpu(x, "recompute")
+    _report("kda_2x2048x16/recompute",
+            tl.compare(gpu, x, heads=[(0, 0), (0, 9), (1, 3), (1, 15)]))
+
+
+def test_kda_8192x16_h0_sampled_heads():
+    _need_gpu()
+    x = WORKLOADS["kda_1x8192x16"].make()
+    gpu = tl.run_gpu(x, "recompute")
+    _report("kda_1x8192x16/recompute", tl.compare(gpu, x, heads=[(0, 0), (0, 11)]))
+
+
+# ------------------------------------------------------------------ edges
+
+def _edge(gate, T=256, H=2, B=1, seed=3, **kw):
+    x = make_inputs(B, T, H, gate=gate, dtype="bf16", seed=seed,
+                    gate_mean=4.0 if gate == "scalar" else 3.0, **kw)
+    return x
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_single_chunk(gate):
+    _need_gpu()
+    x = _edge(gate, T=64, H=3)
+    _report(f"single_chunk/{gate}", tl.compare(tl.run_gpu(x), x))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_nonzero_initial_and_terminal_state(gate):
+    _need_gpu()
+    x = _edge(gate, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"h0_dht/{gate}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_zero_and_tiny_beta(gate):
+    _need_gpu()
+    x = _edge(gate, h0_std=0.1, dht_std=0.1)
+    x["beta"] = x["beta"].copy()
+    x["beta"][:, ::3] = 0.0
+    x["beta"][:, 1::7] = 1e-8 if x["dtype"] == "fp32" else np.float64(np.float32(1e-8))
+    from delta_rule_linear_gdr_amd.inputs import round_to
+    x["beta"] = round_to(x["beta"], x["dtype"])
+    _report(f"zero_tiny_beta/{gate}", tl.compare(tl.run_gpu(x), x))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_all_zero_beta(gate):
+    _need_gpu()
+    x = _edge(gate, h0_std=0.1, dht_std=0.1)
+    x["beta"] = np.zeros_like(x["beta"])
+    _report(f"beta0/{gate}", tl.compare(tl.run_gpu(x), x))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_strong_decay(gate):
+    _need_gpu()
+    x = make_inputs(1, 256, 2, gate=gate, dtype="bf16", seed=5, gate_mean=0.0)
+    _report(f"strong_decay/{gate}", tl.compare(tl.run_gpu(x), x))
+
+
+def test_deterministic_and_policy_independent():
+    _need_gpu()
+    x = _edge("vector", T=512, H=4, h0_std=0.1, dht_std=0.1)
+    a = tl.run_gpu(x, "recompute")
+    b = tl.run_gpu(x, "recompute")
+    c = tl.run_gpu(x, "full_save")
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"repeat {n}")
+        np.testing.assert_array_equal(a[n], c[n], err_msg=f"policy {n}")
+
+
+def test_unsupported_length_raises():
+    _need_gpu()
+    import delta_rule_linear_gdr_amd as gdr
+    x = _edge("scalar", T=128)
+    d = tl.device_inputs(x)
+    with pytest.raises(gdr.GdrError) as ei:
+        gdr.gdr_fwd(d["q"][:, :100].contiguous(), d["k"][:, :100].contiguous(),
+                    d["v"][:, :100].contiguous(), d["g"][:, :100].contiguous(),
+                    d["beta"][:, :100].contiguous())
+    assert ei.value.status == -2
