@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise gated delta-rule backward on one MI355X.
+
+Workload: GDN (scalar gate) at (B, T, H) = (1, 8192, 16), chunk 64,
+d_k = d_v = 128, bf16 inputs with fp32 gates and state, seeded synthetic
+inputs (delta_rule_linear_gdr_amd.inputs). One step = one complete low-level
+backward under the recompute policy: gate cumsum and chunk preparation, the
+forward state scan that rebuilds the per-chunk states, the reverse state
+scan, and the chunk-local ReWY backward with Gram elimination. Inputs are
+resident in device memory before the timed region.
+
+Prints one JSON line. Besides the headline value it reports the per-stage
+durations (HIP events recorded by the library on the launch stream over a
+second timed pass), the roofline of the dominant kernel, the forward, the
+full-save policy, the seven-product ablation, the KDA backward at the same
+shape, and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CH = 64
+
+# Algorithmic work per (chunk, head) of each kernel: the bytes it must move
+# (every input read once, every output written once, at their stored types)
+# and its dense matrix-product FLOPs (2 m n k). Tiles: 64 x 128 bf16 = 16 KiB,
+# 64 x 64 bf16 = 8 KiB, 128 x 128 bf16 state = 32 KiB.
+T16, T8, S32 = 16384, 8192, 32768
+
+
+def kernel_work(gate: str, policy: str) -> dict:
+    g_bytes = 64 * 4 if gate == "scalar" else 64 * 128 * 4
+    return {
+        # reads q, k, v, g, beta; writes W, U, Kt, Qg, Hm, gn (+ A)
+        "prep": (3 * T16 + g_bytes + 128 + 4 * T16 + T8 + 512 + T8, 4 * 1048576),
+        # reads W, U, Kt, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
+        "scan_fwd": (3 * T16 + 512 + S32 + T16, 2 * 2097152),
+        # reads Kt, Qg, W, Hm, dO, gn; writes dh, Rb
+        "scan_bwd": (3 * T16 + T8 + T16 + 512 + S32 + T16, 3 * 2097152 + 1048576),
+        # reads q, k, v, dO, g, beta, A, R, Rb, h, dh; writes dq, dk, dv, dg, dbeta
+        "bwd_local": (4 * T16 + g_bytes + 128 + T8 + 2 * T16 + 2 * S32 + 3 * T16 + g_bytes + 128,
+                      3 * 1048576 + 3 * 2097152 + 4 * 1048576),
+        "bwd_local_wy7": (4 * T16 + g_bytes + 128 + T8 + 2 * T16 + 2 * S32 + 3 * T16 + g_bytes
+                          + 128, 3 * 1048576 + 3 * 2097152 + 4 * 1048576 + 3145728),
+    }
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=2,
+                    help="heads of the workload the CPU oracle runs (bounded sample)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    from delta_rule_linear_gdr_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(x):
+        bf = torch.bfloat16
+        d = {n: torch.from_numpy(x[n]).to(dev, bf) for n in ("q", "k", "v", "beta", "dO")}
+        d["g"] = torch.from_numpy(x["g"]).to(dev, torch.float32)
+        d["h0"] = torch.from_numpy(x["h0"]).to(dev, torch.float32)
+        return d
+
+    wl = WORKLOADS["gdn_1x8192x16"]
+    x = wl.make()
+    d = to_dev(x)
+    B, T, H = wl.B, wl.T, wl.H
+    units = B * H * (T // CH)
+
+    def make_runner(dd, fn, policy, saved=None):
+        _, sc = gdr.workspace_size(B, T, H, "vector" if dd["g"].dim() == 4 else "scalar",
+                                   "bf16", policy)
+        scratch = torch.empty(sc, dtype=torch.uint8, device=dev)
+        out = dict(dq=torch.empty_like(dd["q"]), dk=torch.empty_like(dd["k"]),
+                   dv=torch.empty_like(dd["v"]), dg=torch.empty_like(dd["g"]),
+                   dbeta=torch.empty_like(dd["beta"]),
+                   dh0=torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev))
+
+        def run():
+            fn(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"], dd["dO"], None,
+               saved=saved, policy=policy, scratch=scratch, out=out)
+        return run
+
+    def time_steps(run, steps, warmup):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per step
+
+    def profiled(run, steps):
+        gdr.profile_begin(8 * steps + 16)
+        for _ in range(steps):
+            run()
+        st = gdr.profile_end()
+        return {k: v[1] / v[0] for k, v in st.items()}  # avg ms per launch
+
+    # ---- headline: GDN backward, recompute policy ----
+    run = make_runner(d, gdr.gdr_bwd, "recompute")
+    t0 = time.perf_counter()
+    ms = time_steps(run, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    print(f"[bench] gdn bwd-R (1,8192,16): {ms:.4f} ms/step", file=sys.stderr, flush=True)
+    stage_ms = profiled(run, args.steps)
+    print(f"[bench] stages (ms): {stage_ms}", file=sys.stderr, flush=True)
+    work = kernel_work("scalar", "recompute")
+    dom = max(stage_ms, key=stage_ms.get)
+    by, fl = work[dom]
+    t_s = stage_ms[dom] * 1e-3
+    hbm_bound = by / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
+    if hbm_bound:
+        achieved = by * units / t_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = fl * units / t_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
+    roof["kernel"] = dom
+    roof["kernel_ms"] = round(stage_ms[dom], 4)
+    roof["traffic"] = None
+    bwd_flops = sum(work[k][1] for k in ("prep", "scan_fwd", "scan_bwd", "bwd_local")) * units
+    bwd_bytes = sum(work[k][0] for k in ("prep", "scan_fwd", "scan_bwd", "bwd_local")) * units
+    tok_s = B * T / (ms * 1e-3)
+    detail = {
+        "bwd_R_ms": round(ms, 4),
+        "bwd_R_tflops": round(bwd_flops / (ms * 1e-3) / 1e12, 2),
+        "bwd_R_kernel_gbs": round(bwd_bytes / (ms * 1e-3) / 1e9, 1),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "per_stage_roofline": {},
+    }
+    for k, v in stage_ms.items():
+        by, fl = work[k]
+        detail["per_stage_roofline"][k] = {
+            "GB/s": round(by * units / (v * 1e-3) / 1e9, 1),
+            "TFLOP/s": round(fl * units / (v * 1e-3) / 1e12, 2)}
+
+    if not args.no_extra:
+        # forward, recompute policy (output + final state)
+        _, sc = gdr.workspace_size(B, T, H, "scalar", "bf16", "recompute")
+        scr = torch.empty(sc, dtype=torch.uint8, device=dev)
+
+        def fwd():
+            gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], policy="recompute",
+                        scratch=scr)
+        fms = time_steps(fwd, args.steps, args.warmup)
+        detail["fwd_R_ms"] = round(fms, 4)
+        detail["fwd_R_tokens_per_s"] = round(B * T / (fms * 1e-3), 1)
+        del scr
+        # full-save policy: forward saves, backward reuses
+        _, _, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                                  policy="full_save")
+        runA = make_runner(d, gdr.gdr_bwd, "full_save", saved)
+        msA = time_steps(runA, args.steps, args.warmup)
+        detail["bwd_A_ms"] = round(msA, 4)
+        detail["bwd_A_tokens_per_s"] = round(B * T / (msA * 1e-3), 1)
+        # seven-product ablation, both policies
+        run7 = make_runner(d, gdr.gdr_bwd_wy7, "recompute")
+        try:
+            ms7 = time_steps(run7, args.steps, args.warmup)
+            run7A = make_runner(d, gdr.gdr_bwd_wy7, "full_save", saved)
+            ms7A = time_steps(run7A, args.steps, args.warmup)
+            detail["wy7_R_ms"] = round(ms7, 4)
+            detail["wy7_A_ms"] = round(ms7A, 4)
+            detail["rewy_speedup_R"] = round(ms7 / ms, 4)
+            detail["rewy_speedup_A"] = round(ms7A / msA, 4)
+            st7 = profiled(run7, max(4, args.steps // 4))
+            stl = stage_ms.get("bwd_local")
+            if stl and "bwd_local_wy7" in st7:
+                detail["rewy_local_kernel_speedup"] = round(st7["bwd_local_wy7"] / stl, 4)
+        except gdr.GdrError as e:
+            detail["wy7"] = f"unavailable: {e}"
+        del saved
+        # KDA at the same shape, recompute policy, h0 ~ 0.1 N(0,1)
+        xk = WORKLOADS["kda_1x8192x16"].make()
+        dk_ = to_dev(xk)
+        runK = make_runner(dk_, gdr.gdr_bwd, "recompute")
+        msK = time_steps(runK, args.steps, args.warmup)
+        detail["kda_bwd_R_ms"] = round(msK, 4)
+        detail["kda_bwd_R_tokens_per_s"] = round(B * T / (msK * 1e-3), 1)
+        detail["kda_stage_ms"] = {k: round(v, 4) for k, v in profiled(runK, args.steps).items()}
+        del dk_, xk
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        heads = [(0, h) for h in range(args.cpu_heads)]
+        t0 = time.perf_counter()
+        for b, h in heads:
+            sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
+            oracle.token_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                             x["h0"][b:b + 1, h:h + 1], sl(x["dO"]), None, threads=threads)
+        tc = time.perf_counter() - t0
+        frac = len(heads) / H
+        cpu = {"value": round(B * T * frac / tc, 2), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{len(heads)} of {H} heads of GDN (1,8192,16): fp64 token-recurrence "
+                         f"backward incl. its forward recompute, {tc:.1f} s; value scaled to "
+                         f"whole (B,T) tokens"}
+
+    line = {
+        "metric": "GDN/KDA backward tokens/s + TFLOP/s (% roofline) at (1,8192,16), C=64, d=128",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN backward, recompute policy, (B,T,H)=(1,8192,16), C=64, "
+                               "d_k=d_v=128, bf16 q/k/v/beta/dO, fp32 gates and state",
+                   "B": B, "T": T, "H": H, "chunk": CH, "policy": "recompute"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": detail,
+        "wall_s": round(wall, 2),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ import ctypes
 import os
 
 __all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "workspace_size", "library_path", "load",
-           "GdrError", "RECOMPUTE", "FULL_SAVE"]
+           "profile_begin", "profile_end", "GdrError", "RECOMPUTE", "FULL_SAVE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -32,14 +32,19 @@ GATE_SCALAR, GATE_VECTOR = 0, 1
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
-EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_status_string",
-           "gdr_last_error", "gdr_version")
+EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_profile_begin",
+           "gdr_profile_end", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
         self.status = status
+
+
+class StageTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double)]
 
 
 class Desc(ctypes.Structure):
@@ -71,6 +76,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, i32] + [p] * 16 + [sz, p]
         fn.restype = i32
+    lib.gdr_profile_begin.argtypes = [i32]
+    lib.gdr_profile_begin.restype = i32
+    lib.gdr_profile_end.argtypes = [ctypes.POINTER(StageTime), i32, ctypes.POINTER(i32)]
+    lib.gdr_profile_end.restype = i32
     lib.gdr_status_string.argtypes = [i32]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
@@ -106,6 +115,19 @@ def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute"):
     _check(load().gdr_workspace_size(ctypes.byref(d), _policy(policy), ctypes.byref(sv),
                                      ctypes.byref(sc)))
     return sv.value, sc.value
+
+
+def profile_begin(max_launches: int = 4096):
+    """Start per-stage event timing of every launch the library makes."""
+    _check(load().gdr_profile_begin(max_launches))
+
+
+def profile_end() -> dict:
+    """Stop timing; returns {stage: (launches, total_ms)} (waits for the GPU)."""
+    arr = (StageTime * 16)()
+    n = ctypes.c_int()
+    _check(load().gdr_profile_end(arr, 16, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
 
 
 # ---------------------------------------------------------------- torch side

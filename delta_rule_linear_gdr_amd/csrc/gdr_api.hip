@@ -7,7 +7,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "gdr.h"
 #include "kernels.h"
@@ -176,6 +178,50 @@ int hip_fail(hipError_t e, const char* what)
     return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ---- optional per-stage timing (gdr_profile_begin / gdr_profile_end) ----
+enum Stage { ST_PREP, ST_SCAN_FWD, ST_SCAN_BWD, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE };
+const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "scan_bwd", "bwd_local",
+                                        "bwd_local_wy7"};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    bool overflow = false;
+    std::vector<hipEvent_t> pool;
+    struct Rec { int stage; hipEvent_t a, b; };
+    std::vector<Rec> recs;
+};
+Profiler& prof()
+{
+    static Profiler p;
+    return p;
+}
+
+// Runs one launch; when profiling is on, brackets it with events on `st`.
+template <typename F>
+hipError_t timed(Stage stage, hipStream_t st, F&& launch)
+{
+    Profiler& P = prof();
+    std::unique_lock<std::mutex> lk(P.mu);
+    if (!P.on) {
+        lk.unlock();
+        return launch();
+    }
+    if (2 * (P.recs.size() + 1) > P.pool.size()) {
+        P.overflow = true;
+        lk.unlock();
+        return launch();
+    }
+    Profiler::Rec r{stage, P.pool[2 * P.recs.size()], P.pool[2 * P.recs.size() + 1]};
+    hipError_t e = hipEventRecord(r.a, st);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(r.b, st);
+    if (e == hipSuccess) P.recs.push_back(r);
+    return e;
+}
+
 int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
             const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
@@ -212,13 +258,16 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     Grads gr{dq, dk, dv, dbeta, dg, dh0};
     hipError_t e;
     if (policy == GDR_RECOMPUTE) {
-        if ((e = launch_prep(s, in, it, true, st)) != hipSuccess) return hip_fail(e, "prep");
-        if ((e = launch_scan_fwd(s, in, it, nullptr, nullptr, st)) != hipSuccess)
-            return hip_fail(e, "scan_fwd");
+        e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, true, st); });
+        if (e != hipSuccess) return hip_fail(e, "prep");
+        e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, nullptr, nullptr, st); });
+        if (e != hipSuccess) return hip_fail(e, "scan_fwd");
     }
-    if ((e = launch_scan_bwd(s, in, it, dh0, st)) != hipSuccess) return hip_fail(e, "scan_bwd");
-    if ((e = launch_bwd_local(s, in, it, gr, wy7, st)) != hipSuccess)
-        return hip_fail(e, "bwd_local");
+    e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
+    if (e != hipSuccess) return hip_fail(e, "scan_bwd");
+    e = timed(wy7 ? ST_BWD_LOCAL_WY7 : ST_BWD_LOCAL, st,
+              [&] { return launch_bwd_local(s, in, it, gr, wy7, st); });
+    if (e != hipSuccess) return hip_fail(e, "bwd_local");
     return GDR_OK;
 }
 
@@ -274,9 +323,10 @@ int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     const Shape s = make_shape(d);
     Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
     hipError_t e;
-    if ((e = launch_prep(s, in, it, policy == GDR_FULL_SAVE, st)) != hipSuccess)
-        return hip_fail(e, "prep");
-    if ((e = launch_scan_fwd(s, in, it, o, ht, st)) != hipSuccess) return hip_fail(e, "scan_fwd");
+    e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, policy == GDR_FULL_SAVE, st); });
+    if (e != hipSuccess) return hip_fail(e, "prep");
+    e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });
+    if (e != hipSuccess) return hip_fail(e, "scan_fwd");
     return GDR_OK;
 }
 
@@ -311,6 +361,56 @@ const char* gdr_status_string(int status)
 }
 
 const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+int gdr_profile_begin(int max_launches)
+{
+    if (max_launches < 1 || max_launches > (1 << 20))
+        return fail(GDR_ERR_INVALID, "max_launches %d out of range", max_launches);
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (P.on) return fail(GDR_ERR_INVALID, "profiling already active");
+    while (P.pool.size() < 2 * (size_t)max_launches) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        P.pool.push_back(ev);
+    }
+    P.recs.clear();
+    P.overflow = false;
+    P.on = true;
+    return GDR_OK;
+}
+
+int gdr_profile_end(gdr_stage_time* out, int cap, int* n_out)
+{
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> lk(P.mu);
+    if (!P.on) return fail(GDR_ERR_INVALID, "profiling is not active");
+    P.on = false;
+    gdr_stage_time acc[NSTAGE];
+    memset(acc, 0, sizeof acc);
+    for (const auto& r : P.recs) {
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        float ms = 0.f;
+        e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+        acc[r.stage].launches += 1;
+        acc[r.stage].total_ms += ms;
+    }
+    int n = 0;
+    for (int i = 0; i < NSTAGE; ++i) {
+        if (acc[i].launches == 0) continue;
+        if (out && n < cap) {
+            out[n] = acc[i];
+            snprintf(out[n].name, sizeof out[n].name, "%s", kStageName[i]);
+        }
+        ++n;
+    }
+    if (n_out) *n_out = n;
+    if (P.overflow) return fail(GDR_ERR_WORKSPACE, "more launches than max_launches; tail not timed");
+    return GDR_OK;
+}
 
 int gdr_version(void) { return 1; }
 

@@ -106,6 +106,24 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
 
+/* Per-stage timing for benchmarks. gdr_profile_begin creates 2*max_launches
+ * HIP events (the only allocation the library makes, and only here) and
+ * turns timing on: every kernel that gdr_fwd / gdr_bwd / gdr_bwd_wy7 then
+ * launch is bracketed by events recorded on the call's stream. Stages are
+ * "prep", "scan_fwd", "scan_bwd", "bwd_local", "bwd_local_wy7".
+ * gdr_profile_end turns timing off, waits for the recorded events (a host
+ * synchronization), and writes up to `cap` per-stage totals; *n_out receives
+ * the number of stages seen. Launches beyond max_launches run untimed and
+ * gdr_profile_end then returns GDR_ERR_WORKSPACE (totals still written).
+ * Not meant to be combined with stream capture. */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+} gdr_stage_time;
+int gdr_profile_begin(int max_launches);
+int gdr_profile_end(gdr_stage_time* out, int cap, int* n_out);
+
 const char* gdr_status_string(int status);
 const char* gdr_last_error(void);
 int gdr_version(void);
