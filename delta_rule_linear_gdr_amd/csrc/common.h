@@ -143,4 +143,72 @@ __device__ __forceinline__ float sum16(float x)
     return x;
 }
 
+
+// ---------------------------------------------------------------- tile formats
+// (see kernels.h for the frag and ctile formats)
+
+__device__ __forceinline__ int lane_r() { return threadIdx.x & 15; }
+__device__ __forceinline__ int lane_g() { return (threadIdx.x >> 4) & 3; }
+
+// k offset inside a 32-wide slab of slot j held by lane group g.
+__host__ __device__ __forceinline__ int pik(int g, int j) { return j < 4 ? 4 * g + j : 12 + 4 * g + j; }
+
+// Two accumulator tiles stacked along M (rows 0..15 in lo, 16..31 in hi)
+// as one frag slab: slots 0..3 from lo, 4..7 from hi.
+__device__ __forceinline__ bf16x8 pack_pi(const f32x4& lo, const f32x4& hi, float s = 1.f)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = (bf16)(lo[i] * s);
+        v[4 + i] = (bf16)(hi[i] * s);
+    }
+    return v;
+}
+__device__ __forceinline__ bf16x4 pack4(const f32x4& c, float s = 1.f)
+{
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(c[i] * s);
+    return v;
+}
+__device__ __forceinline__ f32x4 unpack4(const bf16x4& v)
+{
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
+// Lane pointer into frag tile `tile` of a buffer.
+__device__ __forceinline__ bf16* frag_ptr(bf16* base, int tile) { return base + (tile * 64 + lane_id()) * 8; }
+__device__ __forceinline__ const bf16* frag_ptr(const bf16* base, int tile)
+{
+    return base + (tile * 64 + lane_id()) * 8;
+}
+__device__ __forceinline__ bf16x8 ld_frag(const bf16* base, int tile) { return *(const bf16x8*)frag_ptr(base, tile); }
+__device__ __forceinline__ void st_frag(bf16* base, int tile, const bf16x8& v) { *(bf16x8*)frag_ptr(base, tile) = v; }
+// Lane pointer into ctile `tile`.
+__device__ __forceinline__ const bf16* ctile_ptr(const bf16* base, int tile)
+{
+    return base + (tile * 64 + lane_id()) * 4;
+}
+__device__ __forceinline__ bf16* ctile_ptr(bf16* base, int tile) { return base + (tile * 64 + lane_id()) * 4; }
+
+// B operand of X * I for output column tile nt: the identity restricted to
+// k slab nt >> 1 (the other slabs are zero). parity = nt & 1.
+__device__ __forceinline__ bf16x8 ident_frag(int parity)
+{
+    const int r = lane_r(), g = lane_g();
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (bf16)((8 * g + j == 16 * parity + r) ? 1.f : 0.f);
+    return v;
+}
+
+// Plain-order fragment of a row-major matrix with row stride ld (elements):
+// lane (r, g) gets X[row0 + r][k0 + 8 g .. + 7] as floats.
+template <typename T>
+__device__ __forceinline__ void ld_plain8(const T* base, int64_t ld, int row0, int k0, float (&x)[8])
+{
+    load8(base + (int64_t)(row0 + lane_r()) * ld + k0 + 8 * lane_g(), x);
+}
+
 }  // namespace gdr

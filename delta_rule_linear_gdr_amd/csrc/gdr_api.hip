@@ -34,10 +34,9 @@ int fail(int status, const char* fmt, ...)
 constexpr size_t ALIGN = 256;
 size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
-// Per-tile byte sizes of the chunk intermediates.
-constexpr size_t B_W = CH * DKD * 2, B_U = CH * DVD * 2, B_KT = CH * DKD * 2, B_QG = CH * DKD * 2;
-constexpr size_t B_A = CH * CH * 2, B_HM = CH * CH * 2, B_GN = DKD * 4;
-constexpr size_t B_H = DKD * DVD * 2, B_R = CH * DVD * 2, B_DH = DKD * DVD * 2, B_RB = CH * DVD * 2;
+// Per-tile byte sizes of the chunk intermediates (formats in kernels.h).
+constexpr size_t B_T64x128 = CH * DKD * 2, B_T128x128 = DKD * DVD * 2, B_T64x64 = CH * CH * 2;
+constexpr size_t B_GN = DKD * 4;
 
 struct Carver {
     char* base;
@@ -54,17 +53,17 @@ struct Carver {
     }
 };
 
-// Chunk quantities shared by the forward (full save) and the backward.
+// What the full-save forward keeps for the backward.
 void carve_saved(Carver& c, Inter& it)
 {
-    it.A = c.take<bf16>(B_A);
-    it.W = c.take<bf16>(B_W);
-    it.Hm = c.take<bf16>(B_HM);
-    it.Kt = c.take<bf16>(B_KT);
-    it.Qg = c.take<bf16>(B_QG);
+    it.A = c.take<bf16>(B_T64x64);
+    it.Kt = c.take<bf16>(B_T64x128);
+    it.WnT = c.take<bf16>(B_T64x128);
     it.gn = c.take<float>(B_GN);
-    it.h = c.take<bf16>(B_H);
-    it.R = c.take<bf16>(B_R);
+    it.HmT = c.take<bf16>(B_T64x64);
+    it.QgT = c.take<bf16>(B_T64x128);
+    it.h = c.take<bf16>(B_T128x128);
+    it.R = c.take<bf16>(B_T64x128);
 }
 
 enum Phase { FWD, BWD };
@@ -75,26 +74,33 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
 {
     memset(&it, 0, sizeof it);
     Carver sv(saved, ntiles), sc(scratch, ntiles);
-    if (policy == GDR_FULL_SAVE) {
-        carve_saved(sv, it);
+    const bool full = policy == GDR_FULL_SAVE;
+    if (full) carve_saved(sv, it);
+    if (ph == FWD || !full) {
+        // operands of the forward scan (and, in the forward, its output)
+        it.Wn = sc.take<bf16>(B_T64x128);
+        it.KtT = sc.take<bf16>(B_T64x128);
+        it.U = sc.take<bf16>(B_T64x128);
+        if (!full) it.gn = sc.take<float>(B_GN);
         if (ph == FWD) {
-            it.U = sc.take<bf16>(B_U);
-        } else {
-            it.dh = sc.take<bf16>(B_DH);
-            it.Rb = sc.take<bf16>(B_RB);
-        }
-    } else {
-        carve_saved(sc, it);
-        it.U = sc.take<bf16>(B_U);
-        if (ph == FWD) {
-            // the forward alone keeps no per-chunk state, A or correction
-            it.A = it.h = it.R = nullptr;
-        } else {
-            it.dh = sc.take<bf16>(B_DH);
-            it.Rb = sc.take<bf16>(B_RB);
+            it.Qg = sc.take<bf16>(B_T64x128);
+            it.Hm = sc.take<bf16>(B_T64x64);
         }
     }
-    saved_bytes = policy == GDR_FULL_SAVE ? align_up(sv.off) : 0;
+    if (ph == BWD) {
+        if (!full) {
+            it.Kt = sc.take<bf16>(B_T64x128);
+            it.WnT = sc.take<bf16>(B_T64x128);
+            it.A = sc.take<bf16>(B_T64x64);
+            it.h = sc.take<bf16>(B_T128x128);
+            it.R = sc.take<bf16>(B_T64x128);
+        }
+        it.X = sc.take<bf16>(B_T64x128);
+        it.Y = sc.take<bf16>(B_T128x128);
+        it.dh = sc.take<bf16>(B_T128x128);
+        it.Rb = sc.take<bf16>(B_T64x128);
+    }
+    saved_bytes = full ? align_up(sv.off) : 0;
     scratch_bytes = align_up(sc.off);
 }
 
@@ -179,8 +185,8 @@ int hip_fail(hipError_t e, const char* what)
 }
 
 // ---- optional per-stage timing (gdr_profile_begin / gdr_profile_end) ----
-enum Stage { ST_PREP, ST_SCAN_FWD, ST_SCAN_BWD, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE };
-const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "scan_bwd", "bwd_local",
+enum Stage { ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE };
+const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "xy", "scan_bwd", "bwd_local",
                                         "bwd_local_wy7"};
 
 struct Profiler {
@@ -258,10 +264,15 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     Grads gr{dq, dk, dv, dbeta, dg, dh0};
     hipError_t e;
     if (policy == GDR_RECOMPUTE) {
-        e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, true, st); });
+        e = timed(ST_PREP, st, [&] {
+            return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A, st);
+        });
         if (e != hipSuccess) return hip_fail(e, "prep");
         e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, nullptr, nullptr, st); });
         if (e != hipSuccess) return hip_fail(e, "scan_fwd");
+    } else {
+        e = timed(ST_XY, st, [&] { return launch_xy(s, in, it, st); });
+        if (e != hipSuccess) return hip_fail(e, "xy");
     }
     e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
     if (e != hipSuccess) return hip_fail(e, "scan_bwd");
@@ -323,7 +334,9 @@ int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     const Shape s = make_shape(d);
     Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
     hipError_t e;
-    e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, policy == GDR_FULL_SAVE, st); });
+    const int what = PREP_FWDSCAN | PREP_OUT |
+                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A : 0);
+    e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, what, st); });
     if (e != hipSuccess) return hip_fail(e, "prep");
     e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });
     if (e != hipSuccess) return hip_fail(e, "scan_fwd");

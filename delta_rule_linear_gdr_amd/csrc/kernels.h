@@ -1,5 +1,23 @@
 // Kernel argument blocks and launch entry points of the chunkwise gated
-// delta rule (gfx950). Host code in gdr_api.cpp sequences these launches.
+// delta rule (gfx950). Host code in gdr_api.hip sequences these launches.
+//
+// Tile formats of the per-(head, chunk) intermediates. Every matrix product
+// runs on v_mfma_f32_16x16x32_bf16; lane l has r = l & 15, g = l >> 4.
+//
+//  frag  (M x K, "contraction along K"): 16 x 32 tiles, tile (mt, ks) at
+//        index mt * (K / 32) + ks, 64 lanes x 8 bf16 = 1 KiB per tile. Lane
+//        (r, g) slot j holds X[16 mt + r][32 ks + pik(g, j)] with
+//        pik(g, j) = 4 g + j (j < 4), 16 + 4 g + (j - 4) (j >= 4).
+//        One 16-byte load per lane gives an MFMA A operand (rows of X) or B
+//        operand (columns of the product = rows of X). The permuted k order
+//        is the order in which two stacked 16 x 16 accumulator tiles hold
+//        their rows, so an accumulator feeds the next contraction over its
+//        rows without any data movement between lanes.
+//  ctile (M x N): 16 x 16 accumulator tiles, tile (nt, mt) at index
+//        nt * (M / 16) + mt, 64 lanes x 4 bf16 = 512 B per tile. Lane (r, g)
+//        element i holds X[16 mt + 4 g + i][16 nt + r]. A column slice of
+//        the matrix (fixed nt) is contiguous.
+//  plain: row-major.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -12,13 +30,30 @@ constexpr int CH = 64;    // chunk length
 constexpr int DKD = 128;  // key width
 constexpr int DVD = 128;  // value width
 
-// Per-chunk intermediates, one tile per (b*H + h, chunk), row-major tiles:
-//   W, U, Kt, Qg, R, Rb : 64 x 128 bf16      A, Hm : 64 x 64 bf16
-//   h, dh               : 128 x 128 bf16 (key-major: [dk][dv])
-//   gn                  : 128 fp32 (exp of the chunk's total log decay)
+// Per-chunk intermediates; every pointer is indexed by tile t = bh * NT + c.
+// Sizes per tile in parentheses. Unused pointers are null.
 struct Inter {
-    bf16 *W, *U, *Kt, *Qg, *A, *Hm, *h, *R, *dh, *Rb;
-    float* gn;
+    // forward scan operands (prep)
+    bf16* Wn;    // -W          frag  M=64 tok,  K=128 key   (16 KiB)
+    bf16* KtT;   // Kt^T        frag  M=128 key, K=64 tok    (16 KiB)
+    bf16* U;     // U           ctile M=64 tok,  N=128 val   (16 KiB)
+    float* gn;   // exp(G_n)    128 fp32 per key             (512 B)
+    // forward output operands (prep)
+    bf16* Qg;    // gam * Q     frag  M=64 tok,  K=128 key   (16 KiB)
+    bf16* Hm;    // Hm          frag  M=64 tok i, K=64 tok j (8 KiB)
+    // reverse scan operands (prep, xy)
+    bf16* Kt;    // Kt          frag  M=64 tok,  K=128 key   (16 KiB)
+    bf16* WnT;   // -W^T        frag  M=128 key, K=64 tok    (16 KiB)
+    bf16* X;     // Hm^T dO     ctile M=64 tok,  N=128 val   (16 KiB)
+    bf16* Y;     // Qg^T dO     ctile M=128 key, N=128 val   (32 KiB)
+    bf16* HmT;   // Hm^T        frag  M=64 tok j, K=64 tok i (8 KiB)
+    bf16* QgT;   // Qg^T        frag  M=128 key, K=64 tok    (16 KiB)
+    // chunk-local backward inputs
+    bf16* A;     // A = (I+L)^-1 plain [i][j]                 (8 KiB)
+    bf16* h;     // state at chunk start, plain [key][val]    (32 KiB)
+    bf16* R;     // correction, plain [tok][val]              (16 KiB)
+    bf16* dh;    // state adjoint at chunk end, plain         (32 KiB)
+    bf16* Rb;    // correction adjoint, plain [tok][val]      (16 KiB)
 };
 
 struct Shape {
@@ -37,13 +72,25 @@ struct Grads {
     float *dg, *dh0;
 };
 
-hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, bool write_A,
+// What prep writes (bit set of PREP_*).
+enum {
+    PREP_FWDSCAN = 1,  // Wn, KtT, U, gn
+    PREP_OUT = 2,      // Qg, Hm
+    PREP_BWDSCAN = 4,  // Kt, WnT (and gn)
+    PREP_XY = 8,       // X, Y from dO
+    PREP_SAVEXY = 16,  // HmT, QgT (for launch_xy)
+    PREP_A = 32,       // A
+};
+
+hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what,
                        hipStream_t st);
-// Forward state scan: R, h per chunk (when the pointers are set), output o
-// (when o != nullptr) and final state ht (when ht != nullptr).
-hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o, float* ht,
-                           hipStream_t st);
-// Reverse state scan: dh, Rb per chunk and dh0.
+// X = Hm^T dO and Y = Qg^T dO from HmT, QgT and dO.
+hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStream_t st);
+// Forward state scan. Writes h and R when set, the output o when o != null
+// and the final state ht when ht != null.
+hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o,
+                           float* ht, hipStream_t st);
+// Reverse state scan. Writes dh and Rb when set, and dh0 when dh0 != null.
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                            hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.

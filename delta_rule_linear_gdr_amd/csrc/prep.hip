@@ -1,17 +1,26 @@
-// chunk_prep: per (chunk, head) WY quantities of the chunkwise gated delta rule.
+// chunk_prep: per (chunk, head) quantities of the chunkwise gated delta rule.
 //
-// ReWY paper, Sec. 2.3 (the chunk system) and the onedev.kr summary, "How it
-// works" (M R = Z - E S with M = I + L, L the strict lower part of E Y^T,
-// A = M^{-1}, W = A E, U = A Z). With G the chunk-local inclusive cumsum of
-// the log decay, gam = exp(G):
+// ReWY paper (paperpeel.com/paper/2611.01940), Sec. 2.3, and the onedev.kr
+// summary, "How it works": the chunk system M R = Z - E S with M = I + L,
+// L the strict lower part of E Y^T, A = M^{-1}, W = A E, U = A Z. With G the
+// chunk-local inclusive cumsum of the log decay and gam = exp(G):
 //   E = diag(beta)(gam * K)   Z = diag(beta) V   Y = K / gam
 //   L = strict_lower(E Y^T)   Hm = lower_incl((gam * Q) Y^T)
 //   Kt = exp(G_n - G) * K     Qg = gam * Q       gn = exp(G_n)
-// Scalar gate: E Y^T is beta_i exp(G_i - G_j) (K K^T)_ij, formed from K K^T.
+// Scalar gate: E Y^T = beta_i exp(G_i - G_j) (K K^T)_ij, formed from K K^T.
 // Vector gate: the centred factors of Sec. 3.3 ("Centered factors"),
-// alpha = exp(G - c), zeta = exp(c - G) with c = (max G + min G)/2 per
-// feature, give E'Y'^T = E Y^T with every factor bounded by exp(range/2).
-// The unit-lower inverse is a 16x16-blocked forward substitution in fp32.
+// alpha = exp(G - c), zeta = exp(c - G) with c = (max G + min G)/2 per key,
+// give E'Y'^T = E Y^T with every factor bounded by exp(range / 2).
+//
+// Work split (four waves): wave w owns keys [32 w, 32 w + 32) and values
+// [32 w, 32 w + 32) of every 64 x 128 operand. Transposed operands come from
+// an MFMA with the identity (X * I leaves X in accumulator order, which is
+// the frag order of X^T), so no operand is transposed through LDS. The
+// unit-lower inverse is a 16 x 16-blocked forward substitution in fp32.
+// Outputs (bit set `what`, formats in kernels.h): the forward-scan operands
+// -W, Kt^T, U, gn; the output operands Qg, Hm; the reverse-scan operands
+// Kt, -W^T and, given dO, X = Hm^T dO and Y = Qg^T dO; Hm^T and Qg^T for a
+// later X/Y pass; and A.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,48 +28,70 @@ namespace gdr {
 
 namespace {
 
-constexpr int LDF = CH + 1;  // fp32 row stride of the 64 x 64 solve buffers
+constexpr int LP = CH + 4;  // fp32 row stride of the 64 x 64 solve buffers
+constexpr int TP = 20;      // fp32 row stride of the 16 x 16 solve temporaries
+
+template <typename T>
+__device__ __forceinline__ bf16x8 to_frag(const float (&x)[8])
+{
+    return pack8(x);
+}
+
+// Store 8 consecutive keys (f0 .. f0 + 7, f0 a multiple of 8) of token row
+// i as part of a frag (M = 64 tok, K = 128 key) buffer.
+__device__ __forceinline__ void st_row8_frag(bf16* base, int i, int f0, const float (&x)[8])
+{
+    const int ks = f0 >> 5, a = (f0 >> 3) & 3;
+    const int tile = (i >> 4) * 4 + ks;
+    const int gA = 2 * (a & 1), slot0 = 4 * (a >> 1), r = i & 15;
+    bf16x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        lo[e] = (bf16)x[e];
+        hi[e] = (bf16)x[4 + e];
+    }
+    *(bf16x4*)(base + (tile * 64 + 16 * gA + r) * 8 + slot0) = lo;
+    *(bf16x4*)(base + (tile * 64 + 16 * (gA + 1) + r) * 8 + slot0) = hi;
+}
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it, int write_A)
+__global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it, int what)
 {
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
-    const int64_t b = bh / s.H, h = bh % s.H;
-    const int64_t tile = (int64_t)bh * s.NT + c;
-    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + h;  // token of row 0
-    const int64_t rs = s.H;                                      // token stride between rows
+    const int64_t b = bh / s.H, hd = bh % s.H;
+    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;  // token of row 0
+    const int64_t ld = s.H * DKD;                                 // row stride (elements)
     const int tid = threadIdx.x;
-    const int l = lane_id();
-    const int w = wave_id();
+    const int l = lane_id(), r = lane_r(), g = lane_g();
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+    const bool fwdscan = what & PREP_FWDSCAN, out = what & PREP_OUT, bwdscan = what & PREP_BWDSCAN;
+    const bool xy = what & PREP_XY, savexy = what & PREP_SAVEXY, wantA = what & PREP_A;
 
     constexpr int GSZ = VEC ? CH * DKD : CH;
     __shared__ float sG[GSZ];
     __shared__ float sCen[DKD];
     __shared__ float sBeta[CH];
-    // X region: three 64 x 136 bf16 operand tiles; later the fp32 solve buffers.
-    __shared__ __attribute__((aligned(16))) char sX[3 * CH * LD128 * 2];
-    __shared__ __attribute__((aligned(16))) bf16 sET[DKD * LD64];  // E^T  [f][i]
-    __shared__ __attribute__((aligned(16))) bf16 sZT[DVD * LD64];  // Z^T  [v][i]
-    bf16* sX1 = (bf16*)sX;
-    bf16* sX2 = sX1 + CH * LD128;
-    bf16* sX3 = sX2 + CH * LD128;
-    float* sL = (float*)sX;                       // L   fp32 [64][65]
-    float* sAi = sL + CH * LDF;                   // A   fp32 [64][65]
-    bf16* sAb = (bf16*)(sX + 2 * CH * LD128 * 2); // A   bf16 [64][72]  (in sX3)
-    float* sT = (float*)(sAb + CH * LD64);        // 3 x 16 x 17 fp32   (in sX3)
+    __shared__ __attribute__((aligned(16))) float sL[CH * LP];
+    __shared__ __attribute__((aligned(16))) float sA[CH * LP];
+    __shared__ __attribute__((aligned(16))) float sT[3 * 16 * TP];
+    __shared__ bf16x8 sHmT[8 * 64];   // Hm^T frag (M = 64 tok j, K = 64 tok i)
+    __shared__ bf16x8 sQgT[16 * 64];  // Qg^T frag (M = 128 key, K = 64 tok)
 
-    const T* q = (const T*)in.q;
-    const T* k = (const T*)in.k;
-    const T* v = (const T*)in.v;
+    const T* q = (const T*)in.q + tok0 * DKD;
+    const T* k = (const T*)in.k + tok0 * DKD;
+    const T* v = (const T*)in.v + tok0 * DVD;
+    const T* dO = (const T*)in.dO + tok0 * DVD;
     const T* beta = (const T*)in.beta;
 
-    // ---- 1. gate cumsum (and centre per feature), beta ----
+    // ---- 1. gate cumsum (and per-key centre), beta ----
     if (VEC) {
         if (tid < DKD) {
             float acc = 0.f, mx = -INFINITY, mn = INFINITY;
             for (int i = 0; i < CH; ++i) {
-                acc += in.g[(tok0 + i * rs) * DKD + tid];
+                acc += in.g[(tok0 + i * s.H) * DKD + tid];
                 sG[i * DKD + tid] = acc;
                 mx = fmaxf(mx, acc);
                 mn = fminf(mn, acc);
@@ -68,201 +99,444 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             sCen[tid] = 0.5f * (mx + mn);
         }
     } else if (w == 0) {
-        float x = in.g[tok0 + l * rs];
+        float x = in.g[tok0 + l * s.H];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            float y = __shfl_up(x, off);
+            const float y = __shfl_up(x, off);
             if (l >= off) x += y;
         }
         sG[l] = x;
     }
-    if (tid < CH) sBeta[tid] = io<T>::ld(beta + tok0 + tid * rs);
+    if (tid < CH) sBeta[tid] = io<T>::ld(beta + tok0 + tid * s.H);
     __syncthreads();
 
-    // ---- 2. operand tiles ----
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int id = tid + 256 * u;
-        const int i = id >> 4;
-        const int f0 = (id & 15) * 8;
-        const int64_t row = (tok0 + i * rs) * DKD + f0;
-        float kx[8], qx[8], vx[8];
-        load8(k + row, kx);
-        load8(q + row, qx);
-        load8(v + row, vx);
-        const float bt = sBeta[i];
-        float Gi[8], Gn[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            Gi[e] = VEC ? sG[i * DKD + f0 + e] : sG[i];
-            Gn[e] = VEC ? sG[(CH - 1) * DKD + f0 + e] : sG[CH - 1];
-        }
-        float kt[8], qg[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float gam = __expf(Gi[e]);
-            sET[(f0 + e) * LD64 + i] = (bf16)(bt * gam * kx[e]);
-            sZT[(f0 + e) * LD64 + i] = (bf16)(bt * vx[e]);
-            kt[e] = __expf(Gn[e] - Gi[e]) * kx[e];
-            qg[e] = gam * qx[e];
-        }
-        store8(it.Kt + (tile * CH + i) * DKD + f0, kt);
-        store8(it.Qg + (tile * CH + i) * DKD + f0, qg);
-        if (VEC) {
-            float ep[8], yp[8], qp[8];
+    auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
+    if ((fwdscan || bwdscan) && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
+
+    // plain fragment of row block i0 .. i0+15, keys 32 ks + 8 g .. + 7, with
+    // an optional per-(row, key) scale (vector gate)
+    auto frag_rows = [&](const T* base, int i0, int ks, int kind) -> bf16x8 {
+        float x[8];
+        ld_plain8(base, ld, i0, 32 * ks, x);
+        if (VEC && kind != 0) {
+            const int i = i0 + r, f0 = 32 * ks + 8 * g;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float cc = sCen[f0 + e];
-                const float al = __expf(Gi[e] - cc);
-                const float ze = __expf(cc - Gi[e]);
-                ep[e] = bt * al * kx[e];
-                yp[e] = ze * kx[e];
-                qp[e] = al * qx[e];
+                const float d = sG[i * DKD + f0 + e] - sCen[f0 + e];
+                // 1: alpha = exp(G - c) (queries);  2: beta alpha (erase keys);
+                // 3: zeta = exp(c - G) (write keys)
+                x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
             }
-            *(bf16x8*)(sX1 + i * LD128 + f0) = pack8(ep);
-            *(bf16x8*)(sX2 + i * LD128 + f0) = pack8(yp);
-            *(bf16x8*)(sX3 + i * LD128 + f0) = pack8(qp);
-        } else {
-            *(bf16x8*)(sX1 + i * LD128 + f0) = pack8(kx);
-            *(bf16x8*)(sX3 + i * LD128 + f0) = pack8(qx);
         }
-    }
-    if (tid < DKD) it.gn[tile * DKD + tid] = __expf(VEC ? sG[(CH - 1) * DKD + tid] : sG[CH - 1]);
-    __syncthreads();
+        return pack8(x);
+    };
 
-    // ---- 3. L = strict_lower(E Y^T), Hm = lower_incl(Qg Y^T) ----
-    f32x4 accL[4], accH[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) { accL[nt] = zero4(); accH[nt] = zero4(); }
+    // ---- 2. L = strict_lower(E Y^T) and Hm = lower_incl(Qg Y^T), 16 x 16 tiles ----
     {
-        const bf16* Aop = sX1;              // K (scalar) or E' (vector)
-        const bf16* Bop = VEC ? sX2 : sX1;  // K (scalar) or Y' (vector)
+        const bool needH = xy || savexy, needHt = out;
+        for (int x = w; x < 10; x += 4) {
+            // lower 16 x 16 tiles (ti, tj <= ti) in row order
+            const int ti = x >= 6 ? 3 : x >= 3 ? 2 : x >= 1 ? 1 : 0;
+            const int tj = x - ti * (ti + 1) / 2;
+            f32x4 aL = zero4(), aH = zero4(), aHt = zero4();
 #pragma unroll
-        for (int kk = 0; kk < DKD; kk += 32) {
-            bf16x8 aL = frag(Aop, LD128, 16 * w, kk);
-            bf16x8 aH = frag(sX3, LD128, 16 * w, kk);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                if (nt <= w) {
-                    bf16x8 bb = frag(Bop, LD128, 16 * nt, kk);
-                    accL[nt] = mfma(aL, bb, accL[nt]);
-                    accH[nt] = mfma(aH, bb, accH[nt]);
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ki = frag_rows(k, 16 * ti, ks, 2);  // E' rows (scalar: K)
+                const bf16x8 kj = frag_rows(k, 16 * tj, ks, 3);  // Y' rows (scalar: K)
+                aL = mfma(ki, kj, aL);
+                if (needH || needHt) {
+                    const bf16x8 qi = frag_rows(q, 16 * ti, ks, 1);  // Q' rows (scalar: Q)
+                    if (needH) aH = mfma(qi, kj, aH);
+                    if (needHt) aHt = mfma(kj, qi, aHt);
                 }
             }
-        }
-    }
-    __syncthreads();  // all reads of sX1/sX2/sX3 done before sL/sAi/sAb overwrite them
+            // aL, aH: lane holds (i = 16 ti + 4 g + e, j = 16 tj + r)
+            // aHt:    lane holds (j = 16 tj + 4 g + e, i = 16 ti + r)
+            bf16x4 hv, htv;
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int j = ccol(16 * nt);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = crow(16 * w, r);
-            float Lv = 0.f, Hv = 0.f;
-            if (nt <= w) {
-                float scale = 1.f, bs = 1.f;
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * ti + 4 * g + e, j = 16 * tj + r;
+                float lam = 1.f, bs = 1.f;
                 if (!VEC) {
-                    scale = __expf(sG[i] - sG[j]);
+                    lam = __expf(sG[i] - sG[j]);
                     bs = sBeta[i];
                 }
-                Lv = (i > j) ? accL[nt][r] * scale * bs : 0.f;
-                Hv = (i >= j) ? accH[nt][r] * scale : 0.f;
+                sL[i * LP + j] = (i > j) ? aL[e] * lam * bs : 0.f;
+                hv[e] = (bf16)((i >= j) ? aH[e] * lam : 0.f);
+                const int i2 = 16 * ti + r, j2 = 16 * tj + 4 * g + e;
+                const float lam2 = VEC ? 1.f : __expf(sG[i2] - sG[j2]);
+                htv[e] = (bf16)((i2 >= j2) ? aHt[e] * lam2 : 0.f);
             }
-            sL[i * LDF + j] = Lv;
-            it.Hm[(tile * CH + i) * CH + j] = (bf16)Hv;
+            // Hm^T frag (M = j, K = i): tile (tj, ti >> 1), half ti & 1
+            const int hoff = (((tj * 2 + (ti >> 1)) * 64 + l) * 8) + 4 * (ti & 1);
+            if (xy) *(bf16x4*)((bf16*)sHmT + hoff) = hv;
+            if (savexy) *(bf16x4*)(it.HmT + t * (CH * CH) + hoff) = hv;
+            // Hm frag (M = i, K = j): tile (ti, tj >> 1), half tj & 1
+            if (out)
+                *(bf16x4*)(it.Hm + t * (CH * CH) + (((ti * 2 + (tj >> 1)) * 64 + l) * 8) + 4 * (tj & 1)) =
+                    htv;
+        }
+        // the zero halves / tiles of the two triangular frag buffers
+        if (w == 0) {
+            const bf16x4 z4 = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+            const bf16x8 z8 = {(bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f,
+                               (bf16)0.f, (bf16)0.f, (bf16)0.f, (bf16)0.f};
+            // Hm^T: (tj=1, ti=0) and (tj=3, ti=2) halves; tiles (tj=2,3; ks=0)
+            if (xy || savexy) {
+                bf16* dst = xy ? (bf16*)sHmT : it.HmT + t * (CH * CH);
+                if (xy && savexy) {
+                    // both: write the global copy too
+                    bf16* g2 = it.HmT + t * (CH * CH);
+                    *(bf16x4*)(g2 + ((1 * 2 + 0) * 64 + l) * 8) = z4;
+                    *(bf16x4*)(g2 + ((3 * 2 + 1) * 64 + l) * 8) = z4;
+                    *(bf16x8*)(g2 + ((2 * 2 + 0) * 64 + l) * 8) = z8;
+                    *(bf16x8*)(g2 + ((3 * 2 + 0) * 64 + l) * 8) = z8;
+                }
+                *(bf16x4*)(dst + ((1 * 2 + 0) * 64 + l) * 8) = z4;
+                *(bf16x4*)(dst + ((3 * 2 + 1) * 64 + l) * 8) = z4;
+                *(bf16x8*)(dst + ((2 * 2 + 0) * 64 + l) * 8) = z8;
+                *(bf16x8*)(dst + ((3 * 2 + 0) * 64 + l) * 8) = z8;
+            }
+            // Hm: (ti=0, tj=1) and (ti=2, tj=3) halves; tiles (ti=0,1; ks=1)
+            if (out) {
+                bf16* dst = it.Hm + t * (CH * CH);
+                *(bf16x4*)(dst + ((0 * 2 + 0) * 64 + l) * 8 + 4) = z4;
+                *(bf16x4*)(dst + ((2 * 2 + 1) * 64 + l) * 8 + 4) = z4;
+                *(bf16x8*)(dst + ((0 * 2 + 1) * 64 + l) * 8) = z8;
+                *(bf16x8*)(dst + ((1 * 2 + 1) * 64 + l) * 8) = z8;
+            }
         }
     }
-    __syncthreads();
 
-    // ---- 4. A = (I + L)^{-1}: 16x16 diagonal blocks, then block rows ----
-    if (l < 16) {
-        const int base = 16 * w;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == l) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc -= sL[(base + i) * LDF + base + m] * x[m];
-            x[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sAi[(base + i) * LDF + base + l] = x[i];
-    }
-    __syncthreads();
+    // ---- 4. transposed operands through X * I (wave w: key / value slab w) ----
+    bf16x8 ET[2][2], ZT[2][2], OT[2][2];  // [n][ks]: E^T, Z^T, dO^T frags
     {
-        const int r = tid >> 4, cc = tid & 15;
+        const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
+        // K * I: lane holds K[tok 16 mt + 4 g + e][key 32 w + 16 n + r]
+        f32x4 KC[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const bf16x8 kf = frag_rows(k, 16 * mt, w, 0);
+            KC[mt][0] = mfma(kf, I0, zero4());
+            KC[mt][1] = mfma(kf, I1, zero4());
+        }
+        f32x4 EC[4][2];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const int f = 32 * w + 16 * n + r;
+                const float gnf = Gat(CH - 1, f);
+                f32x4 kt;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * mt + 4 * g + e;
+                    const float G = Gat(i, f);
+                    kt[e] = KC[mt][n][e] * __expf(gnf - G);
+                    EC[mt][n][e] = KC[mt][n][e] * __expf(G) * sBeta[i];
+                }
+                KC[mt][n] = kt;
+            }
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                ET[n][ks] = pack_pi(EC[2 * ks][n], EC[2 * ks + 1][n]);
+                if (fwdscan)
+                    st_frag(it.KtT + t * (CH * DKD), (2 * w + n) * 2 + ks,
+                            pack_pi(KC[2 * ks][n], KC[2 * ks + 1][n]));
+            }
+        // V * I scaled by beta: Z^T frags of value slab w
+        {
+            f32x4 VC[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 vf = frag_rows(v, 16 * mt, w, 0);
+                VC[mt][0] = mfma(vf, I0, zero4());
+                VC[mt][1] = mfma(vf, I1, zero4());
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) VC[mt][n][e] *= sBeta[16 * mt + 4 * g + e];
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) ZT[n][ks] = pack_pi(VC[2 * ks][n], VC[2 * ks + 1][n]);
+        }
+        if (xy) {
+            f32x4 OC[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 of = frag_rows(dO, 16 * mt, w, 0);
+                OC[mt][0] = mfma(of, I0, zero4());
+                OC[mt][1] = mfma(of, I1, zero4());
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) OT[n][ks] = pack_pi(OC[2 * ks][n], OC[2 * ks + 1][n]);
+        }
+        if (xy || savexy) {
+            // Q * I scaled by gam: Qg^T frags of key slab w
+            f32x4 QC[4][2];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const bf16x8 qf = frag_rows(q, 16 * mt, w, 0);
+                QC[mt][0] = mfma(qf, I0, zero4());
+                QC[mt][1] = mfma(qf, I1, zero4());
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        QC[mt][n][e] *= __expf(Gat(16 * mt + 4 * g + e, 32 * w + 16 * n + r));
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8 fr = pack_pi(QC[2 * ks][n], QC[2 * ks + 1][n]);
+                    const int tl = (2 * w + n) * 2 + ks;
+                    if (xy) sQgT[tl * 64 + l] = fr;
+                    if (savexy) st_frag(it.QgT + t * (CH * DKD), tl, fr);
+                }
+        }
+    }
+    // Kt and Qg frags (M = tok, K = key) straight from the rows
+    if (bwdscan || out) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int id = tid + 256 * u;
+            const int i = id >> 4, f0 = (id & 15) * 8;
+            float kx[8], qx[8];
+            if (bwdscan) load8(k + (int64_t)i * ld + f0, kx);
+            if (out) load8(q + (int64_t)i * ld + f0, qx);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float G = Gat(i, f0 + e);
+                kx[e] *= __expf(Gat(CH - 1, f0 + e) - G);
+                qx[e] *= __expf(G);
+            }
+            if (bwdscan) st_row8_frag(it.Kt + t * (CH * DKD), i, f0, kx);
+            if (out) st_row8_frag(it.Qg + t * (CH * DKD), i, f0, qx);
+        }
+    }
+    __syncthreads();  // sL complete
+
+    // ---- 3. A = (I + L)^{-1}: diagonal 16 x 16 blocks, then block rows ----
+    {
+        // zero the upper blocks of sA
+        for (int e = tid; e < 6 * 256; e += 256) {
+            // upper blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int bk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+            const int bi = bk < 3 ? 0 : bk < 5 ? 1 : 2;
+            const int bj = bi == 0 ? bk + 1 : bi == 1 ? bk - 1 : 3;
+            sA[(16 * bi + rr) * LP + 16 * bj + cc] = 0.f;
+        }
+        if (l < 16) {
+            const int base = 16 * w;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == l) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc -= sL[(base + i) * LP + base + m] * x[m];
+                x[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
+        }
+        __syncthreads();
+        const int jb = w, rr = (tid >> 2) & 15, c4 = (tid & 3) * 4;
         for (int bi = 1; bi < 4; ++bi) {
-            // T_bj = sum_{m in [16 bj, 16 bi)} L[16 bi + r][m] A[m][16 bj + cc]
-            for (int bj = 0; bj < bi; ++bj) {
-                float acc = 0.f;
-                for (int m = 16 * bj; m < 16 * bi; ++m)
-                    acc += sL[(16 * bi + r) * LDF + m] * sAi[m * LDF + 16 * bj + cc];
-                sT[(bj * 16 + r) * 17 + cc] = acc;
+            if (jb < bi) {
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int lb = jb; lb < bi; ++lb) {
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) {
+                        const float lv = sL[(16 * bi + rr) * LP + 16 * lb + m];
+                        const float4 a4 = *(const float4*)&sA[(16 * lb + m) * LP + 16 * jb + c4];
+                        acc.x += lv * a4.x; acc.y += lv * a4.y;
+                        acc.z += lv * a4.z; acc.w += lv * a4.w;
+                    }
+                }
+                *(float4*)&sT[(jb * 16 + rr) * TP + c4] = acc;
             }
             __syncthreads();
-            // A[bi][bj] = -A[bi][bi] T_bj
-            for (int bj = 0; bj < bi; ++bj) {
-                float acc = 0.f;
+            if (jb < bi) {
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    acc += sAi[(16 * bi + r) * LDF + 16 * bi + m] * sT[(bj * 16 + m) * 17 + cc];
-                sAi[(16 * bi + r) * LDF + 16 * bj + cc] = -acc;
+                for (int m = 0; m < 16; ++m) {
+                    const float dv = sA[(16 * bi + rr) * LP + 16 * bi + m];
+                    const float4 t4 = *(const float4*)&sT[(jb * 16 + m) * TP + c4];
+                    acc.x += dv * t4.x; acc.y += dv * t4.y;
+                    acc.z += dv * t4.z; acc.w += dv * t4.w;
+                }
+                *(float4*)&sA[(16 * bi + rr) * LP + 16 * jb + c4] =
+                    make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
             }
             __syncthreads();
         }
     }
 
-    // ---- 5. A to bf16 (zero above the diagonal) ----
-    for (int e = tid; e < CH * CH; e += 256) {
-        const int i = e >> 6, j = e & 63;
-        const float a = (j <= i) ? sAi[i * LDF + j] : 0.f;
-        sAb[i * LD64 + j] = (bf16)a;
-        if (write_A) it.A[(tile * CH + i) * CH + j] = (bf16)a;
-    }
-    __syncthreads();
-
-    // ---- 6. W = A E, U = A Z ----
-    f32x4 aw[4][2], au[4][2];
+    // ---- 5. W = A E, W^T = E^T A^T, U = A Z; A ----
+    {
+        // A frag (M = tok i, K = tok j): rows 16 mt + r, cols 32 ks + pik(g, .)
+        auto afrag = [&](int mt, int ks) -> bf16x8 {
+            const float* row = &sA[(16 * mt + r) * LP + 32 * ks + 4 * g];
+            const float4 lo = *(const float4*)row, hi = *(const float4*)(row + 16);
+            const f32x4 a{lo.x, lo.y, lo.z, lo.w}, bq{hi.x, hi.y, hi.z, hi.w};
+            return pack_pi(a, bq);
+        };
+        bf16x8 AF[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) { aw[mt][nt] = zero4(); au[mt][nt] = zero4(); }
-    wave_gemm<4, 2, CH>(sAb, LD64, 0, sET, LD64, 32 * w, aw);
-    wave_gemm<4, 2, CH>(sAb, LD64, 0, sZT, LD64, 32 * w, au);
-    __syncthreads();  // sET/sZT become staging buffers
-    bf16* stW = sET;  // [64][136] fits in 128 x 72
-    bf16* stU = sZT;
+            for (int ks = 0; ks < 2; ++ks)
+                if (ks == 0 || mt >= 2) AF[mt][ks] = afrag(mt, ks);
+        if (bwdscan) {
+            // W (tok x key) -> -W^T frags (M = key, K = tok)
+            f32x4 WC[4][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            put_c(stW, LD128, 16 * mt, 32 * w + 16 * nt, aw[mt][nt]);
-            put_c(stU, LD128, 16 * mt, 32 * w + 16 * nt, au[mt][nt]);
+                for (int n = 0; n < 2; ++n) {
+                    f32x4 acc = mfma(AF[mt][0], ET[n][0], zero4());
+                    if (mt >= 2) acc = mfma(AF[mt][1], ET[n][1], acc);
+                    WC[mt][n] = acc;
+                }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    st_frag(it.WnT + t * (CH * DKD), (2 * w + n) * 2 + ks,
+                            pack_pi(WC[2 * ks][n], WC[2 * ks + 1][n], -1.f));
         }
-    __syncthreads();
+        if (fwdscan) {
+            // W^T (key x tok) -> -W frags (M = tok, K = key), key slab w
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int id = tid + 256 * u;
-        const int i = id >> 4;
-        const int f0 = (id & 15) * 8;
-        *(bf16x8*)(it.W + (tile * CH + i) * DKD + f0) = *(const bf16x8*)(stW + i * LD128 + f0);
-        *(bf16x8*)(it.U + (tile * CH + i) * DVD + f0) = *(const bf16x8*)(stU + i * LD128 + f0);
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 acc0 = mfma(ET[0][0], AF[mt][0], zero4());
+                f32x4 acc1 = mfma(ET[1][0], AF[mt][0], zero4());
+                if (mt >= 2) {
+                    acc0 = mfma(ET[0][1], AF[mt][1], acc0);
+                    acc1 = mfma(ET[1][1], AF[mt][1], acc1);
+                }
+                st_frag(it.Wn + t * (CH * DKD), mt * 4 + w, pack_pi(acc0, acc1, -1.f));
+            }
+            // U = A Z (tok x value), value slab w -> ctiles
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    f32x4 acc = mfma(AF[mt][0], ZT[n][0], zero4());
+                    if (mt >= 2) acc = mfma(AF[mt][1], ZT[n][1], acc);
+                    *(bf16x4*)ctile_ptr(it.U + t * (CH * DVD), (2 * w + n) * 4 + mt) = pack4(acc);
+                }
+        }
+        if (wantA) {
+            const int row = tid >> 2, c0 = (tid & 3) * 16;
+            float x[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = sA[row * LP + c0 + 8 * hh + e];
+                store8(it.A + (t * CH + row) * CH + c0 + 8 * hh, x);
+            }
+        }
     }
+
+    // ---- 6. X = Hm^T dO, Y = Qg^T dO (value slab w) ----
+    if (xy) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f32x4 acc = zero4();
+                if (mt < 2) acc = mfma(sHmT[(mt * 2 + 0) * 64 + l], OT[n][0], acc);
+                acc = mfma(sHmT[(mt * 2 + 1) * 64 + l], OT[n][1], acc);
+                *(bf16x4*)ctile_ptr(it.X + t * (CH * DVD), (2 * w + n) * 4 + mt) = pack4(acc);
+            }
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                f32x4 acc = mfma(sQgT[(mt * 2 + 0) * 64 + l], OT[n][0], zero4());
+                acc = mfma(sQgT[(mt * 2 + 1) * 64 + l], OT[n][1], acc);
+                *(bf16x4*)ctile_ptr(it.Y + t * (DKD * DVD), (2 * w + n) * 8 + mt) = pack4(acc);
+            }
+    }
+}
+
+// X = Hm^T dO, Y = Qg^T dO from stored Hm^T / Qg^T frags (full-save policy).
+template <typename T>
+__global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
+{
+    const int c = blockIdx.x;
+    const int bh = blockIdx.y;
+    const int64_t b = bh / s.H, hd = bh % s.H;
+    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
+    const int64_t ld = s.H * DVD;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const T* dO = (const T*)in.dO + tok0 * DVD;
+
+    const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
+    f32x4 OC[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        float x[8];
+        ld_plain8(dO, ld, 16 * mt, 32 * w, x);
+        const bf16x8 of = pack8(x);
+        OC[mt][0] = mfma(of, I0, zero4());
+        OC[mt][1] = mfma(of, I1, zero4());
+    }
+    bf16x8 OT[2][2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) OT[n][ks] = pack_pi(OC[2 * ks][n], OC[2 * ks + 1][n]);
+    const bf16* HmT = it.HmT + t * (CH * CH);
+    const bf16* QgT = it.QgT + t * (CH * DKD);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            f32x4 acc = zero4();
+            if (mt < 2) acc = mfma(ld_frag(HmT, mt * 2 + 0), OT[n][0], acc);
+            acc = mfma(ld_frag(HmT, mt * 2 + 1), OT[n][1], acc);
+            *(bf16x4*)ctile_ptr(it.X + t * (CH * DVD), (2 * w + n) * 4 + mt) = pack4(acc);
+        }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            f32x4 acc = mfma(ld_frag(QgT, mt * 2 + 0), OT[n][0], zero4());
+            acc = mfma(ld_frag(QgT, mt * 2 + 1), OT[n][1], acc);
+            *(bf16x4*)ctile_ptr(it.Y + t * (DKD * DVD), (2 * w + n) * 8 + mt) = pack4(acc);
+        }
 }
 
 }  // namespace
 
-hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, bool write_A,
-                       hipStream_t st)
+hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what, hipStream_t st)
 {
     dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
     if (s.f32) {
-        if (s.vec) prep_kernel<float, true><<<grid, 256, 0, st>>>(s, in, it, write_A);
-        else prep_kernel<float, false><<<grid, 256, 0, st>>>(s, in, it, write_A);
+        if (s.vec) prep_kernel<float, true><<<grid, 256, 0, st>>>(s, in, it, what);
+        else prep_kernel<float, false><<<grid, 256, 0, st>>>(s, in, it, what);
     } else {
-        if (s.vec) prep_kernel<bf16, true><<<grid, 256, 0, st>>>(s, in, it, write_A);
-        else prep_kernel<bf16, false><<<grid, 256, 0, st>>>(s, in, it, write_A);
+        if (s.vec) prep_kernel<bf16, true><<<grid, 256, 0, st>>>(s, in, it, what);
+        else prep_kernel<bf16, false><<<grid, 256, 0, st>>>(s, in, it, what);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStream_t st)
+{
+    dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
+    if (s.f32) xy_kernel<float><<<grid, 256, 0, st>>>(s, in, it);
+    else xy_kernel<bf16><<<grid, 256, 0, st>>>(s, in, it);
     return hipGetLastError();
 }
 

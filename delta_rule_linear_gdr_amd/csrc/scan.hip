@@ -1,22 +1,30 @@
 // Inter-chunk state scans of the chunkwise gated delta rule.
 //
-// ReWY paper, Sec. 2.1 and Sec. 3.5 ("The state scan remains serial across
-// chunks and parallel across independent value columns"). The state S is
-// key-major (128 x 128, fp32 in registers); one workgroup owns BV value
-// columns of one head and walks the chunks in order.
+// ReWY paper (paperpeel.com/paper/2611.01940), Sec. 2.1 and Sec. 3.5: the
+// state scan is serial across chunks and parallel across value columns.
+// One workgroup owns 16 value columns of one head and walks the chunks; its
+// four waves hold the 128 x 16 fp32 state, wave w owning key rows
+// [32 w, 32 w + 32) as two accumulator tiles.
 //
-// Forward, per chunk c (onedev.kr summary, "How it works": R = U - W S):
-//   h_c = S;  R_c = U_c - W_c S;  O_c = Qg_c S + Hm_c R_c;
-//   S <- diag(gn_c) S + Kt_c^T R_c
-// Reverse, per chunk c from last to first, with Sb the adjoint of the state
-// at the end of chunk c (paper Sec. 3.1, "State and gate composition": the
-// output and next-state adjoints are summed before the local pullback):
-//   dh_c = Sb;  Rb_c = Hm_c^T dO_c + Kt_c Sb;
-//   Sb <- diag(gn_c) Sb + Qg_c^T dO_c - W_c^T Rb_c
-//
-// Per-chunk tiles are double-buffered in LDS; the next chunk's tiles are read
-// from memory one step ahead. Workgroup -> (head, column slice) mapping keeps
-// all slices of a head on one XCD so they share that XCD's L2.
+// Both directions run the same two-product step (the chunk system of Sec.
+// 2.3, M R = Z - E S with W = A E and U = A Z, as the onedev.kr summary
+// writes it in "How it works"):
+//   forward, chunk c = 0 .. NT-1, state S = h_c:
+//     Z = U - W S            (the correction R_c)
+//     O = Qg S + Hm Z        (optional output)
+//     S <- diag(gn) S + Kt^T Z
+//   reverse, chunk c = NT-1 .. 0, state Sb = adjoint of the state at the end
+//   of chunk c (output and next-state adjoints are summed before the local
+//   pullback, paper Sec. 3.1 "State and gate composition"):
+//     Z = Hm^T dO + Kt Sb    (the correction adjoint Rb_c)
+//     Sb <- diag(gn) Sb + Qg^T dO - W^T Z
+// Per step: A1 (16 x 128 per wave) times the state slabs, then A2 (32 x 64
+// per wave) times the Z slabs. The chunk operands arrive pre-swizzled in
+// frag/ctile order (kernels.h) and are prefetched three chunks ahead into
+// registers; the only on-chip exchange is the state and Z slabs through LDS
+// (one 16-byte write and a few 16-byte reads per lane, two barriers).
+// The blockIdx -> (head, slice) map keeps the eight slices of a head on one
+// XCD so they share its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,8 +32,7 @@ namespace gdr {
 
 namespace {
 
-constexpr int BV = 16;         // value columns per workgroup
-constexpr int NV = DVD / BV;   // workgroups per head
+constexpr int NVS = DVD / 16;  // value slices (workgroups) per head
 
 __device__ __forceinline__ void map_block(int nblk, int& bh, int& vs)
 {
@@ -34,314 +41,168 @@ __device__ __forceinline__ void map_block(int nblk, int& bh, int& vs)
         const int per = nblk / 8;
         id = (id % 8) * per + id / 8;
     }
-    bh = id / NV;
-    vs = id % NV;
+    bh = id / NVS;
+    vs = id % NVS;
 }
 
-// Read a 64 x 128 bf16 tile: each thread holds 4 chunks of 8 elements.
-struct Tile64x128 {
-    bf16x8 x[4];
-    __device__ void load(const bf16* src)
-    {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            x[u] = *(const bf16x8*)(src + (id >> 4) * 128 + (id & 15) * 8);
-        }
-    }
-    __device__ void store_rows(bf16* dst, int ld) const
-    {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            *(bf16x8*)(dst + (id >> 4) * ld + (id & 15) * 8) = x[u];
-        }
-    }
-    // dst[col][row] (transposed), optionally negated.
-    __device__ void store_cols(bf16* dst, int ld, bool neg = false) const
-    {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            const int i = id >> 4, f0 = (id & 15) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[(f0 + e) * ld + i] = neg ? (bf16)(-(float)x[u][e]) : x[u][e];
-        }
-    }
+template <bool BWD, bool OUT>
+struct Ops {
+    bf16x8 a1[4];     // A1 tiles (mt = w, ks = 0..3)
+    bf16x8 a2[2][2];  // A2 tiles (mt = 2w + m, ks = 0..1)
+    bf16x4 c1;        // C1 ctile (nt = vs, mt = w)
+    bf16x4 c2[2];     // C2 ctiles (nt = vs, mt = 2w + m)      (reverse)
+    float4 gn[2];     // gn for keys 32w + 16m + 4g .. +3
+    bf16x8 qg[4];     // Qg tiles (mt = w, ks = 0..3)          (output)
+    bf16x8 hm[2];     // Hm tiles (mt = w, ks = 0..1)          (output)
 };
 
-// Read a 64 x 64 bf16 tile: each thread holds 2 chunks of 8 elements.
-struct Tile64x64 {
-    bf16x8 x[2];
-    __device__ void load(const bf16* src)
-    {
+template <bool BWD, bool OUT>
+__device__ __forceinline__ void load_ops(Ops<BWD, OUT>& o, const bf16* A1, const bf16* A2,
+                                         const bf16* C1, const bf16* C2, const float* gn,
+                                         const bf16* Qg, const bf16* Hm, int64_t t, int w, int vs)
+{
+    const int g = lane_g();
+    const bf16* a1 = A1 + t * (CH * DKD);
+    const bf16* a2 = A2 + t * (CH * DKD);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            x[u] = *(const bf16x8*)(src + (id >> 3) * 64 + (id & 7) * 8);
-        }
+    for (int ks = 0; ks < 4; ++ks) o.a1[ks] = ld_frag(a1, w * 4 + ks);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o.a2[m][ks] = ld_frag(a2, (2 * w + m) * 2 + ks);
+    o.c1 = *(const bf16x4*)ctile_ptr(C1 + t * (CH * DVD), vs * 4 + w);
+    if (BWD) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            o.c2[m] = *(const bf16x4*)ctile_ptr(C2 + t * (DKD * DVD), vs * 8 + 2 * w + m);
     }
-    __device__ void store_rows(bf16* dst, int ld) const
-    {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            *(bf16x8*)(dst + (id >> 3) * ld + (id & 7) * 8) = x[u];
-        }
+    for (int m = 0; m < 2; ++m) o.gn[m] = *(const float4*)(gn + t * DKD + 32 * w + 16 * m + 4 * g);
+    if (OUT) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o.qg[ks] = ld_frag(Qg + t * (CH * DKD), w * 4 + ks);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) o.hm[ks] = ld_frag(Hm + t * (CH * CH), w * 2 + ks);
     }
-    __device__ void store_cols(bf16* dst, int ld) const
-    {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int id = threadIdx.x + 256 * u;
-            const int i = id >> 3, j0 = (id & 7) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[(j0 + e) * ld + i] = x[u][e];
-        }
-    }
-};
+}
 
-// ---------------------------------------------------------------- forward
-
-template <typename T>
-__global__ __launch_bounds__(256) void scan_fwd_kernel(Shape s, Inputs in, Inter it, T* o, float* ht)
+template <bool BWD, bool OUT, typename T>
+__global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it, T* o, float* fin)
 {
     int bh, vs;
-    map_block((int)(s.B * s.H * NV), bh, vs);
-    const int64_t b = bh / s.H, h = bh % s.H;
-    const int v0 = vs * BV;
+    map_block((int)(s.B * s.H * NVS), bh, vs);
+    const int64_t b = bh / s.H, hd = bh % s.H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l = lane_id();
-    const bool out = (o != nullptr);
+    const int l = lane_id(), r = lane_r(), g = lane_g();
+    const int NT = (int)s.NT;
+    const int v = 16 * vs + r;  // this lane's value column
 
-    __shared__ __attribute__((aligned(16))) bf16 sW[2][CH * LD128];
-    __shared__ __attribute__((aligned(16))) bf16 sKtT[2][DKD * LD64];
-    __shared__ __attribute__((aligned(16))) bf16 sQg[2][CH * LD128];
-    __shared__ __attribute__((aligned(16))) bf16 sHm[2][CH * LD64];
-    __shared__ __attribute__((aligned(16))) bf16 sSt[BV * LD128];
-    __shared__ __attribute__((aligned(16))) bf16 sRt[BV * LD64];
+    __shared__ bf16x8 sS[4][64];  // state slabs: B operands over keys
+    __shared__ bf16x8 sZ[2][64];  // Z slabs: B operands over tokens
 
-    // state: wave w owns key rows [32w, 32w + 32), two 16-row tiles
+    const bf16* A1 = BWD ? it.Kt : it.Wn;
+    const bf16* A2 = BWD ? it.WnT : it.KtT;
+    const bf16* C1 = BWD ? it.X : it.U;
+    const bf16* C2 = it.Y;
+    bf16* Sout = BWD ? it.dh : it.h;
+    bf16* Zout = BWD ? it.Rb : it.R;
+    const float* init = BWD ? in.dht : in.h0;
+
     f32x4 S[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dk = crow(32 * w + 16 * m, r);
-            S[m][r] = in.h0 ? in.h0[((int64_t)bh * DKD + dk) * DVD + v0 + ccol(0)] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i)
+            S[m][i] = init ? init[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] : 0.f;
 
-    Tile64x128 pW, pKt, pQg;
-    Tile64x64 pHm;
-    auto fetch = [&](int c) {
-        const int64_t tile = (int64_t)bh * s.NT + c;
-        pW.load(it.W + tile * CH * DKD);
-        pKt.load(it.Kt + tile * CH * DKD);
-        if (out) {
-            pQg.load(it.Qg + tile * CH * DKD);
-            pHm.load(it.Hm + tile * CH * CH);
-        }
-    };
-    auto stash = [&](int buf) {
-        pW.store_rows(sW[buf], LD128);
-        pKt.store_cols(sKtT[buf], LD64);
-        if (out) {
-            pQg.store_rows(sQg[buf], LD128);
-            pHm.store_rows(sHm[buf], LD64);
-        }
-    };
+    auto chunk = [&](int p) { return BWD ? NT - 1 - p : p; };
+    auto tile = [&](int c) { return (int64_t)bh * s.NT + c; };
 
-    fetch(0);
-    stash(0);
-    if (s.NT > 1) fetch(1);
-
-    for (int c = 0; c < s.NT; ++c) {
-        const int cur = c & 1;
-        const int64_t tile = (int64_t)bh * s.NT + c;
-        // U rows of this wave's R tile, and gn of this wave's key rows
-        float u4[4], gnr[2][4];
+    auto step = [&](const Ops<BWD, OUT>& op, int c) {
+        const int64_t t = tile(c);
+        // state before the update (h_c, or dh_c = adjoint at the chunk end)
+        if (Sout) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            u4[r] = (float)it.U[(tile * CH + crow(16 * w, r)) * DVD + v0 + ccol(0)];
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+                for (int i = 0; i < 4; ++i)
+                    Sout[(t * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = (bf16)S[m][i];
+        }
+        sS[w][l] = pack_pi(S[0], S[1]);
+        __syncthreads();
+        bf16x8 sf[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) gnr[m][r] = it.gn[tile * DKD + crow(32 * w + 16 * m, r)];
-
-        // 1. state to LDS (S^T, bf16) and to memory
+        for (int ks = 0; ks < 4; ++ks) sf[ks] = sS[ks][l];
+        // Z = C1 + A1 S   (rows 16w .. 16w + 15)
+        f32x4 z = unpack4(op.c1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) z = mfma(op.a1[ks], sf[ks], z);
+        f32x4 oacc = zero4();
+        if (OUT) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) oacc = mfma(op.qg[ks], sf[ks], oacc);
+        }
+        if (Zout) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Zout[(t * CH + 16 * w + 4 * g + i) * DVD + v] = (bf16)z[i];
+        }
+        *(bf16x4*)((bf16*)&sZ[w >> 1][l] + 4 * (w & 1)) = pack4(z);
+        __syncthreads();
+        bf16x8 zf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) zf[ks] = sZ[ks][l];
+        // S <- gn S (+ C2) + A2 Z
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            put_c_t(sSt, LD128, 32 * w + 16 * m, 0, S[m]);
-            if (it.h)
+            const float gv[4] = {op.gn[m].x, op.gn[m].y, op.gn[m].z, op.gn[m].w};
+            f32x4 acc;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    it.h[(tile * DKD + crow(32 * w + 16 * m, r)) * DVD + v0 + ccol(0)] = (bf16)S[m][r];
+            for (int i = 0; i < 4; ++i) acc[i] = gv[i] * S[m][i];
+            if (BWD) {
+                const f32x4 y = unpack4(op.c2[m]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += y[i];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mfma(op.a2[m][ks], zf[ks], acc);
+            S[m] = acc;
         }
-        __syncthreads();
-
-        // 2. R = U - W S   (rows 16w .. 16w+15)
-        f32x4 acc[1][1];
+        if (OUT) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[0][0][r] = -u4[r];
-        wave_gemm<1, 1, DKD>(sW[cur], LD128, 16 * w, sSt, LD128, 0, acc);
-        f32x4 R;
+            for (int ks = 0; ks < 2; ++ks) oacc = mfma(op.hm[ks], zf[ks], oacc);
+            const int64_t tok0 = (b * s.T + (int64_t)c * CH + 16 * w + 4 * g) * s.H + hd;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) R[r] = -acc[0][0][r];
-        put_c_t(sRt, LD64, 16 * w, 0, R);
-        if (it.R)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                it.R[(tile * CH + crow(16 * w, r)) * DVD + v0 + ccol(0)] = (bf16)R[r];
-        f32x4 oacc[1][1] = {{zero4()}};
-        if (out) wave_gemm<1, 1, DKD>(sQg[cur], LD128, 16 * w, sSt, LD128, 0, oacc);
-        __syncthreads();
-
-        // 3. S <- diag(gn) S + Kt^T R ;  O += Hm R
-        f32x4 sacc[2][1];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[m][0][r] = S[m][r] * gnr[m][r];
-        wave_gemm<2, 1, CH>(sKtT[cur], LD64, 32 * w, sRt, LD64, 0, sacc);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) S[m] = sacc[m][0];
-        if (out) {
-            wave_gemm<1, 1, CH>(sHm[cur], LD64, 16 * w, sRt, LD64, 0, oacc);
-            const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + h;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                io<T>::st(o + (tok0 + (int64_t)crow(16 * w, r) * s.H) * DVD + v0 + ccol(0), oacc[0][0][r]);
-        }
-
-        // 4. next chunk's tiles into the other buffer; fetch the one after
-        if (c + 1 < s.NT) {
-            stash(cur ^ 1);
-            if (c + 2 < s.NT) fetch(c + 2);
-        }
-    }
-    if (ht)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                ht[((int64_t)bh * DKD + crow(32 * w + 16 * m, r)) * DVD + v0 + ccol(0)] = S[m][r];
-}
-
-// ---------------------------------------------------------------- reverse
-
-template <typename T>
-__global__ __launch_bounds__(256) void scan_bwd_kernel(Shape s, Inputs in, Inter it, float* dh0)
-{
-    int bh, vs;
-    map_block((int)(s.B * s.H * NV), bh, vs);
-    const int64_t b = bh / s.H, h = bh % s.H;
-    const int v0 = vs * BV;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int tid = threadIdx.x;
-
-    __shared__ __attribute__((aligned(16))) bf16 sKt[2][CH * LD128];
-    __shared__ __attribute__((aligned(16))) bf16 sHT[2][CH * LD64];
-    __shared__ __attribute__((aligned(16))) bf16 sQgT[2][DKD * LD64];
-    __shared__ __attribute__((aligned(16))) bf16 sWT[2][DKD * LD64];  // holds -W^T
-    __shared__ __attribute__((aligned(16))) bf16 sObT[2][BV * LD64];
-    __shared__ __attribute__((aligned(16))) bf16 sSbt[BV * LD128];
-    __shared__ __attribute__((aligned(16))) bf16 sRbt[BV * LD64];
-
-    f32x4 Sb[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int dk = crow(32 * w + 16 * m, r);
-            Sb[m][r] = in.dht ? in.dht[((int64_t)bh * DKD + dk) * DVD + v0 + ccol(0)] : 0.f;
-        }
-
-    const T* dO = (const T*)in.dO;
-    Tile64x128 pKt, pQg, pW;
-    Tile64x64 pHm;
-    float pO[8];  // dO slice: threads < 128 hold 8 values of one row
-    auto fetch = [&](int c) {
-        const int64_t tile = (int64_t)bh * s.NT + c;
-        pKt.load(it.Kt + tile * CH * DKD);
-        pQg.load(it.Qg + tile * CH * DKD);
-        pW.load(it.W + tile * CH * DKD);
-        pHm.load(it.Hm + tile * CH * CH);
-        if (tid < CH * BV / 8) {
-            const int i = tid / (BV / 8), e0 = (tid % (BV / 8)) * 8;
-            const int64_t tok = (b * s.T + (int64_t)c * CH + i) * s.H + h;
-            load8(dO + tok * DVD + v0 + e0, pO);
-        }
-    };
-    auto stash = [&](int buf) {
-        pKt.store_rows(sKt[buf], LD128);
-        pQg.store_cols(sQgT[buf], LD64);
-        pW.store_cols(sWT[buf], LD64, true);
-        pHm.store_cols(sHT[buf], LD64);
-        if (tid < CH * BV / 8) {
-            const int i = tid / (BV / 8), e0 = (tid % (BV / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sObT[buf][(e0 + e) * LD64 + i] = (bf16)pO[e];
+            for (int i = 0; i < 4; ++i) io<T>::st(o + (tok0 + (int64_t)i * s.H) * DVD + v, oacc[i]);
         }
     };
 
-    const int NT = (int)s.NT;
-    fetch(NT - 1);
-    stash((NT - 1) & 1);
-    if (NT > 1) fetch(NT - 2);
-
-    for (int c = NT - 1; c >= 0; --c) {
-        const int cur = c & 1;
-        const int64_t tile = (int64_t)bh * s.NT + c;
-        float gnr[2][4];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) gnr[m][r] = it.gn[tile * DKD + crow(32 * w + 16 * m, r)];
-
-        // 1. dh_c = Sb
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            put_c_t(sSbt, LD128, 32 * w + 16 * m, 0, Sb[m]);
-            if (it.dh)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    it.dh[(tile * DKD + crow(32 * w + 16 * m, r)) * DVD + v0 + ccol(0)] = (bf16)Sb[m][r];
+    // three register sets of chunk operands in flight
+    Ops<BWD, OUT> P0, P1, P2;
+    auto load = [&](Ops<BWD, OUT>& op, int p) {
+        load_ops<BWD, OUT>(op, A1, A2, C1, C2, it.gn, it.Qg, it.Hm, tile(chunk(p)), w, vs);
+    };
+    load(P0, 0);
+    if (NT > 1) load(P1, 1);
+    if (NT > 2) load(P2, 2);
+    for (int p = 0; p < NT; p += 3) {
+        step(P0, chunk(p));
+        if (p + 3 < NT) load(P0, p + 3);
+        if (p + 1 < NT) {
+            step(P1, chunk(p + 1));
+            if (p + 4 < NT) load(P1, p + 4);
         }
-        __syncthreads();
-
-        // 2. Rb = Kt Sb + Hm^T dO   (rows 16w .. 16w+15)
-        f32x4 racc[1][1] = {{zero4()}};
-        wave_gemm<1, 1, DKD>(sKt[cur], LD128, 16 * w, sSbt, LD128, 0, racc);
-        wave_gemm<1, 1, CH>(sHT[cur], LD64, 16 * w, sObT[cur], LD64, 0, racc);
-        put_c_t(sRbt, LD64, 16 * w, 0, racc[0][0]);
-        if (it.Rb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                it.Rb[(tile * CH + crow(16 * w, r)) * DVD + v0 + ccol(0)] = (bf16)racc[0][0][r];
-        __syncthreads();
-
-        // 3. Sb <- diag(gn) Sb + Qg^T dO - W^T Rb
-        f32x4 sacc[2][1];
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[m][0][r] = Sb[m][r] * gnr[m][r];
-        wave_gemm<2, 1, CH>(sQgT[cur], LD64, 32 * w, sObT[cur], LD64, 0, sacc);
-        wave_gemm<2, 1, CH>(sWT[cur], LD64, 32 * w, sRbt, LD64, 0, sacc);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) Sb[m] = sacc[m][0];
-
-        if (c - 1 >= 0) {
-            stash(cur ^ 1);
-            if (c - 2 >= 0) fetch(c - 2);
+        if (p + 2 < NT) {
+            step(P2, chunk(p + 2));
+            if (p + 5 < NT) load(P2, p + 5);
         }
     }
-    if (dh0)
+    if (fin) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dh0[((int64_t)bh * DKD + crow(32 * w + 16 * m, r)) * DVD + v0 + ccol(0)] = Sb[m][r];
+            for (int i = 0; i < 4; ++i)
+                fin[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = S[m][i];
+    }
 }
 
 }  // namespace
@@ -349,18 +210,21 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(Shape s, Inputs in, Inter
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o, float* ht,
                            hipStream_t st)
 {
-    const unsigned nblk = (unsigned)(s.B * s.H * NV);
-    if (s.f32) scan_fwd_kernel<float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
-    else scan_fwd_kernel<bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
+    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    if (o) {
+        if (s.f32) scan_kernel<false, true, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
+        else scan_kernel<false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
+    } else {
+        scan_kernel<false, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, ht);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                            hipStream_t st)
 {
-    const unsigned nblk = (unsigned)(s.B * s.H * NV);
-    if (s.f32) scan_bwd_kernel<float><<<nblk, 256, 0, st>>>(s, in, it, dh0);
-    else scan_bwd_kernel<bf16><<<nblk, 256, 0, st>>>(s, in, it, dh0);
+    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    scan_kernel<true, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, dh0);
     return hipGetLastError();
 }
 

@@ -41,14 +41,20 @@ def _ws(d, policy=0):
 
 
 def test_workspace_sizes():
+    T64x128, T128x128, T64x64, GN = 16384, 32768, 8192, 512
     rc, sv, sc = _ws(_desc(T=8192, H=16), 0)
     assert rc == 0 and sv == 0
-    # recompute scratch holds every per-chunk intermediate of the backward:
-    # W,U,Kt,Qg,R,Rb 16 KiB, A,Hm 8 KiB, gn 512 B, h,dh 32 KiB per (chunk, head)
-    assert sc == 2048 * (6 * 16384 + 2 * 8192 + 512 + 2 * 32768)
+    # recompute: the backward holds the forward-scan operands (-W, Kt^T, U, gn),
+    # the reverse-scan operands (Kt, -W^T, X, Y), A, and the per-chunk h, R,
+    # dh, Rb of every (chunk, head)
+    per = 3 * T64x128 + GN + 2 * T64x128 + T64x64 + T128x128 + T64x128 \
+        + T64x128 + T128x128 + T128x128 + T64x128
+    assert sc == 2048 * per
     rc, sv, sc = _ws(_desc(T=8192, H=16), 1)
     assert rc == 0
-    assert sv == 2048 * (8192 + 16384 + 8192 + 16384 + 16384 + 512 + 32768 + 16384)
+    # full save keeps A, Kt, -W^T, gn, Hm^T, Qg^T, h, R
+    assert sv == 2048 * (T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
+    assert sc == 2048 * max(4 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128)
 
 
 @pytest.mark.parametrize("kw,status", [
