@@ -2,7 +2,8 @@
 // (chunk, head), after the reverse state scan has produced Rb (the summed
 // correction adjoint) and dh (the adjoint of the state at the chunk end).
 //
-// Producer (ReWY paper, Sec. 3.1, and the onedev.kr summary, "How it works"):
+// Producer (ReWY paper, paperpeel.com/paper/2611.01940, Sec. 3.1, and the
+// onedev.kr summary, "How it works"):
 //   P = A^T Rb;  dv = beta * P;  D = -strict_lower(P R^T);  Eb_dir = -P h^T
 // Output coefficient adjoint: Hb = lower_incl(dO R^T).
 // State-direct terms: Qgb = dO h^T, Ktb = R dh^T (paper Sec. 3.5: the joint
@@ -21,16 +22,23 @@
 //     dbeta += <U_e, alpha k>, Gbar += Q' U_q + E' U_e - Y' U_y
 // Feature-local chain rules for the remaining terms, with gam = exp(G):
 //   dq += gam Qgb;  dk += beta gam Eb_dir + exp(G_n - G) Ktb;
-//   dbeta += <P, v> + <Eb_dir, gam k>   (undivided, App. B.3)
+//   dbeta += <P, v> + <Eb_dir, gam k>   (undivided form, App. B.3)
 //   Gbar += gam q Qgb + beta gam k Eb_dir - exp(G_n - G) k Ktb;
 //   Gbar_n += sum_j exp(G_n - G_j) k_j Ktb_j + gam_n rowsum(h o dh)
 // and dg is the chunk-local reverse cumsum of Gbar (Sec. 3.5), summed over
 // features for a scalar gate (App. E.1).
 //
-// The expanded seven-product producer (Sec. 2.3, "conventional WY
-// backward"; onedev.kr: Wb = -Rb S^T, Ab = Rb Z^T + Wb E^T, -A^T Ab A^T) is a
-// compile-time variant used only for the ablation; everything after the
-// producer is shared.
+// Schedule (eight waves; wave w owns feature tile [16 w, 16 w + 16) of
+// every 64 x 128 product, all 64 token rows, so the chain rules and the
+// gradient accumulators stay in that wave's registers):
+//   1. P^T = Rb^T A from the Rb accumulator tiles (no transpose needed);
+//      dv and <P, v> from it; P, R, dO fragments (contraction over values)
+//      into LDS; h, dh fragments and the rowsum of h o dh in registers;
+//      K, Q in accumulator order through K * I (exact).
+//   2. D, D^T, Hb, Hb^T tiles (contraction over values) into LDS as the
+//      A operands of the Gram / matrix-intra products; Eb_dir, Qgb, Ktb.
+//   3. The four consumer products; reductions of dbeta and dg.
+// Orientation changes use MFMA products with the identity, which are exact.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,415 +46,437 @@ namespace gdr {
 
 namespace {
 
-constexpr int SZ_T128 = CH * LD128 * 2;   // 64 x 136 bf16 = 17408 B
-constexpr int SZ_TT = DKD * LD64 * 2;     // 128 x 72 bf16 = 18432 B
-constexpr int SZ_T64 = CH * LD64 * 2;     // 64 x 72 bf16  = 9216 B
-constexpr int R1_BYTES = 3 * SZ_TT;       // >= 3 * SZ_T128 and >= 64 x 129 fp32
-constexpr int R2_BYTES = 4 * SZ_T64;      // >= SZ_T64 + SZ_TT
+constexpr int NW = 8;
+constexpr int NTHR = 64 * NW;
 
-template <typename T>
-__device__ __forceinline__ float ldT(const T* p) { return io<T>::ld(p); }
-
-// Eight waves; wave w owns the 16 feature columns [16w, 16w + 16) of every
-// 64 x 128 product (all 64 rows), so the per-element chain rules and the
-// gradient accumulators stay in that wave's registers.
-constexpr int NWAVE = 8;
-constexpr int NTHR = 64 * NWAVE;
+__device__ __forceinline__ void st_half(bf16x8* buf, int tile, int half, const bf16x4& v)
+{
+    *(bf16x4*)((bf16*)&buf[tile * 64 + lane_id()] + 4 * half) = v;
+}
 
 template <typename T, bool VEC, bool WY7>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr)
 {
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
-    const int64_t b = bh / s.H, h = bh % s.H;
-    const int64_t tile = (int64_t)bh * s.NT + c;
-    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + h;
-    const int64_t rs = s.H;
+    const int64_t b = bh / s.H, hd = bh % s.H;
+    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
+    // Row stride (elements) of q, k, v, dO and their gradients. In-chunk
+    // offsets stay below 64 * H * 128 < 2^31 (H <= 65535), so they are 32-bit
+    // and every pointer below is a uniform per-chunk base.
+    const int ld = (int)(s.H * DKD);
+    const int Hs = (int)s.H;
     const int tid = threadIdx.x;
-    const int l = lane_id();
+    const int l = lane_id(), r = lane_r(), g = lane_g();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int f = 16 * w + (l & 15);  // this lane's feature column in every 64 x 128 product
+    const int f = 16 * w + r;  // this lane's feature (key or value) column
 
-    constexpr int GSZ = VEC ? CH * DKD : CH;
-    __shared__ float sG[GSZ];
-    __shared__ float sCen[DKD];
-    __shared__ float sBeta[CH];
-    __shared__ float sRedB[NWAVE][CH];
-    __shared__ float sRedG[NWAVE][CH];
+    __shared__ bf16x8 lP[16 * 64], lR[16 * 64], lO[16 * 64];  // frags M = 64 tok, K = 128 val
+    __shared__ bf16x8 lGm[8 * 64], lGT[8 * 64], lGq[8 * 64], lGqT[8 * 64];  // frags 64 x 64
+    __shared__ float sG[CH], sBeta[CH];
+    __shared__ float sRedB[NW][CH], sRedP[NW][CH], sRedG[NW][CH];
     __shared__ float sExtra[DKD];
-    __shared__ __attribute__((aligned(16))) char R1[R1_BYTES];
-    __shared__ __attribute__((aligned(16))) char R2[R2_BYTES];
-    bf16* Ol = (bf16*)(R1);
-    bf16* Rl = (bf16*)(R1 + SZ_T128);
-    bf16* Pl = (bf16*)(R1 + 2 * SZ_T128);
-    bf16* sAT = (bf16*)(R2);
-    bf16* sRbT = (bf16*)(R2 + SZ_T64);
-    bf16* C1 = (bf16*)(R2);
-    bf16* C2 = (bf16*)(R2 + SZ_T64);
-    bf16* C3 = (bf16*)(R2 + 2 * SZ_T64);
-    bf16* C4 = (bf16*)(R2 + 3 * SZ_T64);
-    bf16* B1 = (bf16*)(R1);
-    bf16* B2 = (bf16*)(R1 + SZ_TT);
-    bf16* B3 = (bf16*)(R1 + 2 * SZ_TT);
+    __shared__ float sEx[NW];
 
-    const T* q = (const T*)in.q;
-    const T* k = (const T*)in.k;
-    const T* v = (const T*)in.v;
-    const T* dO = (const T*)in.dO;
-    const T* beta = (const T*)in.beta;
-    const bf16* hg = it.h + tile * DKD * DVD;
-    const bf16* dhg = it.dh + tile * DKD * DVD;
+    const T* q = (const T*)in.q + tok0 * DKD;
+    const T* k = (const T*)in.k + tok0 * DKD;
+    const T* v = (const T*)in.v + tok0 * DVD;
+    const T* dO = (const T*)in.dO + tok0 * DVD;
+    const float* gin = in.g + (VEC ? tok0 * DKD : tok0);
+    T* dqo = (T*)gr.dq + tok0 * DKD;
+    T* dko = (T*)gr.dk + tok0 * DKD;
+    T* dvo = (T*)gr.dv + tok0 * DVD;
+    float* dgo = gr.dg + (VEC ? tok0 * DKD : tok0);
+    const T* betai = (const T*)in.beta + tok0;
+    T* dbo = (T*)gr.dbeta + tok0;
 
-    // ---- S0: gate cumsum, beta, operand tiles ----
+    // ---- 0. gates, beta; zero the consumer operand buffers ----
+    float Gv[4][4];  // vector gate: G at (tok 16 it + 4 g + e, f)
+    float Gnf, cen = 0.f;
+    if (tid < CH) sBeta[tid] = io<T>::ld(betai + tid * Hs);
     if (VEC) {
-        if (tid < DKD) {
-            float acc = 0.f, mx = -INFINITY, mn = INFINITY;
-            for (int i = 0; i < CH; ++i) {
-                acc += in.g[(tok0 + i * rs) * DKD + tid];
-                sG[i * DKD + tid] = acc;
-                mx = fmaxf(mx, acc);
-                mn = fminf(mn, acc);
+        float x[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[m][e] = gin[(16 * m + 4 * g + e) * ld + f];
+        float base = 0.f, mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+            for (int e = 1; e < 4; ++e) x[m][e] += x[m][e - 1];
+            const float tot = x[m][3];
+            float incl = tot;
+            float y = __shfl_up(incl, 16);
+            if (g >= 1) incl += y;
+            y = __shfl_up(incl, 32);
+            if (g >= 2) incl += y;
+            const float tile_tot = __shfl(incl, 48 + r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Gv[m][e] = x[m][e] + (incl - tot) + base;
+                mx = fmaxf(mx, Gv[m][e]);
+                mn = fminf(mn, Gv[m][e]);
             }
-            sCen[tid] = 0.5f * (mx + mn);
+            base += tile_tot;
         }
+        Gnf = __shfl(Gv[3][3], 48 + r);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mn = fminf(mn, __shfl_xor(mn, 16));
+        mn = fminf(mn, __shfl_xor(mn, 32));
+        cen = 0.5f * (mx + mn);
     } else if (w == 0) {
-        float x = in.g[tok0 + l * rs];
+        float x = gin[l * Hs];
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            float y = __shfl_up(x, off);
+            const float y = __shfl_up(x, off);
             if (l >= off) x += y;
         }
         sG[l] = x;
     }
-    if (tid < CH) sBeta[tid] = ldT(beta + tok0 + tid * rs);
+    {
+        const bf16x8 z8 = {};
+        bf16x8* zb[4] = {lGm, lGT, lGq, lGqT};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int id = tid + NTHR * u;
-        const int i = id >> 4, f0 = (id & 15) * 8;
+        for (int u = 0; u < 4; ++u) zb[u][tid] = z8;
+    }
+    __syncthreads();
+    if (!VEC) Gnf = sG[CH - 1];
+    // G at this lane's accumulator position (tok 16 m + 4 g + e, f)
+    auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : sG[16 * m + 4 * g + e]; };
+
+    const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
+    const bf16x8 Iw = (w & 1) ? I1 : I0;
+    const bf16x8 Ipw = ident_pi(w & 1);
+    const bf16x4 z4 = {};
+
+    // ---- 1a. P^T = Rb^T A for value tile w ----
+    {
+        const bf16* Rb = it.Rb + t * (CH * DVD);
+        const bf16* AT = it.AT + t * (CH * CH);
+        bf16x8 RbT[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            RbT[ks] = cat8(*(const bf16x4*)ctile_ptr(Rb, w * 4 + 2 * ks),
+                           *(const bf16x4*)ctile_ptr(Rb, w * 4 + 2 * ks + 1));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // A^T is upper triangular in (i, j): token slab 0 only reaches i < 32
+            f32x4 acc = mfma(RbT[1], ld_frag(AT, m * 2 + 1), zero4());
+            if (m < 2) acc = mfma(RbT[0], ld_frag(AT, m * 2 + 0), acc);
+            // lane: P[tok 16 m + r][val 16 w + 4 g + e]
+            const int i = 16 * m + r;
+            const float bt = sBeta[i];
+            float dvv[4], vx[4];
+            load4(v + i * ld + 16 * w + 4 * g, vx);
+            float pv = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dvv[e] = bt * acc[e];
+                pv += acc[e] * vx[e];
+            }
+            store4(dvo + i * ld + 16 * w + 4 * g, dvv);
+            pv += __shfl_xor(pv, 16);
+            pv += __shfl_xor(pv, 32);
+            if (g == 0) sRedP[w][i] = pv;
+            st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
+        }
+    }
+    // ---- 1b. R and dO fragments (contraction over values) of value tile w ----
+    {
+        const bf16* Rr = it.R + t * (CH * DVD);
+        bf16x8 RT[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            RT[ks] = cat8(*(const bf16x4*)ctile_ptr(Rr, w * 4 + 2 * ks),
+                          *(const bf16x4*)ctile_ptr(Rr, w * 4 + 2 * ks + 1));
+        const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // lane: R[tok 16 m + r][val 16 w + 4 g + e]
+            const f32x4 cc = mfma(RT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
+            st_half(lR, m * 4 + (w >> 1), w & 1, pack4(cc));
+            float ox[4];
+            load4(dO + (16 * m + r) * ld + 16 * w + 4 * g, ox);
+            bf16x4 o4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o4[e] = (bf16)ox[e];
+            st_half(lO, m * 4 + (w >> 1), w & 1, o4);
+        }
+    }
+    // ---- 1c. h, dh fragments (M = key tile w, K = values); rowsum(h o dh) ----
+    bf16x8 hF[4], dhF[4];
+    {
+        const bf16* hb = it.h + t * (DKD * DVD);
+        const bf16* dhb = it.dh + t * (DKD * DVD);
+        float hdp[4] = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Ch[8], Cd[8];
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) {
+            // lane: h[key 16 w + 4 g + e][val 16 vt + r]
+            const bf16x4 hv = *(const bf16x4*)ctile_ptr(hb, vt * 8 + w);
+            const bf16x4 dv4 = *(const bf16x4*)ctile_ptr(dhb, vt * 8 + w);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) hdp[e] += (float)hv[e] * (float)dv4[e];
+            // lane: h[key 16 w + r][val 16 vt + 4 g + e]
+            Ch[vt] = mfma((w & 1) ? cat8(z4, hv) : cat8(hv, z4), Ipw, zero4());
+            Cd[vt] = mfma((w & 1) ? cat8(z4, dv4) : cat8(dv4, z4), Ipw, zero4());
+        }
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            hF[sl] = pack_pi(Ch[2 * sl], Ch[2 * sl + 1]);
+            dhF[sl] = pack_pi(Cd[2 * sl], Cd[2 * sl + 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = sum16(hdp[e]);
+            if (r == 0) sExtra[16 * w + 4 * g + e] = x;
+        }
+    }
+    // ---- 1d. K and Q in accumulator order (tok 16 m + 4 g + e, key f) ----
+    f32x4 KC[4], QC[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
         float x[8];
-        load8(dO + (tok0 + i * rs) * DVD + f0, x);
-        *(bf16x8*)(Ol + i * LD128 + f0) = pack8(x);
-        *(bf16x8*)(Rl + i * LD128 + f0) = *(const bf16x8*)(it.R + (tile * CH + i) * DVD + f0);
-        const bf16x8 rb = *(const bf16x8*)(it.Rb + (tile * CH + i) * DVD + f0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sRbT[(f0 + e) * LD64 + i] = rb[e];
+        ld_plain8(k, ld, 16 * m, 32 * (w >> 1), x);
+        KC[m] = mfma(pack8(x), Iw, zero4());
+        ld_plain8(q, ld, 16 * m, 32 * (w >> 1), x);
+        QC[m] = mfma(pack8(x), Iw, zero4());
     }
-    {
-        const int i = tid >> 3, j0 = (tid & 7) * 8;
-        const bf16x8 a = *(const bf16x8*)(it.A + (tile * CH + i) * CH + j0);
+    // Consumer B operands (this wave's key tile, K = tokens). Vector gate:
+    // the centred factors span exp(+-range/2), and the Gbar terms built from
+    // them cancel to far below their size (the diagonal of Hb enters Q'U_q
+    // and Y'U_y with opposite signs), so Y', Q', E' are carried as bf16
+    // hi + lo pairs; a single bf16 rounding would dominate dg for strong
+    // decays.
+    bf16x8 B0[2], B1[2], B2[2], L0[2], L1[2], L2[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sAT[(j0 + e) * LD64 + i] = a[e];
-    }
-    // this lane's q and k entries: rows 16mt + 4(l >> 4) + r, column f
-    float qv[4][4], kv[4][4];
+    for (int ks = 0; ks < 2; ++ks) {
+        if (VEC) {
+            f32x4 y[2], qq[2], ee[2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+            for (int hh = 0; hh < 2; ++hh) {
+                const int m = 2 * ks + hh;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t off = (tok0 + crow(16 * mt, r) * rs) * DKD + f;
-            qv[mt][r] = ldT(q + off);
-            kv[mt][r] = ldT(k + off);
-        }
-    __syncthreads();
-
-    auto Gat = [&](int i) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
-    const float Gnf = VEC ? sG[(CH - 1) * DKD + f] : sG[CH - 1];
-    const float cen = VEC ? sCen[f] : 0.f;
-
-    float dq[4][4], dk[4][4], Gacc[4][4], brow[4][4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dq[mt][r] = dk[mt][r] = Gacc[mt][r] = brow[mt][r] = 0.f;
-    auto rowi = [&](int mt, int r) { return crow(16 * mt, r); };
-    f32x4 X[4][1];
-    auto clear = [&]() {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) X[mt][0] = zero4();
-    };
-
-    // ---- S1: producer.  P = A^T Rb;  dv = beta P;  dbeta += <P, v> ----
-    clear();
-    wave_gemm<4, 1, CH>(sAT, LD64, 0, sRbT, LD64, 16 * w, X);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = rowi(mt, r);
-            const int64_t off = (tok0 + i * rs) * DVD + f;
-            io<T>::st((T*)gr.dv + off, sBeta[i] * X[mt][0][r]);
-            brow[mt][r] += X[mt][0][r] * ldT(v + off);
-        }
-        put_c(Pl, LD128, 16 * mt, 16 * w, X[mt][0]);
-    }
-    __syncthreads();
-
-    // ---- S2: D = -strict_lower(P R^T) (even waves), Hb = lower_incl(dO R^T)
-    //      (odd waves), rows 16 rb .. 16 rb + 15; consumer A operands ----
-    {
-        const int rb = w >> 1;
-        const bool isH = (w & 1) != 0;
-        const bf16* Aop = isH ? Ol : Pl;
-        f32x4 acc[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[nt] = zero4();
-#pragma unroll
-        for (int kk = 0; kk < DVD; kk += 32) {
-            const bf16x8 fa = frag(Aop, LD128, 16 * rb, kk);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                if (nt <= rb) acc[nt] = mfma(fa, frag(Rl, LD128, 16 * nt, kk), acc[nt]);
-        }
-        // sAT / sRbT (aliased by C1..C4) were last read in S1, before the barrier.
-        bf16* Cn = isH ? C3 : C1;  // [i][j]
-        bf16* Ct = isH ? C4 : C2;  // [j][i]
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-            const int j = ccol(16 * nt);
-            bf16x4 tt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = crow(16 * rb, r);
-                const bool keep = nt <= rb && (isH ? i >= j : i > j);
-                float x = keep ? (isH ? acc[nt][r] : -acc[nt][r]) : 0.f;
-                float xt = x;
-                if (!VEC) {
-                    x *= keep ? __expf(sG[i] - sG[j]) : 0.f;   // Gam = D o Lam, Gq = Hb o Lam
-                    xt = isH ? x : x * sBeta[i];                // Gam^T diag(beta) as [j][i]
+                for (int e = 0; e < 4; ++e) {
+                    const float d = Gt(m, e) - cen;
+                    const float al = __expf(d), ze = __expf(-d);
+                    y[hh][e] = ze * KC[m][e];
+                    qq[hh][e] = al * QC[m][e];
+                    ee[hh][e] = sBeta[16 * m + 4 * g + e] * al * KC[m][e];
                 }
-                Cn[i * LD64 + j] = (bf16)x;
-                tt[r] = (bf16)xt;
             }
-            *(bf16x4*)(Ct + j * LD64 + crow(16 * rb, 0)) = tt;
+            B0[ks] = pack_pi(y[0], y[1]);
+            B1[ks] = pack_pi(qq[0], qq[1]);
+            B2[ks] = pack_pi(ee[0], ee[1]);
+            // low parts: x - bf16(x)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[hh][e] -= (float)B0[ks][4 * hh + e];
+                    qq[hh][e] -= (float)B1[ks][4 * hh + e];
+                    ee[hh][e] -= (float)B2[ks][4 * hh + e];
+                }
+            L0[ks] = pack_pi(y[0], y[1]);
+            L1[ks] = pack_pi(qq[0], qq[1]);
+            L2[ks] = pack_pi(ee[0], ee[1]);
+        } else {
+            B0[ks] = pack_pi(KC[2 * ks], KC[2 * ks + 1]);
+            B1[ks] = pack_pi(QC[2 * ks], QC[2 * ks + 1]);
         }
     }
 
-    // ---- S3: state-direct terms (h, dh read as B operands straight from memory) ----
-    {
-        // Qgb = dO h^T:  dq += gam X;  Gbar += gam q X
-        clear();
-        wave_gemm<4, 1, DVD>(Ol, LD128, 0, hg, DVD, 16 * w, X);
+    __syncthreads();  // lP, lR, lO, sExtra complete
+
+    // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands ----
+    for (int x = w; x < 40; x += NW) {
+        const int kind = x / 10, tl = x % 10;
+        const int ti = tl >= 6 ? 3 : tl >= 3 ? 2 : tl >= 1 ? 1 : 0;
+        const int tj = tl - ti * (ti + 1) / 2;
+        const bf16x8* Aop = kind == 0 ? lP : kind == 2 ? lO : lR;
+        const bf16x8* Bop = kind == 0 ? lR : kind == 1 ? lP : kind == 2 ? lR : lO;
+        const int ma = (kind & 1) ? tj : ti, nb = (kind & 1) ? ti : tj;
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int sl = 0; sl < 4; ++sl) acc = mfma(Aop[(ma * 4 + sl) * 64 + l], Bop[(nb * 4 + sl) * 64 + l], acc);
+        bf16x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float gam = __expf(Gat(rowi(mt, r)));
-                dq[mt][r] += gam * X[mt][0][r];
-                Gacc[mt][r] += gam * qv[mt][r] * X[mt][0][r];
+        for (int e = 0; e < 4; ++e) {
+            const int i = (kind & 1) ? 16 * ti + r : 16 * ti + 4 * g + e;
+            const int j = (kind & 1) ? 16 * tj + 4 * g + e : 16 * tj + r;
+            const bool keep = kind < 2 ? i > j : i >= j;
+            float val = keep ? (kind < 2 ? -acc[e] : acc[e]) : 0.f;
+            if (!VEC) {
+                val *= keep ? __expf(sG[i] - sG[j]) : 0.f;  // Lam
+                if (kind == 0) val *= sBeta[i];             // Gam^T diag(beta)
             }
-        // Eb_dir = -P h^T:  dk += beta gam Eb;  dbeta += gam k Eb;  Gbar += beta gam k Eb
-        clear();
-        wave_gemm<4, 1, DVD>(Pl, LD128, 0, hg, DVD, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = rowi(mt, r);
-                const float gam = __expf(Gat(i));
-                const float eb = -X[mt][0][r];
-                const float bt = sBeta[i];
-                dk[mt][r] += bt * gam * eb;
-                brow[mt][r] += gam * kv[mt][r] * eb;
-                Gacc[mt][r] += bt * gam * kv[mt][r] * eb;
-            }
-        // Ktb = R dh^T:  dk += kt X;  Gbar -= kt k X;  Gbar_n += sum_i kt k X
-        float colsum = 0.f;
-        clear();
-        wave_gemm<4, 1, DVD>(Rl, LD128, 0, dhg, DVD, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float kt = __expf(Gnf - Gat(rowi(mt, r)));
-                const float t = kt * X[mt][0][r];
-                dk[mt][r] += t;
-                Gacc[mt][r] -= kv[mt][r] * t;
-                colsum += kv[mt][r] * t;
-            }
-        colsum += __shfl_xor(colsum, 16);
-        colsum += __shfl_xor(colsum, 32);
-        // rowsum(h o dh) for this wave's 16 key rows: 4 lanes per row
-        float hd = 0.f;
-        {
-            const int fr = 16 * w + (l >> 2);
-            const int v0 = (l & 3) * 32;
-#pragma unroll
-            for (int e = 0; e < 32; e += 8) {
-                const bf16x8 a = *(const bf16x8*)(hg + fr * DVD + v0 + e);
-                const bf16x8 bb = *(const bf16x8*)(dhg + fr * DVD + v0 + e);
-#pragma unroll
-                for (int z = 0; z < 8; ++z) hd += (float)a[z] * (float)bb[z];
-            }
-            hd += __shfl_xor(hd, 1);
-            hd += __shfl_xor(hd, 2);
+            o[e] = (bf16)val;
         }
-        if (l < 16) sExtra[f] = colsum;
-        __syncthreads();  // sExtra colsums visible; all reads of Ol/Rl/Pl done
-        if ((l & 3) == 0) {
-            const int fr = 16 * w + (l >> 2);
-            const float gn = __expf(VEC ? sG[(CH - 1) * DKD + fr] : sG[CH - 1]);
-            sExtra[fr] += gn * hd;
-        }
+        if (kind == 0) st_half(lGT, tj * 2 + (ti >> 1), ti & 1, o);        // D:    (M = j, K = i)
+        else if (kind == 1) st_half(lGm, ti * 2 + (tj >> 1), tj & 1, o);   // D^T:  (M = i, K = j)
+        else if (kind == 2) st_half(lGqT, tj * 2 + (ti >> 1), ti & 1, o);  // Hb:   (M = j, K = i)
+        else st_half(lGq, ti * 2 + (tj >> 1), tj & 1, o);                  // Hb^T: (M = i, K = j)
     }
 
-    // ---- S4: consumer B operands (transposed, feature-major) ----
+    __syncthreads();  // consumer A operands complete
+
+    // ---- 2b. Gbar_n extra term: sum_j exp(G_n - G_j) k_j Ktb_j + gam_n rowsum(h o dh) ----
+    float colsum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int id = tid + NTHR * u;
-        const int j = id >> 4, f0 = (id & 15) * 8;
-        float kx[8], qx[8];
-        load8(k + (tok0 + j * rs) * DKD + f0, kx);
-        load8(q + (tok0 + j * rs) * DKD + f0, qx);
-        const float bt = sBeta[j];
+    for (int m = 0; m < 4; ++m) {
+        f32x4 Kb = zero4();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int fe = f0 + e;
+        for (int sl = 0; sl < 4; ++sl) Kb = mfma(lR[(m * 4 + sl) * 64 + l], dhF[sl], Kb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ks = m >> 1, sl = 4 * (m & 1) + e;
+            float kv = (float)B0[ks][sl];
+            if (VEC) kv = (kv + (float)L0[ks][sl]) * __expf(Gt(m, e) - cen);
+            colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
+        }
+    }
+    colsum += __shfl_xor(colsum, 16);
+    colsum += __shfl_xor(colsum, 32);
+    const float extra = colsum + __expf(Gnf) * sExtra[f];
+
+    // ---- 3. per token tile, last to first: producer and state-direct terms,
+    //      the four consumer products, chain rules, dq / dk, the per-token
+    //      dbeta partials and (vector gate) dg with a running suffix sum ----
+    float carry = extra;  // vector gate: suffix sum of Gbar over later tokens
+#pragma unroll
+    for (int m = 3; m >= 0; --m) {
+        f32x4 E = zero4(), Qb = zero4(), Kb = zero4();
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+            E = mfma(lP[(m * 4 + sl) * 64 + l], hF[sl], E);
+            Qb = mfma(lO[(m * 4 + sl) * 64 + l], hF[sl], Qb);
+            Kb = mfma(lR[(m * 4 + sl) * 64 + l], dhF[sl], Kb);
+        }
+        // lower operands (Gam, Gq: K index <= M index) skip slab 1 for m < 2;
+        // upper operands (Gam^T, Gq^T) skip slab 0 for m >= 2
+        f32x4 X1 = zero4(), X2 = zero4(), X3 = zero4(), X4 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 0 || m >= 2) {
+                const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
+                X1 = mfma(a1, B0[ks], X1);  // Gam K    | D Y'
+                X3 = mfma(a3, B0[ks], X3);  // Gq K     | Hb Y'
+                if (VEC) {
+                    X1 = mfma(a1, L0[ks], X1);
+                    X3 = mfma(a3, L0[ks], X3);
+                }
+            }
+            if (ks == 1 || m < 2) {
+                const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
+                X2 = mfma(a2, VEC ? B2[ks] : B0[ks], X2);  // Gam^T bK | D^T E'
+                X4 = mfma(a4, B1[ks], X4);                 // Gq^T Q   | Hb^T Q'
+                if (VEC) {
+                    X2 = mfma(a2, L2[ks], X2);
+                    X4 = mfma(a4, L1[ks], X4);
+                }
+            }
+        }
+        float Ga[4], br[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * m + 4 * g + e;
+            const float G = Gt(m, e), gam = __expf(G), kt = __expf(Gnf - G);
+            const float bt = sBeta[i];
+            // k and q back from the consumer operands (exact for the scalar
+            // gate; hi + lo over the centred factor for the vector gate)
+            const int ks = m >> 1, sl = 4 * (m & 1) + e;
+            float kv = (float)B0[ks][sl], qv = (float)B1[ks][sl];
+            float al = 1.f, ze = 1.f;
             if (VEC) {
-                const float cc = sCen[fe];
-                const float G = sG[j * DKD + fe];
-                const float al = __expf(G - cc), ze = __expf(cc - G);
-                B1[fe * LD64 + j] = (bf16)(ze * kx[e]);       // Y'^T
-                B2[fe * LD64 + j] = (bf16)(al * qx[e]);       // Q'^T
-                B3[fe * LD64 + j] = (bf16)(bt * al * kx[e]);  // E'^T
+                const float d = G - cen;
+                al = __expf(d);
+                ze = __expf(-d);
+                kv = (kv + (float)L0[ks][sl]) * al;
+                qv = (qv + (float)L1[ks][sl]) * ze;
+            }
+            const float eb = -E[e];  // Eb_dir = -P h^T
+            float dq = gam * Qb[e];
+            float dk = bt * gam * eb + kt * Kb[e];
+            br[e] = gam * kv * eb;
+            Ga[e] = gam * qv * Qb[e] + bt * gam * kv * eb - kt * kv * Kb[e];
+            if (VEC) {
+                const float uq = X3[e], ue = X1[e], uy = X2[e] + X4[e];
+                dq += al * uq;
+                dk += bt * al * ue + ze * uy;
+                br[e] += al * kv * ue;
+                Ga[e] += al * qv * uq + bt * al * kv * ue - ze * kv * uy;
             } else {
-                B1[fe * LD64 + j] = (bf16)kx[e];              // K^T
-                B2[fe * LD64 + j] = (bf16)qx[e];              // Q^T
+                dq += X3[e];
+                dk += bt * X1[e] + X2[e] + X4[e];
+                br[e] += kv * X1[e];
+                Ga[e] += bt * kv * X1[e] - kv * X2[e] + qv * X3[e] - kv * X4[e];
+            }
+            const int off = i * ld + f;
+            io<T>::st(dqo + off, dq);
+            io<T>::st(dko + off, dk);
+        }
+        // per-token sums over this wave's features
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float bsum = sum16(br[e]);
+            const float gsum = VEC ? 0.f : sum16(Ga[e]);
+            if (r == 0) {
+                sRedB[w][16 * m + 4 * g + e] = bsum;
+                if (!VEC) sRedG[w][16 * m + 4 * g + e] = gsum;
             }
         }
+        if (VEC) {
+            // reverse cumsum down this lane's feature column, tokens 16 m .. 16 m + 15
+            float suf[4];
+            suf[3] = Ga[3];
+#pragma unroll
+            for (int e = 2; e >= 0; --e) suf[e] = suf[e + 1] + Ga[e];
+            const float tot = suf[0];
+            float incl = tot;
+            float y = __shfl_down(incl, 16);
+            if (g < 3) incl += y;
+            y = __shfl_down(incl, 32);
+            if (g < 2) incl += y;
+            const float excl = incl - tot;
+            const float ttot = __shfl(incl, r);  // g = 0 lane holds the tile total
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dgo[(16 * m + 4 * g + e) * ld + f] = suf[e] + excl + carry;
+            carry += ttot;
+        }
+        // keep the scheduler from hoisting the next tile's operand reads
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- 4. dbeta; scalar gate: dg ----
+    if (!VEC) {
+        const float ex = sum16(extra);
+        if (l == 0) sEx[w] = ex;
     }
     __syncthreads();
-
-    // ---- S5: consumer products ----
-    if (!VEC) {
-        // A_K = Gam K
-        clear();
-        wave_gemm<4, 1, CH>(C1, LD64, 0, B1, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x = X[mt][0][r], bt = sBeta[rowi(mt, r)];
-                dk[mt][r] += bt * x;
-                brow[mt][r] += kv[mt][r] * x;
-                Gacc[mt][r] += bt * kv[mt][r] * x;
-            }
-        // B_K = Gam^T diag(beta) K,  plus Gq^T Q  (same chain rule)
-        clear();
-        wave_gemm<4, 1, CH>(C2, LD64, 0, B1, LD64, 16 * w, X);
-        wave_gemm<4, 1, CH>(C4, LD64, 0, B2, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dk[mt][r] += X[mt][0][r];
-                Gacc[mt][r] -= kv[mt][r] * X[mt][0][r];
-            }
-        // Gq K
-        clear();
-        wave_gemm<4, 1, CH>(C3, LD64, 0, B1, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dq[mt][r] += X[mt][0][r];
-                Gacc[mt][r] += qv[mt][r] * X[mt][0][r];
-            }
-    } else {
-        // U_q = Hb Y'
-        clear();
-        wave_gemm<4, 1, CH>(C3, LD64, 0, B1, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float al = __expf(Gat(rowi(mt, r)) - cen);
-                dq[mt][r] += al * X[mt][0][r];
-                Gacc[mt][r] += al * qv[mt][r] * X[mt][0][r];
-            }
-        // U_e = D Y'
-        clear();
-        wave_gemm<4, 1, CH>(C1, LD64, 0, B1, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = rowi(mt, r);
-                const float al = __expf(Gat(i) - cen);
-                const float x = X[mt][0][r], bt = sBeta[i];
-                dk[mt][r] += bt * al * x;
-                brow[mt][r] += al * kv[mt][r] * x;
-                Gacc[mt][r] += bt * al * kv[mt][r] * x;
-            }
-        // U_y = Hb^T Q' + D^T E'
-        clear();
-        wave_gemm<4, 1, CH>(C4, LD64, 0, B2, LD64, 16 * w, X);
-        wave_gemm<4, 1, CH>(C2, LD64, 0, B3, LD64, 16 * w, X);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ze = __expf(cen - Gat(rowi(mt, r)));
-                dk[mt][r] += ze * X[mt][0][r];
-                Gacc[mt][r] -= ze * kv[mt][r] * X[mt][0][r];
-            }
-    }
-
-    // ---- S6: outputs ----
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t off = (tok0 + rowi(mt, r) * rs) * DKD + f;
-            io<T>::st((T*)gr.dq + off, dq[mt][r]);
-            io<T>::st((T*)gr.dk + off, dk[mt][r]);
-        }
-    // row sums over the wave's features: dbeta (and Gbar for a scalar gate)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float bsum = sum16(brow[mt][r]);
-            const float gsum = VEC ? 0.f : sum16(Gacc[mt][r]);
-            if ((l & 15) == 0) {
-                sRedB[w][rowi(mt, r)] = bsum;
-                if (!VEC) sRedG[w][rowi(mt, r)] = gsum;
-            }
-        }
-    __syncthreads();  // all S5 reads of R1 (B1..B3) done; reductions visible
     if (tid < CH) {
         float sb = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) sb += sRedB[ww][tid];
-        io<T>::st((T*)gr.dbeta + tok0 + tid * rs, sb);
+        for (int ww = 0; ww < NW; ++ww) sb += sRedB[ww][tid] + sRedP[ww][tid];
+        io<T>::st(dbo + tid * Hs, sb);
     }
-    if (VEC) {
-        float* sGb = (float*)R1;  // [64][129]
+    if (!VEC && w == 0) {
+        // sum the extra over features, then reverse cumsum over tokens
+        float xg = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int ww = 0; ww < NW; ++ww) xg += sRedG[ww][l];
+        if (l == CH - 1) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sGb[rowi(mt, r) * (DKD + 1) + f] = Gacc[mt][r];
-        __syncthreads();
-        if (tid < DKD) {
-            float run = sExtra[tid];
-            for (int i = CH - 1; i >= 0; --i) {
-                run += sGb[i * (DKD + 1) + tid];
-                gr.dg[(tok0 + i * rs) * DKD + tid] = run;
-            }
+            for (int ww = 0; ww < NW; ++ww) xg += sEx[ww];
         }
-    } else if (w == 0) {
-        float ex = sExtra[l] + sExtra[l + 64];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ex += __shfl_xor(ex, off);
-        float x = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) x += sRedG[ww][l];
-        if (l == CH - 1) x += ex;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(x, off);
-            if (l + off < 64) x += y;
+            const float y = __shfl_down(xg, off);
+            if (l + off < 64) xg += y;
         }
-        gr.dg[tok0 + l * rs] = x;
+        dgo[l * Hs] = xg;
     }
 }
 

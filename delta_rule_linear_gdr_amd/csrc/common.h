@@ -203,12 +203,59 @@ __device__ __forceinline__ bf16x8 ident_frag(int parity)
     return v;
 }
 
+// The same identity for an A operand in frag (pik) k order, e.g. one
+// assembled from accumulator tiles: slot j is 1 where pik(g, j) is the
+// output column.
+__device__ __forceinline__ bf16x8 ident_pi(int parity)
+{
+    const int r = lane_r(), g = lane_g();
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (bf16)((pik(g, j) == 16 * parity + r) ? 1.f : 0.f);
+    return v;
+}
+
+__device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi)
+{
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[i] = lo[i];
+        v[4 + i] = hi[i];
+    }
+    return v;
+}
+
+// Four consecutive elements of an input/output row.
+__device__ __forceinline__ void load4(const bf16* p, float (&x)[4])
+{
+    const bf16x4 v = *(const bf16x4*)p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void load4(const float* p, float (&x)[4])
+{
+    const float4 v = *(const float4*)p;
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+__device__ __forceinline__ void store4(bf16* p, const float (&x)[4])
+{
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+    *(bf16x4*)p = v;
+}
+__device__ __forceinline__ void store4(float* p, const float (&x)[4])
+{
+    *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+}
+
 // Plain-order fragment of a row-major matrix with row stride ld (elements):
 // lane (r, g) gets X[row0 + r][k0 + 8 g .. + 7] as floats.
 template <typename T>
-__device__ __forceinline__ void ld_plain8(const T* base, int64_t ld, int row0, int k0, float (&x)[8])
+__device__ __forceinline__ void ld_plain8(const T* base, int ld, int row0, int k0, float (&x)[8])
 {
-    load8(base + (int64_t)(row0 + lane_r()) * ld + k0 + 8 * lane_g(), x);
+    load8(base + (row0 + lane_r()) * ld + k0 + 8 * lane_g(), x);
 }
 
 }  // namespace gdr

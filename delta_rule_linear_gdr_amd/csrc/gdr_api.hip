@@ -56,7 +56,8 @@ struct Carver {
 // What the full-save forward keeps for the backward.
 void carve_saved(Carver& c, Inter& it)
 {
-    it.A = c.take<bf16>(B_T64x64);
+    it.AT = c.take<bf16>(B_T64x64);
+    it.Af = c.take<bf16>(B_T64x64);
     it.Kt = c.take<bf16>(B_T64x128);
     it.WnT = c.take<bf16>(B_T64x128);
     it.gn = c.take<float>(B_GN);
@@ -91,7 +92,8 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
         if (!full) {
             it.Kt = sc.take<bf16>(B_T64x128);
             it.WnT = sc.take<bf16>(B_T64x128);
-            it.A = sc.take<bf16>(B_T64x64);
+            it.AT = sc.take<bf16>(B_T64x64);
+            it.Af = sc.take<bf16>(B_T64x64);
             it.h = sc.take<bf16>(B_T128x128);
             it.R = sc.take<bf16>(B_T64x128);
         }
@@ -265,7 +267,7 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     hipError_t e;
     if (policy == GDR_RECOMPUTE) {
         e = timed(ST_PREP, st, [&] {
-            return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A, st);
+            return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A | PREP_AF, st);
         });
         if (e != hipSuccess) return hip_fail(e, "prep");
         e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, nullptr, nullptr, st); });
@@ -335,7 +337,7 @@ int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
     hipError_t e;
     const int what = PREP_FWDSCAN | PREP_OUT |
-                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A : 0);
+                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A | PREP_AF : 0);
     e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, what, st); });
     if (e != hipSuccess) return hip_fail(e, "prep");
     e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });

@@ -49,11 +49,12 @@ struct Inter {
     bf16* HmT;   // Hm^T        frag  M=64 tok j, K=64 tok i (8 KiB)
     bf16* QgT;   // Qg^T        frag  M=128 key, K=64 tok    (16 KiB)
     // chunk-local backward inputs
-    bf16* A;     // A = (I+L)^-1 plain [i][j]                 (8 KiB)
-    bf16* h;     // state at chunk start, plain [key][val]    (32 KiB)
-    bf16* R;     // correction, plain [tok][val]              (16 KiB)
-    bf16* dh;    // state adjoint at chunk end, plain         (32 KiB)
-    bf16* Rb;    // correction adjoint, plain [tok][val]      (16 KiB)
+    bf16* AT;    // A^T = (I+L)^-T  frag  M=64 tok i, K=64 tok j (8 KiB)
+    bf16* Af;    // A             frag  M=64 tok i, K=64 tok j (8 KiB)
+    bf16* h;     // state at chunk start   ctile M=128 key, N=128 val (32 KiB)
+    bf16* R;     // correction             ctile M=64 tok,  N=128 val (16 KiB)
+    bf16* dh;    // state adjoint at chunk end, ctile like h         (32 KiB)
+    bf16* Rb;    // correction adjoint, ctile like R                 (16 KiB)
 };
 
 struct Shape {
@@ -79,7 +80,8 @@ enum {
     PREP_BWDSCAN = 4,  // Kt, WnT (and gn)
     PREP_XY = 8,       // X, Y from dO
     PREP_SAVEXY = 16,  // HmT, QgT (for launch_xy)
-    PREP_A = 32,       // A
+    PREP_A = 32,       // AT (and Af when PREP_AF is set)
+    PREP_AF = 64,
 };
 
 hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what,

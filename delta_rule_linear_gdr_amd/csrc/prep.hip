@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
     const int64_t b = bh / s.H, hd = bh % s.H;
     const int64_t t = (int64_t)bh * s.NT + c;
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;  // token of row 0
-    const int64_t ld = s.H * DKD;                                 // row stride (elements)
+    const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
     const int tid = threadIdx.x;
     const int l = lane_id(), r = lane_r(), g = lane_g();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -435,13 +435,22 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
                 }
         }
         if (wantA) {
-            const int row = tid >> 2, c0 = (tid & 3) * 16;
-            float x[8];
+            // A^T frag (M = i, K = j): slot jj of lane (r, g) = A[32 ks + pik(g, jj)][16 mt + r]
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int u = 0; u < 2; ++u) {
+                const int tl = 2 * w + u, mt = tl >> 1, ks = tl & 1;
+                float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = sA[row * LP + c0 + 8 * hh + e];
-                store8(it.A + (t * CH + row) * CH + c0 + 8 * hh, x);
+                for (int jj = 0; jj < 8; ++jj) x[jj] = sA[(32 * ks + pik(g, jj)) * LP + 16 * mt + r];
+                st_frag(it.AT + t * (CH * CH), tl, pack8(x));
+            }
+            if (what & PREP_AF) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int tl = 2 * w + u, mt = tl >> 1, ks = tl & 1;
+                    st_frag(it.Af + t * (CH * CH), tl,
+                            (ks == 0 || mt >= 2) ? afrag(mt, ks) : bf16x8{});
+                }
             }
         }
     }
@@ -477,7 +486,7 @@ __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
     const int64_t b = bh / s.H, hd = bh % s.H;
     const int64_t t = (int64_t)bh * s.NT + c;
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
-    const int64_t ld = s.H * DVD;
+    const int ld = (int)(s.H * DVD);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* dO = (const T*)in.dO + tok0 * DVD;
 

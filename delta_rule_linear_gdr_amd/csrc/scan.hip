@@ -86,7 +86,7 @@ __device__ __forceinline__ void load_ops(Ops<BWD, OUT>& o, const bf16* A1, const
     }
 }
 
-template <bool BWD, bool OUT, typename T>
+template <bool BWD, bool OUT, bool STORE, typename T>
 __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it, T* o, float* fin)
 {
     int bh, vs;
@@ -120,13 +120,12 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
 
     auto step = [&](const Ops<BWD, OUT>& op, int c) {
         const int64_t t = tile(c);
-        // state before the update (h_c, or dh_c = adjoint at the chunk end)
-        if (Sout) {
+        // state before the update (h_c, or dh_c = adjoint at the chunk end),
+        // as ctiles (key tile 2w + m, value tile vs)
+        if (STORE) {
 #pragma unroll
             for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Sout[(t * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = (bf16)S[m][i];
+                *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), vs * 8 + 2 * w + m) = pack4(S[m]);
         }
         sS[w][l] = pack_pi(S[0], S[1]);
         __syncthreads();
@@ -142,10 +141,7 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) oacc = mfma(op.qg[ks], sf[ks], oacc);
         }
-        if (Zout) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Zout[(t * CH + 16 * w + 4 * g + i) * DVD + v] = (bf16)z[i];
-        }
+        if (STORE) *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), vs * 4 + w) = pack4(z);
         *(bf16x4*)((bf16*)&sZ[w >> 1][l] + 4 * (w & 1)) = pack4(z);
         __syncthreads();
         bf16x8 zf[2];
@@ -176,26 +172,29 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
         }
     };
 
-    // three register sets of chunk operands in flight
+    // Three register sets of chunk operands in flight. Every prefetch is
+    // issued unconditionally (past the end it re-reads the last chunk), so
+    // the number of memory operations per step is fixed and the waits on
+    // the vector-memory counter stay exact.
     Ops<BWD, OUT> P0, P1, P2;
     auto load = [&](Ops<BWD, OUT>& op, int p) {
-        load_ops<BWD, OUT>(op, A1, A2, C1, C2, it.gn, it.Qg, it.Hm, tile(chunk(p)), w, vs);
+        load_ops<BWD, OUT>(op, A1, A2, C1, C2, it.gn, it.Qg, it.Hm,
+                           tile(chunk(p < NT ? p : NT - 1)), w, vs);
     };
     load(P0, 0);
-    if (NT > 1) load(P1, 1);
-    if (NT > 2) load(P2, 2);
-    for (int p = 0; p < NT; p += 3) {
+    load(P1, 1);
+    load(P2, 2);
+    int p = 0;
+    for (; p + 3 <= NT; p += 3) {
         step(P0, chunk(p));
-        if (p + 3 < NT) load(P0, p + 3);
-        if (p + 1 < NT) {
-            step(P1, chunk(p + 1));
-            if (p + 4 < NT) load(P1, p + 4);
-        }
-        if (p + 2 < NT) {
-            step(P2, chunk(p + 2));
-            if (p + 5 < NT) load(P2, p + 5);
-        }
+        load(P0, p + 3);
+        step(P1, chunk(p + 1));
+        load(P1, p + 4);
+        step(P2, chunk(p + 2));
+        load(P2, p + 5);
     }
+    if (p < NT) step(P0, chunk(p));
+    if (p + 1 < NT) step(P1, chunk(p + 1));
     if (fin) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -211,11 +210,17 @@ hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, vo
                            hipStream_t st)
 {
     const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    const bool store = it.h != nullptr;
     if (o) {
-        if (s.f32) scan_kernel<false, true, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
-        else scan_kernel<false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
+        if (s.f32) {
+            if (store) scan_kernel<false, true, true, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
+            else scan_kernel<false, true, false, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
+        } else {
+            if (store) scan_kernel<false, true, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
+            else scan_kernel<false, true, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
+        }
     } else {
-        scan_kernel<false, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, ht);
+        scan_kernel<false, false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, ht);
     }
     return hipGetLastError();
 }
@@ -224,7 +229,7 @@ hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, fl
                            hipStream_t st)
 {
     const unsigned nblk = (unsigned)(s.B * s.H * NVS);
-    scan_kernel<true, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, dh0);
+    scan_kernel<true, false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, dh0);
     return hipGetLastError();
 }
 

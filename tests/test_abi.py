@@ -45,15 +45,15 @@ def test_workspace_sizes():
     rc, sv, sc = _ws(_desc(T=8192, H=16), 0)
     assert rc == 0 and sv == 0
     # recompute: the backward holds the forward-scan operands (-W, Kt^T, U, gn),
-    # the reverse-scan operands (Kt, -W^T, X, Y), A, and the per-chunk h, R,
-    # dh, Rb of every (chunk, head)
-    per = 3 * T64x128 + GN + 2 * T64x128 + T64x64 + T128x128 + T64x128 \
+    # the reverse-scan operands (Kt, -W^T, X, Y), A^T and A, and the per-chunk
+    # h, R, dh, Rb of every (chunk, head)
+    per = 3 * T64x128 + GN + 2 * T64x128 + 2 * T64x64 + T128x128 + T64x128 \
         + T64x128 + T128x128 + T128x128 + T64x128
     assert sc == 2048 * per
     rc, sv, sc = _ws(_desc(T=8192, H=16), 1)
     assert rc == 0
-    # full save keeps A, Kt, -W^T, gn, Hm^T, Qg^T, h, R
-    assert sv == 2048 * (T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
+    # full save keeps A^T, A, Kt, -W^T, gn, Hm^T, Qg^T, h, R
+    assert sv == 2048 * (2 * T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
     assert sc == 2048 * max(4 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128)
 
 
