@@ -72,8 +72,28 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int f = 16 * w + r;  // this lane's feature (key or value) column
 
-    __shared__ bf16x8 lP[16 * 64], lR[16 * 64], lO[16 * 64];  // frags M = 64 tok, K = 128 val
-    __shared__ bf16x8 lGm[8 * 64], lGT[8 * 64], lGq[8 * 64], lGqT[8 * 64];  // frags 64 x 64
+    // LDS fragment buffers (16 x 32 frag tiles; 1024 entries = 64 x 128,
+    // 512 entries = 64 x 64). Both producers: R, dO (M = tok, K = val) and the
+    // consumer A operands Gm, GT, Gq, GqT. ReWY: P (M = tok, K = val). The
+    // seven-product producer: Rb, Z (M = tok, K = val), E, W (M = tok,
+    // K = key) with W = Rb h^T, Abar^T (M = col, K = row) and X (M = tok,
+    // K = tok) with X = A^T Abar.
+    constexpr int NLDS = WY7 ? 9216 : 5120;
+    __shared__ bf16x8 lds[NLDS];
+    bf16x8* const lR = lds;
+    bf16x8* const lO = lds + 1024;
+    bf16x8* const lP = lds + 2048;                      // ReWY
+    bf16x8* const lRb = lds + 2048;                     // seven-product
+    bf16x8* const lZ = lds + 3072;
+    bf16x8* const lE = lds + 4096;
+    bf16x8* const lWb = lds + 5120;
+    bf16x8* const lAbT = lds + 6144;
+    bf16x8* const lX = lds + 6656;
+    bf16x8* const lG = lds + (WY7 ? 7168 : 3072);
+    bf16x8* const lGm = lG;
+    bf16x8* const lGT = lG + 512;
+    bf16x8* const lGq = lG + 1024;
+    bf16x8* const lGqT = lG + 1536;
     __shared__ float sG[CH], sBeta[CH];
     __shared__ float sRedB[NW][CH], sRedP[NW][CH], sRedG[NW][CH];
     __shared__ float sExtra[DKD];
@@ -138,9 +158,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     }
     {
         const bf16x8 z8 = {};
-        bf16x8* zb[4] = {lGm, lGT, lGq, lGqT};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) zb[u][tid] = z8;
+        for (int u = 0; u < 4; ++u) lG[u * NTHR + tid] = z8;
     }
     __syncthreads();
     if (!VEC) Gnf = sG[CH - 1];
@@ -181,7 +200,24 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             pv += __shfl_xor(pv, 16);
             pv += __shfl_xor(pv, 32);
             if (g == 0) sRedP[w][i] = pv;
-            st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
+            if (!WY7) st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
+        }
+        if (WY7) {
+            // Rb fragments (contraction over values) through Rb^T * I, and
+            // Z = diag(beta) V fragments, value tile w
+            const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 cc = mfma(RbT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
+                st_half(lRb, m * 4 + (w >> 1), w & 1, pack4(cc));
+                float vx[4];
+                load4(v + (16 * m + r) * ld + 16 * w + 4 * g, vx);
+                const float bt = sBeta[16 * m + r];
+                bf16x4 z4v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) z4v[e] = (bf16)(bt * vx[e]);
+                st_half(lZ, m * 4 + (w >> 1), w & 1, z4v);
+            }
         }
     }
     // ---- 1b. R and dO fragments (contraction over values) of value tile w ----
@@ -245,6 +281,30 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         ld_plain8(q, ld, 16 * m, 32 * (w >> 1), x);
         QC[m] = mfma(pack8(x), Iw, zero4());
     }
+    if (WY7) {
+        // E = diag(beta)(gam * K) fragments (M = tok, K = key) of key tile w:
+        // E^T frags from the K * I accumulators, transposed through E^T * I
+        const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+        bf16x8 ETf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            f32x4 ec[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int m = 2 * ks + hh;
+                    ec[hh][e] = sBeta[16 * m + 4 * g + e] * __expf(Gt(m, e)) * KC[m][e];
+                }
+            ETf[ks] = pack_pi(ec[0], ec[1]);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            // lane: E[tok 16 m + r][key 16 w + 4 g + e]
+            const f32x4 cc = mfma(ETf[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
+            st_half(lE, m * 4 + (w >> 1), w & 1, pack4(cc));
+        }
+    }
     // Consumer B operands (this wave's key tile, K = tokens). Vector gate:
     // the centred factors span exp(+-range/2), and the Gbar terms built from
     // them cancel to far below their size (the diagonal of Hb enters Q'U_q
@@ -291,17 +351,81 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 
     __syncthreads();  // lP, lR, lO, sExtra complete
 
-    // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands ----
+    // ---- 2a'. seven-product producer (ablation): W = Rb h^T (so Wbar = -W),
+    //      Abar = Rb Z^T + Wbar E^T, X = A^T Abar; Mbar = -X A^T follows below
+    bf16x8 WT[2];  // W^T frags (M = key tile w, K = tok), B operands of Eb_dir
+    const bf16* ATg = it.AT + t * (CH * CH);
+    const bf16* Afg = it.Af + t * (CH * CH);
+    if (WY7) {
+        f32x4 Wc[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 a = zero4(), at = zero4();
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                a = mfma(lRb[(m * 4 + sl) * 64 + l], hF[sl], a);    // W tile (m, w)
+                at = mfma(hF[sl], lRb[(m * 4 + sl) * 64 + l], at);  // W^T tile (w, m)
+            }
+            Wc[m] = a;
+            // lane: W^T[key 16 w + 4 g + e][tok 16 m + r] -> W frag (M = tok, K = key)
+            st_half(lWb, m * 4 + (w >> 1), w & 1, pack4(at));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) WT[ks] = pack_pi(Wc[2 * ks], Wc[2 * ks + 1]);
+        __syncthreads();  // lWb complete
+        // Abar (full 64 x 64), two tiles per wave -> Abar^T frags (M = col, K = row)
+        for (int x = w; x < 16; x += NW) {
+            const int ta = x >> 2, tb = x & 3;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) acc = mfma(lRb[(ta * 4 + sl) * 64 + l], lZ[(tb * 4 + sl) * 64 + l], acc);
+            f32x4 acw = zero4();
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) acw = mfma(lWb[(ta * 4 + sl) * 64 + l], lE[(tb * 4 + sl) * 64 + l], acw);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] -= acw[e];
+            // lane: Abar[a = 16 ta + 4 g + e][b = 16 tb + r]
+            st_half(lAbT, tb * 2 + (ta >> 1), ta & 1, pack4(acc));
+        }
+        __syncthreads();  // lAbT complete
+        // X^T = Abar^T A (A^T is upper triangular: skip row slab 0 for i >= 32)
+        for (int x = w; x < 16; x += NW) {
+            const int tc = x >> 2, ti = x & 3;
+            f32x4 acc = mfma(lAbT[(tc * 2 + 1) * 64 + l], ld_frag(ATg, ti * 2 + 1), zero4());
+            if (ti < 2) acc = mfma(lAbT[(tc * 2 + 0) * 64 + l], ld_frag(ATg, ti * 2 + 0), acc);
+            // lane: X[i = 16 ti + r][c = 16 tc + 4 g + e] -> X frag (M = i, K = c)
+            st_half(lX, ti * 2 + (tc >> 1), tc & 1, pack4(acc));
+        }
+        __syncthreads();  // lX complete
+    }
+
+    // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands. ReWY:
+    //      D = -strict_lower(P R^T). Seven-product: D = strict_lower(Mbar)
+    //      with Mbar = -X A^T, formed here as -strict_lower(X A^T). ----
     for (int x = w; x < 40; x += NW) {
         const int kind = x / 10, tl = x % 10;
         const int ti = tl >= 6 ? 3 : tl >= 3 ? 2 : tl >= 1 ? 1 : 0;
         const int tj = tl - ti * (ti + 1) / 2;
-        const bf16x8* Aop = kind == 0 ? lP : kind == 2 ? lO : lR;
-        const bf16x8* Bop = kind == 0 ? lR : kind == 1 ? lP : kind == 2 ? lR : lO;
-        const int ma = (kind & 1) ? tj : ti, nb = (kind & 1) ? ti : tj;
         f32x4 acc = zero4();
+        if (WY7 && kind < 2) {
+            // A is lower triangular: its column slab 1 is zero for rows < 32
+            const int rj = tj;  // A row tile
+            if (kind == 0) {
+                // (X A^T)[i][j]: A operand X frag (i), B operand A frag (j)
+                acc = mfma(lX[(ti * 2 + 0) * 64 + l], ld_frag(Afg, rj * 2 + 0), acc);
+                if (rj >= 2) acc = mfma(lX[(ti * 2 + 1) * 64 + l], ld_frag(Afg, rj * 2 + 1), acc);
+            } else {
+                // (A X^T)[j][i]
+                acc = mfma(ld_frag(Afg, rj * 2 + 0), lX[(ti * 2 + 0) * 64 + l], acc);
+                if (rj >= 2) acc = mfma(ld_frag(Afg, rj * 2 + 1), lX[(ti * 2 + 1) * 64 + l], acc);
+            }
+        } else {
+            const bf16x8* Aop = kind == 0 ? lP : kind == 2 ? lO : lR;
+            const bf16x8* Bop = kind == 0 ? lR : kind == 1 ? lP : kind == 2 ? lR : lO;
+            const int ma = (kind & 1) ? tj : ti, nb = (kind & 1) ? ti : tj;
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) acc = mfma(Aop[(ma * 4 + sl) * 64 + l], Bop[(nb * 4 + sl) * 64 + l], acc);
+            for (int sl = 0; sl < 4; ++sl) acc = mfma(Aop[(ma * 4 + sl) * 64 + l], Bop[(nb * 4 + sl) * 64 + l], acc);
+        }
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -348,10 +472,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     float carry = extra;  // vector gate: suffix sum of Gbar over later tokens
 #pragma unroll
     for (int m = 3; m >= 0; --m) {
+        // E = P h^T (ReWY) or A^T W with W = Rb h^T (seven-product); both are -Eb_dir
         f32x4 E = zero4(), Qb = zero4(), Kb = zero4();
+        if (WY7) {
+            E = mfma(ld_frag(ATg, m * 2 + 1), WT[1], E);
+            if (m < 2) E = mfma(ld_frag(ATg, m * 2 + 0), WT[0], E);
+        }
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-            E = mfma(lP[(m * 4 + sl) * 64 + l], hF[sl], E);
+            if (!WY7) E = mfma(lP[(m * 4 + sl) * 64 + l], hF[sl], E);
             Qb = mfma(lO[(m * 4 + sl) * 64 + l], hF[sl], Qb);
             Kb = mfma(lR[(m * 4 + sl) * 64 + l], dhF[sl], Kb);
         }
@@ -486,14 +615,19 @@ hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, c
                             bool wy7, hipStream_t st)
 {
     dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
-    if (wy7) return hipErrorNotSupported;
-    if (s.f32) {
-        if (s.vec) bwd_local_kernel<float, true, false><<<grid, NTHR, 0, st>>>(s, in, it, gr);
-        else bwd_local_kernel<float, false, false><<<grid, NTHR, 0, st>>>(s, in, it, gr);
-    } else {
-        if (s.vec) bwd_local_kernel<bf16, true, false><<<grid, NTHR, 0, st>>>(s, in, it, gr);
-        else bwd_local_kernel<bf16, false, false><<<grid, NTHR, 0, st>>>(s, in, it, gr);
-    }
+#define GDR_BWD_LOCAL(W7)                                                                        \
+    do {                                                                                         \
+        if (s.f32) {                                                                             \
+            if (s.vec) bwd_local_kernel<float, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);  \
+            else bwd_local_kernel<float, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);       \
+        } else {                                                                                 \
+            if (s.vec) bwd_local_kernel<bf16, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);   \
+            else bwd_local_kernel<bf16, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);        \
+        }                                                                                        \
+    } while (0)
+    if (wy7) GDR_BWD_LOCAL(true);
+    else GDR_BWD_LOCAL(false);
+#undef GDR_BWD_LOCAL
     return hipGetLastError();
 }
 

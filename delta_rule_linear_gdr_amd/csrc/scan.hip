@@ -118,15 +118,32 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
     auto chunk = [&](int p) { return BWD ? NT - 1 - p : p; };
     auto tile = [&](int c) { return (int64_t)bh * s.NT + c; };
 
-    auto step = [&](const Ops<BWD, OUT>& op, int c) {
-        const int64_t t = tile(c);
-        // state before the update (h_c, or dh_c = adjoint at the chunk end),
-        // as ctiles (key tile 2w + m, value tile vs)
+    // Stores of a step are issued after the next group of prefetch loads:
+    // loads and stores share one in-order completion counter, so a store
+    // issued ahead of a prefetch would have to be acknowledged before that
+    // prefetch counts as complete.
+    bf16x4 pend_s[2], pend_z;
+    f32x4 pend_o;
+    int64_t pend_t = 0, pend_tok = 0;
+    auto flush = [&]() {
+        if (OUT) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) io<T>::st(o + (pend_tok + (int64_t)i * s.H) * DVD + v, pend_o[i]);
+        }
         if (STORE) {
+            // state before the update (h_c, or dh_c = adjoint at the chunk
+            // end) as ctiles (key tile 2w + m, value tile vs); Z likewise
 #pragma unroll
             for (int m = 0; m < 2; ++m)
-                *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), vs * 8 + 2 * w + m) = pack4(S[m]);
+                *(bf16x4*)ctile_ptr(Sout + pend_t * (DKD * DVD), vs * 8 + 2 * w + m) = pend_s[m];
+            *(bf16x4*)ctile_ptr(Zout + pend_t * (CH * DVD), vs * 4 + w) = pend_z;
         }
+    };
+    auto step = [&](const Ops<BWD, OUT>& op, int c) {
+        const int64_t t = tile(c);
+        pend_t = t;
+        pend_s[0] = pack4(S[0]);
+        pend_s[1] = pack4(S[1]);
         sS[w][l] = pack_pi(S[0], S[1]);
         __syncthreads();
         bf16x8 sf[4];
@@ -141,7 +158,7 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) oacc = mfma(op.qg[ks], sf[ks], oacc);
         }
-        if (STORE) *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), vs * 4 + w) = pack4(z);
+        pend_z = pack4(z);
         *(bf16x4*)((bf16*)&sZ[w >> 1][l] + 4 * (w & 1)) = pack4(z);
         __syncthreads();
         bf16x8 zf[2];
@@ -166,9 +183,8 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
         if (OUT) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) oacc = mfma(op.hm[ks], zf[ks], oacc);
-            const int64_t tok0 = (b * s.T + (int64_t)c * CH + 16 * w + 4 * g) * s.H + hd;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) io<T>::st(o + (tok0 + (int64_t)i * s.H) * DVD + v, oacc[i]);
+            pend_tok = (b * s.T + (int64_t)c * CH + 16 * w + 4 * g) * s.H + hd;
+            pend_o = oacc;
         }
     };
 
@@ -176,10 +192,16 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
     // issued unconditionally (past the end it re-reads the last chunk), so
     // the number of memory operations per step is fixed and the waits on
     // the vector-memory counter stay exact.
+    // The scheduling barriers pin each group of loads where it is written:
+    // without them the compiler reorders independent loads across the
+    // groups, and the in-order vector-memory counter then makes the first
+    // step of every iteration wait for loads issued just before it.
     Ops<BWD, OUT> P0, P1, P2;
     auto load = [&](Ops<BWD, OUT>& op, int p) {
+        __builtin_amdgcn_sched_barrier(0);
         load_ops<BWD, OUT>(op, A1, A2, C1, C2, it.gn, it.Qg, it.Hm,
                            tile(chunk(p < NT ? p : NT - 1)), w, vs);
+        __builtin_amdgcn_sched_barrier(0);
     };
     load(P0, 0);
     load(P1, 1);
@@ -188,13 +210,22 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
     for (; p + 3 <= NT; p += 3) {
         step(P0, chunk(p));
         load(P0, p + 3);
+        flush();
         step(P1, chunk(p + 1));
         load(P1, p + 4);
+        flush();
         step(P2, chunk(p + 2));
         load(P2, p + 5);
+        flush();
     }
-    if (p < NT) step(P0, chunk(p));
-    if (p + 1 < NT) step(P1, chunk(p + 1));
+    if (p < NT) {
+        step(P0, chunk(p));
+        flush();
+    }
+    if (p + 1 < NT) {
+        step(P1, chunk(p + 1));
+        flush();
+    }
     if (fin) {
 #pragma unroll
         for (int m = 0; m < 2; ++m)

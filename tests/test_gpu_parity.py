@@ -128,3 +128,29 @@ def test_unsupported_length_raises():
                     d["v"][:, :100].contiguous(), d["g"][:, :100].contiguous(),
                     d["beta"][:, :100].contiguous())
     assert ei.value.status == -2
+
+
+# ------------------------------------------------- seven-product ablation
+
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_wy7_gdn_8192x16_sampled_heads(policy):
+    """The expanded seven-product producer gives the same gradients."""
+    _need_gpu()
+    x = WORKLOADS["gdn_1x8192x16"].make()
+    gpu = tl.run_gpu(x, policy, wy7=True)
+    _report(f"wy7 gdn_1x8192x16/{policy}", tl.compare(gpu, x, heads=[(0, 0), (0, 9)]))
+
+
+def test_wy7_kda_2x2048x16():
+    _need_gpu()
+    x = WORKLOADS["kda_2x2048x16"].make()
+    gpu = tl.run_gpu(x, "recompute", wy7=True)
+    _report("wy7 kda_2x2048x16/recompute", tl.compare(gpu, x, heads=[(0, 3), (1, 12)]))
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_wy7_edges_fp32_and_strong_decay(gate):
+    _need_gpu()
+    x = make_inputs(1, 256, 2, gate=gate, dtype="fp32", seed=7,
+                    gate_mean=0.0, h0_std=0.1, dht_std=0.1)
+    _report(f"wy7 strong_decay_fp32/{gate}", tl.compare(tl.run_gpu(x, wy7=True), x))
