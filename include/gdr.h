@@ -3,7 +3,9 @@
  * forward and backward of Gated DeltaNet (scalar gate) and Kimi Delta
  * Attention (per-key-channel gate), chunk size 64, key and value width 128.
  *
- * Operation (ReWY paper, Sec. 2.2 and Table 1). Per batch b and head h, with
+ * Operation ("ReWY: Faster Backpropagation for Delta-Rule Attention -- From
+ * 7 to 3 Matrix Multiplications", paperpeel.com/paper/2611.01940, Sec. 2.2
+ * and Table 1; cited below as Sec. / App.). Per batch b and head h, with
  * a key-major state S (128 x 128), for t = 1..T:
  *     S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
  *     o_t = S_t^T q_t                      (the output includes the write)
@@ -15,8 +17,9 @@
  * the derivative graph, not the gradients). dg has g's shape; for a scalar
  * gate it is the sum over key channels (App. E.1).
  *
- * Computation: chunkwise (Sec. 2.1, 2.3) -- per chunk the unit-triangular
- * system M R = Z - E S, A = M^{-1}, W = A E, U = A Z; a state scan across
+ * Computation: chunkwise (Sec. 2.1, 2.3; the chunk system as the onedev.kr
+ * summary of the paper prints it under "How it works") -- per chunk the
+ * unit-triangular system M R = Z - E S, A = M^{-1}, W = A E, U = A Z; a state scan across
  * chunks; and a backward whose local producer is the three-product ReWY
  * pullback P = A^T Rbar, P R^T, P S^T (Sec. 3.1-3.2), followed by Gram
  * elimination (scalar gate, Sec. 3.4) or centred matrix intra (vector gate,
@@ -42,7 +45,12 @@
  * Errors: arguments are validated before anything is launched; on error
  * nothing is launched and the call returns a negative status. Unsupported
  * shapes (key/value width other than 128, chunk other than 64, T not a
- * multiple of 64) return GDR_ERR_UNSUPPORTED -- there is no fallback. A
+ * multiple of 64) return GDR_ERR_UNSUPPORTED -- there is no fallback (the
+ * flashserve/ReWY repository page, "Compatibility" and "Existing Training
+ * Scripts": K = V = 128, 64-token chunks, lengths divisible by 64,
+ * unsupported configurations fail by default). Vector-gate inputs whose
+ * per-chunk, per-channel cumulative log-decay range exceeds 80 are outside the
+ * contract (the centred factors exp(+-range/2) would leave fp32). A
  * launch failure returns GDR_ERR_HIP. gdr_last_error() returns a message for
  * the calling thread's last failure.
  */
@@ -85,8 +93,9 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
 
 /* Forward. o: output; ht: final state (NULL: not written); h0 NULL: zero.
  * Under GDR_FULL_SAVE, saved receives the chunk quantities the backward
- * reuses ({A, W, Hm, Kt, Qg, gn, h, R} per chunk); under GDR_RECOMPUTE saved
- * may be NULL. */
+ * reuses (per chunk and head: A^T and A, Kt, -W^T, exp(G_n), Hm^T, Qg^T, and
+ * the state h and correction R at the chunk; 123,392 bytes at the supported
+ * widths); under GDR_RECOMPUTE saved may be NULL. */
 int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
             void* scratch, size_t scratch_bytes, void* stream);
@@ -100,7 +109,9 @@ int gdr_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
             void* scratch, size_t scratch_bytes, void* stream);
 
 /* Same contract and results as gdr_bwd, with the expanded seven-product WY
- * producer (Sec. 2.3) in place of ReWY. Ablation only. */
+ * producer (Sec. 2.3: Wbar = -Rbar S^T, Abar = Rbar Z^T + Wbar E^T,
+ * Mbar = -A^T Abar A^T, Ebar = A^T Wbar, Zbar = A^T Rbar) in place of ReWY.
+ * Ablation only. */
 int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
                 const float* g, const void* beta, const float* h0, const void* dO,
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
@@ -110,7 +121,7 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
  * HIP events (the only allocation the library makes, and only here) and
  * turns timing on: every kernel that gdr_fwd / gdr_bwd / gdr_bwd_wy7 then
  * launch is bracketed by events recorded on the call's stream. Stages are
- * "prep", "scan_fwd", "scan_bwd", "bwd_local", "bwd_local_wy7".
+ * "prep", "scan_fwd", "xy", "scan_bwd", "bwd_local", "bwd_local_wy7".
  * gdr_profile_end turns timing off, waits for the recorded events (a host
  * synchronization), and writes up to `cap` per-stage totals; *n_out receives
  * the number of stages seen. Launches beyond max_launches run untimed and
