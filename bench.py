@@ -11,15 +11,22 @@ resident in device memory before the timed region.
 
 Prints one JSON line. Besides the headline value it reports the per-stage
 durations (HIP events recorded by the library on the launch stream over a
-second timed pass), the roofline of the dominant kernel, the forward, the
-full-save policy, the seven-product ablation, the KDA backward at the same
-shape, and the fp64 CPU oracle timed on a bounded sample.
+second timed pass), the roofline of the dominant kernel, the whole-path
+roofline, the forward, the full-save policy, the seven-product ablation, the
+KDA backward at the same shape, and the fp64 CPU oracle on the same workload.
+
+--profile-pass runs a known-size elementwise copy and a few headline steps
+only; it is the command the hardware-counter summaries under profiles/ are
+taken with (the copy calibrates FETCH_SIZE / WRITE_SIZE to bytes).
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,31 +34,40 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CH = 64
+T16, T32, T8, GN = 16384, 32768, 8192, 512   # bf16 64x128, 128x128, 64x64 tiles; exp(G_n)
+M = 1048576                                   # 2 * 64 * 64 * 128 FLOPs
 
-# Algorithmic work per (chunk, head) of each kernel: the bytes it must move
-# (every input read once, every output written once, at their stored types)
-# and its dense matrix-product FLOPs (2 m n k). Tiles: 64 x 128 bf16 = 16 KiB,
-# 64 x 64 bf16 = 8 KiB, 128 x 128 bf16 state = 32 KiB.
-T16, T8, S32 = 16384, 8192, 32768
+# Whole-path algorithmic bytes per token-head of the operator's inputs and
+# outputs (GDN, recompute backward): q, k, v, dO read and dq, dk, dv written
+# in bf16, g, beta, dg, dbeta.
+PATH_BYTES_PER_TOKEN_HEAD = {"gdn_bwd_R": 1804, "kda_bwd_R": 2820}
 
 
-def kernel_work(gate: str, policy: str) -> dict:
-    g_bytes = 64 * 4 if gate == "scalar" else 64 * 128 * 4
+def kernel_work(gate: str) -> dict:
+    """(algorithmic bytes, algorithmic FLOPs) per (chunk, head) of each kernel,
+    as tabulated in the design notes: every operand read once and every result
+    written once at its stored type; FLOPs of the method's dense products."""
+    g_bytes = CH * 4 if gate == "scalar" else CH * 128 * 4
+    beta = CH * 2
+    inputs4 = 4 * T16
     return {
-        # reads q, k, v, g, beta; writes W, U, Kt, Qg, Hm, gn (+ A)
-        "prep": (3 * T16 + g_bytes + 128 + 4 * T16 + T8 + 512 + T8, 4 * 1048576),
-        # reads W, U, Kt, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
-        "scan_fwd": (3 * T16 + 512 + S32 + T16, 2 * 2097152),
-        # reads Kt, Qg, W, Hm, dO, gn; writes dh, Rb
-        "scan_bwd": (3 * T16 + T8 + T16 + 512 + S32 + T16, 3 * 2097152 + 1048576),
-        # reads q, k, v, dO, g, beta, A, R, Rb, h, dh; writes dq, dk, dv, dg, dbeta
-        "bwd_local": (4 * T16 + g_bytes + 128 + T8 + 2 * T16 + 2 * S32 + 3 * T16 + g_bytes + 128,
-                      3 * 1048576 + 3 * 2097152 + 4 * 1048576),
-        "bwd_local_wy7": (4 * T16 + g_bytes + 128 + T8 + 2 * T16 + 2 * S32 + 3 * T16 + g_bytes
-                          + 128, 3 * 1048576 + 3 * 2097152 + 4 * 1048576 + 3145728),
+        # reads q, k, v, dO, g, beta; writes -W, Kt^T, U, Kt, -W^T, X, Y, A^T, A, gn
+        "prep": (inputs4 + g_bytes + beta + 6 * T16 + T32 + 2 * T8 + GN,
+                 int(1.0 * M + 1.0 * M + 0.09 * M + 2 * M + 1 * M + 2 * M)),
+        # reads -W, Kt^T, U, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
+        "scan_fwd": (3 * T16 + GN + T32 + T16, 4 * M),
+        # reads Kt, -W^T, X, Y, gn; writes dh, Rb
+        "scan_bwd": (3 * T16 + T32 + GN + T32 + T16, 4 * M),
+        # reads q, k, v, dO, g, beta, R, Rb, h, dh, A^T; writes dq, dk, dv, dg, dbeta
+        "bwd_local": (inputs4 + g_bytes + beta + 2 * T16 + 2 * T32 + T8 + 3 * T16 + g_bytes + beta,
+                      13 * M),
+        "bwd_local_wy7": (inputs4 + g_bytes + beta + 2 * T16 + 2 * T32 + 2 * T8 + 3 * T16 + g_bytes
+                          + beta, 16 * M),
+        # reads Hm^T, Qg^T, dO; writes X, Y
+        "xy": (T8 + T16 + T16 + T16 + T32, 3 * M),
     }
 
 
@@ -62,9 +78,36 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=2,
-                    help="heads of the workload the CPU oracle runs (bounded sample)")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="calibration copy + a few headline steps, for rocprofv3 counter runs")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; counter summaries record it so a stale
+    summary (kernels changed since the counters were taken) is not used."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "delta_rule_linear_gdr_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, units: int):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None if there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "gdn_bwd_R_1x8192x16_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel sources sha256\[:16\]: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    row = re.search(r"^\| %s \| ([0-9.]+) \| ([0-9.]+) \|" % re.escape(kernel), text, re.M)
+    if not row:
+        return None
+    return round(float(row.group(1)) + float(row.group(2)), 0)
 
 
 def main():
@@ -73,7 +116,6 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import delta_rule_linear_gdr_amd as gdr
     from delta_rule_linear_gdr_amd.inputs import WORKLOADS
@@ -131,19 +173,36 @@ def main():
         st = gdr.profile_end()
         return {k: v[1] / v[0] for k, v in st.items()}  # avg ms per launch
 
-    # ---- headline: GDN backward, recompute policy ----
     run = make_runner(d, gdr.gdr_bwd, "recompute")
-    t0 = time.perf_counter()
+
+    if args.profile_pass:
+        # calibration: an elementwise kernel that reads and writes exactly
+        # 256 MiB each (torch.mul over fp32), then the headline steps
+        n = 64 * 1024 * 1024
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes_each_way": 4 * n,
+                          "steps": args.steps, "kernel_sources": kernel_source_hash()}),
+              flush=True)
+        return
+
+    # ---- headline: GDN backward, recompute policy ----
     ms = time_steps(run, args.steps, args.warmup)
-    wall = time.perf_counter() - t0
     print(f"[bench] gdn bwd-R (1,8192,16): {ms:.4f} ms/step", file=sys.stderr, flush=True)
     stage_ms = profiled(run, args.steps)
     print(f"[bench] stages (ms): {stage_ms}", file=sys.stderr, flush=True)
-    work = kernel_work("scalar", "recompute")
+    work = kernel_work("scalar")
     dom = max(stage_ms, key=stage_ms.get)
     by, fl = work[dom]
     t_s = stage_ms[dom] * 1e-3
     hbm_bound = by / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
+    traffic = measured_traffic(dom, units)
     if hbm_bound:
         achieved = by * units / t_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -152,24 +211,29 @@ def main():
         achieved = fl * units / t_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4)}
+    roof["traffic"] = traffic
     roof["kernel"] = dom
     roof["kernel_ms"] = round(stage_ms[dom], 4)
-    roof["traffic"] = None
-    bwd_flops = sum(work[k][1] for k in ("prep", "scan_fwd", "scan_bwd", "bwd_local")) * units
-    bwd_bytes = sum(work[k][0] for k in ("prep", "scan_fwd", "scan_bwd", "bwd_local")) * units
+    roof["algorithmic_bytes_per_launch"] = by * units
+    steps_bwd = ("prep", "scan_fwd", "scan_bwd", "bwd_local")
+    bwd_flops = sum(work[k][1] for k in steps_bwd) * units
+    path_bytes = PATH_BYTES_PER_TOKEN_HEAD["gdn_bwd_R"] * B * T * H
     tok_s = B * T / (ms * 1e-3)
     detail = {
         "bwd_R_ms": round(ms, 4),
         "bwd_R_tflops": round(bwd_flops / (ms * 1e-3) / 1e12, 2),
-        "bwd_R_kernel_gbs": round(bwd_bytes / (ms * 1e-3) / 1e9, 1),
+        "path_roofline": {"bytes": path_bytes,
+                          "GB/s": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+                          "frac_hbm": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "per_stage_roofline": {},
     }
     for k, v in stage_ms.items():
-        by, fl = work[k]
+        by_k, fl_k = work[k]
         detail["per_stage_roofline"][k] = {
-            "GB/s": round(by * units / (v * 1e-3) / 1e9, 1),
-            "TFLOP/s": round(fl * units / (v * 1e-3) / 1e12, 2)}
+            "GB/s": round(by_k * units / (v * 1e-3) / 1e9, 1),
+            "frac_hbm": round(by_k * units / (v * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "TFLOP/s": round(fl_k * units / (v * 1e-3) / 1e12, 2)}
 
     if not args.no_extra:
         # forward, recompute policy (output + final state)
@@ -192,28 +256,28 @@ def main():
         detail["bwd_A_tokens_per_s"] = round(B * T / (msA * 1e-3), 1)
         # seven-product ablation, both policies
         run7 = make_runner(d, gdr.gdr_bwd_wy7, "recompute")
-        try:
-            ms7 = time_steps(run7, args.steps, args.warmup)
-            run7A = make_runner(d, gdr.gdr_bwd_wy7, "full_save", saved)
-            ms7A = time_steps(run7A, args.steps, args.warmup)
-            detail["wy7_R_ms"] = round(ms7, 4)
-            detail["wy7_A_ms"] = round(ms7A, 4)
-            detail["rewy_speedup_R"] = round(ms7 / ms, 4)
-            detail["rewy_speedup_A"] = round(ms7A / msA, 4)
-            st7 = profiled(run7, max(4, args.steps // 4))
-            stl = stage_ms.get("bwd_local")
-            if stl and "bwd_local_wy7" in st7:
-                detail["rewy_local_kernel_speedup"] = round(st7["bwd_local_wy7"] / stl, 4)
-        except gdr.GdrError as e:
-            detail["wy7"] = f"unavailable: {e}"
+        ms7 = time_steps(run7, args.steps, args.warmup)
+        run7A = make_runner(d, gdr.gdr_bwd_wy7, "full_save", saved)
+        ms7A = time_steps(run7A, args.steps, args.warmup)
+        detail["wy7_R_ms"] = round(ms7, 4)
+        detail["wy7_A_ms"] = round(ms7A, 4)
+        detail["rewy_speedup_R"] = round(ms7 / ms, 4)
+        detail["rewy_speedup_A"] = round(ms7A / msA, 4)
+        st7 = profiled(run7, max(4, args.steps // 4))
+        stl = stage_ms.get("bwd_local")
+        if stl and "bwd_local_wy7" in st7:
+            detail["bwd_local_wy7_ms"] = round(st7["bwd_local_wy7"], 4)
+            detail["rewy_local_kernel_speedup"] = round(st7["bwd_local_wy7"] / stl, 4)
         del saved
         # KDA at the same shape, recompute policy, h0 ~ 0.1 N(0,1)
         xk = WORKLOADS["kda_1x8192x16"].make()
         dk_ = to_dev(xk)
         runK = make_runner(dk_, gdr.gdr_bwd, "recompute")
         msK = time_steps(runK, args.steps, args.warmup)
+        kpath = PATH_BYTES_PER_TOKEN_HEAD["kda_bwd_R"] * B * T * H
         detail["kda_bwd_R_ms"] = round(msK, 4)
         detail["kda_bwd_R_tokens_per_s"] = round(B * T / (msK * 1e-3), 1)
+        detail["kda_path_frac_hbm"] = round(kpath / (msK * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         detail["kda_stage_ms"] = {k: round(v, 4) for k, v in profiled(runK, args.steps).items()}
         del dk_, xk
 
@@ -221,7 +285,7 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         threads = oracle.default_threads()
-        heads = [(0, h) for h in range(args.cpu_heads)]
+        heads = [(0, h) for h in range(H)]
         t0 = time.perf_counter()
         for b, h in heads:
             sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
@@ -231,9 +295,8 @@ def main():
         frac = len(heads) / H
         cpu = {"value": round(B * T * frac / tc, 2), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{len(heads)} of {H} heads of GDN (1,8192,16): fp64 token-recurrence "
-                         f"backward incl. its forward recompute, {tc:.1f} s; value scaled to "
-                         f"whole (B,T) tokens"}
+               "sample": f"{len(heads)} of {H} heads of GDN (1,8192,16) (the whole workload): fp64 "
+                         f"token-recurrence backward incl. its forward recompute, {tc:.1f} s"}
 
     line = {
         "metric": "GDN/KDA backward tokens/s + TFLOP/s (% roofline) at (1,8192,16), C=64, d=128",
@@ -254,7 +317,6 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": detail,
-        "wall_s": round(wall, 2),
     }
     print(json.dumps(line), flush=True)
 
