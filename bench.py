@@ -61,6 +61,8 @@ def kernel_work(gate: str) -> dict:
         "scan_fwd": (3 * T16 + GN + T32 + T16, 4 * M),
         # reads Kt, -W^T, X, Y, gn; writes dh, Rb
         "scan_bwd": (3 * T16 + T32 + GN + T32 + T16, 4 * M),
+        # both scans in one launch
+        "scan_pair": (3 * T16 + GN + T32 + T16 + 3 * T16 + T32 + GN + T32 + T16, 8 * M),
         # reads q, k, v, dO, g, beta, R, Rb, h, dh, A^T; writes dq, dk, dv, dg, dbeta
         "bwd_local": (inputs4 + g_bytes + beta + 2 * T16 + 2 * T32 + T8 + 3 * T16 + g_bytes + beta,
                       13 * M),
@@ -215,7 +217,7 @@ def main():
     roof["kernel"] = dom
     roof["kernel_ms"] = round(stage_ms[dom], 4)
     roof["algorithmic_bytes_per_launch"] = by * units
-    steps_bwd = ("prep", "scan_fwd", "scan_bwd", "bwd_local")
+    steps_bwd = ("prep", "scan_pair", "bwd_local")
     bwd_flops = sum(work[k][1] for k in steps_bwd) * units
     path_bytes = PATH_BYTES_PER_TOKEN_HEAD["gdn_bwd_R"] * B * T * H
     tok_s = B * T / (ms * 1e-3)

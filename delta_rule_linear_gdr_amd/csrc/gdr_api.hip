@@ -187,9 +187,11 @@ int hip_fail(hipError_t e, const char* what)
 }
 
 // ---- optional per-stage timing (gdr_profile_begin / gdr_profile_end) ----
-enum Stage { ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE };
-const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "xy", "scan_bwd", "bwd_local",
-                                        "bwd_local_wy7"};
+enum Stage {
+    ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_SCAN_PAIR, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE
+};
+const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "xy", "scan_bwd", "scan_pair",
+                                        "bwd_local", "bwd_local_wy7"};
 
 struct Profiler {
     std::mutex mu;
@@ -270,14 +272,14 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
             return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A | PREP_AF, st);
         });
         if (e != hipSuccess) return hip_fail(e, "prep");
-        e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, nullptr, nullptr, st); });
-        if (e != hipSuccess) return hip_fail(e, "scan_fwd");
+        e = timed(ST_SCAN_PAIR, st, [&] { return launch_scan_pair(s, in, it, dh0, st); });
+        if (e != hipSuccess) return hip_fail(e, "scan_pair");
     } else {
         e = timed(ST_XY, st, [&] { return launch_xy(s, in, it, st); });
         if (e != hipSuccess) return hip_fail(e, "xy");
+        e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
+        if (e != hipSuccess) return hip_fail(e, "scan_bwd");
     }
-    e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
-    if (e != hipSuccess) return hip_fail(e, "scan_bwd");
     e = timed(wy7 ? ST_BWD_LOCAL_WY7 : ST_BWD_LOCAL, st,
               [&] { return launch_bwd_local(s, in, it, gr, wy7, st); });
     if (e != hipSuccess) return hip_fail(e, "bwd_local");

@@ -95,6 +95,10 @@ hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, vo
 // Reverse state scan. Writes dh and Rb when set, and dh0 when dh0 != null.
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                            hipStream_t st);
+// Both scans of the recompute backward in one launch (the reverse scan does
+// not depend on the forward one): h, R, dh, Rb and dh0.
+hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
+                            hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st);

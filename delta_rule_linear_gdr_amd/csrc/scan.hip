@@ -34,9 +34,9 @@ namespace {
 
 constexpr int NVS = DVD / 16;  // value slices (workgroups) per head
 
-__device__ __forceinline__ void map_block(int nblk, int& bh, int& vs)
+__device__ __forceinline__ void map_block(int nblk, int block, int& bh, int& vs)
 {
-    int id = blockIdx.x;
+    int id = block;
     if (nblk % 8 == 0) {
         const int per = nblk / 8;
         id = (id % 8) * per + id / 8;
@@ -86,11 +86,14 @@ __device__ __forceinline__ void load_ops(Ops<BWD, OUT>& o, const bf16* A1, const
     }
 }
 
+// One workgroup's walk over the chunks. `block` is its index among the
+// B * H * 8 workgroups of this scan.
 template <bool BWD, bool OUT, bool STORE, typename T>
-__global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it, T* o, float* fin)
+__device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, const Inter& it, T* o,
+                                          float* fin, int block)
 {
     int bh, vs;
-    map_block((int)(s.B * s.H * NVS), bh, vs);
+    map_block((int)(s.B * s.H * NVS), block, bh, vs);
     const int64_t b = bh / s.H, hd = bh % s.H;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id(), r = lane_r(), g = lane_g();
@@ -235,6 +238,26 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
     }
 }
 
+template <bool BWD, bool OUT, bool STORE, typename T>
+__global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it, T* o, float* fin)
+{
+    scan_body<BWD, OUT, STORE, T>(s, in, it, o, fin, blockIdx.x);
+}
+
+// The two scans of the recompute backward in one launch: the reverse scan
+// reads only prep's operands (Kt, -W^T, X, Y, gn), not the forward states,
+// so the first B*H*8 workgroups walk forward and the next B*H*8 walk
+// backward side by side (each half keeps its XCD mapping, the half size
+// being a multiple of 8).
+__global__ __launch_bounds__(256) void scan_pair_kernel(Shape s, Inputs in, Inter it, float* dh0)
+{
+    const int nblk = (int)(s.B * s.H * NVS);
+    if ((int)blockIdx.x < nblk)
+        scan_body<false, false, true, bf16>(s, in, it, nullptr, nullptr, blockIdx.x);
+    else
+        scan_body<true, false, true, bf16>(s, in, it, nullptr, dh0, blockIdx.x - nblk);
+}
+
 }  // namespace
 
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o, float* ht,
@@ -264,4 +287,14 @@ hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, fl
     return hipGetLastError();
 }
 
+}  // namespace gdr
+
+namespace gdr {
+hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
+                            hipStream_t st)
+{
+    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    scan_pair_kernel<<<2 * nblk, 256, 0, st>>>(s, in, it, dh0);
+    return hipGetLastError();
+}
 }  // namespace gdr

@@ -121,7 +121,8 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
  * HIP events (the only allocation the library makes, and only here) and
  * turns timing on: every kernel that gdr_fwd / gdr_bwd / gdr_bwd_wy7 then
  * launch is bracketed by events recorded on the call's stream. Stages are
- * "prep", "scan_fwd", "xy", "scan_bwd", "bwd_local", "bwd_local_wy7".
+ * "prep", "scan_fwd", "xy", "scan_bwd", "scan_pair" (both scans of the
+ * recompute backward in one launch), "bwd_local", "bwd_local_wy7".
  * gdr_profile_end turns timing off, waits for the recorded events (a host
  * synchronization), and writes up to `cap` per-stage totals; *n_out receives
  * the number of stages seen. Launches beyond max_launches run untimed and
