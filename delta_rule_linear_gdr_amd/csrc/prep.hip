@@ -74,8 +74,11 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
     __shared__ float sG[GSZ];
     __shared__ float sCen[DKD];
     __shared__ float sBeta[CH];
+    // L, then A = (I + L)^{-1} in place: block row i reads its L blocks
+    // before a barrier and only then writes its A blocks; a diagonal block
+    // is read and rewritten by one wave.
     __shared__ __attribute__((aligned(16))) float sL[CH * LP];
-    __shared__ __attribute__((aligned(16))) float sA[CH * LP];
+    float* const sA = sL;
     __shared__ __attribute__((aligned(16))) float sT[3 * 16 * TP];
     __shared__ bf16x8 sHmT[8 * 64];   // Hm^T frag (M = 64 tok j, K = 64 tok i)
     __shared__ bf16x8 sQgT[16 * 64];  // Qg^T frag (M = 128 key, K = 64 tok)
@@ -208,6 +211,64 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
         }
     }
 
+    __syncthreads();  // sL complete
+
+    // ---- 3. A = (I + L)^{-1}: diagonal 16 x 16 blocks, then block rows ----
+    {
+        // zero the upper blocks of sA
+        for (int e = tid; e < 6 * 256; e += 256) {
+            // upper blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+            const int bk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+            const int bi = bk < 3 ? 0 : bk < 5 ? 1 : 2;
+            const int bj = bi == 0 ? bk + 1 : bi == 1 ? bk - 1 : 3;
+            sA[(16 * bi + rr) * LP + 16 * bj + cc] = 0.f;
+        }
+        if (l < 16) {
+            const int base = 16 * w;
+            float x[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float acc = (i == l) ? 1.f : 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc -= sL[(base + i) * LP + base + m] * x[m];
+                x[i] = acc;
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
+        }
+        __syncthreads();
+        const int jb = w, rr = (tid >> 2) & 15, c4 = (tid & 3) * 4;
+        for (int bi = 1; bi < 4; ++bi) {
+            if (jb < bi) {
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int lb = jb; lb < bi; ++lb) {
+#pragma unroll
+                    for (int m = 0; m < 16; ++m) {
+                        const float lv = sL[(16 * bi + rr) * LP + 16 * lb + m];
+                        const float4 a4 = *(const float4*)&sA[(16 * lb + m) * LP + 16 * jb + c4];
+                        acc.x += lv * a4.x; acc.y += lv * a4.y;
+                        acc.z += lv * a4.z; acc.w += lv * a4.w;
+                    }
+                }
+                *(float4*)&sT[(jb * 16 + rr) * TP + c4] = acc;
+            }
+            __syncthreads();
+            if (jb < bi) {
+                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    const float dv = sA[(16 * bi + rr) * LP + 16 * bi + m];
+                    const float4 t4 = *(const float4*)&sT[(jb * 16 + m) * TP + c4];
+                    acc.x += dv * t4.x; acc.y += dv * t4.y;
+                    acc.z += dv * t4.z; acc.w += dv * t4.w;
+                }
+                *(float4*)&sA[(16 * bi + rr) * LP + 16 * jb + c4] =
+                    make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
+            }
+            __syncthreads();
+        }
+    }
+
     // ---- 4. transposed operands through X * I (wave w: key / value slab w) ----
     bf16x8 ET[2][2], ZT[2][2], OT[2][2];  // [n][ks]: E^T, Z^T, dO^T frags
     {
@@ -321,63 +382,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             if (out) st_row8_frag(it.Qg + t * (CH * DKD), i, f0, qx);
         }
     }
-    __syncthreads();  // sL complete
-
-    // ---- 3. A = (I + L)^{-1}: diagonal 16 x 16 blocks, then block rows ----
-    {
-        // zero the upper blocks of sA
-        for (int e = tid; e < 6 * 256; e += 256) {
-            // upper blocks (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-            const int bk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
-            const int bi = bk < 3 ? 0 : bk < 5 ? 1 : 2;
-            const int bj = bi == 0 ? bk + 1 : bi == 1 ? bk - 1 : 3;
-            sA[(16 * bi + rr) * LP + 16 * bj + cc] = 0.f;
-        }
-        if (l < 16) {
-            const int base = 16 * w;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == l) ? 1.f : 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc -= sL[(base + i) * LP + base + m] * x[m];
-                x[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
-        }
-        __syncthreads();
-        const int jb = w, rr = (tid >> 2) & 15, c4 = (tid & 3) * 4;
-        for (int bi = 1; bi < 4; ++bi) {
-            if (jb < bi) {
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int lb = jb; lb < bi; ++lb) {
-#pragma unroll
-                    for (int m = 0; m < 16; ++m) {
-                        const float lv = sL[(16 * bi + rr) * LP + 16 * lb + m];
-                        const float4 a4 = *(const float4*)&sA[(16 * lb + m) * LP + 16 * jb + c4];
-                        acc.x += lv * a4.x; acc.y += lv * a4.y;
-                        acc.z += lv * a4.z; acc.w += lv * a4.w;
-                    }
-                }
-                *(float4*)&sT[(jb * 16 + rr) * TP + c4] = acc;
-            }
-            __syncthreads();
-            if (jb < bi) {
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const float dv = sA[(16 * bi + rr) * LP + 16 * bi + m];
-                    const float4 t4 = *(const float4*)&sT[(jb * 16 + m) * TP + c4];
-                    acc.x += dv * t4.x; acc.y += dv * t4.y;
-                    acc.z += dv * t4.z; acc.w += dv * t4.w;
-                }
-                *(float4*)&sA[(16 * bi + rr) * LP + 16 * jb + c4] =
-                    make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
-            }
-            __syncthreads();
-        }
-    }
+    __syncthreads();  // sQgT complete
 
     // ---- 5. W = A E, W^T = E^T A^T, U = A Z; A ----
     {
