@@ -78,8 +78,20 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // seven-product producer: Rb, Z (M = tok, K = val), E, W (M = tok,
     // K = key) with W = Rb h^T, Abar^T (M = col, K = row) and X (M = tok,
     // K = tok) with X = A^T Abar.
+    // Vector gate (ReWY): each wave also parks the lo halves of its centred
+    // consumer operands (3 operands x 2 token slabs) at lds + NLDS + w * 384;
+    // the seven-product variant has no LDS left for them and keeps them in
+    // registers.
+    constexpr bool LO_LDS = VEC && !WY7;
     constexpr int NLDS = WY7 ? 9216 : 5120;
-    __shared__ bf16x8 lds[NLDS];
+    __shared__ bf16x8 lds[NLDS + (LO_LDS ? NW * 6 * 64 : 0)];
+    bf16x8* const lLo = lds + NLDS + (LO_LDS ? w * 6 * 64 : 0);
+    bf16x8 loReg[LO_LDS ? 1 : 6];
+    auto lo_get = [&](int x) -> bf16x8 { return LO_LDS ? lLo[x * 64 + l] : loReg[LO_LDS ? 0 : x]; };
+    auto lo_set = [&](int x, const bf16x8& v) {
+        if (LO_LDS) lLo[x * 64 + l] = v;
+        else loReg[LO_LDS ? 0 : x] = v;
+    };
     bf16x8* const lR = lds;
     bf16x8* const lO = lds + 1024;
     bf16x8* const lP = lds + 2048;                      // ReWY
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // and Y'U_y with opposite signs), so Y', Q', E' are carried as bf16
     // hi + lo pairs; a single bf16 rounding would dominate dg for strong
     // decays.
-    bf16x8 B0[2], B1[2], B2[2], L0[2], L1[2], L2[2];
+    bf16x8 B0[2], B1[2], B2[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         if (VEC) {
@@ -340,9 +352,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                     qq[hh][e] -= (float)B1[ks][4 * hh + e];
                     ee[hh][e] -= (float)B2[ks][4 * hh + e];
                 }
-            L0[ks] = pack_pi(y[0], y[1]);
-            L1[ks] = pack_pi(qq[0], qq[1]);
-            L2[ks] = pack_pi(ee[0], ee[1]);
+            lo_set(0 * 2 + ks, pack_pi(y[0], y[1]));
+            lo_set(1 * 2 + ks, pack_pi(qq[0], qq[1]));
+            lo_set(2 * 2 + ks, pack_pi(ee[0], ee[1]));
         } else {
             B0[ks] = pack_pi(KC[2 * ks], KC[2 * ks + 1]);
             B1[ks] = pack_pi(QC[2 * ks], QC[2 * ks + 1]);
@@ -458,7 +470,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         for (int e = 0; e < 4; ++e) {
             const int ks = m >> 1, sl = 4 * (m & 1) + e;
             float kv = (float)B0[ks][sl];
-            if (VEC) kv = (kv + (float)L0[ks][sl]) * __expf(Gt(m, e) - cen);
+            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - cen);
             colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
         }
     }
@@ -470,6 +482,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     //      the four consumer products, chain rules, dq / dk, the per-token
     //      dbeta partials and (vector gate) dg with a running suffix sum ----
     float carry = extra;  // vector gate: suffix sum of Gbar over later tokens
+    // bf16 outputs: dq / dk of token tiles 2s and 2s + 1 are turned into rows
+    // (4 consecutive keys per lane, one 8-byte store) by one identity product
+    // per tile; exact, since each output is a bf16 value times 1.
+    constexpr bool ROWSTORE = sizeof(T) == 2;
+    f32x4 dqP[2], dkP[2];
+    const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
 #pragma unroll
     for (int m = 3; m >= 0; --m) {
         // E = P h^T (ReWY) or A^T W with W = Rb h^T (seven-product); both are -Eb_dir
@@ -494,8 +512,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 X1 = mfma(a1, B0[ks], X1);  // Gam K    | D Y'
                 X3 = mfma(a3, B0[ks], X3);  // Gq K     | Hb Y'
                 if (VEC) {
-                    X1 = mfma(a1, L0[ks], X1);
-                    X3 = mfma(a3, L0[ks], X3);
+                    const bf16x8 lo = lo_get(0 * 2 + ks);
+                    X1 = mfma(a1, lo, X1);
+                    X3 = mfma(a3, lo, X3);
                 }
             }
             if (ks == 1 || m < 2) {
@@ -503,8 +522,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 X2 = mfma(a2, VEC ? B2[ks] : B0[ks], X2);  // Gam^T bK | D^T E'
                 X4 = mfma(a4, B1[ks], X4);                 // Gq^T Q   | Hb^T Q'
                 if (VEC) {
-                    X2 = mfma(a2, L2[ks], X2);
-                    X4 = mfma(a4, L1[ks], X4);
+                    X2 = mfma(a2, lo_get(2 * 2 + ks), X2);
+                    X4 = mfma(a4, lo_get(1 * 2 + ks), X4);
                 }
             }
         }
@@ -523,8 +542,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 const float d = G - cen;
                 al = __expf(d);
                 ze = __expf(-d);
-                kv = (kv + (float)L0[ks][sl]) * al;
-                qv = (qv + (float)L1[ks][sl]) * ze;
+                kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * al;
+                qv = (qv + (float)lo_get(1 * 2 + ks)[sl]) * ze;
             }
             const float eb = -E[e];  // Eb_dir = -P h^T
             float dq = gam * Qb[e];
@@ -543,9 +562,28 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 br[e] += kv * X1[e];
                 Ga[e] += bt * kv * X1[e] - kv * X2[e] + qv * X3[e] - kv * X4[e];
             }
-            const int off = i * ld + f;
-            io<T>::st(dqo + off, dq);
-            io<T>::st(dko + off, dk);
+            if (ROWSTORE) {
+                dqP[m & 1][e] = dq;
+                dkP[m & 1][e] = dk;
+            } else {
+                const int off = i * ld + f;
+                io<T>::st(dqo + off, dq);
+                io<T>::st(dko + off, dk);
+            }
+        }
+        if (ROWSTORE && (m & 1) == 0) {
+            // tiles m and m + 1 -> frag (M = key tile w, K = tokens) -> rows
+            const bf16x8 aq = pack_pi(dqP[0], dqP[1]), ak = pack_pi(dkP[0], dkP[1]);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                // lane: d*[tok 16 (m + hh) + r][key 16 w + 4 g + e]
+                const f32x4 tq = mfma(aq, hh ? Ip1 : Ip0, zero4());
+                const f32x4 tk = mfma(ak, hh ? Ip1 : Ip0, zero4());
+                const int off = (16 * (m + hh) + r) * ld + 16 * w + 4 * g;
+                float xq[4] = {tq[0], tq[1], tq[2], tq[3]}, xk[4] = {tk[0], tk[1], tk[2], tk[3]};
+                store4(dqo + off, xq);
+                store4(dko + off, xk);
+            }
         }
         // per-token sums over this wave's features
 #pragma unroll
