@@ -123,50 +123,97 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const T* betai = (const T*)in.beta + tok0;
     T* dbo = (T*)gr.dbeta + tok0;
 
+    // ---- every global read of this chunk, issued before the first is used
+    //      (one memory round trip instead of one per phase) ----
+    typedef decltype(ld4raw(q)) R4;
+    typedef decltype(ld8raw(q)) R8;
+    const bf16* const Rbg = it.Rb + t * (CH * DVD);
+    const bf16* const Rg = it.R + t * (CH * DVD);
+    const bf16* const hg = it.h + t * (DKD * DVD);
+    const bf16* const dhg = it.dh + t * (DKD * DVD);
+    const bf16* const ATg = it.AT + t * (CH * CH);
+    const bf16* const Afg = it.Af + t * (CH * CH);
+    // (beta and a scalar gate are read by every wave, so that no branch
+    // has to wait for them)
+    const T braw = betai[l * Hs];
+    float graw[VEC ? 16 : 1];
+    if (VEC) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) graw[VEC ? 4 * m + e : 0] = gin[(16 * m + 4 * g + e) * ld + f];
+    } else {
+        graw[0] = gin[l * Hs];
+    }
+    bf16x4 rbq[4], rq[4], hq[8], dhq[8];
+    bf16x8 atf[6];  // A^T frags m * 2 + 1 (m = 0..3), then m * 2 + 0 (m = 0, 1)
+    R4 vr[4], orw[4];
+    R8 kr[4], qr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rbq[i] = *(const bf16x4*)ctile_ptr(Rbg, w * 4 + i);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) atf[m] = ld_frag(ATg, m * 2 + 1);
+    atf[4] = ld_frag(ATg, 0);
+    atf[5] = ld_frag(ATg, 2);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vr[m] = ld4raw(v + (16 * m + r) * ld + 16 * w + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rq[i] = *(const bf16x4*)ctile_ptr(Rg, w * 4 + i);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) orw[m] = ld4raw(dO + (16 * m + r) * ld + 16 * w + 4 * g);
+#pragma unroll
+    for (int vt = 0; vt < 8; ++vt) {
+        hq[vt] = *(const bf16x4*)ctile_ptr(hg, vt * 8 + w);
+        dhq[vt] = *(const bf16x4*)ctile_ptr(dhg, vt * 8 + w);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        kr[m] = ld8raw(k + (16 * m + r) * ld + 32 * (w >> 1) + 8 * g);
+        qr[m] = ld8raw(q + (16 * m + r) * ld + 32 * (w >> 1) + 8 * g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
     // ---- 0. gates, beta; zero the consumer operand buffers ----
     float Gv[4][4];  // vector gate: G at (tok 16 it + 4 g + e, f)
     float Gnf, cen = 0.f;
-    if (tid < CH) sBeta[tid] = io<T>::ld(betai + tid * Hs);
+    if (w == 0) sBeta[l] = to_f32(braw);
     if (VEC) {
         float x[4][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[m][e] = gin[(16 * m + 4 * g + e) * ld + f];
+            for (int e = 0; e < 4; ++e) x[m][e] = graw[VEC ? 4 * m + e : 0];
         float base = 0.f, mx = -INFINITY, mn = INFINITY;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
             for (int e = 1; e < 4; ++e) x[m][e] += x[m][e - 1];
+            // exclusive prefix over the four row groups of this tile
             const float tot = x[m][3];
-            float incl = tot;
-            float y = __shfl_up(incl, 16);
-            if (g >= 1) incl += y;
-            y = __shfl_up(incl, 32);
-            if (g >= 2) incl += y;
-            const float tile_tot = __shfl(incl, 48 + r);
+            const float p16 = partner16(tot);
+            const float pair = tot + p16;
+            const float p32 = partner32(pair);
+            const float excl = ((g & 1) ? p16 : 0.f) + ((g & 2) ? p32 : 0.f);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                Gv[m][e] = x[m][e] + (incl - tot) + base;
+                Gv[m][e] = x[m][e] + excl + base;
                 mx = fmaxf(mx, Gv[m][e]);
                 mn = fminf(mn, Gv[m][e]);
             }
-            base += tile_tot;
+            base += pair + p32;
         }
-        Gnf = __shfl(Gv[3][3], 48 + r);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        mn = fminf(mn, __shfl_xor(mn, 16));
-        mn = fminf(mn, __shfl_xor(mn, 32));
+        // G at the last token (row group 3) to every row group
+        const float pa = partner16(Gv[3][3]);
+        const float b1 = (g & 1) ? Gv[3][3] : pa;
+        const float pb = partner32(b1);
+        Gnf = (g & 2) ? b1 : pb;
+        mx = fmaxf(mx, partner16(mx));
+        mx = fmaxf(mx, partner32(mx));
+        mn = fminf(mn, partner16(mn));
+        mn = fminf(mn, partner32(mn));
         cen = 0.5f * (mx + mn);
     } else if (w == 0) {
-        float x = gin[l * Hs];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (l >= off) x += y;
-        }
-        sG[l] = x;
+        sG[l] = wave_incl_scan(graw[0]);
     }
     {
         const bf16x8 z8 = {};
@@ -185,23 +232,17 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 
     // ---- 1a. P^T = Rb^T A for value tile w ----
     {
-        const bf16* Rb = it.Rb + t * (CH * DVD);
-        const bf16* AT = it.AT + t * (CH * CH);
-        bf16x8 RbT[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            RbT[ks] = cat8(*(const bf16x4*)ctile_ptr(Rb, w * 4 + 2 * ks),
-                           *(const bf16x4*)ctile_ptr(Rb, w * 4 + 2 * ks + 1));
+        const bf16x8 RbT[2] = {cat8(rbq[0], rbq[1]), cat8(rbq[2], rbq[3])};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             // A^T is upper triangular in (i, j): token slab 0 only reaches i < 32
-            f32x4 acc = mfma(RbT[1], ld_frag(AT, m * 2 + 1), zero4());
-            if (m < 2) acc = mfma(RbT[0], ld_frag(AT, m * 2 + 0), acc);
+            f32x4 acc = mfma(RbT[1], atf[m], zero4());
+            if (m < 2) acc = mfma(RbT[0], atf[4 + m], acc);
             // lane: P[tok 16 m + r][val 16 w + 4 g + e]
             const int i = 16 * m + r;
             const float bt = sBeta[i];
-            float dvv[4], vx[4];
-            load4(v + i * ld + 16 * w + 4 * g, vx);
+            const f32x4 vx = tof4(vr[m]);
+            float dvv[4];
             float pv = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -209,8 +250,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 pv += acc[e] * vx[e];
             }
             store4(dvo + i * ld + 16 * w + 4 * g, dvv);
-            pv += __shfl_xor(pv, 16);
-            pv += __shfl_xor(pv, 32);
+            pv = sum_rows(pv);
             if (g == 0) sRedP[w][i] = pv;
             if (!WY7) st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
         }
@@ -222,8 +262,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             for (int m = 0; m < 4; ++m) {
                 const f32x4 cc = mfma(RbT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
                 st_half(lRb, m * 4 + (w >> 1), w & 1, pack4(cc));
-                float vx[4];
-                load4(v + (16 * m + r) * ld + 16 * w + 4 * g, vx);
+                const f32x4 vx = tof4(vr[m]);
                 const float bt = sBeta[16 * m + r];
                 bf16x4 z4v;
 #pragma unroll
@@ -234,38 +273,26 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     }
     // ---- 1b. R and dO fragments (contraction over values) of value tile w ----
     {
-        const bf16* Rr = it.R + t * (CH * DVD);
-        bf16x8 RT[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            RT[ks] = cat8(*(const bf16x4*)ctile_ptr(Rr, w * 4 + 2 * ks),
-                          *(const bf16x4*)ctile_ptr(Rr, w * 4 + 2 * ks + 1));
+        const bf16x8 RT[2] = {cat8(rq[0], rq[1]), cat8(rq[2], rq[3])};
         const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             // lane: R[tok 16 m + r][val 16 w + 4 g + e]
             const f32x4 cc = mfma(RT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
             st_half(lR, m * 4 + (w >> 1), w & 1, pack4(cc));
-            float ox[4];
-            load4(dO + (16 * m + r) * ld + 16 * w + 4 * g, ox);
-            bf16x4 o4;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = (bf16)ox[e];
-            st_half(lO, m * 4 + (w >> 1), w & 1, o4);
+            st_half(lO, m * 4 + (w >> 1), w & 1, tobf4(orw[m]));
         }
     }
     // ---- 1c. h, dh fragments (M = key tile w, K = values); rowsum(h o dh) ----
     bf16x8 hF[4], dhF[4];
     {
-        const bf16* hb = it.h + t * (DKD * DVD);
-        const bf16* dhb = it.dh + t * (DKD * DVD);
         float hdp[4] = {0.f, 0.f, 0.f, 0.f};
         f32x4 Ch[8], Cd[8];
 #pragma unroll
         for (int vt = 0; vt < 8; ++vt) {
             // lane: h[key 16 w + 4 g + e][val 16 vt + r]
-            const bf16x4 hv = *(const bf16x4*)ctile_ptr(hb, vt * 8 + w);
-            const bf16x4 dv4 = *(const bf16x4*)ctile_ptr(dhb, vt * 8 + w);
+            const bf16x4 hv = hq[vt];
+            const bf16x4 dv4 = dhq[vt];
 #pragma unroll
             for (int e = 0; e < 4; ++e) hdp[e] += (float)hv[e] * (float)dv4[e];
             // lane: h[key 16 w + r][val 16 vt + 4 g + e]
@@ -287,11 +314,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     f32x4 KC[4], QC[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        float x[8];
-        ld_plain8(k, ld, 16 * m, 32 * (w >> 1), x);
-        KC[m] = mfma(pack8(x), Iw, zero4());
-        ld_plain8(q, ld, 16 * m, 32 * (w >> 1), x);
-        QC[m] = mfma(pack8(x), Iw, zero4());
+        KC[m] = mfma(tobf8(kr[m]), Iw, zero4());
+        QC[m] = mfma(tobf8(qr[m]), Iw, zero4());
     }
     if (WY7) {
         // E = diag(beta)(gam * K) fragments (M = tok, K = key) of key tile w:
@@ -366,8 +390,6 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // ---- 2a'. seven-product producer (ablation): W = Rb h^T (so Wbar = -W),
     //      Abar = Rb Z^T + Wbar E^T, X = A^T Abar; Mbar = -X A^T follows below
     bf16x8 WT[2];  // W^T frags (M = key tile w, K = tok), B operands of Eb_dir
-    const bf16* ATg = it.AT + t * (CH * CH);
-    const bf16* Afg = it.Af + t * (CH * CH);
     if (WY7) {
         f32x4 Wc[4];
 #pragma unroll
@@ -474,8 +496,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
         }
     }
-    colsum += __shfl_xor(colsum, 16);
-    colsum += __shfl_xor(colsum, 32);
+    colsum = sum_rows(colsum);
     const float extra = colsum + __expf(Gnf) * sExtra[f];
 
     // ---- 3. per token tile, last to first: producer and state-direct terms,
@@ -601,14 +622,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             suf[3] = Ga[3];
 #pragma unroll
             for (int e = 2; e >= 0; --e) suf[e] = suf[e + 1] + Ga[e];
+            // suffix over the row groups after this one, and the tile total
             const float tot = suf[0];
-            float incl = tot;
-            float y = __shfl_down(incl, 16);
-            if (g < 3) incl += y;
-            y = __shfl_down(incl, 32);
-            if (g < 2) incl += y;
-            const float excl = incl - tot;
-            const float ttot = __shfl(incl, r);  // g = 0 lane holds the tile total
+            const float p16 = partner16(tot);
+            const float pair = tot + p16;
+            const float p32 = partner32(pair);
+            const float excl = ((g & 1) ? 0.f : p16) + ((g & 2) ? 0.f : p32);
+            const float ttot = pair + p32;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dgo[(16 * m + 4 * g + e) * ld + f] = suf[e] + excl + carry;
             carry += ttot;

@@ -132,15 +132,71 @@ __device__ __forceinline__ void put_c_t(bf16* buf, int ld, int m0, int n0, const
     *(bf16x4*)(buf + ccol(n0) * ld + crow(m0, 0)) = v;
 }
 
+// ---------------------------------------------------------------- cross-lane
+// Register-only exchanges (no LDS round trip): DPP row rotations inside a
+// 16-lane row, and the gfx950 permlane swaps between rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
 // Sum over the 16 lanes that share (lane >> 4), i.e. over the columns of a C
-// fragment row group.
+// fragment row group; every lane of the row receives a sum (row rotations
+// by 8, 4, 2, 1).
 __device__ __forceinline__ float sum16(float x)
 {
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    x += __shfl_xor(x, 8);
+    x += dpp_f<0x128>(x);
+    x += dpp_f<0x124>(x);
+    x += dpp_f<0x122>(x);
+    x += dpp_f<0x121>(x);
     return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: scans inside each
+// 16-lane row (row shifts by 1, 2, 4, 8), then the last lane of a row is
+// added to the next row (row_bcast:15, rows 1 and 3) and lane 31 to rows 2
+// and 3 (row_bcast:31). Lanes a shift does not reach add zero.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_zero(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_incl_scan(float x)
+{
+    x += dpp_zero<0x111, 0xf>(x);
+    x += dpp_zero<0x112, 0xf>(x);
+    x += dpp_zero<0x114, 0xf>(x);
+    x += dpp_zero<0x118, 0xf>(x);
+    x += dpp_zero<0x142, 0xa>(x);
+    x += dpp_zero<0x143, 0xc>(x);
+    return x;
+}
+
+// Value held by lane l ^ 16 (rows 0 <-> 1, 2 <-> 3) and by lane l ^ 32.
+// A swap returns this lane's own value in one result and the partner's in
+// the other; comparing bits picks the partner's (if both are equal, either
+// is right). Call these as plain statements, never as an operand of ?: or
+// under a lane-dependent branch: a swap issued with some lanes masked off
+// does not receive those lanes' values.
+__device__ __forceinline__ float partner16(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(p[0] == u ? p[1] : p[0]);
+}
+__device__ __forceinline__ float partner32(float x)
+{
+    const unsigned u = __float_as_uint(x);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(p[0] == u ? p[1] : p[0]);
+}
+// x summed over the lanes l, l ^ 16, l ^ 32, l ^ 48 (the four rows); the
+// same value in all four (addition is commutative).
+__device__ __forceinline__ float sum_rows(float x)
+{
+    x += partner16(x);
+    return x + partner32(x);
 }
 
 
@@ -249,6 +305,25 @@ __device__ __forceinline__ void store4(float* p, const float (&x)[4])
 {
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
 }
+
+// Unconverted reads of 4 and 8 consecutive elements, so that a batch of
+// reads can be issued before the first of them is consumed.
+struct f32x8 {
+    f32x4 a, b;
+};
+__device__ __forceinline__ bf16x4 ld4raw(const bf16* p) { return *(const bf16x4*)p; }
+__device__ __forceinline__ f32x4 ld4raw(const float* p) { return *(const f32x4*)p; }
+__device__ __forceinline__ bf16x8 ld8raw(const bf16* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ f32x8 ld8raw(const float* p)
+{
+    return f32x8{*(const f32x4*)p, *(const f32x4*)(p + 4)};
+}
+__device__ __forceinline__ f32x4 tof4(const bf16x4& v) { return unpack4(v); }
+__device__ __forceinline__ f32x4 tof4(const f32x4& v) { return v; }
+__device__ __forceinline__ bf16x4 tobf4(const bf16x4& v) { return v; }
+__device__ __forceinline__ bf16x4 tobf4(const f32x4& v) { return pack4(v); }
+__device__ __forceinline__ bf16x8 tobf8(const bf16x8& v) { return v; }
+__device__ __forceinline__ bf16x8 tobf8(const f32x8& v) { return cat8(pack4(v.a), pack4(v.b)); }
 
 // Plain-order fragment of a row-major matrix with row stride ld (elements):
 // lane (r, g) gets X[row0 + r][k0 + 8 g .. + 7] as floats.

@@ -102,13 +102,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             sCen[tid] = 0.5f * (mx + mn);
         }
     } else if (w == 0) {
-        float x = in.g[tok0 + l * s.H];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(x, off);
-            if (l >= off) x += y;
-        }
-        sG[l] = x;
+        sG[l] = wave_incl_scan(in.g[tok0 + l * s.H]);
     }
     if (tid < CH) sBeta[tid] = io<T>::ld(beta + tok0 + tid * s.H);
     __syncthreads();
