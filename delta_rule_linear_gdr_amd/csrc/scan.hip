@@ -20,11 +20,15 @@
 //     Sb <- diag(gn) Sb + Qg^T dO - W^T Z
 // Per step: A1 (16 x 128 per wave) times the state slabs, then A2 (32 x 64
 // per wave) times the Z slabs. The chunk operands arrive pre-swizzled in
-// frag/ctile order (kernels.h) and are prefetched three chunks ahead into
-// registers; the only on-chip exchange is the state and Z slabs through LDS
-// (one 16-byte write and a few 16-byte reads per lane, two barriers).
+// frag/ctile order (kernels.h); the only on-chip exchange is the state and
+// Z slabs through LDS (one 16-byte write and a few 16-byte reads per lane,
+// two barriers). The forward launch (with the output O) prefetches them
+// three chunks ahead into registers; the backward launches (the pair, and
+// the reverse scan alone) use the loader-fed form further down.
 // The blockIdx -> (head, slice) map keeps the eight slices of a head on one
-// XCD so they share its L2.
+// XCD so they share its L2. Every slice of a head reads the head's whole
+// A1 and A2 (32 KiB per step), so the step time is set by each CU's
+// L2-to-CU stream rather than by the arithmetic.
 #include "common.h"
 #include "kernels.h"
 
@@ -244,18 +248,215 @@ __global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it,
     scan_body<BWD, OUT, STORE, T>(s, in, it, o, fin, blockIdx.x);
 }
 
-// The two scans of the recompute backward in one launch: the reverse scan
-// reads only prep's operands (Kt, -W^T, X, Y, gn), not the forward states,
-// so the first B*H*8 workgroups walk forward and the next B*H*8 walk
-// backward side by side (each half keeps its XCD mapping, the half size
-// being a multiple of 8).
-__global__ __launch_bounds__(256) void scan_pair_kernel(Shape s, Inputs in, Inter it, float* dh0)
+// ---------------------------------------------------------------------------
+// Loader-fed form of the pair launch. Eight waves per workgroup: waves 0..3
+// run the step above; waves 4..7 only move each step's operand tiles from
+// global memory into a ring of three LDS slots, two steps ahead, with
+// direct-to-LDS loads (global_load_lds_dwordx4: 64 lanes x 16 B = one 1 KiB
+// block per instruction, i.e. one frag tile or two ctiles, copied as is).
+// The compute waves' instruction streams then carry no global loads, so a
+// stall issuing loads behind the shared address unit no longer adds to the
+// step's dependent chain (LDS exchange, MFMA, barrier).
+//
+// Synchronisation uses the two per-step barriers of the step itself:
+// slot p % 3 is read by the compute waves in step p; the loaders refill it
+// for step p + 3 after the first barrier of step p + 1, and wait for step
+// p + 1's blocks before the first barrier of step p + 1.
+namespace fed {
+constexpr int A1 = 0;           // 16 frag tiles of A1
+constexpr int A2 = 16384;       // 16 frag tiles of A2
+constexpr int C1 = 32768;       // ctiles 4 vs .. 4 vs + 3 of C1
+constexpr int C2 = 34816;       // ctiles 8 vs .. 8 vs + 7 of C2 (reverse)
+constexpr int GN = 38912;       // gn (512 B, twice)
+constexpr int SLOT = 39936;
+constexpr int NSLOT = 3;
+constexpr int NB_FWD = 35;      // 1 KiB blocks per step
+constexpr int NB_BWD = 39;
+constexpr int NL_FWD = (NB_FWD + 3) / 4;  // per loader wave (padded)
+constexpr int NL_BWD = (NB_BWD + 3) / 4;
+}  // namespace fed
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt at their
+// maxima), and on the LDS counter only.
+template <int N>
+__device__ __forceinline__ void wait_vm()
 {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// Workgroup barrier with no implied waits (each side waits for exactly what
+// the other reads after it); the clobber keeps memory accesses in place.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Loader wave J (0..3): blocks J, J + 4, ... of one step into `slot`. The
+// block count is padded to a multiple of four by repeating the gn block
+// (same bytes to the same place).
+template <bool BWD, int J>
+__device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, uint8_t* slot)
+{
+    constexpr int NB = BWD ? fed::NB_BWD : fed::NB_FWD;
+    constexpr int NPAD = (NB + 3) / 4 * 4;
+    const int l = lane_id();
+    const bf16* A1 = BWD ? it.Kt : it.Wn;
+    const bf16* A2 = BWD ? it.WnT : it.KtT;
+    const bf16* C1 = BWD ? it.X : it.U;
+#pragma unroll
+    for (int b = J; b < NPAD; b += 4) {
+        const void* src;
+        int dst;
+        if (b < 16) {
+            src = A1 + t * (CH * DKD) + b * 512 + l * 8;
+            dst = fed::A1 + b * 1024;
+        } else if (b < 32) {
+            src = A2 + t * (CH * DKD) + (b - 16) * 512 + l * 8;
+            dst = fed::A2 + (b - 16) * 1024;
+        } else if (b < 34) {
+            src = C1 + t * (CH * DVD) + vs * 1024 + (b - 32) * 512 + l * 8;
+            dst = fed::C1 + (b - 32) * 1024;
+        } else if (BWD && b < 38) {
+            src = it.Y + t * (DKD * DVD) + vs * 2048 + (b - 34) * 512 + l * 8;
+            dst = fed::C2 + (b - 34) * 1024;
+        } else {
+            src = it.gn + t * DKD + (l & 31) * 4;
+            dst = fed::GN;
+        }
+        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + dst), 16, 0, 0);
+    }
+}
+
+template <bool BWD, int J>
+__device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, int bh, int vs, uint8_t* ring)
+{
+    constexpr int NL = BWD ? fed::NL_BWD : fed::NL_FWD;
+    const int NT = (int)s.NT;
+    auto issue = [&](int p) {
+        const int pc = p < NT ? p : NT - 1;  // past the end: the last chunk again
+        const int c = BWD ? NT - 1 - pc : pc;
+        fed_issue<BWD, J>(it, (int64_t)bh * s.NT + c, vs, ring + (p % fed::NSLOT) * fed::SLOT);
+    };
+    issue(0);
+    issue(1);
+    wait_vm<NL>();  // step 0 has landed
+    for (int p = 0; p < NT; ++p) {
+        bar();  // first barrier of step p: slot (p + 2) % 3 is free
+        issue(p + 2);
+        bar();  // second barrier of step p
+        wait_vm<NL>();  // step p + 1 has landed
+    }
+    // no LDS write may still be in flight when the workgroup's LDS is released
+    wait_vm<0>();
+}
+
+template <bool BWD>
+__device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, const Inter& it, float* fin,
+                                            int bh, int vs, const uint8_t* ring)
+{
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = lane_id(), r = lane_r(), g = lane_g();
+    const int NT = (int)s.NT;
+    const int v = 16 * vs + r;
+
+    __shared__ bf16x8 sS[4][64];
+    __shared__ bf16x8 sZ[2][64];
+
+    bf16* Sout = BWD ? it.dh : it.h;
+    bf16* Zout = BWD ? it.Rb : it.R;
+    const float* init = BWD ? in.dht : in.h0;
+
+    f32x4 S[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[m][i] = init ? init[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] : 0.f;
+
+    for (int p = 0; p < NT; ++p) {
+        const int c = BWD ? NT - 1 - p : p;
+        const int64_t t = (int64_t)bh * s.NT + c;
+        const uint8_t* slot = ring + (p % fed::NSLOT) * fed::SLOT;
+        // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile vs)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), vs * 8 + 2 * w + m) = pack4(S[m]);
+        sS[w][l] = pack_pi(S[0], S[1]);
+        wait_lgkm0();
+        bar();
+        bf16x8 sf[4], a1[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            sf[ks] = sS[ks][l];
+            a1[ks] = *(const bf16x8*)(slot + fed::A1 + (w * 4 + ks) * 1024 + l * 16);
+        }
+        // Z = C1 + A1 S   (rows 16w .. 16w + 15)
+        f32x4 z = unpack4(*(const bf16x4*)(slot + fed::C1 + (w * 64 + l) * 8));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) z = mfma(a1[ks], sf[ks], z);
+        const bf16x4 z4 = pack4(z);
+        *(bf16x4*)((bf16*)&sZ[w >> 1][l] + 4 * (w & 1)) = z4;
+        wait_lgkm0();
+        bar();
+        *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), vs * 4 + w) = z4;
+        bf16x8 zf[2], a2[2][2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) zf[ks] = sZ[ks][l];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                a2[m][ks] = *(const bf16x8*)(slot + fed::A2 + ((2 * w + m) * 2 + ks) * 1024 + l * 16);
+        // S <- gn S (+ C2) + A2 Z
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const float4 gv = *(const float4*)(slot + fed::GN + (32 * w + 16 * m + 4 * g) * 4);
+            f32x4 acc = {gv.x * S[m][0], gv.y * S[m][1], gv.z * S[m][2], gv.w * S[m][3]};
+            if (BWD) {
+                const f32x4 y = unpack4(*(const bf16x4*)(slot + fed::C2 + ((2 * w + m) * 64 + l) * 8));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] += y[i];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mfma(a2[m][ks], zf[ks], acc);
+            S[m] = acc;
+        }
+    }
+    if (fin) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fin[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = S[m][i];
+    }
+}
+
+template <bool BWD>
+__device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const Inter& it, float* fin,
+                                         int block, uint8_t* ring)
+{
+    int bh, vs;
+    map_block((int)(s.B * s.H * NVS), block, bh, vs);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    switch (w) {
+    case 4: fed_loader<BWD, 0>(s, it, bh, vs, ring); break;
+    case 5: fed_loader<BWD, 1>(s, it, bh, vs, ring); break;
+    case 6: fed_loader<BWD, 2>(s, it, bh, vs, ring); break;
+    case 7: fed_loader<BWD, 3>(s, it, bh, vs, ring); break;
+    default: fed_compute<BWD>(s, in, it, fin, bh, vs, ring); break;
+    }
+}
+
+// both = 1: the first B*H*8 workgroups walk forward and the next B*H*8
+// walk backward side by side (the reverse scan reads only prep's operands,
+// not the forward states; each half keeps its XCD mapping, the half size
+// being a multiple of 8). both = 0: the reverse scan alone.
+__global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* dh0, int both)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t ring[fed::NSLOT * fed::SLOT];
     const int nblk = (int)(s.B * s.H * NVS);
-    if ((int)blockIdx.x < nblk)
-        scan_body<false, false, true, bf16>(s, in, it, nullptr, nullptr, blockIdx.x);
-    else
-        scan_body<true, false, true, bf16>(s, in, it, nullptr, dh0, blockIdx.x - nblk);
+    if (both && (int)blockIdx.x < nblk) fed_body<false>(s, in, it, nullptr, blockIdx.x, ring);
+    else fed_body<true>(s, in, it, dh0, both ? blockIdx.x - nblk : blockIdx.x, ring);
 }
 
 }  // namespace
@@ -283,7 +484,7 @@ hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, fl
                            hipStream_t st)
 {
     const unsigned nblk = (unsigned)(s.B * s.H * NVS);
-    scan_kernel<true, false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, dh0);
+    scan_fed_kernel<<<nblk, 512, 0, st>>>(s, in, it, dh0, 0);
     return hipGetLastError();
 }
 
@@ -294,7 +495,7 @@ hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, f
                             hipStream_t st)
 {
     const unsigned nblk = (unsigned)(s.B * s.H * NVS);
-    scan_pair_kernel<<<2 * nblk, 256, 0, st>>>(s, in, it, dh0);
+    scan_fed_kernel<<<2 * nblk, 512, 0, st>>>(s, in, it, dh0, 1);
     return hipGetLastError();
 }
 }  // namespace gdr
