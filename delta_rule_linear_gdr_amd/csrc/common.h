@@ -325,6 +325,20 @@ __device__ __forceinline__ bf16x4 tobf4(const f32x4& v) { return pack4(v); }
 __device__ __forceinline__ bf16x8 tobf8(const bf16x8& v) { return v; }
 __device__ __forceinline__ bf16x8 tobf8(const f32x8& v) { return cat8(pack4(v.a), pack4(v.b)); }
 
+__device__ __forceinline__ void to_f8(const bf16x8& v, float (&x)[8])
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)v[e];
+}
+__device__ __forceinline__ void to_f8(const f32x8& v, float (&x)[8])
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[e] = v.a[e];
+        x[4 + e] = v.b[e];
+    }
+}
+
 // Plain-order fragment of a row-major matrix with row stride ld (elements):
 // lane (r, g) gets X[row0 + r][k0 + 8 g .. + 7] as floats.
 template <typename T>

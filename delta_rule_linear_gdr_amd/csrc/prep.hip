@@ -55,7 +55,7 @@ __device__ __forceinline__ void st_row8_frag(bf16* base, int i, int f0, const fl
 }
 
 template <typename T, bool VEC>
-__global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it, int what)
+__global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter it, int what)
 {
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
@@ -90,40 +90,77 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
     const T* beta = (const T*)in.beta;
 
     // ---- 1. gate cumsum (and per-key centre), beta ----
+    // (beta and a scalar gate are read by every wave, so that no branch has
+    // to wait for them)
+    const T braw = beta[tok0 + l * s.H];
+    const float graw = VEC ? 0.f : in.g[tok0 + l * s.H];
     if (VEC) {
-        if (tid < DKD) {
-            float acc = 0.f, mx = -INFINITY, mn = INFINITY;
-            for (int i = 0; i < CH; ++i) {
-                acc += in.g[(tok0 + i * s.H) * DKD + tid];
-                sG[i * DKD + tid] = acc;
-                mx = fmaxf(mx, acc);
-                mn = fminf(mn, acc);
+        // wave w: keys 32 w .. 32 w + 31 as two 16-key passes; lane (r, g)
+        // holds tokens 16 m + 4 g + e of key f (all 32 reads issued first)
+        float x[2][4][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[u][m][e] = in.g[(tok0 + (int64_t)(16 * m + 4 * g + e) * s.H) * DKD + 32 * w + 16 * u + r];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int f = 32 * w + 16 * u + r;
+            float base = 0.f, mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                for (int e = 1; e < 4; ++e) x[u][m][e] += x[u][m][e - 1];
+                // exclusive prefix over the four row groups of this tile
+                const float tot = x[u][m][3];
+                const float p16 = partner16(tot);
+                const float pair = tot + p16;
+                const float p32 = partner32(pair);
+                const float excl = ((g & 1) ? p16 : 0.f) + ((g & 2) ? p32 : 0.f);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float G = x[u][m][e] + excl + base;
+                    sG[(16 * m + 4 * g + e) * DKD + f] = G;
+                    mx = fmaxf(mx, G);
+                    mn = fminf(mn, G);
+                }
+                base += pair + p32;
             }
-            sCen[tid] = 0.5f * (mx + mn);
+            mx = fmaxf(mx, partner16(mx));
+            mx = fmaxf(mx, partner32(mx));
+            mn = fminf(mn, partner16(mn));
+            mn = fminf(mn, partner32(mn));
+            if (g == 0) sCen[f] = 0.5f * (mx + mn);
         }
     } else if (w == 0) {
-        sG[l] = wave_incl_scan(in.g[tok0 + l * s.H]);
+        sG[l] = wave_incl_scan(graw);
     }
-    if (tid < CH) sBeta[tid] = io<T>::ld(beta + tok0 + tid * s.H);
+    if (w == 0) sBeta[l] = to_f32(braw);
     __syncthreads();
 
     auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
     if ((fwdscan || bwdscan) && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
 
-    // plain fragment of row block i0 .. i0+15, keys 32 ks + 8 g .. + 7, with
-    // an optional per-(row, key) scale (vector gate)
-    auto frag_rows = [&](const T* base, int i0, int ks, int kind) -> bf16x8 {
+    // plain fragment of row block i0 .. i0+15, keys 32 ks + 8 g .. + 7: the
+    // unconverted read, then the bf16 operand with an optional per-(row, key)
+    // scale (vector gate)
+    typedef decltype(ld8raw(k)) R8;
+    auto raw_rows = [&](const T* base, int i0, int ks) -> R8 {
+        return ld8raw(base + (i0 + r) * ld + 32 * ks + 8 * g);
+    };
+    auto cook = [&](const R8& raw, int i0, int ks, int kind) -> bf16x8 {
+        if (!VEC || kind == 0) return tobf8(raw);
         float x[8];
-        ld_plain8(base, ld, i0, 32 * ks, x);
-        if (VEC && kind != 0) {
-            const int i = i0 + r, f0 = 32 * ks + 8 * g;
+        to_f8(raw, x);
+        const int i = i0 + r, f0 = 32 * ks + 8 * g;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float d = sG[i * DKD + f0 + e] - sCen[f0 + e];
-                // 1: alpha = exp(G - c) (queries);  2: beta alpha (erase keys);
-                // 3: zeta = exp(c - G) (write keys)
-                x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const float d = sG[i * DKD + f0 + e] - sCen[f0 + e];
+            // 1: alpha = exp(G - c) (queries);  2: beta alpha (erase keys);
+            // 3: zeta = exp(c - G) (write keys)
+            x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
         }
         return pack8(x);
     };
@@ -131,18 +168,43 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
     // ---- 2. L = strict_lower(E Y^T) and Hm = lower_incl(Qg Y^T), 16 x 16 tiles ----
     {
         const bool needH = xy || savexy, needHt = out;
-        for (int x = w; x < 10; x += 4) {
-            // lower 16 x 16 tiles (ti, tj <= ti) in row order
-            const int ti = x >= 6 ? 3 : x >= 3 ? 2 : x >= 1 ? 1 : 0;
-            const int tj = x - ti * (ti + 1) / 2;
+        // lower 16 x 16 tiles (ti, tj <= ti) in row order; wave w takes tiles
+        // w, w + 4, w + 8 and reads the next tile's fragments before it
+        // computes the current one
+        auto tile_ij = [](int x, int& ti, int& tj) {
+            ti = x >= 6 ? 3 : x >= 3 ? 2 : x >= 1 ? 1 : 0;
+            tj = x - ti * (ti + 1) / 2;
+        };
+        R8 buf[2][3][4];  // [parity][K rows ti, K rows tj, Q rows ti][ks]
+        auto read_tile = [&](int x, R8 (&b)[3][4]) {
+            int ti, tj;
+            tile_ij(x, ti, tj);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                b[0][ks] = raw_rows(k, 16 * ti, ks);
+                b[1][ks] = raw_rows(k, 16 * tj, ks);
+                b[2][ks] = raw_rows(q, 16 * ti, ks);
+            }
+        };
+        read_tile(w, buf[0]);
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int x = w + 4 * u;
+            if (x >= 10) break;
+            // (unconditional, the last tile again past the end, so that the
+            // waits on the in-order memory counter stay exact)
+            read_tile(x + 4 < 10 ? x + 4 : 9, buf[(u + 1) & 1]);
+            int ti, tj;
+            tile_ij(x, ti, tj);
+            const R8(&b)[3][4] = buf[u & 1];
             f32x4 aL = zero4(), aH = zero4(), aHt = zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ki = frag_rows(k, 16 * ti, ks, 2);  // E' rows (scalar: K)
-                const bf16x8 kj = frag_rows(k, 16 * tj, ks, 3);  // Y' rows (scalar: K)
+                const bf16x8 ki = cook(b[0][ks], 16 * ti, ks, 2);  // E' rows (scalar: K)
+                const bf16x8 kj = cook(b[1][ks], 16 * tj, ks, 3);  // Y' rows (scalar: K)
                 aL = mfma(ki, kj, aL);
                 if (needH || needHt) {
-                    const bf16x8 qi = frag_rows(q, 16 * ti, ks, 1);  // Q' rows (scalar: Q)
+                    const bf16x8 qi = cook(b[2][ks], 16 * ti, ks, 1);  // Q' rows (scalar: Q)
                     if (needH) aH = mfma(qi, kj, aH);
                     if (needHt) aHt = mfma(kj, qi, aHt);
                 }
@@ -202,6 +264,28 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
                 *(bf16x8*)(dst + ((0 * 2 + 1) * 64 + l) * 8) = z8;
                 *(bf16x8*)(dst + ((1 * 2 + 1) * 64 + l) * 8) = z8;
             }
+        }
+    }
+
+    // ---- reads of phases 4 and 4b, issued now so that they land during the
+    //      solve: K, V, dO, Q fragments of slab w, and four K and Q row pieces
+    //      per thread (dO is read only when X, Y are made; otherwise Q again) ----
+    R8 rk[4], rv[4], ro[4], rq[4], rkr[4], rqr[4];
+    {
+        const T* dOs = xy ? dO : q;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            rk[mt] = raw_rows(k, 16 * mt, w);
+            rv[mt] = raw_rows(v, 16 * mt, w);
+            ro[mt] = raw_rows(dOs, 16 * mt, w);
+            rq[mt] = raw_rows(q, 16 * mt, w);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int id = tid + 256 * u;
+            const int i = id >> 4, f0 = (id & 15) * 8;
+            rkr[u] = ld8raw(k + i * ld + f0);
+            rqr[u] = ld8raw(q + i * ld + f0);
         }
     }
 
@@ -271,7 +355,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
         f32x4 KC[4][2];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            const bf16x8 kf = frag_rows(k, 16 * mt, w, 0);
+            const bf16x8 kf = tobf8(rk[mt]);
             KC[mt][0] = mfma(kf, I0, zero4());
             KC[mt][1] = mfma(kf, I1, zero4());
         }
@@ -306,7 +390,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             f32x4 VC[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 vf = frag_rows(v, 16 * mt, w, 0);
+                const bf16x8 vf = tobf8(rv[mt]);
                 VC[mt][0] = mfma(vf, I0, zero4());
                 VC[mt][1] = mfma(vf, I1, zero4());
 #pragma unroll
@@ -323,7 +407,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             f32x4 OC[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 of = frag_rows(dO, 16 * mt, w, 0);
+                const bf16x8 of = tobf8(ro[mt]);
                 OC[mt][0] = mfma(of, I0, zero4());
                 OC[mt][1] = mfma(of, I1, zero4());
             }
@@ -337,7 +421,7 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             f32x4 QC[4][2];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8 qf = frag_rows(q, 16 * mt, w, 0);
+                const bf16x8 qf = tobf8(rq[mt]);
                 QC[mt][0] = mfma(qf, I0, zero4());
                 QC[mt][1] = mfma(qf, I1, zero4());
 #pragma unroll
@@ -364,8 +448,8 @@ __global__ __launch_bounds__(256) void prep_kernel(Shape s, Inputs in, Inter it,
             const int id = tid + 256 * u;
             const int i = id >> 4, f0 = (id & 15) * 8;
             float kx[8], qx[8];
-            if (bwdscan) load8(k + (int64_t)i * ld + f0, kx);
-            if (out) load8(q + (int64_t)i * ld + f0, qx);
+            to_f8(rkr[u], kx);
+            to_f8(rqr[u], qx);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float G = Gat(i, f0 + e);
