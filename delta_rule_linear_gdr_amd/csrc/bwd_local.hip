@@ -60,7 +60,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
     const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t t = tile_of(s, bh, c);
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
     // Row stride (elements) of q, k, v, dO and their gradients. In-chunk
     // offsets stay below 64 * H * 128 < 2^31 (H <= 65535), so they are 32-bit

@@ -30,7 +30,10 @@ constexpr int CH = 64;    // chunk length
 constexpr int DKD = 128;  // key width
 constexpr int DVD = 128;  // value width
 
-// Per-chunk intermediates; every pointer is indexed by tile t = bh * NT + c.
+// Per-chunk intermediates; every pointer is indexed by tile t (tile_of):
+// chunk-major, so the tiles of all heads for one chunk are contiguous and a
+// scan step, which visits one chunk of every head, reads and writes a few
+// contiguous regions rather than one region per head.
 // Sizes per tile in parentheses. Unused pointers are null.
 struct Inter {
     // forward scan operands (prep)
@@ -62,6 +65,11 @@ struct Shape {
     int vec;   // 1: per-channel gate [B,T,H,128]; 0: scalar gate [B,T,H]
     int f32;   // 1: q,k,v,beta,o,dO,dq,dk,dv,dbeta are fp32; 0: bf16
 };
+
+__host__ __device__ inline int64_t tile_of(const Shape& s, int64_t bh, int64_t c)
+{
+    return c * (s.B * s.H) + bh;
+}
 
 struct Inputs {
     const void *q, *k, *v, *beta, *dO;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
     const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t t = tile_of(s, bh, c);
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;  // token of row 0
     const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
     const int tid = threadIdx.x;
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
     const int c = blockIdx.x;
     const int bh = blockIdx.y;
     const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = (int64_t)bh * s.NT + c;
+    const int64_t t = tile_of(s, bh, c);
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
     const int ld = (int)(s.H * DVD);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

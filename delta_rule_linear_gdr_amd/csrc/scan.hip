@@ -123,7 +123,7 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
             S[m][i] = init ? init[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] : 0.f;
 
     auto chunk = [&](int p) { return BWD ? NT - 1 - p : p; };
-    auto tile = [&](int c) { return (int64_t)bh * s.NT + c; };
+    auto tile = [&](int c) { return tile_of(s, bh, c); };
 
     // Stores of a step are issued after the next group of prefetch loads:
     // loads and stores share one in-order completion counter, so a store
@@ -303,16 +303,22 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
     const bf16* A1 = BWD ? it.Kt : it.Wn;
     const bf16* A2 = BWD ? it.WnT : it.KtT;
     const bf16* C1 = BWD ? it.X : it.U;
+    // The eight slices of a head read the same A1 / A2 tiles; each starts
+    // at a different tile (rotation by 2 vs) so that they do not request
+    // the same lines at the same moment.
+    const int rot = 2 * vs;
 #pragma unroll
     for (int b = J; b < NPAD; b += 4) {
         const void* src;
         int dst;
         if (b < 16) {
-            src = A1 + t * (CH * DKD) + b * 512 + l * 8;
-            dst = fed::A1 + b * 1024;
+            const int bb = (b + rot) & 15;
+            src = A1 + t * (CH * DKD) + bb * 512 + l * 8;
+            dst = fed::A1 + bb * 1024;
         } else if (b < 32) {
-            src = A2 + t * (CH * DKD) + (b - 16) * 512 + l * 8;
-            dst = fed::A2 + (b - 16) * 1024;
+            const int bb = (b - 16 + rot) & 15;
+            src = A2 + t * (CH * DKD) + bb * 512 + l * 8;
+            dst = fed::A2 + bb * 1024;
         } else if (b < 34) {
             src = C1 + t * (CH * DVD) + vs * 1024 + (b - 32) * 512 + l * 8;
             dst = fed::C1 + (b - 32) * 1024;
@@ -335,7 +341,7 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, int 
     auto issue = [&](int p) {
         const int pc = p < NT ? p : NT - 1;  // past the end: the last chunk again
         const int c = BWD ? NT - 1 - pc : pc;
-        fed_issue<BWD, J>(it, (int64_t)bh * s.NT + c, vs, ring + (p % fed::NSLOT) * fed::SLOT);
+        fed_issue<BWD, J>(it, tile_of(s, bh, c), vs, ring + (p % fed::NSLOT) * fed::SLOT);
     };
     issue(0);
     issue(1);
@@ -375,7 +381,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 
     for (int p = 0; p < NT; ++p) {
         const int c = BWD ? NT - 1 - p : p;
-        const int64_t t = (int64_t)bh * s.NT + c;
+        const int64_t t = tile_of(s, bh, c);
         const uint8_t* slot = ring + (p % fed::NSLOT) * fed::SLOT;
         // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile vs)
 #pragma unroll
