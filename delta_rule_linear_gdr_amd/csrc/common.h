@@ -306,6 +306,14 @@ __device__ __forceinline__ void store4(float* p, const float (&x)[4])
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
 }
 
+// Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
+// reads src and its bytes land at lds_base + 16 L; lds_base must be the
+// same for every lane. Completion is counted by the vector-memory counter.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base)
+{
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
 // Unconverted reads of 4 and 8 consecutive elements, so that a batch of
 // reads can be issued before the first of them is consumed.
 struct f32x8 {

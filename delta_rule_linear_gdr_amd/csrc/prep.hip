@@ -89,6 +89,26 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     const T* dO = (const T*)in.dO + tok0 * DVD;
     const T* beta = (const T*)in.beta;
 
+    // bf16 scalar-gate path: the chunk's K and Q rows are copied once into
+    // LDS (64 rows x 256 B each; 16-byte chunk j of row i stored at chunk
+    // j ^ (i & 15), so fragment reads over 16 rows and row reads over 16
+    // chunks are both free of bank conflicts) and every later K / Q read
+    // comes from there. Direct-to-LDS loads: instruction b of wave w covers
+    // rows 4 (b & 15) .. + 3 of K (b < 16) or Q, lane L landing at row
+    // 4 (b & 15) + L / 16, stored chunk L % 16.
+    constexpr bool STAGE = sizeof(T) == 2 && !VEC;
+    __shared__ __attribute__((aligned(16))) bf16 sKQ[STAGE ? 2 * CH * DKD : 8];
+    if (STAGE) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int b = w * 8 + i, mat = b >> 4, row = 4 * (b & 15) + (l >> 4);
+            const int chunk = (l & 15) ^ (row & 15);
+            const T* src = (mat ? q : k) + row * ld + chunk * 8;
+            bf16* dst = sKQ + mat * CH * DKD + 4 * (b & 15) * DKD;
+            lds_dma16(src, dst);
+        }
+    }
+
     // ---- 1. gate cumsum (and per-key centre), beta ----
     // (beta and a scalar gate are read by every wave, so that no branch has
     // to wait for them)
@@ -138,6 +158,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         sG[l] = wave_incl_scan(graw);
     }
     if (w == 0) sBeta[l] = to_f32(braw);
+    if (STAGE) __builtin_amdgcn_s_waitcnt(0);  // the K / Q copies have landed
     __syncthreads();
 
     auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
@@ -149,6 +170,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     typedef decltype(ld8raw(k)) R8;
     auto raw_rows = [&](const T* base, int i0, int ks) -> R8 {
         return ld8raw(base + (i0 + r) * ld + 32 * ks + 8 * g);
+    };
+    // 16-byte chunk j of row i of staged K (mat 0) or Q (mat 1)
+    auto kq_chunk = [&](int mat, int i, int j) -> bf16x8 {
+        return *(const bf16x8*)(sKQ + mat * CH * DKD + i * DKD + ((j ^ (i & 15)) * 8));
+    };
+    auto raw_k = [&](int i0, int ks) -> R8 {
+        if constexpr (STAGE) return kq_chunk(0, i0 + r, 4 * ks + g);
+        else return raw_rows(k, i0, ks);
+    };
+    auto raw_q = [&](int i0, int ks) -> R8 {
+        if constexpr (STAGE) return kq_chunk(1, i0 + r, 4 * ks + g);
+        else return raw_rows(q, i0, ks);
     };
     auto cook = [&](const R8& raw, int i0, int ks, int kind) -> bf16x8 {
         if (!VEC || kind == 0) return tobf8(raw);
@@ -181,9 +214,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             tile_ij(x, ti, tj);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                b[0][ks] = raw_rows(k, 16 * ti, ks);
-                b[1][ks] = raw_rows(k, 16 * tj, ks);
-                b[2][ks] = raw_rows(q, 16 * ti, ks);
+                b[0][ks] = raw_k(16 * ti, ks);
+                b[1][ks] = raw_k(16 * tj, ks);
+                b[2][ks] = raw_q(16 * ti, ks);
             }
         };
         read_tile(w, buf[0]);
@@ -275,17 +308,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         const T* dOs = xy ? dO : q;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-            rk[mt] = raw_rows(k, 16 * mt, w);
+            rk[mt] = raw_k(16 * mt, w);
             rv[mt] = raw_rows(v, 16 * mt, w);
             ro[mt] = raw_rows(dOs, 16 * mt, w);
-            rq[mt] = raw_rows(q, 16 * mt, w);
+            rq[mt] = raw_q(16 * mt, w);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int id = tid + 256 * u;
             const int i = id >> 4, f0 = (id & 15) * 8;
-            rkr[u] = ld8raw(k + i * ld + f0);
-            rqr[u] = ld8raw(q + i * ld + f0);
+            if constexpr (STAGE) {
+                rkr[u] = kq_chunk(0, i, id & 15);
+                rqr[u] = kq_chunk(1, i, id & 15);
+            } else {
+                rkr[u] = ld8raw(k + i * ld + f0);
+                rqr[u] = ld8raw(q + i * ld + f0);
+            }
         }
     }
 

@@ -289,8 +289,6 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 // the other reads after it); the clobber keeps memory accesses in place.
 __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
 // Loader wave J (0..3): blocks J, J + 4, ... of one step into `slot`. The
 // block count is padded to a multiple of four by repeating the gn block
 // (same bytes to the same place).
@@ -329,7 +327,7 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
             src = it.gn + t * DKD + (l & 31) * 4;
             dst = fed::GN;
         }
-        __builtin_amdgcn_global_load_lds(src, (lds_ptr)(slot + dst), 16, 0, 0);
+        lds_dma16(src, slot + dst);
     }
 }
 
