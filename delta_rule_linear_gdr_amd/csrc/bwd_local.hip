@@ -106,7 +106,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     bf16x8* const lGT = lG + 512;
     bf16x8* const lGq = lG + 1024;
     bf16x8* const lGqT = lG + 1536;
-    __shared__ float sG[CH], sBeta[CH];
+    __shared__ __attribute__((aligned(16))) float sG[CH], sBeta[CH];
     __shared__ float sRedB[NW][CH], sRedP[NW][CH], sRedG[NW][CH];
     __shared__ float sExtra[DKD];
     __shared__ float sEx[NW];
@@ -223,7 +223,27 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     __syncthreads();
     if (!VEC) Gnf = sG[CH - 1];
     // G at this lane's accumulator position (tok 16 m + 4 g + e, f)
-    auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : sG[16 * m + 4 * g + e]; };
+    // G and beta at this lane's accumulator rows (tok 16 m + 4 g + e), read
+    // once as 16-byte vectors (the scalar gate's G lives in LDS)
+    // (scalar gate only: the vector-gate kernel has no registers to spare
+    // and reads beta from LDS where it is used)
+    float Gs[VEC ? 1 : 4][4], Bs[VEC ? 1 : 4][4];
+    if (!VEC) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float4 b4 = *(const float4*)&sBeta[16 * m + 4 * g];
+            const float4 g4 = *(const float4*)&sG[16 * m + 4 * g];
+            const float bv[4] = {b4.x, b4.y, b4.z, b4.w}, gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                Bs[VEC ? 0 : m][e] = bv[e];
+                Gs[VEC ? 0 : m][e] = gv[e];
+            }
+        }
+    }
+    // G and beta at this lane's accumulator position (tok 16 m + 4 g + e, f)
+    auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : Gs[VEC ? 0 : m][e]; };
+    auto Bt = [&](int m, int e) -> float { return VEC ? sBeta[16 * m + 4 * g + e] : Bs[VEC ? 0 : m][e]; };
 
     const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
     const bf16x8 Iw = (w & 1) ? I1 : I0;
@@ -330,7 +350,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = 2 * ks + hh;
-                    ec[hh][e] = sBeta[16 * m + 4 * g + e] * __expf(Gt(m, e)) * KC[m][e];
+                    ec[hh][e] = Bt(m, e) * __expf(Gt(m, e)) * KC[m][e];
                 }
             ETf[ks] = pack_pi(ec[0], ec[1]);
         }
@@ -361,7 +381,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                     const float al = __expf(d), ze = __expf(-d);
                     y[hh][e] = ze * KC[m][e];
                     qq[hh][e] = al * QC[m][e];
-                    ee[hh][e] = sBeta[16 * m + 4 * g + e] * al * KC[m][e];
+                    ee[hh][e] = Bt(m, e) * al * KC[m][e];
                 }
             }
             B0[ks] = pack_pi(y[0], y[1]);
@@ -436,7 +456,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands. ReWY:
     //      D = -strict_lower(P R^T). Seven-product: D = strict_lower(Mbar)
     //      with Mbar = -X A^T, formed here as -strict_lower(X A^T). ----
-    for (int x = w; x < 40; x += NW) {
+    // (scalar gate: five items per wave unrolled, so that one item's LDS
+    // reads overlap the previous item's products; the vector-gate kernel
+    // keeps the rolled loop, having no registers to spare)
+    auto item2a = [&](int x) {
         const int kind = x / 10, tl = x % 10;
         const int ti = tl >= 6 ? 3 : tl >= 3 ? 2 : tl >= 1 ? 1 : 0;
         const int tj = tl - ti * (ti + 1) / 2;
@@ -460,6 +483,20 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) acc = mfma(Aop[(ma * 4 + sl) * 64 + l], Bop[(nb * 4 + sl) * 64 + l], acc);
         }
+        // scalar gate: the gate values (and for D, beta) of this lane's rows
+        // and column, as one 16-byte and one 4-byte LDS read each
+        float4 G4 = {0.f, 0.f, 0.f, 0.f}, B4 = {1.f, 1.f, 1.f, 1.f};
+        float G1 = 0.f;
+        if (!VEC) {
+            // kinds 0, 2: lane holds (i = 16 ti + 4 g + e, j = 16 tj + r);
+            // kinds 1, 3: (i = 16 ti + r, j = 16 tj + 4 g + e)
+            const int i4 = (kind & 1) ? 16 * tj + 4 * g : 16 * ti + 4 * g;
+            const int i1 = (kind & 1) ? 16 * ti + r : 16 * tj + r;
+            G4 = *(const float4*)&sG[i4];
+            G1 = sG[i1];
+            if (kind == 0) B4 = *(const float4*)&sBeta[i4];
+        }
+        const float G4v[4] = {G4.x, G4.y, G4.z, G4.w}, B4v[4] = {B4.x, B4.y, B4.z, B4.w};
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -468,8 +505,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             const bool keep = kind < 2 ? i > j : i >= j;
             float val = keep ? (kind < 2 ? -acc[e] : acc[e]) : 0.f;
             if (!VEC) {
-                val *= keep ? __expf(sG[i] - sG[j]) : 0.f;  // Lam
-                if (kind == 0) val *= sBeta[i];             // Gam^T diag(beta)
+                const float Gi = (kind & 1) ? G1 : G4v[e], Gj = (kind & 1) ? G4v[e] : G1;
+                val *= keep ? __expf(Gi - Gj) : 0.f;  // Lam
+                if (kind == 0) val *= B4v[e];         // Gam^T diag(beta)
             }
             o[e] = (bf16)val;
         }
@@ -477,6 +515,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         else if (kind == 1) st_half(lGm, ti * 2 + (tj >> 1), tj & 1, o);   // D^T:  (M = i, K = j)
         else if (kind == 2) st_half(lGqT, tj * 2 + (ti >> 1), ti & 1, o);  // Hb:   (M = j, K = i)
         else st_half(lGq, ti * 2 + (tj >> 1), tj & 1, o);                  // Hb^T: (M = i, K = j)
+    };
+    if constexpr (VEC) {
+        for (int x = w; x < 40; x += NW) item2a(x);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 40 / NW; ++u) item2a(w + NW * u);
     }
 
     __syncthreads();  // consumer A operands complete
@@ -553,7 +597,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * m + 4 * g + e;
             const float G = Gt(m, e), gam = __expf(G), kt = __expf(Gnf - G);
-            const float bt = sBeta[i];
+            const float bt = Bt(m, e);
             // k and q back from the consumer operands (exact for the scalar
             // gate; hi + lo over the centred factor for the vector gate)
             const int ks = m >> 1, sl = 4 * (m & 1) + e;
