@@ -100,11 +100,13 @@ hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStrea
 // and the final state ht when ht != null.
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o,
                            float* ht, hipStream_t st);
-// Reverse state scan. Writes dh and Rb when set, and dh0 when dh0 != null.
+// Reverse state scan (loader-fed). Writes dh and Rb (both required), and dh0
+// when dh0 != null.
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                            hipStream_t st);
-// Both scans of the recompute backward in one launch (the reverse scan does
-// not depend on the forward one): h, R, dh, Rb and dh0.
+// Both scans of the recompute backward in one loader-fed launch (the reverse
+// scan does not depend on the forward one): h, R, dh, Rb (all required) and
+// dh0 when dh0 != null.
 hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                             hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
