@@ -79,6 +79,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the six-shape sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="calibration copy + a few headline steps, for rocprofv3 counter runs")
@@ -112,6 +113,39 @@ def measured_traffic(kernel: str, units: int):
     return round(float(row.group(1)) + float(row.group(2)), 0)
 
 
+def shape_sweep(gdr, to_dev, make_runner, time_steps, args):
+    """The six shapes of the pages' evaluation, scalar and vector gate (gate
+    means 4 and 3, the distributions of the (1,2048,16) and (2,2048,16)
+    workloads), backward under both policies and the recompute forward:
+    ms per call and backward tokens/s."""
+    import torch
+    from delta_rule_linear_gdr_amd.inputs import SHAPES6, make_inputs
+    rows = []
+    for Bs, Ts, Hs in SHAPES6:
+        for gate in ("scalar", "vector"):
+            xs = make_inputs(Bs, Ts, Hs, gate=gate, dtype="bf16", seed=0,
+                             gate_mean=4.0 if gate == "scalar" else 3.0)
+            ds = to_dev(xs)
+            row = {"B": Bs, "T": Ts, "H": Hs, "gate": gate}
+            msR = time_steps(make_runner(ds, gdr.gdr_bwd, "recompute"), args.steps, args.warmup)
+            _, _, saved = gdr.gdr_fwd(ds["q"], ds["k"], ds["v"], ds["g"], ds["beta"], ds["h0"],
+                                      policy="full_save")
+            msA = time_steps(make_runner(ds, gdr.gdr_bwd, "full_save", saved), args.steps,
+                             args.warmup)
+            _, sc = gdr.workspace_size(Bs, Ts, Hs, gate, "bf16", "recompute")
+            scr = torch.empty(sc, dtype=torch.uint8, device=ds["q"].device)
+            msF = time_steps(lambda: gdr.gdr_fwd(ds["q"], ds["k"], ds["v"], ds["g"], ds["beta"],
+                                                 ds["h0"], policy="recompute", scratch=scr),
+                             args.steps, args.warmup)
+            row.update(bwd_R_ms=round(msR, 4), bwd_A_ms=round(msA, 4), fwd_R_ms=round(msF, 4),
+                       bwd_R_tokens_per_s=round(Bs * Ts / (msR * 1e-3), 1),
+                       bwd_A_tokens_per_s=round(Bs * Ts / (msA * 1e-3), 1))
+            rows.append(row)
+            print(f"[bench] sweep {row}", file=sys.stderr, flush=True)
+            del ds, xs, saved, scr
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,13 +176,14 @@ def main():
     units = B * H * (T // CH)
 
     def make_runner(dd, fn, policy, saved=None):
-        _, sc = gdr.workspace_size(B, T, H, "vector" if dd["g"].dim() == 4 else "scalar",
+        Bq, Tq, Hq = dd["q"].shape[:3]
+        _, sc = gdr.workspace_size(Bq, Tq, Hq, "vector" if dd["g"].dim() == 4 else "scalar",
                                    "bf16", policy)
         scratch = torch.empty(sc, dtype=torch.uint8, device=dev)
         out = dict(dq=torch.empty_like(dd["q"]), dk=torch.empty_like(dd["k"]),
                    dv=torch.empty_like(dd["v"]), dg=torch.empty_like(dd["g"]),
                    dbeta=torch.empty_like(dd["beta"]),
-                   dh0=torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev))
+                   dh0=torch.empty((Bq, Hq, 128, 128), dtype=torch.float32, device=dev))
 
         def run():
             fn(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], dd["h0"], dd["dO"], None,
@@ -282,6 +317,8 @@ def main():
         detail["kda_path_frac_hbm"] = round(kpath / (msK * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         detail["kda_stage_ms"] = {k: round(v, 4) for k, v in profiled(runK, args.steps).items()}
         del dk_, xk
+        if not args.no_sweep:
+            detail["shape_sweep"] = shape_sweep(gdr, to_dev, make_runner, time_steps, args)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -73,6 +73,10 @@ class Workload:
 
 # The five workloads of the build: GDN at (1,512,4) fp32, (1,2048,16) and
 # (1,8192,16) bf16; KDA at (2,2048,16) and (1,8192,16) bf16 with h0 ~ 0.1 N(0,1).
+# The six (B, T, H) shapes of the pages' evaluation (Eq. 4 of the paper page,
+# listed in the onedev.kr summary's "How to use"), C = 64, d_k = d_v = 128.
+SHAPES6 = ((1, 512, 4), (1, 2048, 4), (1, 8192, 4), (1, 2048, 16), (2, 2048, 16), (1, 8192, 16))
+
 WORKLOADS = {
     "gdn_1x512x4_fp32": Workload("gdn_1x512x4_fp32", "scalar", 1, 512, 4, "fp32"),
     "gdn_1x2048x16": Workload("gdn_1x2048x16", "scalar", 1, 2048, 16),

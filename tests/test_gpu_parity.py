@@ -57,6 +57,20 @@ def test_kda_8192x16_h0_sampled_heads():
     _report("kda_1x8192x16/recompute", tl.compare(gpu, x, heads=[(0, 0), (0, 11)]))
 
 
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_four_head_shapes(gate):
+    """The two four-head shapes of the pages' six-shape evaluation that the
+    workloads above do not cover, both policies; (1,8192,4) on sampled heads."""
+    _need_gpu()
+    mean = 4.0 if gate == "scalar" else 3.0
+    x = make_inputs(1, 2048, 4, gate=gate, dtype="bf16", seed=0, gate_mean=mean)
+    for pol in ("recompute", "full_save"):
+        _report(f"{gate}_1x2048x4/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+    x = make_inputs(1, 8192, 4, gate=gate, dtype="bf16", seed=0, gate_mean=mean)
+    for pol in ("recompute", "full_save"):
+        _report(f"{gate}_1x8192x4/{pol}", tl.compare(tl.run_gpu(x, pol), x, heads=[(0, 1), (0, 3)]))
+
+
 # ------------------------------------------------------------------ edges
 
 def _edge(gate, T=256, H=2, B=1, seed=3, **kw):
