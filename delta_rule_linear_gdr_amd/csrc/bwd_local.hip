@@ -62,6 +62,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const int64_t b = bh / s.H, hd = bh % s.H;
     const int64_t t = tile_of(s, bh, c);
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
+    const int nv = chunk_rows(s, c);  // rows past it read as zeros and are not written
     // Row stride (elements) of q, k, v, dO and their gradients. In-chunk
     // offsets stay below 64 * H * 128 < 2^31 (H <= 65535), so they are 32-bit
     // and every pointer below is a uniform per-chunk base.
@@ -135,15 +136,26 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const bf16* const Afg = it.Af + t * (CH * CH);
     // (beta and a scalar gate are read by every wave, so that no branch
     // has to wait for them)
-    const T braw = betai[l * Hs];
+    // Rows past nv: the read is made from a clamped row (always in range, so
+    // it stays an unconditional read in the batch) and its value replaced by
+    // zero with a select.
+    const int lc = l < nv ? l : nv - 1;
+    const T bload = betai[lc * Hs];
+    const T braw = l < nv ? bload : (T)0.f;
     float graw[VEC ? 16 : 1];
     if (VEC) {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) graw[VEC ? 4 * m + e : 0] = gin[(16 * m + 4 * g + e) * ld + f];
+            for (int e = 0; e < 4; ++e)
+            {
+                const int i = 16 * m + 4 * g + e;
+                const float gl = gin[(i < nv ? i : nv - 1) * ld + f];
+                graw[VEC ? 4 * m + e : 0] = i < nv ? gl : 0.f;
+            }
     } else {
-        graw[0] = gin[l * Hs];
+        const float gl = gin[lc * Hs];
+        graw[0] = l < nv ? gl : 0.f;
     }
     bf16x4 rbq[4], rq[4], hq[8], dhq[8];
     bf16x8 atf[6];  // A^T frags m * 2 + 1 (m = 0..3), then m * 2 + 0 (m = 0, 1)
@@ -155,12 +167,21 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     for (int m = 0; m < 4; ++m) atf[m] = ld_frag(ATg, m * 2 + 1);
     atf[4] = ld_frag(ATg, 0);
     atf[5] = ld_frag(ATg, 2);
+    // token row 16 m + r, clamped into the chunk (zeros past nv)
+    auto rowc = [&](int m) { return 16 * m + r < nv ? 16 * m + r : nv - 1; };
+    const bool rv[4] = {r < nv, 16 + r < nv, 32 + r < nv, 48 + r < nv};
 #pragma unroll
-    for (int m = 0; m < 4; ++m) vr[m] = ld4raw(v + (16 * m + r) * ld + 16 * w + 4 * g);
+    for (int m = 0; m < 4; ++m) {
+        const R4 x = ld4raw(v + rowc(m) * ld + 16 * w + 4 * g);
+        vr[m] = rv[m] ? x : R4{};
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) rq[i] = *(const bf16x4*)ctile_ptr(Rg, w * 4 + i);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) orw[m] = ld4raw(dO + (16 * m + r) * ld + 16 * w + 4 * g);
+    for (int m = 0; m < 4; ++m) {
+        const R4 x = ld4raw(dO + rowc(m) * ld + 16 * w + 4 * g);
+        orw[m] = rv[m] ? x : R4{};
+    }
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
         hq[vt] = *(const bf16x4*)ctile_ptr(hg, vt * 8 + w);
@@ -168,8 +189,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        kr[m] = ld8raw(k + (16 * m + r) * ld + 32 * (w >> 1) + 8 * g);
-        qr[m] = ld8raw(q + (16 * m + r) * ld + 32 * (w >> 1) + 8 * g);
+        const R8 xk = ld8raw(k + rowc(m) * ld + 32 * (w >> 1) + 8 * g);
+        const R8 xq = ld8raw(q + rowc(m) * ld + 32 * (w >> 1) + 8 * g);
+        kr[m] = rv[m] ? xk : R8{};
+        qr[m] = rv[m] ? xq : R8{};
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -269,7 +292,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 dvv[e] = bt * acc[e];
                 pv += acc[e] * vx[e];
             }
-            store4(dvo + i * ld + 16 * w + 4 * g, dvv);
+            if (i < nv) store4(dvo + i * ld + 16 * w + 4 * g, dvv);
             pv = sum_rows(pv);
             if (g == 0) sRedP[w][i] = pv;
             if (!WY7) st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
@@ -632,8 +655,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 dkP[m & 1][e] = dk;
             } else {
                 const int off = i * ld + f;
-                io<T>::st(dqo + off, dq);
-                io<T>::st(dko + off, dk);
+                if (i < nv) {
+                    io<T>::st(dqo + off, dq);
+                    io<T>::st(dko + off, dk);
+                }
             }
         }
         if (ROWSTORE && (m & 1) == 0) {
@@ -644,10 +669,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 // lane: d*[tok 16 (m + hh) + r][key 16 w + 4 g + e]
                 const f32x4 tq = mfma(aq, hh ? Ip1 : Ip0, zero4());
                 const f32x4 tk = mfma(ak, hh ? Ip1 : Ip0, zero4());
-                const int off = (16 * (m + hh) + r) * ld + 16 * w + 4 * g;
+                const int row = 16 * (m + hh) + r;
+                const int off = row * ld + 16 * w + 4 * g;
                 float xq[4] = {tq[0], tq[1], tq[2], tq[3]}, xk[4] = {tk[0], tk[1], tk[2], tk[3]};
-                store4(dqo + off, xq);
-                store4(dko + off, xk);
+                if (row < nv) {
+                    store4(dqo + off, xq);
+                    store4(dko + off, xk);
+                }
             }
         }
         // per-token sums over this wave's features
@@ -674,7 +702,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             const float excl = ((g & 1) ? 0.f : p16) + ((g & 2) ? 0.f : p32);
             const float ttot = pair + p32;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dgo[(16 * m + 4 * g + e) * ld + f] = suf[e] + excl + carry;
+            for (int e = 0; e < 4; ++e)
+                if (16 * m + 4 * g + e < nv) dgo[(16 * m + 4 * g + e) * ld + f] = suf[e] + excl + carry;
             carry += ttot;
         }
         // keep the scheduler from hoisting the next tile's operand reads
@@ -687,7 +716,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         if (l == 0) sEx[w] = ex;
     }
     __syncthreads();
-    if (tid < CH) {
+    if (tid < nv) {
         float sb = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) sb += sRedB[ww][tid] + sRedP[ww][tid];
@@ -707,7 +736,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             const float y = __shfl_down(xg, off);
             if (l + off < 64) xg += y;
         }
-        dgo[l * Hs] = xg;
+        if (l < nv) dgo[l * Hs] = xg;
     }
 }
 

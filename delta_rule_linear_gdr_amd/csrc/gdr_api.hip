@@ -139,11 +139,9 @@ int check_desc(const gdr_desc* d)
                     (long long)d->DK, (long long)d->DV);
     if (d->C != CH)
         return fail(GDR_ERR_UNSUPPORTED, "chunk length %lld: only 64 is supported", (long long)d->C);
-    if (d->T % CH != 0)
-        return fail(GDR_ERR_UNSUPPORTED, "T=%lld is not a multiple of 64", (long long)d->T);
     if (d->B * d->H > 65535)
         return fail(GDR_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(d->B * d->H));
-    if (d->T / CH > (int64_t)1 << 30)
+    if ((d->T + CH - 1) / CH > (int64_t)1 << 30)
         return fail(GDR_ERR_UNSUPPORTED, "T=%lld too long", (long long)d->T);
     return GDR_OK;
 }
@@ -175,7 +173,7 @@ Shape make_shape(const gdr_desc* d)
     s.B = d->B;
     s.T = d->T;
     s.H = d->H;
-    s.NT = d->T / CH;
+    s.NT = (d->T + CH - 1) / CH;  // the last chunk may be partial
     s.vec = d->gate == GDR_GATE_VECTOR;
     s.f32 = d->dtype == GDR_F32;
     return s;
@@ -253,7 +251,7 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(dg, 4); REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(dht, 4); CHECK_ALIGN(dh0, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
     Inter it;
     size_t sb = 0, need = 0;
     layout(policy, BWD, nullptr, nullptr, ntiles, it, sb, need);
@@ -298,7 +296,7 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_policy(policy))) return rc;
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
     Inter it;
     size_t s1 = 0, c1 = 0, s2 = 0, c2 = 0;
     layout(policy, FWD, nullptr, nullptr, ntiles, it, s1, c1);
@@ -326,7 +324,7 @@ int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(beta, esz);
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)(d->T / CH);
+    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
     Inter it;
     size_t sb = 0, need = 0;
     layout(policy, FWD, nullptr, nullptr, ntiles, it, sb, need);

@@ -66,6 +66,16 @@ struct Shape {
     int f32;   // 1: q,k,v,beta,o,dO,dq,dk,dv,dbeta are fp32; 0: bf16
 };
 
+// Tokens of chunk c: 64, except in a ragged last chunk when T % 64 != 0.
+// The missing rows act as identity steps (g = 0, beta = 0, zero q, k, v and
+// dO): kernels read zeros for them and write nothing for them, which leaves
+// every state, output and gradient of the real tokens exact.
+__host__ __device__ inline int chunk_rows(const Shape& s, int64_t c)
+{
+    const int64_t r = s.T - c * CH;
+    return r < CH ? (int)r : CH;
+}
+
 __host__ __device__ inline int64_t tile_of(const Shape& s, int64_t bh, int64_t c)
 {
     return c * (s.B * s.H) + bh;

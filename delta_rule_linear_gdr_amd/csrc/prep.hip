@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     const int64_t t = tile_of(s, bh, c);
     const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;  // token of row 0
     const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
+    const int nv = chunk_rows(s, c);  // rows past it are read as zeros
     const int tid = threadIdx.x;
     const int l = lane_id(), r = lane_r(), g = lane_g();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -105,15 +106,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             const int chunk = (l & 15) ^ (row & 15);
             const T* src = (mat ? q : k) + row * ld + chunk * 8;
             bf16* dst = sKQ + mat * CH * DKD + 4 * (b & 15) * DKD;
-            lds_dma16(src, dst);
+            if (row < nv) lds_dma16(src, dst);
+            else *(bf16x8*)(dst + l * 8) = bf16x8{};
         }
     }
 
     // ---- 1. gate cumsum (and per-key centre), beta ----
     // (beta and a scalar gate are read by every wave, so that no branch has
     // to wait for them)
-    const T braw = beta[tok0 + l * s.H];
-    const float graw = VEC ? 0.f : in.g[tok0 + l * s.H];
+    // Rows past nv: the read is made from a clamped row (always in range, so
+    // it stays an unconditional read in the batch) and its value replaced by
+    // zero with a select.
+    const int lc = l < nv ? l : nv - 1;
+    const T bload = beta[tok0 + lc * s.H];
+    const float gload = VEC ? 0.f : in.g[tok0 + lc * s.H];
+    const T braw = l < nv ? bload : (T)0.f;
+    const float graw = l < nv ? gload : 0.f;
     if (VEC) {
         // wave w: keys 32 w .. 32 w + 31 as two 16-key passes; lane (r, g)
         // holds tokens 16 m + 4 g + e of key f (all 32 reads issued first)
@@ -123,8 +131,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x[u][m][e] = in.g[(tok0 + (int64_t)(16 * m + 4 * g + e) * s.H) * DKD + 32 * w + 16 * u + r];
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * m + 4 * g + e, ic = i < nv ? i : nv - 1;
+                    x[u][m][e] = in.g[(tok0 + (int64_t)ic * s.H) * DKD + 32 * w + 16 * u + r];
+                }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[u][m][e] = 16 * m + 4 * g + e < nv ? x[u][m][e] : 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int f = 32 * w + 16 * u + r;
@@ -169,7 +185,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     // scale (vector gate)
     typedef decltype(ld8raw(k)) R8;
     auto raw_rows = [&](const T* base, int i0, int ks) -> R8 {
-        return ld8raw(base + (i0 + r) * ld + 32 * ks + 8 * g);
+        const int i = i0 + r;
+        const R8 x = ld8raw(base + (i < nv ? i : nv - 1) * ld + 32 * ks + 8 * g);
+        return i < nv ? x : R8{};
     };
     // 16-byte chunk j of row i of staged K (mat 0) or Q (mat 1)
     auto kq_chunk = [&](int mat, int i, int j) -> bf16x8 {
@@ -321,8 +339,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 rkr[u] = kq_chunk(0, i, id & 15);
                 rqr[u] = kq_chunk(1, i, id & 15);
             } else {
-                rkr[u] = ld8raw(k + i * ld + f0);
-                rqr[u] = ld8raw(q + i * ld + f0);
+                const int ic = i < nv ? i : nv - 1;
+                const R8 xk = ld8raw(k + ic * ld + f0), xq = ld8raw(q + ic * ld + f0);
+                rkr[u] = i < nv ? xk : R8{};
+                rqr[u] = i < nv ? xq : R8{};
             }
         }
     }
@@ -610,14 +630,16 @@ __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
     const int ld = (int)(s.H * DVD);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* dO = (const T*)in.dO + tok0 * DVD;
+    const int nv = chunk_rows(s, c);  // rows past it are read as zeros
 
     const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
     f32x4 OC[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
+        const int i = 16 * mt + lane_r();
         float x[8];
-        ld_plain8(dO, ld, 16 * mt, 32 * w, x);
-        const bf16x8 of = pack8(x);
+        load8(dO + (i < nv ? i : nv - 1) * ld + 32 * w + 8 * lane_g(), x);
+        const bf16x8 of = i < nv ? pack8(x) : bf16x8{};
         OC[mt][0] = mfma(of, I0, zero4());
         OC[mt][1] = mfma(of, I1, zero4());
     }

@@ -132,10 +132,13 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
     bf16x4 pend_s[2], pend_z;
     f32x4 pend_o;
     int64_t pend_t = 0, pend_tok = 0;
+    int pend_rows = CH;  // rows of the pending chunk (a ragged last chunk has fewer)
     auto flush = [&]() {
         if (OUT) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) io<T>::st(o + (pend_tok + (int64_t)i * s.H) * DVD + v, pend_o[i]);
+            for (int i = 0; i < 4; ++i)
+                if (16 * w + 4 * g + i < pend_rows)
+                    io<T>::st(o + (pend_tok + (int64_t)i * s.H) * DVD + v, pend_o[i]);
         }
         if (STORE) {
             // state before the update (h_c, or dh_c = adjoint at the chunk
@@ -191,6 +194,7 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) oacc = mfma(op.hm[ks], zf[ks], oacc);
             pend_tok = (b * s.T + (int64_t)c * CH + 16 * w + 4 * g) * s.H + hd;
+            pend_rows = chunk_rows(s, c);
             pend_o = oacc;
         }
     };

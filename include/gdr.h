@@ -44,11 +44,14 @@
  *
  * Errors: arguments are validated before anything is launched; on error
  * nothing is launched and the call returns a negative status. Unsupported
- * shapes (key/value width other than 128, chunk other than 64, T not a
- * multiple of 64) return GDR_ERR_UNSUPPORTED -- there is no fallback (the
- * flashserve/ReWY repository page, "Compatibility" and "Existing Training
- * Scripts": K = V = 128, 64-token chunks, lengths divisible by 64,
- * unsupported configurations fail by default). Vector-gate inputs whose
+ * shapes (key/value width other than 128, chunk other than 64) return
+ * GDR_ERR_UNSUPPORTED -- there is no fallback (the flashserve/ReWY repository
+ * page, "Compatibility" and "Existing Training Scripts": K = V = 128, 64-token
+ * chunks, unsupported configurations fail by default). T may be any length:
+ * where that page requires a multiple of 64, a ragged last chunk is handled
+ * here, its missing rows acting as identity steps (g = 0, beta = 0, zero
+ * q, k, v, dO), which leaves every output, state and gradient of the real
+ * tokens exact; workspaces count whole chunks. Vector-gate inputs whose
  * per-chunk, per-channel cumulative log-decay range exceeds 80 are outside the
  * contract (the centred factors exp(+-range/2) would leave fp32). A
  * launch failure returns GDR_ERR_HIP. gdr_last_error() returns a message for

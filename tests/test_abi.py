@@ -58,13 +58,24 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(DK=64), -2), (dict(DV=96), -2), (dict(C=32), -2), (dict(T=100), -2),
+    (dict(DK=64), -2), (dict(DV=96), -2), (dict(C=32), -2),
     (dict(gate=5), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
 ])
 def test_descriptor_validation(kw, status):
     rc, _, _ = _ws(_desc(**kw))
     assert rc == status
     assert gdr.load().gdr_last_error()
+
+
+def test_ragged_length_sizes_whole_chunks():
+    # T = 100: two chunks, the second holding 36 tokens; workspaces count tiles
+    rc, sv100, sc100 = _ws(_desc(T=100), 1)
+    assert rc == 0
+    rc, sv128, sc128 = _ws(_desc(T=128), 1)
+    assert rc == 0 and (sv100, sc100) == (sv128, sc128)
+    rc, sv1, sc1 = _ws(_desc(T=1), 0)
+    rc64, sv64, sc64 = _ws(_desc(T=64), 0)
+    assert rc == 0 and rc64 == 0 and (sv1, sc1) == (sv64, sc64)
 
 
 def test_null_descriptor_and_bad_policy():

@@ -132,16 +132,36 @@ def test_deterministic_and_policy_independent():
         np.testing.assert_array_equal(a[n], c[n], err_msg=f"policy {n}")
 
 
-def test_unsupported_length_raises():
+def test_unsupported_width_raises():
     _need_gpu()
     import delta_rule_linear_gdr_amd as gdr
     x = _edge("scalar", T=128)
     d = tl.device_inputs(x)
     with pytest.raises(gdr.GdrError) as ei:
-        gdr.gdr_fwd(d["q"][:, :100].contiguous(), d["k"][:, :100].contiguous(),
-                    d["v"][:, :100].contiguous(), d["g"][:, :100].contiguous(),
-                    d["beta"][:, :100].contiguous())
+        gdr.gdr_fwd(d["q"][..., :64].contiguous(), d["k"][..., :64].contiguous(),
+                    d["v"], d["g"], d["beta"])
     assert ei.value.status == -2
+
+
+# ---------------------------------------------- ragged last chunk (T % 64 != 0)
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_ragged_tail(gate):
+    """Lengths that end inside a chunk, two batch entries (the ragged chunk of
+    entry 0 sits right before entry 1's tokens), both policies, nonzero h0 and
+    dht: the missing rows must neither be read nor written."""
+    _need_gpu()
+    for T in (1, 63, 65, 100, 191, 257):
+        x = _edge(gate, T=T, H=2, B=2, seed=11, h0_std=0.1, dht_std=0.1)
+        for pol in ("recompute", "full_save"):
+            _report(f"ragged/{gate}/T={T}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+
+
+def test_ragged_tail_fp32():
+    _need_gpu()
+    x = make_inputs(2, 100, 3, gate="scalar", dtype="fp32", seed=12, gate_mean=4.0, h0_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"ragged/fp32/T=100/{pol}", tl.compare(tl.run_gpu(x, pol), x))
 
 
 # ------------------------------------------------- seven-product ablation
