@@ -13,7 +13,11 @@ unbuilt library raises.
 Shapes: q, k, v, dO [B,T,H,128]; g [B,T,H] (GDN, scalar gate) or
 [B,T,H,128] (KDA, per-channel gate), fp32; beta [B,T,H]; h0, dht
 [B,H,128,128] fp32 (key-major) or None. q, k, v, beta, dO share one dtype,
-bfloat16 or float32.
+bfloat16 or float32. Any T (a ragged last chunk is handled).
+
+Packed variable-length batches: pass ``cu_seqlens`` (int64 device tensor of
+n_seq + 1 token offsets) with batch size 1; the states h0, ht, dht, dh0 are
+then [n_seq,H,128,128].
 """
 from __future__ import annotations
 
@@ -32,7 +36,8 @@ GATE_SCALAR, GATE_VECTOR = 0, 1
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
-EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_profile_begin",
+EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
+           "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen", "gdr_profile_begin",
            "gdr_profile_end", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
@@ -76,6 +81,14 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, i32] + [p] * 16 + [sz, p]
         fn.restype = i32
+    i64 = ctypes.c_int64
+    lib.gdr_workspace_size_varlen.argtypes = [dp, i64, i32, ctypes.POINTER(sz),
+                                              ctypes.POINTER(sz)]
+    lib.gdr_workspace_size_varlen.restype = i32
+    lib.gdr_fwd_varlen.argtypes = [dp, i32, p, i64] + [p] * 10 + [sz, p]
+    lib.gdr_fwd_varlen.restype = i32
+    lib.gdr_bwd_varlen.argtypes = [dp, i32, p, i64] + [p] * 16 + [sz, p]
+    lib.gdr_bwd_varlen.restype = i32
     lib.gdr_profile_begin.argtypes = [i32]
     lib.gdr_profile_begin.restype = i32
     lib.gdr_profile_end.argtypes = [ctypes.POINTER(StageTime), i32, ctypes.POINTER(i32)]
@@ -107,13 +120,22 @@ def make_desc(B, T, H, gate, dtype, DK=128, DV=128, C=64) -> Desc:
     return Desc(B, T, H, DK, DV, C, gate, dtype)
 
 
-def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute"):
-    """(saved_bytes, scratch_bytes) for a problem."""
+def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute", n_seq=None):
+    """(saved_bytes, scratch_bytes) for a problem; n_seq: sequences of a packed
+    variable-length batch (B = 1), None for a regular batch."""
     d = make_desc(B, T, H, GATE_VECTOR if gate == "vector" else GATE_SCALAR,
                   DT_F32 if dtype == "fp32" else DT_BF16)
+    return _sizes(d, _policy(policy), n_seq)
+
+
+def _sizes(d, pol, n_seq):
     sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(load().gdr_workspace_size(ctypes.byref(d), _policy(policy), ctypes.byref(sv),
-                                     ctypes.byref(sc)))
+    lib = load()
+    if n_seq is None:
+        _check(lib.gdr_workspace_size(ctypes.byref(d), pol, ctypes.byref(sv), ctypes.byref(sc)))
+    else:
+        _check(lib.gdr_workspace_size_varlen(ctypes.byref(d), n_seq, pol, ctypes.byref(sv),
+                                             ctypes.byref(sc)))
     return sv.value, sc.value
 
 
@@ -180,61 +202,92 @@ def _scratch(nbytes, device):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch=None):
-    """Forward. Returns (o, ht or None, saved or None)."""
+def _seqs(cu_seqlens, q):
+    """Sequence count of a packed batch (None for a regular batch)."""
+    torch = _torch()
+    if cu_seqlens is None:
+        return None
+    if not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int64 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int64 device tensor")
+    if not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be contiguous with n_seq + 1 >= 1 entries")
+    if q.shape[0] != 1:
+        raise ValueError(f"a packed batch has batch size 1, got {q.shape[0]}")
+    return cu_seqlens.numel() - 1
+
+
+def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch=None,
+            cu_seqlens=None):
+    """Forward. Returns (o, ht or None, saved or None).
+
+    cu_seqlens (int64 device tensor of n_seq + 1 token offsets) makes the
+    single row of q (batch size 1) a packed batch of n_seq sequences, each
+    with its own state: h0 and ht are then [n_seq, H, 128, 128]."""
     torch = _torch()
     _validate(q, k, v, g, beta, (("h0", h0),))
     d = _desc_from(q, g)
     pol = _policy(policy)
-    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    n_seq = _seqs(cu_seqlens, q)
     lib = load()
-    _check(lib.gdr_workspace_size(ctypes.byref(d), pol, ctypes.byref(sv), ctypes.byref(sc)))
+    saved_b, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
+    ns = B if n_seq is None else n_seq
     o = torch.empty_like(v)
-    ht = torch.empty((B, H, 128, 128), dtype=torch.float32, device=q.device) if want_ht else None
-    saved = torch.empty(sv.value, dtype=torch.uint8, device=q.device) if sv.value else None
+    ht = torch.empty((ns, H, 128, 128), dtype=torch.float32, device=q.device) if want_ht else None
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None
     if scratch is None:
-        scratch = _scratch(sc.value, q.device)
-    _check(lib.gdr_fwd(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                       _ptr(h0), _ptr(o), _ptr(ht), _ptr(saved), _ptr(scratch),
-                       scratch.numel(), _stream()))
+        scratch = _scratch(scratch_b, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(o), _ptr(ht),
+            _ptr(saved), _ptr(scratch), scratch.numel(), _stream())
+    if n_seq is None:
+        _check(lib.gdr_fwd(ctypes.byref(d), pol, *args))
+    else:
+        _check(lib.gdr_fwd_varlen(ctypes.byref(d), pol, _ptr(cu_seqlens), n_seq, *args))
     return o, ht, saved
 
 
-def _bwd(fn, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, out):
+def _bwd(name, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, out,
+         cu_seqlens=None):
     torch = _torch()
     _validate(q, k, v, g, beta, (("h0", h0), ("dO", dO), ("dht", dht)))
     if dO.dtype != q.dtype:
         raise TypeError("dO dtype differs from q dtype")
     d = _desc_from(q, g)
     pol = _policy(policy)
+    n_seq = _seqs(cu_seqlens, q)
     lib = load()
-    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib.gdr_workspace_size(ctypes.byref(d), pol, ctypes.byref(sv), ctypes.byref(sc)))
+    _, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
+    ns = B if n_seq is None else n_seq
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                    dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
-                   dh0=torch.empty((B, H, 128, 128), dtype=torch.float32, device=q.device)
+                   dh0=torch.empty((ns, H, 128, 128), dtype=torch.float32, device=q.device)
                    if want_dh0 else None)
     if scratch is None:
-        scratch = _scratch(sc.value, q.device)
-    _check(fn(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0),
-              _ptr(dO), _ptr(dht), _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]),
-              _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out.get("dh0")),
-              _ptr(scratch), scratch.numel(), _stream()))
+        scratch = _scratch(scratch_b, q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dht),
+            _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+            _ptr(out["dbeta"]), _ptr(out.get("dh0")), _ptr(scratch), scratch.numel(), _stream())
+    if n_seq is None:
+        _check(getattr(lib, name)(ctypes.byref(d), pol, *args))
+    elif name == "gdr_bwd":
+        _check(lib.gdr_bwd_varlen(ctypes.byref(d), pol, _ptr(cu_seqlens), n_seq, *args))
+    else:
+        raise ValueError(f"{name} has no packed-batch form")
     return out
 
 
 def gdr_bwd(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
-            want_dh0=True, scratch=None, out=None):
-    """Backward (ReWY producer). Returns dict dq, dk, dv, dg, dbeta, dh0."""
-    return _bwd(load().gdr_bwd, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
-                scratch, out)
+            want_dh0=True, scratch=None, out=None, cu_seqlens=None):
+    """Backward (ReWY producer). Returns dict dq, dk, dv, dg, dbeta, dh0.
+    cu_seqlens as for gdr_fwd (the same offsets the forward ran with)."""
+    return _bwd("gdr_bwd", q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch,
+                out, cu_seqlens)
 
 
 def gdr_bwd_wy7(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
                 want_dh0=True, scratch=None, out=None):
     """Backward with the expanded seven-product WY producer (ablation)."""
-    return _bwd(load().gdr_bwd_wy7, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
+    return _bwd("gdr_bwd_wy7", q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
                 scratch, out)

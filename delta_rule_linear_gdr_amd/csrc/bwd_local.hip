@@ -57,12 +57,12 @@ __device__ __forceinline__ void st_half(bf16x8* buf, int tile, int half, const b
 template <typename T, bool VEC, bool WY7>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr)
 {
-    const int c = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = tile_of(s, bh, c);
-    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
-    const int nv = chunk_rows(s, c);  // rows past it read as zeros and are not written
+    SeqView sv;
+    int64_t c;
+    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    const int64_t t = seq_tile(s, sv, c);
+    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
+    const int nv = seq_rows(sv, c);  // rows past it read as zeros and are not written
     // Row stride (elements) of q, k, v, dO and their gradients. In-chunk
     // offsets stay below 64 * H * 128 < 2^31 (H <= 65535), so they are 32-bit
     // and every pointer below is a uniform per-chunk base.
@@ -745,7 +745,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st)
 {
-    dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
+    dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
 #define GDR_BWD_LOCAL(W7)                                                                        \
     do {                                                                                         \
         if (s.f32) {                                                                             \

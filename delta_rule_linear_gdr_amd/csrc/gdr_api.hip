@@ -124,6 +124,28 @@ hipError_t fill_state(float* dst, const float* src, int64_t n, hipStream_t st)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// A packed variable-length batch (on == false: a regular batch).
+struct Packed {
+    bool on = false;
+    const int64_t* cu = nullptr;  // device offsets, n + 1
+    int64_t n = 0;                // sequences
+};
+
+int64_t nchunks(const gdr_desc* d) { return (d->T + CH - 1) / CH; }  // the last may be partial
+// Chunk slots per head: all chunks of a regular row, or an upper bound on
+// the chunks of the packed sequences.
+int64_t nslots(const gdr_desc* d, const Packed& pk) { return nchunks(d) + (pk.on ? pk.n : 0); }
+size_t ntiles(const gdr_desc* d, const Packed& pk)
+{
+    return (size_t)(pk.on ? d->H : d->B * d->H) * (size_t)nslots(d, pk);
+}
+// Bytes of the sequence tables at the start of scratch (packed batches).
+size_t table_bytes(const gdr_desc* d, const Packed& pk)
+{
+    if (!pk.on) return 0;
+    return align_up(8 * (size_t)(pk.n + 1)) + align_up(8 * (size_t)pk.n) + align_up(8 * (size_t)nslots(d, pk));
+}
+
 int check_desc(const gdr_desc* d)
 {
     if (!d) return fail(GDR_ERR_INVALID, "descriptor is NULL");
@@ -167,16 +189,57 @@ int check_policy(int policy)
             return fail(GDR_ERR_INVALID, "pointer '%s' is not %d-byte aligned", #p, (int)(a)); \
     } while (0)
 
-Shape make_shape(const gdr_desc* d)
+Shape make_shape(const gdr_desc* d, const Packed& pk, void* scratch)
 {
     Shape s;
     s.B = d->B;
     s.T = d->T;
     s.H = d->H;
-    s.NT = (d->T + CH - 1) / CH;  // the last chunk may be partial
+    s.NT = nchunks(d);
     s.vec = d->gate == GDR_GATE_VECTOR;
     s.f32 = d->dtype == GDR_F32;
+    s.NS = pk.on ? pk.n : d->B;
+    s.NC = nslots(d, pk);
+    s.cu = nullptr;
+    s.stab = nullptr;
+    s.ctab = nullptr;
+    if (pk.on) {
+        char* p = (char*)scratch;
+        s.cu = (const int64_t*)p;
+        p += align_up(8 * (size_t)(pk.n + 1));
+        s.stab = (const int2*)p;
+        p += align_up(8 * (size_t)pk.n);
+        s.ctab = (const int2*)p;
+    }
     return s;
+}
+
+// Validation specific to packed batches: the shape, then the offsets pointer.
+int check_packed_shape(const gdr_desc* d, int64_t n_seq)
+{
+    if (n_seq < 0) return fail(GDR_ERR_INVALID, "negative sequence count %lld", (long long)n_seq);
+    if (d->B != 1)
+        return fail(GDR_ERR_INVALID, "a packed batch has B = 1 (sequences along T), got B=%lld",
+                    (long long)d->B);
+    if (nchunks(d) + n_seq > ((int64_t)1 << 30))
+        return fail(GDR_ERR_UNSUPPORTED, "%lld sequences over T=%lld: too many chunk slots",
+                    (long long)n_seq, (long long)d->T);
+    return GDR_OK;
+}
+int check_packed(const gdr_desc* d, const Packed& pk)
+{
+    int rc = check_packed_shape(d, pk.n);
+    if (rc) return rc;
+    if (!pk.cu) return fail(GDR_ERR_INVALID, "cu_seqlens is NULL");
+    if ((uintptr_t)pk.cu % 8) return fail(GDR_ERR_INVALID, "cu_seqlens is not 8-byte aligned");
+    return GDR_OK;
+}
+
+// Builds the sequence tables of a packed batch in scratch (no-op otherwise).
+hipError_t seq_tables(const Shape& s, const Packed& pk, hipStream_t st)
+{
+    if (!pk.on) return hipSuccess;
+    return launch_seq_tables(s, pk.cu, (int64_t*)s.cu, (int2*)s.stab, (int2*)s.ctab, st);
 }
 
 int hip_fail(hipError_t e, const char* what)
@@ -230,17 +293,19 @@ hipError_t timed(Stage stage, hipStream_t st, F&& launch)
     return e;
 }
 
-int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
-            const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
-            const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
-            void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
+            const void* v, const float* g, const void* beta, const float* h0, const void* dO,
+            const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta,
+            float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7)
 {
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_policy(policy))) return rc;
+    if (pk.on && (rc = check_packed(d, pk))) return rc;
     hipStream_t st = (hipStream_t)stream;
-    const int64_t nstate = d->B * d->H * DKD * DVD;
-    if (d->B * d->H == 0) return GDR_OK;
+    const int64_t nseq = pk.on ? pk.n : d->B;
+    const int64_t nstate = nseq * d->H * DKD * DVD;
+    if (nseq * d->H == 0) return GDR_OK;
     if (d->T == 0) {
         hipError_t e = fill_state(dh0, dht, nstate, st);
         return e == hipSuccess ? GDR_OK : hip_fail(e, "dh0 copy");
@@ -251,20 +316,22 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(dg, 4); REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(dht, 4); CHECK_ALIGN(dh0, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
+    const size_t tb = table_bytes(d, pk);
     Inter it;
     size_t sb = 0, need = 0;
-    layout(policy, BWD, nullptr, nullptr, ntiles, it, sb, need);
+    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
+    need += tb;
     if (!scratch || scratch_bytes < need)
         return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
                     scratch ? scratch_bytes : (size_t)0);
     if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
-    layout(policy, BWD, (void*)saved, scratch, ntiles, it, sb, need);
+    layout(policy, BWD, (void*)saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
 
-    const Shape s = make_shape(d);
+    const Shape s = make_shape(d, pk, scratch);
     Inputs in{q, k, v, beta, dO, g, h0, dht};
     Grads gr{dq, dk, dv, dbeta, dg, dh0};
-    hipError_t e;
+    hipError_t e = seq_tables(s, pk, st);
+    if (e != hipSuccess) return hip_fail(e, "sequence tables");
     if (policy == GDR_RECOMPUTE) {
         e = timed(ST_PREP, st, [&] {
             return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A | PREP_AF, st);
@@ -284,6 +351,61 @@ int run_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const v
     return GDR_OK;
 }
 
+int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
+            const void* v, const float* g, const void* beta, const float* h0, void* o, float* ht,
+            void* saved, void* scratch, size_t scratch_bytes, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    if (pk.on && (rc = check_packed(d, pk))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nseq = pk.on ? pk.n : d->B;
+    if (nseq * d->H == 0) return GDR_OK;
+    if (d->T == 0) {
+        hipError_t e = fill_state(ht, h0, nseq * d->H * DKD * DVD, st);
+        return e == hipSuccess ? GDR_OK : hip_fail(e, "ht copy");
+    }
+    const int esz = d->dtype == GDR_F32 ? 4 : 2;
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
+    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(beta, esz);
+    CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
+    if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
+    const size_t tb = table_bytes(d, pk);
+    Inter it;
+    size_t sb = 0, need = 0;
+    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
+    need += tb;
+    if (!scratch || scratch_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
+                    scratch ? scratch_bytes : (size_t)0);
+    if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
+    layout(policy, FWD, saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
+    const Shape s = make_shape(d, pk, scratch);
+    Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
+    hipError_t e = seq_tables(s, pk, st);
+    if (e != hipSuccess) return hip_fail(e, "sequence tables");
+    const int what = PREP_FWDSCAN | PREP_OUT |
+                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A | PREP_AF : 0);
+    e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, what, st); });
+    if (e != hipSuccess) return hip_fail(e, "prep");
+    e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });
+    if (e != hipSuccess) return hip_fail(e, "scan_fwd");
+    return GDR_OK;
+}
+
+
+int workspace(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_bytes, size_t* scratch_bytes)
+{
+    Inter it;
+    size_t s1 = 0, c1 = 0, s2 = 0, c2 = 0;
+    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, s1, c1);
+    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, s2, c2);
+    if (saved_bytes) *saved_bytes = s1;
+    if (scratch_bytes) *scratch_bytes = table_bytes(d, pk) + (c1 > c2 ? c1 : c2);
+    return GDR_OK;
+}
+
 }  // namespace
 }  // namespace gdr
 
@@ -296,61 +418,61 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_policy(policy))) return rc;
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
-    Inter it;
-    size_t s1 = 0, c1 = 0, s2 = 0, c2 = 0;
-    layout(policy, FWD, nullptr, nullptr, ntiles, it, s1, c1);
-    layout(policy, BWD, nullptr, nullptr, ntiles, it, s2, c2);
-    if (saved_bytes) *saved_bytes = s1;
-    if (scratch_bytes) *scratch_bytes = c1 > c2 ? c1 : c2;
-    return GDR_OK;
+    return workspace(d, Packed{}, policy, saved_bytes, scratch_bytes);
 }
 
 int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
             void* scratch, size_t scratch_bytes, void* stream)
 {
+    return run_fwd(d, Packed{}, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes,
+                   stream);
+}
+
+int gdr_fwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                   const void* q, const void* k, const void* v, const float* g, const void* beta,
+                   const float* h0, void* o, float* ht, void* saved, void* scratch,
+                   size_t scratch_bytes, void* stream)
+{
+    Packed pk;
+    pk.on = true;
+    pk.cu = cu_seqlens;
+    pk.n = n_seq;
+    return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
+}
+
+int gdr_workspace_size_varlen(const gdr_desc* d, int64_t n_seq, int policy, size_t* saved_bytes,
+                              size_t* scratch_bytes)
+{
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_policy(policy))) return rc;
-    hipStream_t st = (hipStream_t)stream;
-    if (d->B * d->H == 0) return GDR_OK;
-    if (d->T == 0) {
-        hipError_t e = fill_state(ht, h0, d->B * d->H * DKD * DVD, st);
-        return e == hipSuccess ? GDR_OK : hip_fail(e, "ht copy");
-    }
-    const int esz = d->dtype == GDR_F32 ? 4 : 2;
-    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
-    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(beta, esz);
-    CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
-    if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t ntiles = (size_t)(d->B * d->H) * (size_t)((d->T + CH - 1) / CH);
-    Inter it;
-    size_t sb = 0, need = 0;
-    layout(policy, FWD, nullptr, nullptr, ntiles, it, sb, need);
-    if (!scratch || scratch_bytes < need)
-        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
-                    scratch ? scratch_bytes : (size_t)0);
-    if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
-    layout(policy, FWD, saved, scratch, ntiles, it, sb, need);
-    const Shape s = make_shape(d);
-    Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
-    hipError_t e;
-    const int what = PREP_FWDSCAN | PREP_OUT |
-                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A | PREP_AF : 0);
-    e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, what, st); });
-    if (e != hipSuccess) return hip_fail(e, "prep");
-    e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });
-    if (e != hipSuccess) return hip_fail(e, "scan_fwd");
-    return GDR_OK;
+    if ((rc = check_packed_shape(d, n_seq))) return rc;
+    Packed pk;
+    pk.on = true;
+    pk.n = n_seq;
+    return workspace(d, pk, policy, saved_bytes, scratch_bytes);
 }
-
 int gdr_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
             const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
             void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_bwd(d, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
+    return run_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+                   dh0, scratch, scratch_bytes, stream, false);
+}
+
+int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                   const void* q, const void* k, const void* v, const float* g, const void* beta,
+                   const float* h0, const void* dO, const float* dht, const void* saved, void* dq,
+                   void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* scratch,
+                   size_t scratch_bytes, void* stream)
+{
+    Packed pk;
+    pk.on = true;
+    pk.cu = cu_seqlens;
+    pk.n = n_seq;
+    return run_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
                    scratch, scratch_bytes, stream, false);
 }
 
@@ -359,8 +481,8 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_bwd(d, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
-                   scratch, scratch_bytes, stream, true);
+    return run_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+                   dh0, scratch, scratch_bytes, stream, true);
 }
 
 const char* gdr_status_string(int status)

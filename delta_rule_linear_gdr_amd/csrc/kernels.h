@@ -64,21 +64,83 @@ struct Shape {
     int64_t B, T, H, NT;
     int vec;   // 1: per-channel gate [B,T,H,128]; 0: scalar gate [B,T,H]
     int f32;   // 1: q,k,v,beta,o,dO,dq,dk,dv,dbeta are fp32; 0: bf16
+    // Sequences (state entries) and chunk slots per head. Regular batch:
+    // NS = B, NC = NT. Packed variable-length batch (B = 1): NS sequences,
+    // NC = ceil(T / 64) + NS (at least the chunks of all sequences) and the
+    // device tables below, null otherwise.
+    int64_t NS, NC;
+    const int64_t* cu;  // sanitized token offsets, NS + 1
+    const int2* stab;   // per sequence: {first chunk slot, chunk count}
+    const int2* ctab;   // per chunk slot: {sequence, chunk in it}, {-1, 0} if unused
 };
 
-// Tokens of chunk c: 64, except in a ragged last chunk when T % 64 != 0.
-// The missing rows act as identity steps (g = 0, beta = 0, zero q, k, v and
-// dO): kernels read zeros for them and write nothing for them, which leaves
-// every state, output and gradient of the real tokens exact.
-__host__ __device__ inline int chunk_rows(const Shape& s, int64_t c)
+// One sequence of one head. Each sequence is chunked on its own; its last
+// chunk may be ragged. The missing rows of a ragged chunk act as identity
+// steps (g = 0, beta = 0, zero q, k, v and dO): kernels read zeros for them
+// and write nothing for them, which leaves every state, output and gradient
+// of the real tokens exact.
+struct SeqView {
+    int64_t tok;     // token index (along T) of the sequence's first token
+    int64_t len;     // its tokens
+    int64_t nchunk;  // its chunks
+    int64_t slot0;   // chunk slot of its chunk 0 (packed batches)
+    int64_t n, hd;   // sequence (state entry) and head
+};
+
+__host__ __device__ inline SeqView seq_view(const Shape& s, int64_t n, int64_t hd)
 {
-    const int64_t r = s.T - c * CH;
+    SeqView v;
+    v.n = n;
+    v.hd = hd;
+    if (s.ctab) {
+        v.tok = s.cu[n];
+        v.len = s.cu[n + 1] - v.tok;
+        v.slot0 = s.stab[n].x;
+        v.nchunk = s.stab[n].y;
+    } else {
+        v.tok = n * s.T;
+        v.len = s.T;
+        v.slot0 = 0;
+        v.nchunk = s.NT;
+    }
+    return v;
+}
+
+// Tile index of chunk c: chunk-major, so the tiles of all heads for one
+// chunk (slot) are contiguous and a scan step, which visits one chunk of
+// every head, reads and writes a few contiguous regions.
+__host__ __device__ inline int64_t seq_tile(const Shape& s, const SeqView& v, int64_t c)
+{
+    return s.ctab ? (v.slot0 + c) * s.H + v.hd : c * (s.B * s.H) + v.n * s.H + v.hd;
+}
+
+// Valid rows of chunk c (64 except in a ragged last chunk).
+__host__ __device__ inline int seq_rows(const SeqView& v, int64_t c)
+{
+    const int64_t r = v.len - c * CH;
     return r < CH ? (int)r : CH;
 }
 
-__host__ __device__ inline int64_t tile_of(const Shape& s, int64_t bh, int64_t c)
+// Row index into [.., T, H, ..] token-major tensors of chunk c's first token.
+__host__ __device__ inline int64_t seq_tok0(const Shape& s, const SeqView& v, int64_t c)
 {
-    return c * (s.B * s.H) + bh;
+    return (v.tok + c * CH) * s.H + v.hd;
+}
+
+// The chunk of a per-chunk workgroup (blockIdx.x = chunk or chunk slot,
+// blockIdx.y = b * H + head); false for an unused slot of a packed batch.
+__device__ inline bool chunk_of_block(const Shape& s, SeqView& v, int64_t& c)
+{
+    if (s.ctab) {
+        const int2 e = s.ctab[blockIdx.x];
+        if (e.x < 0) return false;
+        v = seq_view(s, e.x, blockIdx.y);
+        c = e.y;
+    } else {
+        v = seq_view(s, blockIdx.y / s.H, blockIdx.y % s.H);
+        c = blockIdx.x;
+    }
+    return true;
 }
 
 struct Inputs {
@@ -119,6 +181,10 @@ hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, fl
 // dh0 when dh0 != null.
 hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                             hipStream_t st);
+// Packed batches: sanitizes cu_in (clamped to [0, T], made nondecreasing)
+// into s.cu and fills s.stab and s.ctab (one workgroup).
+hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, int2* stab, int2* ctab,
+                             hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st);

@@ -57,13 +57,13 @@ __device__ __forceinline__ void st_row8_frag(bf16* base, int i, int f0, const fl
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter it, int what)
 {
-    const int c = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = tile_of(s, bh, c);
-    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;  // token of row 0
+    SeqView sv;
+    int64_t c;
+    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    const int64_t t = seq_tile(s, sv, c);
+    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
     const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
-    const int nv = chunk_rows(s, c);  // rows past it are read as zeros
+    const int nv = seq_rows(sv, c);  // rows past it are read as zeros
     const int tid = threadIdx.x;
     const int l = lane_id(), r = lane_r(), g = lane_g();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -622,15 +622,15 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 template <typename T>
 __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
 {
-    const int c = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int64_t b = bh / s.H, hd = bh % s.H;
-    const int64_t t = tile_of(s, bh, c);
-    const int64_t tok0 = (b * s.T + (int64_t)c * CH) * s.H + hd;
+    SeqView sv;
+    int64_t c;
+    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    const int64_t t = seq_tile(s, sv, c);
+    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
     const int ld = (int)(s.H * DVD);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* dO = (const T*)in.dO + tok0 * DVD;
-    const int nv = chunk_rows(s, c);  // rows past it are read as zeros
+    const int nv = seq_rows(sv, c);  // rows past it are read as zeros
 
     const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
     f32x4 OC[4][2];
@@ -673,7 +673,7 @@ __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
 
 hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what, hipStream_t st)
 {
-    dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
+    dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
     if (s.f32) {
         if (s.vec) prep_kernel<float, true><<<grid, 256, 0, st>>>(s, in, it, what);
         else prep_kernel<float, false><<<grid, 256, 0, st>>>(s, in, it, what);
@@ -686,7 +686,7 @@ hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int wh
 
 hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStream_t st)
 {
-    dim3 grid((unsigned)s.NT, (unsigned)(s.B * s.H));
+    dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
     if (s.f32) xy_kernel<float><<<grid, 256, 0, st>>>(s, in, it);
     else xy_kernel<bf16><<<grid, 256, 0, st>>>(s, in, it);
     return hipGetLastError();

@@ -97,11 +97,11 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
                                           float* fin, int block)
 {
     int bh, vs;
-    map_block((int)(s.B * s.H * NVS), block, bh, vs);
-    const int64_t b = bh / s.H, hd = bh % s.H;
+    map_block((int)(s.NS * s.H * NVS), block, bh, vs);
+    const SeqView sq = seq_view(s, bh / s.H, bh % s.H);  // bh = sequence * H + head
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id(), r = lane_r(), g = lane_g();
-    const int NT = (int)s.NT;
+    const int NT = (int)sq.nchunk;
     const int v = 16 * vs + r;  // this lane's value column
 
     __shared__ bf16x8 sS[4][64];  // state slabs: B operands over keys
@@ -121,9 +121,22 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             S[m][i] = init ? init[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] : 0.f;
+    auto write_fin = [&]() {
+        if (fin) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    fin[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = S[m][i];
+        }
+    };
+    if (NT == 0) {  // an empty sequence of a packed batch: nothing to walk
+        write_fin();
+        return;
+    }
 
     auto chunk = [&](int p) { return BWD ? NT - 1 - p : p; };
-    auto tile = [&](int c) { return tile_of(s, bh, c); };
+    auto tile = [&](int c) { return seq_tile(s, sq, c); };
 
     // Stores of a step are issued after the next group of prefetch loads:
     // loads and stores share one in-order completion counter, so a store
@@ -193,8 +206,8 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
         if (OUT) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) oacc = mfma(op.hm[ks], zf[ks], oacc);
-            pend_tok = (b * s.T + (int64_t)c * CH + 16 * w + 4 * g) * s.H + hd;
-            pend_rows = chunk_rows(s, c);
+            pend_tok = seq_tok0(s, sq, c) + (int64_t)(16 * w + 4 * g) * s.H;
+            pend_rows = seq_rows(sq, c);
             pend_o = oacc;
         }
     };
@@ -237,13 +250,7 @@ __device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, cons
         step(P1, chunk(p + 1));
         flush();
     }
-    if (fin) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fin[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = S[m][i];
-    }
+    write_fin();
 }
 
 template <bool BWD, bool OUT, bool STORE, typename T>
@@ -336,14 +343,15 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
 }
 
 template <bool BWD, int J>
-__device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, int bh, int vs, uint8_t* ring)
+__device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, const SeqView& sq, int vs,
+                                           uint8_t* ring)
 {
     constexpr int NL = BWD ? fed::NL_BWD : fed::NL_FWD;
-    const int NT = (int)s.NT;
+    const int NT = (int)sq.nchunk;  // >= 1
     auto issue = [&](int p) {
         const int pc = p < NT ? p : NT - 1;  // past the end: the last chunk again
         const int c = BWD ? NT - 1 - pc : pc;
-        fed_issue<BWD, J>(it, tile_of(s, bh, c), vs, ring + (p % fed::NSLOT) * fed::SLOT);
+        fed_issue<BWD, J>(it, seq_tile(s, sq, c), vs, ring + (p % fed::NSLOT) * fed::SLOT);
     };
     issue(0);
     issue(1);
@@ -360,11 +368,11 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, int 
 
 template <bool BWD>
 __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, const Inter& it, float* fin,
-                                            int bh, int vs, const uint8_t* ring)
+                                            const SeqView& sq, int bh, int vs, const uint8_t* ring)
 {
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id(), r = lane_r(), g = lane_g();
-    const int NT = (int)s.NT;
+    const int NT = (int)sq.nchunk;  // 0 for an empty sequence: the state passes through
     const int v = 16 * vs + r;
 
     __shared__ bf16x8 sS[4][64];
@@ -383,7 +391,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 
     for (int p = 0; p < NT; ++p) {
         const int c = BWD ? NT - 1 - p : p;
-        const int64_t t = tile_of(s, bh, c);
+        const int64_t t = seq_tile(s, sq, c);
         const uint8_t* slot = ring + (p % fed::NSLOT) * fed::SLOT;
         // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile vs)
 #pragma unroll
@@ -444,14 +452,16 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
                                          int block, uint8_t* ring)
 {
     int bh, vs;
-    map_block((int)(s.B * s.H * NVS), block, bh, vs);
+    map_block((int)(s.NS * s.H * NVS), block, bh, vs);
+    const SeqView sq = seq_view(s, bh / s.H, bh % s.H);  // bh = sequence * H + head
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (sq.nchunk == 0 && w >= 4) return;  // an empty sequence: no steps, no barriers
     switch (w) {
-    case 4: fed_loader<BWD, 0>(s, it, bh, vs, ring); break;
-    case 5: fed_loader<BWD, 1>(s, it, bh, vs, ring); break;
-    case 6: fed_loader<BWD, 2>(s, it, bh, vs, ring); break;
-    case 7: fed_loader<BWD, 3>(s, it, bh, vs, ring); break;
-    default: fed_compute<BWD>(s, in, it, fin, bh, vs, ring); break;
+    case 4: fed_loader<BWD, 0>(s, it, sq, vs, ring); break;
+    case 5: fed_loader<BWD, 1>(s, it, sq, vs, ring); break;
+    case 6: fed_loader<BWD, 2>(s, it, sq, vs, ring); break;
+    case 7: fed_loader<BWD, 3>(s, it, sq, vs, ring); break;
+    default: fed_compute<BWD>(s, in, it, fin, sq, bh, vs, ring); break;
     }
 }
 
@@ -462,7 +472,7 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
 __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* dh0, int both)
 {
     __shared__ __attribute__((aligned(16))) uint8_t ring[fed::NSLOT * fed::SLOT];
-    const int nblk = (int)(s.B * s.H * NVS);
+    const int nblk = (int)(s.NS * s.H * NVS);
     if (both && (int)blockIdx.x < nblk) fed_body<false>(s, in, it, nullptr, blockIdx.x, ring);
     else fed_body<true>(s, in, it, dh0, both ? blockIdx.x - nblk : blockIdx.x, ring);
 }
@@ -472,7 +482,7 @@ __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o, float* ht,
                            hipStream_t st)
 {
-    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    const unsigned nblk = (unsigned)(s.NS * s.H * NVS);
     const bool store = it.h != nullptr;
     if (o) {
         if (s.f32) {
@@ -491,7 +501,7 @@ hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, vo
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                            hipStream_t st)
 {
-    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    const unsigned nblk = (unsigned)(s.NS * s.H * NVS);
     scan_fed_kernel<<<nblk, 512, 0, st>>>(s, in, it, dh0, 0);
     return hipGetLastError();
 }
@@ -502,7 +512,7 @@ namespace gdr {
 hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                             hipStream_t st)
 {
-    const unsigned nblk = (unsigned)(s.B * s.H * NVS);
+    const unsigned nblk = (unsigned)(s.NS * s.H * NVS);
     scan_fed_kernel<<<2 * nblk, 512, 0, st>>>(s, in, it, dh0, 1);
     return hipGetLastError();
 }

@@ -111,3 +111,33 @@ def make_inputs(B, T, H, DK=128, DV=128, gate="scalar", dtype="bf16", seed=0,
         h0=round_fp32(h0), dht=round_fp32(dht),
         gate=gate, dtype=dtype,
     )
+
+
+def packed_lengths(total: int, n: int, seed: int = 0) -> list[int]:
+    """Lengths of n sequences packed into `total` tokens: n - 1 cut points
+    drawn uniformly (with replacement) from [0, total] and sorted, so the mix
+    holds short, long and occasionally empty sequences."""
+    rng = np.random.default_rng(seed)
+    cuts = np.sort(rng.integers(0, total + 1, size=max(n - 1, 0)))
+    edges = np.concatenate([[0], cuts, [total]])
+    return [int(x) for x in np.diff(edges)]
+
+
+def make_packed_inputs(lengths, H, gate="scalar", dtype="bf16", seed=0, gate_mean=4.0,
+                       state_std=0.1, cover=None) -> dict:
+    """A packed variable-length batch: the sequences of `lengths` laid end to
+    end in one row of `cover` tokens (default: their sum; more leaves a tail
+    that belongs to no sequence). Token inputs follow make_inputs(1, cover, H,
+    seed=seed); then numpy.random.default_rng(seed + 1) draws the per-sequence
+    states h0 and dht = state_std * N(0, 1), [n, H, DK, DV] each, rounded to
+    fp32. cu holds the n + 1 int64 token offsets."""
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths) if cover is None else int(cover)
+    assert T >= sum(lengths)
+    x = make_inputs(1, T, H, gate=gate, dtype=dtype, seed=seed, gate_mean=gate_mean)
+    n = len(lengths)
+    rng = np.random.default_rng(seed + 1)
+    x["h0"] = round_fp32(state_std * rng.standard_normal((n, H, 128, 128)))
+    x["dht"] = round_fp32(state_std * rng.standard_normal((n, H, 128, 128)))
+    x["cu"] = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    return x

@@ -120,6 +120,34 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
 
+/* Packed variable-length batches (several sequences in one row of tokens,
+ * the cu_seqlens convention of flash-linear-attention, which the pages'
+ * reference implementation builds on). d->B must be 1; the row of d->T
+ * tokens holds n_seq sequences, sequence i spanning tokens
+ * [cu_seqlens[i], cu_seqlens[i+1]). cu_seqlens is a DEVICE array of n_seq + 1
+ * int64 offsets, 8-byte aligned, expected nondecreasing from 0 (the library
+ * reads it only on the device, clamps it to [0, T] and makes it
+ * nondecreasing, so malformed offsets cannot make it read or write outside
+ * the tensors; tokens outside every sequence are left untouched). Each
+ * sequence is chunked on its own (its last chunk may be ragged) and starts
+ * from its own state: h0, ht, dht, dh0 are [n_seq, H, 128, 128] fp32.
+ * Empty sequences pass their state through. Everything else (tensors,
+ * dtypes, policies, errors) is as for gdr_fwd / gdr_bwd. The workspace
+ * holds ceil(T / 64) + n_seq chunk slots per head plus small sequence
+ * tables; a full-save `saved` area is tied to the cu_seqlens it was written
+ * with. */
+int gdr_workspace_size_varlen(const gdr_desc* d, int64_t n_seq, int policy, size_t* saved_bytes,
+                              size_t* scratch_bytes);
+int gdr_fwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                   const void* q, const void* k, const void* v, const float* g, const void* beta,
+                   const float* h0, void* o, float* ht, void* saved, void* scratch,
+                   size_t scratch_bytes, void* stream);
+int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                   const void* q, const void* k, const void* v, const float* g, const void* beta,
+                   const float* h0, const void* dO, const float* dht, const void* saved, void* dq,
+                   void* dk, void* dv, float* dg, void* dbeta, float* dh0, void* scratch,
+                   size_t scratch_bytes, void* stream);
+
 /* Per-stage timing for benchmarks. gdr_profile_begin creates 2*max_launches
  * HIP events (the only allocation the library makes, and only here) and
  * turns timing on: every kernel that gdr_fwd / gdr_bwd / gdr_bwd_wy7 then

@@ -114,3 +114,72 @@ def compare(gpu, x, heads=None, names=None, report=None):
     if report is not None:
         report.update(errs)
     return errs
+
+
+# ---------------------------------------------------- packed (varlen) batches
+
+SENTINEL = 7.0  # prefilled into gradient outputs; tokens of no sequence keep it
+
+
+def run_gpu_packed(x, policy="recompute"):
+    """Packed forward + backward (cu_seqlens) on the device; numpy float64."""
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    d = device_inputs(x)
+    cu = torch.from_numpy(x["cu"]).to("cuda")
+    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+                               policy=policy, cu_seqlens=cu)
+    out = {n: torch.full_like(d[s], SENTINEL) for n, s in
+           (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"))}
+    out["dh0"] = torch.empty_like(d["h0"])
+    gr = gdr.gdr_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["dO"], d["dht"],
+                     saved=saved, policy=policy, out=out, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    res = {"o": o, "ht": ht, **gr}
+    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items()}
+
+
+def oracle_packed(x, heads=None):
+    """Oracle per (sequence, head): each sequence is its own problem with its
+    own h0 and dht. An empty sequence passes its state through (ht = h0,
+    dh0 = dht), which needs no oracle call."""
+    cu = x["cu"]
+    H = x["q"].shape[2]
+    heads = range(H) if heads is None else heads
+    ref = {}
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for h in heads:
+            sl = lambda t: t[:, a:b, h:h + 1]       # noqa: E731
+            st = lambda t: t[i:i + 1, h:h + 1]      # noqa: E731
+            if b == a:
+                ref[i, h] = {"ht": st(x["h0"]), "dh0": st(x["dht"])}
+                continue
+            o, ht = oracle.token_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]),
+                                     sl(x["beta"]), st(x["h0"]))
+            gr = oracle.token_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
+                                  st(x["h0"]), sl(x["dO"]), st(x["dht"]))
+            ref[i, h] = {"o": o, "ht": ht, **gr}
+    return ref
+
+
+def compare_packed(gpu, x, heads=None, report=None):
+    """Per-tensor acceptance over the covered tokens of the chosen heads, and
+    the gradient outputs of tokens outside every sequence left untouched."""
+    cu = x["cu"]
+    ref = oracle_packed(x, heads)
+    got_all, ref_all = {}, {}
+    for (i, h), r in ref.items():
+        a, b = int(cu[i]), int(cu[i + 1])
+        for n, arr in r.items():
+            g = gpu[n][i:i + 1, h:h + 1] if n in ("ht", "dh0") else gpu[n][:, a:b, h:h + 1]
+            got_all.setdefault(n, []).append(g.ravel())
+            ref_all.setdefault(n, []).append(np.asarray(arr).ravel())
+    errs = {n: check(n, np.concatenate(got_all[n]), np.concatenate(ref_all[n]))
+            for n in got_all}
+    tail = int(cu[-1])
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.all(gpu[n][:, tail:] == SENTINEL), f"{n}: tokens past the last sequence written"
+    if report is not None:
+        report.update(errs)
+    return errs

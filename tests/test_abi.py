@@ -114,3 +114,59 @@ def test_status_strings():
     lib = gdr.load()
     for st in (0, -1, -2, -3, -4, 99):
         assert lib.gdr_status_string(st)
+
+
+def _ws_varlen(d, n_seq, policy=0):
+    sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+    rc = gdr.load().gdr_workspace_size_varlen(ctypes.byref(d), n_seq, policy, ctypes.byref(sv),
+                                              ctypes.byref(sc))
+    return rc, sv.value, sc.value
+
+
+def test_packed_workspace_counts_slots_and_tables():
+    """A packed batch of n sequences over T tokens has at most ceil(T/64) + n
+    chunks per head; the workspace holds that many tiles (each tile kind in
+    its own 256-byte-aligned block, as for a regular row of that many chunks)
+    plus the offsets, the per-sequence table and the per-slot table."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for T, n in ((8192, 7), (100, 3), (64, 0), (1, 1)):
+        for pol in (0, 1):
+            nslot = (T + 63) // 64 + n
+            rc, sv, sc = _ws_varlen(_desc(T=T, H=4), n, pol)
+            assert rc == 0
+            # a regular row with nslot chunks has exactly the tile part
+            rc, sv_r, sc_r = _ws(_desc(T=64 * nslot, H=4), pol)
+            assert rc == 0
+            assert sv == sv_r
+            assert sc == sc_r + al(8 * (n + 1)) + al(8 * n) + al(8 * nslot)
+
+
+def test_packed_validation_without_launching():
+    lib = gdr.load()
+    assert _ws_varlen(_desc(B=2), 3)[0] == -1            # sequences live along T
+    assert _ws_varlen(_desc(), -1)[0] == -1
+    assert _ws_varlen(_desc(DK=64), 2)[0] == -2
+    fake = 1 << 20  # never dereferenced: validation fails first
+    d = _desc(T=256)
+    sc = _ws_varlen(d, 2)[2]
+
+    def fwd(cu, n=2, nbytes=sc, **p):
+        P = {x: p.get(x, fake) for x in ("q", "k", "v", "g", "beta", "o", "scratch")}
+        return lib.gdr_fwd_varlen(ctypes.byref(d), 0, cu, n, P["q"], P["k"], P["v"], P["g"],
+                                  P["beta"], None, P["o"], None, None, P["scratch"], nbytes,
+                                  None)
+
+    assert fwd(None) == -1
+    assert b"cu_seqlens" in lib.gdr_last_error()
+    assert fwd(fake + 4) == -1                            # not 8-byte aligned
+    assert fwd(fake, nbytes=sc // 4) == -3                # tables + tiles do not fit
+    assert fwd(fake, q=None) == -1
+    assert fwd(fake, n=-2) == -1
+    # no sequences, or no tokens with no state to pass through: nothing to do
+    assert fwd(fake, n=0) == 0
+    d0 = _desc(T=0)
+    assert lib.gdr_fwd_varlen(ctypes.byref(d0), 0, fake, 3, None, None, None, None, None, None,
+                              None, None, None, None, 0, None) == 0
+    P = [None] * 16
+    assert lib.gdr_bwd_varlen(ctypes.byref(_desc(B=2)), 0, fake, 1, *P, 0, None) == -1
+    assert lib.gdr_bwd_varlen(ctypes.byref(d), 0, None, 1, *P, 0, None) == -1
