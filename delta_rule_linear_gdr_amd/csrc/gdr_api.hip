@@ -143,7 +143,8 @@ size_t ntiles(const gdr_desc* d, const Packed& pk)
 size_t table_bytes(const gdr_desc* d, const Packed& pk)
 {
     if (!pk.on) return 0;
-    return align_up(8 * (size_t)(pk.n + 1)) + align_up(8 * (size_t)pk.n) + align_up(8 * (size_t)nslots(d, pk));
+    return align_up(8 * (size_t)(pk.n + 1)) + align_up(8 * (size_t)pk.n) + align_up(8 * (size_t)nslots(d, pk)) +
+           align_up(4 * (size_t)pk.n);
 }
 
 int check_desc(const gdr_desc* d)
@@ -203,6 +204,7 @@ Shape make_shape(const gdr_desc* d, const Packed& pk, void* scratch)
     s.cu = nullptr;
     s.stab = nullptr;
     s.ctab = nullptr;
+    s.order = nullptr;
     if (pk.on) {
         char* p = (char*)scratch;
         s.cu = (const int64_t*)p;
@@ -210,6 +212,8 @@ Shape make_shape(const gdr_desc* d, const Packed& pk, void* scratch)
         s.stab = (const int2*)p;
         p += align_up(8 * (size_t)pk.n);
         s.ctab = (const int2*)p;
+        p += align_up(8 * (size_t)s.NC);
+        s.order = (const int*)p;
     }
     return s;
 }
@@ -239,7 +243,7 @@ int check_packed(const gdr_desc* d, const Packed& pk)
 hipError_t seq_tables(const Shape& s, const Packed& pk, hipStream_t st)
 {
     if (!pk.on) return hipSuccess;
-    return launch_seq_tables(s, pk.cu, (int64_t*)s.cu, (int2*)s.stab, (int2*)s.ctab, st);
+    return launch_seq_tables(s, pk.cu, (int64_t*)s.cu, (int2*)s.stab, (int2*)s.ctab, (int*)s.order, st);
 }
 
 int hip_fail(hipError_t e, const char* what)

@@ -72,6 +72,7 @@ struct Shape {
     const int64_t* cu;  // sanitized token offsets, NS + 1
     const int2* stab;   // per sequence: {first chunk slot, chunk count}
     const int2* ctab;   // per chunk slot: {sequence, chunk in it}, {-1, 0} if unused
+    const int* order;   // sequences, longest first (by length class), for the scans
 };
 
 // One sequence of one head. Each sequence is chunked on its own; its last
@@ -182,9 +183,9 @@ hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, fl
 hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
                             hipStream_t st);
 // Packed batches: sanitizes cu_in (clamped to [0, T], made nondecreasing)
-// into s.cu and fills s.stab and s.ctab (one workgroup).
+// into s.cu and fills s.stab, s.ctab and s.order (one workgroup).
 hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, int2* stab, int2* ctab,
-                             hipStream_t st);
+                             int* order, hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st);

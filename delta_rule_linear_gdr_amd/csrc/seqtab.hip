@@ -1,7 +1,16 @@
 // Packed variable-length batches (several sequences in one row of T tokens,
 // FLA's cu_seqlens convention): the sequence and chunk-slot tables every
-// other kernel reads (kernels.h, Shape::cu / stab / ctab). One workgroup;
-// N + 1 offsets are processed in tiles of 1024 with a running carry.
+// other kernel reads (kernels.h, Shape::cu / stab / ctab / order). One
+// workgroup; N + 1 offsets are processed in tiles of 1024 with a running
+// carry.
+//
+// `order` lists the sequences longest first, so that the scans, whose
+// workgroups each walk one sequence's chunks serially, start the longest
+// walks first (longest-processing-time-first list scheduling). Lengths are
+// ranked by class -- the chunk count itself below 4, else its octave and the
+// two bits after the leading one -- which keeps the ranking a single
+// histogram pass; ties within a class are placed in any order (only the
+// schedule depends on it, never a result).
 //
 // The caller's offsets are sanitized first (clamped to [0, T], cu[0] = 0,
 // made nondecreasing), so no table entry can send a kernel outside the
@@ -15,6 +24,15 @@ namespace gdr {
 namespace {
 
 constexpr int NTH = 1024;
+constexpr int NCLASS = 128;
+
+// Length class of a chunk count n < 2^30; nondecreasing in n, below NCLASS.
+__device__ __forceinline__ int len_class(int n)
+{
+    if (n < 4) return n;
+    const int e = 31 - __clz(n);
+    return 4 * (e - 1) + ((n >> (e - 2)) & 3);
+}
 
 // Inclusive block scan of x over the 1024 threads with `op`; every thread
 // also receives the tile total in *tot.
@@ -36,9 +54,10 @@ __device__ int64_t block_scan(int64_t x, int64_t* buf, int64_t* tot, Op op)
 }
 
 __global__ __launch_bounds__(NTH) void seq_tables_kernel(Shape s, const int64_t* cu_in, int64_t* cu,
-                                                         int2* stab, int2* ctab)
+                                                         int2* stab, int2* ctab, int* order)
 {
     __shared__ int64_t buf[NTH];
+    __shared__ int cls_next[NCLASS];
     const int tid = threadIdx.x;
     const int64_t N = s.NS, T = s.T;
     auto mx = [](int64_t a, int64_t b) { return a > b ? a : b; };
@@ -74,19 +93,34 @@ __global__ __launch_bounds__(NTH) void seq_tables_kernel(Shape s, const int64_t*
 
     // 3. chunk slots: unused by default, then each sequence claims its own
     for (int64_t j = tid; j < s.NC; j += NTH) ctab[j] = make_int2(-1, 0);
+    if (tid < NCLASS) cls_next[tid] = 0;
     __syncthreads();
     for (int64_t i = tid; i < N; i += NTH) {
         const int2 e = stab[i];
         for (int c = 0; c < e.y; ++c) ctab[e.x + c] = make_int2((int)i, c);
+        atomicAdd(&cls_next[len_class(e.y)], 1);
     }
+    __syncthreads();
+
+    // 4. order: class counts -> first position of each class, longest first
+    if (tid == 0) {
+        int pos = 0;
+        for (int k = NCLASS - 1; k >= 0; --k) {
+            const int n = cls_next[k];
+            cls_next[k] = pos;
+            pos += n;
+        }
+    }
+    __syncthreads();
+    for (int64_t i = tid; i < N; i += NTH) order[atomicAdd(&cls_next[len_class(stab[i].y)], 1)] = (int)i;
 }
 
 }  // namespace
 
 hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, int2* stab, int2* ctab,
-                             hipStream_t st)
+                             int* order, hipStream_t st)
 {
-    seq_tables_kernel<<<1, NTH, 0, st>>>(s, cu_in, cu, stab, ctab);
+    seq_tables_kernel<<<1, NTH, 0, st>>>(s, cu_in, cu, stab, ctab, order);
     return hipGetLastError();
 }
 

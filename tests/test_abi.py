@@ -127,7 +127,8 @@ def test_packed_workspace_counts_slots_and_tables():
     """A packed batch of n sequences over T tokens has at most ceil(T/64) + n
     chunks per head; the workspace holds that many tiles (each tile kind in
     its own 256-byte-aligned block, as for a regular row of that many chunks)
-    plus the offsets, the per-sequence table and the per-slot table."""
+    plus the offsets, the per-sequence table, the per-slot table and the
+    longest-first sequence order."""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for T, n in ((8192, 7), (100, 3), (64, 0), (1, 1)):
         for pol in (0, 1):
@@ -138,7 +139,7 @@ def test_packed_workspace_counts_slots_and_tables():
             rc, sv_r, sc_r = _ws(_desc(T=64 * nslot, H=4), pol)
             assert rc == 0
             assert sv == sv_r
-            assert sc == sc_r + al(8 * (n + 1)) + al(8 * n) + al(8 * nslot)
+            assert sc == sc_r + al(8 * (n + 1)) + al(8 * n) + al(8 * nslot) + al(4 * n)
 
 
 def test_packed_validation_without_launching():
