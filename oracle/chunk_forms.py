@@ -44,6 +44,19 @@ Consumers of D and Hb:
              min G)/2 per feature, alpha = exp(G - c), zeta = exp(c - G),
              Q' = alpha Q, E' = beta alpha K, Y' = zeta K;
              U_q = Hb Y', U_e = D Y', U_y = Hb^T Q' + D^T E'.
+  "windowed" the centred factors applied per window of the chunk (32 tokens:
+             the token slab of one MFMA contraction) for a vector gate with
+             strong decay: a block of two tokens in the same window uses that
+             window's centre; the block of a later window's rows against an
+             earlier window's columns uses a boundary pivot p (G at the last
+             token of the earlier window for Hb Y' and D Y', at the first token
+             of the later window for Hb^T Q' and D^T E'), for which G_i <= p <=
+             G_j, so both factors exp(G_i - p) and exp(p - G_j) are at most 1
+             when g <= 0. The factors then span exp(+-window range / 2) instead
+             of exp(+-chunk range / 2). (Paper Sec. 3.3 centres per chunk; the
+             windows are this implementation's reading of the "subchunk path"
+             that the repository page's "Compatibility" section gives stronger
+             gates.)
 Readings where the pages are silent are the ones listed with the design notes:
 decay before erase, inclusive output, key-major state, undivided dbeta.
 """
@@ -124,13 +137,15 @@ def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
 
 
 def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="direct",
-                   flops: FlopCounter | None = None, centre=None):
+                   flops: FlopCounter | None = None, centre=None, window=32):
     """Chunkwise backward of one (b, h) sequence.
 
     producer: "rewy" (three products) or "wy7" (expanded graph).
-    consumer: "direct", "gram" (scalar gate only) or "centred" (any gate).
+    consumer: "direct", "gram" (scalar gate only), "centred" or "windowed"
+              (any gate).
     centre:   optional override of the centring constants, a function
               (G (n, DK)) -> c (DK,), used to test centring invariance.
+    window:   window length of the "windowed" consumer.
     Returns dict dq, dk, dv, dg, dbeta, dh0.
     """
     fc = flops if flops is not None else FlopCounter()
@@ -200,6 +215,35 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
             gl = bt * np.sum(K * AK, axis=1) - np.sum(K * BK, axis=1) \
                 + np.sum(Q * GqK, axis=1) - np.sum(K * GqtQ, axis=1)
             Gb[:, 0] += gl  # scalar gate: all feature columns are summed below
+        elif consumer == "windowed":
+            n = e - s
+            wins = [(a, min(a + window, n)) for a in range(0, n, window)]
+            for ia, (a0, a1) in enumerate(wins):
+                for ib, (b0, b1) in enumerate(wins[:ia + 1]):
+                    Gi, Gj = G[a0:a1], G[b0:b1]          # rows i (later), columns j
+                    if ia == ib:
+                        c = 0.5 * (Gi.max(axis=0) + Gi.min(axis=0))
+                        p_lo = p_up = c
+                    else:
+                        p_lo = G[b1 - 1]                 # last token of window b
+                        p_up = G[a0]                     # first token of window a
+                    Hb_ab, D_ab = Hb[a0:a1, b0:b1], D[a0:a1, b0:b1]
+                    Ki, Qi, bi = K[a0:a1], Q[a0:a1], bt[a0:a1]
+                    Kj = K[b0:b1]
+                    # rows i: Hb Y' and D Y', scaled back by exp(G_i - p_lo)
+                    al = np.exp(Gi - p_lo)
+                    Yp = np.exp(p_lo - Gj) * Kj
+                    uq = al * (Hb_ab @ Yp)
+                    ue = al * (D_ab @ Yp)
+                    dq_c[a0:a1] += uq
+                    dk_c[a0:a1] += bi[:, None] * ue
+                    db_c[a0:a1] += np.sum(ue * Ki, axis=1)
+                    Gb[a0:a1] += Qi * uq + bi[:, None] * Ki * ue
+                    # columns j: Hb^T Q' + D^T E', scaled back by exp(p_up - G_j)
+                    al2 = np.exp(Gi - p_up)
+                    uy = np.exp(p_up - Gj) * (Hb_ab.T @ (al2 * Qi) + D_ab.T @ (bi[:, None] * al2 * Ki))
+                    dk_c[b0:b1] += uy
+                    Gb[b0:b1] -= Kj * uy
         elif consumer == "centred":
             c = centre(G) if centre is not None else 0.5 * (G.max(axis=0) + G.min(axis=0))
             al = np.exp(G - c[None, :])
@@ -231,6 +275,29 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
         # --- reverse state scan ---
         Sbn = gn[:, None] * Sbn + Qg.T @ Ob + Sb_res
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=Sbn)
+
+
+def pivoted_lower(X, Y, G, incl, tile=16):
+    """lower((X o exp(G)) (Y o exp(-G))^T) of one chunk -- entries
+    sum_f X_if Y_jf exp(G_if - G_jf) for j < i (j <= i if incl) -- formed tile
+    by tile as a product of factors that stay in range under strong decay:
+    a diagonal tile uses its rows' centre c = (max G + min G)/2, a tile below
+    the diagonal the pivot p = G at the last row of its column tile, so that
+    exp(G_i - p) <= 1 and exp(p - G_j) <= 1 when g <= 0. The per-chunk L and
+    Hm of the forward (X = beta K or Q, Y = K) are formed this way on the
+    device."""
+    n = X.shape[0]
+    out = np.zeros((n, n))
+    tiles = [(a, min(a + tile, n)) for a in range(0, n, tile)]
+    for ia, (a0, a1) in enumerate(tiles):
+        for (b0, b1) in tiles[:ia + 1]:
+            if b0 == a0:
+                Ga = G[a0:a1]
+                p = 0.5 * (Ga.max(axis=0) + Ga.min(axis=0))
+            else:
+                p = G[b1 - 1]
+            out[a0:a1, b0:b1] = (np.exp(G[a0:a1] - p) * X[a0:a1]) @ (np.exp(p - G[b0:b1]) * Y[b0:b1]).T
+    return np.tril(out, 0 if incl else -1)
 
 
 def local_wy_flops(n: int, dk: int, dv: int, producer: str) -> tuple[int, int]:

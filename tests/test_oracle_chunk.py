@@ -124,3 +124,79 @@ def test_removed_flops_identity(n, dk, dv):
     f7, _ = cf.local_wy_flops(n, dk, dv, "wy7")
     f3, _ = cf.local_wy_flops(n, dk, dv, "rewy")
     assert f7 - f3 == 4 * n * n * dk + 4 * n ** 3
+
+
+def _strong(gate, T, DK, DV, seed, lo=-5.0):
+    """Inputs whose log decays are drawn uniformly from [lo, 0] (strong decay:
+    a 64-token chunk spans a log-decay range of about 64 |lo| / 2)."""
+    q, k, v, g, beta, h0, dO, dht = _seq(gate, T, DK, DV, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    g = rng.uniform(lo, 0.0, size=g.shape)
+    return q, k, v, g, beta, h0, dO, dht
+
+
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("window", [32, 16, 7])
+def test_windowed_matrix_intra_equals_dense_route(gate, window):
+    args = _seq(gate, 150, 16, 12, seed=71, strong=True)  # 150: a ragged last chunk
+    a = cf.chunk_backward(*args, 64, "rewy", "direct")
+    b = cf.chunk_backward(*args, 64, "rewy", "windowed", window=window)
+    for n in a:
+        assert _rel(b[n], a[n]) < 1e-12, n
+
+
+@pytest.mark.parametrize("producer", ["rewy", "wy7"])
+def test_windowed_reproduces_token_oracle_under_strong_decay(producer):
+    """|g| up to 5 per token: a chunk's range reaches about 160, two windows
+    of 32 tokens about 80 each. The windowed chunk form, in fp64, equals the
+    token recurrence."""
+    q, k, v, g, beta, h0, dO, dht = _strong("vector", 150, 8, 5, seed=81)
+    o_t, ht_t, gr_t = _token(q, k, v, g, beta, h0, dO, dht)
+    gr_c = cf.chunk_backward(q, k, v, g, beta, h0, dO, dht, 64, producer, "windowed")
+    for n in gr_t:
+        assert _rel(gr_c[n], gr_t[n]) < 1e-10, n
+
+
+def test_windowed_factors_stay_within_fp32_range():
+    """Under per-token decays down to exp(-5), every exponent of a windowed
+    factor (32-token windows of a 64-token chunk) and of the per-key scale
+    that turns a diagonal-window operand into a boundary-pivot one is at most
+    80 in magnitude, while the chunk-wide centring of Sec. 3.3 needs factors
+    beyond exp(88), past the largest fp32."""
+    rng = np.random.default_rng(91)
+    worst_win, worst_chunk = 0.0, 0.0
+    for _ in range(50):
+        g = rng.uniform(-5.0, 0.0, size=(64, 128))
+        G = np.cumsum(g, axis=0)
+        c = []
+        for a0 in (0, 32):
+            W = G[a0:a0 + 32]
+            c.append(0.5 * (W.max(0) + W.min(0)))
+            worst_win = max(worst_win, np.abs(W - c[-1]).max())
+        # boundary pivots: rows of window 1 against G[31], columns of window 0
+        # against G[32] -- all exponents <= 0 -- and the operand scales
+        # exp(G[31] - c0), exp(c1 - G[32])
+        assert np.all(G[32:] - G[31] <= 0) and np.all(G[32] - G[:32] <= 0)
+        worst_win = max(worst_win, np.abs(G[31] - c[0]).max(), np.abs(c[1] - G[32]).max())
+        cc = 0.5 * (G.max(0) + G.min(0))
+        worst_chunk = max(worst_chunk, np.abs(G - cc).max())
+    assert worst_win <= 80.0
+    assert worst_chunk > 88.0
+
+
+@pytest.mark.parametrize("n", [64, 45])
+@pytest.mark.parametrize("incl", [True, False])
+def test_pivoted_lower_equals_pairwise_definition(n, incl):
+    """The tile-pivoted product equals its definition entry by entry,
+    sum_f X_if Y_jf exp(G_if - G_jf), each exponent formed per pair, under
+    decays strong enough that exp(-G) alone would leave fp32."""
+    rng = np.random.default_rng(100 + n)
+    X = rng.standard_normal((n, 12))
+    Y = rng.standard_normal((n, 12))
+    G = np.cumsum(rng.uniform(-5.0, 0.0, size=(n, 12)), axis=0)
+    ref = np.zeros((n, n))
+    for i in range(n):
+        for j in range(i + 1 if incl else i):
+            ref[i, j] = np.sum(X[i] * Y[j] * np.exp(G[i] - G[j]))
+    got = cf.pivoted_lower(X, Y, G, incl)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(np.max(np.abs(ref)), 1.0)
