@@ -15,11 +15,18 @@
 //     dk += beta A_K + B_K + Gq^T Q,  dq += Gq K,  dbeta += <k, A_K>,
 //     Gbar += beta <k, A_K> - <k, B_K> + <q, Gq K> - <k, Gq^T Q>
 //   vector gate -- centred matrix intra (Sec. 3.3, "Centered factors"):
-//     alpha = exp(G - c), zeta = exp(c - G), c = (max G + min G)/2;
+//     alpha = exp(G - c), zeta = exp(c - G);
 //     U_q = Hb Y', U_e = D Y', U_y = Hb^T Q' + D^T E'  (Y' = zeta K,
 //     Q' = alpha Q, E' = beta alpha K);
 //     dq += alpha U_q, dk += beta alpha U_e + zeta U_y,
 //     dbeta += <U_e, alpha k>, Gbar += Q' U_q + E' U_e - Y' U_y
+//     applied per 32-token window (the token slab of one contraction): the
+//     products within a window use its centre c = (max G + min G)/2; the
+//     block of window 1's rows against window 0's columns uses a boundary
+//     pivot (G at token 31 for Hb Y' and D Y', at token 32 for Hb^T Q' and
+//     D^T E'), so that both of its factors are at most 1 for decays g <= 0.
+//     The factors then span exp(+-range of 32 tokens / 2) rather than that
+//     of the chunk, which keeps strong decays within fp32 range.
 // Feature-local chain rules for the remaining terms, with gam = exp(G):
 //   dq += gam Qgb;  dk += beta gam Eb_dir + exp(G_n - G) Ktb;
 //   dbeta += <P, v> + <Eb_dir, gam k>   (undivided form, App. B.3)
@@ -198,7 +205,10 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 
     // ---- 0. gates, beta; zero the consumer operand buffers ----
     float Gv[4][4];  // vector gate: G at (tok 16 it + 4 g + e, f)
-    float Gnf, cen = 0.f;
+    // vector gate, key f: window centres and G at tokens 31 and 32
+    // (kept in LDS, read where used: registers are the scarce resource)
+    __shared__ float sWin[VEC ? 4 : 1][DKD];
+    float Gnf;
     if (w == 0) sBeta[l] = to_f32(braw);
     if (VEC) {
         float x[4][4];
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[m][e] = graw[VEC ? 4 * m + e : 0];
-        float base = 0.f, mx = -INFINITY, mn = INFINITY;
+        float base = 0.f, mx[2] = {-INFINITY, -INFINITY}, mn[2] = {INFINITY, INFINITY};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -220,21 +230,35 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 Gv[m][e] = x[m][e] + excl + base;
-                mx = fmaxf(mx, Gv[m][e]);
-                mn = fminf(mn, Gv[m][e]);
+                mx[m >> 1] = fmaxf(mx[m >> 1], Gv[m][e]);
+                mn[m >> 1] = fminf(mn[m >> 1], Gv[m][e]);
             }
             base += pair + p32;
         }
-        // G at the last token (row group 3) to every row group
-        const float pa = partner16(Gv[3][3]);
-        const float b1 = (g & 1) ? Gv[3][3] : pa;
-        const float pb = partner32(b1);
-        Gnf = (g & 2) ? b1 : pb;
-        mx = fmaxf(mx, partner16(mx));
-        mx = fmaxf(mx, partner32(mx));
-        mn = fminf(mn, partner16(mn));
-        mn = fminf(mn, partner32(mn));
-        cen = 0.5f * (mx + mn);
+        // G at tokens 63 and 31 (row group 3) and 32 (row group 0) to every row group
+        {
+            const float pa = partner16(Gv[3][3]);
+            const float b1 = (g & 1) ? Gv[3][3] : pa;
+            const float pb = partner32(b1);
+            Gnf = (g & 2) ? b1 : pb;
+        }
+        if (g == 3) sWin[VEC ? 2 : 0][f] = Gv[1][3];  // G at token 31
+        if (g == 0) sWin[VEC ? 3 : 0][f] = Gv[2][0];  // G at token 32
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float x16 = partner16(mx[h]);
+            mx[h] = fmaxf(mx[h], x16);
+            const float x32 = partner32(mx[h]);
+            mx[h] = fmaxf(mx[h], x32);
+            const float n16 = partner16(mn[h]);
+            mn[h] = fminf(mn[h], n16);
+            const float n32 = partner32(mn[h]);
+            mn[h] = fminf(mn[h], n32);
+        }
+        if (g == 0) {
+            sWin[0][f] = 0.5f * (mx[0] + mn[0]);  // window centres
+            sWin[VEC ? 1 : 0][f] = 0.5f * (mx[1] + mn[1]);
+        }
     } else if (w == 0) {
         sG[l] = wave_incl_scan(graw[0]);
     }
@@ -245,6 +269,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     }
     __syncthreads();
     if (!VEC) Gnf = sG[CH - 1];
+    // vector gate, this lane's key: centre of window 0 / 1, G at tokens 31 / 32
+    auto win = [&](int x) -> float { return VEC ? sWin[VEC ? x : 0][f] : 0.f; };
     // G at this lane's accumulator position (tok 16 m + 4 g + e, f)
     // G and beta at this lane's accumulator rows (tok 16 m + 4 g + e), read
     // once as 16-byte vectors (the scalar gate's G lives in LDS)
@@ -384,12 +410,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             st_half(lE, m * 4 + (w >> 1), w & 1, pack4(cc));
         }
     }
-    // Consumer B operands (this wave's key tile, K = tokens). Vector gate:
-    // the centred factors span exp(+-range/2), and the Gbar terms built from
-    // them cancel to far below their size (the diagonal of Hb enters Q'U_q
-    // and Y'U_y with opposite signs), so Y', Q', E' are carried as bf16
-    // hi + lo pairs; a single bf16 rounding would dominate dg for strong
-    // decays.
+    // Consumer B operands (this wave's key tile, K = tokens; token slab ks is
+    // window ks, centred at its own centre). Vector gate: the centred factors
+    // span exp(+-range/2), and the Gbar terms built from them cancel to far
+    // below their size (the diagonal of Hb enters Q'U_q and Y'U_y with
+    // opposite signs), so Y', Q', E' are carried as bf16 hi + lo pairs; a
+    // single bf16 rounding would dominate dg for strong decays.
     bf16x8 B0[2], B1[2], B2[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -400,7 +426,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
                 const int m = 2 * ks + hh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float d = Gt(m, e) - cen;
+                    const float d = Gt(m, e) - win(ks);
                     const float al = __expf(d), ze = __expf(-d);
                     y[hh][e] = ze * KC[m][e];
                     qq[hh][e] = al * QC[m][e];
@@ -559,7 +585,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         for (int e = 0; e < 4; ++e) {
             const int ks = m >> 1, sl = 4 * (m & 1) + e;
             float kv = (float)B0[ks][sl];
-            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - cen);
+            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - win(ks));
             colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
         }
     }
@@ -593,25 +619,64 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         // lower operands (Gam, Gq: K index <= M index) skip slab 1 for m < 2;
         // upper operands (Gam^T, Gq^T) skip slab 0 for m >= 2
         f32x4 X1 = zero4(), X2 = zero4(), X3 = zero4(), X4 = zero4();
+        // vector gate: the cross-window block, kept apart since its factors
+        // differ (m >= 2: D Y'x, Hb Y'x; m < 2: D^T E'x, Hb^T Q'x)
+        f32x4 Xa = zero4(), Xb = zero4();
+        if constexpr (VEC) {
+            const int wm = m >> 1;  // window of this row tile
+            // cross operands from the window-centred ones by a per-key factor
+            // at most 1 in either case: exp(G31 - c0) = exp(-range0 / 2) and
+            // exp(c1 - G32) = exp(-range1 / 2) for decays. (The hi part alone:
+            // the cancellation that needs the lo part is on the diagonal,
+            // which no cross block holds.)
+            auto rescale = [&](const bf16x8& hi, float sc) -> bf16x8 {
+                float x[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks == 0 || m >= 2) {
-                const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
-                X1 = mfma(a1, B0[ks], X1);  // Gam K    | D Y'
-                X3 = mfma(a3, B0[ks], X3);  // Gq K     | Hb Y'
-                if (VEC) {
-                    const bf16x8 lo = lo_get(0 * 2 + ks);
-                    X1 = mfma(a1, lo, X1);
-                    X3 = mfma(a3, lo, X3);
+                for (int j = 0; j < 8; ++j) x[j] = (float)hi[j] * sc;
+                return pack8(x);
+            };
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 0 || m >= 2) {
+                    const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
+                    if (ks == wm) {
+                        const bf16x8 lo = lo_get(0 * 2 + ks);
+                        X1 = mfma(a1, B0[ks], X1);  // D Y'
+                        X3 = mfma(a3, B0[ks], X3);  // Hb Y'
+                        X1 = mfma(a1, lo, X1);
+                        X3 = mfma(a3, lo, X3);
+                    } else {
+                        const bf16x8 yx = rescale(B0[0], __expf(win(2) - win(0)));
+                        Xa = mfma(a1, yx, Xa);
+                        Xb = mfma(a3, yx, Xb);
+                    }
+                }
+                if (ks == 1 || m < 2) {
+                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
+                    if (ks == wm) {
+                        X2 = mfma(a2, B2[ks], X2);  // D^T E'
+                        X4 = mfma(a4, B1[ks], X4);  // Hb^T Q'
+                        X2 = mfma(a2, lo_get(2 * 2 + ks), X2);
+                        X4 = mfma(a4, lo_get(1 * 2 + ks), X4);
+                    } else {
+                        const float sc = __expf(win(1) - win(3));
+                        Xa = mfma(a2, rescale(B2[1], sc), Xa);
+                        Xb = mfma(a4, rescale(B1[1], sc), Xb);
+                    }
                 }
             }
-            if (ks == 1 || m < 2) {
-                const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
-                X2 = mfma(a2, VEC ? B2[ks] : B0[ks], X2);  // Gam^T bK | D^T E'
-                X4 = mfma(a4, B1[ks], X4);                 // Gq^T Q   | Hb^T Q'
-                if (VEC) {
-                    X2 = mfma(a2, lo_get(2 * 2 + ks), X2);
-                    X4 = mfma(a4, lo_get(1 * 2 + ks), X4);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 0 || m >= 2) {
+                    const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
+                    X1 = mfma(a1, B0[ks], X1);  // Gam K
+                    X3 = mfma(a3, B0[ks], X3);  // Gq K
+                }
+                if (ks == 1 || m < 2) {
+                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
+                    X2 = mfma(a2, B0[ks], X2);  // Gam^T bK
+                    X4 = mfma(a4, B1[ks], X4);  // Gq^T Q
                 }
             }
         }
@@ -627,7 +692,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             float kv = (float)B0[ks][sl], qv = (float)B1[ks][sl];
             float al = 1.f, ze = 1.f;
             if (VEC) {
-                const float d = G - cen;
+                const float d = G - win(ks);  // ks = m >> 1: this row's window
                 al = __expf(d);
                 ze = __expf(-d);
                 kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * al;
@@ -639,11 +704,19 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             br[e] = gam * kv * eb;
             Ga[e] = gam * qv * Qb[e] + bt * gam * kv * eb - kt * kv * Kb[e];
             if (VEC) {
-                const float uq = X3[e], ue = X1[e], uy = X2[e] + X4[e];
-                dq += al * uq;
-                dk += bt * al * ue + ze * uy;
-                br[e] += al * kv * ue;
-                Ga[e] += al * qv * uq + bt * al * kv * ue - ze * kv * uy;
+                // U_q, U_e, U_y with their factors applied
+                float uq = al * X3[e], ue = al * X1[e], uy = ze * (X2[e] + X4[e]);
+                if (m >= 2) {
+                    const float ax = __expf(G - win(2));
+                    uq += ax * Xb[e];
+                    ue += ax * Xa[e];
+                } else {
+                    uy += __expf(win(3) - G) * (Xa[e] + Xb[e]);
+                }
+                dq += uq;
+                dk += bt * ue + uy;
+                br[e] += kv * ue;
+                Ga[e] += qv * uq + bt * kv * ue - kv * uy;
             } else {
                 dq += X3[e];
                 dk += bt * X1[e] + X2[e] + X4[e];

@@ -9,8 +9,13 @@
 //   Kt = exp(G_n - G) * K     Qg = gam * Q       gn = exp(G_n)
 // Scalar gate: E Y^T = beta_i exp(G_i - G_j) (K K^T)_ij, formed from K K^T.
 // Vector gate: the centred factors of Sec. 3.3 ("Centered factors"),
-// alpha = exp(G - c), zeta = exp(c - G) with c = (max G + min G)/2 per key,
-// give E'Y'^T = E Y^T with every factor bounded by exp(range / 2).
+// alpha = exp(G - p), zeta = exp(p - G), give E'Y'^T = E Y^T for any
+// per-key pivot p. Each 16 x 16 tile takes its own: a diagonal tile the
+// centre (max G + min G)/2 of its 16 rows, a tile below the diagonal G at
+// the last row of its column tile (then G_i <= p <= G_j and both factors
+// are at most 1 for decays g <= 0). Every factor then stays within
+// exp(+-range of 16 tokens / 2), so strong per-token decays stay in fp32
+// range where a chunk-wide centre would not.
 //
 // Work split (four waves): wave w owns keys [32 w, 32 w + 32) and values
 // [32 w, 32 w + 32) of every 64 x 128 operand. Transposed operands come from
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 
     constexpr int GSZ = VEC ? CH * DKD : CH;
     __shared__ float sG[GSZ];
-    __shared__ float sCen[DKD];
+    __shared__ float sCen[VEC ? 4 : 1][DKD];  // per 16-row tile: centre of G over its rows
     __shared__ float sBeta[CH];
     // L, then A = (I + L)^{-1} in place: block row i reads its L blocks
     // before a barrier and only then writes its A blocks; a diagonal block
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int f = 32 * w + 16 * u + r;
-            float base = 0.f, mx = -INFINITY, mn = INFINITY;
+            float base = 0.f;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -155,6 +160,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 const float pair = tot + p16;
                 const float p32 = partner32(pair);
                 const float excl = ((g & 1) ? p16 : 0.f) + ((g & 2) ? p32 : 0.f);
+                float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float G = x[u][m][e] + excl + base;
@@ -163,12 +169,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                     mn = fminf(mn, G);
                 }
                 base += pair + p32;
+                // centre of this 16-row tile
+                const float mx16 = partner16(mx);
+                mx = fmaxf(mx, mx16);
+                const float mx32 = partner32(mx);
+                mx = fmaxf(mx, mx32);
+                const float mn16 = partner16(mn);
+                mn = fminf(mn, mn16);
+                const float mn32 = partner32(mn);
+                mn = fminf(mn, mn32);
+                if (g == 0) sCen[VEC ? m : 0][f] = 0.5f * (mx + mn);
             }
-            mx = fmaxf(mx, partner16(mx));
-            mx = fmaxf(mx, partner32(mx));
-            mn = fminf(mn, partner16(mn));
-            mn = fminf(mn, partner32(mn));
-            if (g == 0) sCen[f] = 0.5f * (mx + mn);
         }
     } else if (w == 0) {
         sG[l] = wave_incl_scan(graw);
@@ -201,16 +212,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         if constexpr (STAGE) return kq_chunk(1, i0 + r, 4 * ks + g);
         else return raw_rows(q, i0, ks);
     };
-    auto cook = [&](const R8& raw, int i0, int ks, int kind) -> bf16x8 {
+    // pv: the tile pair's per-key pivot (vector gate)
+    auto cook = [&](const R8& raw, int i0, int ks, int kind, const float* pv) -> bf16x8 {
         if (!VEC || kind == 0) return tobf8(raw);
         float x[8];
         to_f8(raw, x);
         const int i = i0 + r, f0 = 32 * ks + 8 * g;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float d = sG[i * DKD + f0 + e] - sCen[f0 + e];
-            // 1: alpha = exp(G - c) (queries);  2: beta alpha (erase keys);
-            // 3: zeta = exp(c - G) (write keys)
+            const float d = sG[i * DKD + f0 + e] - pv[f0 + e];
+            // 1: alpha = exp(G - p) (queries);  2: beta alpha (erase keys);
+            // 3: zeta = exp(p - G) (write keys)
             x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
         }
         return pack8(x);
@@ -248,14 +260,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             int ti, tj;
             tile_ij(x, ti, tj);
             const R8(&b)[3][4] = buf[u & 1];
+            // vector gate: the centre of a diagonal tile, else G at the last
+            // row of the column tile
+            const float* pv = ti == tj ? sCen[VEC ? ti : 0] : &sG[VEC ? (16 * tj + 15) * DKD : 0];
             f32x4 aL = zero4(), aH = zero4(), aHt = zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 ki = cook(b[0][ks], 16 * ti, ks, 2);  // E' rows (scalar: K)
-                const bf16x8 kj = cook(b[1][ks], 16 * tj, ks, 3);  // Y' rows (scalar: K)
+                const bf16x8 ki = cook(b[0][ks], 16 * ti, ks, 2, pv);  // E' rows (scalar: K)
+                const bf16x8 kj = cook(b[1][ks], 16 * tj, ks, 3, pv);  // Y' rows (scalar: K)
                 aL = mfma(ki, kj, aL);
                 if (needH || needHt) {
-                    const bf16x8 qi = cook(b[2][ks], 16 * ti, ks, 1);  // Q' rows (scalar: Q)
+                    const bf16x8 qi = cook(b[2][ks], 16 * ti, ks, 1, pv);  // Q' rows (scalar: Q)
                     if (needH) aH = mfma(qi, kj, aH);
                     if (needHt) aHt = mfma(kj, qi, aHt);
                 }

@@ -51,10 +51,12 @@
  * where that page requires a multiple of 64, a ragged last chunk is handled
  * here, its missing rows acting as identity steps (g = 0, beta = 0, zero
  * q, k, v, dO), which leaves every output, state and gradient of the real
- * tokens exact; workspaces count whole chunks. Vector-gate inputs whose
- * per-chunk, per-channel cumulative log-decay range exceeds 80 are outside the
- * contract (the centred factors exp(+-range/2) would leave fp32). A
- * launch failure returns GDR_ERR_HIP. gdr_last_error() returns a message for
+ * tokens exact; workspaces count whole chunks. Vector gate: the centred
+ * factors (Sec. 3.3) are formed per window of the chunk, with boundary pivots
+ * between windows, so they span exp(+-range/2) of a 32-token half-chunk; g
+ * must be a log decay (g <= 0) whose per-channel range over each 32-token
+ * half of a chunk is at most 160 (e.g. every |g| <= 5). A launch failure
+ * returns GDR_ERR_HIP. gdr_last_error() returns a message for
  * the calling thread's last failure.
  */
 #ifndef GDR_H

@@ -242,3 +242,40 @@ def test_packed_single_sequence_matches_regular_batch():
         r = tl.run_gpu(x, pol)
         for n in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
             assert np.array_equal(p[n], r[n]), n
+
+
+# ---------------------------------------- strong decay under the vector gate
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_kda_strong_decay_windowed(dtype):
+    """Per-key log decays around -4 per token (log-sigmoid of N(-4, 1)): a
+    64-token chunk spans a range near 256, far past what chunk-wide centred
+    factors can hold in fp32, a 32-token window about 125. Both policies,
+    the seven-product producer, nonzero states and a ragged last chunk."""
+    _need_gpu()
+    x = make_inputs(1, 300, 2, gate="vector", dtype=dtype, seed=31, gate_mean=-4.0,
+                    h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"kda_strong/{dtype}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+    _report(f"kda_strong/{dtype}/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
+
+
+@pytest.mark.gpu
+def test_kda_decay_at_the_window_limit():
+    """Every log decay -5 (a 32-token window spans 155, its factors reach
+    exp(77.5)): the edge of the vector gate's contract."""
+    _need_gpu()
+    x = make_inputs(1, 256, 2, gate="vector", dtype="bf16", seed=32, h0_std=0.1, dht_std=0.1)
+    x["g"] = np.full_like(x["g"], -5.0)
+    _report("kda_limit", tl.compare(tl.run_gpu(x), x))
+
+
+@pytest.mark.gpu
+def test_kda_8192x16_strong_decay_sampled_heads():
+    """Full length and width with log decays around -3 per token."""
+    _need_gpu()
+    x = make_inputs(1, 8192, 16, gate="vector", dtype="bf16", seed=33, gate_mean=-3.0,
+                    h0_std=0.1)
+    gpu = tl.run_gpu(x)
+    _report("kda_8192x16_strong", tl.compare(gpu, x, heads=[(0, 0), (0, 9)]))
