@@ -10,8 +10,9 @@ unbuilt library raises.
     grads = gdr_bwd(q, k, v, g, beta, h0, dO, dht, saved=saved, policy="recompute")
     grads = gdr_bwd_wy7(...)          # seven-product producer (ablation)
 
-Shapes: q, k, v, dO [B,T,H,128]; g [B,T,H] (GDN, scalar gate) or
-[B,T,H,128] (KDA, per-channel gate), fp32; beta [B,T,H]; h0, dht
+Shapes: q, k, v, dO [B,T,H,128]; g [B,T,H] (GDN, scalar gate),
+[B,T,H,128] (KDA, per-channel gate), fp32, or None (DeltaNet: no decay, and
+no dg); beta [B,T,H]; h0, dht
 [B,H,128,128] fp32 (key-major) or None. q, k, v, beta, dO share one dtype,
 bfloat16 or float32. Any T (a ragged last chunk is handled).
 
@@ -32,7 +33,7 @@ _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 _lib = None
 
 RECOMPUTE, FULL_SAVE = 0, 1
-GATE_SCALAR, GATE_VECTOR = 0, 1
+GATE_SCALAR, GATE_VECTOR, GATE_NONE = 0, 1, 2
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
@@ -121,10 +122,11 @@ def make_desc(B, T, H, gate, dtype, DK=128, DV=128, C=64) -> Desc:
 
 
 def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute", n_seq=None):
-    """(saved_bytes, scratch_bytes) for a problem; n_seq: sequences of a packed
-    variable-length batch (B = 1), None for a regular batch."""
-    d = make_desc(B, T, H, GATE_VECTOR if gate == "vector" else GATE_SCALAR,
-                  DT_F32 if dtype == "fp32" else DT_BF16)
+    """(saved_bytes, scratch_bytes) for a problem; gate "scalar", "vector" or
+    "none" (DeltaNet); n_seq: sequences of a packed variable-length batch
+    (B = 1), None for a regular batch."""
+    kind = {"scalar": GATE_SCALAR, "vector": GATE_VECTOR, "none": GATE_NONE}[gate]
+    d = make_desc(B, T, H, kind, DT_F32 if dtype == "fp32" else DT_BF16)
     return _sizes(d, _policy(policy), n_seq)
 
 
@@ -166,7 +168,7 @@ def _ptr(t):
 def _desc_from(q, g):
     torch = _torch()
     B, T, H, DK = q.shape
-    gate = GATE_VECTOR if g.dim() == 4 else GATE_SCALAR
+    gate = GATE_NONE if g is None else GATE_VECTOR if g.dim() == 4 else GATE_SCALAR
     if q.dtype == torch.bfloat16:
         dt = DT_BF16
     elif q.dtype == torch.float32:
@@ -188,7 +190,7 @@ def _validate(q, k, v, g, beta, extra=()):
     for name, t in (("k", k), ("v", v), ("beta", beta)):
         if t.dtype != q.dtype:
             raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
-    if g.dtype != torch.float32:
+    if g is not None and g.dtype != torch.float32:
         raise TypeError("g must be float32")
 
 
@@ -261,13 +263,13 @@ def _bwd(name, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, 
     ns = B if n_seq is None else n_seq
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                   dg=torch.empty_like(g), dbeta=torch.empty_like(beta),
+                   dg=None if g is None else torch.empty_like(g), dbeta=torch.empty_like(beta),
                    dh0=torch.empty((ns, H, 128, 128), dtype=torch.float32, device=q.device)
                    if want_dh0 else None)
     if scratch is None:
         scratch = _scratch(scratch_b, q.device)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(h0), _ptr(dO), _ptr(dht),
-            _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+            _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out.get("dg")),
             _ptr(out["dbeta"]), _ptr(out.get("dh0")), _ptr(scratch), scratch.numel(), _stream())
     if n_seq is None:
         _check(getattr(lib, name)(ctypes.byref(d), pol, *args))

@@ -122,6 +122,11 @@ hipError_t fill_state(float* dst, const float* src, int64_t n, hipStream_t st)
     return hipGetLastError();
 }
 
+hipError_t zero_fill(float* dst, int64_t n, hipStream_t st)
+{
+    return fill_state(dst, nullptr, n, st);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // A packed variable-length batch (on == false: a regular batch).
@@ -147,13 +152,19 @@ size_t table_bytes(const gdr_desc* d, const Packed& pk)
            align_up(4 * (size_t)pk.n);
 }
 
+// DeltaNet (no decay): a zero log-decay array for the kernels and a sink for
+// its gradient, after the sequence tables at the front of scratch.
+bool nogate(const gdr_desc* d) { return d->gate == GDR_GATE_NONE; }
+size_t gate_bytes(const gdr_desc* d) { return align_up(4 * (size_t)(d->B * d->T * d->H)); }
+size_t nogate_bytes(const gdr_desc* d) { return nogate(d) ? 2 * gate_bytes(d) : 0; }
+
 int check_desc(const gdr_desc* d)
 {
     if (!d) return fail(GDR_ERR_INVALID, "descriptor is NULL");
     if (d->B < 0 || d->T < 0 || d->H < 0)
         return fail(GDR_ERR_INVALID, "negative size (B=%lld T=%lld H=%lld)", (long long)d->B,
                     (long long)d->T, (long long)d->H);
-    if (d->gate != GDR_GATE_SCALAR && d->gate != GDR_GATE_VECTOR)
+    if (d->gate != GDR_GATE_SCALAR && d->gate != GDR_GATE_VECTOR && d->gate != GDR_GATE_NONE)
         return fail(GDR_ERR_INVALID, "unknown gate kind %d", d->gate);
     if (d->dtype != GDR_BF16 && d->dtype != GDR_F32)
         return fail(GDR_ERR_INVALID, "unknown dtype %d", d->dtype);
@@ -317,10 +328,14 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     const int esz = d->dtype == GDR_F32 ? 4 : 2;
     REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(dO);
     REQUIRE_PTR(dq); REQUIRE_PTR(dk); REQUIRE_PTR(dv);
-    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(dg, 4); REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
+    if (!nogate(d)) {
+        REQUIRE_PTR_A(g, 4);
+        REQUIRE_PTR_A(dg, 4);
+    }
+    REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(dht, 4); CHECK_ALIGN(dh0, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t tb = table_bytes(d, pk);
+    const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
     Inter it;
     size_t sb = 0, need = 0;
     layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
@@ -332,9 +347,16 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     layout(policy, BWD, (void*)saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
 
     const Shape s = make_shape(d, pk, scratch);
+    hipError_t e = hipSuccess;
+    if (nogate(d)) {
+        float* z = (float*)((char*)scratch + table_bytes(d, pk));
+        g = z;
+        dg = (float*)((char*)z + gate_bytes(d));
+        if ((e = zero_fill(z, d->B * d->T * d->H, st)) != hipSuccess) return hip_fail(e, "zero gate");
+    }
     Inputs in{q, k, v, beta, dO, g, h0, dht};
     Grads gr{dq, dk, dv, dbeta, dg, dh0};
-    hipError_t e = seq_tables(s, pk, st);
+    e = seq_tables(s, pk, st);
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     if (policy == GDR_RECOMPUTE) {
         e = timed(ST_PREP, st, [&] {
@@ -372,10 +394,11 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     }
     const int esz = d->dtype == GDR_F32 ? 4 : 2;
     REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
-    REQUIRE_PTR_A(g, 4); REQUIRE_PTR_A(beta, esz);
+    if (!nogate(d)) REQUIRE_PTR_A(g, 4);
+    REQUIRE_PTR_A(beta, esz);
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
-    const size_t tb = table_bytes(d, pk);
+    const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
     Inter it;
     size_t sb = 0, need = 0;
     layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
@@ -386,8 +409,14 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
     layout(policy, FWD, saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
     const Shape s = make_shape(d, pk, scratch);
+    hipError_t e = hipSuccess;
+    if (nogate(d)) {
+        float* z = (float*)((char*)scratch + table_bytes(d, pk));
+        g = z;
+        if ((e = zero_fill(z, d->B * d->T * d->H, st)) != hipSuccess) return hip_fail(e, "zero gate");
+    }
     Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
-    hipError_t e = seq_tables(s, pk, st);
+    e = seq_tables(s, pk, st);
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     const int what = PREP_FWDSCAN | PREP_OUT |
                      (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A | PREP_AF : 0);
@@ -406,7 +435,7 @@ int workspace(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_byt
     layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, s1, c1);
     layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, s2, c2);
     if (saved_bytes) *saved_bytes = s1;
-    if (scratch_bytes) *scratch_bytes = table_bytes(d, pk) + (c1 > c2 ? c1 : c2);
+    if (scratch_bytes) *scratch_bytes = table_bytes(d, pk) + nogate_bytes(d) + (c1 > c2 ? c1 : c2);
     return GDR_OK;
 }
 

@@ -77,7 +77,12 @@ typedef enum {
     GDR_ERR_HIP = -4          /* a HIP launch failed */
 } gdr_status;
 
-typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_VECTOR = 1 } gdr_gate;
+/* GDR_GATE_NONE: DeltaNet, the recurrence with no decay (g = 0; the pages'
+ * Table 1 lists it beside GDN and KDA). g and dg are neither read nor written
+ * and may be NULL; the workspace holds a zero log-decay array and a sink for
+ * its gradient (8 bytes per token and head), and the scalar-gate kernels run
+ * on them. */
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_VECTOR = 1, GDR_GATE_NONE = 2 } gdr_gate;
 typedef enum { GDR_RECOMPUTE = 0, GDR_FULL_SAVE = 1 } gdr_policy;
 typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 

@@ -54,20 +54,23 @@ def device_inputs(x):
     return d
 
 
-def run_gpu(x, policy="recompute", wy7=False, use_h0=True, use_dht=True):
-    """Forward + backward on the device; returns numpy float64 results."""
+def run_gpu(x, policy="recompute", wy7=False, use_h0=True, use_dht=True, nogate=False):
+    """Forward + backward on the device; returns numpy float64 results.
+    nogate: call with g = None (DeltaNet; x["g"] must then be all zero)."""
     import torch
     import delta_rule_linear_gdr_amd as gdr
     d = device_inputs(x)
     h0 = d["h0"] if use_h0 else None
     dht = d["dht"] if use_dht else None
-    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, policy=policy)
+    g = None if nogate else d["g"]
+    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], g, d["beta"], h0, policy=policy)
     fn = gdr.gdr_bwd_wy7 if wy7 else gdr.gdr_bwd
-    gr = fn(d["q"], d["k"], d["v"], d["g"], d["beta"], h0, d["dO"], dht, saved=saved,
+    gr = fn(d["q"], d["k"], d["v"], g, d["beta"], h0, d["dO"], dht, saved=saved,
             policy=policy)
     torch.cuda.synchronize()
     out = {"o": o, "ht": ht, **gr}
-    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()}
+    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in out.items()
+            if t is not None}
 
 
 def oracle_heads(x, heads=None, threads=None):

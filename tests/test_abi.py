@@ -59,7 +59,7 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(DK=64), -2), (dict(DV=96), -2), (dict(C=32), -2),
-    (dict(gate=5), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
+    (dict(gate=5), -1), (dict(gate=3), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
 ])
 def test_descriptor_validation(kw, status):
     rc, _, _ = _ws(_desc(**kw))
@@ -171,3 +171,21 @@ def test_packed_validation_without_launching():
     P = [None] * 16
     assert lib.gdr_bwd_varlen(ctypes.byref(_desc(B=2)), 0, fake, 1, *P, 0, None) == -1
     assert lib.gdr_bwd_varlen(ctypes.byref(d), 0, None, 1, *P, 0, None) == -1
+
+
+def test_no_gate_workspace_and_null_gate():
+    """DeltaNet (gate kind 2): the scalar-gate workspace plus a zero log-decay
+    array and a sink for its gradient; g may be NULL."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for T, H in ((8192, 16), (100, 3)):
+        for pol in (0, 1):
+            rc, sv, sc = _ws(_desc(T=T, H=H, gate=2), pol)
+            rc2, sv2, sc2 = _ws(_desc(T=T, H=H, gate=0), pol)
+            assert rc == 0 and rc2 == 0
+            assert sv == sv2 and sc == sc2 + 2 * al(4 * T * H)
+    fake = 1 << 20  # never dereferenced: validation fails first
+    d = _desc(gate=2)
+    # g NULL passes validation; the too-small workspace is what fails
+    assert _fwd(d, q=fake, k=fake, v=fake, beta=fake, o=fake, scratch=fake, scratch_bytes=16) == -3
+    assert _fwd(_desc(gate=0), q=fake, k=fake, v=fake, beta=fake, o=fake, scratch=fake,
+                scratch_bytes=16) == -1

@@ -279,3 +279,54 @@ def test_kda_8192x16_strong_decay_sampled_heads():
                     h0_std=0.1)
     gpu = tl.run_gpu(x)
     _report("kda_8192x16_strong", tl.compare(gpu, x, heads=[(0, 0), (0, 9)]))
+
+
+# --------------------------------------------------- DeltaNet (no decay)
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_deltanet_no_gate(dtype):
+    """g = None runs the recurrence without decay (the oracle with g = 0): a
+    ragged last chunk, nonzero states, both policies and the seven-product
+    producer; dg is not produced. Equal, bit for bit, to the scalar-gate call
+    with an all-zero g."""
+    _need_gpu()
+    x = make_inputs(1, 300, 2, gate="scalar", dtype=dtype, seed=41, h0_std=0.1, dht_std=0.1)
+    x["g"] = np.zeros_like(x["g"])
+    for pol in ("recompute", "full_save"):
+        got = tl.run_gpu(x, pol, nogate=True)
+        assert "dg" not in got
+        _report(f"deltanet/{dtype}/{pol}", tl.compare(got, x))
+        ref = tl.run_gpu(x, pol)
+        for n in got:
+            assert np.array_equal(got[n], ref[n]), n
+    _report(f"deltanet/{dtype}/wy7", tl.compare(tl.run_gpu(x, wy7=True, nogate=True), x))
+
+
+@pytest.mark.gpu
+def test_deltanet_packed():
+    """DeltaNet over a packed batch (per-sequence states)."""
+    _need_gpu()
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    x = make_packed_inputs([100, 0, 129, 64], H=2, gate="scalar", seed=42)
+    x["g"] = np.zeros_like(x["g"])
+    d = tl.device_inputs(x)
+    cu = torch.from_numpy(x["cu"]).to("cuda")
+    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], None, d["beta"], d["h0"], cu_seqlens=cu)
+    gr = gdr.gdr_bwd(d["q"], d["k"], d["v"], None, d["beta"], d["h0"], d["dO"], d["dht"],
+                     cu_seqlens=cu)
+    torch.cuda.synchronize()
+    got = {n: t.float().cpu().numpy().astype(np.float64)
+           for n, t in {"o": o, "ht": ht, **gr}.items() if t is not None}
+    ref = tl.oracle_packed(x)
+    for n in ("o", "ht", "dq", "dk", "dv", "dbeta", "dh0"):
+        g_all, r_all = [], []
+        for (i, h), r in ref.items():
+            if n not in r:
+                continue
+            a, b = int(x["cu"][i]), int(x["cu"][i + 1])
+            g_all.append((got[n][i:i + 1, h:h + 1] if n in ("ht", "dh0") else got[n][:, a:b, h:h + 1]).ravel())
+            r_all.append(np.asarray(r[n]).ravel())
+        tl.check(n, np.concatenate(g_all), np.concatenate(r_all))
