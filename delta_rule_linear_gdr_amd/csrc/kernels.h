@@ -169,8 +169,9 @@ hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int wh
                        hipStream_t st);
 // X = Hm^T dO and Y = Qg^T dO from HmT, QgT and dO.
 hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStream_t st);
-// Forward state scan. Writes h and R when set, the output o when o != null
-// and the final state ht when ht != null.
+// Forward state scan (loader-fed; its loader waves also form the output).
+// Writes the output o (required), h and R when it.h is set, and the final
+// state ht when ht != null.
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o,
                            float* ht, hipStream_t st);
 // Reverse state scan (loader-fed). Writes dh and Rb (both required), and dh0

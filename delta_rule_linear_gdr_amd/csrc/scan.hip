@@ -2,9 +2,9 @@
 //
 // ReWY paper (paperpeel.com/paper/2611.01940), Sec. 2.1 and Sec. 3.5: the
 // state scan is serial across chunks and parallel across value columns.
-// One workgroup owns 16 value columns of one head and walks the chunks; its
-// four waves hold the 128 x 16 fp32 state, wave w owning key rows
-// [32 w, 32 w + 32) as two accumulator tiles.
+// One workgroup owns 16 (or 32) value columns of one head and walks the
+// chunks; its four compute waves hold the 128 x 16 fp32 state per value
+// tile, wave w owning key rows [32 w, 32 w + 32) as two accumulator tiles.
 //
 // Both directions run the same two-product step (the chunk system of Sec.
 // 2.3, M R = Z - E S with W = A E and U = A Z, as the onedev.kr summary
@@ -22,9 +22,8 @@
 // per wave) times the Z slabs. The chunk operands arrive pre-swizzled in
 // frag/ctile order (kernels.h); the only on-chip exchange is the state and
 // Z slabs through LDS (one 16-byte write and a few 16-byte reads per lane,
-// two barriers). The forward launch (with the output O) prefetches them
-// three chunks ahead into registers; the backward launches (the pair, and
-// the reverse scan alone) use the loader-fed form further down.
+// two barriers). Every launch uses the loader-fed form below; in the
+// forward launch the loader waves also form the output O.
 // Parallelism is one serial walk ("chain") per (sequence, head, value
 // slice, direction); see chain_of_block for how workgroups map onto chains.
 // Every slice of a head reads the head's whole A1 and A2 (32 KiB per step),
@@ -78,221 +77,10 @@ unsigned scan_grid(const Shape& s, int nvs, int ndir)
     return (unsigned)((s.NS * s.H * ndir + 7) / 8 * 8 * nvs);
 }
 
-template <bool BWD, bool OUT>
-struct Ops {
-    bf16x8 a1[4];     // A1 tiles (mt = w, ks = 0..3)
-    bf16x8 a2[2][2];  // A2 tiles (mt = 2w + m, ks = 0..1)
-    bf16x4 c1;        // C1 ctile (nt = vs, mt = w)
-    bf16x4 c2[2];     // C2 ctiles (nt = vs, mt = 2w + m)      (reverse)
-    float4 gn[2];     // gn for keys 32w + 16m + 4g .. +3
-    bf16x8 qg[4];     // Qg tiles (mt = w, ks = 0..3)          (output)
-    bf16x8 hm[2];     // Hm tiles (mt = w, ks = 0..1)          (output)
-};
-
-template <bool BWD, bool OUT>
-__device__ __forceinline__ void load_ops(Ops<BWD, OUT>& o, const bf16* A1, const bf16* A2,
-                                         const bf16* C1, const bf16* C2, const float* gn,
-                                         const bf16* Qg, const bf16* Hm, int64_t t, int w, int vs)
-{
-    const int g = lane_g();
-    const bf16* a1 = A1 + t * (CH * DKD);
-    const bf16* a2 = A2 + t * (CH * DKD);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) o.a1[ks] = ld_frag(a1, w * 4 + ks);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o.a2[m][ks] = ld_frag(a2, (2 * w + m) * 2 + ks);
-    o.c1 = *(const bf16x4*)ctile_ptr(C1 + t * (CH * DVD), vs * 4 + w);
-    if (BWD) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-            o.c2[m] = *(const bf16x4*)ctile_ptr(C2 + t * (DKD * DVD), vs * 8 + 2 * w + m);
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) o.gn[m] = *(const float4*)(gn + t * DKD + 32 * w + 16 * m + 4 * g);
-    if (OUT) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) o.qg[ks] = ld_frag(Qg + t * (CH * DKD), w * 4 + ks);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) o.hm[ks] = ld_frag(Hm + t * (CH * CH), w * 2 + ks);
-    }
-}
-
-// One workgroup's walk over the chunks of one chain.
-template <bool BWD, bool OUT, bool STORE, typename T>
-__device__ __forceinline__ void scan_body(const Shape& s, const Inputs& in, const Inter& it, T* o,
-                                          float* fin, int block)
-{
-    Chain ch;
-    if (!chain_of_block(s, NVS, 1, BWD, block, ch)) return;
-    const SeqView sq = seq_view(s, ch.n, ch.hd);
-    const int64_t bh = ch.n * s.H + ch.hd;  // state entry
-    const int vs = ch.vs;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int l = lane_id(), r = lane_r(), g = lane_g();
-    const int NT = (int)sq.nchunk;
-    const int v = 16 * vs + r;  // this lane's value column
-
-    __shared__ bf16x8 sS[4][64];  // state slabs: B operands over keys
-    __shared__ bf16x8 sZ[2][64];  // Z slabs: B operands over tokens
-
-    const bf16* A1 = BWD ? it.Kt : it.Wn;
-    const bf16* A2 = BWD ? it.WnT : it.KtT;
-    const bf16* C1 = BWD ? it.X : it.U;
-    const bf16* C2 = it.Y;
-    bf16* Sout = BWD ? it.dh : it.h;
-    bf16* Zout = BWD ? it.Rb : it.R;
-    const float* init = BWD ? in.dht : in.h0;
-
-    f32x4 S[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[m][i] = init ? init[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] : 0.f;
-    auto write_fin = [&]() {
-        if (fin) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    fin[((int64_t)bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + v] = S[m][i];
-        }
-    };
-    if (NT == 0) {  // an empty sequence of a packed batch: nothing to walk
-        write_fin();
-        return;
-    }
-
-    auto chunk = [&](int p) { return BWD ? NT - 1 - p : p; };
-    auto tile = [&](int c) { return seq_tile(s, sq, c); };
-
-    // Stores of a step are issued after the next group of prefetch loads:
-    // loads and stores share one in-order completion counter, so a store
-    // issued ahead of a prefetch would have to be acknowledged before that
-    // prefetch counts as complete.
-    bf16x4 pend_s[2], pend_z;
-    f32x4 pend_o;
-    int64_t pend_t = 0, pend_tok = 0;
-    int pend_rows = CH;  // rows of the pending chunk (a ragged last chunk has fewer)
-    auto flush = [&]() {
-        if (OUT) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (16 * w + 4 * g + i < pend_rows)
-                    io<T>::st(o + (pend_tok + (int64_t)i * s.H) * DVD + v, pend_o[i]);
-        }
-        if (STORE) {
-            // state before the update (h_c, or dh_c = adjoint at the chunk
-            // end) as ctiles (key tile 2w + m, value tile vs); Z likewise
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                *(bf16x4*)ctile_ptr(Sout + pend_t * (DKD * DVD), vs * 8 + 2 * w + m) = pend_s[m];
-            *(bf16x4*)ctile_ptr(Zout + pend_t * (CH * DVD), vs * 4 + w) = pend_z;
-        }
-    };
-    auto step = [&](const Ops<BWD, OUT>& op, int c) {
-        const int64_t t = tile(c);
-        pend_t = t;
-        pend_s[0] = pack4(S[0]);
-        pend_s[1] = pack4(S[1]);
-        sS[w][l] = pack_pi(S[0], S[1]);
-        __syncthreads();
-        bf16x8 sf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) sf[ks] = sS[ks][l];
-        // Z = C1 + A1 S   (rows 16w .. 16w + 15)
-        f32x4 z = unpack4(op.c1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) z = mfma(op.a1[ks], sf[ks], z);
-        f32x4 oacc = zero4();
-        if (OUT) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) oacc = mfma(op.qg[ks], sf[ks], oacc);
-        }
-        pend_z = pack4(z);
-        *(bf16x4*)((bf16*)&sZ[w >> 1][l] + 4 * (w & 1)) = pack4(z);
-        __syncthreads();
-        bf16x8 zf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) zf[ks] = sZ[ks][l];
-        // S <- gn S (+ C2) + A2 Z
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const float gv[4] = {op.gn[m].x, op.gn[m].y, op.gn[m].z, op.gn[m].w};
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gv[i] * S[m][i];
-            if (BWD) {
-                const f32x4 y = unpack4(op.c2[m]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] += y[i];
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mfma(op.a2[m][ks], zf[ks], acc);
-            S[m] = acc;
-        }
-        if (OUT) {
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) oacc = mfma(op.hm[ks], zf[ks], oacc);
-            pend_tok = seq_tok0(s, sq, c) + (int64_t)(16 * w + 4 * g) * s.H;
-            pend_rows = seq_rows(sq, c);
-            pend_o = oacc;
-        }
-    };
-
-    // Three register sets of chunk operands in flight. Every prefetch is
-    // issued unconditionally (past the end it re-reads the last chunk), so
-    // the number of memory operations per step is fixed and the waits on
-    // the vector-memory counter stay exact.
-    // The scheduling barriers pin each group of loads where it is written:
-    // without them the compiler reorders independent loads across the
-    // groups, and the in-order vector-memory counter then makes the first
-    // step of every iteration wait for loads issued just before it.
-    Ops<BWD, OUT> P0, P1, P2;
-    auto load = [&](Ops<BWD, OUT>& op, int p) {
-        __builtin_amdgcn_sched_barrier(0);
-        load_ops<BWD, OUT>(op, A1, A2, C1, C2, it.gn, it.Qg, it.Hm,
-                           tile(chunk(p < NT ? p : NT - 1)), w, vs);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    load(P0, 0);
-    load(P1, 1);
-    load(P2, 2);
-    int p = 0;
-    for (; p + 3 <= NT; p += 3) {
-        step(P0, chunk(p));
-        load(P0, p + 3);
-        flush();
-        step(P1, chunk(p + 1));
-        load(P1, p + 4);
-        flush();
-        step(P2, chunk(p + 2));
-        load(P2, p + 5);
-        flush();
-    }
-    if (p < NT) {
-        step(P0, chunk(p));
-        flush();
-    }
-    if (p + 1 < NT) {
-        step(P1, chunk(p + 1));
-        flush();
-    }
-    write_fin();
-}
-
-template <bool BWD, bool OUT, bool STORE, typename T>
-__global__ __launch_bounds__(256) void scan_kernel(Shape s, Inputs in, Inter it, T* o, float* fin)
-{
-    scan_body<BWD, OUT, STORE, T>(s, in, it, o, fin, blockIdx.x);
-}
-
 // ---------------------------------------------------------------------------
-// Loader-fed form of the reverse scan and of the pair launch. Eight waves
-// per workgroup: waves 0..3 run the step above; waves 4..7 only move each
-// step's operand tiles from global memory into a ring of three LDS slots,
+// Loader-fed form. Eight waves per workgroup: waves 0..3 run the step
+// above; waves 4..7 move each step's operand tiles from global memory into
+// a ring of three LDS slots,
 // two steps ahead, with direct-to-LDS loads (global_load_lds_dwordx4: 64
 // lanes x 16 B = one 1 KiB block per instruction, i.e. one frag tile or two
 // ctiles, copied as is). The compute waves' instruction streams then carry
@@ -383,9 +171,9 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
     }
 }
 
-template <bool BWD, int J, int NV>
+template <bool BWD, int J, int NV, bool OUT, typename T>
 __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, const SeqView& sq, int vs,
-                                           uint8_t* ring)
+                                           uint8_t* ring, bf16x8 (*xs)[64], T* o)
 {
     using L = Fed<NV>;
     constexpr int NL = BWD ? L::NL_BWD : L::NL_FWD;
@@ -395,14 +183,87 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
         const int c = BWD ? NT - 1 - pc : pc;
         fed_issue<BWD, J, NV>(it, seq_tile(s, sq, c), vs, ring + (p % L::NSLOT) * L::SLOT);
     };
-    issue(0);
-    issue(1);
-    wait_vm<NL>();  // step 0 has landed
-    for (int p = 0; p < NT; ++p) {
-        bar();  // first barrier of step p: slot (p + 2) % 3 is free
-        issue(p + 2);
-        bar();  // second barrier of step p
-        wait_vm<NL>();  // step p + 1 has landed
+    if constexpr (!OUT) {
+        issue(0);
+        issue(1);
+        wait_vm<NL>();  // step 0 has landed
+        for (int p = 0; p < NT; ++p) {
+            bar();  // first barrier of step p: slot (p + 2) % 3 is free
+            issue(p + 2);
+            bar();  // second barrier of step p
+            wait_vm<NL>();  // step p + 1 has landed
+        }
+    } else {
+        // Forward with output: this wave also forms output rows 16 J .. 16 J + 15
+        // of every chunk, O = Qg S + Hm Z, from the state and Z slabs the compute
+        // waves leave in the LDS exchange (S between the step's two barriers, Z
+        // after the second). Its Qg / Hm fragments are read two steps ahead into
+        // three rotating register sets, each step's just before that step's
+        // ring blocks, so that the wait closing a step -- for the next step's
+        // ring blocks -- also covers the fragments the next step uses, and no
+        // wait ever has to cover younger ring blocks.
+        constexpr int NQ = 6;   // Qg / Hm fragment reads per step
+        constexpr int NO = NV;  // output row stores per step (one per value tile)
+        bf16x8 (*sS)[4][64] = (bf16x8 (*)[4][64])xs;
+        bf16x8 (*sZ)[2][64] = (bf16x8 (*)[2][64])(xs + 4 * NV);
+        const int l = lane_id(), r = lane_r(), g = lane_g();
+        const bf16x8 Ip0 = ident_pi(0);
+        struct QH {
+            bf16x8 qg[4], hm[2];
+        };
+        auto ldo = [&](QH& x, int p) {
+            const int64_t t = seq_tile(s, sq, p < NT ? p : NT - 1);  // past the end: the last chunk again
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) x.qg[ks] = ld_frag(it.Qg + t * (CH * DKD), J * 4 + ks);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) x.hm[ks] = ld_frag(it.Hm + t * (CH * CH), J * 2 + ks);
+        };
+        auto step = [&](const QH& cur, QH& ahead, int p) {
+            bar();  // first barrier of step p: the state slabs hold S_p; slot (p + 2) % 3 is free
+            ldo(ahead, p + 2);
+            issue(p + 2);
+            f32x4 acc[NV];
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                acc[u] = zero4();
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc[u] = mfma(cur.qg[ks], sS[u][ks][l], acc[u]);
+            }
+            wait_lgkm0();  // S read before the compute waves replace it
+            bar();         // second barrier of step p: the Z slabs hold Z_p
+#pragma unroll
+            for (int u = 0; u < NV; ++u)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) acc[u] = mfma(cur.hm[ks], sZ[u][ks][l], acc[u]);
+            wait_lgkm0();  // Z read before the compute waves replace it
+            // rows: lane (r, g) gets row 16 J + r, values 16 vt + 4 g .. + 3
+            const int row = 16 * J + r;
+            T* orow = o + (seq_tok0(s, sq, p) + (int64_t)row * s.H) * DVD;
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const f32x4 x = mfma(pack_pi(acc[u], zero4()), Ip0, zero4());
+                float xv[4] = {x[0], x[1], x[2], x[3]};
+                if (row < seq_rows(sq, p)) store4(orow + 16 * (NV * vs + u) + 4 * g, xv);
+            }
+            // step p + 1's ring blocks and fragments have landed: younger than
+            // them are this step's fragment reads, ring blocks and stores (the
+            // previous step's stores are waited for too, at worst a little early)
+            wait_vm<NL + NQ + NO>();
+        };
+        QH qa, qb, qc;
+        ldo(qa, 0);
+        issue(0);
+        ldo(qb, 1);
+        issue(1);
+        wait_vm<NL + NQ>();  // step 0's fragments and ring blocks have landed
+        int p = 0;
+        for (; p + 3 <= NT; p += 3) {
+            step(qa, qc, p);
+            step(qb, qa, p + 1);
+            step(qc, qb, p + 2);
+        }
+        if (p < NT) step(qa, qc, p);
+        if (p + 1 < NT) step(qb, qa, p + 1);
     }
     // no LDS write may still be in flight when the workgroup's LDS is released
     wait_vm<0>();
@@ -421,8 +282,9 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
     bf16x8 (*sS)[4][64] = (bf16x8 (*)[4][64])xs;           // [NV][4][64]
     bf16x8 (*sZ)[2][64] = (bf16x8 (*)[2][64])(xs + 4 * NV);  // [NV][2][64]
 
-    bf16* Sout = BWD ? it.dh : it.h;
+    bf16* Sout = BWD ? it.dh : it.h;  // null: not stored (the forward without a backward)
     bf16* Zout = BWD ? it.Rb : it.R;
+    const bool store = Sout != nullptr;
     const float* init = BWD ? in.dht : in.h0;
 
     // state: value tile NV vs + u, key rows 32 w + 16 m + 4 g + i, column 16 (NV vs + u) + r
@@ -443,9 +305,11 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile NV vs + u)
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
+            if (store) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-                *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m) = pack4(S[u][m]);
+                for (int m = 0; m < 2; ++m)
+                    *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m) = pack4(S[u][m]);
+            }
             sS[u][w][l] = pack_pi(S[u][0], S[u][1]);
         }
         wait_lgkm0();
@@ -469,9 +333,11 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         }
         wait_lgkm0();
         bar();
+        if (store) {
 #pragma unroll
-        for (int u = 0; u < NV; ++u)
-            *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w) = z4[u];
+            for (int u = 0; u < NV; ++u)
+                *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w) = z4[u];
+        }
         bf16x8 zf[NV][2], a2[2][2];
 #pragma unroll
         for (int u = 0; u < NV; ++u)
@@ -512,35 +378,41 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
     }
 }
 
-template <bool BWD, int NV>
+template <bool BWD, int NV, bool OUT, typename T>
 __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const Inter& it, float* fin,
-                                         const Chain& ch, uint8_t* ring, bf16x8 (*xs)[64])
+                                         const Chain& ch, uint8_t* ring, bf16x8 (*xs)[64], T* o)
 {
     const SeqView sq = seq_view(s, ch.n, ch.hd);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (sq.nchunk == 0 && w >= 4) return;  // an empty sequence: no steps, no barriers
     switch (w) {
-    case 4: fed_loader<BWD, 0, NV>(s, it, sq, ch.vs, ring); break;
-    case 5: fed_loader<BWD, 1, NV>(s, it, sq, ch.vs, ring); break;
-    case 6: fed_loader<BWD, 2, NV>(s, it, sq, ch.vs, ring); break;
-    case 7: fed_loader<BWD, 3, NV>(s, it, sq, ch.vs, ring); break;
+    case 4: fed_loader<BWD, 0, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
+    case 5: fed_loader<BWD, 1, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
+    case 6: fed_loader<BWD, 2, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
+    case 7: fed_loader<BWD, 3, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
     default: fed_compute<BWD, NV>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs); break;
     }
 }
 
-// ndir = 2: forward and reverse chains side by side (the reverse scan reads
-// only prep's operands, not the forward states); ndir = 1: the reverse scan
-// alone. Only the reverse chains write dh0.
-template <int NV>
-__global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* dh0, int ndir)
+// Backward launches (OUT = false): ndir = 2 runs forward and reverse chains
+// side by side (the reverse scan reads only prep's operands, not the
+// forward states); ndir = 1 the reverse scan alone. Only the reverse chains
+// write fin (dh0). The forward launch (OUT = true, ndir = 1) writes the
+// output o and fin (ht), and h and R when it.h is set.
+template <int NV, bool OUT, typename T>
+__global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* fin, int ndir, T* o)
 {
     using L = Fed<NV>;
     __shared__ __attribute__((aligned(16))) uint8_t ring[L::NSLOT * L::SLOT];
     __shared__ bf16x8 xs[L::XCH][64];
     Chain ch;
-    if (!chain_of_block(s, NVS / NV, ndir, true, blockIdx.x, ch)) return;
-    if (ch.bwd) fed_body<true, NV>(s, in, it, dh0, ch, ring, xs);
-    else fed_body<false, NV>(s, in, it, nullptr, ch, ring, xs);
+    if (!chain_of_block(s, NVS / NV, ndir, !OUT, blockIdx.x, ch)) return;
+    if constexpr (OUT) {
+        fed_body<false, NV, true, T>(s, in, it, fin, ch, ring, xs, o);
+    } else {
+        if (ch.bwd) fed_body<true, NV, false, T>(s, in, it, fin, ch, ring, xs, o);
+        else fed_body<false, NV, false, T>(s, in, it, nullptr, ch, ring, xs, o);
+    }
 }
 
 // Compute units of the current device (cached per device).
@@ -562,13 +434,25 @@ int cu_count()
 
 // One workgroup per CU fits (LDS); NV = 2 when NV = 1 would need more than
 // one round of workgroups.
+bool wide(const Shape& s, int ndir) { return s.NS * s.H * NVS * ndir > cu_count(); }
+
 hipError_t launch_fed(const Shape& s, const Inputs& in, const Inter& it, float* dh0, int ndir,
                       hipStream_t st)
 {
-    if (s.NS * s.H * NVS * ndir > cu_count())
-        scan_fed_kernel<2><<<scan_grid(s, NVS / 2, ndir), 512, 0, st>>>(s, in, it, dh0, ndir);
+    if (wide(s, ndir))
+        scan_fed_kernel<2, false, bf16><<<scan_grid(s, NVS / 2, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
     else
-        scan_fed_kernel<1><<<scan_grid(s, NVS, ndir), 512, 0, st>>>(s, in, it, dh0, ndir);
+        scan_fed_kernel<1, false, bf16><<<scan_grid(s, NVS, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fed_out(const Shape& s, const Inputs& in, const Inter& it, T* o, float* ht, hipStream_t st)
+{
+    if (wide(s, 1))
+        scan_fed_kernel<2, true, T><<<scan_grid(s, NVS / 2, 1), 512, 0, st>>>(s, in, it, ht, 1, o);
+    else
+        scan_fed_kernel<1, true, T><<<scan_grid(s, NVS, 1), 512, 0, st>>>(s, in, it, ht, 1, o);
     return hipGetLastError();
 }
 
@@ -577,20 +461,8 @@ hipError_t launch_fed(const Shape& s, const Inputs& in, const Inter& it, float* 
 hipError_t launch_scan_fwd(const Shape& s, const Inputs& in, const Inter& it, void* o, float* ht,
                            hipStream_t st)
 {
-    const unsigned nblk = scan_grid(s, NVS, 1);
-    const bool store = it.h != nullptr;
-    if (o) {
-        if (s.f32) {
-            if (store) scan_kernel<false, true, true, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
-            else scan_kernel<false, true, false, float><<<nblk, 256, 0, st>>>(s, in, it, (float*)o, ht);
-        } else {
-            if (store) scan_kernel<false, true, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
-            else scan_kernel<false, true, false, bf16><<<nblk, 256, 0, st>>>(s, in, it, (bf16*)o, ht);
-        }
-    } else {
-        scan_kernel<false, false, true, bf16><<<nblk, 256, 0, st>>>(s, in, it, nullptr, ht);
-    }
-    return hipGetLastError();
+    if (!o) return hipErrorInvalidValue;
+    return s.f32 ? launch_fed_out(s, in, it, (float*)o, ht, st) : launch_fed_out(s, in, it, (bf16*)o, ht, st);
 }
 
 hipError_t launch_scan_bwd(const Shape& s, const Inputs& in, const Inter& it, float* dh0,
