@@ -13,7 +13,8 @@ Prints one JSON line. Besides the headline value it reports the per-stage
 durations (HIP events recorded by the library on the launch stream over a
 second timed pass), the roofline of the dominant kernel, the whole-path
 roofline, the forward, the full-save policy, the seven-product ablation, the
-KDA backward at the same shape, and the fp64 CPU oracle on the same workload.
+KDA backward at the same shape (and the KDA forward + backward end to end),
+and the fp64 CPU oracle on the same workload.
 
 --profile-pass runs a known-size elementwise copy and a few headline steps
 only; it is the command the hardware-counter summaries under profiles/ are
@@ -316,7 +317,19 @@ def main():
         detail["kda_bwd_R_tokens_per_s"] = round(B * T / (msK * 1e-3), 1)
         detail["kda_path_frac_hbm"] = round(kpath / (msK * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         detail["kda_stage_ms"] = {k: round(v, 4) for k, v in profiled(runK, args.steps).items()}
-        del dk_, xk
+        # the same workload end to end: recompute forward (output and final
+        # state) followed by the recompute backward, one step per call pair
+        _, scK = gdr.workspace_size(B, T, H, "vector", "bf16", "recompute")
+        scrK = torch.empty(scK, dtype=torch.uint8, device=dev)
+
+        def runKFB():
+            gdr.gdr_fwd(dk_["q"], dk_["k"], dk_["v"], dk_["g"], dk_["beta"], dk_["h0"],
+                        policy="recompute", scratch=scrK)
+            runK()
+        msKFB = time_steps(runKFB, args.steps, args.warmup)
+        detail["kda_fwd_bwd_R_ms"] = round(msKFB, 4)
+        detail["kda_fwd_bwd_R_tokens_per_s"] = round(B * T / (msKFB * 1e-3), 1)
+        del dk_, xk, scrK
         if not args.no_sweep:
             detail["shape_sweep"] = shape_sweep(gdr, to_dev, make_runner, time_steps, args)
 

@@ -10,11 +10,11 @@ unbuilt library raises.
     grads = gdr_bwd(q, k, v, g, beta, h0, dO, dht, saved=saved, policy="recompute")
     grads = gdr_bwd_wy7(...)          # seven-product producer (ablation)
 
-Shapes: q, k, v, dO [B,T,H,128]; g [B,T,H] (GDN, scalar gate),
-[B,T,H,128] (KDA, per-channel gate), fp32, or None (DeltaNet: no decay, and
-no dg); beta [B,T,H]; h0, dht
-[B,H,128,128] fp32 (key-major) or None. q, k, v, beta, dO share one dtype,
-bfloat16 or float32. Any T (a ragged last chunk is handled).
+Shapes: q, k [B,T,H,DK]; v, dO [B,T,H,DV]; g [B,T,H] (GDN, scalar gate),
+[B,T,H,DK] (KDA, per-channel gate), fp32, or None (DeltaNet: no decay, and
+no dg); beta [B,T,H]; h0, dht [B,H,DK,DV] fp32 (key-major) or None.
+DK, DV <= 128 (below 128 through zero-padded copies). q, k, v, beta, dO
+share one dtype, bfloat16 or float32. Any T (a ragged last chunk is handled).
 
 Packed variable-length batches: pass ``cu_seqlens`` (int64 device tensor of
 n_seq + 1 token offsets) with batch size 1; the states h0, ht, dht, dh0 are
@@ -121,12 +121,13 @@ def make_desc(B, T, H, gate, dtype, DK=128, DV=128, C=64) -> Desc:
     return Desc(B, T, H, DK, DV, C, gate, dtype)
 
 
-def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute", n_seq=None):
+def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute", n_seq=None,
+                   DK=128, DV=128):
     """(saved_bytes, scratch_bytes) for a problem; gate "scalar", "vector" or
     "none" (DeltaNet); n_seq: sequences of a packed variable-length batch
     (B = 1), None for a regular batch."""
     kind = {"scalar": GATE_SCALAR, "vector": GATE_VECTOR, "none": GATE_NONE}[gate]
-    d = make_desc(B, T, H, kind, DT_F32 if dtype == "fp32" else DT_BF16)
+    d = make_desc(B, T, H, kind, DT_F32 if dtype == "fp32" else DT_BF16, DK=DK, DV=DV)
     return _sizes(d, _policy(policy), n_seq)
 
 
@@ -165,9 +166,10 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _desc_from(q, g):
+def _desc_from(q, g, v):
     torch = _torch()
     B, T, H, DK = q.shape
+    DV = v.shape[-1]
     gate = GATE_NONE if g is None else GATE_VECTOR if g.dim() == 4 else GATE_SCALAR
     if q.dtype == torch.bfloat16:
         dt = DT_BF16
@@ -175,7 +177,7 @@ def _desc_from(q, g):
         dt = DT_F32
     else:
         raise TypeError(f"q dtype {q.dtype}: expected bfloat16 or float32")
-    return make_desc(B, T, H, gate, dt, DK=DK)
+    return make_desc(B, T, H, gate, dt, DK=DK, DV=DV)
 
 
 def _validate(q, k, v, g, beta, extra=()):
@@ -227,7 +229,7 @@ def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch
     with its own state: h0 and ht are then [n_seq, H, 128, 128]."""
     torch = _torch()
     _validate(q, k, v, g, beta, (("h0", h0),))
-    d = _desc_from(q, g)
+    d = _desc_from(q, g, v)
     pol = _policy(policy)
     n_seq = _seqs(cu_seqlens, q)
     lib = load()
@@ -235,7 +237,8 @@ def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch
     B, T, H, _ = q.shape
     ns = B if n_seq is None else n_seq
     o = torch.empty_like(v)
-    ht = torch.empty((ns, H, 128, 128), dtype=torch.float32, device=q.device) if want_ht else None
+    ht = torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+                     device=q.device) if want_ht else None
     saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None
     if scratch is None:
         scratch = _scratch(scratch_b, q.device)
@@ -254,7 +257,7 @@ def _bwd(name, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, 
     _validate(q, k, v, g, beta, (("h0", h0), ("dO", dO), ("dht", dht)))
     if dO.dtype != q.dtype:
         raise TypeError("dO dtype differs from q dtype")
-    d = _desc_from(q, g)
+    d = _desc_from(q, g, v)
     pol = _policy(policy)
     n_seq = _seqs(cu_seqlens, q)
     lib = load()
@@ -264,7 +267,8 @@ def _bwd(name, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, 
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                    dg=None if g is None else torch.empty_like(g), dbeta=torch.empty_like(beta),
-                   dh0=torch.empty((ns, H, 128, 128), dtype=torch.float32, device=q.device)
+                   dh0=torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+                                   device=q.device)
                    if want_dh0 else None)
     if scratch is None:
         scratch = _scratch(scratch_b, q.device)

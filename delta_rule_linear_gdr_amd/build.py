@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.hip", "prep.hip", "scan.hip", "bwd_local.hip", "seqtab.hip"]
+SOURCES = ["gdr_api.hip", "prep.hip", "scan.hip", "bwd_local.hip", "seqtab.hip", "pad.hip"]
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 

@@ -168,8 +168,10 @@ int check_desc(const gdr_desc* d)
         return fail(GDR_ERR_INVALID, "unknown gate kind %d", d->gate);
     if (d->dtype != GDR_BF16 && d->dtype != GDR_F32)
         return fail(GDR_ERR_INVALID, "unknown dtype %d", d->dtype);
-    if (d->DK != DKD || d->DV != DVD)
-        return fail(GDR_ERR_UNSUPPORTED, "key/value width %lld/%lld: only 128/128 is supported",
+    if (d->DK < 1 || d->DV < 1)
+        return fail(GDR_ERR_INVALID, "key/value width %lld/%lld", (long long)d->DK, (long long)d->DV);
+    if (d->DK > DKD || d->DV > DVD)
+        return fail(GDR_ERR_UNSUPPORTED, "key/value width %lld/%lld: at most 128/128 is supported",
                     (long long)d->DK, (long long)d->DV);
     if (d->C != CH)
         return fail(GDR_ERR_UNSUPPORTED, "chunk length %lld: only 64 is supported", (long long)d->C);
@@ -264,10 +266,10 @@ int hip_fail(hipError_t e, const char* what)
 
 // ---- optional per-stage timing (gdr_profile_begin / gdr_profile_end) ----
 enum Stage {
-    ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_SCAN_PAIR, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, NSTAGE
+    ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_SCAN_PAIR, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, ST_PAD, NSTAGE
 };
 const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "xy", "scan_bwd", "scan_pair",
-                                        "bwd_local", "bwd_local_wy7"};
+                                        "bwd_local", "bwd_local_wy7", "pad"};
 
 struct Profiler {
     std::mutex mu;
@@ -439,6 +441,191 @@ int workspace(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_byt
     return GDR_OK;
 }
 
+// ---- key / value widths below 128: the 128-wide path on zero-padded copies ----
+bool padded(const gdr_desc* d) { return d->DK != DKD || d->DV != DVD; }
+gdr_desc inner_desc(const gdr_desc* d)
+{
+    gdr_desc e = *d;
+    e.DK = DKD;
+    e.DV = DVD;
+    return e;
+}
+
+// The padded copies at the front of scratch (base null: sizes only).
+struct PadBufs {
+    void *q, *k, *v, *t4, *dq, *dk, *dv;  // token tensors, 128 wide (t4: o forward, dO backward)
+    float *g, *dg;                          // vector gate and its gradient, 128 wide
+    float *s0, *s1, *s2;                    // states: h0, ht or dht, dh0
+    size_t bytes;
+};
+PadBufs pad_layout(const gdr_desc* d, const Packed& pk, void* base)
+{
+    PadBufs p;
+    memset(&p, 0, sizeof p);
+    if (!padded(d)) return p;
+    const size_t rows = (size_t)(d->B * d->T * d->H), esz = d->dtype == GDR_F32 ? 4 : 2;
+    const size_t nst = (size_t)((pk.on ? pk.n : d->B) * d->H);
+    char* b = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t n) -> void* {
+        void* r = b ? b + off : nullptr;
+        off += align_up(n);
+        return r;
+    };
+    p.q = take(rows * DKD * esz);
+    p.k = take(rows * DKD * esz);
+    p.v = take(rows * DVD * esz);
+    p.t4 = take(rows * DVD * esz);
+    p.dq = take(rows * DKD * esz);
+    p.dk = take(rows * DKD * esz);
+    p.dv = take(rows * DVD * esz);
+    if (d->gate == GDR_GATE_VECTOR) {
+        p.g = (float*)take(rows * DKD * 4);
+        p.dg = (float*)take(rows * DKD * 4);
+    }
+    p.s0 = (float*)take(nst * DKD * DVD * 4);
+    p.s1 = (float*)take(nst * DKD * DVD * 4);
+    p.s2 = (float*)take(nst * DKD * DVD * 4);
+    p.bytes = off;
+    return p;
+}
+
+int workspace_any(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_bytes, size_t* scratch_bytes)
+{
+    if (!padded(d)) return workspace(d, pk, policy, saved_bytes, scratch_bytes);
+    const gdr_desc e = inner_desc(d);
+    size_t sv = 0, sc = 0;
+    workspace(&e, pk, policy, &sv, &sc);
+    if (saved_bytes) *saved_bytes = sv;
+    if (scratch_bytes) *scratch_bytes = pad_layout(d, pk, nullptr).bytes + sc;
+    return GDR_OK;
+}
+
+// Shared checks of the padded calls; returns GDR_OK and fills pb, or a status.
+int pad_prologue(const gdr_desc* d, const Packed& pk, int policy, void* scratch, size_t scratch_bytes,
+                 PadBufs& pb)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    if (pk.on && (rc = check_packed(d, pk))) return rc;
+    size_t sc = 0;
+    workspace_any(d, pk, policy, nullptr, &sc);
+    if (!scratch || scratch_bytes < sc)
+        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", sc,
+                    scratch ? scratch_bytes : (size_t)0);
+    if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
+    pb = pad_layout(d, pk, scratch);
+    return GDR_OK;
+}
+
+#define PAD_LAUNCH(expr)                                                   \
+    do {                                                                   \
+        hipError_t pe = timed(ST_PAD, st, [&] { return (expr); });         \
+        if (pe != hipSuccess) return hip_fail(pe, "pad");                  \
+    } while (0)
+
+int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
+                   const void* v, const float* g, const void* beta, const float* h0, void* o, float* ht,
+                   void* saved, void* scratch, size_t scratch_bytes, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    if (pk.on && (rc = check_packed(d, pk))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nseq = pk.on ? pk.n : d->B;
+    if (nseq * d->H == 0) return GDR_OK;
+    if (d->T == 0) {
+        hipError_t e = fill_state(ht, h0, nseq * d->H * d->DK * d->DV, st);
+        return e == hipSuccess ? GDR_OK : hip_fail(e, "ht copy");
+    }
+    if (!q || !k || !v || !o || !beta || (!g && !nogate(d)))
+        return fail(GDR_ERR_INVALID, "a required pointer is NULL");
+    PadBufs pb;
+    if ((rc = pad_prologue(d, pk, policy, scratch, scratch_bytes, pb))) return rc;
+    const gdr_desc e = inner_desc(d);
+    const int64_t rows = d->B * d->T * d->H;
+    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, dv = (int)d->DV;
+    const bool vec = d->gate == GDR_GATE_VECTOR;
+    PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
+    PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
+    PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st));
+    if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
+    if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nseq * d->H, dk, dv, st));
+    rc = run_fwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
+                 ht ? pb.s1 : nullptr, saved, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream);
+    if (rc) return rc;
+    PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st));
+    if (ht) PAD_LAUNCH(launch_unpad_state(ht, pb.s1, nseq * d->H, dk, dv, st));
+    return GDR_OK;
+}
+
+int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
+                   const void* v, const float* g, const void* beta, const float* h0, const void* dO,
+                   const float* dht, const void* saved, void* dq, void* dk_, void* dv_, float* dg,
+                   void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    if (pk.on && (rc = check_packed(d, pk))) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nseq = pk.on ? pk.n : d->B;
+    if (nseq * d->H == 0) return GDR_OK;
+    if (d->T == 0) {
+        hipError_t e = fill_state(dh0, dht, nseq * d->H * d->DK * d->DV, st);
+        return e == hipSuccess ? GDR_OK : hip_fail(e, "dh0 copy");
+    }
+    if (!q || !k || !v || !dO || !dq || !dk_ || !dv_ || !beta || !dbeta || (!nogate(d) && (!g || !dg)))
+        return fail(GDR_ERR_INVALID, "a required pointer is NULL");
+    PadBufs pb;
+    if ((rc = pad_prologue(d, pk, policy, scratch, scratch_bytes, pb))) return rc;
+    const gdr_desc e = inner_desc(d);
+    const int64_t rows = d->B * d->T * d->H;
+    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, dv = (int)d->DV;
+    const bool vec = d->gate == GDR_GATE_VECTOR;
+    PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
+    PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
+    PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st));
+    PAD_LAUNCH(launch_pad_rows(pb.t4, dO, rows, dv, esz, st));
+    if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
+    if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nseq * d->H, dk, dv, st));
+    if (dht) PAD_LAUNCH(launch_pad_state(pb.s1, dht, nseq * d->H, dk, dv, st));
+    rc = run_bwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
+                 dht ? pb.s1 : nullptr, saved, pb.dq, pb.dk, pb.dv, vec ? pb.dg : dg, dbeta,
+                 dh0 ? pb.s2 : nullptr, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream, wy7);
+    if (rc) return rc;
+    PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st));
+    PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st));
+    PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st));
+    if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st));
+    if (dh0) PAD_LAUNCH(launch_unpad_state(dh0, pb.s2, nseq * d->H, dk, dv, st));
+    return GDR_OK;
+}
+#undef PAD_LAUNCH
+
+// Entry dispatch: the padded path for widths below 128.
+int any_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
+            void* scratch, size_t scratch_bytes, void* stream)
+{
+    if (d && padded(d))
+        return run_fwd_padded(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
+    return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
+}
+int any_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k, const void* v,
+            const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
+            const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
+            void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+{
+    if (d && padded(d))
+        return run_bwd_padded(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
+                              scratch, scratch_bytes, stream, wy7);
+    return run_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0, scratch,
+                   scratch_bytes, stream, wy7);
+}
+
 }  // namespace
 }  // namespace gdr
 
@@ -451,14 +638,14 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
     int rc = check_desc(d);
     if (rc) return rc;
     if ((rc = check_policy(policy))) return rc;
-    return workspace(d, Packed{}, policy, saved_bytes, scratch_bytes);
+    return workspace_any(d, Packed{}, policy, saved_bytes, scratch_bytes);
 }
 
 int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
             void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_fwd(d, Packed{}, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes,
+    return any_fwd(d, Packed{}, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes,
                    stream);
 }
 
@@ -471,7 +658,7 @@ int gdr_fwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int
     pk.on = true;
     pk.cu = cu_seqlens;
     pk.n = n_seq;
-    return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
+    return any_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
 }
 
 int gdr_workspace_size_varlen(const gdr_desc* d, int64_t n_seq, int policy, size_t* saved_bytes,
@@ -484,14 +671,14 @@ int gdr_workspace_size_varlen(const gdr_desc* d, int64_t n_seq, int policy, size
     Packed pk;
     pk.on = true;
     pk.n = n_seq;
-    return workspace(d, pk, policy, saved_bytes, scratch_bytes);
+    return workspace_any(d, pk, policy, saved_bytes, scratch_bytes);
 }
 int gdr_bwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
             const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
             void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+    return any_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
                    dh0, scratch, scratch_bytes, stream, false);
 }
 
@@ -505,7 +692,7 @@ int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int
     pk.on = true;
     pk.cu = cu_seqlens;
     pk.n = n_seq;
-    return run_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
+    return any_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
                    scratch, scratch_bytes, stream, false);
 }
 
@@ -514,7 +701,7 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream)
 {
-    return run_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+    return any_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
                    dh0, scratch, scratch_bytes, stream, true);
 }
 

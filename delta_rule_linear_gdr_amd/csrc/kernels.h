@@ -187,6 +187,12 @@ hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, f
 // into s.cu and fills s.stab, s.ctab and s.order (one workgroup).
 hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, int2* stab, int2* ctab,
                              int* order, hipStream_t st);
+// Widths below 128 (pad.hip): rows of width w <-> rows of width 128 (zeros
+// past w), esz = element bytes; states [n][dk][dv] <-> [n][128][128].
+hipError_t launch_pad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st);
+hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st);
+hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
+hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st);

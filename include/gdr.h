@@ -42,12 +42,20 @@
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream);
  * the library never synchronizes. Concurrent calls must not share `scratch`.
  *
+ * Widths: the kernels are built for key and value width 128 (the
+ * flashserve/ReWY repository page, "Compatibility": K = V = 128, 64-token
+ * chunks). Narrower widths (1 <= DK, DV <= 128; the pages' extended tests
+ * use 80/112 and 96/80) run exactly on the same kernels through zero-padded
+ * copies in the workspace -- zero key features leave the recurrence
+ * unchanged and zero value columns only add zero columns -- at the cost of
+ * the padded work and the copies. In the layouts above, 128 then reads DK
+ * (q, k, dq, dk, a vector g and dg), DV (v, o, dO, dv) and DK x DV (states).
+ *
  * Errors: arguments are validated before anything is launched; on error
  * nothing is launched and the call returns a negative status. Unsupported
- * shapes (key/value width other than 128, chunk other than 64) return
- * GDR_ERR_UNSUPPORTED -- there is no fallback (the flashserve/ReWY repository
- * page, "Compatibility" and "Existing Training Scripts": K = V = 128, 64-token
- * chunks, unsupported configurations fail by default). T may be any length:
+ * shapes (a width above 128, chunk other than 64) return GDR_ERR_UNSUPPORTED
+ * -- there is no fallback (that page's "Existing Training Scripts":
+ * unsupported configurations fail by default). T may be any length:
  * where that page requires a multiple of 64, a ragged last chunk is handled
  * here, its missing rows acting as identity steps (g = 0, beta = 0, zero
  * q, k, v, dO), which leaves every output, state and gradient of the real
@@ -88,7 +96,7 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
 typedef struct {
     int64_t B, T, H;  /* batch, sequence length, heads */
-    int64_t DK, DV;   /* key and value width: must be 128 */
+    int64_t DK, DV;   /* key and value width: 1 .. 128 (128 without padding) */
     int64_t C;        /* chunk length: must be 64 */
     int32_t gate;     /* gdr_gate */
     int32_t dtype;    /* gdr_dtype */
@@ -160,7 +168,8 @@ int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int
  * turns timing on: every kernel that gdr_fwd / gdr_bwd / gdr_bwd_wy7 then
  * launch is bracketed by events recorded on the call's stream. Stages are
  * "prep", "scan_fwd", "xy", "scan_bwd", "scan_pair" (both scans of the
- * recompute backward in one launch), "bwd_local", "bwd_local_wy7".
+ * recompute backward in one launch), "bwd_local", "bwd_local_wy7", "pad" (the
+ * copies of widths below 128).
  * gdr_profile_end turns timing off, waits for the recorded events (a host
  * synchronization), and writes up to `cap` per-stage totals; *n_out receives
  * the number of stages seen. Launches beyond max_launches run untimed and

@@ -58,7 +58,7 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(DK=64), -2), (dict(DV=96), -2), (dict(C=32), -2),
+    (dict(DK=192), -2), (dict(DV=160), -2), (dict(DK=0), -1), (dict(DV=-3), -1), (dict(C=32), -2),
     (dict(gate=5), -1), (dict(gate=3), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
 ])
 def test_descriptor_validation(kw, status):
@@ -146,7 +146,7 @@ def test_packed_validation_without_launching():
     lib = gdr.load()
     assert _ws_varlen(_desc(B=2), 3)[0] == -1            # sequences live along T
     assert _ws_varlen(_desc(), -1)[0] == -1
-    assert _ws_varlen(_desc(DK=64), 2)[0] == -2
+    assert _ws_varlen(_desc(DK=192), 2)[0] == -2
     fake = 1 << 20  # never dereferenced: validation fails first
     d = _desc(T=256)
     sc = _ws_varlen(d, 2)[2]
@@ -189,3 +189,23 @@ def test_no_gate_workspace_and_null_gate():
     assert _fwd(d, q=fake, k=fake, v=fake, beta=fake, o=fake, scratch=fake, scratch_bytes=16) == -3
     assert _fwd(_desc(gate=0), q=fake, k=fake, v=fake, beta=fake, o=fake, scratch=fake,
                 scratch_bytes=16) == -1
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+@pytest.mark.parametrize("dk,dv", [(80, 112), (96, 80), (128, 64)])
+def test_narrow_widths_workspace(gate, dk, dv):
+    """Widths below 128: the 128-wide workspace plus zero-padded copies of the
+    token tensors (q, k, v, o or dO, dq, dk, dv at 128 wide), of a vector gate
+    and its gradient, and of three states."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, T, H = 2, 100, 3
+    for pol in (0, 1):
+        for dtype, esz in ((0, 2), (1, 4)):
+            rc, sv, sc = _ws(_desc(B=B, T=T, H=H, gate=gate, dtype=dtype, DK=dk, DV=dv), pol)
+            rc2, sv2, sc2 = _ws(_desc(B=B, T=T, H=H, gate=gate, dtype=dtype), pol)
+            assert rc == 0 and rc2 == 0 and sv == sv2
+            rows = B * T * H
+            pad = 7 * al(rows * 128 * esz) + 3 * al(B * H * 128 * 128 * 4)
+            if gate == 1:
+                pad += 2 * al(rows * 128 * 4)
+            assert sc == sc2 + pad

@@ -133,13 +133,15 @@ def test_deterministic_and_policy_independent():
 
 
 def test_unsupported_width_raises():
+    """A key width above 128 is refused before anything is launched."""
     _need_gpu()
+    import torch
     import delta_rule_linear_gdr_amd as gdr
     x = _edge("scalar", T=128)
     d = tl.device_inputs(x)
+    wide = lambda t: torch.cat([t, t[..., :64]], dim=-1).contiguous()  # noqa: E731
     with pytest.raises(gdr.GdrError) as ei:
-        gdr.gdr_fwd(d["q"][..., :64].contiguous(), d["k"][..., :64].contiguous(),
-                    d["v"], d["g"], d["beta"])
+        gdr.gdr_fwd(wide(d["q"]), wide(d["k"]), d["v"], d["g"], d["beta"])
     assert ei.value.status == -2
 
 
@@ -330,3 +332,39 @@ def test_deltanet_packed():
             g_all.append((got[n][i:i + 1, h:h + 1] if n in ("ht", "dh0") else got[n][:, a:b, h:h + 1]).ravel())
             r_all.append(np.asarray(r[n]).ravel())
         tl.check(n, np.concatenate(g_all), np.concatenate(r_all))
+
+
+# ---------------------------------------------- key / value widths below 128
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("dk,dv", [(80, 112), (96, 80)])
+def test_narrow_widths(gate, dk, dv):
+    """The pages' extended-test widths (80/112, 96/80) through zero-padded
+    copies: two batch entries, a ragged last chunk, nonzero states, both
+    policies."""
+    _need_gpu()
+    x = make_inputs(2, 100, 2, DK=dk, DV=dv, gate=gate, dtype="bf16", seed=51,
+                    gate_mean=4.0 if gate == "scalar" else 3.0, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"narrow/{gate}/{dk}x{dv}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+
+
+@pytest.mark.gpu
+def test_narrow_widths_fp32_wy7_and_packed():
+    """fp32 storage and the seven-product producer at 64/96, and a packed
+    batch at 80/112."""
+    _need_gpu()
+    x = make_inputs(1, 150, 2, DK=64, DV=96, gate="vector", dtype="fp32", seed=52, gate_mean=3.0,
+                    h0_std=0.1, dht_std=0.1)
+    _report("narrow/fp32/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=53)
+    # narrow copies of the packed inputs: keys and values cut to 80 and 112
+    for n in ("q", "k"):
+        xp[n] = np.ascontiguousarray(xp[n][..., :80])
+    for n in ("v", "dO"):
+        xp[n] = np.ascontiguousarray(xp[n][..., :112])
+    xp["h0"] = np.ascontiguousarray(xp["h0"][:, :, :80, :112])
+    xp["dht"] = np.ascontiguousarray(xp["dht"][:, :, :80, :112])
+    _report("narrow/packed", tl.compare_packed(tl.run_gpu_packed(xp), xp))
