@@ -115,9 +115,11 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     bf16x8* const lGq = lG + 1024;
     bf16x8* const lGqT = lG + 1536;
     __shared__ __attribute__((aligned(16))) float sG[CH], sBeta[CH];
-    __shared__ float sRedB[NW][CH], sRedP[NW][CH], sRedG[NW][CH];
+    // per-token partial sums of the eight waves (token-major: a token's eight
+    // partials are two 16-byte reads)
+    __shared__ __attribute__((aligned(16))) float sRedB[CH][NW], sRedP[CH][NW], sRedG[CH][NW];
     __shared__ float sExtra[DKD];
-    __shared__ float sEx[NW];
+    __shared__ __attribute__((aligned(16))) float sEx[NW];
 
     const T* q = (const T*)in.q + tok0 * DKD;
     const T* k = (const T*)in.k + tok0 * DKD;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 #pragma unroll
         for (int u = 0; u < 4; ++u) lG[u * NTHR + tid] = z8;
     }
-    __syncthreads();
+    lds_barrier();
     if (!VEC) Gnf = sG[CH - 1];
     // vector gate, this lane's key: centre of window 0 / 1, G at tokens 31 / 32
     auto win = [&](int x) -> float { return VEC ? sWin[VEC ? x : 0][f] : 0.f; };
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             }
             if (i < nv) store4(dvo + i * ld + 16 * w + 4 * g, dvv);
             pv = sum_rows(pv);
-            if (g == 0) sRedP[w][i] = pv;
+            if (g == 0) sRedP[i][w] = pv;
             if (!WY7) st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
         }
         if (WY7) {
@@ -454,7 +456,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         }
     }
 
-    __syncthreads();  // lP, lR, lO, sExtra complete
+    lds_barrier();  // lP, lR, lO, sExtra complete
 
     // ---- 2a'. seven-product producer (ablation): W = Rb h^T (so Wbar = -W),
     //      Abar = Rb Z^T + Wbar E^T, X = A^T Abar; Mbar = -X A^T follows below
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) WT[ks] = pack_pi(Wc[2 * ks], Wc[2 * ks + 1]);
-        __syncthreads();  // lWb complete
+        lds_barrier();  // lWb complete
         // Abar (full 64 x 64), two tiles per wave -> Abar^T frags (M = col, K = row)
         for (int x = w; x < 16; x += NW) {
             const int ta = x >> 2, tb = x & 3;
@@ -490,7 +492,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             // lane: Abar[a = 16 ta + 4 g + e][b = 16 tb + r]
             st_half(lAbT, tb * 2 + (ta >> 1), ta & 1, pack4(acc));
         }
-        __syncthreads();  // lAbT complete
+        lds_barrier();  // lAbT complete
         // X^T = Abar^T A (A^T is upper triangular: skip row slab 0 for i >= 32)
         for (int x = w; x < 16; x += NW) {
             const int tc = x >> 2, ti = x & 3;
@@ -499,7 +501,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             // lane: X[i = 16 ti + r][c = 16 tc + 4 g + e] -> X frag (M = i, K = c)
             st_half(lX, ti * 2 + (tc >> 1), tc & 1, pack4(acc));
         }
-        __syncthreads();  // lX complete
+        lds_barrier();  // lX complete
     }
 
     // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands. ReWY:
@@ -572,7 +574,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         for (int u = 0; u < 40 / NW; ++u) item2a(w + NW * u);
     }
 
-    __syncthreads();  // consumer A operands complete
+    lds_barrier();  // consumer A operands complete
 
     // ---- 2b. Gbar_n extra term: sum_j exp(G_n - G_j) k_j Ktb_j + gam_n rowsum(h o dh) ----
     float colsum = 0.f;
@@ -757,8 +759,8 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
             const float bsum = sum16(br[e]);
             const float gsum = VEC ? 0.f : sum16(Ga[e]);
             if (r == 0) {
-                sRedB[w][16 * m + 4 * g + e] = bsum;
-                if (!VEC) sRedG[w][16 * m + 4 * g + e] = gsum;
+                sRedB[16 * m + 4 * g + e][w] = bsum;
+                if (!VEC) sRedG[16 * m + 4 * g + e][w] = gsum;
             }
         }
         if (VEC) {
@@ -783,32 +785,25 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- 4. dbeta; scalar gate: dg ----
+    // ---- 4. dbeta (wave 1); scalar gate: dg (wave 0), side by side ----
     if (!VEC) {
         const float ex = sum16(extra);
         if (l == 0) sEx[w] = ex;
     }
-    __syncthreads();
-    if (tid < nv) {
-        float sb = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) sb += sRedB[ww][tid] + sRedP[ww][tid];
-        io<T>::st(dbo + tid * Hs, sb);
+    lds_barrier();
+    auto sum8 = [](const float* p) {
+        const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+        return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    };
+    if (w == 1) {
+        const float sb = sum8(sRedB[l]) + sum8(sRedP[l]);
+        if (l < nv) io<T>::st(dbo + l * Hs, sb);
     }
     if (!VEC && w == 0) {
         // sum the extra over features, then reverse cumsum over tokens
-        float xg = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) xg += sRedG[ww][l];
-        if (l == CH - 1) {
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) xg += sEx[ww];
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(xg, off);
-            if (l + off < 64) xg += y;
-        }
+        float xg = sum8(sRedG[l]);
+        if (l == CH - 1) xg += sum8(sEx);
+        xg = wave_incl_suffix(xg);
         if (l < nv) dgo[l * Hs] = xg;
     }
 }

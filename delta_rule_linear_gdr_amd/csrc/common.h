@@ -173,6 +173,23 @@ __device__ __forceinline__ float wave_incl_scan(float x)
     return x;
 }
 
+// Inclusive suffix sum over the 64 lanes of a wave (lane l receives the
+// sum over lanes l .. 63): suffix sums inside each 16-lane row (row shifts
+// left by 1, 2, 4, 8), then the totals of the later rows, read from their
+// first lanes.
+__device__ __forceinline__ float wave_incl_suffix(float x)
+{
+    x += dpp_zero<0x101, 0xf>(x);
+    x += dpp_zero<0x102, 0xf>(x);
+    x += dpp_zero<0x104, 0xf>(x);
+    x += dpp_zero<0x108, 0xf>(x);
+    const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float t3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    const int row = lane_id() >> 4;
+    return x + (row < 3 ? t3 : 0.f) + (row < 2 ? t2 : 0.f) + (row < 1 ? t1 : 0.f);
+}
+
 // Value held by lane l ^ 16 (rows 0 <-> 1, 2 <-> 3) and by lane l ^ 32.
 // A swap returns this lane's own value in one result and the partner's in
 // the other; comparing bits picks the partner's (if both are equal, either
@@ -304,6 +321,19 @@ __device__ __forceinline__ void store4(bf16* p, const float (&x)[4])
 __device__ __forceinline__ void store4(float* p, const float (&x)[4])
 {
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+// Workgroup barrier for an LDS exchange only. __syncthreads() also orders
+// global memory, so it waits for every outstanding global load and store of
+// the wave (a full vmcnt(0)); these kernels never read back global data that
+// another wave of the workgroup wrote, so the barrier waits only for the
+// wave's LDS accesses and leaves its loads in flight and its stores
+// draining. (The inline s_barrier carries no implied waits; the clobber
+// keeps memory accesses on their side of it.)
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0); vmcnt, expcnt at their maxima
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
