@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     }
     if (w == 0) sBeta[l] = to_f32(braw);
     if (STAGE) __builtin_amdgcn_s_waitcnt(0);  // the K / Q copies have landed
-    __syncthreads();
+    lds_barrier();
 
     auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
     if ((fwdscan || bwdscan) && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         }
     }
 
-    __syncthreads();  // sL complete
+    lds_barrier();  // sL complete
 
     // ---- 3. A = (I + L)^{-1}: diagonal 16 x 16 blocks, then block rows ----
     {
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
             for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
         }
-        __syncthreads();
+        lds_barrier();
         const int jb = w, rr = (tid >> 2) & 15, c4 = (tid & 3) * 4;
         for (int bi = 1; bi < 4; ++bi) {
             if (jb < bi) {
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 }
                 *(float4*)&sT[(jb * 16 + rr) * TP + c4] = acc;
             }
-            __syncthreads();
+            lds_barrier();
             if (jb < bi) {
                 float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 *(float4*)&sA[(16 * bi + rr) * LP + 16 * jb + c4] =
                     make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
             }
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -533,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             if (out) st_row8_frag(it.Qg + t * (CH * DKD), i, f0, qx);
         }
     }
-    __syncthreads();  // sQgT complete
+    lds_barrier();  // sQgT complete
 
     // ---- 5. W = A E, W^T = E^T A^T, U = A Z; A ----
     {

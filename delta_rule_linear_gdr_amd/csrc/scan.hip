@@ -270,7 +270,8 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
 }
 
 // xs: the LDS exchange, NV x 4 state slabs then NV x 2 Z slabs of 64 x 16 B.
-template <bool BWD, int NV>
+// STORE: write the state before each step and Z (h, R or dh, Rb).
+template <bool BWD, int NV, bool STORE>
 __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, const Inter& it, float* fin,
                                             const SeqView& sq, int64_t bh, int vs, const uint8_t* ring,
                                             bf16x8 (*xs)[64])
@@ -282,9 +283,8 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
     bf16x8 (*sS)[4][64] = (bf16x8 (*)[4][64])xs;           // [NV][4][64]
     bf16x8 (*sZ)[2][64] = (bf16x8 (*)[2][64])(xs + 4 * NV);  // [NV][2][64]
 
-    bf16* Sout = BWD ? it.dh : it.h;  // null: not stored (the forward without a backward)
+    bf16* Sout = BWD ? it.dh : it.h;
     bf16* Zout = BWD ? it.Rb : it.R;
-    const bool store = Sout != nullptr;
     const float* init = BWD ? in.dht : in.h0;
 
     // state: value tile NV vs + u, key rows 32 w + 16 m + 4 g + i, column 16 (NV vs + u) + r
@@ -305,7 +305,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile NV vs + u)
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            if (store) {
+            if constexpr (STORE) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
                     *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m) = pack4(S[u][m]);
@@ -333,7 +333,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         }
         wait_lgkm0();
         bar();
-        if (store) {
+        if constexpr (STORE) {
 #pragma unroll
             for (int u = 0; u < NV; ++u)
                 *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w) = z4[u];
@@ -378,7 +378,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
     }
 }
 
-template <bool BWD, int NV, bool OUT, typename T>
+template <bool BWD, int NV, bool OUT, typename T, bool STORE>
 __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const Inter& it, float* fin,
                                          const Chain& ch, uint8_t* ring, bf16x8 (*xs)[64], T* o)
 {
@@ -390,7 +390,7 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
     case 5: fed_loader<BWD, 1, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
     case 6: fed_loader<BWD, 2, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
     case 7: fed_loader<BWD, 3, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
-    default: fed_compute<BWD, NV>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs); break;
+    default: fed_compute<BWD, NV, STORE>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs); break;
     }
 }
 
@@ -398,8 +398,8 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
 // side by side (the reverse scan reads only prep's operands, not the
 // forward states); ndir = 1 the reverse scan alone. Only the reverse chains
 // write fin (dh0). The forward launch (OUT = true, ndir = 1) writes the
-// output o and fin (ht), and h and R when it.h is set.
-template <int NV, bool OUT, typename T>
+// output o and fin (ht), and h and R when STORE (full save).
+template <int NV, bool OUT, typename T, bool STORE>
 __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* fin, int ndir, T* o)
 {
     using L = Fed<NV>;
@@ -408,10 +408,10 @@ __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter
     Chain ch;
     if (!chain_of_block(s, NVS / NV, ndir, !OUT, blockIdx.x, ch)) return;
     if constexpr (OUT) {
-        fed_body<false, NV, true, T>(s, in, it, fin, ch, ring, xs, o);
+        fed_body<false, NV, true, T, STORE>(s, in, it, fin, ch, ring, xs, o);
     } else {
-        if (ch.bwd) fed_body<true, NV, false, T>(s, in, it, fin, ch, ring, xs, o);
-        else fed_body<false, NV, false, T>(s, in, it, nullptr, ch, ring, xs, o);
+        if (ch.bwd) fed_body<true, NV, false, T, STORE>(s, in, it, fin, ch, ring, xs, o);
+        else fed_body<false, NV, false, T, STORE>(s, in, it, nullptr, ch, ring, xs, o);
     }
 }
 
@@ -440,19 +440,23 @@ hipError_t launch_fed(const Shape& s, const Inputs& in, const Inter& it, float* 
                       hipStream_t st)
 {
     if (wide(s, ndir))
-        scan_fed_kernel<2, false, bf16><<<scan_grid(s, NVS / 2, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
+        scan_fed_kernel<2, false, bf16, true><<<scan_grid(s, NVS / 2, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
     else
-        scan_fed_kernel<1, false, bf16><<<scan_grid(s, NVS, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
+        scan_fed_kernel<1, false, bf16, true><<<scan_grid(s, NVS, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
     return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_fed_out(const Shape& s, const Inputs& in, const Inter& it, T* o, float* ht, hipStream_t st)
 {
-    if (wide(s, 1))
-        scan_fed_kernel<2, true, T><<<scan_grid(s, NVS / 2, 1), 512, 0, st>>>(s, in, it, ht, 1, o);
-    else
-        scan_fed_kernel<1, true, T><<<scan_grid(s, NVS, 1), 512, 0, st>>>(s, in, it, ht, 1, o);
+    const unsigned g2 = scan_grid(s, NVS / 2, 1), g1 = scan_grid(s, NVS, 1);
+    if (it.h) {  // full save: h and R too
+        if (wide(s, 1)) scan_fed_kernel<2, true, T, true><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
+        else scan_fed_kernel<1, true, T, true><<<g1, 512, 0, st>>>(s, in, it, ht, 1, o);
+    } else {
+        if (wide(s, 1)) scan_fed_kernel<2, true, T, false><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
+        else scan_fed_kernel<1, true, T, false><<<g1, 512, 0, st>>>(s, in, it, ht, 1, o);
+    }
     return hipGetLastError();
 }
 
