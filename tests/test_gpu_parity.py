@@ -368,3 +368,24 @@ def test_narrow_widths_fp32_wy7_and_packed():
     xp["h0"] = np.ascontiguousarray(xp["h0"][:, :, :80, :112])
     xp["dht"] = np.ascontiguousarray(xp["dht"][:, :, :80, :112])
     _report("narrow/packed", tl.compare_packed(tl.run_gpu_packed(xp), xp))
+
+
+@pytest.mark.gpu
+def test_packed_more_sequences_than_one_table_tile():
+    """1500 sequences (the sequence tables are built in tiles of 1024 with a
+    running carry), most of them short or empty, over 3000 tokens; the
+    oracle checks every sequence of head 1."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs, packed_lengths
+    x = make_packed_inputs(packed_lengths(3000, 1500, seed=7), H=2, gate="vector", seed=61,
+                           gate_mean=3.0)
+    _report("packed/1500", tl.compare_packed(tl.run_gpu_packed(x), x, heads=(1,)))
+
+
+@pytest.mark.gpu
+def test_many_heads_and_batch():
+    """B = 4, H = 48 (768 state entries: wide scan launches), sampled heads."""
+    _need_gpu()
+    x = make_inputs(4, 192, 48, gate="scalar", dtype="bf16", seed=62, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"B4H48/{pol}", tl.compare(tl.run_gpu(x, pol), x, heads=[(0, 0), (3, 47), (2, 17)]))
