@@ -76,8 +76,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     const bool fwdscan = what & PREP_FWDSCAN, out = what & PREP_OUT, bwdscan = what & PREP_BWDSCAN;
     const bool xy = what & PREP_XY, savexy = what & PREP_SAVEXY, wantA = what & PREP_A;
 
-    constexpr int GSZ = VEC ? CH * DKD : CH;
-    __shared__ float sG[GSZ];
+    // Vector gate: G per (token, key), rows padded to 132 floats so that the
+    // 16 rows a fragment read spans land on distinct LDS banks (a 128-float
+    // stride puts them all on the same banks).
+    constexpr int GST = DKD + 4;
+    constexpr int GSZ = VEC ? CH * GST : CH;
+    __shared__ __attribute__((aligned(16))) float sG[GSZ];
     __shared__ float sCen[VEC ? 4 : 1][DKD];  // per 16-row tile: centre of G over its rows
     __shared__ float sBeta[CH];
     // L, then A = (I + L)^{-1} in place: block row i reads its L blocks
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float G = x[u][m][e] + excl + base;
-                    sG[(16 * m + 4 * g + e) * DKD + f] = G;
+                    sG[(16 * m + 4 * g + e) * GST + f] = G;
                     mx = fmaxf(mx, G);
                     mn = fminf(mn, G);
                 }
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     if (STAGE) __builtin_amdgcn_s_waitcnt(0);  // the K / Q copies have landed
     lds_barrier();
 
-    auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * DKD + f] : sG[i]; };
+    auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * GST + f] : sG[i]; };
     if ((fwdscan || bwdscan) && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
 
     // plain fragment of row block i0 .. i0+15, keys 32 ks + 8 g .. + 7: the
@@ -220,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         const int i = i0 + r, f0 = 32 * ks + 8 * g;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float d = sG[i * DKD + f0 + e] - pv[f0 + e];
+            const float d = sG[i * GST + f0 + e] - pv[f0 + e];
             // 1: alpha = exp(G - p) (queries);  2: beta alpha (erase keys);
             // 3: zeta = exp(p - G) (write keys)
             x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             const R8(&b)[3][4] = buf[u & 1];
             // vector gate: the centre of a diagonal tile, else G at the last
             // row of the column tile
-            const float* pv = ti == tj ? sCen[VEC ? ti : 0] : &sG[VEC ? (16 * tj + 15) * DKD : 0];
+            const float* pv = ti == tj ? sCen[VEC ? ti : 0] : &sG[VEC ? (16 * tj + 15) * GST : 0];
             f32x4 aL = zero4(), aH = zero4(), aHt = zero4();
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
