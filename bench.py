@@ -114,7 +114,7 @@ def measured_traffic(kernel: str, units: int):
     return round(float(row.group(1)) + float(row.group(2)), 0)
 
 
-def shape_sweep(gdr, to_dev, make_runner, time_steps, args):
+def shape_sweep(gdr, to_dev, make_runner, time_steps, graph_ms, args):
     """The six shapes of the pages' evaluation, scalar and vector gate (gate
     means 4 and 3, the distributions of the (1,2048,16) and (2,2048,16)
     workloads), backward under both policies and the recompute forward:
@@ -128,7 +128,9 @@ def shape_sweep(gdr, to_dev, make_runner, time_steps, args):
                              gate_mean=4.0 if gate == "scalar" else 3.0)
             ds = to_dev(xs)
             row = {"B": Bs, "T": Ts, "H": Hs, "gate": gate}
-            msR = time_steps(make_runner(ds, gdr.gdr_bwd, "recompute"), args.steps, args.warmup)
+            runR = make_runner(ds, gdr.gdr_bwd, "recompute")
+            msR = time_steps(runR, args.steps, args.warmup)
+            msRg = graph_ms(runR, args.steps, args.warmup)
             _, _, saved = gdr.gdr_fwd(ds["q"], ds["k"], ds["v"], ds["g"], ds["beta"], ds["h0"],
                                       policy="full_save")
             msA = time_steps(make_runner(ds, gdr.gdr_bwd, "full_save", saved), args.steps,
@@ -138,7 +140,8 @@ def shape_sweep(gdr, to_dev, make_runner, time_steps, args):
             msF = time_steps(lambda: gdr.gdr_fwd(ds["q"], ds["k"], ds["v"], ds["g"], ds["beta"],
                                                  ds["h0"], policy="recompute", scratch=scr),
                              args.steps, args.warmup)
-            row.update(bwd_R_ms=round(msR, 4), bwd_A_ms=round(msA, 4), fwd_R_ms=round(msF, 4),
+            row.update(bwd_R_ms=round(msR, 4), bwd_R_graph_ms=round(msRg, 4), bwd_A_ms=round(msA, 4),
+                       fwd_R_ms=round(msF, 4),
                        bwd_R_tokens_per_s=round(Bs * Ts / (msR * 1e-3), 1),
                        bwd_A_tokens_per_s=round(Bs * Ts / (msA * 1e-3), 1))
             rows.append(row)
@@ -203,6 +206,22 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps  # ms per step
+
+    def graph_ms(run, steps, warmup):
+        """ms per call of `run` replayed from a HIP graph (the pages time the
+        backward as warmed device-graph replays); run uses static buffers."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        ms_g = time_steps(graph.replay, steps, warmup)
+        del graph
+        return ms_g
 
     def profiled(run, steps):
         gdr.profile_begin(8 * steps + 16)
@@ -274,6 +293,8 @@ def main():
             "TFLOP/s": round(fl_k * units / (v * 1e-3) / 1e12, 2)}
 
     if not args.no_extra:
+        # the same step replayed from a HIP graph
+        detail["bwd_R_graph_ms"] = round(graph_ms(run, args.steps, args.warmup), 4)
         # forward, recompute policy (output + final state)
         _, sc = gdr.workspace_size(B, T, H, "scalar", "bf16", "recompute")
         scr = torch.empty(sc, dtype=torch.uint8, device=dev)
@@ -331,7 +352,7 @@ def main():
         detail["kda_fwd_bwd_R_tokens_per_s"] = round(B * T / (msKFB * 1e-3), 1)
         del dk_, xk, scrK
         if not args.no_sweep:
-            detail["shape_sweep"] = shape_sweep(gdr, to_dev, make_runner, time_steps, args)
+            detail["shape_sweep"] = shape_sweep(gdr, to_dev, make_runner, time_steps, graph_ms, args)
 
     cpu = None
     if not args.no_cpu_baseline:

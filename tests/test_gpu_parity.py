@@ -389,3 +389,87 @@ def test_many_heads_and_batch():
     x = make_inputs(4, 192, 48, gate="scalar", dtype="bf16", seed=62, h0_std=0.1, dht_std=0.1)
     for pol in ("recompute", "full_save"):
         _report(f"B4H48/{pol}", tl.compare(tl.run_gpu(x, pol), x, heads=[(0, 0), (3, 47), (2, 17)]))
+
+
+# ------------------------------------------------------ HIP graph capture
+
+def _graph_case(x, policy, packed):
+    """Forward + backward into preallocated outputs; returns a callable that
+    launches both on the current stream, and the output tensors."""
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    d = tl.device_inputs(x)
+    cu = torch.from_numpy(x["cu"]).to("cuda") if packed else None
+    B, T, H = d["q"].shape[:3]
+    ns = len(x["cu"]) - 1 if packed else B
+    gate = "vector" if d["g"].dim() == 4 else "scalar"
+    sv, sc = gdr.workspace_size(B, T, H, gate, "bf16", policy, n_seq=ns if packed else None)
+    scratch = torch.empty(max(sc, 256), dtype=torch.uint8, device="cuda")
+    saved = torch.empty(max(sv, 256), dtype=torch.uint8, device="cuda") if sv else None
+    o = torch.empty_like(d["v"])
+    ht = torch.empty((ns, H, 128, 128), dtype=torch.float32, device="cuda")
+    out = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+               dg=torch.empty_like(d["g"]), dbeta=torch.empty_like(d["beta"]),
+               dh0=torch.empty((ns, H, 128, 128), dtype=torch.float32, device="cuda"))
+    lib = gdr.load()
+    desc = gdr._desc_from(d["q"], d["g"], d["v"])
+    pol = gdr._policy(policy)
+    P = gdr._ptr
+
+    def launch():
+        st = gdr._stream()
+        fa = (P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]), P(o), P(ht),
+              P(saved), P(scratch), scratch.numel(), st)
+        ba = (P(d["q"]), P(d["k"]), P(d["v"]), P(d["g"]), P(d["beta"]), P(d["h0"]), P(d["dO"]),
+              P(d["dht"]), P(saved), P(out["dq"]), P(out["dk"]), P(out["dv"]), P(out["dg"]),
+              P(out["dbeta"]), P(out["dh0"]), P(scratch), scratch.numel(), st)
+        import ctypes
+        if packed:
+            assert lib.gdr_fwd_varlen(ctypes.byref(desc), pol, P(cu), ns, *fa) == 0
+            assert lib.gdr_bwd_varlen(ctypes.byref(desc), pol, P(cu), ns, *ba) == 0
+        else:
+            assert lib.gdr_fwd(ctypes.byref(desc), pol, *fa) == 0
+            assert lib.gdr_bwd(ctypes.byref(desc), pol, *ba) == 0
+    return launch, {"o": o, "ht": ht, **out}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+@pytest.mark.parametrize("packed", [False, True])
+def test_graph_replay_matches_eager(policy, packed):
+    """The forward + backward captured once in a HIP graph and replayed three
+    times, with eager launches, output clearing and synchronizations between
+    the replays: every replay equals the eager result bit for bit (the
+    library allocates nothing, never synchronizes, clears memory with kernels
+    and has no atomics)."""
+    _need_gpu()
+    import torch
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    if packed:
+        x = make_packed_inputs([100, 0, 64, 131], H=2, gate="vector", seed=71, gate_mean=3.0)
+    else:
+        x = make_inputs(2, 200, 2, gate="vector", dtype="bf16", seed=72, gate_mean=3.0,
+                        h0_std=0.1, dht_std=0.1)
+    launch, outs = _graph_case(x, policy, packed)
+    launch()
+    torch.cuda.synchronize()
+    ref = {n: t.clone() for n, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        launch()
+    for rep in range(3):
+        for t in outs.values():
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n, t in outs.items():
+            assert torch.equal(t, ref[n]), f"replay {rep}: {n}"
+        launch()  # eager work between replays
+        torch.cuda.synchronize()
