@@ -473,3 +473,18 @@ def test_graph_replay_matches_eager(policy, packed):
             assert torch.equal(t, ref[n]), f"replay {rep}: {n}"
         launch()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.gpu
+def test_out_of_contract_decay_fails_loudly():
+    """Every log decay -8 (a 32-token window spans 248, past the vector gate's
+    contract of 160): the backward's centred factors leave fp32, and its
+    gradients come out non-finite rather than finite and wrong. The forward's
+    16-token windows still hold (range 120): o and ht match the oracle."""
+    _need_gpu()
+    x = make_inputs(1, 256, 2, gate="vector", dtype="bf16", seed=3, h0_std=0.1, dht_std=0.1)
+    x["g"] = np.full_like(x["g"], -8.0)
+    gpu = tl.run_gpu(x)
+    for n in ("dq", "dk", "dg"):
+        assert not np.all(np.isfinite(gpu[n])), n
+    tl.compare(gpu, x, names=("o", "ht"))
