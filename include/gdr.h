@@ -1,7 +1,8 @@
 /*
  * gdr.h -- C ABI of the MI355X (gfx950) chunkwise gated delta-rule operator:
- * forward and backward of Gated DeltaNet (scalar gate) and Kimi Delta
- * Attention (per-key-channel gate), chunk size 64, key and value width 128.
+ * forward and backward of Gated DeltaNet (scalar gate), Kimi Delta
+ * Attention (per-key-channel gate) and DeltaNet (no decay), chunk size 64,
+ * key and value width up to 128, regular or packed variable-length batches.
  *
  * Operation ("ReWY: Faster Backpropagation for Delta-Rule Attention -- From
  * 7 to 3 Matrix Multiplications", paperpeel.com/paper/2611.01940, Sec. 2.2
@@ -63,7 +64,8 @@
  * factors (Sec. 3.3) are formed per window of the chunk, with boundary pivots
  * between windows, so they span exp(+-range/2) of a 32-token half-chunk; g
  * must be a log decay (g <= 0) whose per-channel range over each 32-token
- * half of a chunk is at most 160 (e.g. every |g| <= 5). A launch failure
+ * half of a chunk is at most 160 (e.g. every |g| <= 5); past that the
+ * backward's results are non-finite, not finite and wrong. A launch failure
  * returns GDR_ERR_HIP. gdr_last_error() returns a message for
  * the calling thread's last failure.
  */
