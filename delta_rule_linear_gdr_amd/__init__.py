@@ -9,6 +9,7 @@ unbuilt library raises.
     o, ht, saved = gdr_fwd(q, k, v, g, beta, h0, policy="recompute")
     grads = gdr_bwd(q, k, v, g, beta, h0, dO, dht, saved=saved, policy="recompute")
     grads = gdr_bwd_wy7(...)          # seven-product producer (ablation)
+    o, ht = chunk_gated_delta_rule(q, k, v, g, beta, h0)   # autograd-aware
 
 Shapes: q, k [B,T,H,DK]; v, dO [B,T,H,DV]; g [B,T,H] (GDN, scalar gate),
 [B,T,H,DK] (KDA, per-channel gate), fp32, or None (DeltaNet: no decay, and
@@ -25,7 +26,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "workspace_size", "library_path", "load",
+__all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "chunk_gated_delta_rule", "workspace_size",
+           "library_path", "load",
            "profile_begin", "profile_end", "GdrError", "RECOMPUTE", "FULL_SAVE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -297,3 +299,58 @@ def gdr_bwd_wy7(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recomput
     """Backward with the expanded seven-product WY producer (ablation)."""
     return _bwd("gdr_bwd_wy7", q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0,
                 scratch, out)
+
+
+# ------------------------------------------------------------- autograd
+
+def _autograd_function():
+    torch = _torch()
+
+    class _ChunkGatedDeltaRule(torch.autograd.Function):
+        """Forward by gdr_fwd, backward by gdr_bwd; no arithmetic here (the
+        only torch work is making the incoming output adjoint contiguous)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, h0, policy, cu_seqlens):
+            ctx.set_materialize_grads(False)
+            o, ht, saved = gdr_fwd(q, k, v, g, beta, h0, policy=policy, cu_seqlens=cu_seqlens)
+            ctx.policy = policy
+            ctx.has_g, ctx.has_h0 = g is not None, h0 is not None
+            ctx.save_for_backward(q, k, v, g if g is not None else q.new_empty(0), beta,
+                                  h0 if h0 is not None else q.new_empty(0),
+                                  saved if saved is not None else q.new_empty(0, dtype=torch.uint8),
+                                  cu_seqlens if cu_seqlens is not None else q.new_empty(0, dtype=torch.int64))
+            ctx.has_saved, ctx.packed = saved is not None, cu_seqlens is not None
+            return o, ht
+
+        @staticmethod
+        def backward(ctx, dO, dht):
+            q, k, v, g, beta, h0, saved, cu = ctx.saved_tensors
+            g = g if ctx.has_g else None
+            h0 = h0 if ctx.has_h0 else None
+            saved = saved if ctx.has_saved else None
+            cu = cu if ctx.packed else None
+            if dO is None and dht is None:
+                return (None,) * 8
+            if dO is None:
+                dO = torch.zeros_like(v)
+            gr = gdr_bwd(q, k, v, g, beta, h0, dO.contiguous(),
+                         None if dht is None else dht.contiguous(), saved=saved,
+                         policy=ctx.policy, want_dh0=h0 is not None, cu_seqlens=cu)
+            return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["dbeta"], gr["dh0"], None, None)
+
+    return _ChunkGatedDeltaRule
+
+
+_AUTOGRAD = None
+
+
+def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, policy="recompute", cu_seqlens=None):
+    """Differentiable operator: returns (o, ht) and back-propagates through
+    the library's backward into q, k, v, g, beta and h0. g None is DeltaNet
+    (no decay); cu_seqlens makes a packed batch. policy "full_save" keeps the
+    forward's chunk quantities for the backward instead of recomputing them."""
+    global _AUTOGRAD
+    if _AUTOGRAD is None:
+        _AUTOGRAD = _autograd_function()
+    return _AUTOGRAD.apply(q, k, v, g, beta, h0, policy, cu_seqlens)

@@ -69,3 +69,10 @@ def test_workspace_size_matches_the_c_call():
     assert sv2 == sv and sc2 == sc + 2 * 4 * 8192 * 16
     svp, scp = gdr.workspace_size(1, 8192, 16, "vector", "bf16", "recompute", n_seq=3, DK=80, DV=112)
     assert svp == 0 and scp > sc
+
+
+def test_autograd_operator_refuses_host_tensors():
+    q, k, v, g, beta = _args()
+    q.requires_grad_(True)
+    with pytest.raises(ValueError, match="device tensor"):
+        gdr.chunk_gated_delta_rule(q, k, v, g, beta)
