@@ -46,6 +46,12 @@
 //      A operands of the Gram / matrix-intra products; Eb_dir, Qgb, Ktb.
 //   3. The four consumer products; reductions of dbeta and dg.
 // Orientation changes use MFMA products with the identity, which are exact.
+//
+// Launch: the scalar-gate three-product kernel is persistent (one workgroup
+// per CU, each taking every G-th (chunk, head)) and streams the next
+// chunk's h and dh into LDS while it works on the current one; the
+// vector-gate and seven-product kernels, which have no LDS left for that,
+// run one workgroup per (chunk, head).
 #include "common.h"
 #include "kernels.h"
 
@@ -61,12 +67,58 @@ __device__ __forceinline__ void st_half(bf16x8* buf, int tile, int half, const b
     *(bf16x4*)((bf16*)&buf[tile * 64 + lane_id()] + 4 * half) = v;
 }
 
-template <typename T, bool VEC, bool WY7>
-__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr)
+// Prefetch of h and dh (persistent form): wave w copies the sixteen
+// fragments it reads itself -- ctiles vt * 8 + w (vt = 0..7) of h, then of
+// dh, 512 bytes each -- into its own 8 KiB staging area, two ctiles per
+// 16-byte-per-lane direct-to-LDS load. A ctile is copied verbatim, so lane
+// l's four elements of ctile vt land at entry vt * 64 + l (h) and
+// 512 + vt * 64 + l (dh) of the area.
+//
+// The loads are issued from inline assembly, which the compiler's wait
+// insertion does not see: it would otherwise make later LDS writes of the
+// chunk wait for them (it cannot tell the staging area from the other LDS
+// buffers) and so serialize the prefetch. Their completion is awaited
+// explicitly instead (PF_WAIT below). Untracked loads issued after a
+// tracked one only make the compiler's own counts conservative, since
+// vector-memory operations complete in order.
+constexpr int STAGE = 1024;  // bf16x4 entries per wave
+
+__device__ __forceinline__ void dma16_untracked(const bf16* src, uint32_t lds_addr)
 {
-    SeqView sv;
-    int64_t c;
-    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    // the LDS base goes in M0 (set by the compiler just before); one wait
+    // state between writing M0 and the load
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr) : "memory");
+}
+
+__device__ __forceinline__ void stage_hdh(const Inter& it, int64_t tt, int w, bf16x4* area)
+{
+    const int l = lane_id();
+    const bf16* const hs = it.h + tt * (DKD * DVD);
+    const bf16* const ds = it.dh + tt * (DKD * DVD);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16x4*)area);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int off = ((2 * j + (l >> 5)) * 8 + w) * 256 + (l & 31) * 8;
+        dma16_untracked(hs + off, base + j * 1024);
+        dma16_untracked(ds + off, base + 4096 + j * 1024);
+    }
+}
+
+// Where a chunk reads its staged h and dh (phase 1c), at least the 32 reads
+// of the chunk's own batch have been issued after the staging loads (which
+// were issued during the previous chunk, or before the first), so
+// vmcnt(PF_WAIT) with PF_WAIT < 32 leaves none of them outstanding.
+constexpr int PF_WAIT = 8;
+
+// One (chunk, head). PF: h and dh come from this wave's staging area
+// `area` (already requested), and the next chunk's (tile tnext >= 0) are
+// requested once they have been read.
+template <typename T, bool VEC, bool WY7, bool PF>
+__device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in, const Inter& it,
+                                                const Grads& gr, const SeqView& sv, int64_t c,
+                                                int64_t tnext, bf16x4* area)
+{
     const int64_t t = seq_tile(s, sv, c);
     const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
     const int nv = seq_rows(sv, c);  // rows past it read as zeros and are not written
@@ -76,7 +128,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     const int ld = (int)(s.H * DKD);
     const int Hs = (int)s.H;
     const int tid = threadIdx.x;
-    const int l = lane_id(), r = lane_r(), g = lane_g();
+    // The lane index, opaque to the compiler in the persistent form:
+    // lane-only values (the identity fragments, lane offsets) are then
+    // formed per chunk instead of being hoisted out of the loop and held in
+    // registers across it.
+    int lx = lane_id();
+    if (PF) asm volatile("" : "+v"(lx));
+    const int l = lx, r = lx & 15, g = (lx >> 4) & 3;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int f = 16 * w + r;  // this lane's feature (key or value) column
 
@@ -191,10 +249,12 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         const R4 x = ld4raw(dO + rowc(m) * ld + 16 * w + 4 * g);
         orw[m] = rv[m] ? x : R4{};
     }
+    if (!PF) {
 #pragma unroll
-    for (int vt = 0; vt < 8; ++vt) {
-        hq[vt] = *(const bf16x4*)ctile_ptr(hg, vt * 8 + w);
-        dhq[vt] = *(const bf16x4*)ctile_ptr(dhg, vt * 8 + w);
+        for (int vt = 0; vt < 8; ++vt) {
+            hq[vt] = *(const bf16x4*)ctile_ptr(hg, vt * 8 + w);
+            dhq[vt] = *(const bf16x4*)ctile_ptr(dhg, vt * 8 + w);
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -296,9 +356,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : Gs[VEC ? 0 : m][e]; };
     auto Bt = [&](int m, int e) -> float { return VEC ? sBeta[16 * m + 4 * g + e] : Bs[VEC ? 0 : m][e]; };
 
-    const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
+    const bf16x8 I0 = ident_frag(0, lx), I1 = ident_frag(1, lx);
     const bf16x8 Iw = (w & 1) ? I1 : I0;
-    const bf16x8 Ipw = ident_pi(w & 1);
+    const bf16x8 Ipw = ident_pi(w & 1, lx);
     const bf16x4 z4 = {};
 
     // ---- 1a. P^T = Rb^T A for value tile w ----
@@ -328,7 +388,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         if (WY7) {
             // Rb fragments (contraction over values) through Rb^T * I, and
             // Z = diag(beta) V fragments, value tile w
-            const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+            const bf16x8 Ip0 = ident_pi(0, lx), Ip1 = ident_pi(1, lx);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const f32x4 cc = mfma(RbT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
@@ -345,7 +405,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // ---- 1b. R and dO fragments (contraction over values) of value tile w ----
     {
         const bf16x8 RT[2] = {cat8(rq[0], rq[1]), cat8(rq[2], rq[3])};
-        const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+        const bf16x8 Ip0 = ident_pi(0, lx), Ip1 = ident_pi(1, lx);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             // lane: R[tok 16 m + r][val 16 w + 4 g + e]
@@ -355,6 +415,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         }
     }
     // ---- 1c. h, dh fragments (M = key tile w, K = values); rowsum(h o dh) ----
+    if (PF) {
+        static_assert(PF_WAIT < 32, "fewer reads than PF_WAIT follow the staging loads");
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(PF_WAIT) : "memory");  // staged h, dh have landed
+#pragma unroll
+        for (int vt = 0; vt < 8; ++vt) {
+            hq[vt] = area[vt * 64 + l];
+            dhq[vt] = area[512 + vt * 64 + l];
+        }
+    }
     bf16x8 hF[4], dhF[4];
     {
         float hdp[4] = {0.f, 0.f, 0.f, 0.f};
@@ -388,10 +457,20 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
         KC[m] = mfma(tobf8(kr[m]), Iw, zero4());
         QC[m] = mfma(tobf8(qr[m]), Iw, zero4());
     }
+    // Next chunk's h, dh: requested only now, after the last use of this
+    // chunk's reads, so that no wait the compiler places for those reads
+    // also waits for the staging loads (they would be younger than the
+    // reads in the in-order count). From here on the chunk only stores.
+    if (PF && tnext >= 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // the area has been read
+        stage_hdh(it, tnext, w, area);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     if (WY7) {
         // E = diag(beta)(gam * K) fragments (M = tok, K = key) of key tile w:
         // E^T frags from the K * I accumulators, transposed through E^T * I
-        const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+        const bf16x8 Ip0 = ident_pi(0, lx), Ip1 = ident_pi(1, lx);
         bf16x8 ETf[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -603,7 +682,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     // per tile; exact, since each output is a bf16 value times 1.
     constexpr bool ROWSTORE = sizeof(T) == 2;
     f32x4 dqP[2], dkP[2];
-    const bf16x8 Ip0 = ident_pi(0), Ip1 = ident_pi(1);
+    const bf16x8 Ip0 = ident_pi(0, lx), Ip1 = ident_pi(1, lx);
 #pragma unroll
     for (int m = 3; m >= 0; --m) {
         // E = P h^T (ReWY) or A^T W with W = Rb h^T (seven-product); both are -Eb_dir
@@ -808,11 +887,63 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     }
 }
 
+template <typename T, bool VEC, bool WY7>
+__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr)
+{
+    SeqView sv;
+    int64_t c;
+    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, sv, c, -1, nullptr);
+}
+
+// Persistent form (scalar gate, three-product producer): workgroup b takes
+// items b, b + G, b + 2G, ... of the per-chunk grid (x = chunk or slot
+// fastest, then b * H + head; G = gridDim.x) and keeps the next item's h and
+// dh streaming into LDS while it works on the current one. With one
+// workgroup per CU, a per-chunk launch leaves each CU idle while a new
+// workgroup's reads arrive; here those of h and dh (64 KiB of the chunk's
+// 169 KiB) arrive during the previous item.
+template <typename T>
+__global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, Inter it, Grads gr)
+{
+    __shared__ bf16x4 sStage[NW][STAGE];
+    const int64_t n = s.NC * (s.B * s.H);
+    const int64_t G = gridDim.x;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    SeqView sv;
+    int64_t c;
+    int64_t i = blockIdx.x;
+    while (i < n && !chunk_at(s, i % s.NC, i / s.NC, sv, c)) i += G;
+    if (i >= n) return;
+    stage_hdh(it, seq_tile(s, sv, c), w, sStage[w]);
+    for (;;) {
+        SeqView sn;
+        int64_t cn = 0;
+        int64_t j = i + G;
+        while (j < n && !chunk_at(s, j % s.NC, j / s.NC, sn, cn)) j += G;
+        bwd_local_chunk<T, false, false, true>(s, in, it, gr, sv, c, j < n ? seq_tile(s, sn, cn) : -1,
+                                               sStage[w]);
+        if (j >= n) break;
+        i = j;
+        sv = sn;
+        c = cn;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, hipStream_t st)
 {
+    if (!wy7 && !s.vec) {
+        // one workgroup per CU (LDS), each taking every G-th (chunk, head)
+        const int64_t n = s.NC * (s.B * s.H);
+        if (n <= 0) return hipSuccess;
+        const unsigned nb = (unsigned)(n < cu_count() ? n : cu_count());
+        if (s.f32) bwd_local_pf_kernel<float><<<nb, NTHR, 0, st>>>(s, in, it, gr);
+        else bwd_local_pf_kernel<bf16><<<nb, NTHR, 0, st>>>(s, in, it, gr);
+        return hipGetLastError();
+    }
     dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
 #define GDR_BWD_LOCAL(W7)                                                                        \
     do {                                                                                         \

@@ -267,26 +267,29 @@ __device__ __forceinline__ bf16* ctile_ptr(bf16* base, int tile) { return base +
 
 // B operand of X * I for output column tile nt: the identity restricted to
 // k slab nt >> 1 (the other slabs are zero). parity = nt & 1.
-__device__ __forceinline__ bf16x8 ident_frag(int parity)
+// (`lane` lets a caller pass a lane index the compiler cannot hoist.)
+__device__ __forceinline__ bf16x8 ident_frag(int parity, int lane)
 {
-    const int r = lane_r(), g = lane_g();
+    const int r = lane & 15, g = (lane >> 4) & 3;
     bf16x8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (bf16)((8 * g + j == 16 * parity + r) ? 1.f : 0.f);
     return v;
 }
+__device__ __forceinline__ bf16x8 ident_frag(int parity) { return ident_frag(parity, lane_id()); }
 
 // The same identity for an A operand in frag (pik) k order, e.g. one
 // assembled from accumulator tiles: slot j is 1 where pik(g, j) is the
 // output column.
-__device__ __forceinline__ bf16x8 ident_pi(int parity)
+__device__ __forceinline__ bf16x8 ident_pi(int parity, int lane)
 {
-    const int r = lane_r(), g = lane_g();
+    const int r = lane & 15, g = (lane >> 4) & 3;
     bf16x8 v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (bf16)((pik(g, j) == 16 * parity + r) ? 1.f : 0.f);
     return v;
 }
+__device__ __forceinline__ bf16x8 ident_pi(int parity) { return ident_pi(parity, lane_id()); }
 
 __device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi)
 {

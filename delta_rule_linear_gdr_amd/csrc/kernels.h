@@ -128,21 +128,31 @@ __host__ __device__ inline int64_t seq_tok0(const Shape& s, const SeqView& v, in
     return (v.tok + c * CH) * s.H + v.hd;
 }
 
-// The chunk of a per-chunk workgroup (blockIdx.x = chunk or chunk slot,
-// blockIdx.y = b * H + head); false for an unused slot of a packed batch.
-__device__ inline bool chunk_of_block(const Shape& s, SeqView& v, int64_t& c)
+// The chunk at (x = chunk or chunk slot, y = b * H + head); false for an
+// unused slot of a packed batch.
+__device__ inline bool chunk_at(const Shape& s, int64_t x, int64_t y, SeqView& v, int64_t& c)
 {
     if (s.ctab) {
-        const int2 e = s.ctab[blockIdx.x];
+        const int2 e = s.ctab[x];
         if (e.x < 0) return false;
-        v = seq_view(s, e.x, blockIdx.y);
+        v = seq_view(s, e.x, y);
         c = e.y;
     } else {
-        v = seq_view(s, blockIdx.y / s.H, blockIdx.y % s.H);
-        c = blockIdx.x;
+        v = seq_view(s, y / s.H, y % s.H);
+        c = x;
     }
     return true;
 }
+
+// The chunk of a per-chunk workgroup (blockIdx.x = chunk or chunk slot,
+// blockIdx.y = b * H + head).
+__device__ inline bool chunk_of_block(const Shape& s, SeqView& v, int64_t& c)
+{
+    return chunk_at(s, blockIdx.x, blockIdx.y, v, c);
+}
+
+// Compute units of the current device (cached per device).
+int cu_count();
 
 struct Inputs {
     const void *q, *k, *v, *beta, *dO;

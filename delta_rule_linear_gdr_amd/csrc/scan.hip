@@ -415,7 +415,8 @@ __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter
     }
 }
 
-// Compute units of the current device (cached per device).
+}  // namespace
+
 int cu_count()
 {
     static std::atomic<int> cache[64];
@@ -431,6 +432,8 @@ int cu_count()
     if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
+
+namespace {
 
 // One workgroup per CU fits (LDS); NV = 2 when NV = 1 would need more than
 // one round of workgroups.
