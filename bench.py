@@ -55,8 +55,9 @@ def kernel_work(gate: str) -> dict:
     beta = CH * 2
     inputs4 = 4 * T16
     return {
-        # reads q, k, v, dO, g, beta; writes -W, Kt^T, U, Kt, -W^T, X, Y, A^T, A, gn
-        "prep": (inputs4 + g_bytes + beta + 6 * T16 + T32 + 2 * T8 + GN,
+        # recompute backward: reads q, k, v, dO, g, beta; writes -W, Kt^T, U, Kt,
+        # -W^T, X, Y, A^T, gn (and A, 8 KiB more, for the seven-product backward)
+        "prep": (inputs4 + g_bytes + beta + 6 * T16 + T32 + T8 + GN,
                  int(1.0 * M + 1.0 * M + 0.09 * M + 2 * M + 1 * M + 2 * M)),
         # reads -W, Kt^T, U, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
         "scan_fwd": (3 * T16 + GN + T32 + T16, 4 * M),

@@ -362,7 +362,9 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     if (policy == GDR_RECOMPUTE) {
         e = timed(ST_PREP, st, [&] {
-            return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A | PREP_AF, st);
+            // A itself (besides A^T) only for the seven-product producer
+            return launch_prep(s, in, it, PREP_FWDSCAN | PREP_BWDSCAN | PREP_XY | PREP_A | (wy7 ? PREP_AF : 0),
+                               st);
         });
         if (e != hipSuccess) return hip_fail(e, "prep");
         e = timed(ST_SCAN_PAIR, st, [&] { return launch_scan_pair(s, in, it, dh0, st); });
