@@ -111,13 +111,26 @@ __device__ __forceinline__ void stage_hdh(const Inter& it, int64_t tt, int w, bf
 // vmcnt(PF_WAIT) with PF_WAIT < 32 leaves none of them outstanding.
 constexpr int PF_WAIT = 8;
 
+// The last phase of a chunk (the dbeta and dg reductions over the eight
+// waves' partials) as the persistent form defers it: run by the next chunk
+// once its reads are issued, so that it overlaps their latency.
+template <typename T>
+struct Tail {
+    T* dbo;
+    float* dgo;
+    int nv;
+    bool on;
+};
+
 // One (chunk, head). PF: h and dh come from this wave's staging area
 // `area` (already requested), and the next chunk's (tile tnext >= 0) are
-// requested once they have been read.
+// requested once they have been read; the previous chunk's deferred last
+// phase (*pend) runs after this chunk's reads are issued, and this chunk's
+// is left in *pend when a next chunk follows.
 template <typename T, bool VEC, bool WY7, bool PF>
 __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in, const Inter& it,
                                                 const Grads& gr, const SeqView& sv, int64_t c,
-                                                int64_t tnext, bf16x4* area)
+                                                int64_t tnext, bf16x4* area, Tail<T>* pend)
 {
     const int64_t t = seq_tile(s, sv, c);
     const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
@@ -264,6 +277,32 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         qr[m] = rv[m] ? xq : R8{};
     }
     __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. (defined here, run last or deferred) dbeta (wave 1); scalar
+    //      gate: dg (wave 0), side by side, from the partials in LDS ----
+    auto sum8 = [](const float* p) {
+        const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+        return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
+    };
+    auto last_phase = [&](T* dbo_, float* dgo_, int nv_) {
+        if (w == 1) {
+            const float sb = sum8(sRedB[l]) + sum8(sRedP[l]);
+            if (l < nv_) io<T>::st(dbo_ + l * Hs, sb);
+        }
+        if (!VEC && w == 0) {
+            // sum the extra over features, then reverse cumsum over tokens
+            float xg = sum8(sRedG[l]);
+            if (l == CH - 1) xg += sum8(sEx);
+            xg = wave_incl_suffix(xg);
+            if (l < nv_) dgo_[l * Hs] = xg;
+        }
+    };
+    if (PF && pend->on) {
+        // the previous chunk's: its partials stay untouched until this
+        // chunk's first barrier, which waves 0 and 1 reach only afterwards
+        last_phase(pend->dbo, pend->dgo, pend->nv);
+        pend->on = false;
+    }
 
     // ---- 0. gates, beta; zero the consumer operand buffers ----
     float Gv[4][4];  // vector gate: G at (tok 16 it + 4 g + e, f)
@@ -870,21 +909,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         if (l == 0) sEx[w] = ex;
     }
     lds_barrier();
-    auto sum8 = [](const float* p) {
-        const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-        return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
-    };
-    if (w == 1) {
-        const float sb = sum8(sRedB[l]) + sum8(sRedP[l]);
-        if (l < nv) io<T>::st(dbo + l * Hs, sb);
-    }
-    if (!VEC && w == 0) {
-        // sum the extra over features, then reverse cumsum over tokens
-        float xg = sum8(sRedG[l]);
-        if (l == CH - 1) xg += sum8(sEx);
-        xg = wave_incl_suffix(xg);
-        if (l < nv) dgo[l * Hs] = xg;
-    }
+    if (PF && tnext >= 0) *pend = Tail<T>{dbo, dgo, nv, true};
+    else last_phase(dbo, dgo, nv);
 }
 
 template <typename T, bool VEC, bool WY7>
@@ -893,7 +919,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     SeqView sv;
     int64_t c;
     if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
-    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, sv, c, -1, nullptr);
+    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, sv, c, -1, nullptr, nullptr);
 }
 
 // Persistent form (scalar gate, three-product producer): workgroup b takes
@@ -916,13 +942,14 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
     while (i < n && !chunk_at(s, i % s.NC, i / s.NC, sv, c)) i += G;
     if (i >= n) return;
     stage_hdh(it, seq_tile(s, sv, c), w, sStage[w]);
+    Tail<T> pend{nullptr, nullptr, 0, false};
     for (;;) {
         SeqView sn;
         int64_t cn = 0;
         int64_t j = i + G;
         while (j < n && !chunk_at(s, j % s.NC, j / s.NC, sn, cn)) j += G;
         bwd_local_chunk<T, false, false, true>(s, in, it, gr, sv, c, j < n ? seq_tile(s, sn, cn) : -1,
-                                               sStage[w]);
+                                               sStage[w], &pend);
         if (j >= n) break;
         i = j;
         sv = sn;

@@ -96,8 +96,9 @@ unsigned scan_grid(const Shape& s, int nvs, int ndir)
 //
 // Synchronisation uses the two per-step barriers of the step itself:
 // slot p % 3 is read by the compute waves in step p; the loaders refill it
-// for step p + 3 after the first barrier of step p + 1, and wait for step
-// p + 1's blocks before the first barrier of step p + 1.
+// for step p + 3 after the first barrier (forward launch) or the second
+// (backward launches) of step p + 1, and wait for step p + 1's blocks
+// before the first barrier of step p + 1.
 template <int NV>
 struct Fed {
     static constexpr int A1 = 0;                   // 16 frag tiles of A1
@@ -189,8 +190,11 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
         wait_vm<NL>();  // step 0 has landed
         for (int p = 0; p < NT; ++p) {
             bar();  // first barrier of step p: slot (p + 2) % 3 is free
-            issue(p + 2);
+            // Step p + 2's blocks are requested only after the second barrier:
+            // a loader held up issuing them would otherwise hold the compute
+            // waves at that barrier (measured ~1.5% slower).
             bar();  // second barrier of step p
+            issue(p + 2);
             wait_vm<NL>();  // step p + 1 has landed
         }
     } else {
