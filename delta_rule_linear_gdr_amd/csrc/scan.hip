@@ -99,19 +99,23 @@ unsigned scan_grid(const Shape& s, int nvs, int ndir)
 // for step p + 3 after the first barrier (forward launch) or the second
 // (backward launches) of step p + 1, and wait for step p + 1's blocks
 // before the first barrier of step p + 1.
-template <int NV>
+//
+// DEEP (backward launches with NV = 1): four slots, the blocks requested
+// three steps ahead instead of two. A step's reads take longer to arrive
+// than two steps of compute when every CU streams at once, and the fourth
+// slot just fits: 4 x 39,424 B of ring + 6 KiB of exchange = 160 KiB.
+template <int NV, bool DEEP = false>
 struct Fed {
     static constexpr int A1 = 0;                   // 16 frag tiles of A1
     static constexpr int A2 = 16384;               // 16 frag tiles of A2
     static constexpr int C1 = 32768;               // 4 NV ctiles of C1 (value tiles NV vs ..)
     static constexpr int C2 = C1 + NV * 2048;      // 8 NV ctiles of C2 (reverse)
-    static constexpr int GN = C2 + NV * 4096;      // gn (512 B, twice)
-    static constexpr int SLOT = GN + 1024;
-    static constexpr int NSLOT = 3;
-    static constexpr int NB_FWD = 32 + 2 * NV + 1;  // 1 KiB blocks per step
+    static constexpr int GN = C2 + NV * 4096;      // gn (512 B)
+    static constexpr int SLOT = GN + 512;
+    static constexpr int NSLOT = DEEP ? 4 : 3;
+    static constexpr int DEPTH = NSLOT - 1;         // steps requested ahead
+    static constexpr int NB_FWD = 32 + 2 * NV + 1;  // blocks per step (the last is gn)
     static constexpr int NB_BWD = 32 + 6 * NV + 1;
-    static constexpr int NL_FWD = (NB_FWD + 3) / 4;  // per loader wave (padded)
-    static constexpr int NL_BWD = (NB_BWD + 3) / 4;
     static constexpr int XCH = NV * 6;              // LDS exchange: NV x (4 state + 2 Z) slabs
 };
 
@@ -130,11 +134,11 @@ __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); 
 
 // Loader wave J (0..3): blocks J, J + 4, ... of one step into `slot`. The
 // block count is padded to a multiple of four by repeating the gn block
-// (same bytes to the same place).
-template <bool BWD, int J, int NV>
+// (same bytes to the same place); a gn block is two copies (fed_loads).
+template <bool BWD, int J, int NV, bool DEEP>
 __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, uint8_t* slot)
 {
-    using L = Fed<NV>;
+    using L = Fed<NV, DEEP>;
     constexpr int NB = BWD ? L::NB_BWD : L::NB_FWD;
     constexpr int NPAD = (NB + 3) / 4 * 4;
     constexpr int E1 = 32 + 2 * NV, E2 = E1 + 4 * NV;  // ends of the C1 and C2 blocks
@@ -165,37 +169,55 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
             src = it.Y + t * (DKD * DVD) + vs * NV * 2048 + (b - E1) * 512 + l * 8;
             dst = L::C2 + (b - E1) * 1024;
         } else {
-            src = it.gn + t * DKD + (l & 31) * 4;
-            dst = L::GN;
+            // gn, 512 B: two 4-byte-per-lane copies (lane L lands at 4 L)
+            const float* gs = it.gn + t * DKD + l;
+            __builtin_amdgcn_global_load_lds(gs, (__attribute__((address_space(3))) void*)(slot + L::GN), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(gs + 64, (__attribute__((address_space(3))) void*)(slot + L::GN + 256),
+                                             4, 0, 0);
+            continue;
         }
         lds_dma16(src, slot + dst);
     }
+}
+
+// Direct-to-LDS copies loader wave J issues per step: one per block, two
+// per gn block (the last block and the padding repeats of it).
+template <bool BWD, int J, int NV>
+constexpr int fed_loads()
+{
+    constexpr int E = BWD ? 32 + 6 * NV : 32 + 2 * NV;  // blocks before gn
+    constexpr int NPAD = (E + 1 + 3) / 4 * 4;
+    int n = 0;
+    for (int b = J; b < NPAD; b += 4) n += b < E ? 1 : 2;
+    return n;
 }
 
 template <bool BWD, int J, int NV, bool OUT, typename T>
 __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, const SeqView& sq, int vs,
                                            uint8_t* ring, bf16x8 (*xs)[64], T* o)
 {
-    using L = Fed<NV>;
-    constexpr int NL = BWD ? L::NL_BWD : L::NL_FWD;
+    constexpr bool DEEP = NV == 1 && !OUT;
+    using L = Fed<NV, DEEP>;
+    constexpr int NL = fed_loads<BWD, J, NV>();
     const int NT = (int)sq.nchunk;  // >= 1
     auto issue = [&](int p) {
         const int pc = p < NT ? p : NT - 1;  // past the end: the last chunk again
         const int c = BWD ? NT - 1 - pc : pc;
-        fed_issue<BWD, J, NV>(it, seq_tile(s, sq, c), vs, ring + (p % L::NSLOT) * L::SLOT);
+        fed_issue<BWD, J, NV, DEEP>(it, seq_tile(s, sq, c), vs, ring + (p % L::NSLOT) * L::SLOT);
     };
     if constexpr (!OUT) {
-        issue(0);
-        issue(1);
-        wait_vm<NL>();  // step 0 has landed
+        constexpr int D = L::DEPTH;
+#pragma unroll
+        for (int q = 0; q < D; ++q) issue(q);
+        wait_vm<(D - 1) * NL>();  // step 0 has landed
         for (int p = 0; p < NT; ++p) {
-            bar();  // first barrier of step p: slot (p + 2) % 3 is free
-            // Step p + 2's blocks are requested only after the second barrier:
+            bar();  // first barrier of step p: slot (p + D) % NSLOT is free
+            // Step p + D's blocks are requested only after the second barrier:
             // a loader held up issuing them would otherwise hold the compute
             // waves at that barrier (measured ~1.5% slower).
             bar();  // second barrier of step p
-            issue(p + 2);
-            wait_vm<NL>();  // step p + 1 has landed
+            issue(p + D);
+            wait_vm<(D - 1) * NL>();  // step p + 1 has landed (younger: steps p + 2 .. p + D)
         }
     } else {
         // Forward with output: this wave also forms output rows 16 J .. 16 J + 15
@@ -275,12 +297,12 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
 
 // xs: the LDS exchange, NV x 4 state slabs then NV x 2 Z slabs of 64 x 16 B.
 // STORE: write the state before each step and Z (h, R or dh, Rb).
-template <bool BWD, int NV, bool STORE>
+template <bool BWD, int NV, bool STORE, bool DEEP>
 __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, const Inter& it, float* fin,
                                             const SeqView& sq, int64_t bh, int vs, const uint8_t* ring,
                                             bf16x8 (*xs)[64])
 {
-    using L = Fed<NV>;
+    using L = Fed<NV, DEEP>;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = lane_id(), r = lane_r(), g = lane_g();
     const int NT = (int)sq.nchunk;  // 0 for an empty sequence: the state passes through
@@ -394,7 +416,9 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
     case 5: fed_loader<BWD, 1, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
     case 6: fed_loader<BWD, 2, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
     case 7: fed_loader<BWD, 3, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
-    default: fed_compute<BWD, NV, STORE>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs); break;
+    default:
+        fed_compute<BWD, NV, STORE, NV == 1 && !OUT>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs);
+        break;
     }
 }
 
@@ -406,7 +430,7 @@ __device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const
 template <int NV, bool OUT, typename T, bool STORE>
 __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* fin, int ndir, T* o)
 {
-    using L = Fed<NV>;
+    using L = Fed<NV, NV == 1 && !OUT>;
     __shared__ __attribute__((aligned(16))) uint8_t ring[L::NSLOT * L::SLOT];
     __shared__ bf16x8 xs[L::XCH][64];
     Chain ch;
