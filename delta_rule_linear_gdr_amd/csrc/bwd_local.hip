@@ -240,7 +240,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     bf16x4 rbq[4], rq[4], hq[8], dhq[8];
     bf16x8 atf[6];  // A^T frags m * 2 + 1 (m = 0..3), then m * 2 + 0 (m = 0, 1)
     R4 vr[4], orw[4];
-    R8 kr[4], qr[4];
+    R4 kr[4], qr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) rbq[i] = *(const bf16x4*)ctile_ptr(Rbg, w * 4 + i);
 #pragma unroll
@@ -271,10 +271,11 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const R8 xk = ld8raw(k + rowc(m) * ld + 32 * (w >> 1) + 8 * g);
-        const R8 xq = ld8raw(q + rowc(m) * ld + 32 * (w >> 1) + 8 * g);
-        kr[m] = rv[m] ? xk : R8{};
-        qr[m] = rv[m] ? xq : R8{};
+        // this wave's 16 keys only (as for v): lane (r, g) gets keys 16 w + 4 g .. + 3
+        const R4 xk = ld4raw(k + rowc(m) * ld + 16 * w + 4 * g);
+        const R4 xq = ld4raw(q + rowc(m) * ld + 16 * w + 4 * g);
+        kr[m] = rv[m] ? xk : R4{};
+        qr[m] = rv[m] ? xq : R4{};
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -395,8 +396,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : Gs[VEC ? 0 : m][e]; };
     auto Bt = [&](int m, int e) -> float { return VEC ? sBeta[16 * m + 4 * g + e] : Bs[VEC ? 0 : m][e]; };
 
-    const bf16x8 I0 = ident_frag(0, lx), I1 = ident_frag(1, lx);
-    const bf16x8 Iw = (w & 1) ? I1 : I0;
+    const bf16x8 Ip0k = ident_pi(0, lx);
     const bf16x8 Ipw = ident_pi(w & 1, lx);
     const bf16x4 z4 = {};
 
@@ -493,8 +493,11 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     f32x4 KC[4], QC[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        KC[m] = mfma(tobf8(kr[m]), Iw, zero4());
-        QC[m] = mfma(tobf8(qr[m]), Iw, zero4());
+        // the four keys in slots 0..3 are k slots pik(g, 0..3) = 4 g .. 4 g + 3
+        // of a 32-wide slab whose upper 16 are zero; the identity in the same
+        // pik order maps slot column c < 16 to output column c
+        KC[m] = mfma(cat8(tobf4(kr[m]), z4), Ip0k, zero4());
+        QC[m] = mfma(cat8(tobf4(qr[m]), z4), Ip0k, zero4());
     }
     // Next chunk's h, dh: requested only now, after the last use of this
     // chunk's reads, so that no wait the compiler places for those reads
