@@ -159,6 +159,19 @@ def test_ragged_tail(gate):
             _report(f"ragged/{gate}/T={T}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_ragged_chunk_late_in_a_persistent_walk(dtype):
+    """(1, 8292, 2): 130 chunks x 2 heads = 260 (chunk, head) items, more
+    than one per workgroup of a one-per-CU launch, unevenly: head 1's ragged
+    last chunk (100 rows) is a later item of its workgroup, after a prefetch
+    and with the previous item's deferred reductions pending. Head 1 is
+    compared in full."""
+    _need_gpu()
+    x = make_inputs(1, 8292, 2, gate="scalar", dtype=dtype, seed=13, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"persistent-ragged/{dtype}/{pol}", tl.compare(tl.run_gpu(x, pol), x, heads=[(0, 1)]))
+
+
 def test_ragged_tail_fp32():
     _need_gpu()
     x = make_inputs(2, 100, 3, gate="scalar", dtype="fp32", seed=12, gate_mean=4.0, h0_std=0.1)
