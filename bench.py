@@ -42,9 +42,37 @@ T16, T32, T8, GN = 16384, 32768, 8192, 512   # bf16 64x128, 128x128, 64x64 tiles
 M = 1048576                                   # 2 * 64 * 64 * 128 FLOPs
 
 # Whole-path algorithmic bytes per token-head of the operator's inputs and
-# outputs (GDN, recompute backward): q, k, v, dO read and dq, dk, dv written
-# in bf16, g, beta, dg, dbeta.
-PATH_BYTES_PER_TOKEN_HEAD = {"gdn_bwd_R": 1804, "kda_bwd_R": 2820}
+# outputs at bf16: forward reads q, k, v, g, beta and writes o; backward
+# reads q, k, v, dO, g, beta and writes dq, dk, dv, dg, dbeta; the full-save
+# forward writes, and its backward reads, the 1152-byte saved area (A, W,
+# per-chunk state, R). The gate is 4 bytes (scalar) or 512 (vector) per
+# token-head, its gradient the same.
+PATH_BYTES_PER_TOKEN_HEAD = {
+    ("scalar", "fwd_R"): 1030, ("scalar", "fwd_A"): 2182,
+    ("scalar", "bwd_R"): 1804, ("scalar", "bwd_A"): 2956,
+    ("vector", "fwd_R"): 1538, ("vector", "fwd_A"): 2690,
+    ("vector", "bwd_R"): 2820, ("vector", "bwd_A"): 3972,
+}
+# 128 x 128 fp32 state tensors a call touches per head: h0 and ht (forward);
+# h0 and dh0 (recompute backward, dht absent); dh0 (full-save backward)
+PATH_STATES = {"fwd_R": 2, "fwd_A": 2, "bwd_R": 2, "bwd_A": 1}
+# Algorithmic FLOPs per (chunk, head): the dense products of each call
+# (2mnk), the same for both gates at d_k = d_v = 128
+PATH_FLOPS_PER_CHUNK_HEAD = {"fwd_R": 11621717, "fwd_A": 11621717,
+                             "bwd_R": 29447509, "bwd_A": 22020096}
+
+
+def path_figures(gate: str, kind: str, B: int, T: int, H: int, ms: float) -> dict:
+    """Whole-call throughput against both rooflines: achieved TFLOP/s as a
+    fraction of the bf16 MFMA peak, algorithmic GB/s as a fraction of the
+    HBM peak, and the fraction of the binding one, max(t_MFMA, t_HBM) / t."""
+    flops = PATH_FLOPS_PER_CHUNK_HEAD[kind] * B * H * ((T + CH - 1) // CH)
+    nbytes = PATH_BYTES_PER_TOKEN_HEAD[(gate, kind)] * B * T * H + PATH_STATES[kind] * 65536 * B * H
+    t = ms * 1e-3
+    tfs, gbs = flops / t / 1e12, nbytes / t / 1e9
+    return {"TFLOP/s": round(tfs, 2), "frac_mfma": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "bytes": nbytes, "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "frac_roofline": round(max(tfs / MFMA_BF16_PEAK_TFS, gbs / HBM_PEAK_GBS), 4)}
 
 
 def kernel_work(gate: str) -> dict:
@@ -144,7 +172,11 @@ def shape_sweep(gdr, to_dev, make_runner, time_steps, graph_ms, args):
             row.update(bwd_R_ms=round(msR, 4), bwd_R_graph_ms=round(msRg, 4), bwd_A_ms=round(msA, 4),
                        fwd_R_ms=round(msF, 4),
                        bwd_R_tokens_per_s=round(Bs * Ts / (msR * 1e-3), 1),
-                       bwd_A_tokens_per_s=round(Bs * Ts / (msA * 1e-3), 1))
+                       bwd_A_tokens_per_s=round(Bs * Ts / (msA * 1e-3), 1),
+                       fwd_R_tokens_per_s=round(Bs * Ts / (msF * 1e-3), 1),
+                       bwd_R_roofline=path_figures(gate, "bwd_R", Bs, Ts, Hs, msR),
+                       bwd_A_roofline=path_figures(gate, "bwd_A", Bs, Ts, Hs, msA),
+                       fwd_R_roofline=path_figures(gate, "fwd_R", Bs, Ts, Hs, msF))
             rows.append(row)
             print(f"[bench] sweep {row}", file=sys.stderr, flush=True)
             del ds, xs, saved, scr
@@ -275,14 +307,11 @@ def main():
     roof["algorithmic_bytes_per_launch"] = by * units
     steps_bwd = ("prep", "scan_pair", "bwd_local")
     bwd_flops = sum(work[k][1] for k in steps_bwd) * units
-    path_bytes = PATH_BYTES_PER_TOKEN_HEAD["gdn_bwd_R"] * B * T * H
     tok_s = B * T / (ms * 1e-3)
     detail = {
         "bwd_R_ms": round(ms, 4),
         "bwd_R_tflops": round(bwd_flops / (ms * 1e-3) / 1e12, 2),
-        "path_roofline": {"bytes": path_bytes,
-                          "GB/s": round(path_bytes / (ms * 1e-3) / 1e9, 1),
-                          "frac_hbm": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "path_roofline": path_figures("scalar", "bwd_R", B, T, H, ms),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "per_stage_roofline": {},
     }
@@ -306,6 +335,7 @@ def main():
         fms = time_steps(fwd, args.steps, args.warmup)
         detail["fwd_R_ms"] = round(fms, 4)
         detail["fwd_R_tokens_per_s"] = round(B * T / (fms * 1e-3), 1)
+        detail["fwd_R_roofline"] = path_figures("scalar", "fwd_R", B, T, H, fms)
         del scr
         # full-save policy: forward saves, backward reuses
         _, _, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
@@ -314,6 +344,7 @@ def main():
         msA = time_steps(runA, args.steps, args.warmup)
         detail["bwd_A_ms"] = round(msA, 4)
         detail["bwd_A_tokens_per_s"] = round(B * T / (msA * 1e-3), 1)
+        detail["bwd_A_roofline"] = path_figures("scalar", "bwd_A", B, T, H, msA)
         # seven-product ablation, both policies
         run7 = make_runner(d, gdr.gdr_bwd_wy7, "recompute")
         ms7 = time_steps(run7, args.steps, args.warmup)
@@ -334,10 +365,9 @@ def main():
         dk_ = to_dev(xk)
         runK = make_runner(dk_, gdr.gdr_bwd, "recompute")
         msK = time_steps(runK, args.steps, args.warmup)
-        kpath = PATH_BYTES_PER_TOKEN_HEAD["kda_bwd_R"] * B * T * H
         detail["kda_bwd_R_ms"] = round(msK, 4)
         detail["kda_bwd_R_tokens_per_s"] = round(B * T / (msK * 1e-3), 1)
-        detail["kda_path_frac_hbm"] = round(kpath / (msK * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        detail["kda_bwd_R_roofline"] = path_figures("vector", "bwd_R", B, T, H, msK)
         detail["kda_stage_ms"] = {k: round(v, 4) for k, v in profiled(runK, args.steps).items()}
         # the same workload end to end: recompute forward (output and final
         # state) followed by the recompute backward, one step per call pair
