@@ -20,13 +20,16 @@
 //     Q' = alpha Q, E' = beta alpha K);
 //     dq += alpha U_q, dk += beta alpha U_e + zeta U_y,
 //     dbeta += <U_e, alpha k>, Gbar += Q' U_q + E' U_e - Y' U_y
-//     applied per 32-token window (the token slab of one contraction): the
-//     products within a window use its centre c = (max G + min G)/2; the
-//     block of window 1's rows against window 0's columns uses a boundary
-//     pivot (G at token 31 for Hb Y' and D Y', at token 32 for Hb^T Q' and
-//     D^T E'), so that both of its factors are at most 1 for decays g <= 0.
-//     The factors then span exp(+-range of 32 tokens / 2) rather than that
-//     of the chunk, which keeps strong decays within fp32 range.
+//     applied per 16-token window (one token tile): the products within a
+//     window use its centre c = (max G + min G)/2; every block of a row
+//     tile m against another window's columns uses a boundary pivot (G at
+//     token 16 m - 1 for the earlier windows, in Hb Y' and D Y'; G at token
+//     16 m + 16 for the later ones, in Hb^T Q' and D^T E'), so that both of
+//     its factors are at most 1 for decays g <= 0. The factors then span
+//     exp(+-range of 16 tokens / 2) rather than that of the chunk, which
+//     keeps strong decays within fp32 range. A 32-token contraction slab
+//     that holds two windows with different factors is split into its two
+//     16-token halves (K = 16 products).
 // Feature-local chain rules for the remaining terms, with gam = exp(G):
 //   dq += gam Qgb;  dk += beta gam Eb_dir + exp(G_n - G) Ktb;
 //   dbeta += <P, v> + <Eb_dir, gam k>   (undivided form, App. B.3)
@@ -307,9 +310,11 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 
     // ---- 0. gates, beta; zero the consumer operand buffers ----
     float Gv[4][4];  // vector gate: G at (tok 16 it + 4 g + e, f)
-    // vector gate, key f: window centres and G at tokens 31 and 32
-    // (kept in LDS, read where used: registers are the scarce resource)
-    __shared__ float sWin[VEC ? 4 : 1][DKD];
+    // vector gate, key f: rows 0..3 the centres of the four 16-token windows,
+    // rows 4..6 G at tokens 15, 31, 47 and rows 7..9 G at tokens 16, 32, 48
+    // (the boundary pivots; kept in LDS, read where used: registers are the
+    // scarce resource)
+    __shared__ float sWin[VEC ? 10 : 1][DKD];
     float Gnf;
     if (w == 0) sBeta[l] = to_f32(braw);
     if (VEC) {
@@ -318,7 +323,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[m][e] = graw[VEC ? 4 * m + e : 0];
-        float base = 0.f, mx[2] = {-INFINITY, -INFINITY}, mn[2] = {INFINITY, INFINITY};
+        float base = 0.f, mx[4], mn[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -329,11 +334,13 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             const float pair = tot + p16;
             const float p32 = partner32(pair);
             const float excl = ((g & 1) ? p16 : 0.f) + ((g & 2) ? p32 : 0.f);
+            mx[m] = -INFINITY;
+            mn[m] = INFINITY;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 Gv[m][e] = x[m][e] + excl + base;
-                mx[m >> 1] = fmaxf(mx[m >> 1], Gv[m][e]);
-                mn[m >> 1] = fminf(mn[m >> 1], Gv[m][e]);
+                mx[m] = fmaxf(mx[m], Gv[m][e]);
+                mn[m] = fminf(mn[m], Gv[m][e]);
             }
             base += pair + p32;
         }
@@ -344,10 +351,13 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             const float pb = partner32(b1);
             Gnf = (g & 2) ? b1 : pb;
         }
-        if (g == 3) sWin[VEC ? 2 : 0][f] = Gv[1][3];  // G at token 31
-        if (g == 0) sWin[VEC ? 3 : 0][f] = Gv[2][0];  // G at token 32
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int m = 0; m < 3; ++m) {
+            if (g == 3) sWin[VEC ? 4 + m : 0][f] = Gv[m][3];      // G at token 16 m + 15
+            if (g == 0) sWin[VEC ? 7 + m : 0][f] = Gv[m + 1][0];  // G at token 16 m + 16
+        }
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
             const float x16 = partner16(mx[h]);
             mx[h] = fmaxf(mx[h], x16);
             const float x32 = partner32(mx[h]);
@@ -358,8 +368,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             mn[h] = fminf(mn[h], n32);
         }
         if (g == 0) {
-            sWin[0][f] = 0.5f * (mx[0] + mn[0]);  // window centres
-            sWin[VEC ? 1 : 0][f] = 0.5f * (mx[1] + mn[1]);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) sWin[VEC ? h : 0][f] = 0.5f * (mx[h] + mn[h]);  // window centres
         }
     } else if (w == 0) {
         sG[l] = wave_incl_scan(graw[0]);
@@ -371,8 +381,12 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     }
     lds_barrier();
     if (!VEC) Gnf = sG[CH - 1];
-    // vector gate, this lane's key: centre of window 0 / 1, G at tokens 31 / 32
-    auto win = [&](int x) -> float { return VEC ? sWin[VEC ? x : 0][f] : 0.f; };
+    // vector gate, this lane's key: the centre of window m (token tile m);
+    // the pivot of row tile m's blocks against earlier windows (G at token
+    // 16 m - 1, m >= 1) and against later ones (G at token 16 m + 16, m <= 2)
+    auto cen = [&](int m) -> float { return VEC ? sWin[VEC ? m : 0][f] : 0.f; };
+    auto piv_lo = [&](int m) -> float { return VEC ? sWin[VEC ? 3 + m : 0][f] : 0.f; };
+    auto piv_up = [&](int m) -> float { return VEC ? sWin[VEC ? 7 + m : 0][f] : 0.f; };
     // G at this lane's accumulator position (tok 16 m + 4 g + e, f)
     // G and beta at this lane's accumulator rows (tok 16 m + 4 g + e), read
     // once as 16-byte vectors (the scalar gate's G lives in LDS)
@@ -533,8 +547,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             st_half(lE, m * 4 + (w >> 1), w & 1, pack4(cc));
         }
     }
-    // Consumer B operands (this wave's key tile, K = tokens; token slab ks is
-    // window ks, centred at its own centre). Vector gate: the centred factors
+    // Consumer B operands (this wave's key tile, K = tokens; token tile m
+    // centred at the centre of its window m). Vector gate: the centred factors
     // span exp(+-range/2), and the Gbar terms built from them cancel to far
     // below their size (the diagonal of Hb enters Q'U_q and Y'U_y with
     // opposite signs), so Y', Q', E' are carried as bf16 hi + lo pairs; a
@@ -549,7 +563,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                 const int m = 2 * ks + hh;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float d = Gt(m, e) - win(ks);
+                    const float d = Gt(m, e) - cen(m);
                     const float al = __expf(d), ze = __expf(-d);
                     y[hh][e] = ze * KC[m][e];
                     qq[hh][e] = al * QC[m][e];
@@ -708,7 +722,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         for (int e = 0; e < 4; ++e) {
             const int ks = m >> 1, sl = 4 * (m & 1) + e;
             float kv = (float)B0[ks][sl];
-            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - win(ks));
+            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - cen(m));
             colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
         }
     }
@@ -742,49 +756,76 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         // lower operands (Gam, Gq: K index <= M index) skip slab 1 for m < 2;
         // upper operands (Gam^T, Gq^T) skip slab 0 for m >= 2
         f32x4 X1 = zero4(), X2 = zero4(), X3 = zero4(), X4 = zero4();
-        // vector gate: the cross-window block, kept apart since its factors
-        // differ (m >= 2: D Y'x, Hb Y'x; m < 2: D^T E'x, Hb^T Q'x)
-        f32x4 Xa = zero4(), Xb = zero4();
+        // vector gate: the blocks against other windows, kept apart since their
+        // factors differ: Xa = D Y'x, Xb = Hb Y'x (earlier windows, m >= 1) and
+        // Xc = D^T E'x + Hb^T Q'x (later windows, m <= 2); X2 takes both
+        // window-centred upper products (they share the factor zeta)
+        f32x4 Xa = zero4(), Xb = zero4(), Xc = zero4();
         if constexpr (VEC) {
-            const int wm = m >> 1;  // window of this row tile
-            // cross operands from the window-centred ones by a per-key factor
-            // at most 1 in either case: exp(G31 - c0) = exp(-range0 / 2) and
-            // exp(c1 - G32) = exp(-range1 / 2) for decays. (The hi part alone:
-            // the cancellation that needs the lo part is on the diagonal,
-            // which no cross block holds.)
-            auto rescale = [&](const bf16x8& hi, float sc) -> bf16x8 {
-                float x[8];
+            // operands against another window from the window-centred ones by a
+            // per-key factor at most 1: exp(G[16 m - 1] - c_w) for a window w < m,
+            // exp(c_w - G[16 m + 16]) for w > m. (The hi part alone: the
+            // cancellation that needs the lo part is in the diagonal blocks.)
+            auto rescale4 = [&](const bf16x4& hi, float sc) -> bf16x4 {
+                bf16x4 y;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[j] = (float)hi[j] * sc;
-                return pack8(x);
+                for (int j = 0; j < 4; ++j) y[j] = (bf16)((float)hi[j] * sc);
+                return y;
+            };
+            auto rescale8 = [&](const bf16x8& hi, float s0, float s1) -> bf16x8 {
+                return cat8(rescale4(half0(hi), s0), rescale4(half1(hi), s1));
             };
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks == 0 || m >= 2) {
                     const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
-                    if (ks == wm) {
+                    if (ks == (m >> 1) && (m & 1) == 0) {
+                        // first half: window m; second half above the diagonal (zero in a1, a3)
                         const bf16x8 lo = lo_get(0 * 2 + ks);
                         X1 = mfma(a1, B0[ks], X1);  // D Y'
                         X3 = mfma(a3, B0[ks], X3);  // Hb Y'
                         X1 = mfma(a1, lo, X1);
                         X3 = mfma(a3, lo, X3);
+                    } else if (ks == (m >> 1)) {
+                        // first half: window m - 1; second half: window m
+                        const bf16x4 lo = half1(lo_get(0 * 2 + ks));
+                        X1 = mfma16(half1(a1), half1(B0[ks]), X1);
+                        X3 = mfma16(half1(a3), half1(B0[ks]), X3);
+                        X1 = mfma16(half1(a1), lo, X1);
+                        X3 = mfma16(half1(a3), lo, X3);
+                        const bf16x4 yx = rescale4(half0(B0[ks]), __expf(piv_lo(m) - cen(m - 1)));
+                        Xa = mfma16(half0(a1), yx, Xa);
+                        Xb = mfma16(half0(a3), yx, Xb);
                     } else {
-                        const bf16x8 yx = rescale(B0[0], __expf(win(2) - win(0)));
+                        // slab 0 for m >= 2: windows 0 and 1, both earlier
+                        const float p = piv_lo(m);
+                        const bf16x8 yx = rescale8(B0[0], __expf(p - cen(0)), __expf(p - cen(1)));
                         Xa = mfma(a1, yx, Xa);
                         Xb = mfma(a3, yx, Xb);
                     }
                 }
                 if (ks == 1 || m < 2) {
                     const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
-                    if (ks == wm) {
+                    if (ks == (m >> 1) && (m & 1) == 1) {
+                        // first half below the diagonal (zero in a2, a4); second half: window m
                         X2 = mfma(a2, B2[ks], X2);  // D^T E'
-                        X4 = mfma(a4, B1[ks], X4);  // Hb^T Q'
+                        X2 = mfma(a4, B1[ks], X2);  // Hb^T Q'
                         X2 = mfma(a2, lo_get(2 * 2 + ks), X2);
-                        X4 = mfma(a4, lo_get(1 * 2 + ks), X4);
+                        X2 = mfma(a4, lo_get(1 * 2 + ks), X2);
+                    } else if (ks == (m >> 1)) {
+                        // first half: window m; second half: window m + 1
+                        X2 = mfma16(half0(a2), half0(B2[ks]), X2);
+                        X2 = mfma16(half0(a4), half0(B1[ks]), X2);
+                        X2 = mfma16(half0(a2), half0(lo_get(2 * 2 + ks)), X2);
+                        X2 = mfma16(half0(a4), half0(lo_get(1 * 2 + ks)), X2);
+                        const float sc = __expf(cen(m + 1) - piv_up(m));
+                        Xc = mfma16(half1(a2), rescale4(half1(B2[ks]), sc), Xc);
+                        Xc = mfma16(half1(a4), rescale4(half1(B1[ks]), sc), Xc);
                     } else {
-                        const float sc = __expf(win(1) - win(3));
-                        Xa = mfma(a2, rescale(B2[1], sc), Xa);
-                        Xb = mfma(a4, rescale(B1[1], sc), Xb);
+                        // slab 1 for m < 2: windows 2 and 3, both later
+                        const float p = piv_up(m), s2 = __expf(cen(2) - p), s3 = __expf(cen(3) - p);
+                        Xc = mfma(a2, rescale8(B2[1], s2, s3), Xc);
+                        Xc = mfma(a4, rescale8(B1[1], s2, s3), Xc);
                     }
                 }
             }
@@ -815,7 +856,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             float kv = (float)B0[ks][sl], qv = (float)B1[ks][sl];
             float al = 1.f, ze = 1.f;
             if (VEC) {
-                const float d = G - win(ks);  // ks = m >> 1: this row's window
+                const float d = G - cen(m);  // this row's window
                 al = __expf(d);
                 ze = __expf(-d);
                 kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * al;
@@ -828,14 +869,13 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             Ga[e] = gam * qv * Qb[e] + bt * gam * kv * eb - kt * kv * Kb[e];
             if (VEC) {
                 // U_q, U_e, U_y with their factors applied
-                float uq = al * X3[e], ue = al * X1[e], uy = ze * (X2[e] + X4[e]);
-                if (m >= 2) {
-                    const float ax = __expf(G - win(2));
+                float uq = al * X3[e], ue = al * X1[e], uy = ze * X2[e];
+                if (m >= 1) {
+                    const float ax = __expf(G - piv_lo(m));
                     uq += ax * Xb[e];
                     ue += ax * Xa[e];
-                } else {
-                    uy += __expf(win(3) - G) * (Xa[e] + Xb[e]);
                 }
+                if (m <= 2) uy += __expf(piv_up(m) - G) * Xc[e];
                 dq += uq;
                 dk += bt * ue + uy;
                 br[e] += kv * ue;

@@ -32,6 +32,18 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// K = 16 product, v_mfma_f32_16x16x16_bf16: lane l holds A row (l & 15) (or B
+// column (l & 15)) at k = 4 (l >> 4) .. + 3; the accumulator layout is that of
+// the K = 32 product. Either half of a pik-ordered frag (below) is such an
+// operand: elements 0..3 carry k-slots 0..15 of the 32, elements 4..7 k-slots
+// 16..31, each in natural order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(bf16x4 a, bf16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                     c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
@@ -301,6 +313,9 @@ __device__ __forceinline__ bf16x8 cat8(const bf16x4& lo, const bf16x4& hi)
     }
     return v;
 }
+// The halves of a pik-ordered frag as K = 16 operands (k-slots 0..15 and 16..31).
+__device__ __forceinline__ bf16x4 half0(const bf16x8& v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
+__device__ __forceinline__ bf16x4 half1(const bf16x8& v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
 
 // Four consecutive elements of an input/output row.
 __device__ __forceinline__ void load4(const bf16* p, float (&x)[4])

@@ -61,11 +61,11 @@
  * here, its missing rows acting as identity steps (g = 0, beta = 0, zero
  * q, k, v, dO), which leaves every output, state and gradient of the real
  * tokens exact; workspaces count whole chunks. Vector gate: the centred
- * factors (Sec. 3.3) are formed per window of the chunk, with boundary pivots
- * between windows, so they span exp(+-range/2) of a 32-token half-chunk; g
- * must be a log decay (g <= 0) whose per-channel range over each 32-token
- * half of a chunk is at most 160 (e.g. every |g| <= 5); past that the
- * backward's results are non-finite, not finite and wrong. A launch failure
+ * factors (Sec. 3.3) are formed per 16-token window of the chunk, with
+ * boundary pivots between windows, so they span exp(+-range/2) of one
+ * window; g must be a log decay (g <= 0) whose per-channel range over each
+ * 16-token window is at most 160 (e.g. every |g| <= 10); past that the
+ * results are non-finite, not finite and wrong. A launch failure
  * returns GDR_ERR_HIP. gdr_last_error() returns a message for
  * the calling thread's last failure.
  */

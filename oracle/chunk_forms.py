@@ -44,8 +44,8 @@ Consumers of D and Hb:
              min G)/2 per feature, alpha = exp(G - c), zeta = exp(c - G),
              Q' = alpha Q, E' = beta alpha K, Y' = zeta K;
              U_q = Hb Y', U_e = D Y', U_y = Hb^T Q' + D^T E'.
-  "windowed" the centred factors applied per window of the chunk (32 tokens:
-             the token slab of one MFMA contraction) for a vector gate with
+  "windowed" the centred factors applied per window of the chunk (16 tokens
+             by default: one token tile of the device kernels) for a vector gate with
              strong decay: a block of two tokens in the same window uses that
              window's centre; the block of a later window's rows against an
              earlier window's columns uses a boundary pivot p (G at the last
@@ -137,7 +137,7 @@ def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
 
 
 def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="direct",
-                   flops: FlopCounter | None = None, centre=None, window=32):
+                   flops: FlopCounter | None = None, centre=None, window=16):
     """Chunkwise backward of one (b, h) sequence.
 
     producer: "rewy" (three products) or "wy7" (expanded graph).

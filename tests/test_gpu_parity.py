@@ -266,7 +266,7 @@ def test_packed_single_sequence_matches_regular_batch():
 def test_kda_strong_decay_windowed(dtype):
     """Per-key log decays around -4 per token (log-sigmoid of N(-4, 1)): a
     64-token chunk spans a range near 256, far past what chunk-wide centred
-    factors can hold in fp32, a 32-token window about 125. Both policies,
+    factors can hold in fp32, a 16-token window about 60. Both policies,
     the seven-product producer, nonzero states and a ragged last chunk."""
     _need_gpu()
     x = make_inputs(1, 300, 2, gate="vector", dtype=dtype, seed=31, gate_mean=-4.0,
@@ -277,13 +277,18 @@ def test_kda_strong_decay_windowed(dtype):
 
 
 @pytest.mark.gpu
-def test_kda_decay_at_the_window_limit():
-    """Every log decay -5 (a 32-token window spans 155, its factors reach
-    exp(77.5)): the edge of the vector gate's contract."""
+@pytest.mark.parametrize("decay", [-5.0, -8.0, -10.0])
+def test_kda_decay_up_to_the_window_limit(decay):
+    """Every log decay the same, up to -10 (a 16-token window spans 150, its
+    factors reach exp(75)): the edge of the vector gate's contract. At -5 and
+    -8 a 32-token window would span 155 and 248: past fp32 for the latter.
+    Both policies and the seven-product producer."""
     _need_gpu()
     x = make_inputs(1, 256, 2, gate="vector", dtype="bf16", seed=32, h0_std=0.1, dht_std=0.1)
-    x["g"] = np.full_like(x["g"], -5.0)
-    _report("kda_limit", tl.compare(tl.run_gpu(x), x))
+    x["g"] = np.full_like(x["g"], decay)
+    for pol in ("recompute", "full_save"):
+        _report(f"kda_limit/{decay}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+    _report(f"kda_limit/{decay}/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
 
 
 @pytest.mark.gpu
@@ -490,14 +495,13 @@ def test_graph_replay_matches_eager(policy, packed):
 
 @pytest.mark.gpu
 def test_out_of_contract_decay_fails_loudly():
-    """Every log decay -8 (a 32-token window spans 248, past the vector gate's
-    contract of 160): the backward's centred factors leave fp32, and its
-    gradients come out non-finite rather than finite and wrong. The forward's
-    16-token windows still hold (range 120): o and ht match the oracle."""
+    """Every log decay -12 (a 16-token window spans 180, past the vector
+    gate's contract of 160): the centred factors leave fp32 (exp(90)), and
+    the output and gradients come out non-finite rather than finite and
+    wrong."""
     _need_gpu()
     x = make_inputs(1, 256, 2, gate="vector", dtype="bf16", seed=3, h0_std=0.1, dht_std=0.1)
-    x["g"] = np.full_like(x["g"], -8.0)
+    x["g"] = np.full_like(x["g"], -12.0)
     gpu = tl.run_gpu(x)
-    for n in ("dq", "dk", "dg"):
+    for n in ("o", "dq", "dk", "dg"):
         assert not np.all(np.isfinite(gpu[n])), n
-    tl.compare(gpu, x, names=("o", "ht"))

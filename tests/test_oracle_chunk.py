@@ -146,11 +146,12 @@ def test_windowed_matrix_intra_equals_dense_route(gate, window):
 
 
 @pytest.mark.parametrize("producer", ["rewy", "wy7"])
-def test_windowed_reproduces_token_oracle_under_strong_decay(producer):
-    """|g| up to 5 per token: a chunk's range reaches about 160, two windows
-    of 32 tokens about 80 each. The windowed chunk form, in fp64, equals the
-    token recurrence."""
-    q, k, v, g, beta, h0, dO, dht = _strong("vector", 150, 8, 5, seed=81)
+@pytest.mark.parametrize("lo", [-5.0, -10.0])
+def test_windowed_reproduces_token_oracle_under_strong_decay(producer, lo):
+    """|g| up to 5 (10) per token: a chunk's range reaches about 160 (320),
+    a 16-token window about 40 (80). The windowed chunk form, in fp64,
+    equals the token recurrence."""
+    q, k, v, g, beta, h0, dO, dht = _strong("vector", 150, 8, 5, seed=81, lo=lo)
     o_t, ht_t, gr_t = _token(q, k, v, g, beta, h0, dO, dht)
     gr_c = cf.chunk_backward(q, k, v, g, beta, h0, dO, dht, 64, producer, "windowed")
     for n in gr_t:
@@ -158,30 +159,38 @@ def test_windowed_reproduces_token_oracle_under_strong_decay(producer):
 
 
 def test_windowed_factors_stay_within_fp32_range():
-    """Under per-token decays down to exp(-5), every exponent of a windowed
-    factor (32-token windows of a 64-token chunk) and of the per-key scale
-    that turns a diagonal-window operand into a boundary-pivot one is at most
-    80 in magnitude, while the chunk-wide centring of Sec. 3.3 needs factors
-    beyond exp(88), past the largest fp32."""
+    """Under per-token decays down to exp(-10), the window-centred factors of
+    16-token windows stay within exp(+-80), while centring per 32-token
+    window needs factors beyond exp(88), past the largest fp32. Every other
+    exponent is at most 0 (it can only underflow, towards a product that is
+    that small): the boundary-pivot factors, G[16 m - 1] against earlier
+    windows and G[16 m + 16] against later ones, and the per-key scales
+    exp(G[16 m - 1] - c_w), exp(c_w - G[16 m + 16]) that turn a
+    window-centred operand into a boundary-pivot one."""
     rng = np.random.default_rng(91)
-    worst_win, worst_chunk = 0.0, 0.0
+    worst16, worst32 = 0.0, 0.0
     for _ in range(50):
-        g = rng.uniform(-5.0, 0.0, size=(64, 128))
+        g = rng.uniform(-10.0, 0.0, size=(64, 128))
         G = np.cumsum(g, axis=0)
-        c = []
+        c = [0.5 * (G[16 * m:16 * m + 16].max(0) + G[16 * m:16 * m + 16].min(0)) for m in range(4)]
+        for m in range(4):
+            W = G[16 * m:16 * m + 16]
+            worst16 = max(worst16, np.abs(W - c[m]).max())
+            if m >= 1:  # rows of window m against earlier columns
+                p = G[16 * m - 1]
+                assert np.all(W - p <= 0) and np.all(p - G[:16 * m] <= 0)
+                for w in range(m):
+                    assert np.all(p - c[w] <= 0)
+            if m <= 2:  # rows of window m against later columns
+                p = G[16 * m + 16]
+                assert np.all(p - W <= 0) and np.all(G[16 * m + 16:] - p <= 0)
+                for w in range(m + 1, 4):
+                    assert np.all(c[w] - p <= 0)
         for a0 in (0, 32):
             W = G[a0:a0 + 32]
-            c.append(0.5 * (W.max(0) + W.min(0)))
-            worst_win = max(worst_win, np.abs(W - c[-1]).max())
-        # boundary pivots: rows of window 1 against G[31], columns of window 0
-        # against G[32] -- all exponents <= 0 -- and the operand scales
-        # exp(G[31] - c0), exp(c1 - G[32])
-        assert np.all(G[32:] - G[31] <= 0) and np.all(G[32] - G[:32] <= 0)
-        worst_win = max(worst_win, np.abs(G[31] - c[0]).max(), np.abs(c[1] - G[32]).max())
-        cc = 0.5 * (G.max(0) + G.min(0))
-        worst_chunk = max(worst_chunk, np.abs(G - cc).max())
-    assert worst_win <= 80.0
-    assert worst_chunk > 88.0
+            worst32 = max(worst32, np.abs(W - 0.5 * (W.max(0) + W.min(0))).max())
+    assert worst16 <= 80.0
+    assert worst32 > 88.0
 
 
 @pytest.mark.parametrize("n", [64, 45])
