@@ -113,6 +113,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="calibration copy + a few headline steps, for rocprofv3 counter runs")
+    ap.add_argument("--workload", default="gdn_1x8192x16", choices=["gdn_1x8192x16", "kda_1x8192x16"],
+                    help="the backward the profile pass steps (the timed bench is always GDN)")
     return ap.parse_args()
 
 
@@ -206,7 +208,10 @@ def main():
         d["h0"] = torch.from_numpy(x["h0"]).to(dev, torch.float32)
         return d
 
-    wl = WORKLOADS["gdn_1x8192x16"]
+    if args.workload != "gdn_1x8192x16" and not args.profile_pass:
+        print("bench.py: --workload selects the profile pass's backward only", file=sys.stderr)
+        sys.exit(2)
+    wl = WORKLOADS[args.workload]
     x = wl.make()
     d = to_dev(x)
     B, T, H = wl.B, wl.T, wl.H
@@ -277,7 +282,7 @@ def main():
         for _ in range(args.steps):
             run()
         torch.cuda.synchronize()
-        print(json.dumps({"profile_pass": True, "copy_bytes_each_way": 4 * n,
+        print(json.dumps({"profile_pass": True, "workload": wl.name, "copy_bytes_each_way": 4 * n,
                           "steps": args.steps, "kernel_sources": kernel_source_hash()}),
               flush=True)
         return
