@@ -957,11 +957,12 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 }
 
 template <typename T, bool VEC, bool WY7>
-__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr)
+__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
     SeqView sv;
     int64_t c;
-    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, sv, c))
+        return;  // an unused slot of a packed batch
     bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, sv, c, -1, nullptr, nullptr);
 }
 
@@ -973,7 +974,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
 // workgroup's reads arrive; here those of h and dh (64 KiB of the chunk's
 // 169 KiB) arrive during the previous item.
 template <typename T>
-__global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, Inter it, Grads gr)
+__global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
     __shared__ bf16x4 sStage[NW][STAGE];
     const int64_t n = s.NC * (s.B * s.H);
@@ -982,7 +983,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
     SeqView sv;
     int64_t c;
     int64_t i = blockIdx.x;
-    while (i < n && !chunk_at(s, i % s.NC, i / s.NC, sv, c)) i += G;
+    while (i < n && !chunk_in_order(s, i, order, sv, c)) i += G;
     if (i >= n) return;
     stage_hdh(it, seq_tile(s, sv, c), w, sStage[w]);
     Tail<T> pend{nullptr, nullptr, 0, false};
@@ -990,7 +991,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
         SeqView sn;
         int64_t cn = 0;
         int64_t j = i + G;
-        while (j < n && !chunk_at(s, j % s.NC, j / s.NC, sn, cn)) j += G;
+        while (j < n && !chunk_in_order(s, j, order, sn, cn)) j += G;
         bwd_local_chunk<T, false, false, true>(s, in, it, gr, sv, c, j < n ? seq_tile(s, sn, cn) : -1,
                                                sStage[w], &pend);
         if (j >= n) break;
@@ -1003,26 +1004,26 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
 }  // namespace
 
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
-                            bool wy7, hipStream_t st)
+                            bool wy7, int order, hipStream_t st)
 {
     if (!wy7 && !s.vec) {
         // one workgroup per CU (LDS), each taking every G-th (chunk, head)
         const int64_t n = s.NC * (s.B * s.H);
         if (n <= 0) return hipSuccess;
         const unsigned nb = (unsigned)(n < cu_count() ? n : cu_count());
-        if (s.f32) bwd_local_pf_kernel<float><<<nb, NTHR, 0, st>>>(s, in, it, gr);
-        else bwd_local_pf_kernel<bf16><<<nb, NTHR, 0, st>>>(s, in, it, gr);
+        if (s.f32) bwd_local_pf_kernel<float><<<nb, NTHR, 0, st>>>(s, in, it, gr, order);
+        else bwd_local_pf_kernel<bf16><<<nb, NTHR, 0, st>>>(s, in, it, gr, order);
         return hipGetLastError();
     }
     dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
 #define GDR_BWD_LOCAL(W7)                                                                        \
     do {                                                                                         \
         if (s.f32) {                                                                             \
-            if (s.vec) bwd_local_kernel<float, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);  \
-            else bwd_local_kernel<float, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);       \
+            if (s.vec) bwd_local_kernel<float, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);  \
+            else bwd_local_kernel<float, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);       \
         } else {                                                                                 \
-            if (s.vec) bwd_local_kernel<bf16, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);   \
-            else bwd_local_kernel<bf16, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr);        \
+            if (s.vec) bwd_local_kernel<bf16, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);   \
+            else bwd_local_kernel<bf16, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);        \
         }                                                                                        \
     } while (0)
     if (wy7) GDR_BWD_LOCAL(true);

@@ -375,8 +375,11 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
         e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
         if (e != hipSuccess) return hip_fail(e, "scan_bwd");
     }
+    // oldest in the last-level cache first: after the two walks the middle
+    // chunks' h and dh; after the reverse walk alone the last chunk's dh
+    const int order = policy == GDR_RECOMPUTE ? CO_MIDDLE_OUT : CO_DESCENDING;
     e = timed(wy7 ? ST_BWD_LOCAL_WY7 : ST_BWD_LOCAL, st,
-              [&] { return launch_bwd_local(s, in, it, gr, wy7, st); });
+              [&] { return launch_bwd_local(s, in, it, gr, wy7, order, st); });
     if (e != hipSuccess) return hip_fail(e, "bwd_local");
     return GDR_OK;
 }

@@ -151,6 +151,36 @@ __device__ inline bool chunk_of_block(const Shape& s, SeqView& v, int64_t& c)
     return chunk_at(s, blockIdx.x, blockIdx.y, v, c);
 }
 
+// Order in which a launch over the (chunk, head) pairs of a regular batch
+// visits them. The chip's 256 MiB last-level cache keeps the most recently
+// written intermediates, so a producer visits the chunks chunk-major (every
+// head of one chunk in turn) and writes last what its consumer reads first:
+//   CO_ASCENDING   0 .. NC-1 (for a consumer walking NC-1 .. 0),
+//   CO_DESCENDING  NC-1 .. 0 (for a consumer walking 0 .. NC-1),
+//   CO_MIDDLE_OUT  the middle chunks first and both ends last (for the
+//                  forward and reverse walks run side by side).
+// A consumer of the walks' own outputs visits first what is oldest in the
+// cache, before the new traffic evicts it.
+enum ChunkOrder { CO_ASCENDING = 0, CO_DESCENDING = 1, CO_MIDDLE_OUT = 2 };
+
+__device__ inline int64_t ordered_chunk(int64_t k, int64_t NC, int order)
+{
+    if (order == CO_ASCENDING) return k;
+    if (order == CO_DESCENDING) return NC - 1 - k;
+    const int64_t mid = (NC - 1) / 2;  // k = 0, 1, 2, 3, ... -> mid, mid + 1, mid - 1, mid + 2, ...
+    return (k & 1) ? mid + 1 + k / 2 : mid - k / 2;
+}
+
+// Item L (0 .. NC * B * H - 1) of a launch: in a regular batch the
+// (chunk, head) pair at position L of `order`; in a packed batch chunk slot
+// L % NC of head L / NC, as chunk_at (the slots already follow the packing).
+__device__ inline bool chunk_in_order(const Shape& s, int64_t L, int order, SeqView& v, int64_t& c)
+{
+    if (s.ctab) return chunk_at(s, L % s.NC, L / s.NC, v, c);
+    const int64_t BH = s.B * s.H;
+    return chunk_at(s, ordered_chunk(L / BH, s.NC, order), L % BH, v, c);
+}
+
 // Compute units of the current device (cached per device).
 int cu_count();
 
@@ -204,7 +234,8 @@ hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, in
 hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
 hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
+// order: the ChunkOrder of the (chunk, head) items (regular batches).
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
-                            bool wy7, hipStream_t st);
+                            bool wy7, int order, hipStream_t st);
 
 }  // namespace gdr

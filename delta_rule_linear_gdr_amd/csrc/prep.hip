@@ -64,7 +64,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 {
     SeqView sv;
     int64_t c;
-    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    // the forward walks chunks 0 .. NC-1; the recompute backward's two walks
+    // start at both ends
+    const int order = (what & PREP_OUT) ? CO_DESCENDING : CO_MIDDLE_OUT;
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, sv, c))
+        return;  // an unused slot of a packed batch
     const int64_t t = seq_tile(s, sv, c);
     const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
     const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
@@ -643,7 +647,9 @@ __global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
 {
     SeqView sv;
     int64_t c;
-    if (!chunk_of_block(s, sv, c)) return;  // an unused slot of a packed batch
+    // the reverse walk reads chunk NC-1 first
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, CO_ASCENDING, sv, c))
+        return;  // an unused slot of a packed batch
     const int64_t t = seq_tile(s, sv, c);
     const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
     const int ld = (int)(s.H * DVD);
