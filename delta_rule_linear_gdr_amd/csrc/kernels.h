@@ -144,13 +144,6 @@ __device__ inline bool chunk_at(const Shape& s, int64_t x, int64_t y, SeqView& v
     return true;
 }
 
-// The chunk of a per-chunk workgroup (blockIdx.x = chunk or chunk slot,
-// blockIdx.y = b * H + head).
-__device__ inline bool chunk_of_block(const Shape& s, SeqView& v, int64_t& c)
-{
-    return chunk_at(s, blockIdx.x, blockIdx.y, v, c);
-}
-
 // Order in which a launch over the (chunk, head) pairs of a regular batch
 // visits them. The chip's 256 MiB last-level cache keeps the most recently
 // written intermediates, so a producer visits the chunks chunk-major (every
