@@ -409,6 +409,23 @@ def test_many_heads_and_batch():
         _report(f"B4H48/{pol}", tl.compare(tl.run_gpu(x, pol), x, heads=[(0, 0), (3, 47), (2, 17)]))
 
 
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("T", [128, 150, 448])
+def test_chunk_orders_small_chunk_counts(gate, T):
+    """The per-chunk launches visit (chunk, head) items chunk-major in a
+    cache-aware order (middle-out, ascending or descending by call); with
+    2, 3 and 7 chunks and B * H = 6 every item must be visited exactly
+    once under each order: both policies (the recompute backward's
+    middle-out prep and local kernel, the forward's descending prep, the
+    full-save backward's ascending xy and descending local kernel) and the
+    seven-product local kernel."""
+    _need_gpu()
+    x = make_inputs(2, T, 3, gate=gate, dtype="bf16", seed=70 + T, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"orders/{gate}/T{T}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+    _report(f"orders/{gate}/T{T}/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
+
+
 # ------------------------------------------------------ HIP graph capture
 
 def _graph_case(x, policy, packed):
