@@ -977,7 +977,7 @@ template <typename T>
 __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
     __shared__ bf16x4 sStage[NW][STAGE];
-    const int64_t n = s.NC * (s.B * s.H);
+    const int64_t n = slots_used(s) * (s.B * s.H);  // items in use, dealt evenly
     const int64_t G = gridDim.x;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     SeqView sv;

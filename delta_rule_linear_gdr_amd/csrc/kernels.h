@@ -164,14 +164,27 @@ __device__ inline int64_t ordered_chunk(int64_t k, int64_t NC, int order)
     return (k & 1) ? mid + 1 + k / 2 : mid - k / 2;
 }
 
-// Item L (0 .. NC * B * H - 1) of a launch: in a regular batch the
-// (chunk, head) pair at position L of `order`; in a packed batch chunk slot
-// L % NC of head L / NC, as chunk_at (the slots already follow the packing).
+// Chunk slots in use: NC in a regular batch; in a packed batch the
+// sequences' slots, which are 0 .. U-1 (each sequence's first slot is the
+// exclusive sum of the chunk counts before it), the rest of NC unused.
+__device__ inline int64_t slots_used(const Shape& s)
+{
+    if (!s.ctab) return s.NC;
+    if (s.NS <= 0) return 0;
+    const int2 e = s.stab[s.NS - 1];
+    return (int64_t)e.x + e.y;
+}
+
+// Item L (0 .. NC * B * H - 1) of a launch: the (chunk, b * H + head) pair
+// at position L of `order` over the slots in use (in a packed batch, B = 1,
+// the order runs over the chunk slots, sequence after sequence); items past
+// them yield false. Either way the concurrent workgroups of a launch touch
+// neighbouring tiles (tiles are chunk- or slot-major).
 __device__ inline bool chunk_in_order(const Shape& s, int64_t L, int order, SeqView& v, int64_t& c)
 {
-    if (s.ctab) return chunk_at(s, L % s.NC, L / s.NC, v, c);
-    const int64_t BH = s.B * s.H;
-    return chunk_at(s, ordered_chunk(L / BH, s.NC, order), L % BH, v, c);
+    const int64_t BH = s.B * s.H, NU = slots_used(s), k = L / BH;
+    if (k >= NU) return false;
+    return chunk_at(s, ordered_chunk(k, NU, order), L % BH, v, c);
 }
 
 // Compute units of the current device (cached per device).
