@@ -130,14 +130,26 @@ struct Tail {
 // requested once they have been read; the previous chunk's deferred last
 // phase (*pend) runs after this chunk's reads are issued, and this chunk's
 // is left in *pend when a next chunk follows.
+// What a chunk's work needs of its (sequence, head, chunk): the tile, the
+// token row of its row 0 and its rows (past them: zeros read, nothing
+// written). The persistent loop carries only this across a chunk.
+struct ChunkRef {
+    int64_t t, tok0;
+    int nv;
+};
+__device__ __forceinline__ ChunkRef chunk_ref(const Shape& s, const SeqView& sv, int64_t c)
+{
+    return ChunkRef{seq_tile(s, sv, c), seq_tok0(s, sv, c), seq_rows(sv, c)};
+}
+
 template <typename T, bool VEC, bool WY7, bool PF>
 __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in, const Inter& it,
-                                                const Grads& gr, const SeqView& sv, int64_t c,
+                                                const Grads& gr, const ChunkRef& cr,
                                                 int64_t tnext, bf16x4* area, Tail<T>* pend)
 {
-    const int64_t t = seq_tile(s, sv, c);
-    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
-    const int nv = seq_rows(sv, c);  // rows past it read as zeros and are not written
+    const int64_t t = cr.t;
+    const int64_t tok0 = cr.tok0;  // token row of the chunk's row 0
+    const int nv = cr.nv;          // rows past it read as zeros and are not written
     // Row stride (elements) of q, k, v, dO and their gradients. In-chunk
     // offsets stay below 64 * H * 128 < 2^31 (H <= 65535), so they are 32-bit
     // and every pointer below is a uniform per-chunk base.
@@ -963,7 +975,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Int
     int64_t c;
     if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, sv, c))
         return;  // an unused slot of a packed batch
-    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, sv, c, -1, nullptr, nullptr);
+    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, chunk_ref(s, sv, c), -1, nullptr, nullptr);
 }
 
 // Persistent form (scalar gate, three-product producer): workgroup b takes
@@ -980,24 +992,26 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
     const int64_t n = slots_used(s) * (s.B * s.H);  // items in use, dealt evenly
     const int64_t G = gridDim.x;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    SeqView sv;
-    int64_t c;
-    int64_t i = blockIdx.x;
-    while (i < n && !chunk_in_order(s, i, order, sv, c)) i += G;
+    // the item (chunk, head) at or after i that is in use, or i >= n
+    auto next_item = [&](int64_t i, ChunkRef& r) -> int64_t {
+        SeqView sv;
+        int64_t c = 0;
+        while (i < n && !chunk_in_order(s, i, order, sv, c)) i += G;
+        if (i < n) r = chunk_ref(s, sv, c);
+        return i;
+    };
+    ChunkRef cur{0, 0, 1};
+    int64_t i = next_item(blockIdx.x, cur);
     if (i >= n) return;
-    stage_hdh(it, seq_tile(s, sv, c), w, sStage[w]);
+    stage_hdh(it, cur.t, w, sStage[w]);
     Tail<T> pend{nullptr, nullptr, 0, false};
     for (;;) {
-        SeqView sn;
-        int64_t cn = 0;
-        int64_t j = i + G;
-        while (j < n && !chunk_in_order(s, j, order, sn, cn)) j += G;
-        bwd_local_chunk<T, false, false, true>(s, in, it, gr, sv, c, j < n ? seq_tile(s, sn, cn) : -1,
-                                               sStage[w], &pend);
+        ChunkRef nxt{-1, 0, 1};
+        const int64_t j = next_item(i + G, nxt);
+        bwd_local_chunk<T, false, false, true>(s, in, it, gr, cur, j < n ? nxt.t : -1, sStage[w], &pend);
         if (j >= n) break;
         i = j;
-        sv = sn;
-        c = cn;
+        cur = nxt;
     }
 }
 
