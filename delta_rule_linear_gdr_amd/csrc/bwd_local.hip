@@ -130,18 +130,6 @@ struct Tail {
 // requested once they have been read; the previous chunk's deferred last
 // phase (*pend) runs after this chunk's reads are issued, and this chunk's
 // is left in *pend when a next chunk follows.
-// What a chunk's work needs of its (sequence, head, chunk): the tile, the
-// token row of its row 0 and its rows (past them: zeros read, nothing
-// written). The persistent loop carries only this across a chunk.
-struct ChunkRef {
-    int64_t t, tok0;
-    int nv;
-};
-__device__ __forceinline__ ChunkRef chunk_ref(const Shape& s, const SeqView& sv, int64_t c)
-{
-    return ChunkRef{seq_tile(s, sv, c), seq_tok0(s, sv, c), seq_rows(sv, c)};
-}
-
 template <typename T, bool VEC, bool WY7, bool PF>
 __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in, const Inter& it,
                                                 const Grads& gr, const ChunkRef& cr,
@@ -971,11 +959,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 template <typename T, bool VEC, bool WY7>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
-    SeqView sv;
-    int64_t c;
-    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, sv, c))
+    ChunkRef cr;
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, cr))
         return;  // an unused slot of a packed batch
-    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, chunk_ref(s, sv, c), -1, nullptr, nullptr);
+    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, cr, -1, nullptr, nullptr);
 }
 
 // Persistent form (scalar gate, three-product producer): workgroup b takes
@@ -989,15 +976,14 @@ template <typename T>
 __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
     __shared__ bf16x4 sStage[NW][STAGE];
-    const int64_t n = slots_used(s) * (s.B * s.H);  // items in use, dealt evenly
+    const int64_t NU = slots_used(s), n = NU * (s.B * s.H);  // items in use, dealt evenly
     const int64_t G = gridDim.x;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // the item (chunk, head) at or after i that is in use, or i >= n
     auto next_item = [&](int64_t i, ChunkRef& r) -> int64_t {
-        SeqView sv;
-        int64_t c = 0;
-        while (i < n && !chunk_in_order(s, i, order, sv, c)) i += G;
-        if (i < n) r = chunk_ref(s, sv, c);
+        ChunkRef x{0, 0, 1};
+        while (i < n && !chunk_in_order(s, i, order, NU, x)) i += G;
+        if (i < n) r = x;
         return i;
     };
     ChunkRef cur{0, 0, 1};

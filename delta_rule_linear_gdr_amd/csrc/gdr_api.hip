@@ -241,6 +241,8 @@ int check_packed_shape(const gdr_desc* d, int64_t n_seq)
     if (nchunks(d) + n_seq > ((int64_t)1 << 30))
         return fail(GDR_ERR_UNSUPPORTED, "%lld sequences over T=%lld: too many chunk slots",
                     (long long)n_seq, (long long)d->T);
+    if (d->T >= ((int64_t)1 << 31))  // the slot table holds 32-bit token indices
+        return fail(GDR_ERR_UNSUPPORTED, "a packed row of T=%lld tokens (at most 2^31 - 1)", (long long)d->T);
     return GDR_OK;
 }
 int check_packed(const gdr_desc* d, const Packed& pk)

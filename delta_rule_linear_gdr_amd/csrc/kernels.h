@@ -71,7 +71,7 @@ struct Shape {
     int64_t NS, NC;
     const int64_t* cu;  // sanitized token offsets, NS + 1
     const int2* stab;   // per sequence: {first chunk slot, chunk count}
-    const int2* ctab;   // per chunk slot: {sequence, chunk in it}, {-1, 0} if unused
+    const int2* ctab;   // per chunk slot: {token (along T) of its row 0, rows}, rows 0 if unused
     const int* order;   // sequences, longest first (by length class), for the scans
 };
 
@@ -128,18 +128,31 @@ __host__ __device__ inline int64_t seq_tok0(const Shape& s, const SeqView& v, in
     return (v.tok + c * CH) * s.H + v.hd;
 }
 
-// The chunk at (x = chunk or chunk slot, y = b * H + head); false for an
-// unused slot of a packed batch.
-__device__ inline bool chunk_at(const Shape& s, int64_t x, int64_t y, SeqView& v, int64_t& c)
+// What a per-chunk kernel needs of its (chunk, head): the tile, the row
+// index (into [.., T, H, ..] token-major tensors) of the chunk's first token,
+// and its rows (past them: zeros read, nothing written).
+struct ChunkRef {
+    int64_t t, tok0;
+    int nv;
+};
+
+// The chunk at (x = chunk or chunk slot, y = b * H + head), as seq_tile,
+// seq_tok0 and seq_rows give it for the sequence view of (b, head); in a
+// packed batch from the slot's table entry alone (one read), false for an
+// unused slot.
+__device__ inline bool chunk_at(const Shape& s, int64_t x, int64_t y, ChunkRef& r)
 {
     if (s.ctab) {
         const int2 e = s.ctab[x];
-        if (e.x < 0) return false;
-        v = seq_view(s, e.x, y);
-        c = e.y;
+        if (e.y <= 0) return false;
+        r.t = x * s.H + y;
+        r.tok0 = (int64_t)e.x * s.H + y;
+        r.nv = e.y;
     } else {
-        v = seq_view(s, y / s.H, y % s.H);
-        c = x;
+        const SeqView v = seq_view(s, y / s.H, y % s.H);
+        r.t = seq_tile(s, v, x);
+        r.tok0 = seq_tok0(s, v, x);
+        r.nv = seq_rows(v, x);
     }
     return true;
 }
@@ -180,11 +193,16 @@ __device__ inline int64_t slots_used(const Shape& s)
 // the order runs over the chunk slots, sequence after sequence); items past
 // them yield false. Either way the concurrent workgroups of a launch touch
 // neighbouring tiles (tiles are chunk- or slot-major).
-__device__ inline bool chunk_in_order(const Shape& s, int64_t L, int order, SeqView& v, int64_t& c)
+// NU: slots_used(s), which a caller mapping many items reads once.
+__device__ inline bool chunk_in_order(const Shape& s, int64_t L, int order, int64_t NU, ChunkRef& r)
 {
-    const int64_t BH = s.B * s.H, NU = slots_used(s), k = L / BH;
+    const int64_t BH = s.B * s.H, k = L / BH;
     if (k >= NU) return false;
-    return chunk_at(s, ordered_chunk(k, NU, order), L % BH, v, c);
+    return chunk_at(s, ordered_chunk(k, NU, order), L % BH, r);
+}
+__device__ inline bool chunk_in_order(const Shape& s, int64_t L, int order, ChunkRef& r)
+{
+    return chunk_in_order(s, L, order, slots_used(s), r);
 }
 
 // Compute units of the current device (cached per device).

@@ -62,17 +62,16 @@ __device__ __forceinline__ void st_row8_frag(bf16* base, int i, int f0, const fl
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter it, int what)
 {
-    SeqView sv;
-    int64_t c;
+    ChunkRef cr;
     // the forward walks chunks 0 .. NC-1; the recompute backward's two walks
     // start at both ends
     const int order = (what & PREP_OUT) ? CO_DESCENDING : CO_MIDDLE_OUT;
-    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, sv, c))
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, cr))
         return;  // an unused slot of a packed batch
-    const int64_t t = seq_tile(s, sv, c);
-    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
+    const int64_t t = cr.t;
+    const int64_t tok0 = cr.tok0;  // token row of the chunk's row 0
     const int ld = (int)(s.H * DKD);  // row stride (elements); in-chunk offsets < 2^31
-    const int nv = seq_rows(sv, c);  // rows past it are read as zeros
+    const int nv = cr.nv;  // rows past it are read as zeros
     const int tid = threadIdx.x;
     const int l = lane_id(), r = lane_r(), g = lane_g();
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -643,19 +642,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 
 // X = Hm^T dO, Y = Qg^T dO from stored Hm^T / Qg^T frags (full-save policy).
 template <typename T>
-__global__ __launch_bounds__(256) void xy_kernel(Shape s, Inputs in, Inter it)
+__global__ __launch_bounds__(256, 8) void xy_kernel(Shape s, Inputs in, Inter it)
 {
-    SeqView sv;
-    int64_t c;
+    ChunkRef cr;
     // the reverse walk reads chunk NC-1 first
-    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, CO_ASCENDING, sv, c))
+    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, CO_ASCENDING, cr))
         return;  // an unused slot of a packed batch
-    const int64_t t = seq_tile(s, sv, c);
-    const int64_t tok0 = seq_tok0(s, sv, c);  // token row of the chunk's row 0
+    const int64_t t = cr.t;
+    const int64_t tok0 = cr.tok0;  // token row of the chunk's row 0
     const int ld = (int)(s.H * DVD);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const T* dO = (const T*)in.dO + tok0 * DVD;
-    const int nv = seq_rows(sv, c);  // rows past it are read as zeros
+    const int nv = cr.nv;  // rows past it are read as zeros
 
     const bf16x8 I0 = ident_frag(0), I1 = ident_frag(1);
     f32x4 OC[4][2];

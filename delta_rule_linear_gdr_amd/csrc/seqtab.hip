@@ -91,13 +91,19 @@ __global__ __launch_bounds__(NTH) void seq_tables_kernel(Shape s, const int64_t*
         carry += tot;
     }
 
-    // 3. chunk slots: unused by default, then each sequence claims its own
-    for (int64_t j = tid; j < s.NC; j += NTH) ctab[j] = make_int2(-1, 0);
+    // 3. chunk slots: unused (no rows) by default, then each sequence claims
+    //    its own: {token of the chunk's row 0, rows} (tokens < 2^31, checked
+    //    by the caller)
+    for (int64_t j = tid; j < s.NC; j += NTH) ctab[j] = make_int2(0, 0);
     if (tid < NCLASS) cls_next[tid] = 0;
     __syncthreads();
     for (int64_t i = tid; i < N; i += NTH) {
         const int2 e = stab[i];
-        for (int c = 0; c < e.y; ++c) ctab[e.x + c] = make_int2((int)i, c);
+        const int64_t tok = cu[i], len = cu[i + 1] - tok;
+        for (int c = 0; c < e.y; ++c) {
+            const int64_t rows = len - (int64_t)c * CH;
+            ctab[e.x + c] = make_int2((int)(tok + (int64_t)c * CH), rows < CH ? (int)rows : CH);
+        }
         atomicAdd(&cls_next[len_class(e.y)], 1);
     }
     __syncthreads();

@@ -147,6 +147,8 @@ def test_packed_validation_without_launching():
     assert _ws_varlen(_desc(B=2), 3)[0] == -1            # sequences live along T
     assert _ws_varlen(_desc(), -1)[0] == -1
     assert _ws_varlen(_desc(DK=192), 2)[0] == -2
+    assert _ws_varlen(_desc(T=1 << 31), 2)[0] == -2       # the slot table holds 32-bit token indices
+    assert _ws_varlen(_desc(T=(1 << 31) - 64), 2)[0] == 0
     fake = 1 << 20  # never dereferenced: validation fails first
     d = _desc(T=256)
     sc = _ws_varlen(d, 2)[2]
