@@ -426,20 +426,26 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
+        # the fp64 oracle, one whole-workload call each (it threads over
+        # (sequence, head, value-row block)), on the five workloads; the
+        # headline workload's call is the CPU baseline
         import oracle
         threads = oracle.default_threads()
-        heads = [(0, h) for h in range(H)]
-        t0 = time.perf_counter()
-        for b, h in heads:
-            sl = lambda a: a[b:b + 1, :, h:h + 1]  # noqa: E731
-            oracle.token_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]),
-                             x["h0"][b:b + 1, h:h + 1], sl(x["dO"]), None, threads=threads)
-        tc = time.perf_counter() - t0
-        frac = len(heads) / H
-        cpu = {"value": round(B * T * frac / tc, 2), "unit": "tokens/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{len(heads)} of {H} heads of GDN (1,8192,16) (the whole workload): fp64 "
-                         f"token-recurrence backward incl. its forward recompute, {tc:.1f} s"}
+        rows = []
+        for name, wl_ in WORKLOADS.items():
+            xw = x if name == wl.name else wl_.make()
+            t0 = time.perf_counter()
+            oracle.token_bwd(xw["q"], xw["k"], xw["v"], xw["g"], xw["beta"], xw["h0"], xw["dO"], None,
+                             threads=threads)
+            tw = time.perf_counter() - t0
+            rows.append({"workload": name, "B": wl_.B, "T": wl_.T, "H": wl_.H, "gate": wl_.gate,
+                         "seconds": round(tw, 3), "tokens_per_s": round(wl_.B * wl_.T / tw, 1)})
+            print(f"[bench] oracle {name}: {tw:.2f} s", file=sys.stderr, flush=True)
+            if name == wl.name:
+                cpu = {"value": round(B * T / tw, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                       "sample": f"the whole GDN (1,8192,16) workload, one call: fp64 token-recurrence "
+                                 f"backward incl. its forward recompute, {tw:.2f} s on {threads} threads"}
+        detail["cpu_oracle_workloads"] = {"threads": threads, "rows": rows}
 
     line = {
         "metric": "GDN/KDA backward tokens/s + TFLOP/s (% roofline) at (1,8192,16), C=64, d=128",
