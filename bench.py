@@ -40,6 +40,7 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CH = 64
 T16, T32, T8, GN = 16384, 32768, 8192, 512   # bf16 64x128, 128x128, 64x64 tiles; exp(G_n)
 M = 1048576                                   # 2 * 64 * 64 * 128 FLOPs
+SOLVE = CH ** 3 // 3                          # inverse of a 64 x 64 unit lower-triangular matrix
 
 # Whole-path algorithmic bytes per token-head of the operator's inputs and
 # outputs at bf16: forward reads q, k, v, g, beta and writes o; backward
@@ -57,9 +58,14 @@ PATH_BYTES_PER_TOKEN_HEAD = {
 # h0 and dh0 (recompute backward, dht absent); dh0 (full-save backward)
 PATH_STATES = {"fwd_R": 2, "fwd_A": 2, "bwd_R": 2, "bwd_A": 1}
 # Algorithmic FLOPs per (chunk, head): the dense products of each call
-# (2mnk), the same for both gates at d_k = d_v = 128
-PATH_FLOPS_PER_CHUNK_HEAD = {"fwd_R": 11621717, "fwd_A": 11621717,
-                             "bwd_R": 29447509, "bwd_A": 22020096}
+# (2mnk, in units of M) plus the triangular solve, the same for both gates at
+# d_k = d_v = 128. Forward: L and H (1 each), W and U (2), the state walk
+# W S and K~^T R (4), the output Q_g S and H R (3). Backward, recompute:
+# prep's L, H, W, U, X = H^T dO (1) and Y = Q_g^T dO (2), both walks (8) and
+# the local kernel (13). Backward, full save: X and Y (3), the reverse walk
+# K~ dS and W^T dR (4) and the local kernel (13).
+PATH_FLOPS_PER_CHUNK_HEAD = {"fwd_R": 11 * M + SOLVE, "fwd_A": 11 * M + SOLVE,
+                             "bwd_R": 28 * M + SOLVE, "bwd_A": 20 * M}
 
 
 def path_figures(gate: str, kind: str, B: int, T: int, H: int, ms: float) -> dict:
@@ -86,7 +92,7 @@ def kernel_work(gate: str) -> dict:
         # recompute backward: reads q, k, v, dO, g, beta; writes -W, Kt^T, U, Kt,
         # -W^T, X, Y, A^T, gn (and A, 8 KiB more, for the seven-product backward)
         "prep": (inputs4 + g_bytes + beta + 6 * T16 + T32 + T8 + GN,
-                 int(1.0 * M + 1.0 * M + 0.09 * M + 2 * M + 1 * M + 2 * M)),
+                 1 * M + 1 * M + SOLVE + 2 * M + 1 * M + 2 * M),
         # reads -W, Kt^T, U, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
         "scan_fwd": (3 * T16 + GN + T32 + T16, 4 * M),
         # reads Kt, -W^T, X, Y, gn; writes dh, Rb
