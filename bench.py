@@ -119,6 +119,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true",
                     help="calibration copy + a few headline steps, for rocprofv3 counter runs")
+    ap.add_argument("--with-wy7", action="store_true",
+                    help="profile pass: after the ReWY steps, as many seven-product backward steps")
     ap.add_argument("--workload", default="gdn_1x8192x16", choices=["gdn_1x8192x16", "kda_1x8192x16"],
                     help="the backward the profile pass steps (the timed bench is always GDN)")
     return ap.parse_args()
@@ -318,8 +320,14 @@ def main():
         for _ in range(args.steps):
             run()
         torch.cuda.synchronize()
+        if args.with_wy7:
+            run7 = make_runner(d, gdr.gdr_bwd_wy7, "recompute")
+            for _ in range(args.steps):
+                run7()
+            torch.cuda.synchronize()
         print(json.dumps({"profile_pass": True, "workload": wl.name, "copy_bytes_each_way": 4 * n,
-                          "steps": args.steps, "kernel_sources": kernel_source_hash()}),
+                          "steps": args.steps, "with_wy7": args.with_wy7,
+                          "kernel_sources": kernel_source_hash()}),
               flush=True)
         return
 
