@@ -146,3 +146,18 @@ def test_profile_tables_use_the_same_figures(gate, path):
     units = 1 * 8192 // CH * 16
     for st in stages:
         assert got[st] == bench.kernel_work(gate)[st][0] * units, st
+
+
+def test_ablation_profile_uses_the_same_figures():
+    with open(os.path.join(ROOT, "profiles", "gdn_bwd_R_1x8192x16_rewy_vs_wy7.md")) as fh:
+        text = fh.read()
+    w = bench.kernel_work("scalar")
+    units = 8192 // CH * 16
+    expect = {("bwd_local", "ReWY"): w["bwd_local"][0], ("bwd_local", "seven-product"): w["bwd_local_wy7"][0],
+              ("scan_pair", "ReWY"): w["scan_pair"][0], ("prep", "ReWY"): w["prep"][0],
+              # the seven-product backward's prep also writes A (64 x 64 bf16)
+              ("prep", "seven-product"): w["prep"][0] + CH * CH * BF16}
+    for (st, kind), per in expect.items():
+        m = re.search(r"^\| %s \| %s \|(?: [0-9.]+ \|){4} ([0-9.]+) \|" % (st, kind), text, re.M)
+        assert m, (st, kind)
+        assert float(m.group(1)) == round(per * units / 1e6, 1), (st, kind)
