@@ -28,7 +28,7 @@ import os
 
 __all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "chunk_gated_delta_rule", "workspace_size",
            "library_path", "load",
-           "profile_begin", "profile_end", "GdrError", "RECOMPUTE", "FULL_SAVE"]
+           "profile_begin", "profile_end", "set_local_form", "GdrError", "RECOMPUTE", "FULL_SAVE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -40,8 +40,10 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
 EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
-           "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen", "gdr_profile_begin",
-           "gdr_profile_end", "gdr_status_string", "gdr_last_error", "gdr_version")
+           "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
+           "gdr_profile_begin",
+           "gdr_profile_end", "gdr_set_local_form", "gdr_status_string", "gdr_last_error",
+           "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -96,6 +98,8 @@ def load():
     lib.gdr_profile_begin.restype = i32
     lib.gdr_profile_end.argtypes = [ctypes.POINTER(StageTime), i32, ctypes.POINTER(i32)]
     lib.gdr_profile_end.restype = i32
+    lib.gdr_set_local_form.argtypes = [i32]
+    lib.gdr_set_local_form.restype = i32
     lib.gdr_status_string.argtypes = [i32]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
@@ -157,6 +161,19 @@ def profile_end() -> dict:
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
 
 
+def set_local_form(form: str) -> str:
+    """Launch form of the scalar-gate three-product local backward:
+    "persistent" (default) or "per_chunk" (one workgroup per chunk and head,
+    the form of the seven-product kernel). Returns the previous form."""
+    forms = {"persistent": 0, "per_chunk": 1}
+    if form not in forms:
+        raise ValueError(f"unknown form {form!r}")
+    rc = load().gdr_set_local_form(forms[form])
+    if rc < 0:
+        _check(rc)
+    return {v: k for k, v in forms.items()}[rc]
+
+
 # ---------------------------------------------------------------- torch side
 
 def _torch():
@@ -182,20 +199,62 @@ def _desc_from(q, g, v):
     return make_desc(B, T, H, gate, dt, DK=DK, DV=DV)
 
 
-def _validate(q, k, v, g, beta, extra=()):
+def _validate(q, k, v, g, beta, n_seq=None, *, h0=None, dO=None, dht=None, out=None,
+              saved=None, saved_bytes=0, scratch=None):
+    """Checks every tensor against the problem q and v define before any
+    pointer reaches the library: device (one device, all of them), layout
+    (contiguous), exact shape against (B, T, H, DK, DV) and the state count
+    (B, or n_seq for a packed batch), and dtype (q's for the token tensors,
+    float32 for g and the states, uint8 for the workspaces)."""
     torch = _torch()
-    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta), *extra):
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError(f"q and v must be [B,T,H,D], got {tuple(q.shape)} and {tuple(v.shape)}")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"q dtype {q.dtype}: expected bfloat16 or float32")
+    B, T, H, DK = q.shape
+    DV = v.shape[3]
+    ns = B if n_seq is None else n_seq
+    tok_k, tok_v, row = (B, T, H, DK), (B, T, H, DV), (B, T, H)
+    state = (ns, H, DK, DV)
+    f32 = torch.float32
+    spec = [("q", q, tok_k, q.dtype), ("k", k, tok_k, q.dtype), ("v", v, tok_v, q.dtype),
+            ("beta", beta, row, q.dtype), ("h0", h0, state, f32), ("dO", dO, tok_v, q.dtype),
+            ("dht", dht, state, f32)]
+    if g is not None:
+        if g.dim() == 3:
+            spec.append(("g", g, row, f32))
+        else:
+            spec.append(("g", g, tok_k, f32))
+    if out is not None:
+        spec += [("dq", out.get("dq"), tok_k, q.dtype), ("dk", out.get("dk"), tok_k, q.dtype),
+                 ("dv", out.get("dv"), tok_v, q.dtype), ("dbeta", out.get("dbeta"), row, q.dtype),
+                 ("dh0", out.get("dh0"), state, f32)]
+        for name in ("dq", "dk", "dv", "dbeta"):
+            if out.get(name) is None:
+                raise ValueError(f"out['{name}'] is required")
+        if g is not None:
+            if out.get("dg") is None:
+                raise ValueError("out['dg'] is required when g is given")
+            spec.append(("dg", out["dg"], tuple(g.shape), f32))
+    if saved is not None:
+        spec.append(("saved", saved, None, torch.uint8))
+    if scratch is not None:
+        spec.append(("scratch", scratch, None, torch.uint8))
+    for name, t, shape, dtype in spec:
         if t is None:
             continue
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    for name, t in (("k", k), ("v", v), ("beta", beta)):
-        if t.dtype != q.dtype:
-            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
-    if g is not None and g.dtype != torch.float32:
-        raise TypeError("g must be float32")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} dtype {t.dtype}: expected {dtype}")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)}: expected {shape}")
+    if saved is not None and saved.numel() < saved_bytes:
+        raise ValueError(f"saved holds {saved.numel()} bytes, {saved_bytes} needed")
 
 
 def _stream():
@@ -230,10 +289,10 @@ def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch
     single row of q (batch size 1) a packed batch of n_seq sequences, each
     with its own state: h0 and ht are then [n_seq, H, 128, 128]."""
     torch = _torch()
-    _validate(q, k, v, g, beta, (("h0", h0),))
+    n_seq = _seqs(cu_seqlens, q)
+    _validate(q, k, v, g, beta, n_seq, h0=h0, scratch=scratch)
     d = _desc_from(q, g, v)
     pol = _policy(policy)
-    n_seq = _seqs(cu_seqlens, q)
     lib = load()
     saved_b, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
@@ -256,14 +315,17 @@ def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch
 def _bwd(name, q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch, out,
          cu_seqlens=None):
     torch = _torch()
-    _validate(q, k, v, g, beta, (("h0", h0), ("dO", dO), ("dht", dht)))
-    if dO.dtype != q.dtype:
-        raise TypeError("dO dtype differs from q dtype")
+    n_seq = _seqs(cu_seqlens, q)
+    if dO is None:
+        raise ValueError("dO is required")
     d = _desc_from(q, g, v)
     pol = _policy(policy)
-    n_seq = _seqs(cu_seqlens, q)
     lib = load()
-    _, scratch_b = _sizes(d, pol, n_seq)
+    saved_b, scratch_b = _sizes(d, pol, n_seq)
+    if pol == FULL_SAVE and saved is None:
+        raise ValueError("the full-save backward needs the forward's saved area")
+    _validate(q, k, v, g, beta, n_seq, h0=h0, dO=dO, dht=dht, out=out, saved=saved,
+              saved_bytes=saved_b, scratch=scratch)
     B, T, H, _ = q.shape
     ns = B if n_seq is None else n_seq
     if out is None:

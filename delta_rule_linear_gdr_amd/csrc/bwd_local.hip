@@ -1004,9 +1004,9 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
 }  // namespace
 
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
-                            bool wy7, int order, hipStream_t st)
+                            bool wy7, int order, bool per_chunk, hipStream_t st)
 {
-    if (!wy7 && !s.vec) {
+    if (!wy7 && !s.vec && !per_chunk) {
         // one workgroup per CU (LDS), each taking every G-th (chunk, head)
         const int64_t n = s.NC * (s.B * s.H);
         if (n <= 0) return hipSuccess;

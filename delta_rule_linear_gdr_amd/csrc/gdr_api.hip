@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -18,6 +19,10 @@ namespace gdr {
 namespace {
 
 thread_local std::string g_last_error;
+
+// Launch form of the scalar-gate three-product local backward
+// (gdr_set_local_form); process-wide.
+std::atomic<int> g_local_form{GDR_LOCAL_PERSISTENT};
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...)
@@ -381,7 +386,10 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     // chunks' h and dh; after the reverse walk alone the last chunk's dh
     const int order = policy == GDR_RECOMPUTE ? CO_MIDDLE_OUT : CO_DESCENDING;
     e = timed(wy7 ? ST_BWD_LOCAL_WY7 : ST_BWD_LOCAL, st,
-              [&] { return launch_bwd_local(s, in, it, gr, wy7, order, st); });
+              [&] {
+                  return launch_bwd_local(s, in, it, gr, wy7, order,
+                                          g_local_form.load() == GDR_LOCAL_PER_CHUNK, st);
+              });
     if (e != hipSuccess) return hip_fail(e, "bwd_local");
     return GDR_OK;
 }
@@ -774,6 +782,13 @@ int gdr_profile_end(gdr_stage_time* out, int cap, int* n_out)
     if (n_out) *n_out = n;
     if (P.overflow) return fail(GDR_ERR_WORKSPACE, "more launches than max_launches; tail not timed");
     return GDR_OK;
+}
+
+int gdr_set_local_form(int form)
+{
+    if (form != GDR_LOCAL_PERSISTENT && form != GDR_LOCAL_PER_CHUNK)
+        return fail(GDR_ERR_INVALID, "unknown local-backward launch form %d", form);
+    return g_local_form.exchange(form);
 }
 
 int gdr_version(void) { return 1; }

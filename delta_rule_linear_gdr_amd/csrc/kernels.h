@@ -259,7 +259,10 @@ hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int
 hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 // order: the ChunkOrder of the (chunk, head) items (regular batches).
+// per_chunk: launch the scalar-gate three-product kernel one workgroup per
+// (chunk, head), like the other local kernels, instead of its persistent
+// form (same results; for like-for-like timing against the seven-product one).
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
-                            bool wy7, int order, hipStream_t st);
+                            bool wy7, int order, bool per_chunk, hipStream_t st);
 
 }  // namespace gdr

@@ -185,6 +185,19 @@ typedef struct {
 int gdr_profile_begin(int max_launches);
 int gdr_profile_end(gdr_stage_time* out, int cap, int* n_out);
 
+/* Launch form of the scalar-gate three-product local backward, for
+ * like-for-like timing of the ablation (process-wide; set it between calls,
+ * not during one). GDR_LOCAL_PERSISTENT (the default): one workgroup per
+ * compute unit walks its share of the (chunk, head) items and streams the
+ * next item's per-chunk states into LDS meanwhile. GDR_LOCAL_PER_CHUNK: one
+ * workgroup per (chunk, head), the form the vector-gate and seven-product
+ * local kernels always use. Both compute the same arithmetic; the two
+ * instantiations may round the fp32 gate and beta reductions differently
+ * in the last bits.
+ * Returns the previous form, or GDR_ERR_INVALID for an unknown one. */
+typedef enum { GDR_LOCAL_PERSISTENT = 0, GDR_LOCAL_PER_CHUNK = 1 } gdr_local_form;
+int gdr_set_local_form(int form);
+
 const char* gdr_status_string(int status);
 const char* gdr_last_error(void);
 int gdr_version(void);

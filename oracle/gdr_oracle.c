@@ -13,8 +13,8 @@
  *            q, k, v, the log decay g, the write weight beta and h0.
  * Gradients are taken against exactly these inputs: g is the log decay
  * (a = exp(g)) and beta the post-activation weight; any normalisation or
- * activation in front of them is the caller's chain rule (Sec. 2.2: "outer
- * normalization and gate activations handled by the chain rule").
+ * activation in front of them is the caller's chain rule (Sec. 2.2 leaves
+ * normalisation and gate activations to the surrounding chain rule).
  *
  * Layouts (row-major): q, k [B,T,H,DK]; v, o, dO [B,T,H,DV]; g [B,T,H]
  * (scalar gate) or [B,T,H,DK] (vector gate); beta [B,T,H];

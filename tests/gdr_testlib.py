@@ -119,6 +119,35 @@ def compare(gpu, x, heads=None, names=None, report=None):
     return errs
 
 
+def compare_all_heads(gpu, x, report=None):
+    """Every (b, h) pair of the workload: one threaded oracle call for the
+    whole problem, then the acceptance rule per tensor over all heads and,
+    so that an error confined to one head or batch entry cannot hide in the
+    total, per tensor on every (b, h) pair on its own."""
+    o, ht = oracle.token_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"])
+    ref = oracle.token_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["h0"], x["dO"], x["dht"])
+    ref.update(o=o, ht=ht)
+    B, _, H = x["q"].shape[:3]
+    errs = {}
+    for n in ("o", "ht", "dq", "dk", "dv", "dg", "dbeta", "dh0"):
+        if n not in gpu:
+            continue
+        errs[n] = check(n, gpu[n], ref[n])
+        worst = 0.0
+        for b in range(B):
+            for h in range(H):
+                if n in ("ht", "dh0"):
+                    g_, r_ = gpu[n][b, h], ref[n][b, h]
+                else:
+                    g_, r_ = gpu[n][b, :, h], ref[n][b, :, h]
+                e = check(n, g_, r_)
+                worst = max(worst, e)
+        errs[n + "_worst_head"] = worst
+    if report is not None:
+        report.update(errs)
+    return errs
+
+
 # ---------------------------------------------------- packed (varlen) batches
 
 SENTINEL = 7.0  # prefilled into gradient outputs; tokens of no sequence keep it

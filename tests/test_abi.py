@@ -211,3 +211,4 @@ def test_narrow_widths_workspace(gate, dk, dv):
             if gate == 1:
                 pad += 2 * al(rows * 128 * 4)
             assert sc == sc2 + pad
+
