@@ -40,7 +40,7 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
 EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
-           "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
+           "gdr_bwd_noalloc", "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
            "gdr_profile_begin",
            "gdr_profile_end", "gdr_set_local_form", "gdr_status_string", "gdr_last_error",
            "gdr_version")
@@ -86,6 +86,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, i32] + [p] * 16 + [sz, p]
         fn.restype = i32
+    lib.gdr_bwd_noalloc.argtypes = [dp, i32] + [p] * 16
+    lib.gdr_bwd_noalloc.restype = i32
     i64 = ctypes.c_int64
     lib.gdr_workspace_size_varlen.argtypes = [dp, i64, i32, ctypes.POINTER(sz),
                                               ctypes.POINTER(sz)]

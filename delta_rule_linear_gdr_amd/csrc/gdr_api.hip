@@ -641,6 +641,40 @@ int any_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
                    scratch_bytes, stream, wy7);
 }
 
+// ---- the entry point that allocates nothing (gdr_bwd_noalloc) ----
+namespace noalloc {
+
+// The workspace of gdr_bwd_noalloc: a fixed array in each device's copy of
+// this code object, held from the library's load on that device to the end
+// of the process. Host code never passes the array's own name to a kernel
+// or a copy (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_MAX];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex mu;
+void* base[MAX_DEVICES];
+
+// The array's address on device `dev` (which must be current).
+int device_base(int dev, void** out)
+{
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(GDR_ERR_UNSUPPORTED, "device ordinal %d (at most %d devices)", dev, MAX_DEVICES);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!base[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(noalloc scratch)");
+        if (!p || ((uintptr_t)p & 255))
+            return fail(GDR_ERR_HIP, "noalloc scratch at %p is not 256-byte aligned", p);
+        base[dev] = p;
+    }
+    *out = base[dev];
+    return GDR_OK;
+}
+
+}  // namespace noalloc
+
 }  // namespace
 }  // namespace gdr
 
@@ -709,6 +743,36 @@ int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int
     pk.n = n_seq;
     return any_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
                    scratch, scratch_bytes, stream, false);
+}
+
+int gdr_bwd_noalloc(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                    const float* g, const void* beta, const float* h0, const void* dO,
+                    const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
+                    void* dbeta, float* dh0, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_policy(policy))) return rc;
+    size_t need = 0;
+    workspace_any(d, Packed{}, policy, nullptr, &need);
+    if (need > GDR_NOALLOC_SCRATCH_MAX)
+        return fail(GDR_ERR_UNSUPPORTED,
+                    "gdr_bwd_noalloc: this problem needs %zu bytes of scratch, more than the fixed "
+                    "%zu-byte array (B*H*ceil(T/64) chunk-heads too many); use gdr_bwd with a workspace",
+                    need, (size_t)GDR_NOALLOC_SCRATCH_MAX);
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if ((int)sdev != cur)
+        return fail(GDR_ERR_INVALID, "gdr_bwd_noalloc: the stream belongs to device %d, device %d is current",
+                    (int)sdev, cur);
+    void* ws = nullptr;
+    if ((rc = noalloc::device_base(cur, &ws))) return rc;
+    return any_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
+                   dh0, ws, GDR_NOALLOC_SCRATCH_MAX, stream, false);
 }
 
 int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,

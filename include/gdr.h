@@ -137,6 +137,27 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): gdr_bwd
+ * with no scratch argument. Its scratch is a fixed array of
+ * GDR_NOALLOC_SCRATCH_MAX bytes inside the library, one per device, held
+ * from the library's first use on that device until the process ends; the
+ * call itself allocates nothing. Same arguments (minus scratch), results and
+ * errors as gdr_bwd for a regular batch; the stream must belong to the
+ * current device (else GDR_ERR_INVALID). A problem whose gdr_bwd scratch
+ * (gdr_workspace_size) exceeds the array returns GDR_ERR_UNSUPPORTED before
+ * anything is launched: about 270 (chunk, head) pairs under GDR_RECOMPUTE,
+ * e.g. (B, T, H) = (1, 2048, 8), about 680 under GDR_FULL_SAVE. Every call on
+ * one device shares that device's array and leaves its contents behind (the
+ * kernels write every part they read before reading it), so calls that
+ * overlap in time on one device -- on two streams, or from two threads --
+ * race on it and must not be issued. */
+#define GDR_NOALLOC_SCRATCH_MAX ((size_t)64 << 20)
+int gdr_bwd_noalloc(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                    const float* g, const void* beta, const float* h0, const void* dO,
+                    const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
+                    void* dbeta, float* dh0, void* stream);
+
 /* Packed variable-length batches (several sequences in one row of tokens,
  * the cu_seqlens convention of flash-linear-attention, which the pages'
  * reference implementation builds on). d->B must be 1; the row of d->T

@@ -212,3 +212,18 @@ def test_narrow_widths_workspace(gate, dk, dv):
                 pad += 2 * al(rows * 128 * 4)
             assert sc == sc2 + pad
 
+
+def test_noalloc_rejects_problems_past_its_array():
+    """gdr_bwd_noalloc refuses, before any device call, a problem whose
+    scratch exceeds the library's fixed array (GDR_NOALLOC_SCRATCH_MAX)."""
+    src = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    m = re.search(r"#define GDR_NOALLOC_SCRATCH_MAX \(\(size_t\)(\d+) << (\d+)\)", src)
+    cap = int(m.group(1)) << int(m.group(2))
+    lib = gdr.load()
+    fits = _desc(T=2048, H=8)
+    too_big = _desc(T=2048, H=9)
+    assert _ws(fits)[2] <= cap < _ws(too_big)[2]
+    rc = lib.gdr_bwd_noalloc(ctypes.byref(too_big), 0, *([None] * 15), None)
+    assert rc == -2 and b"fixed" in lib.gdr_last_error()
+    rc = lib.gdr_bwd_noalloc(ctypes.byref(_desc(DK=200)), 0, *([None] * 15), None)
+    assert rc == -2
