@@ -16,10 +16,15 @@ states scaled by 0.1; log gates from a log-sigmoid; weights in (0, 1)):
     dO ~ N(0, 1)                                    [B,T,H,DV]
     h0  = h0_std  * N(0, 1)                         [B,H,DK,DV]  (only if h0_std > 0)
     dht = dht_std * N(0, 1)                         [B,H,DK,DV]  (only if dht_std > 0)
+    GDN2 only (gate "gdn2": per-key-channel gate_pre as for "vector"):
+    ers_pre ~ N(0, 1) [B,T,H,DK], wrt_pre ~ N(0, 1) [B,T,H,DV]
   q = q_raw / |q_raw| / sqrt(DK);  k = k_raw / |k_raw|   (per token and head)
   g = log_sigmoid(gate_pre)  (stored fp32);  beta = sigmoid(beta_pre)
-  q, k, v, beta, dO are rounded to the storage dtype (bf16: round-to-nearest-
-  even through fp32); g, h0, dht are fp32.
+  GDN2: erase ers = sigmoid(ers_pre), write wrt = sigmoid(wrt_pre) (weights in
+  (0, 1) per channel, like beta; the paper's main experiments keep the
+  erase/write weights in the input format, Sec. 3.5)
+  q, k, v, beta, dO (and ers, wrt) are rounded to the storage dtype (bf16:
+  round-to-nearest-even through fp32); g, h0, dht are fp32.
 Every returned array is float64 holding exactly the rounded values, so a
 reference computed from them sees the same numbers as the device.
 """
@@ -93,12 +98,20 @@ def make_inputs(B, T, H, DK=128, DV=128, gate="scalar", dtype="bf16", seed=0,
     q_raw = rng.standard_normal((B, T, H, DK))
     k_raw = rng.standard_normal((B, T, H, DK))
     v = rng.standard_normal((B, T, H, DV))
+    if gate not in ("scalar", "vector", "gdn2"):
+        raise ValueError(f"unknown gate {gate!r}")
     gshape = (B, T, H) if gate == "scalar" else (B, T, H, DK)
     gate_pre = rng.standard_normal(gshape) + gate_mean
     beta_pre = rng.standard_normal((B, T, H))
     dO = rng.standard_normal((B, T, H, DV))
     h0 = h0_std * rng.standard_normal((B, H, DK, DV)) if h0_std > 0 else np.zeros((B, H, DK, DV))
     dht = dht_std * rng.standard_normal((B, H, DK, DV)) if dht_std > 0 else np.zeros((B, H, DK, DV))
+    extra = {}
+    if gate == "gdn2":
+        ers_pre = rng.standard_normal((B, T, H, DK))
+        wrt_pre = rng.standard_normal((B, T, H, DV))
+        extra["ers"] = round_to(1.0 / (1.0 + np.exp(-ers_pre)), dtype)
+        extra["wrt"] = round_to(1.0 / (1.0 + np.exp(-wrt_pre)), dtype)
     qn = np.linalg.norm(q_raw, axis=-1, keepdims=True)
     kn = np.linalg.norm(k_raw, axis=-1, keepdims=True)
     q = q_raw / np.maximum(qn, 1e-30) / np.sqrt(DK)
@@ -109,7 +122,7 @@ def make_inputs(B, T, H, DK=128, DV=128, gate="scalar", dtype="bf16", seed=0,
         q=round_to(q, dtype), k=round_to(k, dtype), v=round_to(v, dtype),
         g=round_fp32(g), beta=round_to(beta, dtype), dO=round_to(dO, dtype),
         h0=round_fp32(h0), dht=round_fp32(dht),
-        gate=gate, dtype=dtype,
+        gate=gate, dtype=dtype, **extra,
     )
 
 

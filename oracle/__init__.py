@@ -10,6 +10,10 @@ Contents
   token_fwd / token_bwd   ctypes wrappers of ``gdr_oracle.c``: the plain
                           token-by-token recurrence (ReWY paper, Sec. 2.2,
                           Table 1) and its hand-derived reverse mode.
+  gdn2_fwd / gdn2_bwd     the same for GDN2 (paper Table 1: per-key-channel
+                          decay, independent erase gate per key channel and
+                          write gate per value channel, in place of beta),
+                          and gdn2_fwd_complex.
   token_fwd_complex       the same recurrence in complex arithmetic, for
                           complex-step derivative checks (paper Sec. 4.5 and
                           App. G.3 name CPU FP64 and complex-step checks).
@@ -61,6 +65,12 @@ def _load():
     lib.gdr_oracle_fwd_complex.restype = i32
     lib.gdr_oracle_bwd.argtypes = [i64] * 5 + [i32] + [p] * 14 + [i32]
     lib.gdr_oracle_bwd.restype = i32
+    lib.gdr_oracle_gdn2_fwd.argtypes = [i64] * 5 + [p] * 9 + [i32]
+    lib.gdr_oracle_gdn2_fwd.restype = i32
+    lib.gdr_oracle_gdn2_fwd_complex.argtypes = [i64] * 5 + [p] * 9
+    lib.gdr_oracle_gdn2_fwd_complex.restype = i32
+    lib.gdr_oracle_gdn2_bwd.argtypes = [i64] * 5 + [p] * 16 + [i32]
+    lib.gdr_oracle_gdn2_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -138,4 +148,61 @@ def token_bwd(q, k, v, g, beta, h0, dO, dht=None, threads: int | None = None):
                             threads or default_threads())
     if rc != 0:
         raise RuntimeError(f"gdr_oracle_bwd failed ({rc})")
+    return out
+
+
+def gdn2_fwd(q, k, v, g, ers, wrt, h0=None, threads: int | None = None):
+    """GDN2 forward in fp64: g, ers [B,T,H,DK], wrt [B,T,H,DV]. Returns (o, ht)."""
+    lib = _load()
+    q, k, v, g, ers, wrt = (_arr(x) for x in (q, k, v, g, ers, wrt))
+    h0 = None if h0 is None else _arr(h0)
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    assert g.shape == (B, T, H, DK) and ers.shape == (B, T, H, DK) and wrt.shape == (B, T, H, DV)
+    o = np.zeros((B, T, H, DV))
+    ht = np.zeros((B, H, DK, DV))
+    rc = lib.gdr_oracle_gdn2_fwd(B, T, H, DK, DV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(ers),
+                                 _ptr(wrt), _ptr(h0), _ptr(o), _ptr(ht),
+                                 threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"gdr_oracle_gdn2_fwd failed ({rc})")
+    return o, ht
+
+
+def gdn2_fwd_complex(q, k, v, g, ers, wrt, h0=None):
+    """GDN2 forward in complex128 (single thread), for complex-step checks."""
+    lib = _load()
+    c = np.complex128
+    q, k, v, g, ers, wrt = (_arr(x, c) for x in (q, k, v, g, ers, wrt))
+    h0 = None if h0 is None else _arr(h0, c)
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    o = np.zeros((B, T, H, DV), c)
+    ht = np.zeros((B, H, DK, DV), c)
+    rc = lib.gdr_oracle_gdn2_fwd_complex(B, T, H, DK, DV, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(ers), _ptr(wrt), _ptr(h0), _ptr(o), _ptr(ht))
+    if rc != 0:
+        raise RuntimeError(f"gdr_oracle_gdn2_fwd_complex failed ({rc})")
+    return o, ht
+
+
+def gdn2_bwd(q, k, v, g, ers, wrt, h0, dO, dht=None, threads: int | None = None):
+    """Exact GDN2 gradients of <o, dO> + <ht, dht>. Returns dict dq, dk, dv,
+    dg, ders, dwrt, dh0."""
+    lib = _load()
+    q, k, v, g, ers, wrt, dO = (_arr(x) for x in (q, k, v, g, ers, wrt, dO))
+    h0 = None if h0 is None else _arr(h0)
+    dht = None if dht is None else _arr(dht)
+    B, T, H, DK = q.shape
+    DV = v.shape[-1]
+    out = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "dg": np.zeros_like(g), "ders": np.zeros_like(ers), "dwrt": np.zeros_like(wrt),
+           "dh0": np.zeros((B, H, DK, DV))}
+    rc = lib.gdr_oracle_gdn2_bwd(B, T, H, DK, DV, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(ers),
+                                 _ptr(wrt), _ptr(h0), _ptr(dO), _ptr(dht), _ptr(out["dq"]),
+                                 _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                                 _ptr(out["ders"]), _ptr(out["dwrt"]), _ptr(out["dh0"]),
+                                 threads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"gdr_oracle_gdn2_bwd failed ({rc})")
     return out

@@ -57,6 +57,11 @@ Consumers of D and Hb:
              windows are this implementation's reading of the "subchunk path"
              that the repository page's "Compatibility" section gives stronger
              gates.)
+GDN2 (paper Table 1: independent vector erase and write gates in place of
+the shared beta; pass ers (T, DK) and wrt (T, DV) with beta None): the same
+forms with E = ers o gam o K and Z = wrt o V; the chain rules then give
+dv = wrt o Zb, dwrt = v o Zb, dk's erase term ers o gam o Eb and
+ders = gam o k o Eb, entry by entry (no sum over channels).
 Readings where the pages are silent are the ones listed with the design notes:
 decay before erase, inclusive output, key-major state, undivided dbeta.
 """
@@ -100,10 +105,20 @@ def _gate_parts(gc, vec, DK):
     return G
 
 
-def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
+def _erase_write(beta, ers, wrt, s, e):
+    """Per-row erase and write weights of rows s..e: (n, 1) columns of the
+    shared beta, or the GDN2 gates (n, DK) and (n, DV)."""
+    if ers is not None:
+        return ers[s:e], wrt[s:e]
+    b = beta[s:e][:, None]
+    return b, b
+
+
+def chunk_forward(q, k, v, g, beta, h0, C, keep=False, ers=None, wrt=None):
     """Chunkwise forward of one (b, h) sequence.
 
     q, k: (T, DK); v: (T, DV); g: (T,) or (T, DK); beta: (T,); h0: (DK, DV).
+    GDN2: beta None, ers (T, DK), wrt (T, DV).
     Returns o (T, DV), ht (DK, DV) and, if keep, the per-chunk intermediates.
     """
     T, DK = q.shape
@@ -114,12 +129,13 @@ def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
     cache = []
     for s, e in _chunks(T, C):
         n = e - s
-        Q, K, V, bt = q[s:e], k[s:e], v[s:e], beta[s:e]
+        Q, K, V = q[s:e], k[s:e], v[s:e]
+        be, bw = _erase_write(beta, ers, wrt, s, e)
         G = _gate_parts(g[s:e], vec, DK)
         gam = np.exp(G)
-        E = bt[:, None] * gam * K
+        E = be * gam * K
         Y = K / gam
-        Z = bt[:, None] * V
+        Z = bw * V
         Qg = gam * Q
         Kt = np.exp(G[-1][None, :] - G) * K
         L = _tril(E @ Y.T, -1)
@@ -137,7 +153,7 @@ def chunk_forward(q, k, v, g, beta, h0, C, keep=False):
 
 
 def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="direct",
-                   flops: FlopCounter | None = None, centre=None, window=16):
+                   flops: FlopCounter | None = None, centre=None, window=16, ers=None, wrt=None):
     """Chunkwise backward of one (b, h) sequence.
 
     producer: "rewy" (three products) or "wy7" (expanded graph).
@@ -146,16 +162,22 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
     centre:   optional override of the centring constants, a function
               (G (n, DK)) -> c (DK,), used to test centring invariance.
     window:   window length of the "windowed" consumer.
-    Returns dict dq, dk, dv, dg, dbeta, dh0.
+    GDN2: beta None, ers (T, DK), wrt (T, DV) ("direct" and "windowed").
+    Returns dict dq, dk, dv, dg, dbeta (GDN2: ders, dwrt), dh0.
     """
     fc = flops if flops is not None else FlopCounter()
     mm = fc.mm
     T, DK = q.shape
     DV = v.shape[1]
     vec = g.ndim == 2
+    gdn2 = ers is not None
     if consumer == "gram" and vec:
         raise ValueError("Gram elimination applies to a scalar gate")
-    _, _, cache = chunk_forward(q, k, v, g, beta, h0, C, keep=True)
+    if gdn2 and consumer not in ("direct", "windowed"):
+        raise ValueError("GDN2 takes the direct or windowed consumer")
+    _, _, cache = chunk_forward(q, k, v, g, beta, h0, C, keep=True, ers=ers, wrt=wrt)
+    ders = np.zeros((T, DK)) if gdn2 else None
+    dwrt = np.zeros((T, DV)) if gdn2 else None
     dq = np.zeros_like(q, dtype=np.float64)
     dk = np.zeros_like(k, dtype=np.float64)
     dv = np.zeros_like(v, dtype=np.float64)
@@ -166,7 +188,10 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
         s, e = ch["s"], ch["e"]
         S, G, gam, E, Y, Z, Qg, Kt, A, W, R, Hm = (ch[x] for x in (
             "S", "G", "gam", "E", "Y", "Z", "Qg", "Kt", "A", "W", "R", "Hm"))
-        Q, K, V, bt, Ob = q[s:e], k[s:e], v[s:e], beta[s:e], dO[s:e]
+        Q, K, V, Ob = q[s:e], k[s:e], v[s:e], dO[s:e]
+        be, bw = _erase_write(beta, ers, wrt, s, e)
+        bt = None if gdn2 else beta[s:e]
+        de_c = np.zeros((e - s, DK))
         gn = gam[-1]
         Rb = Hm.T @ Ob + Kt @ Sbn
         # --- local WY producer ---
@@ -228,7 +253,7 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
                         p_lo = G[b1 - 1]                 # last token of window b
                         p_up = G[a0]                     # first token of window a
                     Hb_ab, D_ab = Hb[a0:a1, b0:b1], D[a0:a1, b0:b1]
-                    Ki, Qi, bi = K[a0:a1], Q[a0:a1], bt[a0:a1]
+                    Ki, Qi, bi = K[a0:a1], Q[a0:a1], be[a0:a1]
                     Kj = K[b0:b1]
                     # rows i: Hb Y' and D Y', scaled back by exp(G_i - p_lo)
                     al = np.exp(Gi - p_lo)
@@ -236,12 +261,15 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
                     uq = al * (Hb_ab @ Yp)
                     ue = al * (D_ab @ Yp)
                     dq_c[a0:a1] += uq
-                    dk_c[a0:a1] += bi[:, None] * ue
-                    db_c[a0:a1] += np.sum(ue * Ki, axis=1)
-                    Gb[a0:a1] += Qi * uq + bi[:, None] * Ki * ue
+                    dk_c[a0:a1] += bi * ue
+                    if gdn2:
+                        de_c[a0:a1] += ue * Ki
+                    else:
+                        db_c[a0:a1] += np.sum(ue * Ki, axis=1)
+                    Gb[a0:a1] += Qi * uq + bi * Ki * ue
                     # columns j: Hb^T Q' + D^T E', scaled back by exp(p_up - G_j)
                     al2 = np.exp(Gi - p_up)
-                    uy = np.exp(p_up - Gj) * (Hb_ab.T @ (al2 * Qi) + D_ab.T @ (bi[:, None] * al2 * Ki))
+                    uy = np.exp(p_up - Gj) * (Hb_ab.T @ (al2 * Qi) + D_ab.T @ (bi * al2 * Ki))
                     dk_c[b0:b1] += uy
                     Gb[b0:b1] -= Kj * uy
         elif consumer == "centred":
@@ -262,9 +290,14 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
             raise ValueError(consumer)
         # --- feature-local chain rules for the remaining terms ---
         dq_c += gam * Qgb
-        dv[s:e] = bt[:, None] * Zb
-        db_c += np.sum(Zb * V, axis=1) + np.sum(Eb * gam * K, axis=1)
-        dk_c += bt[:, None] * gam * Eb + Yb / gam + np.exp(G[-1][None, :] - G) * Ktb
+        dv[s:e] = bw * Zb
+        if gdn2:
+            dwrt[s:e] = Zb * V
+            de_c += Eb * gam * K
+            ders[s:e] = de_c
+        else:
+            db_c += np.sum(Zb * V, axis=1) + np.sum(Eb * gam * K, axis=1)
+        dk_c += be * gam * Eb + Yb / gam + np.exp(G[-1][None, :] - G) * Ktb
         Gb += Qg * Qgb + E * Eb - Y * Yb - Kt * Ktb
         Gb[-1] += np.sum(Kt * Ktb, axis=0) + gn * np.sum(S * Sbn, axis=1)
         Gtok = Gb if vec else Gb.sum(axis=1)
@@ -274,6 +307,8 @@ def chunk_backward(q, k, v, g, beta, h0, dO, dht, C, producer="rewy", consumer="
         dbeta[s:e] = db_c
         # --- reverse state scan ---
         Sbn = gn[:, None] * Sbn + Qg.T @ Ob + Sb_res
+    if gdn2:
+        return dict(dq=dq, dk=dk, dv=dv, dg=dg, ders=ders, dwrt=dwrt, dh0=Sbn)
     return dict(dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, dh0=Sbn)
 
 

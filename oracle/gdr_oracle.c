@@ -35,6 +35,15 @@
  * and dh0 = Xb^T at the start. The states needed in reverse are rebuilt from
  * checkpoints taken every 64 tokens.
  *
+ * GDN2 (gdr_oracle_gdn2_*; paper Table 1: vector decay with independent
+ * vector erase and write gates, Sec. 3.1 keeps their gradients separate;
+ * the step is in token_fwd_body.h). Per token, with s = Xb k_t after the
+ * output adjoint is added, P = X_{t-1} Diag(a_t) and e = wrt o v - P (ers o k):
+ *   dv_t = wrt_t o s              dwrt_t = v_t o s
+ *   dk_t = Xb^T e - ers_t o (P^T s)          ders_t = -k_t o (P^T s)
+ *   Pb   = Xb - s (ers_t o k_t)^T
+ * and the decay and state adjoints as above.
+ *
  * Threads split the work over (b, h, block of value rows); per-row-block
  * partial sums of dq, dk, dbeta and dg are added in a fixed order, so the
  * result does not depend on the thread count or scheduling.
@@ -69,7 +78,9 @@ typedef struct {
     int vec_gate;
     int64_t nvb, rows;  /* value-row blocks per head, rows per block */
     const double *q, *k, *v, *g, *beta, *h0, *dO, *dht;
+    const double *ers, *wrt;   /* GDN2 gates (NULL otherwise) */
     double *o, *ht, *dq, *dk, *dv, *dg, *dbeta, *dh0;
+    double *ders, *dwrt;       /* GDN2 gate gradients */
     double* part;       /* per-item partials when nvb > 1 */
     int64_t part_w;     /* doubles per token in a partial row */
     int64_t next;       /* work counter (atomic) */
@@ -94,7 +105,7 @@ static void* fwd_worker(void* arg)
         if (v1 > J->DV) v1 = J->DV;
         if (v0 >= v1) continue;
         fwd_rows_d(J->T, J->H, J->DK, J->DV, J->vec_gate, b, h, v0, v1, J->q, J->k, J->v,
-                   J->g, J->beta, J->h0, J->o, J->ht, X, X + J->rows * J->DK);
+                   J->g, J->beta, J->ers, J->wrt, J->h0, J->o, J->ht, X, X + J->rows * J->DK);
     }
     free(X);
     return NULL;
@@ -135,18 +146,38 @@ static void split_rows(job_t* J)
     J->nitems = bh * J->nvb;
 }
 
-int gdr_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
+static int fwd_any(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
                    const double* q, const double* k, const double* v, const double* g,
-                   const double* beta, const double* h0, double* o, double* ht, int nthreads)
+                   const double* beta, const double* ers, const double* wrt, const double* h0,
+                   double* o, double* ht, int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || DK < 1 || DV < 1) return 1;
     job_t J;
     memset(&J, 0, sizeof J);
     J.B = B; J.T = T; J.H = H; J.DK = DK; J.DV = DV; J.vec_gate = vec_gate;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0; J.o = o; J.ht = ht;
+    J.ers = ers; J.wrt = wrt;
     if (B * H == 0) return 0;
     split_rows(&J);
     return run_threads(&J, fwd_worker, nthreads);
+}
+
+int gdr_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
+                   const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, const double* h0, double* o, double* ht, int nthreads)
+{
+    return fwd_any(B, T, H, DK, DV, vec_gate, q, k, v, g, beta, NULL, NULL, h0, o, ht, nthreads);
+}
+
+/* GDN2: per-key-channel log decay g [B,T,H,DK], erase gate ers [B,T,H,DK],
+ * write gate wrt [B,T,H,DV]. */
+int gdr_oracle_gdn2_fwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV,
+                        const double* q, const double* k, const double* v, const double* g,
+                        const double* ers, const double* wrt, const double* h0, double* o,
+                        double* ht, int nthreads)
+{
+    if (!ers || !wrt) return 1;
+    return fwd_any(B, T, H, DK, DV, 1, q, k, v, g, NULL, ers, wrt, h0, o, ht, nthreads);
 }
 
 /* Complex-step forward: same recurrence in double complex, single thread.
@@ -162,7 +193,24 @@ int gdr_oracle_fwd_complex(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t 
     if (!X) return 1;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < H; ++h)
-            fwd_rows_z(T, H, DK, DV, vec_gate, b, h, 0, DV, q, k, v, g, beta, h0, o, ht, X,
+            fwd_rows_z(T, H, DK, DV, vec_gate, b, h, 0, DV, q, k, v, g, beta, NULL, NULL, h0, o, ht,
+                       X, X + DV * DK);
+    free(X);
+    return 0;
+}
+
+int gdr_oracle_gdn2_fwd_complex(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV,
+                                const double complex* q, const double complex* k,
+                                const double complex* v, const double complex* g,
+                                const double complex* ers, const double complex* wrt,
+                                const double complex* h0, double complex* o, double complex* ht)
+{
+    if (B < 0 || T < 0 || H < 0 || DK < 1 || DV < 1 || !ers || !wrt) return 1;
+    double complex* X = (double complex*)malloc(sizeof(double complex) * (size_t)(DV * DK + DK));
+    if (!X) return 1;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            fwd_rows_z(T, H, DK, DV, 1, b, h, 0, DV, q, k, v, g, NULL, ers, wrt, h0, o, ht, X,
                        X + DV * DK);
     free(X);
     return 0;
@@ -179,8 +227,21 @@ static void step_fwd(const job_t* J, int64_t b, int64_t h, int64_t t, int64_t v0
     const int64_t tok = (b * J->T + t) * J->H + h;
     const double* kt = J->k + tok * DK;
     const double* vt = J->v + tok * J->DV;
-    const double bt = J->beta[tok];
     for (int64_t j = 0; j < DK; ++j) a[j] = exp(J->vec_gate ? J->g[tok * DK + j] : J->g[tok]);
+    if (J->ers) {
+        /* GDN2: u = P (ers o k), e = wrt o v - u, X = P + e k^T */
+        const double* et = J->ers + tok * DK;
+        const double* wt = J->wrt + tok * J->DV;
+        for (int64_t r = 0; r < nr; ++r) {
+            double* x = X + r * DK;
+            double u = 0;
+            for (int64_t j = 0; j < DK; ++j) { x[j] *= a[j]; u += x[j] * (et[j] * kt[j]); }
+            const double e = wt[v0 + r] * vt[v0 + r] - u;
+            for (int64_t j = 0; j < DK; ++j) x[j] += e * kt[j];
+        }
+        return;
+    }
+    const double bt = J->beta[tok];
     for (int64_t r = 0; r < nr; ++r) {
         double* x = X + r * DK;
         double u = 0;
@@ -250,17 +311,67 @@ static void* bwd_worker(void* arg)
                 const double* kt = J->k + tok * DK;
                 const double* vt = J->v + tok * DV;
                 const double* dot = J->dO + tok * DV;
-                const double bt = J->beta[tok];
                 const double* Xp = seg + (size_t)(t - ts) * st;      /* X_{t-1} */
                 const double* Xc = seg + (size_t)(t - ts + 1) * st;  /* X_t */
                 const int64_t gw = J->vec_gate ? DK : 1;
+                memset(acc, 0, sizeof(double) * (size_t)J->part_w);
+                for (int64_t j = 0; j < DK; ++j) a[j] = exp(J->vec_gate ? J->g[tok * DK + j] : J->g[tok]);
+                if (J->ers) {
+                    /* GDN2; acc layout: [dq DK | dk DK | ders DK | dg DK] */
+                    const double* et = J->ers + tok * DK;
+                    const double* wt = J->wrt + tok * DV;
+                    double* adq = acc;
+                    double* adk = acc + DK;
+                    double* ade = acc + 2 * DK;
+                    double* adg = acc + 3 * DK;
+                    for (int64_t r = 0; r < nr; ++r) {
+                        double u = 0;
+                        for (int64_t j = 0; j < DK; ++j) {
+                            Pm[r * DK + j] = Xp[r * DK + j] * a[j];
+                            u += Pm[r * DK + j] * (et[j] * kt[j]);
+                        }
+                        e[r] = wt[v0 + r] * vt[v0 + r] - u;
+                    }
+                    for (int64_t r = 0; r < nr; ++r) {
+                        const double dor = dot[v0 + r];
+                        double* xb = Xb + r * DK;
+                        double sr = 0;
+                        for (int64_t j = 0; j < DK; ++j) {
+                            xb[j] += dor * qt[j];                 /* Xb += dO q^T */
+                            adq[j] += Xc[r * DK + j] * dor;       /* dq = X_t^T dO */
+                            sr += xb[j] * kt[j];                  /* s = Xb k (adjoint of e) */
+                        }
+                        J->dv[tok * DV + v0 + r] = wt[v0 + r] * sr;     /* dv = wrt o s */
+                        J->dwrt[tok * DV + v0 + r] = vt[v0 + r] * sr;   /* dwrt = v o s */
+                        for (int64_t j = 0; j < DK; ++j) {
+                            const double ps = Pm[r * DK + j] * sr;       /* (P^T s)_j part */
+                            adk[j] += xb[j] * e[r] - et[j] * ps;
+                            ade[j] -= kt[j] * ps;
+                            const double pb = xb[j] - sr * (et[j] * kt[j]);  /* Pb */
+                            adg[j] += Xp[r * DK + j] * pb * a[j];
+                            xb[j] = pb * a[j];                           /* Xb <- Pb Diag(a) */
+                        }
+                    }
+                    if (direct) {
+                        for (int64_t j = 0; j < DK; ++j) {
+                            J->dq[tok * DK + j] = adq[j];
+                            J->dk[tok * DK + j] = adk[j];
+                            J->ders[tok * DK + j] = ade[j];
+                            J->dg[tok * DK + j] = adg[j];
+                        }
+                    } else {
+                        double* p = J->part + ((size_t)(bh * J->nvb + vb) * (size_t)T + (size_t)t) *
+                                                  (size_t)J->part_w;
+                        memcpy(p, acc, sizeof(double) * (size_t)J->part_w);
+                    }
+                    continue;
+                }
+                const double bt = J->beta[tok];
                 /* acc layout: [dq DK | dk DK | dbeta 1 | dg gw] */
                 double* adq = acc;
                 double* adk = acc + DK;
                 double* adb = acc + 2 * DK;
                 double* adg = acc + 2 * DK + 1;
-                memset(acc, 0, sizeof(double) * (size_t)J->part_w);
-                for (int64_t j = 0; j < DK; ++j) a[j] = exp(J->vec_gate ? J->g[tok * DK + j] : J->g[tok]);
                 /* P = X_{t-1} Diag(a), e = v - P k */
                 for (int64_t r = 0; r < nr; ++r) {
                     double u = 0;
@@ -315,10 +426,11 @@ out:
     return NULL;
 }
 
-int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
+static int bwd_any(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
                    const double* q, const double* k, const double* v, const double* g,
-                   const double* beta, const double* h0, const double* dO, const double* dht,
-                   double* dq, double* dk, double* dv, double* dg, double* dbeta, double* dh0,
+                   const double* beta, const double* ers, const double* wrt, const double* h0,
+                   const double* dO, const double* dht, double* dq, double* dk, double* dv,
+                   double* dg, double* dbeta, double* ders, double* dwrt, double* dh0,
                    int nthreads)
 {
     if (B < 0 || T < 0 || H < 0 || DK < 1 || DV < 1) return 1;
@@ -327,6 +439,7 @@ int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int 
     J.B = B; J.T = T; J.H = H; J.DK = DK; J.DV = DV; J.vec_gate = vec_gate;
     J.q = q; J.k = k; J.v = v; J.g = g; J.beta = beta; J.h0 = h0; J.dO = dO; J.dht = dht;
     J.dq = dq; J.dk = dk; J.dv = dv; J.dg = dg; J.dbeta = dbeta; J.dh0 = dh0;
+    J.ers = ers; J.wrt = wrt; J.ders = ders; J.dwrt = dwrt;
     if (B * H == 0) return 0;
     if (T == 0) {
         if (dh0)
@@ -334,8 +447,9 @@ int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int 
         return 0;
     }
     split_rows(&J);
+    const int gdn2 = ers != NULL;
     const int64_t gw = vec_gate ? DK : 1;
-    J.part_w = 2 * DK + 1 + gw;
+    J.part_w = gdn2 ? 4 * DK : 2 * DK + 1 + gw;
     if (J.nvb > 1) {
         J.part = (double*)malloc(sizeof(double) * (size_t)(B * H * J.nvb) * (size_t)T *
                                  (size_t)J.part_w);
@@ -355,6 +469,8 @@ int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int 
                                         (size_t)J.part_w + (size_t)x];
                     if (x < DK) dq[tok * DK + x] = s;
                     else if (x < 2 * DK) dk[tok * DK + x - DK] = s;
+                    else if (gdn2 && x < 3 * DK) ders[tok * DK + x - 2 * DK] = s;
+                    else if (gdn2) dg[tok * DK + x - 3 * DK] = s;
                     else if (x == 2 * DK) dbeta[tok] = s;
                     else dg[tok * gw + (x - 2 * DK - 1)] = s;
                 }
@@ -363,4 +479,25 @@ int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int 
     }
     free(J.part);
     return rc;
+}
+
+int gdr_oracle_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV, int vec_gate,
+                   const double* q, const double* k, const double* v, const double* g,
+                   const double* beta, const double* h0, const double* dO, const double* dht,
+                   double* dq, double* dk, double* dv, double* dg, double* dbeta, double* dh0,
+                   int nthreads)
+{
+    return bwd_any(B, T, H, DK, DV, vec_gate, q, k, v, g, beta, NULL, NULL, h0, dO, dht, dq, dk,
+                   dv, dg, dbeta, NULL, NULL, dh0, nthreads);
+}
+
+int gdr_oracle_gdn2_bwd(int64_t B, int64_t T, int64_t H, int64_t DK, int64_t DV,
+                        const double* q, const double* k, const double* v, const double* g,
+                        const double* ers, const double* wrt, const double* h0, const double* dO,
+                        const double* dht, double* dq, double* dk, double* dv, double* dg,
+                        double* ders, double* dwrt, double* dh0, int nthreads)
+{
+    if (!ers || !wrt || !ders || !dwrt) return 1;
+    return bwd_any(B, T, H, DK, DV, 1, q, k, v, g, NULL, ers, wrt, h0, dO, dht, dq, dk, dv, dg,
+                   NULL, ders, dwrt, dh0, nthreads);
 }

@@ -209,3 +209,59 @@ def test_pivoted_lower_equals_pairwise_definition(n, incl):
             ref[i, j] = np.sum(X[i] * Y[j] * np.exp(G[i] - G[j]))
     got = cf.pivoted_lower(X, Y, G, incl)
     assert np.max(np.abs(got - ref)) <= 1e-12 * max(np.max(np.abs(ref)), 1.0)
+
+
+# ------------------------------------------------------------------ GDN2
+
+def _gdn2_seq(T, DK, DV, seed=0, mean=3.0):
+    q, k, v, g, beta, h0, dO, dht = _seq("vector", T, DK, DV, seed=seed)
+    rng = np.random.default_rng(seed + 100)
+    g = -np.logaddexp(0, -(rng.standard_normal((T, DK)) + mean))
+    ers = 1 / (1 + np.exp(-rng.standard_normal((T, DK))))
+    wrt = 1 / (1 + np.exp(-rng.standard_normal((T, DV))))
+    ers[::5] = 0.0
+    wrt[1::7] = 0.0
+    return q, k, v, g, ers, wrt, h0, dO, dht
+
+
+def _gdn2_token(q, k, v, g, ers, wrt, h0, dO, dht):
+    B = lambda x: x[None, :, None]  # noqa: E731
+    o, ht = oracle.gdn2_fwd(B(q), B(k), B(v), B(g), B(ers), B(wrt), h0[None, None])
+    gr = oracle.gdn2_bwd(B(q), B(k), B(v), B(g), B(ers), B(wrt), h0[None, None], B(dO),
+                         dht[None, None])
+    gr = {n: (a[0, :, 0] if n != "dh0" else a[0, 0]) for n, a in gr.items()}
+    return o[0, :, 0], ht[0, 0], gr
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("producer, consumer", [("rewy", "direct"), ("wy7", "direct"),
+                                                ("rewy", "windowed")])
+def test_gdn2_chunk_forms_reproduce_token_oracle(C, producer, consumer):
+    """GDN2 chunk forms (E = ers o gam o K, Z = wrt o V) equal the GDN2 token
+    oracle at every chunk size with a tail, for both producers and for the
+    windowed matrix-intra consumer the device kernels use."""
+    T = 150
+    x = _gdn2_seq(T, 8, 5, seed=C)
+    q, k, v, g, ers, wrt, h0, dO, dht = x
+    o_t, ht_t, gr_t = _gdn2_token(*x)
+    o_c, ht_c = cf.chunk_forward(q, k, v, g, None, h0, C, ers=ers, wrt=wrt)
+    assert _rel(o_c, o_t) < 1e-12
+    assert _rel(ht_c, ht_t) < 1e-12
+    gr_c = cf.chunk_backward(q, k, v, g, None, h0, dO, dht, C, producer, consumer,
+                             ers=ers, wrt=wrt)
+    assert set(gr_c) == set(gr_t)
+    for n in gr_t:
+        assert _rel(gr_c[n], gr_t[n]) < 1e-10, n
+
+
+def test_gdn2_windowed_under_strong_decay():
+    """Per-token decays around e^-4 (chunk range ~256): the windowed GDN2
+    consumer stays finite and equals the token oracle."""
+    x = _gdn2_seq(130, 8, 5, seed=3, mean=-4.0)
+    q, k, v, g, ers, wrt, h0, dO, dht = x
+    _, _, gr_t = _gdn2_token(*x)
+    gr_c = cf.chunk_backward(q, k, v, g, None, h0, dO, dht, 64, "rewy", "windowed",
+                             ers=ers, wrt=wrt)
+    for n in gr_t:
+        assert np.all(np.isfinite(gr_c[n])), n
+        assert _rel(gr_c[n], gr_t[n]) < 1e-9, n
