@@ -9,6 +9,8 @@ unbuilt library raises.
     o, ht, saved = gdr_fwd(q, k, v, g, beta, h0, policy="recompute")
     grads = gdr_bwd(q, k, v, g, beta, h0, dO, dht, saved=saved, policy="recompute")
     grads = gdr_bwd_wy7(...)          # seven-product producer (ablation)
+    o, ht, saved = gdr_fwd_gdn2(q, k, v, g, erase, write, h0)      # GDN2
+    grads = gdr_bwd_gdn2(q, k, v, g, erase, write, h0, dO, dht, saved=saved)
     o, ht = chunk_gated_delta_rule(q, k, v, g, beta, h0)   # autograd-aware
 
 Shapes: q, k [B,T,H,DK]; v, dO [B,T,H,DV]; g [B,T,H] (GDN, scalar gate),
@@ -26,7 +28,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "chunk_gated_delta_rule", "workspace_size",
+__all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_fwd_gdn2", "gdr_bwd_gdn2",
+           "chunk_gated_delta_rule", "workspace_size",
            "library_path", "load",
            "profile_begin", "profile_end", "set_local_form", "GdrError", "RECOMPUTE", "FULL_SAVE"]
 
@@ -35,11 +38,12 @@ _LIB_PATH = os.path.join(_HERE, "libgdr.so")
 _lib = None
 
 RECOMPUTE, FULL_SAVE = 0, 1
-GATE_SCALAR, GATE_VECTOR, GATE_NONE = 0, 1, 2
+GATE_SCALAR, GATE_VECTOR, GATE_NONE, GATE_GDN2 = 0, 1, 2, 3
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
 EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
+           "gdr_fwd_gdn2", "gdr_bwd_gdn2",
            "gdr_bwd_noalloc", "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
            "gdr_profile_begin",
            "gdr_profile_end", "gdr_set_local_form", "gdr_status_string", "gdr_last_error",
@@ -86,6 +90,10 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = [dp, i32] + [p] * 16 + [sz, p]
         fn.restype = i32
+    lib.gdr_fwd_gdn2.argtypes = [dp, i32] + [p] * 11 + [sz, p]
+    lib.gdr_fwd_gdn2.restype = i32
+    lib.gdr_bwd_gdn2.argtypes = [dp, i32] + [p] * 18 + [sz, p]
+    lib.gdr_bwd_gdn2.restype = i32
     lib.gdr_bwd_noalloc.argtypes = [dp, i32] + [p] * 16
     lib.gdr_bwd_noalloc.restype = i32
     i64 = ctypes.c_int64
@@ -202,7 +210,7 @@ def _desc_from(q, g, v):
 
 
 def _validate(q, k, v, g, beta, n_seq=None, *, h0=None, dO=None, dht=None, out=None,
-              saved=None, saved_bytes=0, scratch=None):
+              saved=None, saved_bytes=0, scratch=None, erase=None, write=None):
     """Checks every tensor against the problem q and v define before any
     pointer reaches the library: device (one device, all of them), layout
     (contiguous), exact shape against (B, T, H, DK, DV) and the state count
@@ -227,11 +235,16 @@ def _validate(q, k, v, g, beta, n_seq=None, *, h0=None, dO=None, dht=None, out=N
             spec.append(("g", g, row, f32))
         else:
             spec.append(("g", g, tok_k, f32))
+    gdn2 = erase is not None or write is not None
+    if gdn2:
+        spec = [x for x in spec if x[0] != "beta"]
+        spec += [("erase", erase, tok_k, q.dtype), ("write", write, tok_v, q.dtype)]
     if out is not None:
         spec += [("dq", out.get("dq"), tok_k, q.dtype), ("dk", out.get("dk"), tok_k, q.dtype),
-                 ("dv", out.get("dv"), tok_v, q.dtype), ("dbeta", out.get("dbeta"), row, q.dtype),
-                 ("dh0", out.get("dh0"), state, f32)]
-        for name in ("dq", "dk", "dv", "dbeta"):
+                 ("dv", out.get("dv"), tok_v, q.dtype), ("dh0", out.get("dh0"), state, f32)]
+        gate_grads = (("derase", tok_k), ("dwrite", tok_v)) if gdn2 else (("dbeta", row),)
+        spec += [(n, out.get(n), shp, q.dtype) for n, shp in gate_grads]
+        for name in ("dq", "dk", "dv") + tuple(n for n, _ in gate_grads):
             if out.get(name) is None:
                 raise ValueError(f"out['{name}'] is required")
         if g is not None:
@@ -356,6 +369,66 @@ def gdr_bwd(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
     cu_seqlens as for gdr_fwd (the same offsets the forward ran with)."""
     return _bwd("gdr_bwd", q, k, v, g, beta, h0, dO, dht, saved, policy, want_dh0, scratch,
                 out, cu_seqlens)
+
+
+def gdr_fwd_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute", want_ht=True,
+                 scratch=None):
+    """GDN2 forward (per-key-channel gate g [B,T,H,128], erase gate [B,T,H,128]
+    per key, write gate [B,T,H,128] per value, bf16). Returns (o, ht, saved)."""
+    torch = _torch()
+    if erase is None or write is None or g is None or g.dim() != 4:
+        raise ValueError("GDN2 needs a per-channel g and both erase and write gates")
+    _validate(q, k, v, g, None, None, h0=h0, scratch=scratch, erase=erase, write=write)
+    d = _desc_from(q, g, v)
+    d.gate = GATE_GDN2
+    pol = _policy(policy)
+    lib = load()
+    saved_b, scratch_b = _sizes(d, pol, None)
+    B, T, H, _ = q.shape
+    o = torch.empty_like(v)
+    ht = torch.empty((B, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+                     device=q.device) if want_ht else None
+    saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None
+    if scratch is None:
+        scratch = _scratch(scratch_b, q.device)
+    _check(lib.gdr_fwd_gdn2(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
+                            _ptr(write), _ptr(h0), _ptr(o), _ptr(ht), _ptr(saved), _ptr(scratch),
+                            scratch.numel(), _stream()))
+    return o, ht, saved
+
+
+def gdr_bwd_gdn2(q, k, v, g, erase, write, h0, dO, dht=None, saved=None, policy="recompute",
+                 want_dh0=True, scratch=None, out=None):
+    """GDN2 backward. Returns dict dq, dk, dv, dg, derase, dwrite, dh0."""
+    torch = _torch()
+    if erase is None or write is None or g is None or g.dim() != 4:
+        raise ValueError("GDN2 needs a per-channel g and both erase and write gates")
+    if dO is None:
+        raise ValueError("dO is required")
+    d = _desc_from(q, g, v)
+    d.gate = GATE_GDN2
+    pol = _policy(policy)
+    lib = load()
+    saved_b, scratch_b = _sizes(d, pol, None)
+    if pol == FULL_SAVE and saved is None:
+        raise ValueError("the full-save backward needs the forward's saved area")
+    _validate(q, k, v, g, None, None, h0=h0, dO=dO, dht=dht, out=out, saved=saved,
+              saved_bytes=saved_b, scratch=scratch, erase=erase, write=write)
+    B, T, H, _ = q.shape
+    if out is None:
+        out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+                   dg=torch.empty_like(g), derase=torch.empty_like(erase),
+                   dwrite=torch.empty_like(write),
+                   dh0=torch.empty((B, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+                                   device=q.device) if want_dh0 else None)
+    if scratch is None:
+        scratch = _scratch(scratch_b, q.device)
+    _check(lib.gdr_bwd_gdn2(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
+                            _ptr(write), _ptr(h0), _ptr(dO), _ptr(dht), _ptr(saved),
+                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                            _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out.get("dh0")),
+                            _ptr(scratch), scratch.numel(), _stream()))
+    return out
 
 
 def gdr_bwd_wy7(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",

@@ -37,6 +37,12 @@
 //   Gbar_n += sum_j exp(G_n - G_j) k_j Ktb_j + gam_n rowsum(h o dh)
 // and dg is the chunk-local reverse cumsum of Gbar (Sec. 3.5), summed over
 // features for a scalar gate (App. E.1).
+// GDN2 (paper Table 1; its erase and write gradients stay separate, Sec. 3.1):
+// the vector-gate kernel with E = ers o gam o K and Z = wrt o V, so every
+// beta of the erase path becomes the per-(token, key) erase gate, dv = wrt o P,
+// and the gate gradients are written entry by entry instead of summed:
+// dwrt = v o P, ders = gam k o (Eb_dir + Eb_intra) (= the per-feature terms
+// the beta gradient would sum).
 //
 // Schedule (eight waves; wave w owns feature tile [16 w, 16 w + 16) of
 // every 64 x 128 product, all 64 token rows, so the chain rules and the
@@ -130,7 +136,7 @@ struct Tail {
 // requested once they have been read; the previous chunk's deferred last
 // phase (*pend) runs after this chunk's reads are issued, and this chunk's
 // is left in *pend when a next chunk follows.
-template <typename T, bool VEC, bool WY7, bool PF>
+template <typename T, bool VEC, bool WY7, bool PF, bool GD2>
 __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in, const Inter& it,
                                                 const Grads& gr, const ChunkRef& cr,
                                                 int64_t tnext, bf16x4* area, Tail<T>* pend)
@@ -194,6 +200,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     __shared__ __attribute__((aligned(16))) float sRedB[CH][NW], sRedP[CH][NW], sRedG[CH][NW];
     __shared__ float sExtra[DKD];
     __shared__ __attribute__((aligned(16))) float sEx[NW];
+    // GDN2: the chunk's erase gates (token rows, per key), rows padded by 16
+    // bytes so that the four row groups of a read fall on different banks
+    constexpr int EST = DKD + 8;
+    __shared__ __attribute__((aligned(16))) bf16 sErs[GD2 ? CH * EST : 8];
 
     const T* q = (const T*)in.q + tok0 * DKD;
     const T* k = (const T*)in.k + tok0 * DKD;
@@ -223,7 +233,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     // it stays an unconditional read in the batch) and its value replaced by
     // zero with a select.
     const int lc = l < nv ? l : nv - 1;
-    const T bload = betai[lc * Hs];
+    const T bload = GD2 ? (T)0.f : betai[lc * Hs];
     const T braw = l < nv ? bload : (T)0.f;
     float graw[VEC ? 16 : 1];
     if (VEC) {
@@ -280,6 +290,25 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         kr[m] = rv[m] ? xk : R4{};
         qr[m] = rv[m] ? xq : R4{};
     }
+    // GDN2: the erase gates of the chunk (two 16-byte row pieces per thread,
+    // for LDS) and the write gates of this lane's P entries
+    bf16x8 eraw[GD2 ? 2 : 1];
+    bf16x4 wraw[GD2 ? 4 : 1];
+    if constexpr (GD2) {
+        const bf16* ers = (const bf16*)in.ers + tok0 * DKD;
+        const bf16* wrt = (const bf16*)in.wrt + tok0 * DVD;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int id = tid + NTHR * u, i = id >> 4, c = (id & 15) * 8;
+            const bf16x8 x = *(const bf16x8*)(ers + (i < nv ? i : nv - 1) * ld + c);
+            eraw[u] = i < nv ? x : bf16x8{};
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const bf16x4 x = *(const bf16x4*)(wrt + rowc(m) * ld + 16 * w + 4 * g);
+            wraw[m] = rv[m] ? x : bf16x4{};
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. (defined here, run last or deferred) dbeta (wave 1); scalar
@@ -289,7 +318,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         return ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w));
     };
     auto last_phase = [&](T* dbo_, float* dgo_, int nv_) {
-        if (w == 1) {
+        if (!GD2 && w == 1) {
             const float sb = sum8(sRedB[l]) + sum8(sRedP[l]);
             if (l < nv_) io<T>::st(dbo_ + l * Hs, sb);
         }
@@ -379,6 +408,13 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 #pragma unroll
         for (int u = 0; u < 4; ++u) lG[u * NTHR + tid] = z8;
     }
+    if constexpr (GD2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int id = tid + NTHR * u;
+            *(bf16x8*)&sErs[(id >> 4) * EST + (id & 15) * 8] = eraw[u];
+        }
+    }
     lds_barrier();
     if (!VEC) Gnf = sG[CH - 1];
     // vector gate, this lane's key: the centre of window m (token tile m);
@@ -409,6 +445,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     // G and beta at this lane's accumulator position (tok 16 m + 4 g + e, f)
     auto Gt = [&](int m, int e) -> float { return VEC ? Gv[m][e] : Gs[VEC ? 0 : m][e]; };
     auto Bt = [&](int m, int e) -> float { return VEC ? sBeta[16 * m + 4 * g + e] : Bs[VEC ? 0 : m][e]; };
+    // the erase-path weight there: beta, or GDN2's erase gate of (token, key f)
+    auto Et = [&](int m, int e) -> float {
+        return GD2 ? (float)sErs[(16 * m + 4 * g + e) * EST + f] : Bt(m, e);
+    };
 
     const bf16x8 Ip0k = ident_pi(0, lx);
     const bf16x8 Ipw = ident_pi(w & 1, lx);
@@ -428,14 +468,29 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             const f32x4 vx = tof4(vr[m]);
             float dvv[4];
             float pv = 0.f;
+            if constexpr (GD2) {
+                // dv = wrt o P, dwrt = v o P (entry by entry)
+                const f32x4 wx = tof4(wraw[m]);
+                float dwv[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                dvv[e] = bt * acc[e];
-                pv += acc[e] * vx[e];
+                for (int e = 0; e < 4; ++e) {
+                    dvv[e] = wx[e] * acc[e];
+                    dwv[e] = vx[e] * acc[e];
+                }
+                if (i < nv) {
+                    store4(dvo + i * ld + 16 * w + 4 * g, dvv);
+                    store4((T*)gr.dwrt + tok0 * DVD + i * ld + 16 * w + 4 * g, dwv);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    dvv[e] = bt * acc[e];
+                    pv += acc[e] * vx[e];
+                }
+                if (i < nv) store4(dvo + i * ld + 16 * w + 4 * g, dvv);
+                pv = sum_rows(pv);
+                if (g == 0) sRedP[i][w] = pv;
             }
-            if (i < nv) store4(dvo + i * ld + 16 * w + 4 * g, dvv);
-            pv = sum_rows(pv);
-            if (g == 0) sRedP[i][w] = pv;
             if (!WY7) st_half(lP, m * 4 + (w >> 1), w & 1, pack4(acc));
         }
         if (WY7) {
@@ -567,7 +622,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                     const float al = __expf(d), ze = __expf(-d);
                     y[hh][e] = ze * KC[m][e];
                     qq[hh][e] = al * QC[m][e];
-                    ee[hh][e] = Bt(m, e) * al * KC[m][e];
+                    ee[hh][e] = Et(m, e) * al * KC[m][e];
                 }
             }
             B0[ks] = pack_pi(y[0], y[1]);
@@ -849,7 +904,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * m + 4 * g + e;
             const float G = Gt(m, e), gam = __expf(G), kt = __expf(Gnf - G);
-            const float bt = Bt(m, e);
+            const float bt = Et(m, e);
             // k and q back from the consumer operands (exact for the scalar
             // gate; hi + lo over the centred factor for the vector gate)
             const int ks = m >> 1, sl = 4 * (m & 1) + e;
@@ -914,14 +969,24 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                 }
             }
         }
-        // per-token sums over this wave's features
+        if constexpr (GD2) {
+            // the erase-gate gradient, entry by entry (what dbeta would sum)
+            T* deo = (T*)gr.ders + tok0 * DKD;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float bsum = sum16(br[e]);
-            const float gsum = VEC ? 0.f : sum16(Ga[e]);
-            if (r == 0) {
-                sRedB[16 * m + 4 * g + e][w] = bsum;
-                if (!VEC) sRedG[16 * m + 4 * g + e][w] = gsum;
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * m + 4 * g + e;
+                if (i < nv) io<T>::st(deo + i * ld + f, br[e]);
+            }
+        } else {
+            // per-token sums over this wave's features
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float bsum = sum16(br[e]);
+                const float gsum = VEC ? 0.f : sum16(Ga[e]);
+                if (r == 0) {
+                    sRedB[16 * m + 4 * g + e][w] = bsum;
+                    if (!VEC) sRedG[16 * m + 4 * g + e][w] = gsum;
+                }
             }
         }
         if (VEC) {
@@ -956,13 +1021,13 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     else last_phase(dbo, dgo, nv);
 }
 
-template <typename T, bool VEC, bool WY7>
+template <typename T, bool VEC, bool WY7, bool GD2 = false>
 __global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
 {
     ChunkRef cr;
     if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, cr))
         return;  // an unused slot of a packed batch
-    bwd_local_chunk<T, VEC, WY7, false>(s, in, it, gr, cr, -1, nullptr, nullptr);
+    bwd_local_chunk<T, VEC, WY7, false, GD2>(s, in, it, gr, cr, -1, nullptr, nullptr);
 }
 
 // Persistent form (scalar gate, three-product producer): workgroup b takes
@@ -994,7 +1059,7 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
     for (;;) {
         ChunkRef nxt{-1, 0, 1};
         const int64_t j = next_item(i + G, nxt);
-        bwd_local_chunk<T, false, false, true>(s, in, it, gr, cur, j < n ? nxt.t : -1, sStage[w], &pend);
+        bwd_local_chunk<T, false, false, true, false>(s, in, it, gr, cur, j < n ? nxt.t : -1, sStage[w], &pend);
         if (j >= n) break;
         i = j;
         cur = nxt;
@@ -1006,6 +1071,13 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, int order, bool per_chunk, hipStream_t st)
 {
+    if (s.gd2) {
+        // GDN2: bf16 inputs, three-product producer only (the host refuses the rest)
+        if (s.f32 || !s.vec || wy7) return hipErrorInvalidValue;
+        dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
+        bwd_local_kernel<bf16, true, false, true><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);
+        return hipGetLastError();
+    }
     if (!wy7 && !s.vec && !per_chunk) {
         // one workgroup per CU (LDS), each taking every G-th (chunk, head)
         const int64_t n = s.NC * (s.B * s.H);

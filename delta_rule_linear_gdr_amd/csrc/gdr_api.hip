@@ -169,7 +169,8 @@ int check_desc(const gdr_desc* d)
     if (d->B < 0 || d->T < 0 || d->H < 0)
         return fail(GDR_ERR_INVALID, "negative size (B=%lld T=%lld H=%lld)", (long long)d->B,
                     (long long)d->T, (long long)d->H);
-    if (d->gate != GDR_GATE_SCALAR && d->gate != GDR_GATE_VECTOR && d->gate != GDR_GATE_NONE)
+    if (d->gate != GDR_GATE_SCALAR && d->gate != GDR_GATE_VECTOR && d->gate != GDR_GATE_NONE &&
+        d->gate != GDR_GATE_GDN2)
         return fail(GDR_ERR_INVALID, "unknown gate kind %d", d->gate);
     if (d->dtype != GDR_BF16 && d->dtype != GDR_F32)
         return fail(GDR_ERR_INVALID, "unknown dtype %d", d->dtype);
@@ -194,6 +195,26 @@ int check_policy(int policy)
     return GDR_OK;
 }
 
+bool gdn2(const gdr_desc* d) { return d->gate == GDR_GATE_GDN2; }
+
+// The GDN2 entry points take the GDN2 gate kind, and only they do; GDN2 runs
+// bf16 inputs at widths 128/128 on regular batches.
+int check_gdn2(const gdr_desc* d, bool gdn2_entry)
+{
+    if (gdn2(d) != gdn2_entry)
+        return fail(GDR_ERR_INVALID, gdn2_entry
+                                         ? "gdr_*_gdn2 takes gate kind GDR_GATE_GDN2, got %d"
+                                         : "gate kind %d (GDN2) goes through gdr_fwd_gdn2 / gdr_bwd_gdn2",
+                    d->gate);
+    if (!gdn2_entry) return GDR_OK;
+    if (d->dtype != GDR_BF16)
+        return fail(GDR_ERR_UNSUPPORTED, "GDN2 is built for bf16 inputs (dtype %d)", d->dtype);
+    if (d->DK != DKD || d->DV != DVD)
+        return fail(GDR_ERR_UNSUPPORTED, "GDN2 is built for key/value width 128/128 (%lld/%lld)",
+                    (long long)d->DK, (long long)d->DV);
+    return GDR_OK;
+}
+
 // Row tensors are read with 16-byte vector accesses; the rest element-wise.
 #define REQUIRE_PTR_A(p, a)                                                            \
     do {                                                                               \
@@ -215,7 +236,8 @@ Shape make_shape(const gdr_desc* d, const Packed& pk, void* scratch)
     s.T = d->T;
     s.H = d->H;
     s.NT = nchunks(d);
-    s.vec = d->gate == GDR_GATE_VECTOR;
+    s.vec = d->gate == GDR_GATE_VECTOR || d->gate == GDR_GATE_GDN2;
+    s.gd2 = d->gate == GDR_GATE_GDN2;
     s.f32 = d->dtype == GDR_F32;
     s.NS = pk.on ? pk.n : d->B;
     s.NC = nslots(d, pk);
@@ -317,10 +339,17 @@ hipError_t timed(Stage stage, hipStream_t st, F&& launch)
     return e;
 }
 
+// GDN2 gate tensors of a call (all null otherwise).
+struct Gdn2Args {
+    const void *ers = nullptr, *wrt = nullptr;
+    void *ders = nullptr, *dwrt = nullptr;
+};
+
 int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
             const void* v, const float* g, const void* beta, const float* h0, const void* dO,
             const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta,
-            float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+            float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7,
+            const Gdn2Args& g2 = Gdn2Args{})
 {
     int rc = check_desc(d);
     if (rc) return rc;
@@ -341,7 +370,14 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
         REQUIRE_PTR_A(g, 4);
         REQUIRE_PTR_A(dg, 4);
     }
-    REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
+    if (gdn2(d)) {
+        if (wy7) return fail(GDR_ERR_UNSUPPORTED, "GDN2 has no seven-product backward");
+        if (pk.on) return fail(GDR_ERR_UNSUPPORTED, "GDN2 runs regular batches only");
+        const void *ers = g2.ers, *wrt = g2.wrt, *ders = g2.ders, *dwrt = g2.dwrt;
+        REQUIRE_PTR(ers); REQUIRE_PTR(wrt); REQUIRE_PTR(ders); REQUIRE_PTR(dwrt);
+    } else {
+        REQUIRE_PTR_A(beta, esz); REQUIRE_PTR_A(dbeta, esz);
+    }
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(dht, 4); CHECK_ALIGN(dh0, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
     const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
@@ -363,8 +399,8 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
         dg = (float*)((char*)z + gate_bytes(d));
         if ((e = zero_fill(z, d->B * d->T * d->H, st)) != hipSuccess) return hip_fail(e, "zero gate");
     }
-    Inputs in{q, k, v, beta, dO, g, h0, dht};
-    Grads gr{dq, dk, dv, dbeta, dg, dh0};
+    Inputs in{q, k, v, beta, dO, g, h0, dht, g2.ers, g2.wrt};
+    Grads gr{dq, dk, dv, dbeta, dg, dh0, g2.ders, g2.dwrt};
     e = seq_tables(s, pk, st);
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     if (policy == GDR_RECOMPUTE) {
@@ -396,7 +432,8 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
 
 int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
             const void* v, const float* g, const void* beta, const float* h0, void* o, float* ht,
-            void* saved, void* scratch, size_t scratch_bytes, void* stream)
+            void* saved, void* scratch, size_t scratch_bytes, void* stream,
+            const Gdn2Args& g2 = Gdn2Args{})
 {
     int rc = check_desc(d);
     if (rc) return rc;
@@ -412,7 +449,13 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     const int esz = d->dtype == GDR_F32 ? 4 : 2;
     REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
     if (!nogate(d)) REQUIRE_PTR_A(g, 4);
-    REQUIRE_PTR_A(beta, esz);
+    if (gdn2(d)) {
+        if (pk.on) return fail(GDR_ERR_UNSUPPORTED, "GDN2 runs regular batches only");
+        const void *ers = g2.ers, *wrt = g2.wrt;
+        REQUIRE_PTR(ers); REQUIRE_PTR(wrt);
+    } else {
+        REQUIRE_PTR_A(beta, esz);
+    }
     CHECK_ALIGN(h0, 4); CHECK_ALIGN(ht, 4);
     if (policy == GDR_FULL_SAVE) REQUIRE_PTR(saved);
     const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
@@ -432,7 +475,7 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
         g = z;
         if ((e = zero_fill(z, d->B * d->T * d->H, st)) != hipSuccess) return hip_fail(e, "zero gate");
     }
-    Inputs in{q, k, v, beta, nullptr, g, h0, nullptr};
+    Inputs in{q, k, v, beta, nullptr, g, h0, nullptr, g2.ers, g2.wrt};
     e = seq_tables(s, pk, st);
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     const int what = PREP_FWDSCAN | PREP_OUT |
@@ -625,6 +668,7 @@ int any_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
             void* scratch, size_t scratch_bytes, void* stream)
 {
+    if (d && gdn2(d)) return check_gdn2(d, false);
     if (d && padded(d))
         return run_fwd_padded(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
     return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
@@ -634,6 +678,7 @@ int any_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
             const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
             void* scratch, size_t scratch_bytes, void* stream, bool wy7)
 {
+    if (d && gdn2(d)) return check_gdn2(d, false);
     if (d && padded(d))
         return run_bwd_padded(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
                               scratch, scratch_bytes, stream, wy7);
@@ -782,6 +827,38 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
 {
     return any_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
                    dh0, scratch, scratch_bytes, stream, true);
+}
+
+int gdr_fwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                 const float* g, const void* erase, const void* write, const float* h0, void* o,
+                 float* ht, void* saved, void* scratch, size_t scratch_bytes, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_gdn2(d, true))) return rc;
+    Gdn2Args g2;
+    g2.ers = erase;
+    g2.wrt = write;
+    return run_fwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, o, ht, saved, scratch, scratch_bytes,
+                   stream, g2);
+}
+
+int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                 const float* g, const void* erase, const void* write, const float* h0,
+                 const void* dO, const float* dht, const void* saved, void* dq, void* dk, void* dv,
+                 float* dg, void* derase, void* dwrite, float* dh0, void* scratch,
+                 size_t scratch_bytes, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_gdn2(d, true))) return rc;
+    Gdn2Args g2;
+    g2.ers = erase;
+    g2.wrt = write;
+    g2.ders = derase;
+    g2.dwrt = dwrite;
+    return run_bwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, nullptr,
+                   dh0, scratch, scratch_bytes, stream, false, g2);
 }
 
 const char* gdr_status_string(int status)

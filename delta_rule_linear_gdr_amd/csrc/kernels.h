@@ -64,6 +64,8 @@ struct Shape {
     int64_t B, T, H, NT;
     int vec;   // 1: per-channel gate [B,T,H,128]; 0: scalar gate [B,T,H]
     int f32;   // 1: q,k,v,beta,o,dO,dq,dk,dv,dbeta are fp32; 0: bf16
+    int gd2;   // 1: GDN2 -- per-channel gate with independent erase and write
+               // gates (Inputs::ers, wrt; Grads::ders, dwrt) in place of beta
     // Sequences (state entries) and chunk slots per head. Regular batch:
     // NS = B, NC = NT. Packed variable-length batch (B = 1): NS sequences,
     // NC = ceil(T / 64) + NS (at least the chunks of all sequences) and the
@@ -211,11 +213,15 @@ int cu_count();
 struct Inputs {
     const void *q, *k, *v, *beta, *dO;
     const float *g, *h0, *dht;
+    // GDN2: erase gate [B,T,H,128] (per key) and write gate [B,T,H,128]
+    // (per value), bf16; null otherwise
+    const void *ers, *wrt;
 };
 
 struct Grads {
     void *dq, *dk, *dv, *dbeta;
     float *dg, *dh0;
+    void *ders, *dwrt;  // GDN2: gradients of the erase and write gates
 };
 
 // What prep writes (bit set of PREP_*).

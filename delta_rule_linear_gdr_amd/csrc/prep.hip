@@ -22,6 +22,9 @@
 // an MFMA with the identity (X * I leaves X in accumulator order, which is
 // the frag order of X^T), so no operand is transposed through LDS. The
 // unit-lower inverse is a 16 x 16-blocked forward substitution in fp32.
+// GDN2 (paper Table 1: independent erase and write gates): E = ers o gam o K
+// and Z = wrt o V, the erase gate per (token, key) and the write gate per
+// (token, value) taking beta's place; both are staged in LDS as fp32.
 // Outputs (bit set `what`, formats in kernels.h): the forward-scan operands
 // -W, Kt^T, U, gn; the output operands Qg, Hm; the reverse-scan operands
 // Kt, -W^T and, given dO, X = Hm^T dO and Y = Qg^T dO; Hm^T and Qg^T for a
@@ -59,7 +62,7 @@ __device__ __forceinline__ void st_row8_frag(bf16* base, int i, int f0, const fl
     *(bf16x4*)(base + (tile * 64 + 16 * (gA + 1) + r) * 8 + slot0) = hi;
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool GD2>
 __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter it, int what)
 {
     ChunkRef cr;
@@ -87,6 +90,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     __shared__ __attribute__((aligned(16))) float sG[GSZ];
     __shared__ float sCen[VEC ? 4 : 1][DKD];  // per 16-row tile: centre of G over its rows
     __shared__ float sBeta[CH];
+    // GDN2: the chunk's erase gates (rows 0..63, per key) and write gates
+    // (rows 64..127, per value), padded like sG
+    __shared__ __attribute__((aligned(16))) float sEW[GD2 ? 2 * CH * GST : 4];
     // L, then A = (I + L)^{-1} in place: block row i reads its L blocks
     // before a barrier and only then writes its A blocks; a diagonal block
     // is read and rewritten by one wave.
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     // it stays an unconditional read in the batch) and its value replaced by
     // zero with a select.
     const int lc = l < nv ? l : nv - 1;
-    const T bload = beta[tok0 + lc * s.H];
+    const T bload = GD2 ? (T)0.f : beta[tok0 + lc * s.H];
     const float gload = VEC ? 0.f : in.g[tok0 + lc * s.H];
     const T braw = l < nv ? bload : (T)0.f;
     const float graw = l < nv ? gload : 0.f;
@@ -192,6 +198,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         sG[l] = wave_incl_scan(graw);
     }
     if (w == 0) sBeta[l] = to_f32(braw);
+    if constexpr (GD2) {
+        // 64 rows x 128 of each gate as groups of four; rows past nv are zero
+        const T* ers = (const T*)in.ers + tok0 * DKD;
+        const T* wrt = (const T*)in.wrt + tok0 * DVD;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int id = tid + 256 * u, i = id >> 5, c = (id & 31) * 4;
+            const int ic = i < nv ? i : nv - 1;
+            const f32x4 e4 = tof4(ld4raw(ers + ic * ld + c)), w4 = tof4(ld4raw(wrt + ic * ld + c));
+            *(f32x4*)&sEW[i * GST + c] = i < nv ? e4 : zero4();
+            *(f32x4*)&sEW[(CH + i) * GST + c] = i < nv ? w4 : zero4();
+        }
+    }
     if (STAGE) __builtin_amdgcn_s_waitcnt(0);  // the K / Q copies have landed
     lds_barrier();
 
@@ -230,7 +249,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             const float d = sG[i * GST + f0 + e] - pv[f0 + e];
             // 1: alpha = exp(G - p) (queries);  2: beta alpha (erase keys);
             // 3: zeta = exp(p - G) (write keys)
-            x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? sBeta[i] : 1.f);
+            const float wgt = GD2 ? sEW[i * GST + f0 + e] : sBeta[i];  // erase weight
+            x[e] *= (kind == 3) ? __expf(-d) : __expf(d) * (kind == 2 ? wgt : 1.f);
         }
         return pack8(x);
     };
@@ -452,7 +472,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                     const int i = 16 * mt + 4 * g + e;
                     const float G = Gat(i, f);
                     kt[e] = KC[mt][n][e] * __expf(gnf - G);
-                    EC[mt][n][e] = KC[mt][n][e] * __expf(G) * sBeta[i];
+                    EC[mt][n][e] = KC[mt][n][e] * __expf(G) * (GD2 ? sEW[i * GST + f] : sBeta[i]);
                 }
                 KC[mt][n] = kt;
             }
@@ -476,7 +496,10 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
                 for (int n = 0; n < 2; ++n)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) VC[mt][n][e] *= sBeta[16 * mt + 4 * g + e];
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 16 * mt + 4 * g + e;
+                        VC[mt][n][e] *= GD2 ? sEW[(CH + i) * GST + 32 * w + 16 * n + r] : sBeta[i];
+                    }
             }
 #pragma unroll
             for (int n = 0; n < 2; ++n)
@@ -697,12 +720,16 @@ __global__ __launch_bounds__(256, 8) void xy_kernel(Shape s, Inputs in, Inter it
 hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what, hipStream_t st)
 {
     dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
-    if (s.f32) {
-        if (s.vec) prep_kernel<float, true><<<grid, 256, 0, st>>>(s, in, it, what);
-        else prep_kernel<float, false><<<grid, 256, 0, st>>>(s, in, it, what);
+    if (s.gd2) {
+        // GDN2 is built for bf16 inputs only (the host refuses the rest)
+        if (s.f32 || !s.vec) return hipErrorInvalidValue;
+        prep_kernel<bf16, true, true><<<grid, 256, 0, st>>>(s, in, it, what);
+    } else if (s.f32) {
+        if (s.vec) prep_kernel<float, true, false><<<grid, 256, 0, st>>>(s, in, it, what);
+        else prep_kernel<float, false, false><<<grid, 256, 0, st>>>(s, in, it, what);
     } else {
-        if (s.vec) prep_kernel<bf16, true><<<grid, 256, 0, st>>>(s, in, it, what);
-        else prep_kernel<bf16, false><<<grid, 256, 0, st>>>(s, in, it, what);
+        if (s.vec) prep_kernel<bf16, true, false><<<grid, 256, 0, st>>>(s, in, it, what);
+        else prep_kernel<bf16, false, false><<<grid, 256, 0, st>>>(s, in, it, what);
     }
     return hipGetLastError();
 }

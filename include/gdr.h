@@ -1,7 +1,8 @@
 /*
  * gdr.h -- C ABI of the MI355X (gfx950) chunkwise gated delta-rule operator:
  * forward and backward of Gated DeltaNet (scalar gate), Kimi Delta
- * Attention (per-key-channel gate) and DeltaNet (no decay), chunk size 64,
+ * Attention (per-key-channel gate), DeltaNet (no decay) and GDN2
+ * (per-key-channel gate, independent erase and write gates), chunk size 64,
  * key and value width up to 128, regular or packed variable-length batches.
  *
  * Operation ("ReWY: Faster Backpropagation for Delta-Rule Attention -- From
@@ -92,7 +93,10 @@ typedef enum {
  * and may be NULL; the workspace holds a zero log-decay array and a sink for
  * its gradient (8 bytes per token and head), and the scalar-gate kernels run
  * on them. */
-typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_VECTOR = 1, GDR_GATE_NONE = 2 } gdr_gate;
+/* GDR_GATE_GDN2: GDN2 (the pages' Table 1: per-key-channel log decay with
+ * independent erase and write gates); its calls are gdr_fwd_gdn2 and
+ * gdr_bwd_gdn2 below, and the beta entry points refuse it. */
+typedef enum { GDR_GATE_SCALAR = 0, GDR_GATE_VECTOR = 1, GDR_GATE_NONE = 2, GDR_GATE_GDN2 = 3 } gdr_gate;
 typedef enum { GDR_RECOMPUTE = 0, GDR_FULL_SAVE = 1 } gdr_policy;
 typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
@@ -136,6 +140,32 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
                 const float* g, const void* beta, const float* h0, const void* dO,
                 const float* dht, const void* saved, void* dq, void* dk, void* dv, float* dg,
                 void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
+
+/* GDN2 (Sec. 2.2, Table 1: a per-key-channel log decay with an erase gate per
+ * key channel and a write gate per value channel, in place of the shared
+ * beta; Sec. 3.1 keeps their gradients separate). Per head, for t = 1..T:
+ *     St = Diag(exp(g_t)) S_{t-1}
+ *     r  = write_t o v_t - St^T (erase_t o k_t)    (prediction from the
+ *                                                  erase-gated key, taken from
+ *                                                  the write-gated value)
+ *     S_t = St + k_t r^T,   o_t = S_t^T q_t
+ * which is the vector-gate recurrence when erase_t = write_t = beta_t. The
+ * chunk system is the same with E = erase o exp(G) o K and Z = write o V.
+ * Layouts: g, dg [B,T,H,128] fp32; erase, derase [B,T,H,128] (per key) and
+ * write, dwrite [B,T,H,128] (per value) in bf16, 16-byte aligned; the rest as
+ * for gdr_fwd / gdr_bwd. d->gate must be GDR_GATE_GDN2, d->dtype GDR_BF16 and
+ * the widths 128/128 (else GDR_ERR_UNSUPPORTED); regular batches only. The
+ * workspace is the vector gate's (gdr_workspace_size with either gate kind).
+ * derase and dwrite are the exact gradients entry by entry; their sums over
+ * channels are what a shared beta's gradient would be. */
+int gdr_fwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                 const float* g, const void* erase, const void* write, const float* h0, void* o,
+                 float* ht, void* saved, void* scratch, size_t scratch_bytes, void* stream);
+int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
+                 const float* g, const void* erase, const void* write, const float* h0,
+                 const void* dO, const float* dht, const void* saved, void* dq, void* dk, void* dv,
+                 float* dg, void* derase, void* dwrite, float* dh0, void* scratch,
+                 size_t scratch_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): gdr_bwd

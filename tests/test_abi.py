@@ -59,7 +59,7 @@ def test_workspace_sizes():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(DK=192), -2), (dict(DV=160), -2), (dict(DK=0), -1), (dict(DV=-3), -1), (dict(C=32), -2),
-    (dict(gate=5), -1), (dict(gate=3), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
+    (dict(gate=5), -1), (dict(gate=4), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
 ])
 def test_descriptor_validation(kw, status):
     rc, _, _ = _ws(_desc(**kw))
@@ -227,3 +227,26 @@ def test_noalloc_rejects_problems_past_its_array():
     assert rc == -2 and b"fixed" in lib.gdr_last_error()
     rc = lib.gdr_bwd_noalloc(ctypes.byref(_desc(DK=200)), 0, *([None] * 15), None)
     assert rc == -2
+
+
+def test_gdn2_entry_points_take_only_gdn2():
+    """GDN2 goes through gdr_fwd_gdn2 / gdr_bwd_gdn2 alone; they take bf16
+    inputs at 128/128 and refuse other gate kinds, all before any launch."""
+    lib = gdr.load()
+    nul = [None] * 20
+    gd2 = _desc(gate=3)
+    # the beta entry points refuse the GDN2 gate kind
+    assert lib.gdr_fwd(ctypes.byref(gd2), 0, *nul[:10], 0, None) == -1
+    assert lib.gdr_bwd(ctypes.byref(gd2), 0, *nul[:16], 0, None) == -1
+    assert b"gdr_fwd_gdn2" in lib.gdr_last_error()
+    # the GDN2 entry points refuse other gate kinds, fp32 and narrow widths
+    for kw, status in ((dict(gate=1), -1), (dict(gate=3, dtype=1), -2), (dict(gate=3, DK=80), -2),
+                       (dict(gate=3, DV=96), -2)):
+        d = _desc(**kw)
+        assert lib.gdr_fwd_gdn2(ctypes.byref(d), 0, *nul[:11], 0, None) == status, kw
+        assert lib.gdr_bwd_gdn2(ctypes.byref(d), 0, *nul[:18], 0, None) == status, kw
+    # a GDN2 descriptor without its gate tensors is refused
+    assert lib.gdr_fwd_gdn2(ctypes.byref(gd2), 0, *nul[:11], 0, None) == -1
+    # the workspace is the vector gate's
+    assert _ws(gd2, 0) == _ws(_desc(gate=1), 0)
+    assert _ws(gd2, 1) == _ws(_desc(gate=1), 1)
