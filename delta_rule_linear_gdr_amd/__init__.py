@@ -31,7 +31,8 @@ import os
 __all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_fwd_gdn2", "gdr_bwd_gdn2",
            "chunk_gated_delta_rule", "workspace_size",
            "library_path", "load",
-           "profile_begin", "profile_end", "set_local_form", "GdrError", "RECOMPUTE", "FULL_SAVE"]
+           "profile_begin", "profile_end", "set_local_form", "gate_status", "GdrError",
+           "RECOMPUTE", "FULL_SAVE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libgdr.so")
@@ -46,7 +47,8 @@ EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
            "gdr_fwd_gdn2", "gdr_bwd_gdn2",
            "gdr_bwd_noalloc", "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
            "gdr_profile_begin",
-           "gdr_profile_end", "gdr_set_local_form", "gdr_status_string", "gdr_last_error",
+           "gdr_profile_end", "gdr_set_local_form", "gdr_gate_status", "gdr_status_string",
+           "gdr_last_error",
            "gdr_version")
 
 
@@ -108,6 +110,8 @@ def load():
     lib.gdr_profile_begin.restype = i32
     lib.gdr_profile_end.argtypes = [ctypes.POINTER(StageTime), i32, ctypes.POINTER(i32)]
     lib.gdr_profile_end.restype = i32
+    lib.gdr_gate_status.argtypes = [dp, ctypes.c_int64, p, sz, p, p]
+    lib.gdr_gate_status.restype = i32
     lib.gdr_set_local_form.argtypes = [i32]
     lib.gdr_set_local_form.restype = i32
     lib.gdr_status_string.argtypes = [i32]
@@ -169,6 +173,22 @@ def profile_end() -> dict:
     n = ctypes.c_int()
     _check(load().gdr_profile_end(arr, 16, ctypes.byref(n)))
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n.value)}
+
+
+GATE_POSITIVE, GATE_RANGE, GATE_NONFINITE = 1, 2, 4
+
+
+def gate_status(q, g, v, scratch, n_seq=None, status=None):
+    """Gate-check bits of the last call that ran with this problem and this
+    scratch (GATE_POSITIVE | GATE_RANGE | GATE_NONFINITE; 0 = in contract),
+    as a device int32 tensor written on the current stream (no sync here)."""
+    torch = _torch()
+    d = _desc_from(q, g, v)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=q.device)
+    _check(load().gdr_gate_status(ctypes.byref(d), -1 if n_seq is None else n_seq, _ptr(scratch),
+                                  scratch.numel(), _ptr(status), _stream()))
+    return status
 
 
 def set_local_form(form: str) -> str:

@@ -58,11 +58,12 @@ struct Carver {
     }
 };
 
-// What the full-save forward keeps for the backward.
+// What the full-save forward keeps for the backward. A is kept once, as the
+// A^T frags the three-product producer reads; the seven-product backward
+// forms its A frags from them in scratch.
 void carve_saved(Carver& c, Inter& it)
 {
     it.AT = c.take<bf16>(B_T64x64);
-    it.Af = c.take<bf16>(B_T64x64);
     it.Kt = c.take<bf16>(B_T64x128);
     it.WnT = c.take<bf16>(B_T64x128);
     it.gn = c.take<float>(B_GN);
@@ -81,6 +82,9 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
     memset(&it, 0, sizeof it);
     Carver sv(saved, ntiles), sc(scratch, ntiles);
     const bool full = policy == GDR_FULL_SAVE;
+    // the gate-check words first, at the same place for every call and
+    // policy, so that gdr_gate_status finds them from the descriptor alone
+    it.flags = sc.take<uint32_t>(16);
     if (full) carve_saved(sv, it);
     if (ph == FWD || !full) {
         // operands of the forward scan (and, in the forward, its output)
@@ -106,6 +110,7 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
         it.Y = sc.take<bf16>(B_T128x128);
         it.dh = sc.take<bf16>(B_T128x128);
         it.Rb = sc.take<bf16>(B_T64x128);
+        if (full) it.Af = sc.take<bf16>(B_T64x64);  // seven-product backward only
     }
     saved_bytes = full ? align_up(sv.off) : 0;
     scratch_bytes = align_up(sc.off);
@@ -295,10 +300,11 @@ int hip_fail(hipError_t e, const char* what)
 
 // ---- optional per-stage timing (gdr_profile_begin / gdr_profile_end) ----
 enum Stage {
-    ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_SCAN_PAIR, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, ST_PAD, NSTAGE
+    ST_PREP, ST_SCAN_FWD, ST_XY, ST_SCAN_BWD, ST_SCAN_PAIR, ST_BWD_LOCAL, ST_BWD_LOCAL_WY7, ST_PAD,
+    ST_A_FROM_AT, NSTAGE
 };
 const char* const kStageName[NSTAGE] = {"prep", "scan_fwd", "xy", "scan_bwd", "scan_pair",
-                                        "bwd_local", "bwd_local_wy7", "pad"};
+                                        "bwd_local", "bwd_local_wy7", "pad", "a_from_at"};
 
 struct Profiler {
     std::mutex mu;
@@ -413,6 +419,10 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
         e = timed(ST_SCAN_PAIR, st, [&] { return launch_scan_pair(s, in, it, dh0, st); });
         if (e != hipSuccess) return hip_fail(e, "scan_pair");
     } else {
+        if (wy7) {
+            e = timed(ST_A_FROM_AT, st, [&] { return launch_a_from_at(s, it, st); });
+            if (e != hipSuccess) return hip_fail(e, "a_from_at");
+        }
         e = timed(ST_XY, st, [&] { return launch_xy(s, in, it, st); });
         if (e != hipSuccess) return hip_fail(e, "xy");
         e = timed(ST_SCAN_BWD, st, [&] { return launch_scan_bwd(s, in, it, dh0, st); });
@@ -479,7 +489,7 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     e = seq_tables(s, pk, st);
     if (e != hipSuccess) return hip_fail(e, "sequence tables");
     const int what = PREP_FWDSCAN | PREP_OUT |
-                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A | PREP_AF : 0);
+                     (policy == GDR_FULL_SAVE ? PREP_BWDSCAN | PREP_SAVEXY | PREP_A : 0);
     e = timed(ST_PREP, st, [&] { return launch_prep(s, in, it, what, st); });
     if (e != hipSuccess) return hip_fail(e, "prep");
     e = timed(ST_SCAN_FWD, st, [&] { return launch_scan_fwd(s, in, it, o, ht, st); });
@@ -686,6 +696,28 @@ int any_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
                    scratch_bytes, stream, wy7);
 }
 
+// ---- gate-range status (gdr_gate_status) ----
+// OR of the gate-check words of every (chunk, head) in use; one workgroup.
+__global__ __launch_bounds__(256) void gate_status_kernel(Shape s, const uint32_t* flags, int32_t* out)
+{
+    const int64_t ntile = s.NC * (s.B * s.H) * 4;
+    uint32_t acc = 0;
+    for (int64_t i = threadIdx.x; i < ntile; i += blockDim.x) {
+        const int64_t tile = i >> 2;
+        // a packed batch's unused slots were not visited by the last call
+        if (s.ctab && s.ctab[tile / s.H].y <= 0) continue;
+        acc |= flags[i];
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] |= red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = (int32_t)red[0];
+}
+
 // ---- the entry point that allocates nothing (gdr_bwd_noalloc) ----
 namespace noalloc {
 
@@ -827,6 +859,41 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
 {
     return any_bwd(d, Packed{}, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta,
                    dh0, scratch, scratch_bytes, stream, true);
+}
+
+int gdr_gate_status(const gdr_desc* d, int64_t n_seq, const void* scratch, size_t scratch_bytes,
+                    int32_t* status, void* stream)
+{
+    int rc = check_desc(d);
+    if (rc) return rc;
+    Packed pk;
+    if (n_seq >= 0) {
+        if ((rc = check_packed_shape(d, n_seq))) return rc;
+        pk.on = true;
+        pk.n = n_seq;
+    }
+    if (!status) return fail(GDR_ERR_INVALID, "required pointer 'status' is NULL");
+    if ((uintptr_t)status % 4) return fail(GDR_ERR_INVALID, "pointer 'status' is not 4-byte aligned");
+    if (!scratch || !aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is NULL or not 16-byte aligned");
+    // where a call with this descriptor placed its words: after the padded
+    // copies (widths below 128), then after the inner call's sequence tables
+    // and DeltaNet gate arrays, first in the per-chunk layout
+    const gdr_desc e = padded(d) ? inner_desc(d) : *d;
+    const size_t front = (padded(d) ? pad_layout(d, pk, nullptr).bytes : 0);
+    const size_t tb = table_bytes(&e, pk) + nogate_bytes(&e);
+    const size_t need = front + tb + align_up(16 * ntiles(&e, pk));
+    if (scratch_bytes < need)
+        return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes cannot hold the gate-check words (%zu)",
+                    scratch_bytes, need);
+    char* inner = (char*)scratch + front;
+    const Shape s = make_shape(&e, pk, inner);
+    if (s.NC * (s.B * s.H) == 0) {
+        hipError_t ez = zero_fill((float*)status, 1, (hipStream_t)stream);  // nothing ran: 0
+        return ez == hipSuccess ? GDR_OK : hip_fail(ez, "status fill");
+    }
+    gate_status_kernel<<<1, 256, 0, (hipStream_t)stream>>>(s, (const uint32_t*)(inner + tb), status);
+    hipError_t ee = hipGetLastError();
+    return ee == hipSuccess ? GDR_OK : hip_fail(ee, "gate_status");
 }
 
 int gdr_fwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,

@@ -58,7 +58,17 @@ struct Inter {
     bf16* R;     // correction             ctile M=64 tok,  N=128 val (16 KiB)
     bf16* dh;    // state adjoint at chunk end, ctile like h         (32 KiB)
     bf16* Rb;    // correction adjoint, ctile like R                 (16 KiB)
+    // gate check (prep): one word per prep wave, OR of GATE_* bits   (16 B)
+    uint32_t* flags;
 };
+
+// Gate-check bits prep records per (chunk, head) (gdr_gate_status).
+enum {
+    GATE_POSITIVE = 1,   // a log decay above 0 (not a decay)
+    GATE_RANGE = 2,      // vector gate: a 16-token window's per-key range above GATE_RANGE_MAX
+    GATE_NONFINITE = 4,  // a log decay that is NaN or infinite
+};
+constexpr float GATE_RANGE_MAX = 160.f;
 
 struct Shape {
     int64_t B, T, H, NT;
@@ -237,6 +247,9 @@ enum {
 
 hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what,
                        hipStream_t st);
+// A frags (it.Af) from the A^T frags (it.AT), every (chunk, head): what the
+// full-save seven-product backward needs, the saved area holding A^T only.
+hipError_t launch_a_from_at(const Shape& s, const Inter& it, hipStream_t st);
 // X = Hm^T dO and Y = Qg^T dO from HmT, QgT and dO.
 hipError_t launch_xy(const Shape& s, const Inputs& in, const Inter& it, hipStream_t st);
 // Forward state scan (loader-fed; its loader waves also form the output).

@@ -135,6 +135,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     // Rows past nv: the read is made from a clamped row (always in range, so
     // it stays an unconditional read in the batch) and its value replaced by
     // zero with a select.
+    // gate check: this lane's log decays and (vector gate) window ranges
+    bool gpos = false, gnonfin = false, grange = false;
     const int lc = l < nv ? l : nv - 1;
     const T bload = GD2 ? (T)0.f : beta[tok0 + lc * s.H];
     const float gload = VEC ? 0.f : in.g[tok0 + lc * s.H];
@@ -158,7 +160,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[u][m][e] = 16 * m + 4 * g + e < nv ? x[u][m][e] : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    x[u][m][e] = 16 * m + 4 * g + e < nv ? x[u][m][e] : 0.f;
+                    gpos |= x[u][m][e] > 0.f;
+                    gnonfin |= !__builtin_isfinite(x[u][m][e]);
+                }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int f = 32 * w + 16 * u + r;
@@ -192,10 +198,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 const float mn32 = partner32(mn);
                 mn = fminf(mn, mn32);
                 if (g == 0) sCen[VEC ? m : 0][f] = 0.5f * (mx + mn);
+                grange |= mx - mn > GATE_RANGE_MAX;
             }
         }
     } else if (w == 0) {
         sG[l] = wave_incl_scan(graw);
+        gpos = graw > 0.f;
+        gnonfin = !__builtin_isfinite(graw);
+    }
+    if (it.flags) {
+        // every prep run rewrites all four words of its (chunk, head)
+        const uint32_t bits = (__ballot(gpos) ? (uint32_t)GATE_POSITIVE : 0u) |
+                              (__ballot(grange) ? (uint32_t)GATE_RANGE : 0u) |
+                              (__ballot(gnonfin) ? (uint32_t)GATE_NONFINITE : 0u);
+        if (l == 0) it.flags[t * 4 + w] = bits;
     }
     if (w == 0) sBeta[l] = to_f32(braw);
     if constexpr (GD2) {
@@ -715,7 +731,43 @@ __global__ __launch_bounds__(256, 8) void xy_kernel(Shape s, Inputs in, Inter it
         }
 }
 
+// A frags from the A^T frags (full-save seven-product backward; the saved
+// area keeps A^T only). A frag (rows 16 rj.., K = 32 ks..) is X^T for
+// X = A^T[32 ks .. + 31][16 rj .. + 15]: the two A^T tiles over rows
+// 32 ks + 16 h times the identity selecting column half rj & 1 give its
+// two accumulator halves, which are the frag's pik slots. Exact (each entry
+// is one bf16 value times 1). One wave per (chunk, head).
+__global__ __launch_bounds__(256) void a_from_at_kernel(Shape s, Inter it)
+{
+    ChunkRef cr;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (item >= s.NC * (s.B * s.H)) return;
+    if (!chunk_in_order(s, item, CO_DESCENDING, cr)) return;
+    const bf16* AT = it.AT + cr.t * (CH * CH);
+    bf16* Af = it.Af + cr.t * (CH * CH);
+#pragma unroll
+    for (int tl = 0; tl < 8; ++tl) {
+        const int rj = tl >> 1, ks = tl & 1;
+        if (ks == 1 && rj < 2) {
+            st_frag(Af, tl, bf16x8{});  // above the diagonal
+            continue;
+        }
+        const bf16x8 I = ident_pi(rj & 1);
+        const f32x4 c0 = mfma(ld_frag(AT, (2 * ks) * 2 + (rj >> 1)), I, zero4());
+        const f32x4 c1 = mfma(ld_frag(AT, (2 * ks + 1) * 2 + (rj >> 1)), I, zero4());
+        st_frag(Af, tl, pack_pi(c0, c1));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_a_from_at(const Shape& s, const Inter& it, hipStream_t st)
+{
+    const int64_t n = s.NC * (s.B * s.H);
+    if (n <= 0) return hipSuccess;
+    a_from_at_kernel<<<(unsigned)((n + 3) / 4), 256, 0, st>>>(s, it);
+    return hipGetLastError();
+}
 
 hipError_t launch_prep(const Shape& s, const Inputs& in, const Inter& it, int what, hipStream_t st)
 {

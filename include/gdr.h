@@ -66,7 +66,9 @@
  * boundary pivots between windows, so they span exp(+-range/2) of one
  * window; g must be a log decay (g <= 0) whose per-channel range over each
  * 16-token window is at most 160 (e.g. every |g| <= 10); past that the
- * results are non-finite, not finite and wrong. A launch failure
+ * results are non-finite, not finite and wrong, and gdr_gate_status reports
+ * it (the check runs inside the kernels; there is no host synchronization,
+ * so the call itself still returns GDR_OK). A launch failure
  * returns GDR_ERR_HIP. gdr_last_error() returns a message for
  * the calling thread's last failure.
  */
@@ -117,8 +119,8 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
 
 /* Forward. o: output; ht: final state (NULL: not written); h0 NULL: zero.
  * Under GDR_FULL_SAVE, saved receives the chunk quantities the backward
- * reuses (per chunk and head: A^T and A, Kt, -W^T, exp(G_n), Hm^T, Qg^T, and
- * the state h and correction R at the chunk; 123,392 bytes at the supported
+ * reuses (per chunk and head: A^T, Kt, -W^T, exp(G_n), Hm^T, Qg^T, and the
+ * state h and correction R at the chunk; 115,200 bytes at the supported
  * widths); under GDR_RECOMPUTE saved may be NULL. */
 int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
@@ -177,7 +179,7 @@ int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, co
  * current device (else GDR_ERR_INVALID). A problem whose gdr_bwd scratch
  * (gdr_workspace_size) exceeds the array returns GDR_ERR_UNSUPPORTED before
  * anything is launched: about 270 (chunk, head) pairs under GDR_RECOMPUTE,
- * e.g. (B, T, H) = (1, 2048, 8), about 680 under GDR_FULL_SAVE. Every call on
+ * e.g. (B, T, H) = (1, 2048, 8), about 630 under GDR_FULL_SAVE. Every call on
  * one device shares that device's array and leaves its contents behind (the
  * kernels write every part they read before reading it), so calls that
  * overlap in time on one device -- on two streams, or from two threads --
@@ -222,7 +224,8 @@ int gdr_bwd_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int
  * launch is bracketed by events recorded on the call's stream. Stages are
  * "prep", "scan_fwd", "xy", "scan_bwd", "scan_pair" (both scans of the
  * recompute backward in one launch), "bwd_local", "bwd_local_wy7", "pad" (the
- * copies of widths below 128).
+ * copies of widths below 128), "a_from_at" (the full-save seven-product
+ * backward's A from the saved A^T).
  * gdr_profile_end turns timing off, waits for the recorded events (a host
  * synchronization), and writes up to `cap` per-stage totals; *n_out receives
  * the number of stages seen. Launches beyond max_launches run untimed and
@@ -235,6 +238,27 @@ typedef struct {
 } gdr_stage_time;
 int gdr_profile_begin(int max_launches);
 int gdr_profile_end(gdr_stage_time* out, int cap, int* n_out);
+
+/* Gate-range status. The chunk preparation of every gdr_fwd*, gdr_bwd* under
+ * GDR_RECOMPUTE and gdr_bwd_noalloc records, per chunk and head, whether the
+ * log decays it read leave the contract above (ReWY paper Sec. 3.3
+ * "Centered factors": the implementation checks gate ranges; the repository
+ * page, "Compatibility": unsupported configurations fail). The words sit in
+ * `scratch` and cost no extra pass or synchronization. gdr_gate_status ORs
+ * those of the last such call made with this descriptor and scratch into
+ * *status (a DEVICE int32, written asynchronously on `stream`):
+ *   GDR_GATE_POSITIVE   a log decay above 0
+ *   GDR_GATE_RANGE      vector gate (and GDN2): a 16-token window whose
+ *                       per-channel range exceeds 160
+ *   GDR_GATE_NONFINITE  a log decay that is NaN or infinite
+ * and 0 when every decay was within it. n_seq: the sequence count of a
+ * packed batch (the offsets the call ran with), or -1 for a regular batch.
+ * A gdr_bwd under GDR_FULL_SAVE reads no gates (its forward checked them).
+ * Results computed past GDR_GATE_RANGE or GDR_GATE_NONFINITE are not
+ * meaningful; a positive decay within range is computed as given. */
+enum { GDR_GATE_POSITIVE = 1, GDR_GATE_RANGE = 2, GDR_GATE_NONFINITE = 4 };
+int gdr_gate_status(const gdr_desc* d, int64_t n_seq, const void* scratch, size_t scratch_bytes,
+                    int32_t* status, void* stream);
 
 /* Launch form of the scalar-gate three-product local backward, for
  * like-for-like timing of the ablation (process-wide; set it between calls,

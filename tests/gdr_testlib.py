@@ -215,3 +215,35 @@ def compare_packed(gpu, x, heads=None, report=None):
     if report is not None:
         report.update(errs)
     return errs
+
+
+# ---------------------------------------------------------------- gate check
+
+GATE_POSITIVE, GATE_RANGE, GATE_NONFINITE = 1, 2, 4
+
+
+def gate_check_bits(g, T=None, window=16, chunk=64, limit=160.0):
+    """The contract of the log decays, stated plainly: bit 1 if any log decay
+    is above 0, bit 4 if any is NaN or infinite, and (per-channel gates,
+    g [B,T,H,DK]) bit 2 if, within any 64-token chunk, the chunk-local
+    cumulative log decay of some channel spans more than `limit` over one
+    16-token window of the chunk. A ragged chunk's missing rows count as
+    zero decay."""
+    g = np.asarray(g, dtype=np.float64)
+    bits = 0
+    if np.any(g > 0):
+        bits |= GATE_POSITIVE
+    if not np.all(np.isfinite(g)):
+        bits |= GATE_NONFINITE
+    if g.ndim == 4:
+        B, T_, H, DK = g.shape
+        for c0 in range(0, T_, chunk):
+            G = np.cumsum(np.nan_to_num(g[:, c0:c0 + chunk], nan=0.0, posinf=0.0, neginf=0.0), axis=1)
+            n = G.shape[1]
+            if n < chunk:  # ragged: missing rows keep the last cumulative value
+                G = np.concatenate([G, np.repeat(G[:, -1:], chunk - n, axis=1)], axis=1)
+            for w0 in range(0, chunk, window):
+                Gw = G[:, w0:w0 + window]
+                if np.any(Gw.max(axis=1) - Gw.min(axis=1) > limit):
+                    bits |= GATE_RANGE
+    return bits

@@ -47,14 +47,17 @@ def test_workspace_sizes():
     # recompute: the backward holds the forward-scan operands (-W, Kt^T, U, gn),
     # the reverse-scan operands (Kt, -W^T, X, Y), A^T and A, and the per-chunk
     # h, R, dh, Rb of every (chunk, head)
+    # (plus the 16 bytes of gate-check words of every (chunk, head))
     per = 3 * T64x128 + GN + 2 * T64x128 + 2 * T64x64 + T128x128 + T64x128 \
-        + T64x128 + T128x128 + T128x128 + T64x128
+        + T64x128 + T128x128 + T128x128 + T64x128 + 16
     assert sc == 2048 * per
     rc, sv, sc = _ws(_desc(T=8192, H=16), 1)
     assert rc == 0
-    # full save keeps A^T, A, Kt, -W^T, gn, Hm^T, Qg^T, h, R
-    assert sv == 2048 * (2 * T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
-    assert sc == 2048 * max(4 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128)
+    # full save keeps A^T, Kt, -W^T, gn, Hm^T, Qg^T, h, R (115,200 B per chunk-head);
+    # the backward's scratch adds A for the seven-product producer
+    assert sv == 2048 * (T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
+    assert sv == 2048 * 115200
+    assert sc == 2048 * (16 + max(4 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128 + T64x64))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -250,3 +253,14 @@ def test_gdn2_entry_points_take_only_gdn2():
     # the workspace is the vector gate's
     assert _ws(gd2, 0) == _ws(_desc(gate=1), 0)
     assert _ws(gd2, 1) == _ws(_desc(gate=1), 1)
+
+
+def test_gate_status_validates_before_any_launch():
+    lib = gdr.load()
+    d = _desc(T=256, gate=1)
+    st = ctypes.c_void_p(64)  # never dereferenced: every case fails validation first
+    assert lib.gdr_gate_status(ctypes.byref(d), -1, None, 0, st, None) == -1
+    assert lib.gdr_gate_status(ctypes.byref(d), -1, ctypes.c_void_p(256), 1 << 30, None, None) == -1
+    assert lib.gdr_gate_status(ctypes.byref(d), -1, ctypes.c_void_p(256), 64, st, None) == -3
+    assert lib.gdr_gate_status(ctypes.byref(_desc(B=2)), 3, ctypes.c_void_p(256), 1 << 30, st,
+                               None) == -1  # a packed batch has B = 1

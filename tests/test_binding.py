@@ -64,7 +64,7 @@ def test_descriptor_follows_the_tensors():
 
 def test_workspace_size_matches_the_c_call():
     sv, sc = gdr.workspace_size(1, 8192, 16, "scalar", "bf16", "full_save")
-    assert sv == 2048 * 123392
+    assert sv == 2048 * 115200
     sv2, sc2 = gdr.workspace_size(1, 8192, 16, "none", "bf16", "full_save")
     assert sv2 == sv and sc2 == sc + 2 * 4 * 8192 * 16
     svp, scp = gdr.workspace_size(1, 8192, 16, "vector", "bf16", "recompute", n_seq=3, DK=80, DV=112)

@@ -131,6 +131,20 @@ def test_deterministic_and_policy_independent():
         np.testing.assert_array_equal(a[n], c[n], err_msg=f"policy {n}")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_wy7_policy_independent(gate):
+    """The seven-product backward under full save forms A from the saved A^T
+    (an exact transpose); under recompute prep writes A itself. Both give
+    the same bits, including a ragged last chunk."""
+    _need_gpu()
+    x = _edge(gate, T=300, H=3, h0_std=0.1, dht_std=0.1)
+    a = tl.run_gpu(x, "recompute", wy7=True)
+    c = tl.run_gpu(x, "full_save", wy7=True)
+    for n in a:
+        np.testing.assert_array_equal(a[n], c[n], err_msg=f"policy {n}")
+    _report(f"wy7 policies/{gate}", tl.compare(c, x))
+
+
 def test_unsupported_width_raises():
     """A key width above 128 is refused before anything is launched."""
     _need_gpu()
@@ -518,6 +532,7 @@ def test_out_of_contract_decay_fails_loudly():
     _need_gpu()
     x = make_inputs(1, 256, 2, gate="vector", dtype="bf16", seed=3, h0_std=0.1, dht_std=0.1)
     x["g"] = np.full_like(x["g"], -12.0)
+    assert tl.gate_check_bits(x["g"]) == tl.GATE_RANGE  # and gdr_gate_status says so (above)
     gpu = tl.run_gpu(x)
     for n in ("o", "dq", "dk", "dg"):
         assert not np.all(np.isfinite(gpu[n])), n
@@ -553,3 +568,45 @@ def test_local_launch_forms_agree(policy):
     print("[launch forms] rel L2 / max abs: " +
           " ".join(f"{n}={a:.1e}/{b:.1e}" for n, (a, b) in diffs.items()), flush=True)
     _report(f"per_chunk/{policy}", tl.compare(got, x))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("case", ["in_contract", "decay_-12", "one_positive", "one_nan",
+                                  "strong_step", "scalar_positive", "ragged_in"])
+def test_gate_status_reports_out_of_contract_decays(case):
+    """The kernels' gate-check bits (gdr_gate_status) equal the plain
+    statement of the contract (gdr_testlib.gate_check_bits) for the forward
+    and the recompute backward, with no host synchronization inside either."""
+    _need_gpu()
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    gate = "scalar" if case == "scalar_positive" else "vector"
+    T = 200 if case == "ragged_in" else 256
+    x = make_inputs(1, T, 2, gate=gate, dtype="bf16", seed=41, gate_mean=3.0)
+    g = x["g"].copy()
+    if case == "decay_-12":
+        g[:] = -12.0
+    elif case == "one_positive":
+        g[0, 100, 1, 5] = 0.25
+    elif case == "one_nan":
+        g[0, 7, 0, 3] = np.nan
+    elif case == "strong_step":
+        g[0, 130, 1, 77] = -170.0  # row 2 of chunk 2's first window
+    elif case == "scalar_positive":
+        g[0, 33, 1] = 0.5
+    x["g"] = g
+    want = tl.gate_check_bits(g)
+    d = tl.device_inputs(x)
+    for policy in ("recompute", "full_save"):
+        _, sc = gdr.workspace_size(1, T, 2, gate, "bf16", policy)
+        scratch = torch.empty(sc, dtype=torch.uint8, device="cuda")
+        gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], policy=policy,
+                    scratch=scratch)
+        got_f = int(gdr.gate_status(d["q"], d["g"], d["v"], scratch).item())
+        assert got_f == want, (policy, "forward", got_f, want)
+        if policy == "recompute":
+            gdr.gdr_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["dO"], None,
+                        scratch=scratch)
+            got_b = int(gdr.gate_status(d["q"], d["g"], d["v"], scratch).item())
+            assert got_b == want, ("backward", got_b, want)
+    print(f"[gate status] {case}: {want}", flush=True)
