@@ -37,6 +37,8 @@ int fail(int status, const char* fmt, ...)
 }
 
 constexpr size_t ALIGN = 256;
+// Value widths above 128 run as 128-wide value blocks (at most 8).
+constexpr int MAX_DV = 8 * DVD;
 size_t align_up(size_t x) { return (x + ALIGN - 1) & ~(ALIGN - 1); }
 
 // Per-tile byte sizes of the chunk intermediates (formats in kernels.h).
@@ -181,9 +183,13 @@ int check_desc(const gdr_desc* d)
         return fail(GDR_ERR_INVALID, "unknown dtype %d", d->dtype);
     if (d->DK < 1 || d->DV < 1)
         return fail(GDR_ERR_INVALID, "key/value width %lld/%lld", (long long)d->DK, (long long)d->DV);
-    if (d->DK > DKD || d->DV > DVD)
-        return fail(GDR_ERR_UNSUPPORTED, "key/value width %lld/%lld: at most 128/128 is supported",
-                    (long long)d->DK, (long long)d->DV);
+    if (d->DK > DKD)
+        return fail(GDR_ERR_UNSUPPORTED,
+                    "key width %lld: at most 128 is supported (keys couple through k k^T, so a wider key "
+                    "cannot be split into 128-wide runs)",
+                    (long long)d->DK);
+    if (d->DV > MAX_DV)
+        return fail(GDR_ERR_UNSUPPORTED, "value width %lld: at most %d is supported", (long long)d->DV, MAX_DV);
     if (d->C != CH)
         return fail(GDR_ERR_UNSUPPORTED, "chunk length %lld: only 64 is supported", (long long)d->C);
     if (d->B * d->H > 65535)
@@ -509,8 +515,10 @@ int workspace(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_byt
     return GDR_OK;
 }
 
-// ---- key / value widths below 128: the 128-wide path on zero-padded copies ----
+// ---- key widths below 128 and value widths other than 128: the 128-wide
+//      path on zero-padded copies, one run per 128-wide value block ----
 bool padded(const gdr_desc* d) { return d->DK != DKD || d->DV != DVD; }
+int value_blocks(const gdr_desc* d) { return (int)((d->DV + DVD - 1) / DVD); }
 gdr_desc inner_desc(const gdr_desc* d)
 {
     gdr_desc e = *d;
@@ -524,6 +532,8 @@ struct PadBufs {
     void *q, *k, *v, *t4, *dq, *dk, *dv;  // token tensors, 128 wide (t4: o forward, dO backward)
     float *g, *dg;                          // vector gate and its gradient, 128 wide
     float *s0, *s1, *s2;                    // states: h0, ht or dht, dh0
+    float* dg1;                             // scalar gate, value blocks after the first: dg
+    void* db1;                              // value blocks after the first: dbeta
     size_t bytes;
 };
 PadBufs pad_layout(const gdr_desc* d, const Packed& pk, void* base)
@@ -554,6 +564,10 @@ PadBufs pad_layout(const gdr_desc* d, const Packed& pk, void* base)
     p.s0 = (float*)take(nst * DKD * DVD * 4);
     p.s1 = (float*)take(nst * DKD * DVD * 4);
     p.s2 = (float*)take(nst * DKD * DVD * 4);
+    if (value_blocks(d) > 1) {
+        if (d->gate == GDR_GATE_SCALAR) p.dg1 = (float*)take(rows * 4);
+        p.db1 = take(rows * esz);
+    }
     p.bytes = off;
     return p;
 }
@@ -564,7 +578,7 @@ int workspace_any(const gdr_desc* d, const Packed& pk, int policy, size_t* saved
     const gdr_desc e = inner_desc(d);
     size_t sv = 0, sc = 0;
     workspace(&e, pk, policy, &sv, &sc);
-    if (saved_bytes) *saved_bytes = sv;
+    if (saved_bytes) *saved_bytes = sv * (size_t)value_blocks(d);  // one saved area per value block
     if (scratch_bytes) *scratch_bytes = pad_layout(d, pk, nullptr).bytes + sc;
     return GDR_OK;
 }
@@ -610,22 +624,30 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     }
     if (!q || !k || !v || !o || !beta || (!g && !nogate(d)))
         return fail(GDR_ERR_INVALID, "a required pointer is NULL");
+    if (policy == GDR_FULL_SAVE && !saved) return fail(GDR_ERR_INVALID, "required pointer 'saved' is NULL");
     PadBufs pb;
     if ((rc = pad_prologue(d, pk, policy, scratch, scratch_bytes, pb))) return rc;
     const gdr_desc e = inner_desc(d);
-    const int64_t rows = d->B * d->T * d->H;
-    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, dv = (int)d->DV;
+    size_t inner_saved = 0;
+    workspace(&e, pk, policy, &inner_saved, nullptr);
+    const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
+    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
     const bool vec = d->gate == GDR_GATE_VECTOR;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
-    PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
-    if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nseq * d->H, dk, dv, st));
-    rc = run_fwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
-                 ht ? pb.s1 : nullptr, saved, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream);
-    if (rc) return rc;
-    PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st));
-    if (ht) PAD_LAUNCH(launch_unpad_state(ht, pb.s1, nseq * d->H, dk, dv, st));
+    for (int b = 0; b < value_blocks(d); ++b) {
+        // value columns [c0, c0 + dv) as their own 128-wide problem
+        const int c0 = b * DVD, dv = DV - c0 < DVD ? DV - c0 : DVD;
+        PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st, DV, c0));
+        if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nst, dk, dv, st, DV, c0));
+        rc = run_fwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
+                     ht ? pb.s1 : nullptr, saved ? (char*)saved + b * inner_saved : nullptr,
+                     (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream);
+        if (rc) return rc;
+        PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st, DV, c0));
+        if (ht) PAD_LAUNCH(launch_unpad_state(ht, pb.s1, nst, dk, dv, st, DV, c0));
+    }
     return GDR_OK;
 }
 
@@ -647,28 +669,46 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     }
     if (!q || !k || !v || !dO || !dq || !dk_ || !dv_ || !beta || !dbeta || (!nogate(d) && (!g || !dg)))
         return fail(GDR_ERR_INVALID, "a required pointer is NULL");
+    if (policy == GDR_FULL_SAVE && !saved) return fail(GDR_ERR_INVALID, "required pointer 'saved' is NULL");
     PadBufs pb;
     if ((rc = pad_prologue(d, pk, policy, scratch, scratch_bytes, pb))) return rc;
     const gdr_desc e = inner_desc(d);
-    const int64_t rows = d->B * d->T * d->H;
-    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, dv = (int)d->DV;
-    const bool vec = d->gate == GDR_GATE_VECTOR;
+    size_t inner_saved = 0;
+    workspace(&e, pk, policy, &inner_saved, nullptr);
+    const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
+    const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
+    const bool vec = d->gate == GDR_GATE_VECTOR, scal = d->gate == GDR_GATE_SCALAR;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
-    PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st));
-    PAD_LAUNCH(launch_pad_rows(pb.t4, dO, rows, dv, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
-    if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nseq * d->H, dk, dv, st));
-    if (dht) PAD_LAUNCH(launch_pad_state(pb.s1, dht, nseq * d->H, dk, dv, st));
-    rc = run_bwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
-                 dht ? pb.s1 : nullptr, saved, pb.dq, pb.dk, pb.dv, vec ? pb.dg : dg, dbeta,
-                 dh0 ? pb.s2 : nullptr, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream, wy7);
-    if (rc) return rc;
-    PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st));
-    PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st));
-    PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st));
-    if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st));
-    if (dh0) PAD_LAUNCH(launch_unpad_state(dh0, pb.s2, nseq * d->H, dk, dv, st));
+    for (int b = 0; b < value_blocks(d); ++b) {
+        // value columns [c0, c0 + dv) as their own 128-wide problem; the
+        // key-side gradients (dq, dk, dg, dbeta) of the blocks are summed in
+        // block order, the value-side ones (dv, dh0) are the block's columns
+        const int c0 = b * DVD, dv = DV - c0 < DVD ? DV - c0 : DVD;
+        const bool first = b == 0;
+        PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st, DV, c0));
+        PAD_LAUNCH(launch_pad_rows(pb.t4, dO, rows, dv, esz, st, DV, c0));
+        if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nst, dk, dv, st, DV, c0));
+        if (dht) PAD_LAUNCH(launch_pad_state(pb.s1, dht, nst, dk, dv, st, DV, c0));
+        float* dgb = vec ? pb.dg : (scal && !first) ? pb.dg1 : dg;
+        void* dbb = first ? dbeta : pb.db1;
+        rc = run_bwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
+                     dht ? pb.s1 : nullptr, saved ? (const char*)saved + b * inner_saved : nullptr, pb.dq, pb.dk,
+                     pb.dv, dgb, dbb, dh0 ? pb.s2 : nullptr, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes,
+                     stream, wy7);
+        if (rc) return rc;
+        PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st, dk, 0, !first));
+        PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st, dk, 0, !first));
+        PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st, DV, c0));
+        if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st, dk, 0, !first));
+        if (!first) {
+            // one entry per token and head: dbeta, and dg of a scalar gate
+            PAD_LAUNCH(launch_add_entries(dbeta, pb.db1, rows, esz, st));
+            if (scal) PAD_LAUNCH(launch_add_entries(dg, pb.dg1, rows, 4, st));
+        }
+        if (dh0) PAD_LAUNCH(launch_unpad_state(dh0, pb.s2, nst, dk, dv, st, DV, c0));
+    }
     return GDR_OK;
 }
 #undef PAD_LAUNCH

@@ -270,12 +270,20 @@ hipError_t launch_scan_pair(const Shape& s, const Inputs& in, const Inter& it, f
 // into s.cu and fills s.stab, s.ctab and s.order (one workgroup).
 hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, int2* stab, int2* ctab,
                              int* order, hipStream_t st);
-// Widths below 128 (pad.hip): rows of width w <-> rows of width 128 (zeros
-// past w), esz = element bytes; states [n][dk][dv] <-> [n][128][128].
-hipError_t launch_pad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st);
-hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st);
-hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
-hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st);
+// Widths other than 128 (pad.hip): rows of width w <-> rows of width 128
+// (zeros past w), esz = element bytes; states [n][dk][dv] <-> [n][128][128].
+// The wide side may be a column block: ld = its row length (0: w), col0 =
+// the block's first column; add = accumulate into dst (type from esz).
+hipError_t launch_pad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st,
+                           int src_ld = 0, int col0 = 0);
+hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st,
+                             int dst_ld = 0, int col0 = 0, bool add = false);
+hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st,
+                            int src_dv = 0, int col0 = 0);
+// dst[i] += src[i] for n entries of esz bytes (bf16 or fp32)
+hipError_t launch_add_entries(void* dst, const void* src, int64_t n, int esz, hipStream_t st);
+hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st,
+                              int dst_dv = 0, int col0 = 0);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.
 // order: the ChunkOrder of the (chunk, head) items (regular batches).
 // per_chunk: launch the scalar-gate three-product kernel one workgroup per

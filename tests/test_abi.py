@@ -61,7 +61,7 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(DK=192), -2), (dict(DV=160), -2), (dict(DK=0), -1), (dict(DV=-3), -1), (dict(C=32), -2),
+    (dict(DK=192), -2), (dict(DV=1025), -2), (dict(DK=192, DV=160), -2), (dict(DK=0), -1), (dict(DV=-3), -1), (dict(C=32), -2),
     (dict(gate=5), -1), (dict(gate=4), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
 ])
 def test_descriptor_validation(kw, status):
@@ -264,3 +264,14 @@ def test_gate_status_validates_before_any_launch():
     assert lib.gdr_gate_status(ctypes.byref(d), -1, ctypes.c_void_p(256), 64, st, None) == -3
     assert lib.gdr_gate_status(ctypes.byref(_desc(B=2)), 3, ctypes.c_void_p(256), 1 << 30, st,
                                None) == -1  # a packed batch has B = 1
+
+
+def test_wide_values_run_as_value_blocks():
+    """A value width above 128 runs as ceil(DV / 128) value blocks of the
+    128-wide path: one saved area per block, scratch for the padded copies."""
+    rc, sv128, sc128 = _ws(_desc(T=256, DV=128), 1)
+    rc2, sv160, sc160 = _ws(_desc(T=256, DV=160), 1)
+    rc3, sv300, _ = _ws(_desc(T=256, DV=300), 1)
+    assert rc == rc2 == rc3 == 0
+    assert sv160 == 2 * sv128 and sv300 == 3 * sv128
+    assert sc160 > sc128

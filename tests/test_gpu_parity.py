@@ -610,3 +610,43 @@ def test_gate_status_reports_out_of_contract_decays(case):
             got_b = int(gdr.gate_status(d["q"], d["g"], d["v"], scratch).item())
             assert got_b == want, ("backward", got_b, want)
     print(f"[gate status] {case}: {want}", flush=True)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("dk,dv", [(128, 160), (80, 160), (64, 300)])
+def test_value_widths_above_128(gate, dk, dv):
+    """Value widths above 128 (the pages' extended tests use a value width of
+    160) run as 128-wide value blocks whose key-side gradients are summed:
+    two batch entries, a ragged last chunk, nonzero states, both policies."""
+    _need_gpu()
+    x = make_inputs(2, 100, 2, DK=dk, DV=dv, gate=gate, dtype="bf16", seed=54,
+                    gate_mean=4.0 if gate == "scalar" else 3.0, h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"wide/{gate}/{dk}x{dv}/{pol}", tl.compare(tl.run_gpu(x, pol), x))
+
+
+@pytest.mark.gpu
+def test_value_width_160_fp32_wy7_deltanet_and_packed():
+    """Value width 160 with fp32 storage and the seven-product producer, with
+    no gate (DeltaNet), and in a packed batch."""
+    _need_gpu()
+    x = make_inputs(1, 150, 2, DK=96, DV=160, gate="vector", dtype="fp32", seed=55, gate_mean=3.0,
+                    h0_std=0.1, dht_std=0.1)
+    _report("wide/fp32/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
+    xn = make_inputs(1, 130, 2, DK=128, DV=160, gate="scalar", dtype="bf16", seed=56,
+                     h0_std=0.1, dht_std=0.1)
+    xn["g"] = np.zeros_like(xn["g"])
+    _report("wide/deltanet", tl.compare(tl.run_gpu(xn, nogate=True), xn))
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=57)
+    rng = np.random.default_rng(58)
+    # value width 160: the packed inputs' 128 value columns and 32 more
+    for n in ("v", "dO"):
+        extra = np.asarray(xp[n][..., :32])[..., ::-1]
+        xp[n] = np.ascontiguousarray(np.concatenate([xp[n], extra], axis=-1))
+    for n in ("h0", "dht"):
+        xp[n] = np.ascontiguousarray(np.concatenate(
+            [xp[n], (0.1 * rng.standard_normal(xp[n].shape[:-1] + (32,))).astype(np.float32)
+             .astype(np.float64)], axis=-1))
+    _report("wide/packed", tl.compare_packed(tl.run_gpu_packed(xp), xp))
