@@ -29,7 +29,7 @@ import ctypes
 import os
 
 __all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_fwd_gdn2", "gdr_bwd_gdn2",
-           "chunk_gated_delta_rule", "workspace_size",
+           "chunk_gated_delta_rule", "chunk_gdn2", "workspace_size",
            "library_path", "load",
            "profile_begin", "profile_end", "set_local_form", "gate_status", "GdrError",
            "RECOMPUTE", "FULL_SAVE"]
@@ -499,7 +499,55 @@ def _autograd_function():
     return _ChunkGatedDeltaRule
 
 
+def _autograd_gdn2():
+    torch = _torch()
+
+    class _ChunkGDN2(torch.autograd.Function):
+        """GDN2 forward by gdr_fwd_gdn2, backward by gdr_bwd_gdn2; no arithmetic
+        here (an absent output adjoint is passed as zeros)."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, erase, write, h0, policy):
+            ctx.set_materialize_grads(False)
+            o, ht, saved = gdr_fwd_gdn2(q, k, v, g, erase, write, h0, policy=policy)
+            ctx.policy = policy
+            ctx.has_h0 = h0 is not None
+            ctx.has_saved = saved is not None
+            ctx.save_for_backward(q, k, v, g, erase, write,
+                                  h0 if h0 is not None else q.new_empty(0),
+                                  saved if saved is not None else q.new_empty(0, dtype=torch.uint8))
+            return o, ht
+
+        @staticmethod
+        def backward(ctx, dO, dht):
+            q, k, v, g, erase, write, h0, saved = ctx.saved_tensors
+            h0 = h0 if ctx.has_h0 else None
+            saved = saved if ctx.has_saved else None
+            if dO is None and dht is None:
+                return (None,) * 8
+            if dO is None:
+                dO = torch.zeros_like(v)
+            gr = gdr_bwd_gdn2(q, k, v, g, erase, write, h0, dO.contiguous(),
+                              None if dht is None else dht.contiguous(), saved=saved,
+                              policy=ctx.policy, want_dh0=h0 is not None)
+            return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["derase"], gr["dwrite"], gr["dh0"], None)
+
+    return _ChunkGDN2
+
+
 _AUTOGRAD = None
+_AUTOGRAD_GDN2 = None
+
+
+def chunk_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute"):
+    """Differentiable GDN2 operator (per-key-channel decay g, erase gate per
+    key channel, write gate per value channel; bf16 q, k, v, erase, write):
+    returns (o, ht) and back-propagates through gdr_bwd_gdn2 into q, k, v,
+    g, erase, write and h0."""
+    global _AUTOGRAD_GDN2
+    if _AUTOGRAD_GDN2 is None:
+        _AUTOGRAD_GDN2 = _autograd_gdn2()
+    return _AUTOGRAD_GDN2.apply(q, k, v, g, erase, write, h0, policy)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, policy="recompute", cu_seqlens=None):

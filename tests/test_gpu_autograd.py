@@ -103,3 +103,35 @@ def test_autograd_packed():
     tail = int(x["cu"][-1])
     assert tail == x["q"].shape[1]
     tl.compare_packed(got, x)
+
+
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_gdn2_autograd_equals_direct_backward_and_oracle(policy):
+    """chunk_gdn2: autograd's gradients are gdr_bwd_gdn2's bit for bit and
+    meet the GDN2 oracle's bar."""
+    _need_gpu()
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    from tests.test_gpu_gdn2 import compare_gdn2
+    x = make_inputs(1, 200, 2, gate="gdn2", seed=52, gate_mean=3.0, h0_std=0.1, dht_std=0.1)
+    d = tl.device_inputs(x)
+    d["ers"] = tl.to_dev(x["ers"], torch.bfloat16)
+    d["wrt"] = tl.to_dev(x["wrt"], torch.bfloat16)
+    lv = _leaves(d, ("q", "k", "v", "g", "ers", "wrt", "h0"))
+    o, ht = gdr.chunk_gdn2(lv["q"], lv["k"], lv["v"], lv["g"], lv["ers"], lv["wrt"], lv["h0"],
+                           policy=policy)
+    loss = (o.float() * d["dO"].float()).sum() + (ht * d["dht"]).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    got = {"o": _np(o), "ht": _np(ht), "dq": _np(lv["q"].grad), "dk": _np(lv["k"].grad),
+           "dv": _np(lv["v"].grad), "dg": _np(lv["g"].grad), "ders": _np(lv["ers"].grad),
+           "dwrt": _np(lv["wrt"].grad), "dh0": _np(lv["h0"].grad)}
+    _, _, saved = gdr.gdr_fwd_gdn2(d["q"], d["k"], d["v"], d["g"], d["ers"], d["wrt"], d["h0"],
+                                   policy=policy)
+    ref = gdr.gdr_bwd_gdn2(d["q"], d["k"], d["v"], d["g"], d["ers"], d["wrt"], d["h0"], d["dO"],
+                           d["dht"], saved=saved, policy=policy)
+    torch.cuda.synchronize()
+    for n, r in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("ders", "derase"),
+                 ("dwrt", "dwrite"), ("dh0", "dh0")):
+        assert np.array_equal(got[n], _np(ref[r])), n
+    compare_gdn2(got, x)
