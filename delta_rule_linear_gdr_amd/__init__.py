@@ -44,7 +44,7 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
           -3: "GDR_ERR_WORKSPACE", -4: "GDR_ERR_HIP"}
 EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
-           "gdr_fwd_gdn2", "gdr_bwd_gdn2",
+           "gdr_fwd_gdn2", "gdr_bwd_gdn2", "gdr_fwd_gdn2_varlen", "gdr_bwd_gdn2_varlen",
            "gdr_bwd_noalloc", "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
            "gdr_profile_begin",
            "gdr_profile_end", "gdr_set_local_form", "gdr_gate_status", "gdr_status_string",
@@ -96,6 +96,10 @@ def load():
     lib.gdr_fwd_gdn2.restype = i32
     lib.gdr_bwd_gdn2.argtypes = [dp, i32] + [p] * 18 + [sz, p]
     lib.gdr_bwd_gdn2.restype = i32
+    lib.gdr_fwd_gdn2_varlen.argtypes = [dp, i32, p, ctypes.c_int64] + [p] * 11 + [sz, p]
+    lib.gdr_fwd_gdn2_varlen.restype = i32
+    lib.gdr_bwd_gdn2_varlen.argtypes = [dp, i32, p, ctypes.c_int64] + [p] * 18 + [sz, p]
+    lib.gdr_bwd_gdn2_varlen.restype = i32
     lib.gdr_bwd_noalloc.argtypes = [dp, i32] + [p] * 16
     lib.gdr_bwd_noalloc.restype = i32
     i64 = ctypes.c_int64
@@ -392,62 +396,74 @@ def gdr_bwd(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
 
 
 def gdr_fwd_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute", want_ht=True,
-                 scratch=None):
-    """GDN2 forward (per-key-channel gate g [B,T,H,128], erase gate [B,T,H,128]
-    per key, write gate [B,T,H,128] per value, bf16). Returns (o, ht, saved)."""
+                 scratch=None, cu_seqlens=None):
+    """GDN2 forward (per-key-channel gate g [B,T,H,DK] fp32, erase gate
+    [B,T,H,DK] per key and write gate [B,T,H,DV] per value, bf16). Returns
+    (o, ht, saved). cu_seqlens: a packed batch, as for gdr_fwd."""
     torch = _torch()
     if erase is None or write is None or g is None or g.dim() != 4:
         raise ValueError("GDN2 needs a per-channel g and both erase and write gates")
-    _validate(q, k, v, g, None, None, h0=h0, scratch=scratch, erase=erase, write=write)
+    n_seq = _seqs(cu_seqlens, q)
+    _validate(q, k, v, g, None, n_seq, h0=h0, scratch=scratch, erase=erase, write=write)
     d = _desc_from(q, g, v)
     d.gate = GATE_GDN2
     pol = _policy(policy)
     lib = load()
-    saved_b, scratch_b = _sizes(d, pol, None)
+    saved_b, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
+    ns = B if n_seq is None else n_seq
     o = torch.empty_like(v)
-    ht = torch.empty((B, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+    ht = torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
                      device=q.device) if want_ht else None
     saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None
     if scratch is None:
         scratch = _scratch(scratch_b, q.device)
-    _check(lib.gdr_fwd_gdn2(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
-                            _ptr(write), _ptr(h0), _ptr(o), _ptr(ht), _ptr(saved), _ptr(scratch),
-                            scratch.numel(), _stream()))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase), _ptr(write), _ptr(h0), _ptr(o), _ptr(ht),
+            _ptr(saved), _ptr(scratch), scratch.numel(), _stream())
+    if n_seq is None:
+        _check(lib.gdr_fwd_gdn2(ctypes.byref(d), pol, *args))
+    else:
+        _check(lib.gdr_fwd_gdn2_varlen(ctypes.byref(d), pol, _ptr(cu_seqlens), n_seq, *args))
     return o, ht, saved
 
 
 def gdr_bwd_gdn2(q, k, v, g, erase, write, h0, dO, dht=None, saved=None, policy="recompute",
-                 want_dh0=True, scratch=None, out=None):
-    """GDN2 backward. Returns dict dq, dk, dv, dg, derase, dwrite, dh0."""
+                 want_dh0=True, scratch=None, out=None, cu_seqlens=None):
+    """GDN2 backward. Returns dict dq, dk, dv, dg, derase, dwrite, dh0.
+    cu_seqlens: the offsets the forward ran with (packed batch)."""
     torch = _torch()
     if erase is None or write is None or g is None or g.dim() != 4:
         raise ValueError("GDN2 needs a per-channel g and both erase and write gates")
     if dO is None:
         raise ValueError("dO is required")
+    n_seq = _seqs(cu_seqlens, q)
     d = _desc_from(q, g, v)
     d.gate = GATE_GDN2
     pol = _policy(policy)
     lib = load()
-    saved_b, scratch_b = _sizes(d, pol, None)
+    saved_b, scratch_b = _sizes(d, pol, n_seq)
     if pol == FULL_SAVE and saved is None:
         raise ValueError("the full-save backward needs the forward's saved area")
-    _validate(q, k, v, g, None, None, h0=h0, dO=dO, dht=dht, out=out, saved=saved,
+    _validate(q, k, v, g, None, n_seq, h0=h0, dO=dO, dht=dht, out=out, saved=saved,
               saved_bytes=saved_b, scratch=scratch, erase=erase, write=write)
     B, T, H, _ = q.shape
+    ns = B if n_seq is None else n_seq
     if out is None:
         out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                    dg=torch.empty_like(g), derase=torch.empty_like(erase),
                    dwrite=torch.empty_like(write),
-                   dh0=torch.empty((B, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
+                   dh0=torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
                                    device=q.device) if want_dh0 else None)
     if scratch is None:
         scratch = _scratch(scratch_b, q.device)
-    _check(lib.gdr_bwd_gdn2(ctypes.byref(d), pol, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase),
-                            _ptr(write), _ptr(h0), _ptr(dO), _ptr(dht), _ptr(saved),
-                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
-                            _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out.get("dh0")),
-                            _ptr(scratch), scratch.numel(), _stream()))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(erase), _ptr(write), _ptr(h0), _ptr(dO), _ptr(dht),
+            _ptr(saved), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+            _ptr(out["derase"]), _ptr(out["dwrite"]), _ptr(out.get("dh0")), _ptr(scratch),
+            scratch.numel(), _stream())
+    if n_seq is None:
+        _check(lib.gdr_bwd_gdn2(ctypes.byref(d), pol, *args))
+    else:
+        _check(lib.gdr_bwd_gdn2_varlen(ctypes.byref(d), pol, _ptr(cu_seqlens), n_seq, *args))
     return out
 
 
@@ -507,30 +523,34 @@ def _autograd_gdn2():
         here (an absent output adjoint is passed as zeros)."""
 
         @staticmethod
-        def forward(ctx, q, k, v, g, erase, write, h0, policy):
+        def forward(ctx, q, k, v, g, erase, write, h0, policy, cu_seqlens):
             ctx.set_materialize_grads(False)
-            o, ht, saved = gdr_fwd_gdn2(q, k, v, g, erase, write, h0, policy=policy)
+            o, ht, saved = gdr_fwd_gdn2(q, k, v, g, erase, write, h0, policy=policy,
+                                        cu_seqlens=cu_seqlens)
             ctx.policy = policy
             ctx.has_h0 = h0 is not None
-            ctx.has_saved = saved is not None
+            ctx.has_saved, ctx.packed = saved is not None, cu_seqlens is not None
             ctx.save_for_backward(q, k, v, g, erase, write,
                                   h0 if h0 is not None else q.new_empty(0),
-                                  saved if saved is not None else q.new_empty(0, dtype=torch.uint8))
+                                  saved if saved is not None else q.new_empty(0, dtype=torch.uint8),
+                                  cu_seqlens if cu_seqlens is not None else q.new_empty(0, dtype=torch.int64))
             return o, ht
 
         @staticmethod
         def backward(ctx, dO, dht):
-            q, k, v, g, erase, write, h0, saved = ctx.saved_tensors
+            q, k, v, g, erase, write, h0, saved, cu = ctx.saved_tensors
             h0 = h0 if ctx.has_h0 else None
             saved = saved if ctx.has_saved else None
+            cu = cu if ctx.packed else None
             if dO is None and dht is None:
-                return (None,) * 8
+                return (None,) * 9
             if dO is None:
                 dO = torch.zeros_like(v)
             gr = gdr_bwd_gdn2(q, k, v, g, erase, write, h0, dO.contiguous(),
                               None if dht is None else dht.contiguous(), saved=saved,
-                              policy=ctx.policy, want_dh0=h0 is not None)
-            return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["derase"], gr["dwrite"], gr["dh0"], None)
+                              policy=ctx.policy, want_dh0=h0 is not None, cu_seqlens=cu)
+            return (gr["dq"], gr["dk"], gr["dv"], gr["dg"], gr["derase"], gr["dwrite"], gr["dh0"],
+                    None, None)
 
     return _ChunkGDN2
 
@@ -539,15 +559,15 @@ _AUTOGRAD = None
 _AUTOGRAD_GDN2 = None
 
 
-def chunk_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute"):
+def chunk_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute", cu_seqlens=None):
     """Differentiable GDN2 operator (per-key-channel decay g, erase gate per
     key channel, write gate per value channel; bf16 q, k, v, erase, write):
     returns (o, ht) and back-propagates through gdr_bwd_gdn2 into q, k, v,
-    g, erase, write and h0."""
+    g, erase, write and h0. cu_seqlens makes a packed batch."""
     global _AUTOGRAD_GDN2
     if _AUTOGRAD_GDN2 is None:
         _AUTOGRAD_GDN2 = _autograd_gdn2()
-    return _AUTOGRAD_GDN2.apply(q, k, v, g, erase, write, h0, policy)
+    return _AUTOGRAD_GDN2.apply(q, k, v, g, erase, write, h0, policy, cu_seqlens)
 
 
 def chunk_gated_delta_rule(q, k, v, g, beta, h0=None, policy="recompute", cu_seqlens=None):

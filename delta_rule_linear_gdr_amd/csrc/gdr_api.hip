@@ -209,7 +209,7 @@ int check_policy(int policy)
 bool gdn2(const gdr_desc* d) { return d->gate == GDR_GATE_GDN2; }
 
 // The GDN2 entry points take the GDN2 gate kind, and only they do; GDN2 runs
-// bf16 inputs at widths 128/128 on regular batches.
+// bf16 inputs.
 int check_gdn2(const gdr_desc* d, bool gdn2_entry)
 {
     if (gdn2(d) != gdn2_entry)
@@ -220,9 +220,6 @@ int check_gdn2(const gdr_desc* d, bool gdn2_entry)
     if (!gdn2_entry) return GDR_OK;
     if (d->dtype != GDR_BF16)
         return fail(GDR_ERR_UNSUPPORTED, "GDN2 is built for bf16 inputs (dtype %d)", d->dtype);
-    if (d->DK != DKD || d->DV != DVD)
-        return fail(GDR_ERR_UNSUPPORTED, "GDN2 is built for key/value width 128/128 (%lld/%lld)",
-                    (long long)d->DK, (long long)d->DV);
     return GDR_OK;
 }
 
@@ -384,7 +381,6 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     }
     if (gdn2(d)) {
         if (wy7) return fail(GDR_ERR_UNSUPPORTED, "GDN2 has no seven-product backward");
-        if (pk.on) return fail(GDR_ERR_UNSUPPORTED, "GDN2 runs regular batches only");
         const void *ers = g2.ers, *wrt = g2.wrt, *ders = g2.ders, *dwrt = g2.dwrt;
         REQUIRE_PTR(ers); REQUIRE_PTR(wrt); REQUIRE_PTR(ders); REQUIRE_PTR(dwrt);
     } else {
@@ -466,7 +462,6 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(o);
     if (!nogate(d)) REQUIRE_PTR_A(g, 4);
     if (gdn2(d)) {
-        if (pk.on) return fail(GDR_ERR_UNSUPPORTED, "GDN2 runs regular batches only");
         const void *ers = g2.ers, *wrt = g2.wrt;
         REQUIRE_PTR(ers); REQUIRE_PTR(wrt);
     } else {
@@ -534,6 +529,7 @@ struct PadBufs {
     float *s0, *s1, *s2;                    // states: h0, ht or dht, dh0
     float* dg1;                             // scalar gate, value blocks after the first: dg
     void* db1;                              // value blocks after the first: dbeta
+    void *ers, *wrt, *ders, *dwrt;          // GDN2 gates and their gradients, 128 wide
     size_t bytes;
 };
 PadBufs pad_layout(const gdr_desc* d, const Packed& pk, void* base)
@@ -557,16 +553,22 @@ PadBufs pad_layout(const gdr_desc* d, const Packed& pk, void* base)
     p.dq = take(rows * DKD * esz);
     p.dk = take(rows * DKD * esz);
     p.dv = take(rows * DVD * esz);
-    if (d->gate == GDR_GATE_VECTOR) {
+    if (d->gate == GDR_GATE_VECTOR || d->gate == GDR_GATE_GDN2) {
         p.g = (float*)take(rows * DKD * 4);
         p.dg = (float*)take(rows * DKD * 4);
+    }
+    if (d->gate == GDR_GATE_GDN2) {
+        p.ers = take(rows * DKD * esz);
+        p.wrt = take(rows * DVD * esz);
+        p.ders = take(rows * DKD * esz);
+        p.dwrt = take(rows * DVD * esz);
     }
     p.s0 = (float*)take(nst * DKD * DVD * 4);
     p.s1 = (float*)take(nst * DKD * DVD * 4);
     p.s2 = (float*)take(nst * DKD * DVD * 4);
     if (value_blocks(d) > 1) {
         if (d->gate == GDR_GATE_SCALAR) p.dg1 = (float*)take(rows * 4);
-        p.db1 = take(rows * esz);
+        if (d->gate != GDR_GATE_GDN2) p.db1 = take(rows * esz);
     }
     p.bytes = off;
     return p;
@@ -609,7 +611,7 @@ int pad_prologue(const gdr_desc* d, const Packed& pk, int policy, void* scratch,
 
 int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
                    const void* v, const float* g, const void* beta, const float* h0, void* o, float* ht,
-                   void* saved, void* scratch, size_t scratch_bytes, void* stream)
+                   void* saved, void* scratch, size_t scratch_bytes, void* stream, const Gdn2Args& g2)
 {
     int rc = check_desc(d);
     if (rc) return rc;
@@ -622,7 +624,8 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
         hipError_t e = fill_state(ht, h0, nseq * d->H * d->DK * d->DV, st);
         return e == hipSuccess ? GDR_OK : hip_fail(e, "ht copy");
     }
-    if (!q || !k || !v || !o || !beta || (!g && !nogate(d)))
+    const bool g2on = gdn2(d);
+    if (!q || !k || !v || !o || (g2on ? (!g2.ers || !g2.wrt) : !beta) || (!g && !nogate(d)))
         return fail(GDR_ERR_INVALID, "a required pointer is NULL");
     if (policy == GDR_FULL_SAVE && !saved) return fail(GDR_ERR_INVALID, "required pointer 'saved' is NULL");
     PadBufs pb;
@@ -632,18 +635,23 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     workspace(&e, pk, policy, &inner_saved, nullptr);
     const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
     const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
-    const bool vec = d->gate == GDR_GATE_VECTOR;
+    const bool vec = d->gate == GDR_GATE_VECTOR || g2on;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
+    if (g2on) PAD_LAUNCH(launch_pad_rows(pb.ers, g2.ers, rows, dk, esz, st));
+    Gdn2Args gi;
+    gi.ers = pb.ers;
+    gi.wrt = pb.wrt;
     for (int b = 0; b < value_blocks(d); ++b) {
         // value columns [c0, c0 + dv) as their own 128-wide problem
         const int c0 = b * DVD, dv = DV - c0 < DVD ? DV - c0 : DVD;
         PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st, DV, c0));
+        if (g2on) PAD_LAUNCH(launch_pad_rows(pb.wrt, g2.wrt, rows, dv, esz, st, DV, c0));
         if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nst, dk, dv, st, DV, c0));
         rc = run_fwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
                      ht ? pb.s1 : nullptr, saved ? (char*)saved + b * inner_saved : nullptr,
-                     (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream);
+                     (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream, g2on ? gi : Gdn2Args{});
         if (rc) return rc;
         PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st, DV, c0));
         if (ht) PAD_LAUNCH(launch_unpad_state(ht, pb.s1, nst, dk, dv, st, DV, c0));
@@ -654,7 +662,8 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
 int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k,
                    const void* v, const float* g, const void* beta, const float* h0, const void* dO,
                    const float* dht, const void* saved, void* dq, void* dk_, void* dv_, float* dg,
-                   void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+                   void* dbeta, float* dh0, void* scratch, size_t scratch_bytes, void* stream, bool wy7,
+                   const Gdn2Args& g2)
 {
     int rc = check_desc(d);
     if (rc) return rc;
@@ -667,8 +676,11 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
         hipError_t e = fill_state(dh0, dht, nseq * d->H * d->DK * d->DV, st);
         return e == hipSuccess ? GDR_OK : hip_fail(e, "dh0 copy");
     }
-    if (!q || !k || !v || !dO || !dq || !dk_ || !dv_ || !beta || !dbeta || (!nogate(d) && (!g || !dg)))
+    const bool g2on = gdn2(d);
+    if (!q || !k || !v || !dO || !dq || !dk_ || !dv_ || (!nogate(d) && (!g || !dg)) ||
+        (g2on ? (!g2.ers || !g2.wrt || !g2.ders || !g2.dwrt) : (!beta || !dbeta)))
         return fail(GDR_ERR_INVALID, "a required pointer is NULL");
+    if (g2on && wy7) return fail(GDR_ERR_UNSUPPORTED, "GDN2 has no seven-product backward");
     if (policy == GDR_FULL_SAVE && !saved) return fail(GDR_ERR_INVALID, "required pointer 'saved' is NULL");
     PadBufs pb;
     if ((rc = pad_prologue(d, pk, policy, scratch, scratch_bytes, pb))) return rc;
@@ -677,10 +689,16 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     workspace(&e, pk, policy, &inner_saved, nullptr);
     const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
     const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
-    const bool vec = d->gate == GDR_GATE_VECTOR, scal = d->gate == GDR_GATE_SCALAR;
+    const bool vec = d->gate == GDR_GATE_VECTOR || g2on, scal = d->gate == GDR_GATE_SCALAR;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
+    if (g2on) PAD_LAUNCH(launch_pad_rows(pb.ers, g2.ers, rows, dk, esz, st));
+    Gdn2Args gi;
+    gi.ers = pb.ers;
+    gi.wrt = pb.wrt;
+    gi.ders = pb.ders;
+    gi.dwrt = pb.dwrt;
     for (int b = 0; b < value_blocks(d); ++b) {
         // value columns [c0, c0 + dv) as their own 128-wide problem; the
         // key-side gradients (dq, dk, dg, dbeta) of the blocks are summed in
@@ -689,20 +707,26 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
         const bool first = b == 0;
         PAD_LAUNCH(launch_pad_rows(pb.v, v, rows, dv, esz, st, DV, c0));
         PAD_LAUNCH(launch_pad_rows(pb.t4, dO, rows, dv, esz, st, DV, c0));
+        if (g2on) PAD_LAUNCH(launch_pad_rows(pb.wrt, g2.wrt, rows, dv, esz, st, DV, c0));
         if (h0) PAD_LAUNCH(launch_pad_state(pb.s0, h0, nst, dk, dv, st, DV, c0));
         if (dht) PAD_LAUNCH(launch_pad_state(pb.s1, dht, nst, dk, dv, st, DV, c0));
         float* dgb = vec ? pb.dg : (scal && !first) ? pb.dg1 : dg;
-        void* dbb = first ? dbeta : pb.db1;
+        void* dbb = g2on ? nullptr : first ? dbeta : pb.db1;
         rc = run_bwd(&e, pk, policy, pb.q, pb.k, pb.v, vec ? pb.g : g, beta, h0 ? pb.s0 : nullptr, pb.t4,
                      dht ? pb.s1 : nullptr, saved ? (const char*)saved + b * inner_saved : nullptr, pb.dq, pb.dk,
                      pb.dv, dgb, dbb, dh0 ? pb.s2 : nullptr, (char*)scratch + pb.bytes, scratch_bytes - pb.bytes,
-                     stream, wy7);
+                     stream, wy7, g2on ? gi : Gdn2Args{});
         if (rc) return rc;
+        if (g2on) {
+            // the erase gradient is key-side (summed over the blocks), the write gradient the block's columns
+            PAD_LAUNCH(launch_unpad_rows(g2.ders, pb.ders, rows, dk, esz, st, dk, 0, !first));
+            PAD_LAUNCH(launch_unpad_rows(g2.dwrt, pb.dwrt, rows, dv, esz, st, DV, c0));
+        }
         PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st, dk, 0, !first));
         PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st, dk, 0, !first));
         PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st, DV, c0));
         if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st, dk, 0, !first));
-        if (!first) {
+        if (!first && !g2on) {
             // one entry per token and head: dbeta, and dg of a scalar gate
             PAD_LAUNCH(launch_add_entries(dbeta, pb.db1, rows, esz, st));
             if (scal) PAD_LAUNCH(launch_add_entries(dg, pb.dg1, rows, 4, st));
@@ -713,27 +737,37 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
 }
 #undef PAD_LAUNCH
 
-// Entry dispatch: the padded path for widths below 128.
+// Entry dispatch: the padded path for widths other than 128. g2: the GDN2
+// entry points' gate tensors (null for the beta entry points).
 int any_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, void* o, float* ht, void* saved,
-            void* scratch, size_t scratch_bytes, void* stream)
+            void* scratch, size_t scratch_bytes, void* stream, const Gdn2Args* g2 = nullptr)
 {
-    if (d && gdn2(d)) return check_gdn2(d, false);
-    if (d && padded(d))
-        return run_fwd_padded(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
-    return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream);
+    if (!d) return check_desc(d);
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_gdn2(d, g2 != nullptr))) return rc;
+    const Gdn2Args ga = g2 ? *g2 : Gdn2Args{};
+    if (padded(d))
+        return run_fwd_padded(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream,
+                              ga);
+    return run_fwd(d, pk, policy, q, k, v, g, beta, h0, o, ht, saved, scratch, scratch_bytes, stream, ga);
 }
 int any_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, const void* k, const void* v,
             const float* g, const void* beta, const float* h0, const void* dO, const float* dht,
             const void* saved, void* dq, void* dk, void* dv, float* dg, void* dbeta, float* dh0,
-            void* scratch, size_t scratch_bytes, void* stream, bool wy7)
+            void* scratch, size_t scratch_bytes, void* stream, bool wy7, const Gdn2Args* g2 = nullptr)
 {
-    if (d && gdn2(d)) return check_gdn2(d, false);
-    if (d && padded(d))
+    if (!d) return check_desc(d);
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if ((rc = check_gdn2(d, g2 != nullptr))) return rc;
+    const Gdn2Args ga = g2 ? *g2 : Gdn2Args{};
+    if (padded(d))
         return run_bwd_padded(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0,
-                              scratch, scratch_bytes, stream, wy7);
+                              scratch, scratch_bytes, stream, wy7, ga);
     return run_bwd(d, pk, policy, q, k, v, g, beta, h0, dO, dht, saved, dq, dk, dv, dg, dbeta, dh0, scratch,
-                   scratch_bytes, stream, wy7);
+                   scratch_bytes, stream, wy7, ga);
 }
 
 // ---- gate-range status (gdr_gate_status) ----
@@ -940,14 +974,26 @@ int gdr_fwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, co
                  const float* g, const void* erase, const void* write, const float* h0, void* o,
                  float* ht, void* saved, void* scratch, size_t scratch_bytes, void* stream)
 {
-    int rc = check_desc(d);
-    if (rc) return rc;
-    if ((rc = check_gdn2(d, true))) return rc;
     Gdn2Args g2;
     g2.ers = erase;
     g2.wrt = write;
-    return run_fwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, o, ht, saved, scratch, scratch_bytes,
-                   stream, g2);
+    return any_fwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, o, ht, saved, scratch, scratch_bytes, stream,
+                   &g2);
+}
+
+int gdr_fwd_gdn2_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                        const void* q, const void* k, const void* v, const float* g, const void* erase,
+                        const void* write, const float* h0, void* o, float* ht, void* saved, void* scratch,
+                        size_t scratch_bytes, void* stream)
+{
+    Packed pk;
+    pk.on = true;
+    pk.cu = cu_seqlens;
+    pk.n = n_seq;
+    Gdn2Args g2;
+    g2.ers = erase;
+    g2.wrt = write;
+    return any_fwd(d, pk, policy, q, k, v, g, nullptr, h0, o, ht, saved, scratch, scratch_bytes, stream, &g2);
 }
 
 int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
@@ -956,16 +1002,32 @@ int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, co
                  float* dg, void* derase, void* dwrite, float* dh0, void* scratch,
                  size_t scratch_bytes, void* stream)
 {
-    int rc = check_desc(d);
-    if (rc) return rc;
-    if ((rc = check_gdn2(d, true))) return rc;
     Gdn2Args g2;
     g2.ers = erase;
     g2.wrt = write;
     g2.ders = derase;
     g2.dwrt = dwrite;
-    return run_bwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, nullptr,
-                   dh0, scratch, scratch_bytes, stream, false, g2);
+    return any_bwd(d, Packed{}, policy, q, k, v, g, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, nullptr, dh0,
+                   scratch, scratch_bytes, stream, false, &g2);
+}
+
+int gdr_bwd_gdn2_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                        const void* q, const void* k, const void* v, const float* g, const void* erase,
+                        const void* write, const float* h0, const void* dO, const float* dht,
+                        const void* saved, void* dq, void* dk, void* dv, float* dg, void* derase,
+                        void* dwrite, float* dh0, void* scratch, size_t scratch_bytes, void* stream)
+{
+    Packed pk;
+    pk.on = true;
+    pk.cu = cu_seqlens;
+    pk.n = n_seq;
+    Gdn2Args g2;
+    g2.ers = erase;
+    g2.wrt = write;
+    g2.ders = derase;
+    g2.dwrt = dwrite;
+    return any_bwd(d, pk, policy, q, k, v, g, nullptr, h0, dO, dht, saved, dq, dk, dv, dg, nullptr, dh0, scratch,
+                   scratch_bytes, stream, false, &g2);
 }
 
 const char* gdr_status_string(int status)

@@ -153,13 +153,16 @@ int gdr_bwd_wy7(const gdr_desc* d, int policy, const void* q, const void* k, con
  *     S_t = St + k_t r^T,   o_t = S_t^T q_t
  * which is the vector-gate recurrence when erase_t = write_t = beta_t. The
  * chunk system is the same with E = erase o exp(G) o K and Z = write o V.
- * Layouts: g, dg [B,T,H,128] fp32; erase, derase [B,T,H,128] (per key) and
- * write, dwrite [B,T,H,128] (per value) in bf16, 16-byte aligned; the rest as
- * for gdr_fwd / gdr_bwd. d->gate must be GDR_GATE_GDN2, d->dtype GDR_BF16 and
- * the widths 128/128 (else GDR_ERR_UNSUPPORTED); regular batches only. The
- * workspace is the vector gate's (gdr_workspace_size with either gate kind).
- * derase and dwrite are the exact gradients entry by entry; their sums over
- * channels are what a shared beta's gradient would be. */
+ * Layouts: g, dg [B,T,H,DK] fp32; erase, derase [B,T,H,DK] (per key) and
+ * write, dwrite [B,T,H,DV] (per value) in bf16, 16-byte aligned; the rest as
+ * for gdr_fwd / gdr_bwd, including widths (keys up to 128, values up to 1024)
+ * and the packed variable-length form (the _varlen calls, with the offsets
+ * and per-sequence states of gdr_fwd_varlen). d->gate must be GDR_GATE_GDN2
+ * and d->dtype GDR_BF16 (fp32 storage returns GDR_ERR_UNSUPPORTED); there is
+ * no seven-product form. The workspace is gdr_workspace_size(_varlen)'s for
+ * the GDN2 descriptor. derase and dwrite are the exact gradients entry by
+ * entry; their sums over channels are what a shared beta's gradient would
+ * be. */
 int gdr_fwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
                  const float* g, const void* erase, const void* write, const float* h0, void* o,
                  float* ht, void* saved, void* scratch, size_t scratch_bytes, void* stream);
@@ -168,6 +171,15 @@ int gdr_bwd_gdn2(const gdr_desc* d, int policy, const void* q, const void* k, co
                  const void* dO, const float* dht, const void* saved, void* dq, void* dk, void* dv,
                  float* dg, void* derase, void* dwrite, float* dh0, void* scratch,
                  size_t scratch_bytes, void* stream);
+int gdr_fwd_gdn2_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                        const void* q, const void* k, const void* v, const float* g, const void* erase,
+                        const void* write, const float* h0, void* o, float* ht, void* saved, void* scratch,
+                        size_t scratch_bytes, void* stream);
+int gdr_bwd_gdn2_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens, int64_t n_seq,
+                        const void* q, const void* k, const void* v, const float* g, const void* erase,
+                        const void* write, const float* h0, const void* dO, const float* dht,
+                        const void* saved, void* dq, void* dk, void* dv, float* dg, void* derase,
+                        void* dwrite, float* dh0, void* scratch, size_t scratch_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): gdr_bwd

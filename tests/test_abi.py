@@ -234,7 +234,7 @@ def test_noalloc_rejects_problems_past_its_array():
 
 def test_gdn2_entry_points_take_only_gdn2():
     """GDN2 goes through gdr_fwd_gdn2 / gdr_bwd_gdn2 alone; they take bf16
-    inputs at 128/128 and refuse other gate kinds, all before any launch."""
+    inputs and refuse other gate kinds, all before any launch."""
     lib = gdr.load()
     nul = [None] * 20
     gd2 = _desc(gate=3)
@@ -243,8 +243,7 @@ def test_gdn2_entry_points_take_only_gdn2():
     assert lib.gdr_bwd(ctypes.byref(gd2), 0, *nul[:16], 0, None) == -1
     assert b"gdr_fwd_gdn2" in lib.gdr_last_error()
     # the GDN2 entry points refuse other gate kinds, fp32 and narrow widths
-    for kw, status in ((dict(gate=1), -1), (dict(gate=3, dtype=1), -2), (dict(gate=3, DK=80), -2),
-                       (dict(gate=3, DV=96), -2)):
+    for kw, status in ((dict(gate=1), -1), (dict(gate=3, dtype=1), -2), (dict(gate=3, DK=192), -2)):
         d = _desc(**kw)
         assert lib.gdr_fwd_gdn2(ctypes.byref(d), 0, *nul[:11], 0, None) == status, kw
         assert lib.gdr_bwd_gdn2(ctypes.byref(d), 0, *nul[:18], 0, None) == status, kw

@@ -135,3 +135,28 @@ def test_gdn2_autograd_equals_direct_backward_and_oracle(policy):
                  ("dwrt", "dwrite"), ("dh0", "dh0")):
         assert np.array_equal(got[n], _np(ref[r])), n
     compare_gdn2(got, x)
+
+
+def test_gdn2_autograd_packed():
+    """chunk_gdn2 over a packed batch that covers every token (autograd's
+    gradient buffers are the library's outputs): per-sequence states, and the
+    GDN2 oracle's bar per sequence."""
+    _need_gpu()
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    from tests.test_gpu_gdn2 import compare_gdn2_packed
+    x = make_packed_inputs([90, 0, 150], H=2, gate="gdn2", seed=53, gate_mean=3.0)
+    d = tl.device_inputs(x)
+    d["ers"] = tl.to_dev(x["ers"], torch.bfloat16)
+    d["wrt"] = tl.to_dev(x["wrt"], torch.bfloat16)
+    cu = torch.from_numpy(x["cu"]).to("cuda")
+    lv = _leaves(d, ("q", "k", "v", "g", "ers", "wrt", "h0"))
+    o, ht = gdr.chunk_gdn2(lv["q"], lv["k"], lv["v"], lv["g"], lv["ers"], lv["wrt"], lv["h0"],
+                           cu_seqlens=cu)
+    loss = (o.float() * d["dO"].float()).sum() + (ht * d["dht"]).sum()
+    loss.backward()
+    torch.cuda.synchronize()
+    got = {"o": _np(o), "ht": _np(ht), "dq": _np(lv["q"].grad), "dk": _np(lv["k"].grad),
+           "dv": _np(lv["v"].grad), "dg": _np(lv["g"].grad), "ders": _np(lv["ers"].grad),
+           "dwrt": _np(lv["wrt"].grad), "dh0": _np(lv["h0"].grad)}
+    compare_gdn2_packed(got, x)

@@ -128,3 +128,103 @@ def test_gdn2_without_states():
     _need_gpu()
     x = make_inputs(1, 192, 2, gate="gdn2", dtype="bf16", seed=35, gate_mean=3.0)
     _report("no states", compare_gdn2(run_gdn2(x, use_states=False), x, use_states=False))
+
+
+# ------------------------------------- packed batches and other widths (GDN2)
+
+def run_gdn2_packed(x, policy="recompute"):
+    """Packed GDN2 forward + backward; gradient outputs prefilled with a
+    sentinel that tokens outside every sequence must keep."""
+    import torch
+    import delta_rule_linear_gdr_amd as gdr
+    d = tl.device_inputs(x)
+    e = tl.to_dev(x["ers"], torch.bfloat16)
+    w = tl.to_dev(x["wrt"], torch.bfloat16)
+    cu = torch.from_numpy(x["cu"]).to("cuda")
+    o, ht, saved = gdr.gdr_fwd_gdn2(d["q"], d["k"], d["v"], d["g"], e, w, d["h0"], policy=policy,
+                                    cu_seqlens=cu)
+    out = {n: torch.full_like(t, tl.SENTINEL) for n, t in
+           (("dq", d["q"]), ("dk", d["k"]), ("dv", d["v"]), ("dg", d["g"]), ("derase", e),
+            ("dwrite", w))}
+    out["dh0"] = torch.empty_like(d["h0"])
+    gr = gdr.gdr_bwd_gdn2(d["q"], d["k"], d["v"], d["g"], e, w, d["h0"], d["dO"], d["dht"],
+                          saved=saved, policy=policy, out=out, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    res = {"o": o, "ht": ht, "dq": gr["dq"], "dk": gr["dk"], "dv": gr["dv"], "dg": gr["dg"],
+           "ders": gr["derase"], "dwrt": gr["dwrite"], "dh0": gr["dh0"]}
+    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items()}
+
+
+def compare_gdn2_packed(gpu, x):
+    """Each sequence is its own GDN2 problem with its own h0 and dht (an empty
+    one passes its state through); acceptance per tensor over the covered
+    tokens, and the sentinel kept past the last sequence."""
+    cu = x["cu"]
+    H = x["q"].shape[2]
+    got, ref = {}, {}
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        for h in range(H):
+            sl = lambda t: t[:, a:b, h:h + 1]       # noqa: E731
+            st = lambda t: t[i:i + 1, h:h + 1]      # noqa: E731
+            if a == b:
+                r = {"ht": st(x["h0"]), "dh0": st(x["dht"])}
+            else:
+                o, ht = oracle.gdn2_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["ers"]),
+                                        sl(x["wrt"]), st(x["h0"]))
+                r = oracle.gdn2_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["ers"]),
+                                    sl(x["wrt"]), st(x["h0"]), sl(x["dO"]), st(x["dht"]))
+                r.update(o=o, ht=ht)
+            for n, arr in r.items():
+                gg = gpu[n][i:i + 1, h:h + 1] if n in ("ht", "dh0") else gpu[n][:, a:b, h:h + 1]
+                got.setdefault(n, []).append(gg.ravel())
+                ref.setdefault(n, []).append(np.asarray(arr).ravel())
+    errs = {n: tl.check(n, np.concatenate(got[n]), np.concatenate(ref[n]), tol=TOL[n]) for n in got}
+    tail = int(cu[-1])
+    for n in ("dq", "dk", "dv", "dg", "ders", "dwrt"):
+        assert np.all(gpu[n][:, tail:] == tl.SENTINEL), f"{n}: tokens past the last sequence written"
+    return errs
+
+
+def _narrow(x, dk, dv, states=True):
+    """Cut seeded 128-wide inputs to dk keys and dv values (the shortened keys
+    are not renormalised: the recurrence takes any key)."""
+    for n in ("q", "k", "g", "ers"):
+        x[n] = np.ascontiguousarray(x[n][..., :dk])
+    for n in ("v", "dO", "wrt"):
+        x[n] = np.ascontiguousarray(x[n][..., :dv])
+    if states:
+        for n in ("h0", "dht"):
+            x[n] = np.ascontiguousarray(x[n][:, :, :dk, :dv])
+    return x
+
+
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_gdn2_packed_mixed_lengths(policy):
+    """Sequences of 100, 0, 129 and 64 tokens (ragged chunks, an empty
+    sequence, chunks that start mid-chunk) in a row of 320 tokens whose last
+    27 belong to no sequence."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    x = make_packed_inputs([100, 0, 129, 64], H=2, gate="gdn2", seed=36, gate_mean=3.0, cover=320)
+    _report(f"packed/{policy}", compare_gdn2_packed(run_gdn2_packed(x, policy), x))
+
+
+def test_gdn2_packed_narrow_widths():
+    """A packed batch at key width 80 and value width 112."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    x = _narrow(make_packed_inputs([70, 0, 130], H=2, gate="gdn2", seed=37, gate_mean=3.0), 80, 112)
+    _report("packed/80x112", compare_gdn2_packed(run_gdn2_packed(x), x))
+
+
+@pytest.mark.parametrize("dk,dv", [(80, 112), (96, 80), (128, 160), (64, 300)])
+def test_gdn2_other_widths(dk, dv):
+    """Key widths below 128 through zero-padded copies; value widths above
+    128 as 128-wide value blocks (the erase gate's gradient, a key-side
+    gradient, summed over the blocks; the write gate's taken per block)."""
+    _need_gpu()
+    x = make_inputs(2, 100, 2, DK=dk, DV=dv, gate="gdn2", dtype="bf16", seed=38, gate_mean=3.0,
+                    h0_std=0.1, dht_std=0.1)
+    for pol in ("recompute", "full_save"):
+        _report(f"{dk}x{dv}/{pol}", compare_gdn2(run_gdn2(x, pol), x, per_head=True))
