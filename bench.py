@@ -89,16 +89,17 @@ def kernel_work(gate: str) -> dict:
     beta = CH * 2
     inputs4 = 4 * T16
     return {
-        # recompute backward: reads q, k, v, dO, g, beta; writes -W, Kt^T, U, Kt,
-        # -W^T, X, Y, A^T, gn (and A, 8 KiB more, for the seven-product backward)
-        "prep": (inputs4 + g_bytes + beta + 6 * T16 + T32 + T8 + GN,
+        # recompute backward: reads q, k, v, dO, g, beta; writes -W, Kt, U, X,
+        # Y, A^T, gn (and A, 8 KiB more, for the seven-product backward)
+        "prep": (inputs4 + g_bytes + beta + 4 * T16 + T32 + T8 + GN,
                  1 * M + 1 * M + SOLVE + 2 * M + 1 * M + 2 * M),
-        # reads -W, Kt^T, U, gn; writes h, R.  R = U - W S; S' = gn S + Kt^T R
+        # reads -W, Kt (read transposed), U, gn; writes h, R.
+        # R = U - W S; S' = gn S + Kt^T R
         "scan_fwd": (3 * T16 + GN + T32 + T16, 4 * M),
-        # reads Kt, -W^T, X, Y, gn; writes dh, Rb
+        # reads Kt, -W (read transposed), X, Y, gn; writes dh, Rb
         "scan_bwd": (3 * T16 + T32 + GN + T32 + T16, 4 * M),
-        # both scans in one launch
-        "scan_pair": (3 * T16 + GN + T32 + T16 + 3 * T16 + T32 + GN + T32 + T16, 8 * M),
+        # both scans in one launch: the -W, Kt and gn they share count once
+        "scan_pair": (4 * T16 + T32 + GN + T32 + T16 + T32 + T16, 8 * M),
         # reads q, k, v, dO, g, beta, R, Rb, h, dh, A^T; writes dq, dk, dv, dg, dbeta
         "bwd_local": (inputs4 + g_bytes + beta + 2 * T16 + 2 * T32 + T8 + 3 * T16 + g_bytes + beta,
                       13 * M),

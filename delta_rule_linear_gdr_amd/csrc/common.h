@@ -270,6 +270,38 @@ __device__ __forceinline__ const bf16* frag_ptr(const bf16* base, int tile)
 }
 __device__ __forceinline__ bf16x8 ld_frag(const bf16* base, int tile) { return *(const bf16x8*)frag_ptr(base, tile); }
 __device__ __forceinline__ void st_frag(bf16* base, int tile, const bf16x8& v) { *(bf16x8*)frag_ptr(base, tile) = v; }
+// Where slot s (the 16 bytes of lane s) of a frag tile sits in an LDS copy
+// read by ld_frag_t64x128: s ^ 4 (s >> 4). An involution; a plain read of
+// the copy by lane l at this position stays conflict-free, and the
+// transposed read below hits 16 distinct bank pairs per 16 lanes instead of
+// 4 (unpermuted, the four key groups of one row lie 256 bytes apart).
+__host__ __device__ __forceinline__ int tr_slot(int s) { return s ^ ((s >> 2) & 12); }
+
+// Frag tile (mt, ks) of X^T read from X's own frag tiles in LDS, X being
+// M x K with K / 32 = 4 (M = 64 tokens, K = 128 keys; X^T is 128 x 64, so
+// mt < 8 and ks < 2). Uses gfx950's transposing LDS read (ds_read_b64_tr_b16):
+// within each group of 16 lanes, lane j receives as element e the element
+// j & 3 of what lane 4 e + (j >> 2) loaded. So lane (r, g) of the group g
+// loads, for the first half of its fragment, 8 bytes of token row
+// R = 32 ks + 4 g + (r >> 2) (the second half: R + 16) -- keys
+// 16 mt + 4 (r & 3) .. + 3, which X's frag tile (R / 16, mt / 2) holds
+// contiguously in slot half mt & 1 of lane (R & 15) + 16 (r & 3) -- and
+// receives X[32 ks + pik(g, j)][16 mt + r], slot j, as the frag format asks.
+// xs: the LDS base of X's 16 frag tiles (1 KiB each, tile (m, k) at m * 4 + k),
+// their slots placed by tr_slot.
+__device__ __forceinline__ bf16x8 ld_frag_t64x128(const uint8_t* xs, int mt, int ks)
+{
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int r = lane_id() & 15, g = lane_id() >> 4;
+    const int slot = tr_slot(4 * g + (r >> 2) + 16 * (r & 3));
+    const uint8_t* p = xs + (2 * ks * 4 + (mt >> 1)) * 1024 + slot * 16 + 8 * (mt & 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * 1024));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Lane pointer into ctile `tile`.
 __device__ __forceinline__ const bf16* ctile_ptr(const bf16* base, int tile)
 {

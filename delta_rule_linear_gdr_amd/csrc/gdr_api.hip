@@ -67,7 +67,7 @@ void carve_saved(Carver& c, Inter& it)
 {
     it.AT = c.take<bf16>(B_T64x64);
     it.Kt = c.take<bf16>(B_T64x128);
-    it.WnT = c.take<bf16>(B_T64x128);
+    it.Wn = c.take<bf16>(B_T64x128);
     it.gn = c.take<float>(B_GN);
     it.HmT = c.take<bf16>(B_T64x64);
     it.QgT = c.take<bf16>(B_T64x128);
@@ -87,13 +87,17 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
     // the gate-check words first, at the same place for every call and
     // policy, so that gdr_gate_status finds them from the descriptor alone
     it.flags = sc.take<uint32_t>(16);
-    if (full) carve_saved(sv, it);
-    if (ph == FWD || !full) {
-        // operands of the forward scan (and, in the forward, its output)
+    if (full) {
+        carve_saved(sv, it);
+    } else {
+        // the scan operands both directions read
         it.Wn = sc.take<bf16>(B_T64x128);
-        it.KtT = sc.take<bf16>(B_T64x128);
+        it.Kt = sc.take<bf16>(B_T64x128);
+        it.gn = sc.take<float>(B_GN);
+    }
+    if (ph == FWD || !full) {
+        // the rest of the forward scan's operands (and, in the forward, its output's)
         it.U = sc.take<bf16>(B_T64x128);
-        if (!full) it.gn = sc.take<float>(B_GN);
         if (ph == FWD) {
             it.Qg = sc.take<bf16>(B_T64x128);
             it.Hm = sc.take<bf16>(B_T64x64);
@@ -101,8 +105,6 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
     }
     if (ph == BWD) {
         if (!full) {
-            it.Kt = sc.take<bf16>(B_T64x128);
-            it.WnT = sc.take<bf16>(B_T64x128);
             it.AT = sc.take<bf16>(B_T64x64);
             it.Af = sc.take<bf16>(B_T64x64);
             it.h = sc.take<bf16>(B_T128x128);

@@ -36,17 +36,17 @@ constexpr int DVD = 128;  // value width
 // contiguous regions rather than one region per head.
 // Sizes per tile in parentheses. Unused pointers are null.
 struct Inter {
-    // forward scan operands (prep)
+    // scan operands (prep), one orientation each: the forward scan reads
+    // -W and Kt^T, the reverse scan Kt and -W^T, the transposes by LDS
+    // transpose reads of the same tiles
     bf16* Wn;    // -W          frag  M=64 tok,  K=128 key   (16 KiB)
-    bf16* KtT;   // Kt^T        frag  M=128 key, K=64 tok    (16 KiB)
-    bf16* U;     // U           ctile M=64 tok,  N=128 val   (16 KiB)
+    bf16* Kt;    // Kt          frag  M=64 tok,  K=128 key   (16 KiB)
     float* gn;   // exp(G_n)    128 fp32 per key             (512 B)
+    bf16* U;     // U           ctile M=64 tok,  N=128 val   (16 KiB, forward scan)
     // forward output operands (prep)
     bf16* Qg;    // gam * Q     frag  M=64 tok,  K=128 key   (16 KiB)
     bf16* Hm;    // Hm          frag  M=64 tok i, K=64 tok j (8 KiB)
     // reverse scan operands (prep, xy)
-    bf16* Kt;    // Kt          frag  M=64 tok,  K=128 key   (16 KiB)
-    bf16* WnT;   // -W^T        frag  M=128 key, K=64 tok    (16 KiB)
     bf16* X;     // Hm^T dO     ctile M=64 tok,  N=128 val   (16 KiB)
     bf16* Y;     // Qg^T dO     ctile M=128 key, N=128 val   (32 KiB)
     bf16* HmT;   // Hm^T        frag  M=64 tok j, K=64 tok i (8 KiB)
@@ -236,9 +236,9 @@ struct Grads {
 
 // What prep writes (bit set of PREP_*).
 enum {
-    PREP_FWDSCAN = 1,  // Wn, KtT, U, gn
+    PREP_FWDSCAN = 1,  // Wn, Kt, gn and U
     PREP_OUT = 2,      // Qg, Hm
-    PREP_BWDSCAN = 4,  // Kt, WnT (and gn)
+    PREP_BWDSCAN = 4,  // Wn, Kt, gn
     PREP_XY = 8,       // X, Y from dO
     PREP_SAVEXY = 16,  // HmT, QgT (for launch_xy)
     PREP_A = 32,       // AT (and Af when PREP_AF is set)

@@ -25,10 +25,11 @@
 // GDN2 (paper Table 1: independent erase and write gates): E = ers o gam o K
 // and Z = wrt o V, the erase gate per (token, key) and the write gate per
 // (token, value) taking beta's place; both are staged in LDS as fp32.
-// Outputs (bit set `what`, formats in kernels.h): the forward-scan operands
-// -W, Kt^T, U, gn; the output operands Qg, Hm; the reverse-scan operands
-// Kt, -W^T and, given dO, X = Hm^T dO and Y = Qg^T dO; Hm^T and Qg^T for a
-// later X/Y pass; and A.
+// Outputs (bit set `what`, formats in kernels.h): the scan operands -W, Kt
+// and gn, each once in one orientation (both scan directions read them, the
+// transposes through LDS transpose reads), U for the forward scan; the
+// output operands Qg, Hm; given dO, X = Hm^T dO and Y = Qg^T dO; Hm^T and
+// Qg^T for a later X/Y pass; and A.
 #include "common.h"
 #include "kernels.h"
 
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 
     const bool fwdscan = what & PREP_FWDSCAN, out = what & PREP_OUT, bwdscan = what & PREP_BWDSCAN;
     const bool xy = what & PREP_XY, savexy = what & PREP_SAVEXY, wantA = what & PREP_A;
+    const bool walk = fwdscan || bwdscan;  // -W, Kt, gn
 
     // Vector gate: G per (token, key), rows padded to 132 floats so that the
     // 16 rows a fragment read spans land on distinct LDS banks (a 128-float
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
     lds_barrier();
 
     auto Gat = [&](int i, int f) -> float { return VEC ? sG[i * GST + f] : sG[i]; };
-    if ((fwdscan || bwdscan) && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
+    if (walk && tid < DKD) it.gn[t * DKD + tid] = __expf(Gat(CH - 1, tid));
 
     // plain fragment of row block i0 .. i0+15, keys 32 ks + 8 g .. + 7: the
     // unconverted read, then the bf16 operand with an optional per-(row, key)
@@ -481,26 +483,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
                 const int f = 32 * w + 16 * n + r;
-                const float gnf = Gat(CH - 1, f);
-                f32x4 kt;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int i = 16 * mt + 4 * g + e;
-                    const float G = Gat(i, f);
-                    kt[e] = KC[mt][n][e] * __expf(gnf - G);
-                    EC[mt][n][e] = KC[mt][n][e] * __expf(G) * (GD2 ? sEW[i * GST + f] : sBeta[i]);
+                    EC[mt][n][e] = KC[mt][n][e] * __expf(Gat(i, f)) * (GD2 ? sEW[i * GST + f] : sBeta[i]);
                 }
-                KC[mt][n] = kt;
             }
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                ET[n][ks] = pack_pi(EC[2 * ks][n], EC[2 * ks + 1][n]);
-                if (fwdscan)
-                    st_frag(it.KtT + t * (CH * DKD), (2 * w + n) * 2 + ks,
-                            pack_pi(KC[2 * ks][n], KC[2 * ks + 1][n]));
-            }
+            for (int ks = 0; ks < 2; ++ks) ET[n][ks] = pack_pi(EC[2 * ks][n], EC[2 * ks + 1][n]);
         // V * I scaled by beta: Z^T frags of value slab w
         {
             f32x4 VC[4][2];
@@ -561,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
         }
     }
     // Kt and Qg frags (M = tok, K = key) straight from the rows
-    if (bwdscan || out) {
+    if (walk || out) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int id = tid + 256 * u;
@@ -575,13 +567,13 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 kx[e] *= __expf(Gat(CH - 1, f0 + e) - G);
                 qx[e] *= __expf(G);
             }
-            if (bwdscan) st_row8_frag(it.Kt + t * (CH * DKD), i, f0, kx);
+            if (walk) st_row8_frag(it.Kt + t * (CH * DKD), i, f0, kx);
             if (out) st_row8_frag(it.Qg + t * (CH * DKD), i, f0, qx);
         }
     }
     lds_barrier();  // sQgT complete
 
-    // ---- 5. W = A E, W^T = E^T A^T, U = A Z; A ----
+    // ---- 5. W = A E, U = A Z; A ----
     {
         // A frag (M = tok i, K = tok j): rows 16 mt + r, cols 32 ks + pik(g, .)
         auto afrag = [&](int mt, int ks) -> bf16x8 {
@@ -596,25 +588,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 if (ks == 0 || mt >= 2) AF[mt][ks] = afrag(mt, ks);
-        if (bwdscan) {
-            // W (tok x key) -> -W^T frags (M = key, K = tok)
-            f32x4 WC[4][2];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    f32x4 acc = mfma(AF[mt][0], ET[n][0], zero4());
-                    if (mt >= 2) acc = mfma(AF[mt][1], ET[n][1], acc);
-                    WC[mt][n] = acc;
-                }
-#pragma unroll
-            for (int n = 0; n < 2; ++n)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    st_frag(it.WnT + t * (CH * DKD), (2 * w + n) * 2 + ks,
-                            pack_pi(WC[2 * ks][n], WC[2 * ks + 1][n], -1.f));
-        }
-        if (fwdscan) {
+        if (walk) {
             // W^T (key x tok) -> -W frags (M = tok, K = key), key slab w
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
@@ -626,6 +600,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
                 }
                 st_frag(it.Wn + t * (CH * DKD), mt * 4 + w, pack_pi(acc0, acc1, -1.f));
             }
+        }
+        if (fwdscan) {
             // U = A Z (tok x value), value slab w -> ctiles
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)

@@ -143,8 +143,10 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
     constexpr int NPAD = (NB + 3) / 4 * 4;
     constexpr int E1 = 32 + 2 * NV, E2 = E1 + 4 * NV;  // ends of the C1 and C2 blocks
     const int l = lane_id();
+    // A2 is the transpose of the other direction's A1: its frag tiles are
+    // copied as they are and read transposed (ld_frag_t64x128)
     const bf16* A1 = BWD ? it.Kt : it.Wn;
-    const bf16* A2 = BWD ? it.WnT : it.KtT;
+    const bf16* A2 = BWD ? it.Wn : it.Kt;
     const bf16* C1 = BWD ? it.X : it.U;
     // The slices of a head read the same A1 / A2 tiles; each starts at a
     // different tile (rotation by 16 / (8 / NV) per slice) so that they do
@@ -159,8 +161,9 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
             src = A1 + t * (CH * DKD) + bb * 512 + l * 8;
             dst = L::A1 + bb * 1024;
         } else if (b < 32) {
+            // slots permuted by tr_slot (lane l lands at position l)
             const int bb = (b - 16 + rot) & 15;
-            src = A2 + t * (CH * DKD) + bb * 512 + l * 8;
+            src = A2 + t * (CH * DKD) + bb * 512 + tr_slot(l) * 8;
             dst = L::A2 + bb * 1024;
         } else if (b < E1) {
             src = C1 + t * (CH * DVD) + vs * NV * 1024 + (b - 32) * 512 + l * 8;
@@ -372,8 +375,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                a2[m][ks] = *(const bf16x8*)(slot + L::A2 + ((2 * w + m) * 2 + ks) * 1024 + l * 16);
+            for (int ks = 0; ks < 2; ++ks) a2[m][ks] = ld_frag_t64x128(slot + L::A2, 2 * w + m, ks);
         // S <- gn S (+ C2) + A2 Z
 #pragma unroll
         for (int m = 0; m < 2; ++m) {

@@ -119,7 +119,7 @@ int gdr_workspace_size(const gdr_desc* d, int policy, size_t* saved_bytes, size_
 
 /* Forward. o: output; ht: final state (NULL: not written); h0 NULL: zero.
  * Under GDR_FULL_SAVE, saved receives the chunk quantities the backward
- * reuses (per chunk and head: A^T, Kt, -W^T, exp(G_n), Hm^T, Qg^T, and the
+ * reuses (per chunk and head: A^T, Kt, -W, exp(G_n), Hm^T, Qg^T, and the
  * state h and correction R at the chunk; 115,200 bytes at the supported
  * widths); under GDR_RECOMPUTE saved may be NULL. */
 int gdr_fwd(const gdr_desc* d, int policy, const void* q, const void* k, const void* v,
@@ -190,8 +190,8 @@ int gdr_bwd_gdn2_varlen(const gdr_desc* d, int policy, const int64_t* cu_seqlens
  * errors as gdr_bwd for a regular batch; the stream must belong to the
  * current device (else GDR_ERR_INVALID). A problem whose gdr_bwd scratch
  * (gdr_workspace_size) exceeds the array returns GDR_ERR_UNSUPPORTED before
- * anything is launched: about 270 (chunk, head) pairs under GDR_RECOMPUTE,
- * e.g. (B, T, H) = (1, 2048, 8), about 630 under GDR_FULL_SAVE. Every call on
+ * anything is launched: about 310 (chunk, head) pairs under GDR_RECOMPUTE,
+ * e.g. (B, T, H) = (1, 2048, 9), about 630 under GDR_FULL_SAVE. Every call on
  * one device shares that device's array and leaves its contents behind (the
  * kernels write every part they read before reading it), so calls that
  * overlap in time on one device -- on two streams, or from two threads --

@@ -44,20 +44,22 @@ def test_workspace_sizes():
     T64x128, T128x128, T64x64, GN = 16384, 32768, 8192, 512
     rc, sv, sc = _ws(_desc(T=8192, H=16), 0)
     assert rc == 0 and sv == 0
-    # recompute: the backward holds the forward-scan operands (-W, Kt^T, U, gn),
-    # the reverse-scan operands (Kt, -W^T, X, Y), A^T and A, and the per-chunk
-    # h, R, dh, Rb of every (chunk, head)
-    # (plus the 16 bytes of gate-check words of every (chunk, head))
-    per = 3 * T64x128 + GN + 2 * T64x128 + 2 * T64x64 + T128x128 + T64x128 \
+    # recompute: the backward holds the scan operands both directions read
+    # (-W, Kt, gn: one orientation each), U for the forward scan, X and Y for
+    # the reverse one, A^T and A, and the per-chunk h, R, dh, Rb of every
+    # (chunk, head) (plus the 16 bytes of gate-check words of every (chunk, head))
+    per = 2 * T64x128 + GN + T64x128 + 2 * T64x64 + T128x128 + T64x128 \
         + T64x128 + T128x128 + T128x128 + T64x128 + 16
+    assert per == 213520
     assert sc == 2048 * per
     rc, sv, sc = _ws(_desc(T=8192, H=16), 1)
     assert rc == 0
-    # full save keeps A^T, Kt, -W^T, gn, Hm^T, Qg^T, h, R (115,200 B per chunk-head);
-    # the backward's scratch adds A for the seven-product producer
+    # full save keeps A^T, Kt, -W, gn, Hm^T, Qg^T, h, R (115,200 B per chunk-head),
+    # which the forward's own scan reads too; the forward's scratch holds U,
+    # Qg, Hm, the backward's X, Y, dh, Rb and A for the seven-product producer
     assert sv == 2048 * (T64x64 + 2 * T64x128 + GN + T64x64 + T64x128 + T128x128 + T64x128)
     assert sv == 2048 * 115200
-    assert sc == 2048 * (16 + max(4 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128 + T64x64))
+    assert sc == 2048 * (16 + max(2 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128 + T64x64))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -223,8 +225,8 @@ def test_noalloc_rejects_problems_past_its_array():
     m = re.search(r"#define GDR_NOALLOC_SCRATCH_MAX \(\(size_t\)(\d+) << (\d+)\)", src)
     cap = int(m.group(1)) << int(m.group(2))
     lib = gdr.load()
-    fits = _desc(T=2048, H=8)
-    too_big = _desc(T=2048, H=9)
+    fits = _desc(T=2048, H=9)
+    too_big = _desc(T=2048, H=10)
     assert _ws(fits)[2] <= cap < _ws(too_big)[2]
     rc = lib.gdr_bwd_noalloc(ctypes.byref(too_big), 0, *([None] * 15), None)
     assert rc == -2 and b"fixed" in lib.gdr_last_error()

@@ -45,13 +45,14 @@ def kernel_tensors(gate):
     inputs = [tok] * 4 + [g, beta]     # q, k, v, dO, g, beta
     grads = [tok] * 3 + [g, beta]      # dq, dk, dv, dg, dbeta
     return {
-        # writes -W, K~^T, U, K~, -W^T, X (64 x 128 each), Y (128 x 128), A^T, gn
-        "prep": inputs + [tok] * 6 + [state, tri, gn],
-        # forward walk reads -W, K~^T, U, gn and writes h, R
+        # writes -W, K~, U, X (64 x 128 each), Y (128 x 128), A^T, gn
+        "prep": inputs + [tok] * 4 + [state, tri, gn],
+        # forward walk reads -W, K~ (as K~^T), U, gn and writes h, R
         "scan_fwd": [tok, tok, tok, gn, state, tok],
-        # reverse walk reads K~, -W^T, X, Y, gn and writes dh, Rbar
+        # reverse walk reads K~, -W (as -W^T), X, Y, gn and writes dh, Rbar
         "scan_bwd": [tok, tok, tok, state, gn, state, tok],
-        "scan_pair": [tok, tok, tok, gn, state, tok] + [tok, tok, tok, state, gn, state, tok],
+        # both walks in one launch read -W, K~ and gn, counted once
+        "scan_pair": [tok, tok, gn] + [tok, state, tok] + [tok, state, state, tok],
         # reads q, k, v, dO, g, beta, R, Rbar, h, dh, A^T; writes the gradients
         "bwd_local": inputs + [tok, tok, state, state, tri] + grads,
         "bwd_local_wy7": inputs + [tok, tok, state, state, tri, tri] + grads,
