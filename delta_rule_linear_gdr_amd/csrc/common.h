@@ -386,6 +386,20 @@ __device__ __forceinline__ void lds_barrier()
     asm volatile("s_barrier" ::: "memory");
 }
 
+// Orders a wave's LDS writes before its later LDS reads of data that other
+// lanes of the same wave wrote. The LDS serves one wave's accesses in issue
+// order, so only the compiler's order has to be held (the memory clobber);
+// the wait also completes the writes before any later read is issued.
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// fp32 product C += A B with A 16 x 4 and B 4 x 16 (v_mfma_f32_16x16x4_f32):
+// lane (r, g) passes A[r][g] and B[g][r]; accumulator element i of lane
+// (r, g) is C[4 g + i][r], as for the bf16 products.
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
 // reads src and its bytes land at lds_base + 16 L; lds_base must be the
 // same for every lane. Completion is counted by the vector-memory counter.

@@ -433,36 +433,41 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
         }
         lds_barrier();
-        const int jb = w, rr = (tid >> 2) & 15, c4 = (tid & 3) * 4;
+        // Block rows: wave jb < bi forms A[bi][jb] = -A[bi][bi] T with
+        // T = sum_{lb = jb}^{bi - 1} L[bi][lb] A[lb][jb], 16 x 16 blocks, on the
+        // fp32 MFMA (four K = 4 steps per block product). T passes through the
+        // wave's own block of sT (accumulator rows in, operand columns out).
+        // A[bi][jb] replaces L[bi][jb], which the waves jb' < jb of the same
+        // block row still read: it is written after the block row's barrier.
+        // Every other block a wave reads is a diagonal block or a block of its
+        // own column from an earlier block row, which it wrote itself.
+        const int jb = w;
+        float* const tb = sT + (jb < 3 ? jb : 0) * 16 * TP;  // waves 0..2 use theirs
         for (int bi = 1; bi < 4; ++bi) {
+            f32x4 d = zero4();
             if (jb < bi) {
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-                for (int lb = jb; lb < bi; ++lb) {
+                f32x4 acc = zero4();
+                for (int lb = jb; lb < bi; ++lb)
 #pragma unroll
-                    for (int m = 0; m < 16; ++m) {
-                        const float lv = sL[(16 * bi + rr) * LP + 16 * lb + m];
-                        const float4 a4 = *(const float4*)&sA[(16 * lb + m) * LP + 16 * jb + c4];
-                        acc.x += lv * a4.x; acc.y += lv * a4.y;
-                        acc.z += lv * a4.z; acc.w += lv * a4.w;
-                    }
-                }
-                *(float4*)&sT[(jb * 16 + rr) * TP + c4] = acc;
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        acc = mfma4(sL[(16 * bi + r) * LP + 16 * lb + 4 * q4 + g],
+                                    sA[(16 * lb + 4 * q4 + g) * LP + 16 * jb + r], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) tb[(4 * g + i) * TP + r] = acc[i];
+                wave_lds_sync();
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+                    d = mfma4(sA[(16 * bi + r) * LP + 16 * bi + 4 * q4 + g], tb[(4 * q4 + g) * TP + r], d);
             }
-            lds_barrier();
+            lds_barrier();  // block row bi's L blocks have been read
             if (jb < bi) {
-                float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const float dv = sA[(16 * bi + rr) * LP + 16 * bi + m];
-                    const float4 t4 = *(const float4*)&sT[(jb * 16 + m) * TP + c4];
-                    acc.x += dv * t4.x; acc.y += dv * t4.y;
-                    acc.z += dv * t4.z; acc.w += dv * t4.w;
-                }
-                *(float4*)&sA[(16 * bi + rr) * LP + 16 * jb + c4] =
-                    make_float4(-acc.x, -acc.y, -acc.z, -acc.w);
+                for (int i = 0; i < 4; ++i) sA[(16 * bi + 4 * g + i) * LP + 16 * jb + r] = -d[i];
+                wave_lds_sync();
             }
-            lds_barrier();
         }
+        // (the last block row's writes reach the other waves through the
+        // barrier that closes phase 4, which touches none of sL, sA, sT)
     }
 
     // ---- 4. transposed operands through X * I (wave w: key / value slab w) ----
