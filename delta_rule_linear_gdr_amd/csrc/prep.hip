@@ -420,15 +420,18 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(Shape s, Inputs in, Inter 
             sA[(16 * bi + rr) * LP + 16 * bj + cc] = 0.f;
         }
         if (l < 16) {
+            // column l of the inverse of diagonal block w by forward
+            // substitution, right-looking: once x[m] is final, column m of
+            // the block is applied to every later x[i]. The dependent chain
+            // is one FMA per row; the 15 - m updates of a step are independent.
             const int base = 16 * w;
             float x[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == l) ? 1.f : 0.f;
+            for (int i = 0; i < 16; ++i) x[i] = (i == l) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc -= sL[(base + i) * LP + base + m] * x[m];
-                x[i] = acc;
-            }
+            for (int m = 0; m < 15; ++m)
+#pragma unroll
+                for (int i = m + 1; i < 16; ++i) x[i] -= sL[(base + i) * LP + base + m] * x[m];
 #pragma unroll
             for (int i = 0; i < 16; ++i) sA[(base + i) * LP + base + l] = x[i];
         }
