@@ -372,6 +372,20 @@ __device__ __forceinline__ void store4(float* p, const float (&x)[4])
 {
     *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
 }
+// The same as a streaming (non-temporal) store, for results that no later
+// access of the same launch reads: they then leave the L2 to the operand
+// tiles the launch's workgroups share.
+__device__ __forceinline__ void store4_stream(bf16* p, const float (&x)[4])
+{
+    bf16x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (bf16)x[e];
+    __builtin_nontemporal_store(v, (bf16x4*)p);
+}
+__device__ __forceinline__ void store4_stream(float* p, const float (&x)[4])
+{
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4*)p);
+}
 
 // Workgroup barrier for an LDS exchange only. __syncthreads() also orders
 // global memory, so it waits for every outstanding global load and store of

@@ -272,7 +272,7 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
             for (int u = 0; u < NV; ++u) {
                 const f32x4 x = mfma(pack_pi(acc[u], zero4()), Ip0, zero4());
                 float xv[4] = {x[0], x[1], x[2], x[3]};
-                if (row < seq_rows(sq, p)) store4(orow + 16 * (NV * vs + u) + 4 * g, xv);
+                if (row < seq_rows(sq, p)) store4_stream(orow + 16 * (NV * vs + u) + 4 * g, xv);
             }
             // step p + 1's ring blocks and fragments have landed: younger than
             // them are this step's fragment reads, ring blocks and stores (the
@@ -331,13 +331,18 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         const int c = BWD ? NT - 1 - p : p;
         const int64_t t = seq_tile(s, sq, c);
         const uint8_t* slot = ring + (p % L::NSLOT) * L::SLOT;
-        // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile NV vs + u)
+        // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile NV vs + u).
+        // The stored states and corrections (like the forward output rows) are
+        // streaming stores: only the local kernel reads them, so in the L2
+        // they would only evict the A1 / A2 tiles the slices of a head share
+        // (128 -> 117 us for the recompute pair at (1,8192,16)).
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             if constexpr (STORE) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
-                    *(bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m) = pack4(S[u][m]);
+                    __builtin_nontemporal_store(
+                        pack4(S[u][m]), (bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m));
             }
             sS[u][w][l] = pack_pi(S[u][0], S[u][1]);
         }
@@ -365,7 +370,8 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         if constexpr (STORE) {
 #pragma unroll
             for (int u = 0; u < NV; ++u)
-                *(bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w) = z4[u];
+                __builtin_nontemporal_store(z4[u],
+                                            (bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w));
         }
         bf16x8 zf[NV][2], a2[2][2];
 #pragma unroll
