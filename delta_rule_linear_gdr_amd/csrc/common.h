@@ -414,6 +414,9 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Cache-policy operand of the load builtins for a streaming ("nt") access.
+constexpr int CPOL_NT = 2;
+
 // Direct-to-LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane L
 // reads src and its bytes land at lds_base + 16 L; lds_base must be the
 // same for every lane. Completion is counted by the vector-memory counter.

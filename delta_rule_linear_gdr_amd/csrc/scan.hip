@@ -179,7 +179,15 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
                                              4, 0, 0);
             continue;
         }
-        lds_dma16(src, slot + dst);
+        if (b < 32) {
+            lds_dma16(src, slot + dst);
+        } else {
+            // this slice's own C1 / C2 blocks, read by no other workgroup: a
+            // streaming load, which leaves the L2 to the shared A1 / A2 tiles
+            // (the recompute pair at (1,8192,16): 115 -> 109 us)
+            __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(slot + dst), 16, 0,
+                                             CPOL_NT);
+        }
     }
 }
 
