@@ -47,12 +47,15 @@ SOLVE = CH ** 3 // 3                          # inverse of a 64 x 64 unit lower-
 # reads q, k, v, dO, g, beta and writes dq, dk, dv, dg, dbeta; the full-save
 # forward writes, and its backward reads, the 1152-byte saved area (A, W,
 # per-chunk state, R). The gate is 4 bytes (scalar) or 512 (vector) per
-# token-head, its gradient the same.
+# token-head, its gradient the same. GDN2 takes a per-key erase gate and a
+# per-value write gate (bf16, 256 bytes each) in place of beta, and returns
+# their gradients.
 PATH_BYTES_PER_TOKEN_HEAD = {
     ("scalar", "fwd_R"): 1030, ("scalar", "fwd_A"): 2182,
     ("scalar", "bwd_R"): 1804, ("scalar", "bwd_A"): 2956,
     ("vector", "fwd_R"): 1538, ("vector", "fwd_A"): 2690,
     ("vector", "bwd_R"): 2820, ("vector", "bwd_A"): 3972,
+    ("gdn2", "fwd_R"): 2048, ("gdn2", "bwd_R"): 3840,
 }
 # 128 x 128 fp32 state tensors a call touches per head: h0 and ht (forward);
 # h0 and dh0 (recompute backward, dht absent); dh0 (full-save backward)
@@ -86,7 +89,9 @@ def kernel_work(gate: str) -> dict:
     as tabulated in the design notes: every operand read once and every result
     written once at its stored type; FLOPs of the method's dense products."""
     g_bytes = CH * 4 if gate == "scalar" else CH * 128 * 4
-    beta = CH * 2
+    # beta, or GDN2's erase (per key) and write (per value) gates; the same
+    # again for the gradient
+    beta = 2 * T16 if gate == "gdn2" else CH * 2
     inputs4 = 4 * T16
     return {
         # recompute backward: reads q, k, v, dO, g, beta; writes -W, Kt, U, X,
@@ -122,7 +127,8 @@ def parse():
                     help="calibration copy + a few headline steps, for rocprofv3 counter runs")
     ap.add_argument("--with-wy7", action="store_true",
                     help="profile pass: after the ReWY steps, as many seven-product backward steps")
-    ap.add_argument("--workload", default="gdn_1x8192x16", choices=["gdn_1x8192x16", "kda_1x8192x16"],
+    ap.add_argument("--workload", default="gdn_1x8192x16",
+                    choices=["gdn_1x8192x16", "kda_1x8192x16", "gdn2_1x8192x16"],
                     help="the backward the profile pass steps (the timed bench is always GDN)")
     return ap.parse_args()
 
@@ -322,6 +328,19 @@ def main():
         return {k: v[1] / v[0] for k, v in st.items()}  # avg ms per launch
 
     run = make_runner(d, gdr.gdr_bwd, "recompute")
+    if wl.gate == "gdn2":
+        # (profile pass only) the GDN2 backward on the same tensors plus both gates
+        ers2 = torch.from_numpy(x["ers"]).to(dev, torch.bfloat16)
+        wrt2 = torch.from_numpy(x["wrt"]).to(dev, torch.bfloat16)
+        _, sc2 = gdr.workspace_size(B, T, H, "gdn2", "bf16", "recompute")
+        scr2 = torch.empty(sc2, dtype=torch.uint8, device=dev)
+        out2 = dict(dq=torch.empty_like(d["q"]), dk=torch.empty_like(d["k"]), dv=torch.empty_like(d["v"]),
+                    dg=torch.empty_like(d["g"]), derase=torch.empty_like(ers2), dwrite=torch.empty_like(wrt2),
+                    dh0=torch.empty((B, H, 128, 128), dtype=torch.float32, device=dev))
+
+        def run():
+            gdr.gdr_bwd_gdn2(d["q"], d["k"], d["v"], d["g"], ers2, wrt2, d["h0"], d["dO"], None,
+                             scratch=scr2, out=out2)
 
     if args.profile_pass:
         # calibration: an elementwise kernel that reads and writes exactly
@@ -499,7 +518,7 @@ def main():
         dg_ = to_dev(xg)
         ers = torch.from_numpy(xg["ers"]).to(dev, torch.bfloat16)
         wrt = torch.from_numpy(xg["wrt"]).to(dev, torch.bfloat16)
-        _, scG = gdr.workspace_size(B, T, H, "vector", "bf16", "recompute")
+        _, scG = gdr.workspace_size(B, T, H, "gdn2", "bf16", "recompute")
         scrG = torch.empty(scG, dtype=torch.uint8, device=dev)
         outG = dict(dq=torch.empty_like(dg_["q"]), dk=torch.empty_like(dg_["k"]),
                     dv=torch.empty_like(dg_["v"]), dg=torch.empty_like(dg_["g"]),
@@ -509,6 +528,10 @@ def main():
         def runG():
             gdr.gdr_bwd_gdn2(dg_["q"], dg_["k"], dg_["v"], dg_["g"], ers, wrt, dg_["h0"], dg_["dO"],
                              None, scratch=scrG, out=outG)
+        msG = time_steps(runG, args.steps, args.warmup)
+        detail["gdn2_bwd_R_ms"] = round(msG, 4)
+        detail["gdn2_bwd_R_tokens_per_s"] = round(B * T / (msG * 1e-3), 1)
+        detail["gdn2_bwd_R_roofline"] = path_figures("gdn2", "bwd_R", B, T, H, msG)
         detail["gdn2_bwd_R_graph_median60_ms"] = round(graph_median_ms(runG), 4)
         detail["gdn2_stage_ms"] = {k: round(v, 4) for k, v in profiled(runG, args.steps).items()}
         del dg_, xg, scrG, outG, ers, wrt

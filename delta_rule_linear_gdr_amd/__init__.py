@@ -147,10 +147,10 @@ def make_desc(B, T, H, gate, dtype, DK=128, DV=128, C=64) -> Desc:
 
 def workspace_size(B, T, H, gate="scalar", dtype="bf16", policy="recompute", n_seq=None,
                    DK=128, DV=128):
-    """(saved_bytes, scratch_bytes) for a problem; gate "scalar", "vector" or
-    "none" (DeltaNet); n_seq: sequences of a packed variable-length batch
-    (B = 1), None for a regular batch."""
-    kind = {"scalar": GATE_SCALAR, "vector": GATE_VECTOR, "none": GATE_NONE}[gate]
+    """(saved_bytes, scratch_bytes) for a problem; gate "scalar", "vector",
+    "none" (DeltaNet) or "gdn2"; n_seq: sequences of a packed variable-length
+    batch (B = 1), None for a regular batch."""
+    kind = {"scalar": GATE_SCALAR, "vector": GATE_VECTOR, "none": GATE_NONE, "gdn2": GATE_GDN2}[gate]
     d = make_desc(B, T, H, kind, DT_F32 if dtype == "fp32" else DT_BF16, DK=DK, DV=DV)
     return _sizes(d, _policy(policy), n_seq)
 

@@ -59,7 +59,7 @@ def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
 class Workload:
     """A named synthetic workload (shape + distributions)."""
     name: str
-    gate: str          # "scalar" (GDN) or "vector" (KDA)
+    gate: str          # "scalar" (GDN), "vector" (KDA) or "gdn2"
     B: int
     T: int
     H: int
@@ -77,7 +77,8 @@ class Workload:
 
 
 # The five workloads of the build: GDN at (1,512,4) fp32, (1,2048,16) and
-# (1,8192,16) bf16; KDA at (2,2048,16) and (1,8192,16) bf16 with h0 ~ 0.1 N(0,1).
+# (1,8192,16) bf16; KDA at (2,2048,16) and (1,8192,16) bf16 with h0 ~ 0.1 N(0,1);
+# and GDN2 at the headline shape, drawn like KDA's with both gates.
 # The six (B, T, H) shapes of the pages' evaluation (Eq. 4 of the paper page,
 # listed in the onedev.kr summary's "How to use"), C = 64, d_k = d_v = 128.
 SHAPES6 = ((1, 512, 4), (1, 2048, 4), (1, 8192, 4), (1, 2048, 16), (2, 2048, 16), (1, 8192, 16))
@@ -89,6 +90,8 @@ WORKLOADS = {
     "kda_2x2048x16": Workload("kda_2x2048x16", "vector", 2, 2048, 16, gate_mean=3.0),
     "kda_1x8192x16": Workload("kda_1x8192x16", "vector", 1, 8192, 16, gate_mean=3.0,
                               h0_std=0.1),
+    "gdn2_1x8192x16": Workload("gdn2_1x8192x16", "gdn2", 1, 8192, 16, gate_mean=3.0,
+                               h0_std=0.1),
 }
 
 

@@ -40,10 +40,16 @@ def kernel_tensors(gate):
     state = nbytes(D, D, BF16)         # a stored 128 x 128 state (h_c, dh_c)
     tri = nbytes(CH, CH, BF16)         # A, A^T, H^T
     gn = nbytes(D, F32)                # exp of the chunk's total log decay, per key channel
-    beta = nbytes(CH, BF16)
     g = gate_bytes(gate)
-    inputs = [tok] * 4 + [g, beta]     # q, k, v, dO, g, beta
-    grads = [tok] * 3 + [g, beta]      # dq, dk, dv, dg, dbeta
+    if gate == "gdn2":
+        # the erase (64 x 128 keys) and write (64 x 128 values) gates in bf16
+        # take beta's place, and their gradients dbeta's
+        inputs = [tok] * 4 + [g, tok, tok]   # q, k, v, dO, g, erase, write
+        grads = [tok] * 3 + [g, tok, tok]    # dq, dk, dv, dg, derase, dwrite
+    else:
+        beta = nbytes(CH, BF16)
+        inputs = [tok] * 4 + [g, beta]     # q, k, v, dO, g, beta
+        grads = [tok] * 3 + [g, beta]      # dq, dk, dv, dg, dbeta
     return {
         # writes -W, K~, U, X (64 x 128 each), Y (128 x 128), A^T, gn
         "prep": inputs + [tok] * 4 + [state, tri, gn],
@@ -61,7 +67,7 @@ def kernel_tensors(gate):
     }
 
 
-@pytest.mark.parametrize("gate", ["scalar", "vector"])
+@pytest.mark.parametrize("gate", ["scalar", "vector", "gdn2"])
 def test_kernel_bytes_match_the_tensor_lists(gate):
     work = bench.kernel_work(gate)
     for name, tensors in kernel_tensors(gate).items():
@@ -90,6 +96,17 @@ def test_whole_path_bytes_per_token_head(gate):
     assert t[(gate, "fwd_A")] == fwd + saved
     assert t[(gate, "bwd_R")] == bwd
     assert t[(gate, "bwd_A")] == bwd + saved
+
+
+def test_gdn2_whole_path_bytes_per_token_head():
+    # GDN2: a per-key fp32 log decay, and per-key erase and per-value write
+    # gates in bf16 in place of beta (their gradients likewise)
+    row = D * BF16
+    g = D * 4
+    fwd = 3 * row + g + 2 * row + row                 # q, k, v, g, erase, write -> o
+    bwd = 4 * row + g + 2 * row + 3 * row + g + 2 * row
+    t = bench.PATH_BYTES_PER_TOKEN_HEAD
+    assert (t[("gdn2", "fwd_R")], t[("gdn2", "bwd_R")]) == (fwd, bwd) == (2048, 3840)
 
 
 def test_path_flops_are_the_launched_kernels_flops():
