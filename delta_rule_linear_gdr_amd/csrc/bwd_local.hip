@@ -219,6 +219,29 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 
     // ---- every global read of this chunk, issued before the first is used
     //      (one memory round trip instead of one per phase) ----
+    // Persistent form (bf16): the chunk's v, dO, k, q rows (4 x 64 x 128)
+    // are first copied into the front 64 KiB of the fragment buffers, which
+    // phase 1 is the first to write, with coalesced direct-to-LDS loads
+    // (1 KiB = four whole rows per instruction). Each wave then reads its
+    // 16-column slices from there.
+    // Read from global memory, a slice takes 8 bytes of 16 rows per
+    // instruction: 16 cache lines of which it uses a quarter, every line
+    // fetched by four waves. A row's 16-byte chunk j is stored at j ^ (row &
+    // 15), so that the 16 rows of a slice read fall on distinct banks.
+    // (bwd_local at (1,8192,16): 141 -> 137 us. The per-chunk kernels, the
+    // vector-gate one in particular, lost more to the extra barrier and the
+    // earlier wait than they gained, so they read their slices directly.)
+    constexpr bool SROW = sizeof(T) == 2 && PF;
+    bf16* const stg = (bf16*)lds;
+    if constexpr (SROW) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = w * 8 + i, mat = j >> 4, row = 4 * (j & 15) + (l >> 4);
+            const int rcl = row < nv ? row : nv - 1;  // rows past nv: row nv - 1 (masked where read)
+            const T* src = mat == 0 ? v : mat == 1 ? dO : mat == 2 ? k : q;
+            lds_dma16(src + rcl * ld + ((l & 15) ^ (row & 15)) * 8, stg + (mat * CH + 4 * (j & 15)) * DKD);
+        }
+    }
     typedef decltype(ld4raw(q)) R4;
     typedef decltype(ld8raw(q)) R8;
     const bf16* const Rbg = it.Rb + t * (CH * DVD);
@@ -263,17 +286,21 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     // token row 16 m + r, clamped into the chunk (zeros past nv)
     auto rowc = [&](int m) { return 16 * m + r < nv ? 16 * m + r : nv - 1; };
     const bool rv[4] = {r < nv, 16 + r < nv, 32 + r < nv, 48 + r < nv};
+    if constexpr (!SROW) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const R4 x = ld4raw(v + rowc(m) * ld + 16 * w + 4 * g);
-        vr[m] = rv[m] ? x : R4{};
+        for (int m = 0; m < 4; ++m) {
+            const R4 x = ld4raw(v + rowc(m) * ld + 16 * w + 4 * g);
+            vr[m] = rv[m] ? x : R4{};
+        }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) rq[i] = *(const bf16x4*)ctile_ptr(Rg, w * 4 + i);
+    if constexpr (!SROW) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const R4 x = ld4raw(dO + rowc(m) * ld + 16 * w + 4 * g);
-        orw[m] = rv[m] ? x : R4{};
+        for (int m = 0; m < 4; ++m) {
+            const R4 x = ld4raw(dO + rowc(m) * ld + 16 * w + 4 * g);
+            orw[m] = rv[m] ? x : R4{};
+        }
     }
     if (!PF) {
 #pragma unroll
@@ -282,13 +309,15 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             dhq[vt] = *(const bf16x4*)ctile_ptr(dhg, vt * 8 + w);
         }
     }
+    if constexpr (!SROW) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        // this wave's 16 keys only (as for v): lane (r, g) gets keys 16 w + 4 g .. + 3
-        const R4 xk = ld4raw(k + rowc(m) * ld + 16 * w + 4 * g);
-        const R4 xq = ld4raw(q + rowc(m) * ld + 16 * w + 4 * g);
-        kr[m] = rv[m] ? xk : R4{};
-        qr[m] = rv[m] ? xq : R4{};
+        for (int m = 0; m < 4; ++m) {
+            // this wave's 16 keys only (as for v): lane (r, g) gets keys 16 w + 4 g .. + 3
+            const R4 xk = ld4raw(k + rowc(m) * ld + 16 * w + 4 * g);
+            const R4 xq = ld4raw(q + rowc(m) * ld + 16 * w + 4 * g);
+            kr[m] = rv[m] ? xk : R4{};
+            qr[m] = rv[m] ? xq : R4{};
+        }
     }
     // GDN2: the erase gates of the chunk (two 16-byte row pieces per thread,
     // for LDS) and the write gates of this lane's P entries
@@ -403,11 +432,12 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     } else if (w == 0) {
         sG[l] = wave_incl_scan(graw[0]);
     }
-    {
+    auto zero_lG = [&]() {
         const bf16x8 z8 = {};
 #pragma unroll
         for (int u = 0; u < 4; ++u) lG[u * NTHR + tid] = z8;
-    }
+    };
+    if constexpr (!SROW) zero_lG();
     if constexpr (GD2) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -415,7 +445,25 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             *(bf16x8*)&sErs[(id >> 4) * EST + (id & 15) * 8] = eraw[u];
         }
     }
+    if constexpr (SROW) __builtin_amdgcn_s_waitcnt(0);  // this wave's row copies have landed
     lds_barrier();
+    if constexpr (SROW) {
+        // this wave's slices: lane (r, g) takes row 16 m + r, columns 16 w + 4 g .. + 3
+        // (16-byte chunk 2 w + g / 2 of the row, its half g & 1)
+        auto slice = [&](int mat, int m) -> R4 {
+            const int row = 16 * m + r, c = 2 * w + (g >> 1);
+            return *(const R4*)(stg + (mat * CH + row) * DKD + (c ^ (row & 15)) * 8 + 4 * (g & 1));
+        };
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            vr[m] = rv[m] ? slice(0, m) : R4{};
+            orw[m] = rv[m] ? slice(1, m) : R4{};
+            kr[m] = rv[m] ? slice(2, m) : R4{};
+            qr[m] = rv[m] ? slice(3, m) : R4{};
+        }
+        lds_barrier();  // every slice is read before phase 1 writes these buffers
+        zero_lG();      // (published by the barrier that closes phase 1)
+    }
     if (!VEC) Gnf = sG[CH - 1];
     // vector gate, this lane's key: the centre of window m (token tile m);
     // the pivot of row tile m's blocks against earlier windows (G at token
