@@ -20,10 +20,12 @@
 //     Sb <- diag(gn) Sb + Qg^T dO - W^T Z
 // Per step: A1 (16 x 128 per wave) times the state slabs, then A2 (32 x 64
 // per wave) times the Z slabs. The chunk operands arrive pre-swizzled in
-// frag/ctile order (kernels.h); the only on-chip exchange is the state and
-// Z slabs through LDS (one 16-byte write and a few 16-byte reads per lane,
-// two barriers). Every launch uses the loader-fed form below; in the
-// forward launch the loader waves also form the output O.
+// frag/ctile order (kernels.h). -W and Kt are stored once each: A1 is one
+// of them and A2 the transpose of the other, read from its frag tiles with
+// LDS transpose reads (ld_frag_t64x128). The only on-chip exchange is the
+// state and Z slabs through LDS (one 16-byte write and a few 16-byte reads
+// per lane, two barriers). Every launch uses the loader-fed form below; in
+// the forward launch the loader waves also form the output O.
 // Parallelism is one serial walk ("chain") per (sequence, head, value
 // slice, direction); see chain_of_block for how workgroups map onto chains.
 // Every slice of a head reads the head's whole A1 and A2 (32 KiB per step),
