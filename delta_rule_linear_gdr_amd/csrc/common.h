@@ -291,7 +291,6 @@ __host__ __device__ __forceinline__ int tr_slot(int s) { return s ^ ((s >> 2) & 
 // their slots placed by tr_slot.
 __device__ __forceinline__ bf16x8 ld_frag_t64x128(const uint8_t* xs, int mt, int ks)
 {
-    typedef short s16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const int r = lane_id() & 15, g = lane_id() >> 4;
     const int slot = tr_slot(4 * g + (r >> 2) + 16 * (r & 3));

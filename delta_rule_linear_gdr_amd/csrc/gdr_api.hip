@@ -60,9 +60,10 @@ struct Carver {
     }
 };
 
-// What the full-save forward keeps for the backward. A is kept once, as the
-// A^T frags the three-product producer reads; the seven-product backward
-// forms its A frags from them in scratch.
+// What the full-save forward keeps for the backward (its own forward scan
+// reads -W and Kt from here too). A is kept once, as the A^T frags the
+// three-product producer reads; the seven-product backward forms its A
+// frags from them in scratch.
 void carve_saved(Carver& c, Inter& it)
 {
     it.AT = c.take<bf16>(B_T64x64);
