@@ -109,7 +109,7 @@ unsigned scan_grid(const Shape& s, int nvs, int ndir)
 template <int NV, bool DEEP = false>
 struct Fed {
     static constexpr int A1 = 0;                   // 16 frag tiles of A1
-    static constexpr int A2 = 16384;               // 16 frag tiles of A2
+    static constexpr int A2 = 16384;               // 16 frag tiles of A2^T, slots by tr_slot
     static constexpr int C1 = 32768;               // 4 NV ctiles of C1 (value tiles NV vs ..)
     static constexpr int C2 = C1 + NV * 2048;      // 8 NV ctiles of C2 (reverse)
     static constexpr int GN = C2 + NV * 4096;      // gn (512 B)
