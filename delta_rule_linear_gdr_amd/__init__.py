@@ -234,7 +234,7 @@ def _desc_from(q, g, v):
 
 
 def _validate(q, k, v, g, beta, n_seq=None, *, h0=None, dO=None, dht=None, out=None,
-              saved=None, saved_bytes=0, scratch=None, erase=None, write=None):
+              saved=None, saved_bytes=0, scratch=None, erase=None, write=None, o=None):
     """Checks every tensor against the problem q and v define before any
     pointer reaches the library: device (one device, all of them), layout
     (contiguous), exact shape against (B, T, H, DK, DV) and the state count
@@ -253,7 +253,7 @@ def _validate(q, k, v, g, beta, n_seq=None, *, h0=None, dO=None, dht=None, out=N
     f32 = torch.float32
     spec = [("q", q, tok_k, q.dtype), ("k", k, tok_k, q.dtype), ("v", v, tok_v, q.dtype),
             ("beta", beta, row, q.dtype), ("h0", h0, state, f32), ("dO", dO, tok_v, q.dtype),
-            ("dht", dht, state, f32)]
+            ("dht", dht, state, f32), ("o", o, tok_v, q.dtype)]
     if g is not None:
         if g.dim() == 3:
             spec.append(("g", g, row, f32))
@@ -321,22 +321,25 @@ def _seqs(cu_seqlens, q):
 
 
 def gdr_fwd(q, k, v, g, beta, h0=None, policy="recompute", want_ht=True, scratch=None,
-            cu_seqlens=None):
+            cu_seqlens=None, o=None):
     """Forward. Returns (o, ht or None, saved or None).
 
     cu_seqlens (int64 device tensor of n_seq + 1 token offsets) makes the
     single row of q (batch size 1) a packed batch of n_seq sequences, each
-    with its own state: h0 and ht are then [n_seq, H, 128, 128]."""
+    with its own state: h0 and ht are then [n_seq, H, DK, DV]. o: an output
+    tensor shaped like v to write into (a new one by default); the rows of
+    tokens outside every sequence keep their contents."""
     torch = _torch()
     n_seq = _seqs(cu_seqlens, q)
-    _validate(q, k, v, g, beta, n_seq, h0=h0, scratch=scratch)
+    _validate(q, k, v, g, beta, n_seq, h0=h0, scratch=scratch, o=o)
     d = _desc_from(q, g, v)
     pol = _policy(policy)
     lib = load()
     saved_b, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
     ns = B if n_seq is None else n_seq
-    o = torch.empty_like(v)
+    if o is None:
+        o = torch.empty_like(v)
     ht = torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
                      device=q.device) if want_ht else None
     saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None
@@ -396,15 +399,15 @@ def gdr_bwd(q, k, v, g, beta, h0, dO, dht=None, saved=None, policy="recompute",
 
 
 def gdr_fwd_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute", want_ht=True,
-                 scratch=None, cu_seqlens=None):
+                 scratch=None, cu_seqlens=None, o=None):
     """GDN2 forward (per-key-channel gate g [B,T,H,DK] fp32, erase gate
     [B,T,H,DK] per key and write gate [B,T,H,DV] per value, bf16). Returns
-    (o, ht, saved). cu_seqlens: a packed batch, as for gdr_fwd."""
+    (o, ht, saved). cu_seqlens and o: as for gdr_fwd."""
     torch = _torch()
     if erase is None or write is None or g is None or g.dim() != 4:
         raise ValueError("GDN2 needs a per-channel g and both erase and write gates")
     n_seq = _seqs(cu_seqlens, q)
-    _validate(q, k, v, g, None, n_seq, h0=h0, scratch=scratch, erase=erase, write=write)
+    _validate(q, k, v, g, None, n_seq, h0=h0, scratch=scratch, erase=erase, write=write, o=o)
     d = _desc_from(q, g, v)
     d.gate = GATE_GDN2
     pol = _policy(policy)
@@ -412,7 +415,8 @@ def gdr_fwd_gdn2(q, k, v, g, erase, write, h0=None, policy="recompute", want_ht=
     saved_b, scratch_b = _sizes(d, pol, n_seq)
     B, T, H, _ = q.shape
     ns = B if n_seq is None else n_seq
-    o = torch.empty_like(v)
+    if o is None:
+        o = torch.empty_like(v)
     ht = torch.empty((ns, H, q.shape[-1], v.shape[-1]), dtype=torch.float32,
                      device=q.device) if want_ht else None
     saved = torch.empty(saved_b, dtype=torch.uint8, device=q.device) if saved_b else None

@@ -588,6 +588,14 @@ int workspace_any(const gdr_desc* d, const Packed& pk, int policy, size_t* saved
     return GDR_OK;
 }
 
+// Packed batches: the device address of the sanitized offsets' last entry
+// (the first token past the last sequence), which the inner call builds at
+// the start of its scratch and which stays there after it; null otherwise.
+const int64_t* seq_end(const Packed& pk, const void* inner_scratch)
+{
+    return pk.on ? (const int64_t*)inner_scratch + pk.n : nullptr;
+}
+
 // Shared checks of the padded calls; returns GDR_OK and fills pb, or a status.
 int pad_prologue(const gdr_desc* d, const Packed& pk, int policy, void* scratch, size_t scratch_bytes,
                  PadBufs& pb)
@@ -639,6 +647,8 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
     const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
     const bool vec = d->gate == GDR_GATE_VECTOR || g2on;
+    const int64_t* end = seq_end(pk, (char*)scratch + pb.bytes);
+    const int H = (int)d->H;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
@@ -656,7 +666,7 @@ int run_fwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
                      ht ? pb.s1 : nullptr, saved ? (char*)saved + b * inner_saved : nullptr,
                      (char*)scratch + pb.bytes, scratch_bytes - pb.bytes, stream, g2on ? gi : Gdn2Args{});
         if (rc) return rc;
-        PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st, DV, c0));
+        PAD_LAUNCH(launch_unpad_rows(o, pb.t4, rows, dv, esz, st, DV, c0, false, end, H));
         if (ht) PAD_LAUNCH(launch_unpad_state(ht, pb.s1, nst, dk, dv, st, DV, c0));
     }
     return GDR_OK;
@@ -693,6 +703,8 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
     const int64_t rows = d->B * d->T * d->H, nst = nseq * d->H;
     const int esz = d->dtype == GDR_F32 ? 4 : 2, dk = (int)d->DK, DV = (int)d->DV;
     const bool vec = d->gate == GDR_GATE_VECTOR || g2on, scal = d->gate == GDR_GATE_SCALAR;
+    const int64_t* end = seq_end(pk, (char*)scratch + pb.bytes);
+    const int H = (int)d->H;
     PAD_LAUNCH(launch_pad_rows(pb.q, q, rows, dk, esz, st));
     PAD_LAUNCH(launch_pad_rows(pb.k, k, rows, dk, esz, st));
     if (vec) PAD_LAUNCH(launch_pad_rows(pb.g, g, rows, dk, 4, st));
@@ -722,17 +734,17 @@ int run_bwd_padded(const gdr_desc* d, const Packed& pk, int policy, const void* 
         if (rc) return rc;
         if (g2on) {
             // the erase gradient is key-side (summed over the blocks), the write gradient the block's columns
-            PAD_LAUNCH(launch_unpad_rows(g2.ders, pb.ders, rows, dk, esz, st, dk, 0, !first));
-            PAD_LAUNCH(launch_unpad_rows(g2.dwrt, pb.dwrt, rows, dv, esz, st, DV, c0));
+            PAD_LAUNCH(launch_unpad_rows(g2.ders, pb.ders, rows, dk, esz, st, dk, 0, !first, end, H));
+            PAD_LAUNCH(launch_unpad_rows(g2.dwrt, pb.dwrt, rows, dv, esz, st, DV, c0, false, end, H));
         }
-        PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st, dk, 0, !first));
-        PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st, dk, 0, !first));
-        PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st, DV, c0));
-        if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st, dk, 0, !first));
+        PAD_LAUNCH(launch_unpad_rows(dq, pb.dq, rows, dk, esz, st, dk, 0, !first, end, H));
+        PAD_LAUNCH(launch_unpad_rows(dk_, pb.dk, rows, dk, esz, st, dk, 0, !first, end, H));
+        PAD_LAUNCH(launch_unpad_rows(dv_, pb.dv, rows, dv, esz, st, DV, c0, false, end, H));
+        if (vec) PAD_LAUNCH(launch_unpad_rows(dg, pb.dg, rows, dk, 4, st, dk, 0, !first, end, H));
         if (!first && !g2on) {
             // one entry per token and head: dbeta, and dg of a scalar gate
-            PAD_LAUNCH(launch_add_entries(dbeta, pb.db1, rows, esz, st));
-            if (scal) PAD_LAUNCH(launch_add_entries(dg, pb.dg1, rows, 4, st));
+            PAD_LAUNCH(launch_add_entries(dbeta, pb.db1, rows, esz, st, end, H));
+            if (scal) PAD_LAUNCH(launch_add_entries(dg, pb.dg1, rows, 4, st, end, H));
         }
         if (dh0) PAD_LAUNCH(launch_unpad_state(dh0, pb.s2, nst, dk, dv, st, DV, c0));
     }

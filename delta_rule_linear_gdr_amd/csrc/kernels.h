@@ -276,12 +276,16 @@ hipError_t launch_seq_tables(const Shape& s, const int64_t* cu_in, int64_t* cu, 
 // the block's first column; add = accumulate into dst (type from esz).
 hipError_t launch_pad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st,
                            int src_ld = 0, int col0 = 0);
+// end: null, or (packed batches) the device address of the first token past
+// the last sequence; rows from token *end on (per rows a token) are skipped
 hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st,
-                             int dst_ld = 0, int col0 = 0, bool add = false);
+                             int dst_ld = 0, int col0 = 0, bool add = false, const int64_t* end = nullptr,
+                             int per = 1);
 hipError_t launch_pad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st,
                             int src_dv = 0, int col0 = 0);
 // dst[i] += src[i] for n entries of esz bytes (bf16 or fp32)
-hipError_t launch_add_entries(void* dst, const void* src, int64_t n, int esz, hipStream_t st);
+hipError_t launch_add_entries(void* dst, const void* src, int64_t n, int esz, hipStream_t st,
+                              const int64_t* end = nullptr, int per = 1);
 hipError_t launch_unpad_state(float* dst, const float* src, int64_t n, int dk, int dv, hipStream_t st,
                               int dst_dv = 0, int col0 = 0);
 // Chunk-local backward. wy7 selects the expanded seven-product producer.

@@ -7,7 +7,10 @@
 // value blocks: the copies then take a block (a column offset into wider
 // rows), and the key-side gradients of the blocks are summed (ADD). Plain
 // copies are bit copies: the element type only sets the width (2 bytes for
-// bf16, 4 for fp32), and zero bits are 0.
+// bf16, 4 for fp32), and zero bits are 0. For a packed batch the copies out
+// stop at the end of the last sequence (`end`, the sanitized offsets' last
+// entry, read on the device; rows are token-major with `per` rows a token):
+// tokens past it are outside every sequence and keep their contents.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,8 +42,10 @@ __global__ void pad_rows_kernel(E* dst, const E* src, int64_t rows, int w, int s
 // rows of width 128 -> the first w entries, to column col0 of rows of dst_ld
 // entries (a copy, or with ADD the sum dst + src rounded once to the type)
 template <typename E, bool ADD>
-__global__ void unpad_rows_kernel(E* dst, const E* src, int64_t rows, int w, int dst_ld, int col0)
+__global__ void unpad_rows_kernel(E* dst, const E* src, int64_t rows, int w, int dst_ld, int col0,
+                                  const int64_t* end, int per)
 {
+    if (end) rows = min(rows, *end * per);
     const int64_t n = rows * w;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t r = i / w;
@@ -76,18 +81,20 @@ __global__ void unpad_state_kernel(float* dst, const float* src, int64_t n, int 
 
 // dst[i] += src[i], i < n, rounded once to the type
 template <typename E>
-__global__ void add_entries_kernel(E* dst, const E* src, int64_t n)
+__global__ void add_entries_kernel(E* dst, const E* src, int64_t n, const int64_t* end, int per)
 {
+    if (end) n = min(n, *end * per);
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = (E)((float)dst[i] + (float)src[i]);
 }
 
 }  // namespace
 
-hipError_t launch_add_entries(void* dst, const void* src, int64_t n, int esz, hipStream_t st)
+hipError_t launch_add_entries(void* dst, const void* src, int64_t n, int esz, hipStream_t st, const int64_t* end,
+                              int per)
 {
-    if (esz == 2) add_entries_kernel<bf16><<<grid_for(n), 256, 0, st>>>((bf16*)dst, (const bf16*)src, n);
-    else add_entries_kernel<float><<<grid_for(n), 256, 0, st>>>((float*)dst, (const float*)src, n);
+    if (esz == 2) add_entries_kernel<bf16><<<grid_for(n), 256, 0, st>>>((bf16*)dst, (const bf16*)src, n, end, per);
+    else add_entries_kernel<float><<<grid_for(n), 256, 0, st>>>((float*)dst, (const float*)src, n, end, per);
     return hipGetLastError();
 }
 
@@ -105,20 +112,24 @@ hipError_t launch_pad_rows(void* dst, const void* src, int64_t rows, int w, int 
 }
 
 hipError_t launch_unpad_rows(void* dst, const void* src, int64_t rows, int w, int esz, hipStream_t st,
-                             int dst_ld, int col0, bool add)
+                             int dst_ld, int col0, bool add, const int64_t* end, int per)
 {
     if (dst_ld <= 0) dst_ld = w;
     const unsigned gr = grid_for(rows * w);
     if (add) {
         // sums need the element type: bf16 (2 bytes) or fp32 (4)
-        if (esz == 2) unpad_rows_kernel<bf16, true><<<gr, 256, 0, st>>>((bf16*)dst, (const bf16*)src, rows, w, dst_ld, col0);
-        else unpad_rows_kernel<float, true><<<gr, 256, 0, st>>>((float*)dst, (const float*)src, rows, w, dst_ld, col0);
+        if (esz == 2)
+            unpad_rows_kernel<bf16, true><<<gr, 256, 0, st>>>((bf16*)dst, (const bf16*)src, rows, w, dst_ld, col0,
+                                                              end, per);
+        else
+            unpad_rows_kernel<float, true><<<gr, 256, 0, st>>>((float*)dst, (const float*)src, rows, w, dst_ld, col0,
+                                                               end, per);
     } else if (esz == 2) {
         unpad_rows_kernel<uint16_t, false><<<gr, 256, 0, st>>>((uint16_t*)dst, (const uint16_t*)src, rows, w, dst_ld,
-                                                              col0);
+                                                              col0, end, per);
     } else {
         unpad_rows_kernel<uint32_t, false><<<gr, 256, 0, st>>>((uint32_t*)dst, (const uint32_t*)src, rows, w, dst_ld,
-                                                              col0);
+                                                              col0, end, per);
     }
     return hipGetLastError();
 }

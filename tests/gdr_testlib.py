@@ -150,7 +150,7 @@ def compare_all_heads(gpu, x, report=None):
 
 # ---------------------------------------------------- packed (varlen) batches
 
-SENTINEL = 7.0  # prefilled into gradient outputs; tokens of no sequence keep it
+SENTINEL = 7.0  # prefilled into o and the gradient outputs; tokens of no sequence keep it
 
 
 def run_gpu_packed(x, policy="recompute"):
@@ -160,7 +160,7 @@ def run_gpu_packed(x, policy="recompute"):
     d = device_inputs(x)
     cu = torch.from_numpy(x["cu"]).to("cuda")
     o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
-                               policy=policy, cu_seqlens=cu)
+                               policy=policy, cu_seqlens=cu, o=torch.full_like(d["v"], SENTINEL))
     out = {n: torch.full_like(d[s], SENTINEL) for n, s in
            (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"))}
     out["dh0"] = torch.empty_like(d["h0"])
@@ -197,7 +197,7 @@ def oracle_packed(x, heads=None):
 
 def compare_packed(gpu, x, heads=None, report=None):
     """Per-tensor acceptance over the covered tokens of the chosen heads, and
-    the gradient outputs of tokens outside every sequence left untouched."""
+    the outputs of tokens outside every sequence left untouched."""
     cu = x["cu"]
     ref = oracle_packed(x, heads)
     got_all, ref_all = {}, {}
@@ -210,7 +210,7 @@ def compare_packed(gpu, x, heads=None, report=None):
     errs = {n: check(n, np.concatenate(got_all[n]), np.concatenate(ref_all[n]))
             for n in got_all}
     tail = int(cu[-1])
-    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+    for n in ("o", "dq", "dk", "dv", "dg", "dbeta"):
         assert np.all(gpu[n][:, tail:] == SENTINEL), f"{n}: tokens past the last sequence written"
     if report is not None:
         report.update(errs)

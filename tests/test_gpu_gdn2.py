@@ -133,8 +133,8 @@ def test_gdn2_without_states():
 # ------------------------------------- packed batches and other widths (GDN2)
 
 def run_gdn2_packed(x, policy="recompute"):
-    """Packed GDN2 forward + backward; gradient outputs prefilled with a
-    sentinel that tokens outside every sequence must keep."""
+    """Packed GDN2 forward + backward; o and the gradient outputs prefilled
+    with a sentinel that tokens outside every sequence must keep."""
     import torch
     import delta_rule_linear_gdr_amd as gdr
     d = tl.device_inputs(x)
@@ -142,7 +142,7 @@ def run_gdn2_packed(x, policy="recompute"):
     w = tl.to_dev(x["wrt"], torch.bfloat16)
     cu = torch.from_numpy(x["cu"]).to("cuda")
     o, ht, saved = gdr.gdr_fwd_gdn2(d["q"], d["k"], d["v"], d["g"], e, w, d["h0"], policy=policy,
-                                    cu_seqlens=cu)
+                                    cu_seqlens=cu, o=torch.full_like(d["v"], tl.SENTINEL))
     out = {n: torch.full_like(t, tl.SENTINEL) for n, t in
            (("dq", d["q"]), ("dk", d["k"]), ("dv", d["v"]), ("dg", d["g"]), ("derase", e),
             ("dwrite", w))}
@@ -181,7 +181,7 @@ def compare_gdn2_packed(gpu, x):
                 ref.setdefault(n, []).append(np.asarray(arr).ravel())
     errs = {n: tl.check(n, np.concatenate(got[n]), np.concatenate(ref[n]), tol=TOL[n]) for n in got}
     tail = int(cu[-1])
-    for n in ("dq", "dk", "dv", "dg", "ders", "dwrt"):
+    for n in ("o", "dq", "dk", "dv", "dg", "ders", "dwrt"):
         assert np.all(gpu[n][:, tail:] == tl.SENTINEL), f"{n}: tokens past the last sequence written"
     return errs
 
@@ -210,12 +210,35 @@ def test_gdn2_packed_mixed_lengths(policy):
     _report(f"packed/{policy}", compare_gdn2_packed(run_gdn2_packed(x, policy), x))
 
 
-def test_gdn2_packed_narrow_widths():
+@pytest.mark.parametrize("policy", ["recompute", "full_save"])
+def test_gdn2_packed_narrow_widths(policy):
     """A packed batch at key width 80 and value width 112."""
     _need_gpu()
     from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
     x = _narrow(make_packed_inputs([70, 0, 130], H=2, gate="gdn2", seed=37, gate_mean=3.0), 80, 112)
-    _report("packed/80x112", compare_gdn2_packed(run_gdn2_packed(x), x))
+    _report(f"packed/80x112/{policy}", compare_gdn2_packed(run_gdn2_packed(x, policy), x))
+
+
+def test_gdn2_packed_value_blocks():
+    """A packed batch at key width 64 and value width 160 (a 128-wide value
+    block and a 32-wide one, each zero-padded), with a tail of tokens outside
+    every sequence: padding, value blocks and the sequence table together."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs, round_bf16, round_fp32
+    x = make_packed_inputs([50, 0, 90], H=2, gate="gdn2", seed=38, gate_mean=3.0, cover=160)
+    # values and value-side tensors widened to 160 with fresh draws (any value is valid)
+    rng = np.random.default_rng(39)
+    wide = lambda a, extra: np.ascontiguousarray(np.concatenate([a, extra], axis=-1))  # noqa: E731
+    T, H = x["q"].shape[1:3]
+    x["v"] = wide(x["v"], round_bf16(rng.standard_normal((1, T, H, 32))))
+    x["dO"] = wide(x["dO"], round_bf16(rng.standard_normal((1, T, H, 32))))
+    x["wrt"] = wide(x["wrt"], round_bf16(1.0 / (1.0 + np.exp(-rng.standard_normal((1, T, H, 32))))))
+    n = len(x["cu"]) - 1
+    x["h0"] = wide(x["h0"], round_fp32(0.1 * rng.standard_normal((n, H, 128, 32))))
+    x["dht"] = wide(x["dht"], round_fp32(0.1 * rng.standard_normal((n, H, 128, 32))))
+    x = _narrow(x, 64, 160)
+    for pol in ("recompute", "full_save"):
+        _report(f"packed/64x160/{pol}", compare_gdn2_packed(run_gdn2_packed(x, pol), x))
 
 
 @pytest.mark.parametrize("dk,dv", [(80, 112), (96, 80), (128, 160), (64, 300)])

@@ -384,13 +384,13 @@ def test_narrow_widths(gate, dk, dv):
 @pytest.mark.gpu
 def test_narrow_widths_fp32_wy7_and_packed():
     """fp32 storage and the seven-product producer at 64/96, and a packed
-    batch at 80/112."""
+    batch at 80/112 with a tail of tokens outside every sequence."""
     _need_gpu()
     x = make_inputs(1, 150, 2, DK=64, DV=96, gate="vector", dtype="fp32", seed=52, gate_mean=3.0,
                     h0_std=0.1, dht_std=0.1)
     _report("narrow/fp32/wy7", tl.compare(tl.run_gpu(x, wy7=True), x))
     from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
-    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=53)
+    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=53, cover=229)
     # narrow copies of the packed inputs: keys and values cut to 80 and 112
     for n in ("q", "k"):
         xp[n] = np.ascontiguousarray(xp[n][..., :80])
@@ -629,7 +629,8 @@ def test_value_widths_above_128(gate, dk, dv):
 @pytest.mark.gpu
 def test_value_width_160_fp32_wy7_deltanet_and_packed():
     """Value width 160 with fp32 storage and the seven-product producer, with
-    no gate (DeltaNet), and in a packed batch."""
+    no gate (DeltaNet), and in a packed batch with a tail of tokens outside
+    every sequence."""
     _need_gpu()
     x = make_inputs(1, 150, 2, DK=96, DV=160, gate="vector", dtype="fp32", seed=55, gate_mean=3.0,
                     h0_std=0.1, dht_std=0.1)
@@ -639,7 +640,7 @@ def test_value_width_160_fp32_wy7_deltanet_and_packed():
     xn["g"] = np.zeros_like(xn["g"])
     _report("wide/deltanet", tl.compare(tl.run_gpu(xn, nogate=True), xn))
     from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
-    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=57)
+    xp = make_packed_inputs([70, 0, 130], H=2, gate="scalar", seed=57, cover=241)
     rng = np.random.default_rng(58)
     # value width 160: the packed inputs' 128 value columns and 32 more
     for n in ("v", "dO"):
