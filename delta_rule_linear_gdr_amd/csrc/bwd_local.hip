@@ -275,14 +275,24 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     }
     bf16x4 rbq[4], rq[4], hq[8], dhq[8];
     bf16x8 atf[6];  // A^T frags m * 2 + 1 (m = 0..3), then m * 2 + 0 (m = 0, 1)
+    // Every wave multiplies by all six nonzero A^T frags. The persistent form
+    // copies them once into LDS (wave j < 6 copies frag j of atf's order) and
+    // each wave reads them from there after the first barrier, instead of
+    // eight waves fetching the same 6 KiB (bwd_local at (1,8192,16): 136.7
+    // -> 135.4 us).
+    __shared__ bf16x8 sAT[SROW ? 6 * 64 : 1];
     R4 vr[4], orw[4];
     R4 kr[4], qr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) rbq[i] = *(const bf16x4*)ctile_ptr(Rbg, w * 4 + i);
+    if constexpr (SROW) {
+        if (w < 6) lds_dma16(frag_ptr(ATg, w < 4 ? w * 2 + 1 : (w - 4) * 2), sAT + w * 64);
+    } else {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) atf[m] = ld_frag(ATg, m * 2 + 1);
-    atf[4] = ld_frag(ATg, 0);
-    atf[5] = ld_frag(ATg, 2);
+        for (int m = 0; m < 4; ++m) atf[m] = ld_frag(ATg, m * 2 + 1);
+        atf[4] = ld_frag(ATg, 0);
+        atf[5] = ld_frag(ATg, 2);
+    }
     // token row 16 m + r, clamped into the chunk (zeros past nv)
     auto rowc = [&](int m) { return 16 * m + r < nv ? 16 * m + r : nv - 1; };
     const bool rv[4] = {r < nv, 16 + r < nv, 32 + r < nv, 48 + r < nv};
@@ -445,7 +455,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             *(bf16x8*)&sErs[(id >> 4) * EST + (id & 15) * 8] = eraw[u];
         }
     }
-    if constexpr (SROW) __builtin_amdgcn_s_waitcnt(0);  // this wave's row copies have landed
+    if constexpr (SROW) __builtin_amdgcn_s_waitcnt(0);  // this wave's row and A^T copies have landed
     lds_barrier();
     if constexpr (SROW) {
         // this wave's slices: lane (r, g) takes row 16 m + r, columns 16 w + 4 g .. + 3
@@ -502,6 +512,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     const bf16x8 Ipw = ident_pi(w & 1, lx);
     const bf16x4 z4 = {};
 
+    if constexpr (SROW) {
+#pragma unroll
+        for (int j = 0; j < 6; ++j) atf[j] = sAT[j * 64 + l];
+    }
     // ---- 1a. P^T = Rb^T A for value tile w ----
     {
         const bf16x8 RbT[2] = {cat8(rbq[0], rbq[1]), cat8(rbq[2], rbq[3])};
