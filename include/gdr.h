@@ -3,7 +3,8 @@
  * forward and backward of Gated DeltaNet (scalar gate), Kimi Delta
  * Attention (per-key-channel gate), DeltaNet (no decay) and GDN2
  * (per-key-channel gate, independent erase and write gates), chunk size 64,
- * key and value width up to 128, regular or packed variable-length batches.
+ * key width up to 128, value width up to 1024, regular or packed
+ * variable-length batches.
  *
  * Operation ("ReWY: Faster Backpropagation for Delta-Rule Attention -- From
  * 7 to 3 Matrix Multiplications", paperpeel.com/paper/2611.01940, Sec. 2.2
@@ -52,10 +53,18 @@
  * unchanged and zero value columns only add zero columns -- at the cost of
  * the padded work and the copies. In the layouts above, 128 then reads DK
  * (q, k, dq, dk, a vector g and dg), DV (v, o, dO, dv) and DK x DV (states).
+ * Value widths above 128 (up to 1024) run as 128-wide value blocks: the value
+ * columns of the state evolve independently, so each block is its own
+ * problem on the same kernels. o, ht, dv and dh0 take the block's columns;
+ * the key-side gradients dq, dk, dg and dbeta are the sums of the blocks'
+ * contributions, added in block order in fp32 and rounded once per addition
+ * to the stored type (no atomics). The key-side work repeats per block, and
+ * a full-save `saved` area holds one block's set per block.
  *
  * Errors: arguments are validated before anything is launched; on error
  * nothing is launched and the call returns a negative status. Unsupported
- * shapes (a width above 128, chunk other than 64) return GDR_ERR_UNSUPPORTED
+ * shapes (a key width above 128, a value width above 1024, chunk other than
+ * 64) return GDR_ERR_UNSUPPORTED
  * -- there is no fallback (that page's "Existing Training Scripts":
  * unsupported configurations fail by default). T may be any length:
  * where that page requires a multiple of 64, a ragged last chunk is handled
@@ -104,7 +113,7 @@ typedef enum { GDR_BF16 = 0, GDR_F32 = 1 } gdr_dtype;
 
 typedef struct {
     int64_t B, T, H;  /* batch, sequence length, heads */
-    int64_t DK, DV;   /* key and value width: 1 .. 128 (128 without padding) */
+    int64_t DK, DV;   /* key width 1 .. 128, value width 1 .. 1024 (128: no padding) */
     int64_t C;        /* chunk length: must be 64 */
     int32_t gate;     /* gdr_gate */
     int32_t dtype;    /* gdr_dtype */
