@@ -16,12 +16,13 @@ unbuilt library raises.
 Shapes: q, k [B,T,H,DK]; v, dO [B,T,H,DV]; g [B,T,H] (GDN, scalar gate),
 [B,T,H,DK] (KDA, per-channel gate), fp32, or None (DeltaNet: no decay, and
 no dg); beta [B,T,H]; h0, dht [B,H,DK,DV] fp32 (key-major) or None.
-DK, DV <= 128 (below 128 through zero-padded copies). q, k, v, beta, dO
-share one dtype, bfloat16 or float32. Any T (a ragged last chunk is handled).
+DK <= 128 and DV <= 1024 (widths below 128 through zero-padded copies, value
+widths above 128 as 128-wide value blocks). q, k, v, beta, dO share one
+dtype, bfloat16 or float32. Any T (a ragged last chunk is handled).
 
 Packed variable-length batches: pass ``cu_seqlens`` (int64 device tensor of
 n_seq + 1 token offsets) with batch size 1; the states h0, ht, dht, dh0 are
-then [n_seq,H,128,128].
+then [n_seq,H,DK,DV].
 """
 from __future__ import annotations
 
