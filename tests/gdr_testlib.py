@@ -153,22 +153,25 @@ def compare_all_heads(gpu, x, report=None):
 SENTINEL = 7.0  # prefilled into o and the gradient outputs; tokens of no sequence keep it
 
 
-def run_gpu_packed(x, policy="recompute"):
-    """Packed forward + backward (cu_seqlens) on the device; numpy float64."""
+def run_gpu_packed(x, policy="recompute", nogate=False):
+    """Packed forward + backward (cu_seqlens) on the device; numpy float64.
+    nogate: call with g = None (DeltaNet; x["g"] must then be all zero)."""
     import torch
     import delta_rule_linear_gdr_amd as gdr
     d = device_inputs(x)
+    g = None if nogate else d["g"]
     cu = torch.from_numpy(x["cu"]).to("cuda")
-    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"],
+    o, ht, saved = gdr.gdr_fwd(d["q"], d["k"], d["v"], g, d["beta"], d["h0"],
                                policy=policy, cu_seqlens=cu, o=torch.full_like(d["v"], SENTINEL))
     out = {n: torch.full_like(d[s], SENTINEL) for n, s in
-           (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"))}
+           (("dq", "q"), ("dk", "k"), ("dv", "v"), ("dg", "g"), ("dbeta", "beta"))
+           if not (nogate and n == "dg")}
     out["dh0"] = torch.empty_like(d["h0"])
-    gr = gdr.gdr_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["h0"], d["dO"], d["dht"],
+    gr = gdr.gdr_bwd(d["q"], d["k"], d["v"], g, d["beta"], d["h0"], d["dO"], d["dht"],
                      saved=saved, policy=policy, out=out, cu_seqlens=cu)
     torch.cuda.synchronize()
     res = {"o": o, "ht": ht, **gr}
-    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items()}
+    return {n: t.float().cpu().numpy().astype(np.float64) for n, t in res.items() if t is not None}
 
 
 def oracle_packed(x, heads=None):
@@ -204,6 +207,8 @@ def compare_packed(gpu, x, heads=None, report=None):
     for (i, h), r in ref.items():
         a, b = int(cu[i]), int(cu[i + 1])
         for n, arr in r.items():
+            if n not in gpu:
+                continue
             g = gpu[n][i:i + 1, h:h + 1] if n in ("ht", "dh0") else gpu[n][:, a:b, h:h + 1]
             got_all.setdefault(n, []).append(g.ravel())
             ref_all.setdefault(n, []).append(np.asarray(arr).ravel())
@@ -211,6 +216,8 @@ def compare_packed(gpu, x, heads=None, report=None):
             for n in got_all}
     tail = int(cu[-1])
     for n in ("o", "dq", "dk", "dv", "dg", "dbeta"):
+        if n not in gpu:
+            continue
         assert np.all(gpu[n][:, tail:] == SENTINEL), f"{n}: tokens past the last sequence written"
     if report is not None:
         report.update(errs)

@@ -651,3 +651,46 @@ def test_value_width_160_fp32_wy7_deltanet_and_packed():
             [xp[n], (0.1 * rng.standard_normal(xp[n].shape[:-1] + (32,))).astype(np.float32)
              .astype(np.float64)], axis=-1))
     _report("wide/packed", tl.compare_packed(tl.run_gpu_packed(xp), xp))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("gate", ["scalar", "vector"])
+def test_packed_value_blocks_both_policies(gate):
+    """A packed batch at value width 200 (two value blocks: 128 + 72) with an
+    empty sequence, a ragged one and a tail of tokens outside every sequence,
+    under both policies (the full-save area holds one block's set per block)."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    xp = make_packed_inputs([90, 0, 150], H=2, gate=gate, seed=63, gate_mean=3.0, cover=270)
+    rng = np.random.default_rng(64)
+    # value width 200: the packed inputs' 128 value columns and 72 more
+    for n in ("v", "dO"):
+        extra = np.asarray(xp[n][..., :72])[..., ::-1]
+        xp[n] = np.ascontiguousarray(np.concatenate([xp[n], extra], axis=-1))
+    for n in ("h0", "dht"):
+        xp[n] = np.ascontiguousarray(np.concatenate(
+            [xp[n], (0.1 * rng.standard_normal(xp[n].shape[:-1] + (72,))).astype(np.float32)
+             .astype(np.float64)], axis=-1))
+    for pol in ("recompute", "full_save"):
+        _report(f"packed/200/{gate}/{pol}", tl.compare_packed(tl.run_gpu_packed(xp, pol), xp))
+
+
+@pytest.mark.gpu
+def test_deltanet_packed_narrow_with_tail():
+    """DeltaNet (no gate) over a packed batch at widths 80/112 with a tail of
+    tokens outside every sequence, under both policies: the zero-gate
+    workspace, the padded copies and the packed tables together."""
+    _need_gpu()
+    from delta_rule_linear_gdr_amd.inputs import make_packed_inputs
+    x = make_packed_inputs([70, 0, 130, 1], H=2, gate="scalar", seed=65, cover=230)
+    x["g"] = np.zeros_like(x["g"])
+    for n in ("q", "k"):
+        x[n] = np.ascontiguousarray(x[n][..., :80])
+    for n in ("v", "dO"):
+        x[n] = np.ascontiguousarray(x[n][..., :112])
+    for n in ("h0", "dht"):
+        x[n] = np.ascontiguousarray(x[n][:, :, :80, :112])
+    for pol in ("recompute", "full_save"):
+        got = tl.run_gpu_packed(x, pol, nogate=True)
+        assert "dg" not in got
+        _report(f"deltanet/packed/80x112/{pol}", tl.compare_packed(got, x))
