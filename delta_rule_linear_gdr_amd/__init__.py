@@ -32,7 +32,8 @@ import os
 __all__ = ["gdr_fwd", "gdr_bwd", "gdr_bwd_wy7", "gdr_fwd_gdn2", "gdr_bwd_gdn2",
            "chunk_gated_delta_rule", "chunk_gdn2", "workspace_size",
            "library_path", "load",
-           "profile_begin", "profile_end", "set_local_form", "gate_status", "GdrError",
+           "profile_begin", "profile_end", "set_local_form", "set_walk_levels", "gate_status",
+           "GdrError",
            "RECOMPUTE", "FULL_SAVE"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,10 +48,8 @@ STATUS = {0: "GDR_OK", -1: "GDR_ERR_INVALID", -2: "GDR_ERR_UNSUPPORTED",
 EXPORTS = ("gdr_workspace_size", "gdr_fwd", "gdr_bwd", "gdr_bwd_wy7",
            "gdr_fwd_gdn2", "gdr_bwd_gdn2", "gdr_fwd_gdn2_varlen", "gdr_bwd_gdn2_varlen",
            "gdr_bwd_noalloc", "gdr_workspace_size_varlen", "gdr_fwd_varlen", "gdr_bwd_varlen",
-           "gdr_profile_begin",
-           "gdr_profile_end", "gdr_set_local_form", "gdr_gate_status", "gdr_status_string",
-           "gdr_last_error",
-           "gdr_version")
+           "gdr_profile_begin", "gdr_profile_end", "gdr_set_local_form", "gdr_set_walk_levels",
+           "gdr_gate_status", "gdr_status_string", "gdr_last_error", "gdr_version")
 
 
 class GdrError(RuntimeError):
@@ -119,6 +118,8 @@ def load():
     lib.gdr_gate_status.restype = i32
     lib.gdr_set_local_form.argtypes = [i32]
     lib.gdr_set_local_form.restype = i32
+    lib.gdr_set_walk_levels.argtypes = [i32]
+    lib.gdr_set_walk_levels.restype = i32
     lib.gdr_status_string.argtypes = [i32]
     lib.gdr_status_string.restype = ctypes.c_char_p
     lib.gdr_last_error.argtypes = []
@@ -204,6 +205,19 @@ def set_local_form(form: str) -> str:
     if form not in forms:
         raise ValueError(f"unknown form {form!r}")
     rc = load().gdr_set_local_form(forms[form])
+    if rc < 0:
+        _check(rc)
+    return {v: k for k, v in forms.items()}[rc]
+
+
+def set_walk_levels(form: str) -> str:
+    """Form of the state walks: "auto" (default: segmented, two-level walks
+    where a one-level launch would leave most compute units idle) or "one"
+    (every walk start to end). Returns the previous form."""
+    forms = {"auto": 0, "one": 1}
+    if form not in forms:
+        raise ValueError(f"unknown form {form!r}")
+    rc = load().gdr_set_walk_levels(forms[form])
     if rc < 0:
         _check(rc)
     return {v: k for k, v in forms.items()}[rc]

@@ -7,6 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <string>
@@ -58,7 +59,25 @@ struct Carver {
         off += per_tile * ntiles;
         return r;
     }
+    template <typename X>
+    X* take_bytes(size_t bytes)
+    {
+        off = align_up(off);
+        X* r = base ? (X*)(base + off) : nullptr;
+        off += bytes;
+        return r;
+    }
 };
+
+// Segments of a call's walk launch (two-level walks, scan.hip): nseg 1 is
+// a one-level walk. nsh: state entries (sequences x heads).
+struct WalkSeg {
+    int nseg = 1;
+    int64_t seglen = 0, nsh = 0;
+};
+// Process-wide choice of walk form (gdr_set_walk_levels): 0 automatic, 1
+// always one level. The workspace is sized for the automatic form either way.
+std::atomic<int> g_walk_levels{0};
 
 // What the full-save forward keeps for the backward (its own forward scan
 // reads -W and Kt from here too). A is kept once, as the A^T frags the
@@ -80,7 +99,7 @@ enum Phase { FWD, BWD };
 
 // Lays out saved/scratch for one call; with null bases it only measures.
 void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Inter& it,
-            size_t& saved_bytes, size_t& scratch_bytes)
+            size_t& saved_bytes, size_t& scratch_bytes, const WalkSeg& ws)
 {
     memset(&it, 0, sizeof it);
     Carver sv(saved, ntiles), sc(scratch, ntiles);
@@ -116,6 +135,15 @@ void layout(int policy, Phase ph, void* saved, void* scratch, size_t ntiles, Int
         it.dh = sc.take<bf16>(B_T128x128);
         it.Rb = sc.take<bf16>(B_T64x128);
         if (full) it.Af = sc.take<bf16>(B_T64x64);  // seven-product backward only
+    }
+    // two-level walks: segment summaries and entry states, both directions
+    it.nseg = 1;
+    it.seglen = ws.seglen;
+    if (ws.nseg > 1) {
+        const size_t st = (size_t)DKD * DVD * 4, nsh = (size_t)ws.nsh;
+        it.seg_sum = sc.take_bytes<float>(2 * (size_t)(ws.nseg - 1) * nsh * 2 * st);
+        it.seg_ent = sc.take_bytes<float>(2 * (size_t)ws.nseg * nsh * st);
+        if (g_walk_levels.load(std::memory_order_relaxed) != 1) it.nseg = ws.nseg;
     }
     saved_bytes = full ? align_up(sv.off) : 0;
     scratch_bytes = align_up(sc.off);
@@ -159,6 +187,38 @@ size_t ntiles(const gdr_desc* d, const Packed& pk)
 {
     return (size_t)(pk.on ? d->H : d->B * d->H) * (size_t)nslots(d, pk);
 }
+// Two-level walks (scan.hip) replace a one-level walk launch that would fill
+// at most a quarter of the chip's 256 CUs, for regular batches: the segment
+// walks (a workgroup per segment and 16 value columns) and the summaries
+// (twice the chains, every segment but one) must each fit one round of
+// workgroups. A summary pass plus a segment walk take 2 / nseg of the
+// serial steps of one walk, but each runs more workgroups at once (a step
+// ~1.0 and ~0.7 us against ~0.65 for the one-level pair at (1,8192,4)), and
+// chaining the entry states costs ~5 us per segment. So a segment keeps at
+// least 20 chunks and there are at least 4 segments: measured at T = 8192
+// with 1, 2 and 4 heads, the launches that qualify gain 11-31%, while the
+// recompute pair at 3 segments, the full-save reverse walk at 4 segments of
+// 16 chunks (T = 4096) and every launch at T = 2048 lose. ph / policy select
+// the launch: the forward's walk, the recompute backward's two directions, or
+// the full-save backward's reverse walk.
+constexpr int64_t WALK_CUS = 256;
+WalkSeg walk_seg(const gdr_desc* d, const Packed& pk, Phase ph, int policy)
+{
+    WalkSeg w;
+    w.nsh = (pk.on ? pk.n : d->B) * d->H;
+    if (pk.on) return w;
+    const int64_t ndir = ph == BWD && policy == GDR_RECOMPUTE ? 2 : 1;
+    const int64_t NT = nchunks(d), base = d->B * d->H * ndir * (DVD / 16);
+    if (base <= 0 || 4 * base > WALK_CUS) return w;
+    int64_t n = std::min(WALK_CUS / base, 1 + WALK_CUS / (2 * base));
+    n = std::min(n, NT / 20);
+    while (n > 1 && (n - 1) * ((NT + n - 1) / n) >= NT) --n;  // no empty segment
+    if (n < 4) return w;
+    w.nseg = (int)n;
+    w.seglen = (NT + n - 1) / n;
+    return w;
+}
+
 // Bytes of the sequence tables at the start of scratch (packed batches).
 size_t table_bytes(const gdr_desc* d, const Packed& pk)
 {
@@ -394,13 +454,14 @@ int run_bwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
     Inter it;
     size_t sb = 0, need = 0;
-    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
+    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, sb, need, walk_seg(d, pk, BWD, policy));
     need += tb;
     if (!scratch || scratch_bytes < need)
         return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
                     scratch ? scratch_bytes : (size_t)0);
     if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
-    layout(policy, BWD, (void*)saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
+    layout(policy, BWD, (void*)saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need,
+           walk_seg(d, pk, BWD, policy));
 
     const Shape s = make_shape(d, pk, scratch);
     hipError_t e = hipSuccess;
@@ -475,13 +536,13 @@ int run_fwd(const gdr_desc* d, const Packed& pk, int policy, const void* q, cons
     const size_t tb = table_bytes(d, pk) + nogate_bytes(d);
     Inter it;
     size_t sb = 0, need = 0;
-    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, sb, need);
+    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, sb, need, walk_seg(d, pk, FWD, policy));
     need += tb;
     if (!scratch || scratch_bytes < need)
         return fail(GDR_ERR_WORKSPACE, "scratch of %zu bytes needed, %zu given", need,
                     scratch ? scratch_bytes : (size_t)0);
     if (!aligned16(scratch)) return fail(GDR_ERR_INVALID, "scratch is not 16-byte aligned");
-    layout(policy, FWD, saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need);
+    layout(policy, FWD, saved, (char*)scratch + tb, ntiles(d, pk), it, sb, need, walk_seg(d, pk, FWD, policy));
     const Shape s = make_shape(d, pk, scratch);
     hipError_t e = hipSuccess;
     if (nogate(d)) {
@@ -506,8 +567,8 @@ int workspace(const gdr_desc* d, const Packed& pk, int policy, size_t* saved_byt
 {
     Inter it;
     size_t s1 = 0, c1 = 0, s2 = 0, c2 = 0;
-    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, s1, c1);
-    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, s2, c2);
+    layout(policy, FWD, nullptr, nullptr, ntiles(d, pk), it, s1, c1, walk_seg(d, pk, FWD, policy));
+    layout(policy, BWD, nullptr, nullptr, ntiles(d, pk), it, s2, c2, walk_seg(d, pk, BWD, policy));
     if (saved_bytes) *saved_bytes = s1;
     if (scratch_bytes) *scratch_bytes = table_bytes(d, pk) + nogate_bytes(d) + (c1 > c2 ? c1 : c2);
     return GDR_OK;
@@ -1114,6 +1175,13 @@ int gdr_set_local_form(int form)
     if (form != GDR_LOCAL_PERSISTENT && form != GDR_LOCAL_PER_CHUNK)
         return fail(GDR_ERR_INVALID, "unknown local-backward launch form %d", form);
     return g_local_form.exchange(form);
+}
+
+int gdr_set_walk_levels(int levels)
+{
+    if (levels != GDR_WALK_AUTO && levels != GDR_WALK_ONE_LEVEL)
+        return fail(GDR_ERR_INVALID, "unknown walk form %d", levels);
+    return g_walk_levels.exchange(levels);
 }
 
 int gdr_version(void) { return 1; }

@@ -60,6 +60,19 @@ struct Inter {
     bf16* Rb;    // correction adjoint, ctile like R                 (16 KiB)
     // gate check (prep): one word per prep wave, OR of GATE_* bits   (16 B)
     uint32_t* flags;
+    // Two-level walks (regular batches whose one-level walks would leave
+    // most CUs idle): each walk is cut into nseg segments of seglen chunks
+    // (the last may be shorter). Per direction d (0 forward, 1 reverse):
+    //   seg_sum [d][nseg - 1][B*H][2][128][128] fp32: a segment's transfer
+    //           map Phi (entry state -> exit state, keys x keys), then its
+    //           exit state from a zero entry state E (keys x values), for
+    //           every segment but the last in walk order (index: the
+    //           segment's position among those);
+    //   seg_ent [d][nseg][B*H][128][128] fp32: each segment's entry state.
+    int nseg;        // 1: one serial walk
+    int64_t seglen;
+    float* seg_sum;
+    float* seg_ent;
 };
 
 // Gate-check bits prep records per (chunk, head) (gdr_gate_status).
@@ -95,9 +108,10 @@ struct Shape {
 struct SeqView {
     int64_t tok;     // token index (along T) of the sequence's first token
     int64_t len;     // its tokens
-    int64_t nchunk;  // its chunks
+    int64_t nchunk;  // its chunks (a segment view: the segment's)
     int64_t slot0;   // chunk slot of its chunk 0 (packed batches)
     int64_t n, hd;   // sequence (state entry) and head
+    int64_t c0;      // chunk 0 of the view within the sequence (a segment of a walk)
 };
 
 __host__ __device__ inline SeqView seq_view(const Shape& s, int64_t n, int64_t hd)
@@ -116,6 +130,15 @@ __host__ __device__ inline SeqView seq_view(const Shape& s, int64_t n, int64_t h
         v.slot0 = 0;
         v.nchunk = s.NT;
     }
+    v.c0 = 0;
+    return v;
+}
+
+// Chunks [c0, c0 + n) of a sequence view, seen as a sequence of their own.
+__host__ __device__ inline SeqView seg_view(SeqView v, int64_t c0, int64_t n)
+{
+    v.c0 += c0;
+    v.nchunk = n;
     return v;
 }
 
@@ -124,20 +147,21 @@ __host__ __device__ inline SeqView seq_view(const Shape& s, int64_t n, int64_t h
 // every head, reads and writes a few contiguous regions.
 __host__ __device__ inline int64_t seq_tile(const Shape& s, const SeqView& v, int64_t c)
 {
+    c += v.c0;
     return s.ctab ? (v.slot0 + c) * s.H + v.hd : c * (s.B * s.H) + v.n * s.H + v.hd;
 }
 
 // Valid rows of chunk c (64 except in a ragged last chunk).
 __host__ __device__ inline int seq_rows(const SeqView& v, int64_t c)
 {
-    const int64_t r = v.len - c * CH;
+    const int64_t r = v.len - (v.c0 + c) * CH;
     return r < CH ? (int)r : CH;
 }
 
 // Row index into [.., T, H, ..] token-major tensors of chunk c's first token.
 __host__ __device__ inline int64_t seq_tok0(const Shape& s, const SeqView& v, int64_t c)
 {
-    return (v.tok + c * CH) * s.H + v.hd;
+    return (v.tok + (v.c0 + c) * CH) * s.H + v.hd;
 }
 
 // What a per-chunk kernel needs of its (chunk, head): the tile, the row

@@ -43,11 +43,13 @@ namespace {
 constexpr int NVS = DVD / 16;  // 16-column value tiles per head
 
 // The chain a scan workgroup walks: sequence n (state entry), head hd, value
-// slice vs (NV consecutive value tiles), direction.
+// slice vs (NV consecutive value tiles), direction, and the segment of the
+// walk (two-level walks; 0 otherwise).
 struct Chain {
     int64_t n, hd;
     int vs;
     bool bwd;
+    int sg;
 };
 
 // Workgroups are dealt to the eight XCDs round-robin by index (block b runs
@@ -58,25 +60,29 @@ struct Chain {
 // launch J alternates forward / reverse; the (sequence, head) pairs follow
 // s.order (longest sequence first) in packed batches, so the longest walks
 // start first. Workgroups past the last group (the grid is rounded up to
-// whole rounds of eight groups) have no chain.
+// whole rounds of eight groups) have no chain. With nseg segments per walk,
+// a group is one segment of one walk, and consecutive groups are the
+// segments of one walk.
 __device__ __forceinline__ bool chain_of_block(const Shape& s, int nvs, int ndir, bool bwd1, int block,
-                                               Chain& ch)
+                                               Chain& ch, int nseg = 1)
 {
     const int x = block & 7, q = block >> 3;
     const int64_t J = (int64_t)(q / nvs) * 8 + x;
-    if (J >= s.NS * s.H * ndir) return false;
+    if (J >= s.NS * s.H * ndir * nseg) return false;
     ch.vs = q % nvs;
-    ch.bwd = ndir == 2 ? (J & 1) != 0 : bwd1;
-    const int64_t j = ndir == 2 ? J >> 1 : J;
+    ch.sg = (int)(J % nseg);
+    const int64_t J2 = J / nseg;
+    ch.bwd = ndir == 2 ? (J2 & 1) != 0 : bwd1;
+    const int64_t j = ndir == 2 ? J2 >> 1 : J2;
     const int64_t k = j / s.H;
     ch.hd = j % s.H;
     ch.n = s.order ? s.order[k] : k;
     return true;
 }
 
-unsigned scan_grid(const Shape& s, int nvs, int ndir)
+unsigned scan_grid(const Shape& s, int nvs, int ndir, int nseg = 1)
 {
-    return (unsigned)((s.NS * s.H * ndir + 7) / 8 * 8 * nvs);
+    return (unsigned)((s.NS * s.H * ndir * nseg + 7) / 8 * 8 * nvs);
 }
 
 // ---------------------------------------------------------------------------
@@ -137,13 +143,16 @@ __device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); 
 // Loader wave J (0..3): blocks J, J + 4, ... of one step into `slot`. The
 // block count is padded to a multiple of four by repeating the gn block
 // (same bytes to the same place); a gn block is two copies (fed_loads).
-template <bool BWD, int J, int NV, bool DEEP>
+// NOC: no C1 / C2 blocks (a walk of the homogeneous recurrence, which maps
+// an entry state to an exit state; see the two-level walks below).
+template <bool BWD, int J, int NV, bool DEEP, bool NOC>
 __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, uint8_t* slot)
 {
     using L = Fed<NV, DEEP>;
-    constexpr int NB = BWD ? L::NB_BWD : L::NB_FWD;
+    constexpr int NB = NOC ? 33 : BWD ? L::NB_BWD : L::NB_FWD;
     constexpr int NPAD = (NB + 3) / 4 * 4;
-    constexpr int E1 = 32 + 2 * NV, E2 = E1 + 4 * NV;  // ends of the C1 and C2 blocks
+    // ends of the C1 and C2 blocks
+    constexpr int E1 = NOC ? 32 : 32 + 2 * NV, E2 = NOC ? 32 : E1 + 4 * NV;
     const int l = lane_id();
     // A2 is the transpose of the other direction's A1: its frag tiles are
     // copied as they are and read transposed (ld_frag_t64x128)
@@ -195,28 +204,28 @@ __device__ __forceinline__ void fed_issue(const Inter& it, int64_t t, int vs, ui
 
 // Direct-to-LDS copies loader wave J issues per step: one per block, two
 // per gn block (the last block and the padding repeats of it).
-template <bool BWD, int J, int NV>
+template <bool BWD, int J, int NV, bool NOC>
 constexpr int fed_loads()
 {
-    constexpr int E = BWD ? 32 + 6 * NV : 32 + 2 * NV;  // blocks before gn
+    constexpr int E = NOC ? 32 : BWD ? 32 + 6 * NV : 32 + 2 * NV;  // blocks before gn
     constexpr int NPAD = (E + 1 + 3) / 4 * 4;
     int n = 0;
     for (int b = J; b < NPAD; b += 4) n += b < E ? 1 : 2;
     return n;
 }
 
-template <bool BWD, int J, int NV, bool OUT, typename T>
+template <bool BWD, int J, int NV, bool OUT, typename T, bool NOC>
 __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, const SeqView& sq, int vs,
                                            uint8_t* ring, bf16x8 (*xs)[64], T* o)
 {
     constexpr bool DEEP = NV == 1 && !OUT;
     using L = Fed<NV, DEEP>;
-    constexpr int NL = fed_loads<BWD, J, NV>();
+    constexpr int NL = fed_loads<BWD, J, NV, NOC>();
     const int NT = (int)sq.nchunk;  // >= 1
     auto issue = [&](int p) {
         const int pc = p < NT ? p : NT - 1;  // past the end: the last chunk again
         const int c = BWD ? NT - 1 - pc : pc;
-        fed_issue<BWD, J, NV, DEEP>(it, seq_tile(s, sq, c), vs, ring + (p % L::NSLOT) * L::SLOT);
+        fed_issue<BWD, J, NV, DEEP, NOC>(it, seq_tile(s, sq, c), vs, ring + (p % L::NSLOT) * L::SLOT);
     };
     if constexpr (!OUT) {
         constexpr int D = L::DEPTH;
@@ -310,10 +319,14 @@ __device__ __forceinline__ void fed_loader(const Shape& s, const Inter& it, cons
 
 // xs: the LDS exchange, NV x 4 state slabs then NV x 2 Z slabs of 64 x 16 B.
 // STORE: write the state before each step and Z (h, R or dh, Rb).
-template <bool BWD, int NV, bool STORE, bool DEEP>
-__device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, const Inter& it, float* fin,
-                                            const SeqView& sq, int64_t bh, int vs, const uint8_t* ring,
-                                            bf16x8 (*xs)[64])
+// init: the initial states ([.][128][128], entry bh; null: zero), or with
+// ident the identity (columns 16 (NV vs + u) + r of I). fin: where the final
+// states go (entry bh; null: nowhere). NOC: the homogeneous recurrence (no
+// C1 / C2 terms).
+template <bool BWD, int NV, bool STORE, bool DEEP, bool NOC>
+__device__ __forceinline__ void fed_compute(const Shape& s, const Inter& it, const float* init, bool ident,
+                                            float* fin, const SeqView& sq, int64_t bh, int vs,
+                                            const uint8_t* ring, bf16x8 (*xs)[64])
 {
     using L = Fed<NV, DEEP>;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -324,7 +337,6 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 
     bf16* Sout = BWD ? it.dh : it.h;
     bf16* Zout = BWD ? it.Rb : it.R;
-    const float* init = BWD ? in.dht : in.h0;
 
     // state: value tile NV vs + u, key rows 32 w + 16 m + 4 g + i, column 16 (NV vs + u) + r
     f32x4 S[NV][2];
@@ -333,9 +345,10 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                S[u][m][i] = init ? init[(bh * DKD + 32 * w + 16 * m + 4 * g + i) * DVD + 16 * (NV * vs + u) + r]
-                                  : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int row = 32 * w + 16 * m + 4 * g + i, col = 16 * (NV * vs + u) + r;
+                S[u][m][i] = ident ? (row == col ? 1.f : 0.f) : init ? init[(bh * DKD + row) * DVD + col] : 0.f;
+            }
 
     for (int p = 0; p < NT; ++p) {
         const int c = BWD ? NT - 1 - p : p;
@@ -369,7 +382,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
         bf16x4 z4[NV];
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
-            f32x4 z = unpack4(*(const bf16x4*)(slot + L::C1 + ((u * 4 + w) * 64 + l) * 8));
+            f32x4 z = NOC ? zero4() : unpack4(*(const bf16x4*)(slot + L::C1 + ((u * 4 + w) * 64 + l) * 8));
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) z = mfma(a1[ks], sf[u][ks], z);
             z4[u] = pack4(z);
@@ -399,7 +412,7 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
 #pragma unroll
             for (int u = 0; u < NV; ++u) {
                 f32x4 acc = {gv.x * S[u][m][0], gv.y * S[u][m][1], gv.z * S[u][m][2], gv.w * S[u][m][3]};
-                if (BWD) {
+                if (BWD && !NOC) {
                     const f32x4 y =
                         unpack4(*(const bf16x4*)(slot + L::C2 + ((u * 8 + 2 * w + m) * 64 + l) * 8));
 #pragma unroll
@@ -422,29 +435,74 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inputs& in, co
     }
 }
 
-template <bool BWD, int NV, bool OUT, typename T, bool STORE>
-__device__ __forceinline__ void fed_body(const Shape& s, const Inputs& in, const Inter& it, float* fin,
-                                         const Chain& ch, uint8_t* ring, bf16x8 (*xs)[64], T* o)
+template <bool BWD, int NV, bool OUT, typename T, bool STORE, bool NOC = false>
+__device__ __forceinline__ void fed_body(const Shape& s, const Inter& it, const SeqView& sq, const float* init,
+                                         bool ident, float* fin, int64_t bh, int vs, uint8_t* ring,
+                                         bf16x8 (*xs)[64], T* o)
 {
-    const SeqView sq = seq_view(s, ch.n, ch.hd);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (sq.nchunk == 0 && w >= 4) return;  // an empty sequence: no steps, no barriers
+    if (sq.nchunk <= 0 && w >= 4) return;  // an empty sequence: no steps, no barriers
     switch (w) {
-    case 4: fed_loader<BWD, 0, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
-    case 5: fed_loader<BWD, 1, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
-    case 6: fed_loader<BWD, 2, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
-    case 7: fed_loader<BWD, 3, NV, OUT, T>(s, it, sq, ch.vs, ring, xs, o); break;
+    case 4: fed_loader<BWD, 0, NV, OUT, T, NOC>(s, it, sq, vs, ring, xs, o); break;
+    case 5: fed_loader<BWD, 1, NV, OUT, T, NOC>(s, it, sq, vs, ring, xs, o); break;
+    case 6: fed_loader<BWD, 2, NV, OUT, T, NOC>(s, it, sq, vs, ring, xs, o); break;
+    case 7: fed_loader<BWD, 3, NV, OUT, T, NOC>(s, it, sq, vs, ring, xs, o); break;
     default:
-        fed_compute<BWD, NV, STORE, NV == 1 && !OUT>(s, in, it, fin, sq, ch.n * s.H + ch.hd, ch.vs, ring, xs);
+        fed_compute<BWD, NV, STORE, NV == 1 && !OUT, NOC>(s, it, init, ident, fin, sq, bh, vs, ring, xs);
         break;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Two-level walks. With few walks (small B * H) a serial walk over every
+// chunk leaves most CUs idle, while its step time is bound by latency. The
+// state recurrence is affine in the state: a walk over chunks [a, b) maps
+// its entry state S to Phi S + E, with Phi the product of the homogeneous
+// steps (the forward walk's S <- diag(gn) S - Kt^T W S, the reverse walk's
+// transpose) and E the exit state from S = 0 (ReWY paper Sec. 2.1: the
+// scan is serial across chunks; the chunk-affine composition of such maps
+// is the two-level form). The walk is cut into segments:
+//   1. for every segment but the last in walk order, Phi (the walk from the
+//      identity without the C terms) and E (the walk from zero), all
+//      segments at once (scan_sum_kernel);
+//   2. the entry state of every segment by S <- Phi S + E through the
+//      segments in walk order, in fp32 (scan_combine_kernel);
+//   3. every segment's own walk from its entry state, storing what the
+//      one-level walk stores (scan_fed_kernel with it.nseg segments).
+// Steps 1 and 3 each take a segment's length in serial steps instead of the
+// whole walk's.
+
+// Chunks of segment sg of a walk over nchunk chunks.
+__device__ __forceinline__ SeqView segment_of(const Inter& it, const SeqView& sq, int sg)
+{
+    const int64_t c0 = sg * it.seglen, left = sq.nchunk - c0;
+    return seg_view(sq, c0, left < it.seglen ? (left > 0 ? left : 0) : it.seglen);
+}
+
+// One chain of a walk launch: its segment (two-level walks), where its
+// initial state comes from and where its final state goes.
+template <bool BWD, int NV, bool OUT, typename T, bool STORE>
+__device__ __forceinline__ void walk_chain(const Shape& s, const Inputs& in, const Inter& it, float* fin,
+                                           const Chain& ch, uint8_t* ring, bf16x8 (*xs)[64], T* o)
+{
+    SeqView sq = seq_view(s, ch.n, ch.hd);
+    const float* init = BWD ? in.dht : in.h0;
+    if (it.nseg > 1) {
+        sq = segment_of(it, sq, ch.sg);
+        const bool first = BWD ? ch.sg == it.nseg - 1 : ch.sg == 0;
+        const bool last = BWD ? ch.sg == 0 : ch.sg == it.nseg - 1;
+        if (!first) init = it.seg_ent + ((int64_t)(BWD ? 1 : 0) * it.nseg + ch.sg) * s.NS * s.H * (DKD * DVD);
+        if (!last) fin = nullptr;
+    }
+    fed_body<BWD, NV, OUT, T, STORE>(s, it, sq, init, false, fin, ch.n * s.H + ch.hd, ch.vs, ring, xs, o);
 }
 
 // Backward launches (OUT = false): ndir = 2 runs forward and reverse chains
 // side by side (the reverse scan reads only prep's operands, not the
 // forward states); ndir = 1 the reverse scan alone. Only the reverse chains
 // write fin (dh0). The forward launch (OUT = true, ndir = 1) writes the
-// output o and fin (ht), and h and R when STORE (full save).
+// output o and fin (ht), and h and R when STORE (full save). With
+// it.nseg > 1 each chain walks one segment (step 3 above).
 template <int NV, bool OUT, typename T, bool STORE>
 __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter it, float* fin, int ndir, T* o)
 {
@@ -452,12 +510,111 @@ __global__ __launch_bounds__(512) void scan_fed_kernel(Shape s, Inputs in, Inter
     __shared__ __attribute__((aligned(16))) uint8_t ring[L::NSLOT * L::SLOT];
     __shared__ bf16x8 xs[L::XCH][64];
     Chain ch;
-    if (!chain_of_block(s, NVS / NV, ndir, !OUT, blockIdx.x, ch)) return;
+    if (!chain_of_block(s, NVS / NV, ndir, !OUT, blockIdx.x, ch, it.nseg)) return;
     if constexpr (OUT) {
-        fed_body<false, NV, true, T, STORE>(s, in, it, fin, ch, ring, xs, o);
+        walk_chain<false, NV, true, T, STORE>(s, in, it, fin, ch, ring, xs, o);
     } else {
-        if (ch.bwd) fed_body<true, NV, false, T, STORE>(s, in, it, fin, ch, ring, xs, o);
-        else fed_body<false, NV, false, T, STORE>(s, in, it, nullptr, ch, ring, xs, o);
+        if (ch.bwd) walk_chain<true, NV, false, T, STORE>(s, in, it, fin, ch, ring, xs, o);
+        else walk_chain<false, NV, false, T, STORE>(s, in, it, nullptr, ch, ring, xs, o);
+    }
+}
+
+// Step 1: chains (walk, summarized segment, slice vs < 16). Slices 0..7
+// walk the homogeneous recurrence from columns 16 vs .. 16 vs + 15 of the
+// identity (Phi), slices 8..15 the full recurrence from zero (E, value
+// columns 16 (vs - 8) ..). The forward walk summarizes segments
+// 0 .. nseg - 2, the reverse walk 1 .. nseg - 1 (its last in walk order is
+// segment 0); a segment's summary sits at its position among those.
+__global__ __launch_bounds__(512) void scan_sum_kernel(Shape s, Inter it, int ndir, int bwd1)
+{
+    using L = Fed<1, true>;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[L::NSLOT * L::SLOT];
+    __shared__ bf16x8 xs[L::XCH][64];
+    Chain ch;
+    if (!chain_of_block(s, 2 * NVS, ndir, bwd1 != 0, blockIdx.x, ch, it.nseg - 1)) return;
+    const SeqView sq = segment_of(it, seq_view(s, ch.n, ch.hd), ch.bwd ? ch.sg + 1 : ch.sg);
+    const bool phi = ch.vs < NVS;
+    const int vs = ch.vs & (NVS - 1);
+    float* fin = it.seg_sum + (((int64_t)(ch.bwd ? 1 : 0) * (it.nseg - 1) + ch.sg) * s.NS * s.H +
+                               ch.n * s.H + ch.hd) * 2 * (DKD * DVD) + (phi ? 0 : DKD * DVD);
+    bf16* const no = nullptr;
+    if (ch.bwd) {
+        if (phi) fed_body<true, 1, false, bf16, false, true>(s, it, sq, nullptr, true, fin, 0, vs, ring, xs, no);
+        else fed_body<true, 1, false, bf16, false, false>(s, it, sq, nullptr, false, fin, 0, vs, ring, xs, no);
+    } else {
+        if (phi) fed_body<false, 1, false, bf16, false, true>(s, it, sq, nullptr, true, fin, 0, vs, ring, xs, no);
+        else fed_body<false, 1, false, bf16, false, false>(s, it, sq, nullptr, false, fin, 0, vs, ring, xs, no);
+    }
+}
+
+// Step 2: one workgroup per (state entry bh, direction, 16 value columns).
+// A segment's Phi (64 KiB) goes to LDS, read from global memory a segment
+// ahead into registers; S <- Phi S + E runs on the fp32 MFMA (wave w: state
+// rows 32 w .. 32 w + 31, all 16 columns), so the chained entry states are
+// exact fp32 products.
+__global__ __launch_bounds__(256) void scan_combine_kernel(Shape s, Inputs in, Inter it, int ndir, int bwd1)
+{
+    const int64_t bh = blockIdx.x, NSH = s.NS * s.H;
+    const bool bwd = ndir == 2 ? blockIdx.y == 1 : bwd1 != 0;
+    const int64_t d = bwd ? 1 : 0;
+    const int c0 = 16 * blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+    __shared__ float S[DKD][16];
+    __shared__ __attribute__((aligned(16))) float P[DKD][DKD + 4];  // padded rows: conflict-free operand reads
+    const float* init = bwd ? in.dht : in.h0;
+    {
+        const int row = tid >> 1, cb = (tid & 1) * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S[row][cb + j] = init ? init[(bh * DKD + row) * DVD + c0 + cb + j] : 0.f;
+    }
+    const int nseg = it.nseg;
+    // the k-th segment summarized in walk order: its Phi and E
+    auto summary = [&](int k) -> const float* {
+        const int cur = bwd ? nseg - 1 - k : k;
+        const int pos = bwd ? cur - 1 : cur;  // its position among the summarized segments
+        return it.seg_sum + ((d * (nseg - 1) + pos) * NSH + bh) * 2 * (DKD * DVD);
+    };
+    float4 pv[16];
+    auto load_phi = [&](int k) {
+        const float* phi = summary(k);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) pv[u] = *(const float4*)(phi + (u * 256 + tid) * 4);
+    };
+    if (nseg > 1) load_phi(0);
+    for (int k = 0; k + 1 < nseg; ++k) {
+        const int cur = bwd ? nseg - 1 - k : k, nxt = bwd ? cur - 1 : cur + 1;
+        const float* E = summary(k) + DKD * DVD;
+        // accumulators start from E: lane (r, g) element i is row 16 mt + 4 g + i, column r.
+        // (E is read before the next Phi is requested: loads complete in
+        // order, so the wait for E then does not wait for that Phi.)
+        f32x4 acc[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][i] = E[(32 * w + 16 * m + 4 * g + i) * DVD + c0 + r];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = (u * 256 + tid) * 4;
+            *(float4*)&P[e / DKD][e % DKD] = pv[u];
+        }
+        if (k + 2 < nseg) load_phi(k + 1);  // the next segment's Phi, while this one runs
+        __syncthreads();  // P and S complete
+#pragma unroll 8
+        for (int ks = 0; ks < DKD / 4; ++ks) {
+            const float b = S[4 * ks + g][r];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) acc[m] = mfma4(P[32 * w + 16 * m + r][4 * ks + g], b, acc[m]);
+        }
+        __syncthreads();  // every read of S and P is done
+        float* ent = it.seg_ent + ((d * nseg + nxt) * NSH + bh) * (DKD * DVD);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 32 * w + 16 * m + 4 * g + i;
+                S[row][r] = acc[m][i];
+                ent[row * DVD + c0 + r] = acc[m][i];
+            }
     }
 }
 
@@ -483,27 +640,58 @@ namespace {
 
 // One workgroup per CU fits (LDS); NV = 2 when NV = 1 would need more than
 // one round of workgroups.
-bool wide(const Shape& s, int ndir) { return s.NS * s.H * NVS * ndir > cu_count(); }
+bool wide(const Shape& s, int ndir, int nseg) { return s.NS * s.H * NVS * ndir * nseg > cu_count(); }
 
-hipError_t launch_fed(const Shape& s, const Inputs& in, const Inter& it, float* dh0, int ndir,
+// Steps 1 and 2 of the two-level walks (a no-op for one-level walks).
+hipError_t two_level_prefix(const Shape& s, const Inputs& in, const Inter& it, int ndir, bool bwd1,
+                            hipStream_t st)
+{
+    if (it.nseg <= 1) return hipSuccess;
+    scan_sum_kernel<<<scan_grid(s, 2 * NVS, ndir, it.nseg - 1), 512, 0, st>>>(s, it, ndir, bwd1 ? 1 : 0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scan_combine_kernel<<<dim3((unsigned)(s.NS * s.H), (unsigned)ndir, NVS), 256, 0, st>>>(s, in, it, ndir,
+                                                                                       bwd1 ? 1 : 0);
+    return hipGetLastError();
+}
+
+// The walk launches' view of it: at least one segment.
+Inter walk_args(const Inter& it)
+{
+    Inter jt = it;
+    if (jt.nseg < 1 || !jt.seg_sum || !jt.seg_ent) jt.nseg = 1;
+    return jt;
+}
+
+hipError_t launch_fed(const Shape& s, const Inputs& in, const Inter& it0, float* dh0, int ndir,
                       hipStream_t st)
 {
-    if (wide(s, ndir))
-        scan_fed_kernel<2, false, bf16, true><<<scan_grid(s, NVS / 2, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
+    const Inter it = walk_args(it0);
+    hipError_t e = two_level_prefix(s, in, it, ndir, true, st);
+    if (e != hipSuccess) return e;
+    const int ns = it.nseg;
+    if (wide(s, ndir, ns))
+        scan_fed_kernel<2, false, bf16, true><<<scan_grid(s, NVS / 2, ndir, ns), 512, 0, st>>>(s, in, it, dh0, ndir,
+                                                                                             nullptr);
     else
-        scan_fed_kernel<1, false, bf16, true><<<scan_grid(s, NVS, ndir), 512, 0, st>>>(s, in, it, dh0, ndir, nullptr);
+        scan_fed_kernel<1, false, bf16, true><<<scan_grid(s, NVS, ndir, ns), 512, 0, st>>>(s, in, it, dh0, ndir,
+                                                                                         nullptr);
     return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_fed_out(const Shape& s, const Inputs& in, const Inter& it, T* o, float* ht, hipStream_t st)
+hipError_t launch_fed_out(const Shape& s, const Inputs& in, const Inter& it0, T* o, float* ht, hipStream_t st)
 {
-    const unsigned g2 = scan_grid(s, NVS / 2, 1), g1 = scan_grid(s, NVS, 1);
+    const Inter it = walk_args(it0);
+    hipError_t e = two_level_prefix(s, in, it, 1, false, st);
+    if (e != hipSuccess) return e;
+    const int ns = it.nseg;
+    const unsigned g2 = scan_grid(s, NVS / 2, 1, ns), g1 = scan_grid(s, NVS, 1, ns);
     if (it.h) {  // full save: h and R too
-        if (wide(s, 1)) scan_fed_kernel<2, true, T, true><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
+        if (wide(s, 1, ns)) scan_fed_kernel<2, true, T, true><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
         else scan_fed_kernel<1, true, T, true><<<g1, 512, 0, st>>>(s, in, it, ht, 1, o);
     } else {
-        if (wide(s, 1)) scan_fed_kernel<2, true, T, false><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
+        if (wide(s, 1, ns)) scan_fed_kernel<2, true, T, false><<<g2, 512, 0, st>>>(s, in, it, ht, 1, o);
         else scan_fed_kernel<1, true, T, false><<<g1, 512, 0, st>>>(s, in, it, ht, 1, o);
     }
     return hipGetLastError();

@@ -294,6 +294,23 @@ int gdr_gate_status(const gdr_desc* d, int64_t n_seq, const void* scratch, size_
 typedef enum { GDR_LOCAL_PERSISTENT = 0, GDR_LOCAL_PER_CHUNK = 1 } gdr_local_form;
 int gdr_set_local_form(int form);
 
+/* Form of the state walks (process-wide; set it between calls, not during
+ * one). The walks are serial over a sequence's chunks (Sec. 2.1). A walk
+ * launch over few (sequence, head) pairs leaves most compute units idle;
+ * GDR_WALK_AUTO (the default) then cuts each walk of a regular batch into
+ * segments: the map from a segment's entry state to its exit state (its
+ * homogeneous part, keys x keys, and its exit state from zero) is formed for
+ * all segments at once, the segments' entry states are chained through those
+ * maps in fp32, and every segment then walks from its own entry state. This
+ * applies when the one-level launch would fill at most a quarter of 256
+ * compute units and the walk is long enough for 3 or more segments of at
+ * least 8 chunks (for example (1, 8192, 4)). GDR_WALK_ONE_LEVEL walks every
+ * sequence start to end. Both give the same results up to rounding; the
+ * workspace is sized for the automatic form either way.
+ * Returns the previous form, or GDR_ERR_INVALID for an unknown one. */
+typedef enum { GDR_WALK_AUTO = 0, GDR_WALK_ONE_LEVEL = 1 } gdr_walk_levels;
+int gdr_set_walk_levels(int levels);
+
 const char* gdr_status_string(int status);
 const char* gdr_last_error(void);
 int gdr_version(void);

@@ -62,6 +62,40 @@ def test_workspace_sizes():
     assert sc == 2048 * (16 + max(2 * T64x128 + T64x64, 2 * T64x128 + 2 * T128x128 + T64x64))
 
 
+def test_workspace_two_level_walk_buffers():
+    """A regular batch whose one-level walk launch would fill at most a
+    quarter of 256 CUs, with walks long enough for 4 or more segments of at
+    least 20 chunks, walks in segments. Its workspace adds, for both
+    directions, each summarized segment's transfer map and zero-entry exit
+    state (2 x 64 KiB per state entry) and each segment's entry state (64 KiB
+    per state entry). At (1, 8192, 2) the recompute backward walks both
+    directions in 5 segments; at (1, 8192, 4) the full-save backward's reverse
+    walk takes 5, while the recompute pair would get only 3 and stays one-level
+    (the forward's 5-segment buffers fit in the backward's larger scratch)."""
+    T64x128, T128x128, T64x64, GN = 16384, 32768, 8192, 512
+    state = 128 * 128 * 4
+
+    def seg_bytes(nseg, nsh):
+        return 2 * (nseg - 1) * nsh * 2 * state + 2 * nseg * nsh * state
+
+    per = 2 * T64x128 + GN + T64x128 + 2 * T64x64 + T128x128 + T64x128 \
+        + T64x128 + T128x128 + T128x128 + T64x128 + 16
+    rc, sv, sc = _ws(_desc(T=8192, H=2), 0)
+    assert rc == 0 and sv == 0
+    assert sc == 256 * per + seg_bytes(5, 2)
+    rc, sv, sc = _ws(_desc(T=8192, H=4), 1)
+    assert rc == 0 and sv == 512 * 115200
+    assert sc == 512 * (16 + 2 * T64x128 + 2 * T128x128 + T64x64) + seg_bytes(5, 4)
+    rc, sv, sc = _ws(_desc(T=8192, H=4), 0)
+    assert rc == 0 and sc == 512 * per
+    # too short for four segments of twenty chunks: one level
+    rc, sv, sc = _ws(_desc(T=4096, H=4), 1)
+    assert rc == 0 and sc == 256 * (16 + 2 * T64x128 + 2 * T128x128 + T64x64)
+    # sixteen heads fill the chip with one-level walks
+    rc, sv, sc = _ws(_desc(T=8192, H=16), 0)
+    assert rc == 0 and sc == 2048 * per
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(DK=192), -2), (dict(DV=1025), -2), (dict(DK=192, DV=160), -2), (dict(DK=0), -1), (dict(DV=-3), -1), (dict(C=32), -2),
     (dict(gate=5), -1), (dict(gate=4), -1), (dict(dtype=7), -1), (dict(B=-1), -1),
@@ -133,15 +167,17 @@ def test_packed_workspace_counts_slots_and_tables():
     chunks per head; the workspace holds that many tiles (each tile kind in
     its own 256-byte-aligned block, as for a regular row of that many chunks)
     plus the offsets, the per-sequence table, the per-slot table and the
-    longest-first sequence order."""
+    longest-first sequence order. (Sixteen heads: the regular row's walks are
+    then one-level, with no segment buffers; packed batches always walk in
+    one level.)"""
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for T, n in ((8192, 7), (100, 3), (64, 0), (1, 1)):
         for pol in (0, 1):
             nslot = (T + 63) // 64 + n
-            rc, sv, sc = _ws_varlen(_desc(T=T, H=4), n, pol)
+            rc, sv, sc = _ws_varlen(_desc(T=T, H=16), n, pol)
             assert rc == 0
             # a regular row with nslot chunks has exactly the tile part
-            rc, sv_r, sc_r = _ws(_desc(T=64 * nslot, H=4), pol)
+            rc, sv_r, sc_r = _ws(_desc(T=64 * nslot, H=16), pol)
             assert rc == 0
             assert sv == sv_r
             assert sc == sc_r + al(8 * (n + 1)) + al(8 * n) + al(8 * nslot) + al(4 * n)

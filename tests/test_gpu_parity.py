@@ -694,3 +694,48 @@ def test_deltanet_packed_narrow_with_tail():
         got = tl.run_gpu_packed(x, pol, nogate=True)
         assert "dg" not in got
         _report(f"deltanet/packed/80x112/{pol}", tl.compare_packed(got, x))
+
+
+# ------------------------------------------------------- two-level walks
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,T,H,gate,dtype", [
+    (1, 8192, 4, "scalar", "bf16"),   # forward and full-save reverse 5 segments; recompute pair one level
+    (1, 6144, 2, "vector", "bf16"),   # 4 segments of 24 chunks, every launch
+    (2, 7000, 1, "scalar", "fp32"),   # ragged last chunk, 5 segments of at most 22 chunks
+])
+def test_two_level_walks_match_oracle_and_one_level(B, T, H, gate, dtype):
+    """Walks cut into segments (entry-to-exit maps formed for all segments at
+    once, entry states chained through them, then every segment walked from
+    its own entry state) against the oracle, with nonzero h0 and dht, under
+    both policies; and against the same calls with one-level walks."""
+    _need_gpu()
+    import delta_rule_linear_gdr_amd as gdr
+    x = make_inputs(B, T, H, gate=gate, dtype=dtype, seed=71, gate_mean=3.0 if gate == "vector" else 4.0,
+                    h0_std=0.1, dht_std=0.1)
+    heads = None if B * H <= 2 else [(0, 0), (0, H - 1)]
+    for pol in ("recompute", "full_save"):
+        two = tl.run_gpu(x, pol)
+        prev = gdr.set_walk_levels("one")
+        try:
+            one = tl.run_gpu(x, pol)
+        finally:
+            gdr.set_walk_levels(prev)
+        _report(f"two-level {B}x{T}x{H}/{gate}/{dtype}/{pol}", tl.compare(two, x, heads=heads))
+        tl.compare(one, x, heads=heads)
+        # the two forms agree far inside the bar
+        for n in two:
+            den = np.linalg.norm(one[n])
+            if den > 0:
+                assert np.linalg.norm(two[n] - one[n]) / den < 4e-3, n
+
+
+@pytest.mark.gpu
+def test_two_level_walks_deltanet_and_seven_product():
+    """Two-level walks with no gate and with the seven-product backward."""
+    _need_gpu()
+    x = make_inputs(1, 6144, 2, gate="scalar", dtype="bf16", seed=72, h0_std=0.1, dht_std=0.1)
+    xn = dict(x)
+    xn["g"] = np.zeros_like(x["g"])
+    _report("two-level deltanet", tl.compare(tl.run_gpu(xn, nogate=True), xn))
+    _report("two-level wy7", tl.compare(tl.run_gpu(x, "full_save", wy7=True), x))
