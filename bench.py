@@ -209,8 +209,8 @@ def shape_sweep(gdr, to_dev, make_runner, time_steps, graph_ms, args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported",
-              file=sys.stderr)
+        print(f"bench.py: the operator runs on one GPU (it has no multi-GPU path); --gpus {args.gpus} "
+              "is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
     import delta_rule_linear_gdr_amd as gdr
@@ -373,8 +373,8 @@ def main():
 
     # ---- headline: GDN backward, recompute policy ----
     # The device is first warmed for at least 2 s, as in the pages' protocol,
-    # followed by one untimed pass of the timing loop itself: measured on the
-    # box, the first timed pass after warm-up runs about 10% slow whatever is
+    # followed by one untimed pass of the timing loop itself: measured on an
+    # MI355X, the first timed pass after warm-up runs about 10% slow whatever is
     # timed, the later ones agree to 1%. A step is one eager call (its three
     # kernels); the same call replayed from a HIP graph is reported beside it.
     t0 = time.perf_counter()

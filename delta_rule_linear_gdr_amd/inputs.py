@@ -76,7 +76,7 @@ class Workload:
                            self.seed, self.gate_mean, self.h0_std, self.dht_std)
 
 
-# The five workloads of the build: GDN at (1,512,4) fp32, (1,2048,16) and
+# The parity and benchmark workloads: GDN at (1,512,4) fp32, (1,2048,16) and
 # (1,8192,16) bf16; KDA at (2,2048,16) and (1,8192,16) bf16 with h0 ~ 0.1 N(0,1);
 # and GDN2 at the headline shape, drawn like KDA's with both gates.
 # The six (B, T, H) shapes of the pages' evaluation (Eq. 4 of the paper page,
