@@ -86,3 +86,18 @@ def test_noalloc_equals_gdr_bwd_on_two_calls():
         res = {n: t.float().cpu().numpy().astype(np.float64) for n, t in got.items()}
         errs = tl.compare(res, x, names=("dq", "dk", "dv", "dg", "dbeta", "dh0"))
         print(f"[noalloc] call {i}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+
+
+def test_noalloc_with_two_level_walks():
+    """A problem whose recompute backward walks in segments, (1, 8192, 2):
+    the segment summaries and entry states live in the fixed array too, and
+    the result equals gdr_bwd's bit for bit."""
+    _need_gpu()
+    import torch
+    x = make_inputs(1, 8192, 2, gate="scalar", dtype="bf16", seed=13, gate_mean=4.0,
+                    h0_std=0.1, dht_std=0.1)
+    print(f"[noalloc] two-level: {x['q'].shape} recompute", flush=True)
+    ref, got = _backward_pair(x, "recompute")
+    for n in ref:
+        assert torch.isfinite(ref[n]).all(), n
+        assert torch.equal(ref[n], got[n]), f"{n} differs"
