@@ -821,6 +821,19 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     };
     if constexpr (VEC) {
         for (int x = w; x < 40; x += NW) item2a(x);
+    } else if constexpr (PF) {
+        // Waves w and w + 4 share a SIMD, and the older one wins its issue
+        // slots: waves 4..7 reach every barrier 1.4-2.4k cycles after waves
+        // 0..3 (per-wave timestamps). So waves 0..3 take six of the 40 items
+        // and waves 4..7 four (bwd_local at (1,8192,16): 135.7 -> 131.5 us;
+        // seven against three: 134 us).
+        if (w < 4) {
+#pragma unroll
+            for (int u = 0; u < 6; ++u) item2a(w + 4 * u);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) item2a(24 + (w - 4) + 4 * u);
+        }
     } else {
 #pragma unroll
         for (int u = 0; u < 40 / NW; ++u) item2a(w + NW * u);
