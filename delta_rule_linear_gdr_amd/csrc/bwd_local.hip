@@ -842,22 +842,27 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     lds_barrier();  // consumer A operands complete
 
     // ---- 2b. Gbar_n extra term: sum_j exp(G_n - G_j) k_j Ktb_j + gam_n rowsum(h o dh) ----
+    // The vector gate needs it first (its dg suffix sum starts from it). The
+    // scalar gate needs it only at the end of the chunk, so phase 3, which
+    // forms the same Kb products, accumulates the sum there instead.
     float colsum = 0.f;
+    float extra = 0.f;
+    if constexpr (VEC) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        f32x4 Kb = zero4();
+        for (int m = 0; m < 4; ++m) {
+            f32x4 Kb = zero4();
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) Kb = mfma(lR[(m * 4 + sl) * 64 + l], dhF[sl], Kb);
+            for (int sl = 0; sl < 4; ++sl) Kb = mfma(lR[(m * 4 + sl) * 64 + l], dhF[sl], Kb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ks = m >> 1, sl = 4 * (m & 1) + e;
-            float kv = (float)B0[ks][sl];
-            if (VEC) kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - cen(m));
-            colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
+            for (int e = 0; e < 4; ++e) {
+                const int ks = m >> 1, sl = 4 * (m & 1) + e;
+                const float kv = ((float)B0[ks][sl] + (float)lo_get(0 * 2 + ks)[sl]) * __expf(Gt(m, e) - cen(m));
+                colsum += __expf(Gnf - Gt(m, e)) * kv * Kb[e];
+            }
         }
+        colsum = sum_rows(colsum);
+        extra = colsum + __expf(Gnf) * sExtra[f];
     }
-    colsum = sum_rows(colsum);
-    const float extra = colsum + __expf(Gnf) * sExtra[f];
 
     // ---- 3. per token tile, last to first: producer and state-direct terms,
     //      the four consumer products, chain rules, dq / dk, the per-token
@@ -992,6 +997,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                 kv = (kv + (float)lo_get(0 * 2 + ks)[sl]) * al;
                 qv = (qv + (float)lo_get(1 * 2 + ks)[sl]) * ze;
             }
+            if (!VEC) colsum += kt * kv * Kb[e];  // the Gbar_n term (phase 2b)
             const float eb = -E[e];  // Eb_dir = -P h^T
             float dq = gam * Qb[e];
             float dk = bt * gam * eb + kt * Kb[e];
@@ -1088,6 +1094,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 
     // ---- 4. dbeta (wave 1); scalar gate: dg (wave 0), side by side ----
     if (!VEC) {
+        colsum = sum_rows(colsum);
+        extra = colsum + __expf(Gnf) * sExtra[f];
         const float ex = sum16(extra);
         if (l == 0) sEx[w] = ex;
     }
