@@ -49,7 +49,9 @@
 // gradient accumulators stay in that wave's registers):
 //   1. P^T = Rb^T A from the Rb accumulator tiles (no transpose needed);
 //      dv and <P, v> from it; P, R, dO fragments (contraction over values)
-//      into LDS; h, dh fragments and the rowsum of h o dh in registers;
+//      into LDS; h, dh fragments (read as stored: the scans write them as
+//      ttiles, whose lane pieces pair up into frag slabs) and the rowsum
+//      of h o dh in registers;
 //      K, Q in accumulator order through K * I (exact).
 //   2. D, D^T, Hb, Hb^T tiles (contraction over values) into LDS as the
 //      A operands of the Gram / matrix-intra products; Eb_dir, Qgb, Ktb.
@@ -77,10 +79,10 @@ __device__ __forceinline__ void st_half(bf16x8* buf, int tile, int half, const b
 }
 
 // Prefetch of h and dh (persistent form): wave w copies the sixteen
-// fragments it reads itself -- ctiles vt * 8 + w (vt = 0..7) of h, then of
-// dh, 512 bytes each -- into its own 8 KiB staging area, two ctiles per
-// 16-byte-per-lane direct-to-LDS load. A ctile is copied verbatim, so lane
-// l's four elements of ctile vt land at entry vt * 64 + l (h) and
+// fragments it reads itself -- ttiles vt * 8 + w (vt = 0..7) of h, then of
+// dh, 512 bytes each -- into its own 8 KiB staging area, two tiles per
+// 16-byte-per-lane direct-to-LDS load. A tile is copied verbatim, so lane
+// l's four elements of tile vt land at entry vt * 64 + l (h) and
 // 512 + vt * 64 + l (dh) of the area.
 //
 // The loads are issued from inline assembly, which the compiler's wait
@@ -509,7 +511,6 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     };
 
     const bf16x8 Ip0k = ident_pi(0, lx);
-    const bf16x8 Ipw = ident_pi(w & 1, lx);
     const bf16x4 z4 = {};
 
     if constexpr (SROW) {
@@ -596,29 +597,20 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     }
     bf16x8 hF[4], dhF[4];
     {
-        float hdp[4] = {0.f, 0.f, 0.f, 0.f};
-        f32x4 Ch[8], Cd[8];
+        // ttiles: lane (r, g) holds h[key 16 w + r][val 16 vt + 4 g + e], so
+        // value tiles 2 sl and 2 sl + 1 side by side are frag slab sl
+        float hdp = 0.f;
 #pragma unroll
-        for (int vt = 0; vt < 8; ++vt) {
-            // lane: h[key 16 w + 4 g + e][val 16 vt + r]
-            const bf16x4 hv = hq[vt];
-            const bf16x4 dv4 = dhq[vt];
+        for (int vt = 0; vt < 8; ++vt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) hdp[e] += (float)hv[e] * (float)dv4[e];
-            // lane: h[key 16 w + r][val 16 vt + 4 g + e]
-            Ch[vt] = mfma((w & 1) ? cat8(z4, hv) : cat8(hv, z4), Ipw, zero4());
-            Cd[vt] = mfma((w & 1) ? cat8(z4, dv4) : cat8(dv4, z4), Ipw, zero4());
-        }
+            for (int e = 0; e < 4; ++e) hdp += (float)hq[vt][e] * (float)dhq[vt][e];
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-            hF[sl] = pack_pi(Ch[2 * sl], Ch[2 * sl + 1]);
-            dhF[sl] = pack_pi(Cd[2 * sl], Cd[2 * sl + 1]);
+            hF[sl] = cat8(hq[2 * sl], hq[2 * sl + 1]);
+            dhF[sl] = cat8(dhq[2 * sl], dhq[2 * sl + 1]);
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float x = sum16(hdp[e]);
-            if (r == 0) sExtra[16 * w + 4 * g + e] = x;
-        }
+        hdp = sum_rows(hdp);  // all 128 values of key 16 w + r
+        if (g == 0) sExtra[16 * w + r] = hdp;
     }
     // ---- 1d. K and Q in accumulator order (tok 16 m + 4 g + e, key f) ----
     f32x4 KC[4], QC[4];

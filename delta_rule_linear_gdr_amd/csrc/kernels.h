@@ -17,6 +17,11 @@
 //        nt * (M / 16) + mt, 64 lanes x 4 bf16 = 512 B per tile. Lane (r, g)
 //        element i holds X[16 mt + 4 g + i][16 nt + r]. A column slice of
 //        the matrix (fixed nt) is contiguous.
+//  ttile (M x N): a ctile's transpose within each tile, same tile order and
+//        size. Lane (r, g) element i holds X[16 mt + r][16 nt + 4 g + i], so
+//        the pieces of tiles (nt, mt) and (nt + 1, mt) of one lane, side by
+//        side, are a frag slab of X (M = rows 16 mt.., K = columns 16 nt..
+//        + 31 in pik order) with no data movement between lanes.
 //  plain: row-major.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -54,9 +59,9 @@ struct Inter {
     // chunk-local backward inputs
     bf16* AT;    // A^T = (I+L)^-T  frag  M=64 tok i, K=64 tok j (8 KiB)
     bf16* Af;    // A             frag  M=64 tok i, K=64 tok j (8 KiB)
-    bf16* h;     // state at chunk start   ctile M=128 key, N=128 val (32 KiB)
+    bf16* h;     // state at chunk start   ttile M=128 key, N=128 val (32 KiB)
     bf16* R;     // correction             ctile M=64 tok,  N=128 val (16 KiB)
-    bf16* dh;    // state adjoint at chunk end, ctile like h         (32 KiB)
+    bf16* dh;    // state adjoint at chunk end, ttile like h         (32 KiB)
     bf16* Rb;    // correction adjoint, ctile like R                 (16 KiB)
     // gate check (prep): one word per prep wave, OR of GATE_* bits   (16 B)
     uint32_t* flags;

@@ -354,20 +354,25 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inter& it, con
         const int c = BWD ? NT - 1 - p : p;
         const int64_t t = seq_tile(s, sq, c);
         const uint8_t* slot = ring + (p % L::NSLOT) * L::SLOT;
-        // state before the update (h_c, or dh_c) as ctiles (key tile 2w + m, value tile NV vs + u).
+        // state before the update (h_c, or dh_c) as ttiles (key tile 2w + m, value tile NV vs + u),
+        // the layout in which the local kernel takes it as an MFMA operand:
+        // the state frag (M = value, K = keys) times the identity of key
+        // half m is the tile's transpose, exact in bf16.
         // The stored states and corrections (like the forward output rows) are
         // streaming stores: only the local kernel reads them, so in the L2
         // they would only evict the A1 / A2 tiles the slices of a head share
         // (128 -> 117 us for the recompute pair at (1,8192,16)).
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
+            const bf16x8 sfrag = pack_pi(S[u][0], S[u][1]);
             if constexpr (STORE) {
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
                     __builtin_nontemporal_store(
-                        pack4(S[u][m]), (bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m));
+                        pack4(mfma(sfrag, ident_pi(m), zero4())),
+                        (bf16x4*)ctile_ptr(Sout + t * (DKD * DVD), (NV * vs + u) * 8 + 2 * w + m));
             }
-            sS[u][w][l] = pack_pi(S[u][0], S[u][1]);
+            sS[u][w][l] = sfrag;
         }
         wait_lgkm0();
         bar();
