@@ -575,13 +575,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     }
     // ---- 1b. R and dO fragments (contraction over values) of value tile w ----
     {
-        const bf16x8 RT[2] = {cat8(rq[0], rq[1]), cat8(rq[2], rq[3])};
-        const bf16x8 Ip0 = ident_pi(0, lx), Ip1 = ident_pi(1, lx);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            // lane: R[tok 16 m + r][val 16 w + 4 g + e]
-            const f32x4 cc = mfma(RT[m >> 1], (m & 1) ? Ip1 : Ip0, zero4());
-            st_half(lR, m * 4 + (w >> 1), w & 1, pack4(cc));
+            // R is stored as ttiles: lane holds R[tok 16 m + r][val 16 w + 4 g + e]
+            st_half(lR, m * 4 + (w >> 1), w & 1, rq[m]);
             st_half(lO, m * 4 + (w >> 1), w & 1, tobf4(orw[m]));
         }
     }

@@ -60,9 +60,9 @@ struct Inter {
     bf16* AT;    // A^T = (I+L)^-T  frag  M=64 tok i, K=64 tok j (8 KiB)
     bf16* Af;    // A             frag  M=64 tok i, K=64 tok j (8 KiB)
     bf16* h;     // state at chunk start   ttile M=128 key, N=128 val (32 KiB)
-    bf16* R;     // correction             ctile M=64 tok,  N=128 val (16 KiB)
+    bf16* R;     // correction             ttile M=64 tok,  N=128 val (16 KiB)
     bf16* dh;    // state adjoint at chunk end, ttile like h         (32 KiB)
-    bf16* Rb;    // correction adjoint, ctile like R                 (16 KiB)
+    bf16* Rb;    // correction adjoint     ctile M=64 tok,  N=128 val (16 KiB)
     // gate check (prep): one word per prep wave, OR of GATE_* bits   (16 B)
     uint32_t* flags;
     // Two-level walks (regular batches whose one-level walks would leave

@@ -396,10 +396,14 @@ __device__ __forceinline__ void fed_compute(const Shape& s, const Inter& it, con
         wait_lgkm0();
         bar();
         if constexpr (STORE) {
+            // Rb as the ctile it is; R as a ttile (its transpose by the
+            // identity, exact), the layout in which the local kernel takes it
+            // as an MFMA operand
 #pragma unroll
-            for (int u = 0; u < NV; ++u)
-                __builtin_nontemporal_store(z4[u],
-                                            (bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w));
+            for (int u = 0; u < NV; ++u) {
+                const bf16x4 zs = BWD ? z4[u] : pack4(mfma(cat8(z4[u], bf16x4{}), ident_pi(0), zero4()));
+                __builtin_nontemporal_store(zs, (bf16x4*)ctile_ptr(Zout + t * (CH * DVD), (NV * vs + u) * 4 + w));
+            }
         }
         bf16x8 zf[NV][2], a2[2][2];
 #pragma unroll
