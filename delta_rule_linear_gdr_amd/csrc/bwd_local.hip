@@ -201,6 +201,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     // partials are two 16-byte reads)
     __shared__ __attribute__((aligned(16))) float sRedB[CH][NW], sRedP[CH][NW], sRedG[CH][NW];
     __shared__ float sExtra[DKD];
+    // scalar gate: exp(G) and exp(G_n - G) per token (wave 0, with the gate scan)
+    __shared__ __attribute__((aligned(16))) float sGam[VEC ? 4 : CH], sKt[VEC ? 4 : CH];
     __shared__ __attribute__((aligned(16))) float sEx[NW];
     // GDN2: the chunk's erase gates (token rows, per key), rows padded by 16
     // bytes so that the four row groups of a read fall on different banks
@@ -442,7 +444,12 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             for (int h = 0; h < 4; ++h) sWin[VEC ? h : 0][f] = 0.5f * (mx[h] + mn[h]);  // window centres
         }
     } else if (w == 0) {
-        sG[l] = wave_incl_scan(graw[0]);
+        const float Gl = wave_incl_scan(graw[0]);
+        sG[l] = Gl;
+        // the consumer loop's per-token factors gam = exp(G) and exp(G_n - G)
+        const float Gn = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Gl), CH - 1));
+        sGam[l] = __expf(Gl);
+        sKt[l] = __expf(Gn - Gl);
     }
     auto zero_lG = [&]() {
         const bf16x8 z8 = {};
@@ -969,10 +976,17 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             }
         }
         float Ga[4], br[4];
+        float gmv[4] = {0.f, 0.f, 0.f, 0.f}, ktv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (!VEC) {
+            const float4 gm4 = *(const float4*)&sGam[16 * m + 4 * g], kt4 = *(const float4*)&sKt[16 * m + 4 * g];
+            gmv[0] = gm4.x; gmv[1] = gm4.y; gmv[2] = gm4.z; gmv[3] = gm4.w;
+            ktv[0] = kt4.x; ktv[1] = kt4.y; ktv[2] = kt4.z; ktv[3] = kt4.w;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * m + 4 * g + e;
-            const float G = Gt(m, e), gam = __expf(G), kt = __expf(Gnf - G);
+            const float G = VEC ? Gt(m, e) : 0.f;
+            const float gam = VEC ? __expf(G) : gmv[e], kt = VEC ? __expf(Gnf - G) : ktv[e];
             const float bt = Et(m, e);
             // k and q back from the consumer operands (exact for the scalar
             // gate; hi + lo over the centred factor for the vector gate)
