@@ -53,8 +53,9 @@
 //      ttiles, whose lane pieces pair up into frag slabs) and the rowsum
 //      of h o dh in registers;
 //      K, Q in accumulator order through K * I (exact).
-//   2. D, D^T, Hb, Hb^T tiles (contraction over values) into LDS as the
-//      A operands of the Gram / matrix-intra products; Eb_dir, Qgb, Ktb.
+//   2. D and Hb tiles (contraction over values) into LDS as the A operands
+//      of the Gram / matrix-intra products, D^T and Hb^T read from the same
+//      tiles with gfx950's transposing LDS read; Eb_dir, Qgb, Ktb.
 //   3. The four consumer products; reductions of dbeta and dg.
 // Orientation changes use MFMA products with the identity, which are exact.
 //
@@ -76,6 +77,12 @@ constexpr int NTHR = 64 * NW;
 __device__ __forceinline__ void st_half(bf16x8* buf, int tile, int half, const bf16x4& v)
 {
     *(bf16x4*)((bf16*)&buf[tile * 64 + lane_id()] + 4 * half) = v;
+}
+// The same into a buffer whose slots are placed by tr_slot (read plainly at
+// tr_slot(lane), or transposed by ld_frag_t64x64).
+__device__ __forceinline__ void st_half_tr(bf16x8* buf, int tile, int half, const bf16x4& v)
+{
+    *(bf16x4*)((bf16*)&buf[tile * 64 + tr_slot(lane_id())] + 4 * half) = v;
 }
 
 // Prefetch of h and dh (persistent form): wave w copies the sixteen
@@ -164,7 +171,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 
     // LDS fragment buffers (16 x 32 frag tiles; 1024 entries = 64 x 128,
     // 512 entries = 64 x 64). Both producers: R, dO (M = tok, K = val) and the
-    // consumer A operands Gm, GT, Gq, GqT. ReWY: P (M = tok, K = val). The
+    // consumer A operands GT, GqT (and Gm, Gq: TRG below). ReWY: P (M = tok,
+    // K = val). The
     // seven-product producer: Rb, Z (M = tok, K = val), E, W (M = tok,
     // K = key) with W = Rb h^T, Abar^T (M = col, K = row) and X (M = tok,
     // K = tok) with X = A^T Abar.
@@ -173,7 +181,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     // the seven-product variant has no LDS left for them and keeps them in
     // registers.
     constexpr bool LO_LDS = VEC && !WY7;
-    constexpr int NLDS = WY7 ? 9216 : 5120;
+    // TRG: D and Hb stored once, D^T and Hb^T read from them transposed
+    // (see lGT below); the vector-gate seven-product kernel keeps all four
+    constexpr bool TRG = !(VEC && WY7);
+    constexpr int NLDS = WY7 ? (TRG ? 8192 : 9216) : 4096;
     __shared__ bf16x8 lds[NLDS + (LO_LDS ? NW * 6 * 64 : 0)];
     bf16x8* const lLo = lds + NLDS + (LO_LDS ? w * 6 * 64 : 0);
     bf16x8 loReg[LO_LDS ? 1 : 6];
@@ -192,10 +203,12 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     bf16x8* const lAbT = lds + 6144;
     bf16x8* const lX = lds + 6656;
     bf16x8* const lG = lds + (WY7 ? 7168 : 3072);
+    // TRG: D and Hb only, slots placed by tr_slot, D^T and Hb^T read from
+    // them with transposing LDS reads; otherwise all four, plainly
     bf16x8* const lGm = lG;
-    bf16x8* const lGT = lG + 512;
+    bf16x8* const lGT = lG + (TRG ? 0 : 512);
     bf16x8* const lGq = lG + 1024;
-    bf16x8* const lGqT = lG + 1536;
+    bf16x8* const lGqT = lG + (TRG ? 512 : 1536);
     __shared__ __attribute__((aligned(16))) float sG[CH], sBeta[CH];
     // per-token partial sums of the eight waves (token-major: a token's eight
     // partials are two 16-byte reads)
@@ -454,7 +467,7 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     auto zero_lG = [&]() {
         const bf16x8 z8 = {};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) lG[u * NTHR + tid] = z8;
+        for (int u = 0; u < (TRG ? 2 : 4); ++u) lG[u * NTHR + tid] = z8;
     };
     if constexpr (!SROW) zero_lG();
     if constexpr (GD2) {
@@ -701,6 +714,14 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         } else {
             B0[ks] = pack_pi(KC[2 * ks], KC[2 * ks + 1]);
             B1[ks] = pack_pi(QC[2 * ks], QC[2 * ks + 1]);
+            // diag(beta) K, the operand Gam^T multiplies (beta sits on the
+            // operand so that D's tiles serve D^T through a transposed read)
+            f32x4 bk[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bk[hh][e] = Bt(2 * ks + hh, e) * KC[2 * ks + hh][e];
+            B2[ks] = pack_pi(bk[0], bk[1]);
         }
     }
 
@@ -752,14 +773,23 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
         lds_barrier();  // lX complete
     }
 
-    // ---- 2a. D, D^T, Hb, Hb^T tiles -> consumer A operands. ReWY:
+    // ---- 2a. D and Hb tiles -> consumer A operands. ReWY:
     //      D = -strict_lower(P R^T). Seven-product: D = strict_lower(Mbar)
     //      with Mbar = -X A^T, formed here as -strict_lower(X A^T). ----
-    // (scalar gate: five items per wave unrolled, so that one item's LDS
+    // One item per 16 x 16 tile of D or Hb, 20 in all (the consumer loop
+    // reads D^T and Hb^T from the same tiles, transposed: 40 items before,
+    // bwd_local at (1,8192,16) 123.3 -> 114.3 us). The scalar gate's beta,
+    // which D^T must not carry, sits on the operand D multiplies instead.
+    // The vector-gate seven-product kernel keeps all four kinds of tiles
+    // (TRG): with the transposed reads its dk and dg did not repeat from
+    // run to run; that kernel spills some 45 registers, and the cause was
+    // not found.
+    // (scalar gate: the items of a wave unrolled, so that one item's LDS
     // reads overlap the previous item's products; the vector-gate kernel
     // keeps the rolled loop, having no registers to spare)
     auto item2a = [&](int x) {
-        const int kind = x / 10, tl = x % 10;
+        // TRG: D (kind 0) and Hb (kind 2); otherwise also D^T (1) and Hb^T (3)
+        const int kind = TRG ? 2 * (x / 10) : x / 10, tl = x % 10;
         const int ti = tl >= 6 ? 3 : tl >= 3 ? 2 : tl >= 1 ? 1 : 0;
         const int tj = tl - ti * (ti + 1) / 2;
         f32x4 acc = zero4();
@@ -782,9 +812,9 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 #pragma unroll
             for (int sl = 0; sl < 4; ++sl) acc = mfma(Aop[(ma * 4 + sl) * 64 + l], Bop[(nb * 4 + sl) * 64 + l], acc);
         }
-        // scalar gate: the gate values (and for D, beta) of this lane's rows
-        // and column, as one 16-byte and one 4-byte LDS read each
-        float4 G4 = {0.f, 0.f, 0.f, 0.f}, B4 = {1.f, 1.f, 1.f, 1.f};
+        // scalar gate: the gate values of this lane's rows and column, as
+        // one 16-byte and one 4-byte LDS read
+        float4 G4 = {0.f, 0.f, 0.f, 0.f};
         float G1 = 0.f;
         if (!VEC) {
             // kinds 0, 2: lane holds (i = 16 ti + 4 g + e, j = 16 tj + r);
@@ -793,9 +823,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             const int i1 = (kind & 1) ? 16 * ti + r : 16 * tj + r;
             G4 = *(const float4*)&sG[i4];
             G1 = sG[i1];
-            if (kind == 0) B4 = *(const float4*)&sBeta[i4];
         }
-        const float G4v[4] = {G4.x, G4.y, G4.z, G4.w}, B4v[4] = {B4.x, B4.y, B4.z, B4.w};
+        const float G4v[4] = {G4.x, G4.y, G4.z, G4.w};
         bf16x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -806,33 +835,39 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
             if (!VEC) {
                 const float Gi = (kind & 1) ? G1 : G4v[e], Gj = (kind & 1) ? G4v[e] : G1;
                 val *= keep ? __expf(Gi - Gj) : 0.f;  // Lam
-                if (kind == 0) val *= B4v[e];         // Gam^T diag(beta)
             }
             o[e] = (bf16)val;
         }
-        if (kind == 0) st_half(lGT, tj * 2 + (ti >> 1), ti & 1, o);        // D:    (M = j, K = i)
-        else if (kind == 1) st_half(lGm, ti * 2 + (tj >> 1), tj & 1, o);   // D^T:  (M = i, K = j)
-        else if (kind == 2) st_half(lGqT, tj * 2 + (ti >> 1), ti & 1, o);  // Hb:   (M = j, K = i)
-        else st_half(lGq, ti * 2 + (tj >> 1), tj & 1, o);                  // Hb^T: (M = i, K = j)
+        if constexpr (TRG) {
+            if (kind == 0) st_half_tr(lGT, tj * 2 + (ti >> 1), ti & 1, o);  // D:  (M = j, K = i)
+            else st_half_tr(lGqT, tj * 2 + (ti >> 1), ti & 1, o);            // Hb: (M = j, K = i)
+        } else {
+            if (kind == 0) st_half(lGT, tj * 2 + (ti >> 1), ti & 1, o);        // D:    (M = j, K = i)
+            else if (kind == 1) st_half(lGm, ti * 2 + (tj >> 1), tj & 1, o);   // D^T:  (M = i, K = j)
+            else if (kind == 2) st_half(lGqT, tj * 2 + (ti >> 1), ti & 1, o);  // Hb:   (M = j, K = i)
+            else st_half(lGq, ti * 2 + (tj >> 1), tj & 1, o);                  // Hb^T: (M = i, K = j)
+        }
     };
     if constexpr (VEC) {
-        for (int x = w; x < 40; x += NW) item2a(x);
+        for (int x = w; x < (TRG ? 20 : 40); x += NW) item2a(x);
     } else if constexpr (PF) {
         // Waves w and w + 4 share a SIMD, and the older one wins its issue
         // slots: waves 4..7 reach every barrier 1.4-2.4k cycles after waves
-        // 0..3 (per-wave timestamps). So waves 0..3 take six of the 40 items
-        // and waves 4..7 four (bwd_local at (1,8192,16): 135.7 -> 131.5 us;
-        // seven against three: 134 us).
+        // 0..3 (per-wave timestamps). So waves 0..3 take three of the 20
+        // items and waves 4..7 two (with the 40 items of four tiles, six and
+        // four: bwd_local at (1,8192,16) 135.7 -> 131.5 us; seven and three:
+        // 134 us).
         if (w < 4) {
 #pragma unroll
-            for (int u = 0; u < 6; ++u) item2a(w + 4 * u);
+            for (int u = 0; u < 3; ++u) item2a(w + 4 * u);
         } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) item2a(24 + (w - 4) + 4 * u);
+            for (int u = 0; u < 2; ++u) item2a(12 + (w - 4) + 4 * u);
         }
     } else {
 #pragma unroll
-        for (int u = 0; u < 40 / NW; ++u) item2a(w + NW * u);
+        for (int u = 0; u < 3; ++u)
+            if (w + NW * u < 20) item2a(w + NW * u);
     }
 
     lds_barrier();  // consumer A operands complete
@@ -909,7 +944,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks == 0 || m >= 2) {
-                    const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
+                    const bf16x8 a1 = TRG ? ld_frag_t64x64(lGT, m, ks) : lGm[(m * 2 + ks) * 64 + l];
+                    const bf16x8 a3 = TRG ? ld_frag_t64x64(lGqT, m, ks) : lGq[(m * 2 + ks) * 64 + l];
                     if (ks == (m >> 1) && (m & 1) == 0) {
                         // first half: window m; second half above the diagonal (zero in a1, a3)
                         const bf16x8 lo = lo_get(0 * 2 + ks);
@@ -936,7 +972,8 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                     }
                 }
                 if (ks == 1 || m < 2) {
-                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
+                    const int ps = TRG ? tr_slot(l) : l;
+                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + ps], a4 = lGqT[(m * 2 + ks) * 64 + ps];
                     if (ks == (m >> 1) && (m & 1) == 1) {
                         // first half below the diagonal (zero in a2, a4); second half: window m
                         X2 = mfma(a2, B2[ks], X2);  // D^T E'
@@ -964,13 +1001,15 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 if (ks == 0 || m >= 2) {
-                    const bf16x8 a1 = lGm[(m * 2 + ks) * 64 + l], a3 = lGq[(m * 2 + ks) * 64 + l];
+                    const bf16x8 a1 = TRG ? ld_frag_t64x64(lGT, m, ks) : lGm[(m * 2 + ks) * 64 + l];
+                    const bf16x8 a3 = TRG ? ld_frag_t64x64(lGqT, m, ks) : lGq[(m * 2 + ks) * 64 + l];
                     X1 = mfma(a1, B0[ks], X1);  // Gam K
                     X3 = mfma(a3, B0[ks], X3);  // Gq K
                 }
                 if (ks == 1 || m < 2) {
-                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + l], a4 = lGqT[(m * 2 + ks) * 64 + l];
-                    X2 = mfma(a2, B0[ks], X2);  // Gam^T bK
+                    const int ps = TRG ? tr_slot(l) : l;
+                    const bf16x8 a2 = lGT[(m * 2 + ks) * 64 + ps], a4 = lGqT[(m * 2 + ks) * 64 + ps];
+                    X2 = mfma(a2, B2[ks], X2);  // Gam^T diag(beta) K
                     X4 = mfma(a4, B1[ks], X4);  // Gq^T Q
                 }
             }

@@ -301,6 +301,20 @@ __device__ __forceinline__ bf16x8 ld_frag_t64x128(const uint8_t* xs, int mt, int
     return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The same for X 64 x 64 (K / 32 = 2: frag tiles (m, k) at m * 2 + k, 8 KiB;
+// X^T is 64 x 64, mt < 4 and ks < 2).
+__device__ __forceinline__ bf16x8 ld_frag_t64x64(const bf16x8* xs, int mt, int ks)
+{
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int r = lane_id() & 15, g = lane_id() >> 4;
+    const int slot = tr_slot(4 * g + (r >> 2) + 16 * (r & 3));
+    const uint8_t* p = (const uint8_t*)xs + (2 * ks * 2 + (mt >> 1)) * 1024 + slot * 16 + 8 * (mt & 1);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * 1024));
+    const bf16x4 l4 = __builtin_bit_cast(bf16x4, lo), h4 = __builtin_bit_cast(bf16x4, hi);
+    return __builtin_shufflevector(l4, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Lane pointer into ctile `tile`.
 __device__ __forceinline__ const bf16* ctile_ptr(const bf16* base, int tile)
 {
