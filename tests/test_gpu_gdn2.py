@@ -69,6 +69,18 @@ def test_gdn2_small_with_states(policy):
     _report(f"1x256x2/{policy}", compare_gdn2(run_gdn2(x, policy), x))
 
 
+def test_gdn2_repeatable_bits():
+    """Two identical calls give identical bits (the GDN2 local kernel reads
+    its D^T and Hb^T operands transposed from shared tiles in LDS)."""
+    _need_gpu()
+    x = make_inputs(2, 300, 3, gate="gdn2", dtype="bf16", seed=33, gate_mean=3.0,
+                    h0_std=0.1, dht_std=0.1)
+    a, b = run_gdn2(x), run_gdn2(x)
+    for n in a:
+        if a[n] is not None:
+            np.testing.assert_array_equal(a[n], b[n], err_msg=f"repeat {n}")
+
+
 @pytest.mark.parametrize("policy", ["recompute", "full_save"])
 def test_gdn2_ragged_two_sequences(policy):
     """T = 300: a ragged last chunk right before the second batch entry."""

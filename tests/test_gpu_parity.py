@@ -131,6 +131,25 @@ def test_deterministic_and_policy_independent():
         np.testing.assert_array_equal(a[n], c[n], err_msg=f"policy {n}")
 
 
+@pytest.mark.parametrize("gate", ["scalar", "vector", "none"])
+@pytest.mark.parametrize("wy7", [False, True])
+def test_repeatable_bits(gate, wy7):
+    """Two identical calls give identical bits, for every local kernel (the
+    persistent scalar-gate one, the per-chunk vector-gate one, DeltaNet, and
+    the seven-product producers), with a ragged last chunk. The local kernels
+    exchange their operand tiles through LDS, some read transposed; a tile
+    read before its writer finished would show here as a difference."""
+    _need_gpu()
+    x = _edge("scalar" if gate == "none" else gate, T=300, H=3, h0_std=0.1, dht_std=0.1)
+    nogate = gate == "none"
+    if nogate:
+        x["g"] = np.zeros_like(x["g"])
+    a = tl.run_gpu(x, "recompute", wy7=wy7, nogate=nogate)
+    b = tl.run_gpu(x, "recompute", wy7=wy7, nogate=nogate)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"repeat {n}")
+
+
 @pytest.mark.parametrize("gate", ["scalar", "vector"])
 def test_wy7_policy_independent(gate):
     """The seven-product backward under full save forms A from the saved A^T
