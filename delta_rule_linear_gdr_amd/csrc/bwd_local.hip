@@ -1130,8 +1130,10 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
                 if (16 * m + 4 * g + e < nv) dgo[(16 * m + 4 * g + e) * ld + f] = suf[e] + excl + carry;
             carry += ttot;
         }
-        // keep the scheduler from hoisting the next tile's operand reads
-        __builtin_amdgcn_sched_barrier(0);
+        // keep the scheduler from hoisting the next tile's operand reads (the
+        // per-chunk kernels, which have no registers to spare; the persistent
+        // one, at 240 VGPRs with the hoist, gains 1-2 us at (1,8192,16))
+        if (!PF) __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- 4. dbeta (wave 1); scalar gate: dg (wave 0), side by side ----
