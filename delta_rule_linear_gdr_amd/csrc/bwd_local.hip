@@ -1148,12 +1148,33 @@ __device__ __forceinline__ void bwd_local_chunk(const Shape& s, const Inputs& in
     else last_phase(dbo, dgo, nv);
 }
 
+// Staggered start of the per-chunk launches. Every workgroup begins with about
+// 200 KiB of reads and then computes; with one workgroup per CU and all CUs in
+// step, each round's reads arrive as one burst. The first workgroup on every
+// odd CU (HW_ID.CU_ID, so half the CUs of each shader array) sleeps about
+// 6.8 us (2 x 127 x 64 cycles) before it starts, a third of a round. Each CU
+// takes its next workgroup when the previous one ends, so the offset carries
+// over to the later rounds. ncu_first = the CU count for launches of eight or
+// more rounds, else 0 (no delay: a short launch would only lengthen its tail).
+__device__ __forceinline__ void staggered_start(int64_t lin, int ncu_first)
+{
+    if (lin >= ncu_first) return;
+    const unsigned cu = __builtin_amdgcn_s_getreg((3 << 11) | (8 << 6) | 4);  // HW_ID bits 8..11
+    if (cu & 1u) {
+        __builtin_amdgcn_s_sleep(127);
+        __builtin_amdgcn_s_sleep(127);
+    }
+}
+
 template <typename T, bool VEC, bool WY7, bool GD2 = false>
-__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr, int order)
+__global__ __launch_bounds__(NTHR) void bwd_local_kernel(Shape s, Inputs in, Inter it, Grads gr, int order,
+                                                         int ncu_first)
 {
     ChunkRef cr;
-    if (!chunk_in_order(s, blockIdx.x + (int64_t)blockIdx.y * gridDim.x, order, cr))
+    const int64_t lin = blockIdx.x + (int64_t)blockIdx.y * gridDim.x;
+    if (!chunk_in_order(s, lin, order, cr))
         return;  // an unused slot of a packed batch
+    staggered_start(lin, ncu_first);
     bwd_local_chunk<T, VEC, WY7, false, GD2>(s, in, it, gr, cr, -1, nullptr, nullptr);
 }
 
@@ -1198,11 +1219,15 @@ __global__ __launch_bounds__(NTHR) void bwd_local_pf_kernel(Shape s, Inputs in, 
 hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, const Grads& gr,
                             bool wy7, int order, bool per_chunk, hipStream_t st)
 {
+    // per-chunk launches: delay half the CUs' first workgroups when the launch
+    // runs eight or more rounds of one workgroup per CU
+    const int ncu = cu_count();
+    const int nf = s.NC * (s.B * s.H) >= 8 * (int64_t)ncu ? ncu : 0;
     if (s.gd2) {
         // GDN2: bf16 inputs, three-product producer only (the host refuses the rest)
         if (s.f32 || !s.vec || wy7) return hipErrorInvalidValue;
         dim3 grid((unsigned)s.NC, (unsigned)(s.B * s.H));
-        bwd_local_kernel<bf16, true, false, true><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);
+        bwd_local_kernel<bf16, true, false, true><<<grid, NTHR, 0, st>>>(s, in, it, gr, order, nf);
         return hipGetLastError();
     }
     if (!wy7 && !s.vec && !per_chunk) {
@@ -1218,11 +1243,11 @@ hipError_t launch_bwd_local(const Shape& s, const Inputs& in, const Inter& it, c
 #define GDR_BWD_LOCAL(W7)                                                                        \
     do {                                                                                         \
         if (s.f32) {                                                                             \
-            if (s.vec) bwd_local_kernel<float, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);  \
-            else bwd_local_kernel<float, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);       \
+            if (s.vec) bwd_local_kernel<float, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order, nf); \
+            else bwd_local_kernel<float, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order, nf);      \
         } else {                                                                                 \
-            if (s.vec) bwd_local_kernel<bf16, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);   \
-            else bwd_local_kernel<bf16, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order);        \
+            if (s.vec) bwd_local_kernel<bf16, true, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order, nf);  \
+            else bwd_local_kernel<bf16, false, W7><<<grid, NTHR, 0, st>>>(s, in, it, gr, order, nf);       \
         }                                                                                        \
     } while (0)
     if (wy7) GDR_BWD_LOCAL(true);
