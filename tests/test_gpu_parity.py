@@ -150,6 +150,19 @@ def test_repeatable_bits(gate, wy7):
         np.testing.assert_array_equal(a[n], b[n], err_msg=f"repeat {n}")
 
 
+@pytest.mark.parametrize("gate,wy7", [("vector", False), ("scalar", True)])
+def test_repeatable_bits_staggered_launch(gate, wy7):
+    """At (1,8192,16) the per-chunk local launches run 2,048 workgroups, eight
+    rounds of one per CU, so half the CUs start their first workgroup late.
+    The delay changes only timing: two calls still give identical bits."""
+    _need_gpu()
+    x = _edge(gate, T=8192, H=16, h0_std=0.1, dht_std=0.1)
+    a = tl.run_gpu(x, "recompute", wy7=wy7)
+    b = tl.run_gpu(x, "recompute", wy7=wy7)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"repeat {n}")
+
+
 @pytest.mark.parametrize("gate", ["scalar", "vector"])
 def test_wy7_policy_independent(gate):
     """The seven-product backward under full save forms A from the saved A^T
